@@ -1,0 +1,202 @@
+"""Seeded synthetic GEMM inputs and the named workloads.
+
+This module draws random operands and lays them out in memory.  It holds no
+GEMM arithmetic, so both the HIP path and the CPU oracle can take their
+inputs from it.
+
+Recipe (one ``torch.Generator`` on the CPU per problem, seeded explicitly):
+draw A, then B, then C, each over its whole stored buffer (padding included).
+- ``"uniform"``: U[-1, 1) as ``2*rand - 1`` in fp32;
+- ``"normal"``:  N(0, 1) as ``randn`` in fp32, then rounded to the operand
+  type (round-to-nearest-even for bf16 / fp16);
+- ``"int"``:     integers uniform in [lo, hi] (``randint``), stored exactly
+  in the operand type.
+
+The named workloads follow the shapes the pages measure on:
+- 256^3, 4096^3 and 6144^3 SGEMM ("Sgemm [128,128,8]" harness; "cuda11/matmul"
+  timing tables);
+- a ragged SGEMM whose sizes are no multiple of any tile, with integer-valued
+  operands in {0..99} (the residual-tile example of the CSDN tile-algorithm
+  page, which fills with ``rand() % 100``);
+- 16-bit inputs with a float accumulator (WMMA API page, type table);
+- strided-batched QK^T with B stored [n, d] ("cuda11/matmul", section
+  "Pytorch", the einsum 'bhqd,bhkd->bhqk' example).
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import numpy as np
+import torch
+
+TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+ELEM_SIZE = {"f32": 4, "f16": 2, "bf16": 2}
+
+
+@dataclasses.dataclass
+class Problem:
+    dtype: str                 # "f32" | "f16" | "bf16" (operand type; C is always fp32)
+    M: int
+    N: int
+    K: int
+    transA: bool = False
+    transB: bool = False
+    batch: int = 1
+    alpha: float = 1.0
+    beta: float = 0.0
+    dist: str = "uniform"      # "uniform" | "normal" | "int"
+    int_lo: int = 0
+    int_hi: int = 99
+    c_dist: Optional[str] = None   # distribution of C0; None -> same as dist
+    seed: int = 0
+    lda: Optional[int] = None
+    ldb: Optional[int] = None
+    ldc: Optional[int] = None
+    strideA: Optional[int] = None
+    strideB: Optional[int] = None
+    strideC: Optional[int] = None
+    pad_value: Optional[float] = None  # fill for padding beyond the logical matrix
+
+    def __post_init__(self):
+        a_rows, a_cols = (self.K, self.M) if self.transA else (self.M, self.K)
+        b_rows, b_cols = (self.N, self.K) if self.transB else (self.K, self.N)
+        self.a_rows, self.a_cols = a_rows, a_cols
+        self.b_rows, self.b_cols = b_rows, b_cols
+        if self.lda is None:
+            self.lda = max(a_cols, 1)
+        if self.ldb is None:
+            self.ldb = max(b_cols, 1)
+        if self.ldc is None:
+            self.ldc = max(self.N, 1)
+        if self.strideA is None:
+            self.strideA = a_rows * self.lda
+        if self.strideB is None:
+            self.strideB = b_rows * self.ldb
+        if self.strideC is None:
+            self.strideC = self.M * self.ldc
+
+    @property
+    def flops(self) -> float:
+        """2*M*N*K per batch entry, the pages' flop count."""
+        return 2.0 * self.M * self.N * self.K * self.batch
+
+    def buffer_elems(self, rows, ld, stride):
+        if self.batch == 0 or rows == 0:
+            return 0
+        return (self.batch - 1) * stride + (rows - 1) * ld + ld
+
+    @property
+    def a_elems(self):
+        return self.buffer_elems(self.a_rows, self.lda, self.strideA)
+
+    @property
+    def b_elems(self):
+        return self.buffer_elems(self.b_rows, self.ldb, self.strideB)
+
+    @property
+    def c_elems(self):
+        return self.buffer_elems(self.M, self.ldc, self.strideC)
+
+    def tolerance_coeff(self) -> float:
+        """c in max|err| <= c * sqrt(K) * max|ref| (fp32: 1e-5, 16-bit: 2e-3)."""
+        return 1e-5 if self.dtype == "f32" else 2e-3
+
+
+def _draw(gen, n, dist, lo, hi):
+    if dist == "uniform":
+        return 2.0 * torch.rand(n, generator=gen, dtype=torch.float32) - 1.0
+    if dist == "normal":
+        return torch.randn(n, generator=gen, dtype=torch.float32)
+    if dist == "int":
+        return torch.randint(lo, hi + 1, (n,), generator=gen).to(torch.float32)
+    raise ValueError(f"unknown distribution {dist!r}")
+
+
+def _logical_mask(total, batch, rows, cols, ld, stride):
+    """Boolean mask over a flat buffer: True where a logical matrix element lives."""
+    mask = np.zeros(total, dtype=bool)
+    if total == 0:
+        return mask
+    r = np.arange(rows)[:, None] * ld + np.arange(cols)[None, :]
+    for b in range(batch):
+        mask[b * stride + r.ravel()] = True
+    return mask
+
+
+def make_inputs(p: Problem):
+    """CPU torch tensors (flat) A, B (operand dtype) and C0 (fp32, or None when beta == 0
+    and no C distribution was asked for)."""
+    gen = torch.Generator()
+    gen.manual_seed(p.seed)
+    tdt = TORCH_DTYPE[p.dtype]
+    bufs = []
+    for elems, rows, cols, ld, stride in ((p.a_elems, p.a_rows, p.a_cols, p.lda, p.strideA),
+                                          (p.b_elems, p.b_rows, p.b_cols, p.ldb, p.strideB)):
+        x = _draw(gen, elems, p.dist, p.int_lo, p.int_hi).to(tdt)
+        if p.pad_value is not None and elems:
+            mask = torch.from_numpy(_logical_mask(elems, p.batch, rows, cols, ld, stride))
+            x[~mask] = p.pad_value
+        bufs.append(x)
+    C0 = None
+    if p.beta != 0.0 or p.c_dist is not None:
+        cd = p.c_dist or p.dist
+        C0 = _draw(gen, p.c_elems, cd, p.int_lo, p.int_hi)
+    return bufs[0], bufs[1], C0
+
+
+def to_numpy_operand(x: torch.Tensor) -> np.ndarray:
+    """Operand buffer as numpy: float32 values, or uint16 bit patterns for 16-bit types."""
+    x = x.detach().cpu().contiguous()
+    if x.dtype == torch.float32:
+        return x.numpy()
+    return x.view(torch.int16).numpy().view(np.uint16)
+
+
+# --------------------------------------------------------------------------------------
+# Named workloads.  Seeds are 1000 + the workload's number.
+# --------------------------------------------------------------------------------------
+
+def sgemm_256() -> Problem:
+    """SGEMM fp32 256^3, A, B ~ U[-1,1), alpha=1, beta=0."""
+    return Problem("f32", 256, 256, 256, dist="uniform", seed=1001)
+
+
+def sgemm_4096() -> Problem:
+    """SGEMM fp32 4096^3, A, B, C ~ U[-1,1), alpha=1.5, beta=0.5."""
+    return Problem("f32", 4096, 4096, 4096, alpha=1.5, beta=0.5, dist="uniform", seed=1002)
+
+
+def sgemm_ragged() -> Problem:
+    """SGEMM fp32 M=1000, N=1027, K=999, integer-valued operands in {0..99}."""
+    return Problem("f32", 1000, 1027, 999, dist="int", int_lo=0, int_hi=99, seed=1003)
+
+
+def gemm16_8192(dtype: str = "bf16") -> Problem:
+    """8192^3 with bf16 (or fp16) N(0,1) operands, fp32 accumulate and fp32 C."""
+    return Problem(dtype, 8192, 8192, 8192, dist="normal", seed=1004)
+
+
+def qkt_batched() -> Problem:
+    """Attention scores Q K^T: 128 (8 x 16 heads) x [1024 x 1024 x 64], fp16 N(0,1),
+    K stored [n, d] (transB), alpha = 1/sqrt(64), beta = 0."""
+    return Problem("f16", 1024, 1024, 64, transB=True, batch=128, alpha=1.0 / math.sqrt(64),
+                   dist="normal", seed=1005)
+
+
+WORKLOADS = {
+    "sgemm_256": sgemm_256,
+    "sgemm_4096": sgemm_4096,
+    "sgemm_ragged": sgemm_ragged,
+    "gemm_bf16_8192": lambda: gemm16_8192("bf16"),
+    "gemm_f16_8192": lambda: gemm16_8192("f16"),
+    "qkt_batched": qkt_batched,
+}
+
+
+def int_shadow(p: Problem, lo: int, hi: int) -> Problem:
+    """The same shape with integer-valued operands in [lo, hi] (and C0 too, when used),
+    chosen so that every partial sum stays below 2^24 and the result is exact in fp32."""
+    return dataclasses.replace(p, dist="int", int_lo=lo, int_hi=hi,
+                               c_dist="int" if p.c_dist or p.beta != 0.0 else None)

@@ -1,0 +1,203 @@
+/*
+ * Oracle for dense row-major GEMM -- TEST INFRASTRUCTURE ONLY.
+ *
+ * Only the test suite, the smoke check and the CPU-baseline leg of the
+ * benchmark may load this library.  The product library (libmgemm) never
+ * calls it, and the two share no source, header, table or helper.
+ *
+ * What it computes (plain definition, no blocking, no reordering):
+ *
+ *   for every batch b, row i < M, column j < N:
+ *       acc      = sum_{k = 0 .. K-1, ascending}  (double) opA[i][k] * (double) opB[k][j]
+ *       out[i,j] = alpha * acc + beta * C[i,j]      (the beta term is dropped when beta == 0)
+ *
+ * Sources on the pages:
+ *   - the GEMM form C = alpha*A*B + beta*C with every matrix row-major:
+ *     "Sgemm [128,128,8]" (jianshu), the kernel's design comment and the
+ *     host_gemm CPU reference that checks it;
+ *   - the triple loop with a scalar accumulator:
+ *     "cuda11/matmul" tutorial (dlog.com.cn), section "什么是矩阵乘法"
+ *     (what matrix multiplication is), the CPU sgemm;
+ *   - op(A)/op(B) with an explicit stride per matrix ("matrices may be
+ *     non-contiguous"): same tutorial, section "Triton", the wrapper that
+ *     passes strides;
+ *   - half and bfloat16 operands with a float accumulator:
+ *     WMMA API page (adg.csdn.net), "1. 概述", the element-type table.
+ *
+ * Readings taken where the pages are silent (each listed in the design doc):
+ *   - accumulation is fp64 (the pages accumulate in the element type; the
+ *     exact fp64 sum of fp32 products is the stricter reference);
+ *   - C is not read when beta == 0 (so NaN in C does not leak);
+ *   - alpha == 0 or K == 0 gives beta * C; M, N or batch == 0 does nothing;
+ *   - 16-bit inputs are decoded exactly from their bit patterns.
+ *
+ * Floating-point determinism: every product of two fp32 (or 16-bit) values
+ * is exact in fp64 (24 + 24 < 53 mantissa bits), and the sum runs over k in
+ * ascending order.  The file must be built with -ffp-contract=off so that
+ * the epilogue alpha*acc + beta*c is never fused.
+ *
+ * Parallelism: OpenMP over output rows only.  Each output element is still
+ * computed by exactly the loop above, so the thread count cannot change a bit.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <string.h>
+
+#define ORACLE_F32 0
+#define ORACLE_F16 1
+#define ORACLE_BF16 2
+
+#define ORACLE_OK 0
+#define ORACLE_BAD_ARG 1
+
+/* IEEE 754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction
+ * bits.  Exponent 0 encodes zero and subnormals (fraction * 2^-24),
+ * exponent 31 encodes infinities and NaNs. */
+double oracle_f16_to_double(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int expo = (h >> 10) & 0x1f;
+    int frac = h & 0x3ff;
+    double v;
+    if (expo == 0)
+        v = ldexp((double)frac, -24);
+    else if (expo == 31)
+        v = frac ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + frac), expo - 25);
+    return sign ? -v : v;
+}
+
+/* bfloat16: 1 sign bit, 8 exponent bits (bias 127), 7 fraction bits.
+ * Exponent 0 encodes zero and subnormals (fraction * 2^-133). */
+double oracle_bf16_to_double(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int expo = (h >> 7) & 0xff;
+    int frac = h & 0x7f;
+    double v;
+    if (expo == 0)
+        v = ldexp((double)frac, -133);
+    else if (expo == 255)
+        v = frac ? NAN : INFINITY;
+    else
+        v = ldexp((double)(128 + frac), expo - 134);
+    return sign ? -v : v;
+}
+
+/* Element (r, c) of a row-major matrix with leading dimension ld, widened. */
+static double load_elem(int dtype, const void *base, int64_t r, int64_t c, int64_t ld)
+{
+    int64_t off = r * ld + c;
+    if (dtype == ORACLE_F32)
+        return (double)((const float *)base)[off];
+    if (dtype == ORACLE_F16)
+        return oracle_f16_to_double(((const uint16_t *)base)[off]);
+    return oracle_bf16_to_double(((const uint16_t *)base)[off]);
+}
+
+/* op(A)[i][k]: A is stored M x K (transA == 0) or K x M (transA == 1). */
+static double op_a(int dtype, const void *A, int transA, int64_t i, int64_t k, int64_t lda)
+{
+    return transA ? load_elem(dtype, A, k, i, lda) : load_elem(dtype, A, i, k, lda);
+}
+
+/* op(B)[k][j]: B is stored K x N (transB == 0) or N x K (transB == 1). */
+static double op_b(int dtype, const void *B, int transB, int64_t k, int64_t j, int64_t ldb)
+{
+    return transB ? load_elem(dtype, B, j, k, ldb) : load_elem(dtype, B, k, j, ldb);
+}
+
+static size_t elem_size(int dtype) { return dtype == ORACLE_F32 ? 4 : 2; }
+
+/* One output element, exactly as the definition at the top of this file. */
+static double one_element(int dtype, int transA, int transB, int64_t K, double alpha,
+                          const void *A, int64_t lda, const void *B, int64_t ldb,
+                          double beta, const float *C, int64_t ldc,
+                          int64_t i, int64_t j)
+{
+    double acc = 0.0;
+    for (int64_t k = 0; k < K; ++k)
+        acc += op_a(dtype, A, transA, i, k, lda) * op_b(dtype, B, transB, k, j, ldb);
+    double out = alpha * acc;
+    if (beta != 0.0)
+        out = out + beta * (double)C[i * ldc + j];
+    return out;
+}
+
+static int check_args(int dtype, int transA, int transB, int64_t M, int64_t N, int64_t K,
+                      int64_t lda, int64_t ldb, int64_t ldc, int64_t batch)
+{
+    if (dtype < ORACLE_F32 || dtype > ORACLE_BF16) return ORACLE_BAD_ARG;
+    if ((transA != 0 && transA != 1) || (transB != 0 && transB != 1)) return ORACLE_BAD_ARG;
+    if (M < 0 || N < 0 || K < 0 || batch < 0) return ORACLE_BAD_ARG;
+    if (lda < (transA ? M : K) || ldb < (transB ? K : N) || ldc < N) return ORACLE_BAD_ARG;
+    return ORACLE_OK;
+}
+
+/*
+ * Full output: out[b*strideO + i*ldo + j] for every b < batch, i < M, j < N.
+ * A, B, C of batch b start at base + b*stride (in elements).
+ * C may be NULL when beta == 0.
+ */
+int oracle_gemm(int dtype, int transA, int transB,
+                int64_t M, int64_t N, int64_t K, double alpha,
+                const void *A, int64_t lda, int64_t strideA,
+                const void *B, int64_t ldb, int64_t strideB,
+                double beta, const float *C, int64_t ldc, int64_t strideC,
+                int64_t batch, double *out, int64_t ldo, int64_t strideO)
+{
+    if (check_args(dtype, transA, transB, M, N, K, lda, ldb, ldc, batch) != ORACLE_OK)
+        return ORACLE_BAD_ARG;
+    if (ldo < N) return ORACLE_BAD_ARG;
+    if (beta != 0.0 && C == NULL) return ORACLE_BAD_ARG;
+    size_t es = elem_size(dtype);
+    int64_t rows = batch * M;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t row = 0; row < rows; ++row) {
+        int64_t b = row / M, i = row % M;
+        const char *Ab = (const char *)A + (size_t)(b * strideA) * es;
+        const char *Bb = (const char *)B + (size_t)(b * strideB) * es;
+        const float *Cb = C ? C + b * strideC : NULL;
+        for (int64_t j = 0; j < N; ++j)
+            out[b * strideO + i * ldo + j] =
+                one_element(dtype, transA, transB, K, alpha, Ab, lda, Bb, ldb,
+                            beta, Cb, ldc, i, j);
+    }
+    return ORACLE_OK;
+}
+
+/*
+ * Selected elements only: out[e] is element (bidx[e], iidx[e], jidx[e]),
+ * computed by the same definition.  Used for full-size problems where the
+ * whole output would take too long on the host.
+ */
+int oracle_gemm_elems(int dtype, int transA, int transB,
+                      int64_t M, int64_t N, int64_t K, double alpha,
+                      const void *A, int64_t lda, int64_t strideA,
+                      const void *B, int64_t ldb, int64_t strideB,
+                      double beta, const float *C, int64_t ldc, int64_t strideC,
+                      int64_t batch, int64_t count,
+                      const int64_t *bidx, const int64_t *iidx, const int64_t *jidx,
+                      double *out)
+{
+    if (check_args(dtype, transA, transB, M, N, K, lda, ldb, ldc, batch) != ORACLE_OK)
+        return ORACLE_BAD_ARG;
+    if (beta != 0.0 && C == NULL) return ORACLE_BAD_ARG;
+    for (int64_t e = 0; e < count; ++e)
+        if (bidx[e] < 0 || bidx[e] >= batch || iidx[e] < 0 || iidx[e] >= M ||
+            jidx[e] < 0 || jidx[e] >= N)
+            return ORACLE_BAD_ARG;
+    size_t es = elem_size(dtype);
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t e = 0; e < count; ++e) {
+        int64_t b = bidx[e];
+        const char *Ab = (const char *)A + (size_t)(b * strideA) * es;
+        const char *Bb = (const char *)B + (size_t)(b * strideB) * es;
+        const float *Cb = C ? C + b * strideC : NULL;
+        out[e] = one_element(dtype, transA, transB, K, alpha, Ab, lda, Bb, ldb,
+                             beta, Cb, ldc, iidx[e], jidx[e]);
+    }
+    return ORACLE_OK;
+}
