@@ -1,0 +1,217 @@
+"""ctypes binding to libmgemm.so: argument marshalling only.
+
+Every function here forwards to the C entry point of the same name declared
+in include/mgemm.h.  Operands may be torch tensors (their ``data_ptr()`` is
+passed, after checking that they live on the GPU and are large enough for the
+sizes, leading dimensions and strides given) or raw integer device
+addresses (no checks beyond the library's own).  The default stream is the
+current torch stream of the operands' device.
+
+There is no fallback: if libmgemm.so is missing, the first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmgemm.so")
+
+OP_N, OP_T = 0, 1
+F32, F16, BF16 = 0, 1, 2
+DTYPE_CODES = {"f32": F32, "f16": F16, "bf16": BF16}
+ELEM_SIZE = {F32: 4, F16: 2, BF16: 2}
+
+STATUS = {0: "MGEMM_OK", 1: "MGEMM_INVALID_ARG", 2: "MGEMM_HIP_ERROR"}
+
+
+class MgemmError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {STATUS.get(status, status)}")
+        self.status = status
+
+
+class VariantInfo(ctypes.Structure):
+    _fields_ = [("id", ctypes.c_int), ("dtype", ctypes.c_int), ("block_m", ctypes.c_int),
+                ("block_n", ctypes.c_int), ("block_k", ctypes.c_int), ("waves_m", ctypes.c_int),
+                ("waves_n", ctypes.c_int), ("threads", ctypes.c_int), ("lds_bytes", ctypes.c_int),
+                ("name", ctypes.c_char * 64)]
+
+    def as_dict(self):
+        d = {f: getattr(self, f) for f, _ in self._fields_}
+        d["name"] = self.name.decode()
+        return d
+
+
+_lib = None
+
+
+def load():
+    """Load libmgemm.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build the HIP library first "
+            "(python -c 'import __graft_entry__ as g; g.build()'). There is no fallback path.")
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, i32, f32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_void_p
+    single = [i32, i32, i64, i64, i64, f32, vp, i64, vp, i64, f32, vp, i64, vp]
+    for name in ("gemm_f32", "gemm_f16", "gemm_bf16"):
+        fn = getattr(lib, name)
+        fn.restype = i32
+        fn.argtypes = single
+    lib.gemm_strided_batched.restype = i32
+    lib.gemm_strided_batched.argtypes = [i32, i32, i32, i64, i64, i64, f32, vp, i64, i64, vp, i64,
+                                         i64, f32, vp, i64, i64, i64, vp]
+    lib.mgemm_status_string.restype = ctypes.c_char_p
+    lib.mgemm_status_string.argtypes = [i32]
+    lib.mgemm_num_variants.restype = i32
+    lib.mgemm_num_variants.argtypes = []
+    lib.mgemm_variant.restype = i32
+    lib.mgemm_variant.argtypes = [i32, ctypes.POINTER(VariantInfo)]
+    lib.mgemm_select.restype = i32
+    lib.mgemm_select.argtypes = [i32, i32, i32, i64, i64, i64, f32, vp, i64, i64, vp, i64, i64,
+                                 f32, vp, i64, i64, i64, ctypes.POINTER(VariantInfo),
+                                 ctypes.POINTER(i64)]
+    lib.mgemm_force_variant.restype = i32
+    lib.mgemm_force_variant.argtypes = [i32, i32]
+    _lib = lib
+    return lib
+
+
+# --------------------------------------------------------------------------- helpers
+
+def _span(rows, cols, ld):
+    return 0 if rows == 0 or cols == 0 else (rows - 1) * ld + cols
+
+
+def _extent(rows, cols, ld, stride, batch):
+    """Elements an operand covers: batch entries at `stride`, each rows x cols at `ld`."""
+    if batch == 0:
+        return 0
+    return (batch - 1) * stride + _span(rows, cols, ld)
+
+
+def _addr(x, need_elems: int, elem_size: int, what: str):
+    """Device address of x; for tensors also checks device and size."""
+    if x is None:
+        return None, None
+    if isinstance(x, int):
+        return x, None
+    import torch
+    if not isinstance(x, torch.Tensor):
+        raise TypeError(f"{what}: expected a torch tensor or an int address")
+    if not x.is_cuda:
+        raise ValueError(f"{what} must be a GPU tensor")
+    if x.element_size() != elem_size:
+        raise ValueError(f"{what}: element size {x.element_size()} != {elem_size}")
+    if not x.is_contiguous():
+        raise ValueError(f"{what} must be a contiguous buffer (express strides with ld/stride)")
+    if x.numel() < need_elems:
+        raise ValueError(f"{what}: buffer holds {x.numel()} elements, sizes need {need_elems}")
+    return x.data_ptr(), x.device
+
+
+def _stream(stream, device):
+    if stream is not None:
+        return int(stream)
+    if device is None:
+        return None
+    import torch
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise MgemmError(status, what)
+
+
+def _single(name, dtype, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream):
+    es = ELEM_SIZE[dtype]
+    a_rows, a_cols = (K, M) if transA else (M, K)
+    b_rows, b_cols = (N, K) if transB else (K, N)
+    reads = M > 0 and N > 0 and K > 0 and alpha != 0.0
+    pa, _ = _addr(A, _span(a_rows, a_cols, lda) if reads else 0, es, "A")
+    pb, _ = _addr(B, _span(b_rows, b_cols, ldb) if reads else 0, es, "B")
+    pc, dev = _addr(C, _span(M, N, ldc), 4, "C")
+    st = getattr(load(), name)(int(transA), int(transB), M, N, K, alpha, pa, lda, pb, ldb, beta,
+                               pc, ldc, _stream(stream, dev))
+    _check(st, name)
+
+
+# --------------------------------------------------------------------------- entry points
+
+def gemm_f32(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None):
+    """C = alpha*op(A)*op(B) + beta*C, fp32 operands (see include/mgemm.h)."""
+    _single("gemm_f32", F32, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
+
+
+def gemm_f16(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None):
+    """binary16 A/B, fp32 accumulate and fp32 C."""
+    _single("gemm_f16", F16, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
+
+
+def gemm_bf16(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None):
+    """bfloat16 A/B, fp32 accumulate and fp32 C."""
+    _single("gemm_bf16", BF16, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+            stream)
+
+
+def gemm_strided_batched(in_dtype, transA, transB, M, N, K, alpha, A, lda, strideA, B, ldb,
+                         strideB, beta, C, ldc, strideC, batch, stream=None):
+    """Strided-batched GEMM; in_dtype is 0/1/2 or "f32"/"f16"/"bf16"."""
+    dt = DTYPE_CODES.get(in_dtype, in_dtype)
+    es = ELEM_SIZE[dt]
+    a_rows, a_cols = (K, M) if transA else (M, K)
+    b_rows, b_cols = (N, K) if transB else (K, N)
+    reads = M > 0 and N > 0 and K > 0 and alpha != 0.0 and batch > 0
+    pa, _ = _addr(A, _extent(a_rows, a_cols, lda, strideA, batch) if reads else 0, es, "A")
+    pb, _ = _addr(B, _extent(b_rows, b_cols, ldb, strideB, batch) if reads else 0, es, "B")
+    pc, dev = _addr(C, _extent(M, N, ldc, strideC, batch), 4, "C")
+    st = load().gemm_strided_batched(dt, int(transA), int(transB), M, N, K, alpha, pa, lda,
+                                     strideA, pb, ldb, strideB, beta, pc, ldc, strideC, batch,
+                                     _stream(stream, dev))
+    _check(st, "gemm_strided_batched")
+
+
+# --------------------------------------------------------------------------- introspection
+
+def status_string(status: int) -> str:
+    return load().mgemm_status_string(status).decode()
+
+
+def variants():
+    lib = load()
+    out = []
+    for i in range(lib.mgemm_num_variants()):
+        info = VariantInfo()
+        _check(lib.mgemm_variant(i, ctypes.byref(info)), "mgemm_variant")
+        out.append(info.as_dict())
+    return out
+
+
+def select(in_dtype, transA, transB, M, N, K, alpha=1.0, A=0, lda=None, strideA=0, B=0,
+           ldb=None, strideB=0, beta=0.0, C=0, ldc=None, strideC=0, batch=1):
+    """(variant info dict, grid size) for a call with these arguments; raises on invalid ones.
+    Pointers are plain integers here (alignment matters, contents do not)."""
+    dt = DTYPE_CODES.get(in_dtype, in_dtype)
+    lda = lda if lda is not None else (M if transA else K)
+    ldb = ldb if ldb is not None else (K if transB else N)
+    ldc = ldc if ldc is not None else N
+    info = VariantInfo()
+    grid = ctypes.c_int64()
+    st = load().mgemm_select(dt, int(transA), int(transB), M, N, K, alpha, A, lda, strideA, B, ldb,
+                             strideB, beta, C, ldc, strideC, batch, ctypes.byref(info),
+                             ctypes.byref(grid))
+    _check(st, "mgemm_select")
+    return info.as_dict(), grid.value
+
+
+def force_variant(in_dtype, variant_id: Optional[int]):
+    """Pin every later call of this input type to one variant (None restores auto)."""
+    dt = DTYPE_CODES.get(in_dtype, in_dtype)
+    _check(load().mgemm_force_variant(dt, -1 if variant_id is None else int(variant_id)),
+           "mgemm_force_variant")

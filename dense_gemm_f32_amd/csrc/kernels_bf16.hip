@@ -1,0 +1,19 @@
+// bf16-input kernel variants: v_mfma_f32_32x32x16_bf16, fp32 accumulate, 64-element K-slabs.
+#include "variants.hpp"
+
+namespace mgemm {
+
+const Variant *bf16_variants(int *count)
+{
+    static const Variant table[] = {
+        MGEMM_VARIANT(__bf16, 2, 256, 256, 64, 2, 2, true, "mgemm_bf16_256x256x64_w2x2"),
+        MGEMM_VARIANT(__bf16, 2, 128, 128, 64, 2, 2, true, "mgemm_bf16_128x128x64_w2x2"),
+        MGEMM_VARIANT(__bf16, 2, 128, 128, 64, 2, 2, false, "mgemm_bf16_128x128x64_w2x2_u"),
+        MGEMM_VARIANT(__bf16, 2, 64, 64, 64, 2, 2, true, "mgemm_bf16_64x64x64_w2x2"),
+        MGEMM_VARIANT(__bf16, 2, 64, 64, 64, 2, 2, false, "mgemm_bf16_64x64x64_w2x2_u"),
+    };
+    *count = sizeof(table) / sizeof(table[0]);
+    return table;
+}
+
+}  // namespace mgemm

@@ -1,0 +1,19 @@
+// f16-input kernel variants: v_mfma_f32_32x32x16_f16, fp32 accumulate, 64-element K-slabs.
+#include "variants.hpp"
+
+namespace mgemm {
+
+const Variant *f16_variants(int *count)
+{
+    static const Variant table[] = {
+        MGEMM_VARIANT(_Float16, 1, 256, 256, 64, 2, 2, true, "mgemm_f16_256x256x64_w2x2"),
+        MGEMM_VARIANT(_Float16, 1, 128, 128, 64, 2, 2, true, "mgemm_f16_128x128x64_w2x2"),
+        MGEMM_VARIANT(_Float16, 1, 128, 128, 64, 2, 2, false, "mgemm_f16_128x128x64_w2x2_u"),
+        MGEMM_VARIANT(_Float16, 1, 64, 64, 64, 2, 2, true, "mgemm_f16_64x64x64_w2x2"),
+        MGEMM_VARIANT(_Float16, 1, 64, 64, 64, 2, 2, false, "mgemm_f16_64x64x64_w2x2_u"),
+    };
+    *count = sizeof(table) / sizeof(table[0]);
+    return table;
+}
+
+}  // namespace mgemm

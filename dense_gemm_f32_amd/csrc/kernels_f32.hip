@@ -1,0 +1,19 @@
+// fp32 (SGEMM) kernel variants: v_mfma_f32_32x32x2_f32, 32-float K-slabs.
+#include "variants.hpp"
+
+namespace mgemm {
+
+const Variant *f32_variants(int *count)
+{
+    static const Variant table[] = {
+        MGEMM_VARIANT(float, 0, 256, 256, 32, 2, 2, true, "mgemm_f32_256x256x32_w2x2"),
+        MGEMM_VARIANT(float, 0, 128, 128, 32, 2, 2, true, "mgemm_f32_128x128x32_w2x2"),
+        MGEMM_VARIANT(float, 0, 128, 128, 32, 2, 2, false, "mgemm_f32_128x128x32_w2x2_u"),
+        MGEMM_VARIANT(float, 0, 64, 64, 32, 2, 2, true, "mgemm_f32_64x64x32_w2x2"),
+        MGEMM_VARIANT(float, 0, 64, 64, 32, 2, 2, false, "mgemm_f32_64x64x32_w2x2_u"),
+    };
+    *count = sizeof(table) / sizeof(table[0]);
+    return table;
+}
+
+}  // namespace mgemm

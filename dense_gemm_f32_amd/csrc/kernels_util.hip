@@ -1,0 +1,31 @@
+// C = beta * C for the alpha == 0 and K == 0 cases.
+#include "variants.hpp"
+
+namespace mgemm {
+
+__global__ void __launch_bounds__(256) scale_c_kernel(float *C, int M, int N, int64_t ldc,
+                                                      int64_t strideC, int batch, float beta)
+{
+    const int64_t total = (int64_t)batch * M * N;
+    const int64_t step = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += step) {
+        const int64_t b = e / ((int64_t)M * N);
+        const int64_t rem = e - b * M * N;
+        const int64_t i = rem / N, j = rem - i * N;
+        float *c = C + b * strideC + i * ldc + j;
+        *c = beta == 0.0f ? 0.0f : beta * *c;
+    }
+}
+
+hipError_t launch_scale_c(float *C, int M, int N, int64_t ldc, int64_t strideC, int batch,
+                          float beta, hipStream_t s)
+{
+    const int64_t total = (int64_t)batch * M * N;
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    void *args[] = {&C, &M, &N, &ldc, &strideC, &batch, &beta};
+    return hipLaunchKernel(reinterpret_cast<const void *>(&scale_c_kernel), dim3((unsigned)blocks),
+                           dim3(256), args, 0, s);
+}
+
+}  // namespace mgemm

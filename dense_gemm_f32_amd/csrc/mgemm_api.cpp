@@ -1,0 +1,294 @@
+// C-ABI entry points: argument validation, variant selection, launch.
+//
+// Validation and selection are pure host code (no HIP call), so the
+// introspection functions work on machines without a GPU.
+#include <atomic>
+#include <climits>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/mgemm.h"
+#include "variants.hpp"
+
+namespace mgemm {
+namespace {
+
+struct Table {
+    const Variant *v;
+    int n;
+    int first_id;  // global id of v[0]
+};
+
+Table table_for(int dtype)
+{
+    int n32, n16, nb16;
+    const Variant *v32 = f32_variants(&n32);
+    const Variant *v16 = f16_variants(&n16);
+    const Variant *vb16 = bf16_variants(&nb16);
+    switch (dtype) {
+    case MGEMM_F32: return {v32, n32, 0};
+    case MGEMM_F16: return {v16, n16, n32};
+    case MGEMM_BF16: return {vb16, nb16, n32 + n16};
+    default: return {nullptr, 0, 0};
+    }
+}
+
+std::atomic<int> g_forced[3] = {{-1}, {-1}, {-1}};
+
+int total_variants() { return table_for(MGEMM_BF16).first_id + table_for(MGEMM_BF16).n; }
+
+const Variant *variant_by_id(int id)
+{
+    for (int d = 0; d < 3; ++d) {
+        Table t = table_for(d);
+        if (id >= t.first_id && id < t.first_id + t.n) return &t.v[id - t.first_id];
+    }
+    return nullptr;
+}
+
+int elem_size(int dtype) { return dtype == MGEMM_F32 ? 4 : 2; }
+
+// What a validated call will do.
+struct Plan {
+    enum Kind { NOTHING, SCALE, GEMM } kind;
+    const Variant *var;
+    int id;
+    KernelArgs args;
+    int64_t grid;
+};
+
+bool aligned(const void *p, int64_t bytes) { return (reinterpret_cast<uintptr_t>(p) % bytes) == 0; }
+
+// Smallest element span one stored matrix occupies: (rows-1)*ld + cols.
+int64_t span(int64_t rows, int64_t cols, int64_t ld) { return rows == 0 || cols == 0 ? 0 : (rows - 1) * ld + cols; }
+
+mgemm_status validate_and_plan(int dtype, int transA, int transB, int64_t M, int64_t N, int64_t K,
+                               float alpha, const void *A, int64_t lda, int64_t strideA,
+                               const void *B, int64_t ldb, int64_t strideB, float beta,
+                               const float *C, int64_t ldc, int64_t strideC, int64_t batch,
+                               Plan *plan)
+{
+    if (dtype != MGEMM_F32 && dtype != MGEMM_F16 && dtype != MGEMM_BF16) return MGEMM_INVALID_ARG;
+    if ((transA != MGEMM_OP_N && transA != MGEMM_OP_T) || (transB != MGEMM_OP_N && transB != MGEMM_OP_T))
+        return MGEMM_INVALID_ARG;
+    if (M < 0 || N < 0 || K < 0 || batch < 0) return MGEMM_INVALID_ARG;
+    if (M > INT_MAX || N > INT_MAX || K > INT_MAX || batch > INT_MAX) return MGEMM_INVALID_ARG;
+    const int64_t a_rows = transA ? K : M, a_cols = transA ? M : K;
+    const int64_t b_rows = transB ? N : K, b_cols = transB ? K : N;
+    if (lda < (a_cols > 1 ? a_cols : 1) || ldb < (b_cols > 1 ? b_cols : 1) || ldc < (N > 1 ? N : 1))
+        return MGEMM_INVALID_ARG;
+    if (strideA < 0 || strideB < 0 || strideC < 0) return MGEMM_INVALID_ARG;
+    if (batch > 1) {
+        if (strideA != 0 && strideA < span(a_rows, a_cols, lda)) return MGEMM_INVALID_ARG;
+        if (strideB != 0 && strideB < span(b_rows, b_cols, ldb)) return MGEMM_INVALID_ARG;
+        if (M > 0 && N > 0 && strideC < span(M, N, ldc)) return MGEMM_INVALID_ARG;
+    }
+    const int es = elem_size(dtype);
+    const bool writes_c = M > 0 && N > 0 && batch > 0;
+    const bool reads_ab = writes_c && K > 0 && alpha != 0.0f;
+    if (writes_c && (C == nullptr || !aligned(C, 4))) return MGEMM_INVALID_ARG;
+    if (reads_ab && (A == nullptr || B == nullptr || !aligned(A, es) || !aligned(B, es)))
+        return MGEMM_INVALID_ARG;
+
+    plan->kind = Plan::NOTHING;
+    plan->var = nullptr;
+    plan->id = -1;
+    plan->grid = 0;
+    if (!writes_c) return MGEMM_OK;
+    KernelArgs &a = plan->args;
+    a.A = A;
+    a.B = B;
+    a.C = const_cast<float *>(C);
+    a.lda = lda;
+    a.ldb = ldb;
+    a.ldc = ldc;
+    a.strideA = strideA;
+    a.strideB = strideB;
+    a.strideC = strideC;
+    a.M = (int)M;
+    a.N = (int)N;
+    a.K = (int)K;
+    a.alpha = alpha;
+    a.beta = beta;
+    a.c_vec = aligned(C, 16) && ldc % 4 == 0 && (batch == 1 || strideC % 4 == 0);
+    if (!reads_ab) {
+        plan->kind = Plan::SCALE;
+        return MGEMM_OK;
+    }
+
+    // 16-byte global accesses need 16-byte aligned operand rows in every batch entry.
+    const int vec = 16 / es;
+    const bool vec_ok = aligned(A, 16) && aligned(B, 16) && lda % vec == 0 && ldb % vec == 0 &&
+                        strideA % vec == 0 && strideB % vec == 0;
+
+    Table t = table_for(dtype);
+    const int forced = g_forced[dtype].load();
+    int pick = -1;
+    if (forced >= 0) {
+        const Variant *v = variant_by_id(forced);
+        if (v && (!v->vec || vec_ok)) pick = forced - t.first_id;
+        // a forced aligned-only variant on unaligned data falls back to the automatic choice
+    }
+    if (pick < 0) {
+        // Largest tile that still gives at least one workgroup per CU (256 CUs);
+        // otherwise the smallest tile, to spread a small problem over more CUs.
+        const int64_t min_wgs = 256;
+        int best = -1, smallest = -1;
+        for (int i = 0; i < t.n; ++i) {
+            const Variant &v = t.v[i];
+            if (v.vec && !vec_ok) continue;
+            if (!v.vec && vec_ok) continue;  // prefer the aligned build of a shape when allowed
+            const int64_t wgs = ((M + v.bm - 1) / v.bm) * ((N + v.bn - 1) / v.bn) * batch;
+            if (smallest < 0 || v.bm * v.bn < t.v[smallest].bm * t.v[smallest].bn) smallest = i;
+            if (wgs >= min_wgs && (best < 0 || v.bm * v.bn > t.v[best].bm * t.v[best].bn)) best = i;
+        }
+        pick = best >= 0 ? best : smallest;
+    }
+    if (pick < 0) return MGEMM_INVALID_ARG;
+    const Variant &v = t.v[pick];
+    a.tiles_m = (int)((M + v.bm - 1) / v.bm);
+    a.tiles_n = (int)((N + v.bn - 1) / v.bn);
+    const int64_t grid = (int64_t)a.tiles_m * a.tiles_n * batch;
+    if (grid > INT_MAX) return MGEMM_INVALID_ARG;
+    // raster group: tile rows walked together (cache reuse of B columns)
+    a.group_m = a.tiles_m < 8 ? a.tiles_m : 8;
+    if (a.group_m < 1) a.group_m = 1;
+    plan->kind = Plan::GEMM;
+    plan->var = &v;
+    plan->id = t.first_id + pick;
+    plan->grid = grid;
+    return MGEMM_OK;
+}
+
+void fill_info(const Variant &v, int id, mgemm_variant_info *out)
+{
+    out->id = id;
+    out->dtype = v.dtype;
+    out->block_m = v.bm;
+    out->block_n = v.bn;
+    out->block_k = v.bk;
+    out->waves_m = v.wm;
+    out->waves_n = v.wn;
+    out->threads = v.wm * v.wn * 64;
+    out->lds_bytes = 2 * (v.bm + v.bn) * v.bk * elem_size(v.dtype);
+    std::snprintf(out->name, sizeof(out->name), "%s", v.name);
+}
+
+mgemm_status run(int dtype, int transA, int transB, int64_t M, int64_t N, int64_t K, float alpha,
+                 const void *A, int64_t lda, int64_t strideA, const void *B, int64_t ldb,
+                 int64_t strideB, float beta, float *C, int64_t ldc, int64_t strideC,
+                 int64_t batch, hipStream_t stream)
+{
+    Plan plan;
+    mgemm_status st = validate_and_plan(dtype, transA, transB, M, N, K, alpha, A, lda, strideA, B,
+                                        ldb, strideB, beta, C, ldc, strideC, batch, &plan);
+    if (st != MGEMM_OK || plan.kind == Plan::NOTHING) return st;
+    hipError_t err;
+    if (plan.kind == Plan::SCALE) {
+        err = launch_scale_c(C, (int)M, (int)N, ldc, strideC, (int)batch, beta, stream);
+    } else {
+        err = plan.var->fn[transA][transB](plan.args, (unsigned)plan.grid, stream);
+    }
+    return err == hipSuccess ? MGEMM_OK : MGEMM_HIP_ERROR;
+}
+
+}  // namespace
+}  // namespace mgemm
+
+using namespace mgemm;
+
+extern "C" {
+
+mgemm_status gemm_f32(mgemm_op transA, mgemm_op transB, int64_t M, int64_t N, int64_t K,
+                      float alpha, const float *A, int64_t lda, const float *B, int64_t ldb,
+                      float beta, float *C, int64_t ldc, hipStream_t stream)
+{
+    return run(MGEMM_F32, transA, transB, M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C, ldc, 0, 1,
+               stream);
+}
+
+mgemm_status gemm_f16(mgemm_op transA, mgemm_op transB, int64_t M, int64_t N, int64_t K,
+                      float alpha, const mgemm_f16 *A, int64_t lda, const mgemm_f16 *B,
+                      int64_t ldb, float beta, float *C, int64_t ldc, hipStream_t stream)
+{
+    return run(MGEMM_F16, transA, transB, M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C, ldc, 0, 1,
+               stream);
+}
+
+mgemm_status gemm_bf16(mgemm_op transA, mgemm_op transB, int64_t M, int64_t N, int64_t K,
+                       float alpha, const mgemm_bf16 *A, int64_t lda, const mgemm_bf16 *B,
+                       int64_t ldb, float beta, float *C, int64_t ldc, hipStream_t stream)
+{
+    return run(MGEMM_BF16, transA, transB, M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C, ldc, 0, 1,
+               stream);
+}
+
+mgemm_status gemm_strided_batched(mgemm_dtype in_dtype, mgemm_op transA, mgemm_op transB,
+                                  int64_t M, int64_t N, int64_t K, float alpha, const void *A,
+                                  int64_t lda, int64_t strideA, const void *B, int64_t ldb,
+                                  int64_t strideB, float beta, float *C, int64_t ldc,
+                                  int64_t strideC, int64_t batch, hipStream_t stream)
+{
+    return run(in_dtype, transA, transB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C,
+               ldc, strideC, batch, stream);
+}
+
+const char *mgemm_status_string(mgemm_status s)
+{
+    switch (s) {
+    case MGEMM_OK: return "MGEMM_OK";
+    case MGEMM_INVALID_ARG: return "MGEMM_INVALID_ARG: an argument failed validation; nothing was launched";
+    case MGEMM_HIP_ERROR: return "MGEMM_HIP_ERROR: the HIP runtime refused the kernel launch";
+    default: return "unknown mgemm_status";
+    }
+}
+
+int mgemm_num_variants(void) { return total_variants(); }
+
+mgemm_status mgemm_variant(int id, mgemm_variant_info *out)
+{
+    const Variant *v = variant_by_id(id);
+    if (!v || !out) return MGEMM_INVALID_ARG;
+    fill_info(*v, id, out);
+    return MGEMM_OK;
+}
+
+mgemm_status mgemm_select(mgemm_dtype in_dtype, mgemm_op transA, mgemm_op transB, int64_t M,
+                          int64_t N, int64_t K, float alpha, const void *A, int64_t lda,
+                          int64_t strideA, const void *B, int64_t ldb, int64_t strideB,
+                          float beta, const float *C, int64_t ldc, int64_t strideC,
+                          int64_t batch, mgemm_variant_info *out, int64_t *grid)
+{
+    Plan plan;
+    mgemm_status st = validate_and_plan(in_dtype, transA, transB, M, N, K, alpha, A, lda, strideA,
+                                        B, ldb, strideB, beta, C, ldc, strideC, batch, &plan);
+    if (st != MGEMM_OK) return st;
+    if (out) {
+        if (plan.kind == Plan::GEMM) {
+            fill_info(*plan.var, plan.id, out);
+        } else {
+            std::memset(out, 0, sizeof(*out));
+            out->id = -1;
+            std::snprintf(out->name, sizeof(out->name), "%s",
+                          plan.kind == Plan::SCALE ? "mgemm_scale_c" : "none");
+        }
+    }
+    if (grid) *grid = plan.kind == Plan::GEMM ? plan.grid : 0;
+    return MGEMM_OK;
+}
+
+mgemm_status mgemm_force_variant(mgemm_dtype dtype, int id)
+{
+    if (dtype != MGEMM_F32 && dtype != MGEMM_F16 && dtype != MGEMM_BF16) return MGEMM_INVALID_ARG;
+    if (id >= 0) {
+        const Variant *v = variant_by_id(id);
+        if (!v || v->dtype != dtype) return MGEMM_INVALID_ARG;
+    } else {
+        id = -1;
+    }
+    g_forced[dtype].store(id);
+    return MGEMM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,47 @@
+// Registry of compiled GEMM kernel variants (one per tile shape and
+// alignment class; each holds the four transpose combinations).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "gemm_kernel.hpp"
+
+namespace mgemm {
+
+using LaunchFn = hipError_t (*)(const KernelArgs &, unsigned grid, hipStream_t);
+
+struct Variant {
+    int dtype;            // mgemm_dtype of A and B
+    int bm, bn, bk;       // workgroup tile and K-slab
+    int wm, wn;           // wavefront grid
+    bool vec;             // needs 16-byte aligned A/B rows (dwordx4 loads)
+    const char *name;
+    LaunchFn fn[2][2];    // [transA][transB]
+};
+
+template <typename T, int BM, int BN, int BK, int WM, int WN, bool TA, bool TB, bool V>
+hipError_t launch_gemm(const KernelArgs &a, unsigned grid, hipStream_t s)
+{
+    KernelArgs copy = a;
+    void *args[] = {&copy};
+    return hipLaunchKernel(reinterpret_cast<const void *>(&gemm_kernel<T, BM, BN, BK, WM, WN, TA, TB, V>),
+                           dim3(grid), dim3(WM * WN * 64), args, 0, s);
+}
+
+#define MGEMM_VARIANT(T, DT, BM, BN, BK, WM, WN, V, NAME)                                   \
+    {DT, BM, BN, BK, WM, WN, V, NAME,                                                        \
+     {{launch_gemm<T, BM, BN, BK, WM, WN, false, false, V>,                                  \
+       launch_gemm<T, BM, BN, BK, WM, WN, false, true, V>},                                  \
+      {launch_gemm<T, BM, BN, BK, WM, WN, true, false, V>,                                   \
+       launch_gemm<T, BM, BN, BK, WM, WN, true, true, V>}}}
+
+// Host-side variant tables, one per input type (function-local statics, so
+// that the device compilation never sees the host launch pointers).
+const Variant *f32_variants(int *count);
+const Variant *f16_variants(int *count);
+const Variant *bf16_variants(int *count);
+
+hipError_t launch_scale_c(float *C, int M, int N, int64_t ldc, int64_t strideC, int batch,
+                          float beta, hipStream_t s);
+
+}  // namespace mgemm

@@ -1,0 +1,176 @@
+/*
+ * mgemm -- dense row-major GEMM for AMD Instinct MI355X (gfx950).
+ *
+ *     C = alpha * op(A) * op(B) + beta * C
+ *
+ * The operation is the one defined on the page "Sgemm [128,128,8]"
+ * (jianshu): C = alpha*A*B + beta*C with every matrix stored row-major
+ * (the kernel's design comment, and host_gemm, its CPU reference).  op(X) is
+ * X or its transpose: the transposed-operand form is the one the
+ * "cuda11/matmul" tutorial (dlog.com.cn) reaches through einsum
+ * 'bhqd,bhkd->bhqk' (section "Pytorch"), and the strided-batched form is its
+ * bmm.  16-bit inputs with a float accumulator are the mixed-precision types
+ * of the WMMA API page (adg.csdn.net), "1. 概述", element-type table.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Layout.  All matrices are row-major: element (r, c) of a matrix with
+ *   leading dimension ld sits at base[r*ld + c].
+ *   op(A) is M x K.  transA == MGEMM_OP_N: A is stored M x K, lda >= max(1,K).
+ *                    transA == MGEMM_OP_T: A is stored K x M, lda >= max(1,M).
+ *   op(B) is K x N.  transB == MGEMM_OP_N: B is stored K x N, ldb >= max(1,N).
+ *                    transB == MGEMM_OP_T: B is stored N x K, ldb >= max(1,K).
+ *   C is M x N, fp32, ldc >= max(1,N).
+ *   Leading dimensions and batch strides are in elements.
+ * Arithmetic.  Products and sums are fp32 (16-bit inputs are converted
+ *   exactly); the summation order over k is unspecified but fixed, so
+ *   repeated calls give identical bits.  Out-of-range parts of edge tiles
+ *   contribute exactly zero (the residual-tile rule of the CSDN tile-algorithm
+ *   page, "使用CUDA和瓦片算法计算矩阵乘法").  No saturation: IEEE inf/NaN.
+ * beta == 0: C is write-only; its old contents (NaN included) are never read.
+ * alpha == 0 or K == 0: C = beta * C; A and B are not read.
+ * M == 0, N == 0 or batch == 0: nothing is launched; MGEMM_OK.
+ * Ownership.  The caller owns A, B and C (device memory, e.g. from PyTorch).
+ *   The library allocates, frees and keeps nothing; it needs no handle and
+ *   no workspace, and may be called from several host threads at once.
+ * Asynchrony.  Each call validates its arguments on the host, enqueues one
+ *   kernel on `stream` (NULL = the default stream) and returns.  Results are
+ *   ready after the stream is synchronised.
+ * Errors.  Invalid arguments are reported synchronously and nothing is
+ *   launched: negative sizes, a leading dimension or stride below its
+ *   minimum, a NULL pointer for an operand that will be read or written,
+ *   a pointer not aligned to its element size, an unknown op or dtype,
+ *   sizes beyond 2^31-1.  A failed launch returns MGEMM_HIP_ERROR.  Faults
+ *   inside a kernel surface at the caller's next synchronisation.
+ * Aliasing.  C must not overlap A or B.
+ * Alignment.  Only element alignment is required; wider (16-byte) accesses
+ *   are used when pointers, leading dimensions and strides allow them.
+ */
+#ifndef MGEMM_H
+#define MGEMM_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MGEMM_OK = 0,
+    MGEMM_INVALID_ARG = 1,
+    MGEMM_HIP_ERROR = 2
+} mgemm_status;
+
+typedef enum { MGEMM_OP_N = 0, MGEMM_OP_T = 1 } mgemm_op;
+
+typedef enum { MGEMM_F32 = 0, MGEMM_F16 = 1, MGEMM_BF16 = 2 } mgemm_dtype;
+
+/* Raw 16-bit storage: IEEE 754 binary16 and bfloat16 bit patterns. */
+typedef uint16_t mgemm_f16;
+typedef uint16_t mgemm_bf16;
+
+/*
+ * SGEMM: fp32 A, B, C; fp32 matrix-core products and fp32 accumulation.
+ * Defined by "Sgemm [128,128,8]" (jianshu), design comment and host_gemm.
+ */
+mgemm_status gemm_f32(mgemm_op transA, mgemm_op transB,
+                      int64_t M, int64_t N, int64_t K, float alpha,
+                      const float *A, int64_t lda,
+                      const float *B, int64_t ldb,
+                      float beta, float *C, int64_t ldc,
+                      hipStream_t stream);
+
+/*
+ * binary16 A and B, fp32 accumulation and fp32 C.
+ * Input/accumulator pairing from the WMMA API page, "1. 概述" type table
+ * (__half inputs, float accumulator).
+ */
+mgemm_status gemm_f16(mgemm_op transA, mgemm_op transB,
+                      int64_t M, int64_t N, int64_t K, float alpha,
+                      const mgemm_f16 *A, int64_t lda,
+                      const mgemm_f16 *B, int64_t ldb,
+                      float beta, float *C, int64_t ldc,
+                      hipStream_t stream);
+
+/*
+ * bfloat16 A and B, fp32 accumulation and fp32 C.
+ * Same table (__nv_bfloat16 inputs, float accumulator).
+ */
+mgemm_status gemm_bf16(mgemm_op transA, mgemm_op transB,
+                       int64_t M, int64_t N, int64_t K, float alpha,
+                       const mgemm_bf16 *A, int64_t lda,
+                       const mgemm_bf16 *B, int64_t ldb,
+                       float beta, float *C, int64_t ldc,
+                       hipStream_t stream);
+
+/*
+ * Strided-batched GEMM: for b in [0, batch)
+ *     C_b = alpha * op(A_b) * op(B_b) + beta * C_b,
+ *     X_b = X + b * strideX   (element offsets, int64).
+ * The bmm / einsum 'bhqd,bhkd->bhqk' forms of the "cuda11/matmul" tutorial
+ * (dlog.com.cn), section "Pytorch".  in_dtype selects A/B's type (C is
+ * always fp32).  strideA or strideB may be 0 (the operand is shared by every
+ * batch entry); otherwise each must cover one operand matrix.  strideC must
+ * cover one M x N matrix (C entries may not overlap).
+ */
+mgemm_status gemm_strided_batched(mgemm_dtype in_dtype, mgemm_op transA, mgemm_op transB,
+                                  int64_t M, int64_t N, int64_t K, float alpha,
+                                  const void *A, int64_t lda, int64_t strideA,
+                                  const void *B, int64_t ldb, int64_t strideB,
+                                  float beta, float *C, int64_t ldc, int64_t strideC,
+                                  int64_t batch, hipStream_t stream);
+
+/* Human-readable text for a status code (static storage). */
+const char *mgemm_status_string(mgemm_status s);
+
+/* ---------------------------------------------------------------------------
+ * Introspection and tuning.  Pure host functions: no device is touched, so
+ * they work on machines without a GPU.
+ * ------------------------------------------------------------------------- */
+
+/* Description of one compiled kernel variant (a tile shape). */
+typedef struct {
+    int id;            /* index accepted by mgemm_force_variant */
+    int dtype;         /* mgemm_dtype of the inputs */
+    int block_m;       /* output tile rows per workgroup */
+    int block_n;       /* output tile columns per workgroup */
+    int block_k;       /* K elements staged in LDS per pipeline step */
+    int waves_m;       /* wavefronts along M */
+    int waves_n;       /* wavefronts along N */
+    int threads;       /* workgroup size */
+    int lds_bytes;     /* LDS per workgroup */
+    char name[64];     /* kernel family name, e.g. "mgemm_f32_256x256x32_w2x2" */
+} mgemm_variant_info;
+
+/* Number of compiled variants (all dtypes). */
+int mgemm_num_variants(void);
+
+/* Fill *out for variant `id`; MGEMM_INVALID_ARG if id is out of range. */
+mgemm_status mgemm_variant(int id, mgemm_variant_info *out);
+
+/*
+ * The variant (and launch grid size) a call with these arguments would use,
+ * after the same validation the entry points perform.  Returns the
+ * validation status; *out and *grid are set on MGEMM_OK (id = -1 and grid = 0
+ * when the call would launch no GEMM kernel).
+ */
+mgemm_status mgemm_select(mgemm_dtype in_dtype, mgemm_op transA, mgemm_op transB,
+                          int64_t M, int64_t N, int64_t K, float alpha,
+                          const void *A, int64_t lda, int64_t strideA,
+                          const void *B, int64_t ldb, int64_t strideB,
+                          float beta, const float *C, int64_t ldc, int64_t strideC,
+                          int64_t batch, mgemm_variant_info *out, int64_t *grid);
+
+/*
+ * Force every later call of dtype `dtype` onto variant `id` (-1 restores the
+ * automatic choice).  Process-wide; meant for tests and tile sweeps.
+ * MGEMM_INVALID_ARG if the variant does not exist or has another dtype.
+ */
+mgemm_status mgemm_force_variant(mgemm_dtype dtype, int id);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MGEMM_H */

@@ -1,0 +1,179 @@
+"""C-ABI boundary checks that need no GPU: the library loads, exports every
+symbol its header declares, validates arguments on the host and selects
+variants.  No kernel is launched here: every call either fails validation
+(which happens before any HIP call) or is a pure-host introspection call."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import dense_gemm_f32_amd as mg
+from dense_gemm_f32_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mgemm.h")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def built_library():
+    if not os.path.exists(_lib.LIB_PATH):
+        from dense_gemm_f32_amd import build
+        build.build()
+    return mg.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for want in ("gemm_f32", "gemm_f16", "gemm_bf16", "gemm_strided_batched",
+                 "mgemm_status_string", "mgemm_select", "mgemm_force_variant"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, missing
+    lib = mg.load()
+    for n in declared_functions():
+        assert getattr(lib, n) is not None
+
+
+def test_status_strings():
+    assert mg.status_string(0) == "MGEMM_OK"
+    assert "INVALID_ARG" in mg.status_string(1)
+    assert "HIP" in mg.status_string(2)
+    assert "unknown" in mg.status_string(99)
+
+
+def test_variant_table():
+    vs = mg.variants()
+    assert len(vs) == mg.load().mgemm_num_variants() >= 3
+    for i, v in enumerate(vs):
+        assert v["id"] == i
+        assert v["threads"] == v["waves_m"] * v["waves_n"] * 64
+        assert v["lds_bytes"] <= 160 * 1024
+        assert v["name"].startswith("mgemm_")
+    assert {v["dtype"] for v in vs} == {0, 1, 2}
+    info = _lib.VariantInfo()
+    assert mg.load().mgemm_variant(len(vs), ctypes.byref(info)) == 1
+
+
+ALIGNED = 1 << 20  # a 16-byte aligned fake address; select() never dereferences it
+
+
+def sel(dtype="f32", tA=0, tB=0, M=64, N=64, K=64, **kw):
+    kw.setdefault("A", ALIGNED)
+    kw.setdefault("B", ALIGNED)
+    kw.setdefault("C", ALIGNED)
+    return mg.select(dtype, tA, tB, M, N, K, **kw)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(M=-1), dict(N=-1), dict(K=-1), dict(batch=-1),
+    dict(lda=63), dict(ldb=63), dict(ldc=63),
+    dict(A=0), dict(B=0), dict(C=0),
+    dict(A=ALIGNED + 2), dict(C=ALIGNED + 2),
+    dict(M=2 ** 31), dict(strideA=-1),
+    dict(batch=2, strideC=64 * 64 - 1), dict(batch=2, strideA=100, strideC=4096),
+])
+def test_validation_rejects(bad):
+    with pytest.raises(mg.MgemmError) as e:
+        sel(**bad)
+    assert e.value.status == 1
+
+
+def test_validation_bad_op_and_dtype():
+    with pytest.raises(mg.MgemmError):
+        sel(tA=2)
+    with pytest.raises(mg.MgemmError):
+        sel(dtype=7)
+
+
+def test_transposed_leading_dimension_rules():
+    # op(A)=A^T: A stored K x M -> lda >= M ; op(B)=B^T: B stored N x K -> ldb >= K
+    sel(tA=1, tB=1, M=100, N=30, K=20, lda=100, ldb=20, ldc=30)
+    with pytest.raises(mg.MgemmError):
+        sel(tA=1, M=100, N=30, K=20, lda=99, ldb=30, ldc=30)
+    with pytest.raises(mg.MgemmError):
+        sel(tB=1, M=100, N=30, K=20, lda=20, ldb=19, ldc=30)
+
+
+def test_quick_returns_launch_no_gemm():
+    info, grid = sel(M=0)
+    assert info["id"] == -1 and grid == 0 and info["name"] == "none"
+    info, grid = sel(batch=0)
+    assert info["name"] == "none"
+    # alpha == 0 or K == 0: C = beta*C, A/B not read (NULL allowed)
+    info, grid = sel(alpha=0.0, A=0, B=0, beta=2.0)
+    assert info["name"] == "mgemm_scale_c" and grid == 0
+    info, grid = sel(K=0, A=0, B=0, lda=1, ldb=64)
+    assert info["name"] == "mgemm_scale_c"
+
+
+def test_broadcast_strides_allowed():
+    sel(batch=4, strideA=0, strideB=64 * 64, strideC=64 * 64)
+    sel(batch=4, strideA=64 * 64, strideB=0, strideC=64 * 64)
+
+
+def test_unaligned_operands_get_unaligned_variant():
+    info, _ = sel(M=1000, N=1027, K=999, lda=999, ldb=1027, ldc=1027)
+    assert info["name"].endswith("_u")
+    info, _ = sel(A=ALIGNED + 4)
+    assert info["name"].endswith("_u")
+    info, _ = sel()
+    assert not info["name"].endswith("_u")
+
+
+def test_selection_for_the_named_workloads():
+    big, g = sel(M=4096, N=4096, K=4096, alpha=1.5, beta=0.5)
+    assert g == (4096 // big["block_m"]) * (4096 // big["block_n"]) and g >= 256
+    info, g = sel("bf16", M=8192, N=8192, K=8192)
+    assert info["dtype"] == 2 and g >= 256
+    info, g = sel("f16", 0, 1, M=1024, N=1024, K=64, lda=64, ldb=64, ldc=1024, batch=128,
+                  strideA=65536, strideB=65536, strideC=1048576, alpha=0.125)
+    assert info["dtype"] == 1 and g == 128 * (1024 // info["block_m"]) * (1024 // info["block_n"])
+
+
+def test_force_variant_roundtrip():
+    vs = mg.variants()
+    f32_ids = [v["id"] for v in vs if v["dtype"] == 0]
+    bf16_ids = [v["id"] for v in vs if v["dtype"] == 2]
+    try:
+        mg.force_variant("f32", f32_ids[-1])
+        info, _ = sel(M=4096, N=4096, K=4096)
+        assert info["id"] == f32_ids[-1]
+        with pytest.raises(mg.MgemmError):
+            mg.force_variant("f32", bf16_ids[0])
+    finally:
+        mg.force_variant("f32", None)
+    info, _ = sel(M=4096, N=4096, K=4096)
+    assert info["id"] != f32_ids[-1] or len(f32_ids) == 1
+
+
+def test_entry_points_reject_bad_arguments_without_a_gpu():
+    lib = mg.load()
+    # negative M: rejected during host validation, before any HIP call
+    assert lib.gemm_f32(0, 0, -1, 4, 4, 1.0, ALIGNED, 4, ALIGNED, 4, 0.0, ALIGNED, 4, None) == 1
+    assert lib.gemm_bf16(0, 0, 4, 4, 4, 1.0, None, 4, ALIGNED, 4, 0.0, ALIGNED, 4, None) == 1
+    assert lib.gemm_f16(0, 1, 4, 4, 4, 1.0, ALIGNED, 4, ALIGNED, 3, 0.0, ALIGNED, 4, None) == 1
+    assert lib.gemm_strided_batched(0, 0, 0, 4, 4, 4, 1.0, ALIGNED, 4, 16, ALIGNED, 4, 16, 0.0,
+                                    ALIGNED, 4, 15, 2, None) == 1
+    # nothing to do: OK with no launch
+    assert lib.gemm_f32(0, 0, 0, 4, 4, 1.0, None, 4, None, 4, 0.0, None, 4, None) == 0
+
+
+def test_binding_refuses_host_tensors_and_short_buffers():
+    import torch
+    a = torch.zeros(16)
+    with pytest.raises(ValueError):
+        mg.gemm_f32(0, 0, 4, 4, 4, 1.0, a, 4, a, 4, 0.0, a, 4)

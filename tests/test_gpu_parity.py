@@ -1,0 +1,236 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bar: bit-exact on integer-valued inputs whose partial sums stay below 2^24
+(the result is then unique); otherwise max|err| <= c*sqrt(K)*max|ref|, with
+c = 1e-5 for fp32 inputs and 2e-3 for f16/bf16 inputs.
+Small problems are compared element by element over the whole output; the
+full-size workloads, in the launch configuration the benchmark times, on
+sampled elements (whole boundary rows/columns plus random positions).
+"""
+import dataclasses
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+from dense_gemm_f32_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import dense_gemm_f32_amd as mg
+    from parity import Run, check_exact, check_tolerance, log, sample_positions
+
+
+@pytest.fixture(autouse=True)
+def _auto_variant():
+    yield
+    for dt in ("f32", "f16", "bf16"):
+        mg.force_variant(dt, None)
+
+
+def full_check(p, exact=False, c_fill=None, what=""):
+    log(f"[{what}] {p.dtype} tA={int(p.transA)} tB={int(p.transB)} M={p.M} N={p.N} K={p.K} "
+        f"batch={p.batch} lda={p.lda} ldb={p.ldb} ldc={p.ldc} alpha={p.alpha} beta={p.beta} "
+        f"dist={p.dist} seed={p.seed}")
+    r = Run(p, c_fill=c_fill)
+    r.launch()
+    got = r.result()
+    ref = r.oracle_full()
+    if exact:
+        check_exact(got, ref, what)
+    else:
+        check_tolerance(got, ref, p, what)
+    return got
+
+
+def sampled_check(p, exact=False, what="", n_random=20000):
+    log(f"[{what}] {p.dtype} tA={int(p.transA)} tB={int(p.transB)} M={p.M} N={p.N} K={p.K} "
+        f"batch={p.batch} alpha={p.alpha} beta={p.beta} dist={p.dist} seed={p.seed} (sampled)")
+    info, grid = mg.select(p.dtype, int(p.transA), int(p.transB), p.M, p.N, p.K, p.alpha,
+                           16, p.lda, p.strideA, 16, p.ldb, p.strideB, p.beta, 16, p.ldc,
+                           p.strideC, p.batch)
+    log(f"  variant {info['name']} grid {grid}")
+    r = Run(p)
+    r.launch()
+    got = r.result()
+    b, i, j = sample_positions(p, n_random=n_random)
+    ref = r.oracle_elems(b, i, j)
+    vals = got[b, i, j]
+    if exact:
+        check_exact(vals, ref, what)
+    else:
+        check_tolerance(vals, ref, p, what)
+    assert not np.isnan(got).any()
+
+
+def variants_of(dtype):
+    code = {"f32": 0, "f16": 1, "bf16": 2}[dtype]
+    return [v for v in mg.variants() if v["dtype"] == code] if torch.cuda.is_available() else []
+
+
+# ------------------------------------------------------------------ every variant, every op
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_every_variant_every_transpose_ragged(dtype):
+    for v in variants_of(dtype):
+        mg.force_variant(dtype, v["id"])
+        bm, bn, bk = v["block_m"], v["block_n"], v["block_k"]
+        M, N, K = 2 * bm + 17, 2 * bn + 9, 3 * bk + 5
+        for tA, tB in itertools.product((False, True), repeat=2):
+            base = wl.Problem(dtype, M, N, K, transA=tA, transB=tB, alpha=1.5, beta=0.5,
+                              dist="uniform" if dtype == "f32" else "normal",
+                              c_dist="uniform", seed=11)
+            full_check(base, what=f"{v['name']} float")
+            full_check(wl.int_shadow(base, -8, 8), exact=True, what=f"{v['name']} int")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_unaligned_leading_dims_and_nan_padding(dtype):
+    # odd leading dimensions (no 16-byte rows) and NaN in every padding element
+    for tA, tB in itertools.product((False, True), repeat=2):
+        M, N, K = 77, 91, 83
+        a_cols = M if tA else K
+        b_cols = K if tB else N
+        p = wl.Problem(dtype, M, N, K, transA=tA, transB=tB, lda=a_cols + 3, ldb=b_cols + 5,
+                       ldc=N + 7, dist="int", int_lo=-9, int_hi=9, pad_value=float("nan"),
+                       seed=12)
+        full_check(p, exact=True, c_fill=float("nan"), what="odd ld, NaN padding")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_aligned_padded_leading_dims(dtype):
+    vec = 4 if dtype == "f32" else 8
+    for tA, tB in itertools.product((False, True), repeat=2):
+        M, N, K = 300, 260, 140
+        a_cols = M if tA else K
+        b_cols = K if tB else N
+        p = wl.Problem(dtype, M, N, K, transA=tA, transB=tB, lda=a_cols + vec, ldb=b_cols + 2 * vec,
+                       ldc=N + 4, alpha=-1.0, beta=2.0, dist="int", int_lo=-9, int_hi=9,
+                       pad_value=float("nan"), seed=13)
+        full_check(p, exact=True, what="aligned padded ld")
+
+
+# ------------------------------------------------------------------ the named workloads
+
+def test_sgemm_256():
+    p = wl.sgemm_256()
+    full_check(p, c_fill=float("nan"), what="sgemm 256^3, beta=0 with NaN C")
+    full_check(wl.int_shadow(p, -50, 50), exact=True, what="sgemm 256^3 int shadow")
+
+
+def test_sgemm_ragged_bit_exact():
+    full_check(wl.sgemm_ragged(), exact=True, c_fill=float("nan"), what="sgemm 1000x1027x999 ints")
+
+
+def test_sgemm_4096():
+    p = wl.sgemm_4096()
+    sampled_check(p, what="sgemm 4096^3 alpha=1.5 beta=0.5")
+    sampled_check(wl.int_shadow(p, -7, 7), exact=True, what="sgemm 4096^3 int shadow")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_gemm16_8192(dtype):
+    p = wl.gemm16_8192(dtype)
+    sampled_check(p, what=f"{dtype} 8192^3")
+    sampled_check(wl.int_shadow(p, -8, 8), exact=True, what=f"{dtype} 8192^3 int shadow")
+
+
+def test_qkt_batched():
+    p = wl.qkt_batched()
+    sampled_check(p, what="QK^T 128 x 1024x1024x64 fp16")
+    sampled_check(wl.int_shadow(p, -8, 8), exact=True, what="QK^T int shadow")
+
+
+# ------------------------------------------------------------------ shapes from the pages
+
+def test_csdn_ragged_integer_example():
+    # A 47 x 804, B 804 x 53, rand() % 100 values (CSDN tile-algorithm page, main)
+    p = wl.Problem("f32", 47, 53, 804, dist="int", int_lo=0, int_hi=99, seed=14)
+    full_check(p, exact=True, what="47x804x53 ints")
+
+
+def test_dlog_shapes():
+    full_check(wl.Problem("f32", 100, 300, 200, dist="normal", seed=15), what="mm 100x200x300")
+    full_check(wl.Problem("f32", 16, 128, 64, batch=10, dist="normal", seed=16),
+               what="bmm (10,16,64)x(10,64,128)")
+    full_check(wl.Problem("f16", 10, 10, 64, transB=True, batch=16, alpha=0.125, dist="normal",
+                          seed=17), what="einsum QK^T (2,8,10,64)")
+
+
+def test_wmma_single_tile_f16_col_major_a():
+    # 16x16x16 half inputs, A column-major (= op(A) = A^T row-major), float accumulator
+    p = wl.Problem("f16", 16, 16, 16, transA=True, dist="normal", seed=18)
+    full_check(p, what="16^3 f16 transA")
+    full_check(wl.int_shadow(p, -8, 8), exact=True, what="16^3 f16 transA int")
+
+
+# ------------------------------------------------------------------ degenerate cases
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_alpha_zero_and_k_zero_give_beta_c(dtype):
+    for p in (wl.Problem(dtype, 70, 50, 30, alpha=0.0, beta=0.5, c_dist="uniform", seed=19),
+              wl.Problem(dtype, 70, 50, 0, alpha=1.0, beta=-2.0, c_dist="uniform", seed=20),
+              wl.Problem(dtype, 70, 50, 0, alpha=1.0, beta=0.0, seed=21)):
+        full_check(p, exact=True, c_fill=float("nan"), what=f"alpha={p.alpha} K={p.K}")
+
+
+def test_empty_problems_touch_nothing():
+    for M, N in ((0, 10), (10, 0)):
+        p = wl.Problem("f32", M, N, 5, seed=22)
+        log(f"[empty] M={M} N={N}")
+        mg.gemm_f32(0, 0, M, N, 5, 1.0, torch.zeros(64, device="cuda"), 5,
+                    torch.zeros(64, device="cuda"), max(N, 1), 0.0, torch.zeros(64, device="cuda"),
+                    max(N, 1))
+    c = torch.full((64,), 3.0, device="cuda")
+    mg.gemm_strided_batched("f32", 0, 0, 4, 4, 4, 1.0, c, 4, 16, c, 4, 16, 0.0, c, 4, 16, 0)
+    torch.cuda.synchronize()
+    assert torch.all(c == 3.0)
+
+
+def test_minimum_sizes():
+    for M, N, K in ((1, 1, 1), (1, 7, 3), (5, 1, 9), (3, 3, 1), (33, 65, 2)):
+        for dt in ("f32", "f16", "bf16"):
+            full_check(wl.Problem(dt, M, N, K, dist="int", int_lo=-9, int_hi=9, seed=23),
+                       exact=True, what="tiny")
+
+
+def test_broadcast_operands_in_batches():
+    p = wl.Problem("f32", 40, 36, 44, batch=5, strideA=0, dist="int", int_lo=-9, int_hi=9,
+                   seed=24)
+    full_check(p, exact=True, what="strideA=0")
+    p = wl.Problem("bf16", 40, 36, 44, batch=5, strideB=0, transB=True, dist="int", int_lo=-9,
+                   int_hi=9, seed=25)
+    full_check(p, exact=True, what="strideB=0")
+
+
+def test_repeated_runs_are_bitwise_identical():
+    p = wl.Problem("f32", 1024, 1024, 1024, alpha=1.0, beta=0.0, dist="uniform", seed=26)
+    log("[determinism] f32 1024^3 x3")
+    r = Run(p)
+    outs = []
+    for _ in range(3):
+        r.launch()
+        outs.append(r.result().copy())
+    assert all(np.array_equal(outs[0], o) for o in outs[1:])
+    q = wl.Problem("bf16", 1024, 1024, 1024, dist="normal", seed=27)
+    log("[determinism] bf16 1024^3 x3")
+    r = Run(q)
+    outs = []
+    for _ in range(3):
+        r.launch()
+        outs.append(r.result().copy())
+    assert all(np.array_equal(outs[0], o) for o in outs[1:])
+
+
+def test_runs_on_a_side_stream():
+    p = wl.Problem("bf16", 512, 384, 256, transA=True, dist="normal", seed=28)
+    log("[side stream] bf16 512x384x256")
+    r = Run(p)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        r.launch()          # binding picks the current (side) stream
+    s.synchronize()
+    got = r.result()
+    check_tolerance(got, r.oracle_full(), p, "side stream")
