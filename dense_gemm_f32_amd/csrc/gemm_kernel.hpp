@@ -8,13 +8,14 @@
 //   * block tiling with a K-slab staged in on-chip memory ("cuda11/matmul",
 //     section "V1 Tile版本") -> LDS tiles;
 //   * 16-byte vector global accesses ("V2 Tile"; the float4 loads of the
-//     jianshu kernel) -> dwordx4 loads and 16-byte LDS writes/reads;
-//   * a transposed on-chip tile so that a thread reads several rows with one
-//     vector access ("V3 双缓冲", the transposed SA; jianshu's transposed A)
-//     -> the fp32 "MN-contiguous" LDS layout read with ds_read_b128;
-//   * double buffering with the next slab fetched to registers while the
-//     current one is consumed, one barrier per slab ("V3 双缓冲"; the
-//     jianshu kernel's two shared stages and peeled tail);
+//     jianshu kernel) -> dwordx4 loads, here issued straight into LDS;
+//   * a transposed on-chip tile so that one access serves several rows
+//     ("V3 双缓冲", the transposed SA; jianshu's transposed A tile) -> on
+//     CDNA4 the transpose happens in the LDS read (ds_read_b64_tr_b16) or,
+//     for fp32, in the choice of which index a lane's vector read runs along;
+//   * overlapping the fetch of later slabs with the math on the current one
+//     ("V3 双缓冲"; the jianshu kernel's double buffer and prefetch) ->
+//     a 4-stage LDS ring filled three slabs ahead;
 //   * zero-filled residual tiles and guarded stores (the CSDN tile-algorithm
 //     page, "使用CUDA和瓦片算法计算矩阵乘法", MatrixMulCUDA);
 //   * grouped tile ordering for cache reuse ("cuda11/matmul", Triton
@@ -22,22 +23,28 @@
 // What replaces the NVIDIA-era pieces: the per-thread 8x8 FMA micro-tile and
 // the WMMA fragments become 32x32 MFMA blocks per wavefront
 // (v_mfma_f32_32x32x2_f32 for fp32, v_mfma_f32_32x32x16_{f16,bf16} for
-// 16-bit inputs), with fp32 accumulators held in registers.
+// 16-bit inputs) with fp32 accumulators.
 //
-// MFMA operand/result placement used below (wave64, lane l, i' = l % 32,
-// h = l / 32):
+// MFMA operand/result placement (wave64, lane l, i' = l % 32, h = l / 32):
 //   32x32x2 f32 : lane supplies A[i'][k_h] and B[k_h][i'] (one value each);
 //   32x32x16    : lane supplies 8 values A[i'][k in group h] and B[k][i'];
 //   result      : accumulator element r (0..15) of lane l is row
 //                 8*(r/4) + 4*h + r%4, column i'.
-// Only the result placement and "lanes index rows of A / columns of B" matter:
-// a sum over k does not depend on which k each (h, element) slot carries, as
-// long as A and B agree, so the kernel assigns k to slots to suit its LDS
+// A sum over k does not depend on which k each (h, element) slot carries as
+// long as A and B agree, so each path assigns k to slots to suit its LDS
 // layout.
+//
+// Each workgroup takes one of two paths (uniform branch):
+//   DmaPath  interior tiles of 16-byte aligned problems with K a multiple of
+//            the slab: global -> LDS by buffer_load ... lds, 4-stage ring;
+//   RegPath  everything else: range-checked loads through registers,
+//            out-of-range elements read as zero, 2 LDS stages.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 namespace mgemm {
 
@@ -46,8 +53,11 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 // Everything a GEMM launch needs; built on the host after validation.
 struct KernelArgs {
@@ -61,6 +71,7 @@ struct KernelArgs {
     int group_m;      // tile rows per raster group
     float alpha, beta;
     int c_vec;        // C pointer/ldc/strideC allow 16-byte accesses
+    int fast_ok;      // operand tiles addressable with 32-bit byte offsets
 };
 
 // ---------------------------------------------------------------------------
@@ -92,99 +103,103 @@ __device__ __forceinline__ void map_tile(const KernelArgs &p, int &b, int &tm, i
 
 template <int BYTES> struct RawOf;
 template <> struct RawOf<16> { using type = u32x4; };
+template <> struct RawOf<8> { using type = u32x2; };
 template <> struct RawOf<4> { using type = uint32_t; };
 template <> struct RawOf<2> { using type = uint16_t; };
 
-// K-contiguous LDS tile: ROWS rows of BK elements (one row = ROWB bytes =
-// NCH 16-byte chunks).  Chunk c of row r is stored at chunk c ^ ((r/IL) % NCH),
-// where IL is the operand's sub-tile interleave: lanes i' = 0..7 of a fragment
-// read rows IL*i' + t, which land in 8 distinct chunk columns.
-template <int ROWB, int IL>
-__device__ __forceinline__ int kc_off(int row, int kbyte)
+// Buffer resource over [base, base + 2 GiB): raw addressing, no swizzle.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base)
 {
-    constexpr int NCH = ROWB / 16;
-    const int chunk = (kbyte >> 4) ^ ((row / IL) & (NCH - 1));
-    return row * ROWB + (chunk << 4) + (kbyte & 15);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, 0x7fffffff,
+                                             0x00020000);
+}
+
+// 16-byte global -> LDS copy: lane l's 16 bytes from rsrc[voff + soff] land at
+// LDS byte lds_addr + 16*l.  Issued through inline asm so that the compiler's
+// memory-counter tracking does not see it: it would otherwise wait for every
+// outstanding copy before any LDS read it cannot prove disjoint (the
+// transposing reads among them), serialising the ring.  Callers order these
+// copies with explicit vmcnt waits.  M0 is written here; nothing else in the
+// copy loop keeps a value in M0 (it is reserved and set before each use).
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, uint32_t lds_addr, int voff, int soff)
+{
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "s"(lds_addr), "v"(voff), "s"(rs), "s"(soff) : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr_of(const char *p)
+{
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p;
+}
+
+// s_waitcnt with vmcnt = VM (<= 63), lgkmcnt = LGKM (<= 15), expcnt unrestricted.
+template <int VM, int LGKM>
+__device__ __forceinline__ void wait_counts()
+{
+    static_assert(VM >= 0 && VM <= 63 && LGKM >= 0 && LGKM <= 15, "waitcnt range");
+    __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (LGKM << 8));
+}
+
+// Workgroup barrier that orders LDS accesses in the compiler but leaves the
+// hardware counters to explicit waits (so loads further ahead stay in flight).
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Physical order of the rows of a K-contiguous LDS tile.  A wavefront's
+// 32*IL rows hold its IL interleaved MFMA sub-tiles (logical row IL*i' + t);
+// physical row 32*t + i' holds logical row IL*i' + t, so the lanes of one
+// fragment read touch consecutive physical rows.
+template <int IL>
+__device__ __forceinline__ int phys_row(int r)
+{
+    constexpr int WT = 32 * IL;
+    const int w = r / WT, rr = r % WT;
+    return w * WT + (rr % IL) * 32 + rr / IL;
+}
+
+template <int IL>
+__device__ __forceinline__ int logical_row(int p)
+{
+    constexpr int WT = 32 * IL;
+    const int w = p / WT, pp = p % WT;
+    return w * WT + (pp % 32) * IL + pp / 32;
+}
+
+// Two 16-bit halves -> one dword: lo16(a) | lo16(b) << 16 (hi = 0) or
+// hi16(a) | hi16(b) << 16 (hi = 1).
+__device__ __forceinline__ uint32_t pack_halves(uint32_t a, uint32_t b, int hi)
+{
+    return hi ? __builtin_amdgcn_perm(b, a, 0x07060302u) : __builtin_amdgcn_perm(b, a, 0x05040100u);
 }
 
 // ---------------------------------------------------------------------------
-// Global -> register loader for one operand tile of one K-slab.
-// The tile is R memory rows by CC contiguous elements; each of the NT threads
-// owns NPT vectors of VEC elements, consecutive threads owning consecutive
-// vectors of a row (coalesced).  Out-of-range elements are loaded as 0.
+// Instruction-group ordering hints for the scheduler (sched_group_barrier):
+// mask 0x008 = MFMA, 0x020 = VMEM read, 0x100 = DS read, 0x200 = DS write.
+// sched_interleave<X, NX, Y, NY>() asks for X, Y, X, Y, ... then the rest of
+// the longer group.
 // ---------------------------------------------------------------------------
-template <int ES, int R, int CC, int VEC, int NT>
-struct TileLoader {
-    static constexpr int VPR = CC / VEC;
-    static constexpr int NV = R * VPR;
-    static constexpr int NPT = NV / NT;
-    static_assert(NV % NT == 0, "tile not divisible among threads");
-    using Raw = typename RawOf<VEC * ES>::type;
-    Raw regs[NPT];
+constexpr int SG_MFMA = 0x008, SG_VMEM_READ = 0x020, SG_DS_READ = 0x100, SG_DS_WRITE = 0x200;
 
-    __device__ __forceinline__ static int row_of(int tid, int q) { return (tid + q * NT) / VPR; }
-    __device__ __forceinline__ static int col_of(int tid, int q) { return ((tid + q * NT) % VPR) * VEC; }
-
-    // base points at memory element (r0, c0); rows < rlim and cols < clim are in range
-    // (limits already relative to r0/c0).  `full` = the whole tile is in range.
-    __device__ __forceinline__ void load(const char *base, int64_t ld, int rlim, int clim,
-                                         bool full, int tid)
-    {
-        if (full) {
+template <int MX, int NX, int MY, int NY>
+__device__ __forceinline__ void sched_interleave()
+{
+    constexpr int P = NX < NY ? NX : NY;
 #pragma unroll
-            for (int q = 0; q < NPT; ++q) {
-                const int r = row_of(tid, q), c = col_of(tid, q);
-                regs[q] = *reinterpret_cast<const Raw *>(base + ((int64_t)r * ld + c) * ES);
-            }
-        } else {
-#pragma unroll
-            for (int q = 0; q < NPT; ++q) {
-                const int r = row_of(tid, q), c = col_of(tid, q);
-                const char *ptr = base + ((int64_t)r * ld + c) * ES;
-                if (r < rlim && c + VEC <= clim) {
-                    regs[q] = *reinterpret_cast<const Raw *>(ptr);
-                } else if constexpr (VEC == 1) {
-                    regs[q] = 0;
-                } else {
-                    regs[q] = masked_vec(ptr, r < rlim ? clim - c : 0);
-                }
-            }
-        }
+    for (int i = 0; i < P; ++i) {
+        __builtin_amdgcn_sched_group_barrier(MX, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(MY, 1, 0);
     }
-
-    // A vector of which only the first `n` elements are in range.
-    __device__ __forceinline__ static Raw masked_vec(const char *ptr, int n)
-    {
-        Raw v = {};
-        if constexpr (ES == 4) {
-#pragma unroll
-            for (int e = 0; e < VEC; ++e)
-                if (e < n) v[e] = reinterpret_cast<const uint32_t *>(ptr)[e];
-        } else {
-#pragma unroll
-            for (int e = 0; e < VEC; ++e)
-                if (e < n) {
-                    const uint32_t h = reinterpret_cast<const uint16_t *>(ptr)[e];
-                    v[e >> 1] |= h << (16 * (e & 1));
-                }
-        }
-        return v;
-    }
-
-    // 16-bit element e of register vector q.
-    __device__ __forceinline__ uint16_t half_of(int q, int e) const
-    {
-        if constexpr (VEC == 1) {
-            return (uint16_t)regs[q];
-        } else {
-            return (uint16_t)(regs[q][e >> 1] >> (16 * (e & 1)));
-        }
-    }
-};
+    if constexpr (NX > P) __builtin_amdgcn_sched_group_barrier(MX, NX - P, 0);
+    if constexpr (NY > P) __builtin_amdgcn_sched_group_barrier(MY, NY - P, 0);
+}
 
 // N adjacent floats from LDS with one access (N = 1, 2 or 4; ptr aligned to 4*N bytes).
 template <int N>
-__device__ __forceinline__ void lds_floats(const float *ptr, float (&out)[N])
+__device__ __forceinline__ void lds_floats(const char *ptr, float (&out)[N])
 {
     if constexpr (N == 4) {
         const f32x4 v = *reinterpret_cast<const f32x4 *>(ptr);
@@ -193,250 +208,677 @@ __device__ __forceinline__ void lds_floats(const float *ptr, float (&out)[N])
         const f32x2 v = *reinterpret_cast<const f32x2 *>(ptr);
         out[0] = v[0]; out[1] = v[1];
     } else {
-        out[0] = ptr[0];
+        out[0] = *reinterpret_cast<const float *>(ptr);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Operand fragments of one k-group and the MFMAs that consume them.
+// fp32: 4 k-slots per operand row (k = 8g + 4h + s); 16-bit: one 8-element
+// vector per row (k = 16g + 8h + 0..7).
+// ---------------------------------------------------------------------------
+template <typename T, int TM, int TN>
+struct Frags {
+    static constexpr bool F32 = sizeof(T) == 4;
+    float a32[F32 ? TM : 1][4], b32[F32 ? TN : 1][4];
+    u32x4 a16[F32 ? 1 : TM], b16[F32 ? 1 : TN];
+
+    __device__ __forceinline__ void mfmas(f32x16 (&acc)[TM][TN]) const
+    {
+        if constexpr (F32) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int t = 0; t < TM; ++t)
+#pragma unroll
+                    for (int u = 0; u < TN; ++u)
+                        acc[t][u] = __builtin_amdgcn_mfma_f32_32x32x2f32(a32[t][s], b32[u][s], acc[t][u], 0, 0, 0);
+        } else {
+#pragma unroll
+            for (int t = 0; t < TM; ++t)
+#pragma unroll
+                for (int u = 0; u < TN; ++u) {
+                    if constexpr (__is_same(T, _Float16))
+                        acc[t][u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                            __builtin_bit_cast(f16x8, a16[t]), __builtin_bit_cast(f16x8, b16[u]), acc[t][u], 0, 0, 0);
+                    else
+                        acc[t][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            __builtin_bit_cast(bf16x8, a16[t]), __builtin_bit_cast(bf16x8, b16[u]), acc[t][u], 0, 0, 0);
+                }
+        }
+    }
+};
+
+// ===========================================================================
+// RegPath: range-checked global loads through registers, 2 LDS stages.
+// K-contiguous LDS rows hold BK elements = 128 bytes, half of the 64-bank x
+// 4-byte LDS line; a 16-byte access is served 16 lanes at a time, so the 16
+// lanes of a fragment read, which touch 16 consecutive physical rows,
+// alternate between the two halves of a line, and chunk c of physical row p
+// sits at chunk c ^ ((p >> 1) & 7), spreading each half over 8 chunks.
+// ===========================================================================
+__device__ __forceinline__ int kc128_off(int p, int kbyte)
+{
+    const int chunk = (kbyte >> 4) ^ ((p >> 1) & 7);
+    return p * 128 + (chunk << 4) + (kbyte & 15);
+}
+
+// One operand (A or B) of one K-slab: global -> registers -> LDS.
+//   ES    element size (4: fp32, 2: f16/bf16)
+//   MN    tile extent along M (for A) or N (for B)
+//   KROW  memory rows run along k (A^T or B), i.e. MN is the contiguous dim
+//   IL    the operand's sub-tile interleave
+// Modes:
+//   vector   (!KROW, or fp32): memory vectors copied as is; LDS rows are
+//            K-contiguous (!KROW) or the fp32 [BK][MN] layout (KROW).
+//   block    (16-bit KROW, aligned): KB x 8 blocks transposed in registers
+//            so LDS rows stay K-contiguous (the MFMA wants 8 k per lane).
+//   scalar   (16-bit KROW, unaligned): element by element.
+template <int ES, int NT, int MN, int BK, int IL, bool KROW, bool VECOK>
+struct RegOperand {
+    static constexpr bool F32 = ES == 4;
+    static constexpr int ROWB = BK * ES;
+    static_assert(ROWB == 128, "K-contiguous rows are 128 bytes");
+    static constexpr bool BLOCK = KROW && !F32 && VECOK;
+    static constexpr int VEC = VECOK ? 16 / ES : 1;
+    static constexpr int R = KROW ? BK : MN;   // memory rows of the tile
+    static constexpr int CC = KROW ? MN : BK;  // contiguous elements per memory row
+    static constexpr int VPR = CC / VEC;
+    static constexpr int NPT = (R * CC / VEC) / NT;
+    static_assert(BLOCK || (R * CC / VEC) % NT == 0, "tile not divisible among threads");
+    static constexpr int KB = ((BK / 8) * (MN / 8) >= NT) ? 8 : ((BK / 4) * (MN / 8) >= NT) ? 4 : 2;
+    static constexpr int KGS = BK / KB;
+    static constexpr int NPB = BLOCK ? (KGS * (MN / 8)) / NT : 1;
+    static_assert(!BLOCK || (KGS * (MN / 8)) % NT == 0, "blocks not divisible among threads");
+    static constexpr int NREG = BLOCK ? NPB * KB : NPT;
+    using Raw = typename RawOf<VEC * ES>::type;
+    Raw regs[NREG];
+
+    // vector mode: slot (tid, q) fills tile row vrow (the physical LDS row for
+    // K-contiguous layouts) at column vcol, from memory row mem_row(vrow).
+    __device__ __forceinline__ static int vrow(int tid, int q) { return (tid + q * NT) / VPR; }
+    __device__ __forceinline__ static int vcol(int tid, int q) { return ((tid + q * NT) % VPR) * VEC; }
+    __device__ __forceinline__ static int mem_row(int v) { return KROW ? v : logical_row<IL>(v); }
+    __device__ __forceinline__ static int bkg(int tid) { return tid % KGS; }
+    __device__ __forceinline__ static int bng(int tid, int q) { return tid / KGS + q * (NT / KGS); }
+
+    // rows < rlim and columns < clim (memory order, relative to the tile
+    // origin `base`) are in range; everything else reads as zero.
+    __device__ __forceinline__ void load(const char *base, int64_t ld, int rlim, int clim, int tid)
+    {
+        if constexpr (BLOCK) {
+#pragma unroll
+            for (int q = 0; q < NPB; ++q)
+#pragma unroll
+                for (int r = 0; r < KB; ++r) {
+                    const int row = bkg(tid) * KB + r, col = bng(tid, q) * 8;
+                    regs[q * KB + r] = masked_vec(base + ((int64_t)row * ld + col) * ES,
+                                                  row < rlim ? clim - col : 0);
+                }
+        } else {
+#pragma unroll
+            for (int q = 0; q < NPT; ++q) {
+                const int r = mem_row(vrow(tid, q)), c = vcol(tid, q);
+                const char *ptr = base + ((int64_t)r * ld + c) * ES;
+                if constexpr (VEC == 1) {
+                    if (r < rlim && c < clim)
+                        regs[q] = *reinterpret_cast<const Raw *>(ptr);
+                    else
+                        regs[q] = 0;
+                } else {
+                    regs[q] = masked_vec(ptr, r < rlim ? clim - c : 0);
+                }
+            }
+        }
+    }
+
+    // A 16-byte vector of which only the first `n` elements are in range.
+    __device__ __forceinline__ static u32x4 masked_vec(const char *ptr, int n)
+    {
+        constexpr int V = 16 / ES;
+        if (n >= V) return *reinterpret_cast<const u32x4 *>(ptr);
+        u32x4 v = {0, 0, 0, 0};
+        if constexpr (ES == 4) {
+#pragma unroll
+            for (int e = 0; e < V; ++e)
+                if (e < n) v[e] = reinterpret_cast<const uint32_t *>(ptr)[e];
+        } else {
+#pragma unroll
+            for (int e = 0; e < V; ++e)
+                if (e < n) v[e >> 1] |= (uint32_t)reinterpret_cast<const uint16_t *>(ptr)[e] << (16 * (e & 1));
+        }
+        return v;
+    }
+
+    // registers -> LDS tile at `s`
+    __device__ __forceinline__ void store(char *s, int tid) const
+    {
+        if constexpr (BLOCK) {
+#pragma unroll
+            for (int q = 0; q < NPB; ++q) {
+                const int kbyte = bkg(tid) * KB * 2, row0 = bng(tid, q) * 8;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    // column e of the block: KB k-values, two per dword
+                    const int d = e >> 1, hi = e & 1;
+                    char *dst = s + kc128_off(phys_row<IL>(row0 + e), kbyte);
+                    if constexpr (KB == 8) {
+                        u32x4 o;
+#pragma unroll
+                        for (int p = 0; p < 4; ++p)
+                            o[p] = pack_halves(regs[q * 8 + 2 * p][d], regs[q * 8 + 2 * p + 1][d], hi);
+                        *reinterpret_cast<u32x4 *>(dst) = o;
+                    } else if constexpr (KB == 4) {
+                        u32x2 o;
+#pragma unroll
+                        for (int p = 0; p < 2; ++p)
+                            o[p] = pack_halves(regs[q * 4 + 2 * p][d], regs[q * 4 + 2 * p + 1][d], hi);
+                        *reinterpret_cast<u32x2 *>(dst) = o;
+                    } else {
+                        *reinterpret_cast<uint32_t *>(dst) = pack_halves(regs[q * 2][d], regs[q * 2 + 1][d], hi);
+                    }
+                }
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < NPT; ++q) {
+                const int r = vrow(tid, q), c = vcol(tid, q);
+                if constexpr (!KROW) {          // memory row = mn, contiguous = k; r is physical
+                    *reinterpret_cast<Raw *>(s + kc128_off(r, c * ES)) = regs[q];
+                } else if constexpr (F32) {     // memory row = k, contiguous = mn -> [BK][MN]
+                    *reinterpret_cast<Raw *>(s + (r * MN + c) * 4) = regs[q];
+                } else {                        // 16-bit, unaligned: one element
+                    *reinterpret_cast<uint16_t *>(s + kc128_off(phys_row<IL>(c), r * 2)) = regs[q];
+                }
+            }
+        }
+    }
+};
+
+template <typename T, int BM, int BN, int BK, int WM, int WN, bool TA, bool TB, bool VECOK>
+struct RegPath {
+    static constexpr int NT = WM * WN * 64;
+    static constexpr int ES = sizeof(T);
+    static constexpr bool F32 = (ES == 4);
+    static constexpr int WTM = BM / WM, WTN = BN / WN;
+    static constexpr int TM = WTM / 32, TN = WTN / 32;
+    static_assert(TM >= 1 && TN >= 1 && TM * 32 * WM == BM && TN * 32 * WN == BN, "tile");
+    static_assert(TN == 1 || TN == 2 || TN == 4, "TN");
+    static constexpr bool A_KC = !TA || !F32;  // LDS layout of A is K-contiguous
+    static constexpr bool B_KC = TB || !F32;
+    static constexpr int A_BYTES = BM * BK * ES, B_BYTES = BN * BK * ES;
+    static constexpr int STAGE = A_BYTES + B_BYTES;
+    static constexpr int LDS_BYTES = 2 * STAGE;
+    static constexpr int G = F32 ? BK / 8 : BK / 16;
+    static constexpr int IL_A = TM, IL_B = TN;  // C mapping: interleaved rows and columns
+
+    using OpA = RegOperand<ES, NT, BM, BK, TM, TA, VECOK>;
+    using OpB = RegOperand<ES, NT, BN, BK, TN, !TB, VECOK>;
+    using Fr = Frags<T, TM, TN>;
+
+    // a_row0/b_row0: first interleaved row of this lane in the fp32 [BK][MN]
+    // layout; a_prow0/b_prow0: its physical row in the K-contiguous layout.
+    __device__ __forceinline__ static void load_frags(const char *sa, const char *sb, int g, int a_row0,
+                                                      int b_row0, int a_prow0, int b_prow0, int lh, Fr &f)
+    {
+        if constexpr (F32) {
+            if constexpr (A_KC) {
+#pragma unroll
+                for (int t = 0; t < TM; ++t) {
+                    const f32x4 v = *reinterpret_cast<const f32x4 *>(sa + kc128_off(a_prow0 + 32 * t, (8 * g + 4 * lh) * 4));
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) f.a32[t][s] = v[s];
+                }
+            } else {
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    float v[TM];
+                    lds_floats<TM>(sa + ((8 * g + 4 * lh + s) * BM + a_row0) * 4, v);
+#pragma unroll
+                    for (int t = 0; t < TM; ++t) f.a32[t][s] = v[t];
+                }
+            }
+            if constexpr (B_KC) {
+#pragma unroll
+                for (int u = 0; u < TN; ++u) {
+                    const f32x4 v = *reinterpret_cast<const f32x4 *>(sb + kc128_off(b_prow0 + 32 * u, (8 * g + 4 * lh) * 4));
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) f.b32[u][s] = v[s];
+                }
+            } else {
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    float v[TN];
+                    lds_floats<TN>(sb + ((8 * g + 4 * lh + s) * BN + b_row0) * 4, v);
+#pragma unroll
+                    for (int u = 0; u < TN; ++u) f.b32[u][s] = v[u];
+                }
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < TM; ++t)
+                f.a16[t] = *reinterpret_cast<const u32x4 *>(sa + kc128_off(a_prow0 + 32 * t, (16 * g + 8 * lh) * 2));
+#pragma unroll
+            for (int u = 0; u < TN; ++u)
+                f.b16[u] = *reinterpret_cast<const u32x4 *>(sb + kc128_off(b_prow0 + 32 * u, (16 * g + 8 * lh) * 2));
+        }
+    }
+
+    __device__ __forceinline__ static void run(const KernelArgs &p, char *smem, int bidx, int m0, int n0,
+                               f32x16 (&acc)[TM][TN])
+    {
+        const int tid = threadIdx.x;
+        const int lane = tid & 63, wave = tid >> 6;
+        const int wm = wave / WN, wn = wave % WN;
+        const int li = lane & 31, lh = lane >> 5;
+        const char *Ap = static_cast<const char *>(p.A) + (int64_t)bidx * p.strideA * ES +
+                         (TA ? (int64_t)m0 : (int64_t)m0 * p.lda) * ES;
+        const char *Bp = static_cast<const char *>(p.B) + (int64_t)bidx * p.strideB * ES +
+                         (TB ? (int64_t)n0 * p.ldb : (int64_t)n0) * ES;
+        const int64_t a_kstep = (TA ? (int64_t)BK * p.lda : (int64_t)BK) * ES;
+        const int64_t b_kstep = (TB ? (int64_t)BK : (int64_t)BK * p.ldb) * ES;
+        const int mrem = p.M - m0, nrem = p.N - n0;
+        const int a_row0 = wm * WTM + TM * li, b_row0 = wn * WTN + TN * li;
+        const int a_prow0 = wm * WTM + li, b_prow0 = wn * WTN + li;
+
+        OpA la;
+        OpB lb;
+        auto load_slab = [&](int kt) {
+            const int krem = p.K - kt * BK;
+            const char *a = Ap + (int64_t)kt * a_kstep;
+            const char *b = Bp + (int64_t)kt * b_kstep;
+            if constexpr (TA) la.load(a, p.lda, krem, mrem, tid);
+            else              la.load(a, p.lda, mrem, krem, tid);
+            if constexpr (TB) lb.load(b, p.ldb, nrem, krem, tid);
+            else              lb.load(b, p.ldb, krem, nrem, tid);
+        };
+        auto compute = [&](int stage) {
+            const char *sa = smem + stage * STAGE;
+            const char *sb = sa + A_BYTES;
+            Fr f[2];
+            load_frags(sa, sb, 0, a_row0, b_row0, a_prow0, b_prow0, lh, f[0]);
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                if (g + 1 < G) load_frags(sa, sb, g + 1, a_row0, b_row0, a_prow0, b_prow0, lh, f[(g + 1) & 1]);
+                f[g & 1].mfmas(acc);
+            }
+        };
+        // two LDS stages, the next slab fetched to registers during the current one
+        const int nk = (p.K + BK - 1) / BK;
+        load_slab(0);
+        la.store(smem, tid);
+        lb.store(smem + A_BYTES, tid);
+        __syncthreads();
+        for (int kt = 0; kt + 1 < nk; ++kt) {
+            load_slab(kt + 1);
+            compute(kt & 1);
+            char *st = smem + ((kt + 1) & 1) * STAGE;
+            la.store(st, tid);
+            lb.store(st + A_BYTES, tid);
+            __syncthreads();
+        }
+        compute((nk - 1) & 1);
+    }
+};
+
+// ===========================================================================
+// DmaPath: interior tiles.  Global -> LDS with buffer_load_dwordx4 ... lds
+// (no registers in between), a ring of 4 LDS stages of BK = BKR/2 elements
+// (32 for 16-bit, 16 for fp32), loads issued 3 slabs ahead.  One barrier per
+// slab, placed before the MFMAs of the slab's second k-group so that the
+// next slab's first fragment reads overlap them.
+//
+// LDS layouts (bank-conflict free for every access of this path):
+//   KC  operand K-contiguous in memory: rows of BK elements = 64 bytes, a
+//       quarter of a bank line; physical row order as phys_row; chunk c of
+//       physical row p at c ^ ((p >> 2) & 3).  A fragment read touches 16
+//       consecutive physical rows per 16 lanes: 4 rows per line position x
+//       4 distinct chunks.
+//   MC  operand MN-contiguous in memory: BK rows of MN elements, stored as
+//       in memory but with its 64-byte pieces permuted per row
+//       (piece ^ key(k)), so the 4 rows read together land in 4 distinct
+//       64-byte groups of banks.  16-bit MC operands are read with
+//       ds_read_b64_tr_b16: within a 16-lane group, source lane j supplies
+//       4 values at row k0 + j/4, columns n0 + 4*(j%4) .. +3, and lane i
+//       receives column n0 + i of rows k0 .. k0+3.  The MFMA lanes of a
+//       16-bit MC operand therefore index consecutive (not interleaved)
+//       rows/columns (interleave 1).
+// ===========================================================================
+template <typename T, int BM, int BN, int BKR, int WM, int WN, bool TA, bool TB>
+struct DmaPath {
+    static constexpr int NT = WM * WN * 64;
+    static constexpr int NW = WM * WN;
+    static constexpr int ES = sizeof(T);
+    static constexpr bool F32 = (ES == 4);
+    static constexpr int WTM = BM / WM, WTN = BN / WN;
+    static constexpr int TM = WTM / 32, TN = WTN / 32;
+    static constexpr int BK = BKR / 2;
+    static constexpr int NS = 4;
+    static_assert(BK * ES == 64, "64-byte K-contiguous rows");
+    static constexpr bool A_KC = !TA, B_KC = TB;
+    static constexpr bool A_TR = TA && !F32, B_TR = !TB && !F32;
+    static constexpr int IL_A = A_TR ? 1 : TM, IL_B = B_TR ? 1 : TN;
+    static constexpr int A_BYTES = BM * BK * ES, B_BYTES = BN * BK * ES;
+    static constexpr int STAGE = A_BYTES + B_BYTES;
+    static constexpr int LDS_BYTES = NS * STAGE;
+    static constexpr int A_ROWB = BM * ES, B_ROWB = BN * ES;  // MC row bytes
+    static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "DMA split");
+    static constexpr int A_IPW = A_BYTES / 1024 / NW, B_IPW = B_BYTES / 1024 / NW;
+    static constexpr int LPS = A_IPW + B_IPW;  // DMA loads per slab per thread
+    static_assert(3 * LPS <= 63, "vmcnt range");
+    static_assert(A_KC || A_ROWB >= 128, "MC rows of at least 128 bytes");
+    static_assert(B_KC || B_ROWB >= 128, "MC rows of at least 128 bytes");
+
+    using Fr = Frags<T, TM, TN>;
+
+    __device__ __forceinline__ static int kc_off(int p, int kbyte)
+    {
+        const int chunk = (kbyte >> 4) ^ ((p >> 2) & 3);
+        return p * 64 + (chunk << 4) + (kbyte & 15);
+    }
+
+    template <int ROWB>
+    __device__ __forceinline__ static int mc_key(int k)
+    {
+        return ROWB >= 256 ? (k & 3) : ((k >> 1) & 1);
+    }
+
+    template <int ROWB>
+    __device__ __forceinline__ static int mc_off(int k, int byte)
+    {
+        return k * ROWB + (((byte >> 6) ^ mc_key<ROWB>(k)) << 6) + (byte & 63);
+    }
+
+    // DMA of one operand's slab: wave `w` issues IPW 1 KB loads into the
+    // operand's region `dst` of a stage, from tile origin `src`.
+    template <bool KC, int IL, int ROWB, int IPW>
+    __device__ __forceinline__ static void dma_operand(const char *src, char *dst, int ld_bytes, int w,
+                                                       int lane)
+    {
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(src);
+#pragma unroll
+        for (int q = 0; q < IPW; ++q) {
+            const int ins = w * IPW + q;
+            if constexpr (KC) {
+                // 16 physical rows pb .. pb+15 (64 bytes each); lane -> row pb + lane/4,
+                // physical chunk lane%4, logical chunk (lane%4) ^ ((lane/16) & 3); the
+                // logical rows are logical_row(pb) + (lane/4)*IL.
+                const int pb = ins * 16;
+                const int voff = (lane >> 2) * IL * ld_bytes + (((lane & 3) ^ ((lane >> 4) & 3)) << 4);
+                const int soff = __builtin_amdgcn_readfirstlane(logical_row<IL>(pb) * ld_bytes);
+                dma16(rs, lds_addr_of(dst + pb * 64), voff, soff);
+            } else {
+                // bytes b = ins*1024 + 16*lane of the [BK][MN] region: row k = b / ROWB,
+                // physical piece (b % ROWB) / 64 holds logical piece ^ key(k)
+                const int b = ins * 1024 + 16 * lane;
+                const int k = b / ROWB, bb = b % ROWB;
+                const int lb = (((bb >> 6) ^ mc_key<ROWB>(k)) << 6) | (bb & 63);
+                dma16(rs, lds_addr_of(dst + ins * 1024), k * ld_bytes + lb, 0);
+            }
+        }
+    }
+
+    // Fragment of one MC 16-bit operand (rows k, columns mn): the 8 k-values
+    // 16g + 8h + 0..7 of column (wave-local) base + 16*((lane/16)&1) + lane%16,
+    // via two transposing reads.
+    template <int ROWB>
+    __device__ __forceinline__ static u32x4 tr_frag(const char *s, int g, int lh, int col_base, int lane)
+    {
+        const int gi = lane & 15;
+        const int col = col_base + 16 * ((lane >> 4) & 1) + 4 * (gi & 3);
+        const int k0 = 16 * g + 8 * lh + (gi >> 2);
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(s + mc_off<ROWB>(k0, col * 2)));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(s + mc_off<ROWB>(k0 + 4, col * 2)));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        return u32x4{l2[0], l2[1], h2[0], h2[1]};
+    }
+
+    struct Lane {
+        int lane, li, lh;
+        int a_row0, b_row0;    // fp32 MC: first interleaved row/column of this lane
+        int a_prow0, b_prow0;  // KC: physical row of sub-tile 0
+        int a_blk, b_blk;      // 16-bit MC: wave-local base of sub-tile 0
+    };
+
+    __device__ __forceinline__ static void load_frags(const char *sa, const char *sb, int g, const Lane &L, Fr &f)
+    {
+        if constexpr (F32) {
+            if constexpr (A_KC) {
+#pragma unroll
+                for (int t = 0; t < TM; ++t) {
+                    const f32x4 v = *reinterpret_cast<const f32x4 *>(sa + kc_off(L.a_prow0 + 32 * t, (8 * g + 4 * L.lh) * 4));
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) f.a32[t][s] = v[s];
+                }
+            } else {
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    float v[TM];
+                    lds_floats<TM>(sa + mc_off<A_ROWB>(8 * g + 4 * L.lh + s, L.a_row0 * 4), v);
+#pragma unroll
+                    for (int t = 0; t < TM; ++t) f.a32[t][s] = v[t];
+                }
+            }
+            if constexpr (B_KC) {
+#pragma unroll
+                for (int u = 0; u < TN; ++u) {
+                    const f32x4 v = *reinterpret_cast<const f32x4 *>(sb + kc_off(L.b_prow0 + 32 * u, (8 * g + 4 * L.lh) * 4));
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) f.b32[u][s] = v[s];
+                }
+            } else {
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    float v[TN];
+                    lds_floats<TN>(sb + mc_off<B_ROWB>(8 * g + 4 * L.lh + s, L.b_row0 * 4), v);
+#pragma unroll
+                    for (int u = 0; u < TN; ++u) f.b32[u][s] = v[u];
+                }
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < TM; ++t) {
+                if constexpr (A_KC)
+                    f.a16[t] = *reinterpret_cast<const u32x4 *>(sa + kc_off(L.a_prow0 + 32 * t, (16 * g + 8 * L.lh) * 2));
+                else
+                    f.a16[t] = tr_frag<A_ROWB>(sa, g, L.lh, L.a_blk + 32 * t, L.lane);
+            }
+#pragma unroll
+            for (int u = 0; u < TN; ++u) {
+                if constexpr (B_KC)
+                    f.b16[u] = *reinterpret_cast<const u32x4 *>(sb + kc_off(L.b_prow0 + 32 * u, (16 * g + 8 * L.lh) * 2));
+                else
+                    f.b16[u] = tr_frag<B_ROWB>(sb, g, L.lh, L.b_blk + 32 * u, L.lane);
+            }
+        }
+    }
+
+    // per-group instruction counts (for the schedule hints)
+    static constexpr int DSR_A = F32 ? (A_KC ? TM : 4) : (A_KC ? TM : 2 * TM);
+    static constexpr int DSR_B = F32 ? (B_KC ? TN : 4) : (B_KC ? TN : 2 * TN);
+    static constexpr int DSR = DSR_A + DSR_B;
+    static constexpr int MF = F32 ? 4 * TM * TN : TM * TN;
+
+    __device__ __forceinline__ static void run(const KernelArgs &p, char *smem, int bidx, int m0, int n0,
+                               f32x16 (&acc)[TM][TN])
+    {
+        const int tid = threadIdx.x;
+        const int lane = tid & 63;
+        const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int wm = w / WN, wn = w % WN;
+        Lane L;
+        L.lane = lane;
+        L.li = lane & 31;
+        L.lh = lane >> 5;
+        L.a_row0 = wm * WTM + TM * L.li;
+        L.b_row0 = wn * WTN + TN * L.li;
+        L.a_prow0 = wm * WTM + L.li;
+        L.b_prow0 = wn * WTN + L.li;
+        L.a_blk = wm * WTM;
+        L.b_blk = wn * WTN;
+
+        const char *Ap = static_cast<const char *>(p.A) + (int64_t)bidx * p.strideA * ES +
+                         (TA ? (int64_t)m0 : (int64_t)m0 * p.lda) * ES;
+        const char *Bp = static_cast<const char *>(p.B) + (int64_t)bidx * p.strideB * ES +
+                         (TB ? (int64_t)n0 * p.ldb : (int64_t)n0) * ES;
+        const int64_t a_kstep = (TA ? (int64_t)BK * p.lda : (int64_t)BK) * ES;
+        const int64_t b_kstep = (TB ? (int64_t)BK : (int64_t)BK * p.ldb) * ES;
+        const int lda_b = (int)(p.lda * ES), ldb_b = (int)(p.ldb * ES);
+
+        auto stage = [&](int s) { return smem + (s & (NS - 1)) * STAGE; };
+        auto issue = [&](int s) {
+            char *st = stage(s);
+            dma_operand<A_KC, IL_A, A_ROWB, A_IPW>(Ap + (int64_t)s * a_kstep, st, lda_b, w, lane);
+            dma_operand<B_KC, IL_B, B_ROWB, B_IPW>(Bp + (int64_t)s * b_kstep, st + A_BYTES, ldb_b, w, lane);
+        };
+        auto frags = [&](int s, int g, Fr &f) {
+            const char *st = stage(s);
+            load_frags(st, st + A_BYTES, g, L, f);
+        };
+
+        const int nk = p.K / BK;
+        // prologue: slabs 0..3 in flight, wait for slab 0
+        issue(0);
+        if (nk > 1) issue(1);
+        if (nk > 2) issue(2);
+        if (nk > 3) issue(3);
+        if (nk > 3)      wait_counts<3 * LPS, 0>();
+        else if (nk > 2) wait_counts<2 * LPS, 0>();
+        else if (nk > 1) wait_counts<LPS, 0>();
+        else             wait_counts<0, 0>();
+        lds_barrier();
+
+        Fr f0, f1;
+        frags(0, 0, f0);
+        int kt = 0;
+        // steady state: slab kt+4 exists; at the wait, slabs kt+2 and kt+3 may
+        // still be in flight
+        for (; kt + 4 < nk; ++kt) {
+            frags(kt, 1, f1);
+            f0.mfmas(acc);
+            sched_interleave<SG_MFMA, MF, SG_DS_READ, DSR>();
+            wait_counts<2 * LPS, 0>();
+            lds_barrier();
+            issue(kt + 4);
+            frags(kt + 1, 0, f0);
+            f1.mfmas(acc);
+            sched_interleave<SG_MFMA, MF, SG_DS_READ, DSR>();
+        }
+        // last slabs: everything already issued
+        for (; kt < nk; ++kt) {
+            frags(kt, 1, f1);
+            f0.mfmas(acc);
+            if (kt + 1 < nk) {
+                const int ahead = nk - kt - 2;  // slabs after kt+1 still possibly in flight
+                if (ahead >= 2)      wait_counts<2 * LPS, 0>();
+                else if (ahead == 1) wait_counts<LPS, 0>();
+                else                 wait_counts<0, 0>();
+                lds_barrier();
+                frags(kt + 1, 0, f0);
+            }
+            f1.mfmas(acc);
+        }
+    }
+};
+
+// ---------------------------------------------------------------------------
+// Epilogue: C = alpha*acc + beta*C (C read only when beta != 0).  IL_A / IL_B
+// give the sub-tile interleave of rows / columns: row of (t, i') is
+// IL_A == 1 ? 32t + i' : TM*i' + t, likewise for columns; with interleaved
+// columns each lane holds TN adjacent columns and stores them as one vector.
+// ---------------------------------------------------------------------------
+template <bool EDGE, int IL_A, int IL_B, int TM, int TN, int WTM, int WTN, int WN>
+__device__ __forceinline__ void epilogue(const KernelArgs &p, int bidx, int m0, int n0,
+                                         const f32x16 (&acc)[TM][TN])
+{
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    const int li = lane & 31, lh = lane >> 5;
+    float *Cb = p.C + (int64_t)bidx * p.strideC;
+    const bool use_beta = p.beta != 0.0f;
+    constexpr bool VCOL = IL_B > 1;  // TN adjacent columns per lane
+    const int colv = n0 + wn * WTN + TN * li;
+    const bool vec_store = VCOL && p.c_vec && (!EDGE || colv + TN <= p.N);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int ip = 8 * (r >> 2) + 4 * lh + (r & 3);
+#pragma unroll
+        for (int t = 0; t < TM; ++t) {
+            const int row = m0 + wm * WTM + (IL_A == 1 ? 32 * t + ip : TM * ip + t);
+            if (EDGE && row >= p.M) continue;
+            float *crow = Cb + (int64_t)row * p.ldc;
+            if constexpr (VCOL) {
+                float v[TN];
+#pragma unroll
+                for (int u = 0; u < TN; ++u) v[u] = p.alpha * acc[t][u][r];
+                float *cp = crow + colv;
+                if (vec_store) {
+                    if constexpr (TN == 4) {
+                        f32x4 o = {v[0], v[1], v[2], v[3]};
+                        if (use_beta) o += p.beta * *reinterpret_cast<const f32x4 *>(cp);
+                        *reinterpret_cast<f32x4 *>(cp) = o;
+                    } else if constexpr (TN == 2) {
+                        f32x2 o = {v[0], v[1]};
+                        if (use_beta) o += p.beta * *reinterpret_cast<const f32x2 *>(cp);
+                        *reinterpret_cast<f32x2 *>(cp) = o;
+                    }
+                } else {
+#pragma unroll
+                    for (int u = 0; u < TN; ++u)
+                        if (!EDGE || colv + u < p.N) cp[u] = use_beta ? v[u] + p.beta * cp[u] : v[u];
+                }
+            } else {
+#pragma unroll
+                for (int u = 0; u < TN; ++u) {
+                    const int col = n0 + wn * WTN + 32 * u + li;
+                    if (EDGE && col >= p.N) continue;
+                    const float v = p.alpha * acc[t][u][r];
+                    crow[col] = use_beta ? v + p.beta * crow[col] : v;
+                }
+            }
+        }
     }
 }
 
 // ---------------------------------------------------------------------------
 // The kernel.
 //   T          float, _Float16 or __bf16 (A and B element type)
-//   BM, BN, BK workgroup tile and K-slab
+//   BM, BN     workgroup tile
+//   BK         K-slab of the register path (the DMA path uses BK/2)
 //   WM, WN     wavefront grid; each wave owns a (BM/WM) x (BN/WN) sub-tile
-//              made of TM x TN MFMA blocks of 32x32, interleaved: block (t,u)
-//              covers wave rows TM*i'+t and wave columns TN*j'+u, so each lane
-//              ends with TN adjacent columns (one vector store).
+//              made of TM x TN MFMA blocks of 32x32
 //   TA, TB     op(A) = A^T, op(B) = B^T
-//   VECOK      A and B allow 16-byte global accesses
+//   VECOK      A and B allow 16-byte global accesses (enables DmaPath)
 // ---------------------------------------------------------------------------
 template <typename T, int BM, int BN, int BK, int WM, int WN, bool TA, bool TB, bool VECOK>
 __global__ void __launch_bounds__(WM * WN * 64)
 gemm_kernel(KernelArgs p)
 {
-    constexpr int NT = WM * WN * 64;
-    constexpr int ES = sizeof(T);
-    constexpr bool F32 = (ES == 4);
-    constexpr int WTM = BM / WM, WTN = BN / WN;
-    constexpr int TM = WTM / 32, TN = WTN / 32;
-    static_assert(TM >= 1 && TN >= 1 && TM * 32 * WM == BM && TN * 32 * WN == BN, "tile");
-    static_assert(TN == 1 || TN == 2 || TN == 4, "TN");
-    constexpr int VEC = VECOK ? 16 / ES : 1;
-    constexpr int ROWB = BK * ES;  // bytes per K-contiguous LDS row
-    static_assert(ROWB == 128, "LDS rows are 128 bytes (8 chunks)");
-    // LDS layouts: fp32 keeps the operand's global orientation; 16-bit
-    // operands are always stored K-contiguous (the MFMA reads 8 k per lane).
-    constexpr bool A_KC = !TA || !F32;
-    constexpr bool B_KC = TB || !F32;
-    constexpr int A_BYTES = BM * BK * ES, B_BYTES = BN * BK * ES;
-    constexpr int STAGE = A_BYTES + B_BYTES;
-    __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
-
-    // memory-order tile shapes: rows x contiguous elements
-    constexpr int A_R = TA ? BK : BM, A_C = TA ? BM : BK;
-    constexpr int B_R = TB ? BN : BK, B_C = TB ? BK : BN;
-    TileLoader<ES, A_R, A_C, VEC, NT> la;
-    TileLoader<ES, B_R, B_C, VEC, NT> lb;
-
+    using R = RegPath<T, BM, BN, BK, WM, WN, TA, TB, VECOK>;
+    using D = DmaPath<T, BM, BN, BK, WM, WN, TA, TB>;
+    constexpr int TM = R::TM, TN = R::TN, WTM = R::WTM, WTN = R::WTN;
+    constexpr int LDS = (VECOK && D::LDS_BYTES > R::LDS_BYTES) ? D::LDS_BYTES : R::LDS_BYTES;
+    __shared__ __attribute__((aligned(1024))) char smem[LDS];
     int bidx, tm, tn;
     map_tile(p, bidx, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave / WN, wn = wave % WN;
-    const int li = lane & 31, lh = lane >> 5;
-
-    const char *Ab = static_cast<const char *>(p.A) + (int64_t)bidx * p.strideA * ES;
-    const char *Bb = static_cast<const char *>(p.B) + (int64_t)bidx * p.strideB * ES;
-    // tile origin in memory coordinates
-    const char *Ap = Ab + (TA ? (int64_t)m0 : (int64_t)m0 * p.lda) * ES;
-    const char *Bp = Bb + (TB ? (int64_t)n0 * p.ldb : (int64_t)n0) * ES;
-    const int64_t a_kstep = (TA ? (int64_t)BK * p.lda : (int64_t)BK) * ES;
-    const int64_t b_kstep = (TB ? (int64_t)BK : (int64_t)BK * p.ldb) * ES;
-    const bool a_in = m0 + BM <= p.M, b_in = n0 + BN <= p.N;
-    const int mrem = p.M - m0, nrem = p.N - n0;
-
-    auto load_slab = [&](int k0) {
-        const int krem = p.K - k0;
-        const bool kfull = krem >= BK;
-        if constexpr (TA) la.load(Ap, p.lda, krem, mrem, a_in && kfull, tid);
-        else              la.load(Ap, p.lda, mrem, krem, a_in && kfull, tid);
-        if constexpr (TB) lb.load(Bp, p.ldb, nrem, krem, b_in && kfull, tid);
-        else              lb.load(Bp, p.ldb, krem, nrem, b_in && kfull, tid);
-    };
-
-    // registers -> LDS stage
-    auto store_slab = [&](int stage) {
-        char *sa = smem + stage * STAGE;
-        char *sb = sa + A_BYTES;
-#pragma unroll
-        for (int q = 0; q < decltype(la)::NPT; ++q) {
-            const int r = decltype(la)::row_of(tid, q), c = decltype(la)::col_of(tid, q);
-            if constexpr (!TA) {  // memory row = m, contiguous = k -> K-contiguous rows
-                if constexpr (VEC > 1)
-                    *reinterpret_cast<u32x4 *>(sa + kc_off<ROWB, TM>(r, c * ES)) = la.regs[q];
-                else
-                    *reinterpret_cast<typename decltype(la)::Raw *>(sa + kc_off<ROWB, TM>(r, c * ES)) = la.regs[q];
-            } else if constexpr (F32) {  // memory row = k, contiguous = m -> [BK][BM]
-                *reinterpret_cast<typename decltype(la)::Raw *>(sa + (r * BM + c) * 4) = la.regs[q];
-            } else {  // 16-bit, memory row = k: transpose into K-contiguous rows
-#pragma unroll
-                for (int e = 0; e < VEC; ++e)
-                    *reinterpret_cast<uint16_t *>(sa + kc_off<ROWB, TM>(c + e, r * 2)) = la.half_of(q, e);
-            }
-        }
-#pragma unroll
-        for (int q = 0; q < decltype(lb)::NPT; ++q) {
-            const int r = decltype(lb)::row_of(tid, q), c = decltype(lb)::col_of(tid, q);
-            if constexpr (TB) {  // memory row = n, contiguous = k
-                if constexpr (VEC > 1)
-                    *reinterpret_cast<u32x4 *>(sb + kc_off<ROWB, TN>(r, c * ES)) = lb.regs[q];
-                else
-                    *reinterpret_cast<typename decltype(lb)::Raw *>(sb + kc_off<ROWB, TN>(r, c * ES)) = lb.regs[q];
-            } else if constexpr (F32) {  // memory row = k, contiguous = n -> [BK][BN]
-                *reinterpret_cast<typename decltype(lb)::Raw *>(sb + (r * BN + c) * 4) = lb.regs[q];
-            } else {
-#pragma unroll
-                for (int e = 0; e < VEC; ++e)
-                    *reinterpret_cast<uint16_t *>(sb + kc_off<ROWB, TN>(c + e, r * 2)) = lb.half_of(q, e);
-            }
-        }
-    };
-
     f32x16 acc[TM][TN];
 #pragma unroll
     for (int t = 0; t < TM; ++t)
 #pragma unroll
         for (int u = 0; u < TN; ++u)
             acc[t][u] = f32x16{};
-
-    const int a_row0 = wm * WTM + TM * li;  // LDS row of sub-tile t is a_row0 + t
-    const int b_row0 = wn * WTN + TN * li;
-
-    auto compute_slab = [&](int stage) {
-        const char *sa = smem + stage * STAGE;
-        const char *sb = sa + A_BYTES;
-        if constexpr (F32) {
-            // 8 k per group: slot (h, s) carries k = 8*g + 4*h + s, s = 0..3
-#pragma unroll
-            for (int g = 0; g < BK / 8; ++g) {
-                float av[TM][4], bv[TN][4];
-                if constexpr (A_KC) {
-#pragma unroll
-                    for (int t = 0; t < TM; ++t) {
-                        const f32x4 v = *reinterpret_cast<const f32x4 *>(
-                            sa + kc_off<ROWB, TM>(a_row0 + t, (8 * g + 4 * lh) * 4));
-#pragma unroll
-                        for (int s = 0; s < 4; ++s) av[t][s] = v[s];
-                    }
-                } else {
-#pragma unroll
-                    for (int s = 0; s < 4; ++s) {
-                        float v[TM];
-                        lds_floats<TM>(reinterpret_cast<const float *>(sa) + (8 * g + 4 * lh + s) * BM + a_row0, v);
-#pragma unroll
-                        for (int t = 0; t < TM; ++t) av[t][s] = v[t];
-                    }
-                }
-                if constexpr (B_KC) {
-#pragma unroll
-                    for (int u = 0; u < TN; ++u) {
-                        const f32x4 v = *reinterpret_cast<const f32x4 *>(
-                            sb + kc_off<ROWB, TN>(b_row0 + u, (8 * g + 4 * lh) * 4));
-#pragma unroll
-                        for (int s = 0; s < 4; ++s) bv[u][s] = v[s];
-                    }
-                } else {
-#pragma unroll
-                    for (int s = 0; s < 4; ++s) {
-                        float v[TN];
-                        lds_floats<TN>(reinterpret_cast<const float *>(sb) + (8 * g + 4 * lh + s) * BN + b_row0, v);
-#pragma unroll
-                        for (int u = 0; u < TN; ++u) bv[u][s] = v[u];
-                    }
-                }
-#pragma unroll
-                for (int s = 0; s < 4; ++s)
-#pragma unroll
-                    for (int t = 0; t < TM; ++t)
-#pragma unroll
-                        for (int u = 0; u < TN; ++u)
-                            acc[t][u] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[t][s], bv[u][s], acc[t][u], 0, 0, 0);
-            }
-        } else {
-            // 16 k per group: lane half h carries k = 16*g + 8*h + (0..7)
-#pragma unroll
-            for (int g = 0; g < BK / 16; ++g) {
-                u32x4 av[TM], bv[TN];
-#pragma unroll
-                for (int t = 0; t < TM; ++t)
-                    av[t] = *reinterpret_cast<const u32x4 *>(sa + kc_off<ROWB, TM>(a_row0 + t, (16 * g + 8 * lh) * 2));
-#pragma unroll
-                for (int u = 0; u < TN; ++u)
-                    bv[u] = *reinterpret_cast<const u32x4 *>(sb + kc_off<ROWB, TN>(b_row0 + u, (16 * g + 8 * lh) * 2));
-#pragma unroll
-                for (int t = 0; t < TM; ++t)
-#pragma unroll
-                    for (int u = 0; u < TN; ++u) {
-                        if constexpr (sizeof(T) == 2 && __is_same(T, _Float16))
-                            acc[t][u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                                __builtin_bit_cast(f16x8, av[t]), __builtin_bit_cast(f16x8, bv[u]), acc[t][u], 0, 0, 0);
-                        else
-                            acc[t][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                                __builtin_bit_cast(bf16x8, av[t]), __builtin_bit_cast(bf16x8, bv[u]), acc[t][u], 0, 0, 0);
-                    }
-            }
-        }
-    };
-
-    // ---- software pipeline: one LDS stage being consumed, the next slab in flight
-    const int nk = (p.K + BK - 1) / BK;
-    load_slab(0);
-    store_slab(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const bool more = kt + 1 < nk;
-        if (more) {
-            Ap += a_kstep;
-            Bp += b_kstep;
-            load_slab((kt + 1) * BK);
-        }
-        compute_slab(kt & 1);
-        if (more) store_slab((kt + 1) & 1);
-        __syncthreads();
-    }
-
-    // ---- epilogue: C = alpha*acc + beta*C, C read only when beta != 0
-    float *Cb = p.C + (int64_t)bidx * p.strideC;
-    const int col = n0 + wn * WTN + TN * li;
-    const bool col_full = col + TN <= p.N;
-    const bool use_beta = p.beta != 0.0f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int ip = 8 * (r >> 2) + 4 * lh + (r & 3);
-#pragma unroll
-        for (int t = 0; t < TM; ++t) {
-            const int row = m0 + wm * WTM + TM * ip + t;
-            if (row >= p.M) continue;
-            float *cp = Cb + (int64_t)row * p.ldc + col;
-            float v[TN];
-#pragma unroll
-            for (int u = 0; u < TN; ++u) v[u] = p.alpha * acc[t][u][r];
-            if (TN > 1 && col_full && p.c_vec) {
-                if constexpr (TN == 4) {
-                    f32x4 o = {v[0], v[1], v[2], v[3]};
-                    if (use_beta) o += p.beta * *reinterpret_cast<const f32x4 *>(cp);
-                    *reinterpret_cast<f32x4 *>(cp) = o;
-                } else if constexpr (TN == 2) {
-                    f32x2 o = {v[0], v[1]};
-                    if (use_beta) o += p.beta * *reinterpret_cast<const f32x2 *>(cp);
-                    *reinterpret_cast<f32x2 *>(cp) = o;
-                }
-            } else {
-#pragma unroll
-                for (int u = 0; u < TN; ++u)
-                    if (col + u < p.N) cp[u] = use_beta ? v[u] + p.beta * cp[u] : v[u];
-            }
+    if constexpr (VECOK) {
+        const bool interior = p.fast_ok && m0 + BM <= p.M && n0 + BN <= p.N && p.K % D::BK == 0;
+        if (interior) {
+            D::run(p, smem, bidx, m0, n0, acc);
+            epilogue<false, D::IL_A, D::IL_B, TM, TN, WTM, WTN, WN>(p, bidx, m0, n0, acc);
+            return;
         }
     }
+    R::run(p, smem, bidx, m0, n0, acc);
+    epilogue<true, R::IL_A, R::IL_B, TM, TN, WTM, WTN, WN>(p, bidx, m0, n0, acc);
 }
 
 // C = beta * C over a strided batch (alpha == 0 or K == 0).  beta == 0 writes

@@ -112,6 +112,10 @@ mgemm_status validate_and_plan(int dtype, int transA, int transB, int64_t M, int
     a.alpha = alpha;
     a.beta = beta;
     a.c_vec = aligned(C, 16) && ldc % 4 == 0 && (batch == 1 || strideC % 4 == 0);
+    // Interior tiles address their operands with 32-bit byte offsets from the
+    // tile origin: at most 256 rows of the larger leading dimension.
+    const int64_t max_ld = lda > ldb ? lda : ldb;
+    a.fast_ok = (256 + 1) * max_ld * es < ((int64_t)1 << 31);
     if (!reads_ab) {
         plan->kind = Plan::SCALE;
         return MGEMM_OK;
