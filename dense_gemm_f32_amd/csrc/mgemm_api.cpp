@@ -135,17 +135,30 @@ mgemm_status validate_and_plan(int dtype, int transA, int transB, int64_t M, int
         // a forced aligned-only variant on unaligned data falls back to the automatic choice
     }
     if (pick < 0) {
-        // Largest tile that still gives at least one workgroup per CU (256 CUs);
-        // otherwise the smallest tile, to spread a small problem over more CUs.
+        // The table is in order of preference (measured on the large square
+        // problems): take the first variant that still gives at least one
+        // workgroup per CU (256 CUs); if none does, the smallest tile, to spread
+        // a small problem over more CUs.  A shallow K (the whole product is a
+        // couple of slabs, e.g. attention scores with a 64-wide head) is bound
+        // by the C store rather than the matrix cores: there the 256x256 tile
+        // with 4x2 wavefronts measured best, so it moves to the front.
         const int64_t min_wgs = 256;
         int best = -1, smallest = -1;
+        auto eligible = [&](const Variant &v) { return v.vec == vec_ok; };  // aligned build when allowed
+        auto wgs_of = [&](const Variant &v) {
+            return ((M + v.bm - 1) / v.bm) * ((N + v.bn - 1) / v.bn) * batch;
+        };
+        if (dtype != MGEMM_F32 && K <= 128) {
+            for (int i = 0; i < t.n && best < 0; ++i)
+                if (eligible(t.v[i]) && t.v[i].bm == 256 && t.v[i].bn == 256 && t.v[i].wm == 4 &&
+                    wgs_of(t.v[i]) >= min_wgs)
+                    best = i;
+        }
         for (int i = 0; i < t.n; ++i) {
             const Variant &v = t.v[i];
-            if (v.vec && !vec_ok) continue;
-            if (!v.vec && vec_ok) continue;  // prefer the aligned build of a shape when allowed
-            const int64_t wgs = ((M + v.bm - 1) / v.bm) * ((N + v.bn - 1) / v.bn) * batch;
+            if (!eligible(v)) continue;
             if (smallest < 0 || v.bm * v.bn < t.v[smallest].bm * t.v[smallest].bn) smallest = i;
-            if (wgs >= min_wgs && (best < 0 || v.bm * v.bn > t.v[best].bm * t.v[best].bn)) best = i;
+            if (best < 0 && wgs_of(v) >= min_wgs) best = i;
         }
         pick = best >= 0 ? best : smallest;
     }
