@@ -222,11 +222,12 @@ def secondary(torch, dev, iters):
     from dense_gemm_f32_amd import workloads as wl
     import dense_gemm_f32_amd as mg
     out = {}
-    for name in ("gemm_bf16_8192", "gemm_f16_8192", "qkt_batched"):
+    for name in ("gemm_bf16_8192", "gemm_f16_8192", "qkt_batched", "sgemm_256", "sgemm_ragged"):
         p = wl.WORKLOADS[name]()
         dA, dB, dC = make_device_problem(p, torch, dev)
         fn = launcher(p, dA, dB, dC)
-        for _ in range(3):
+        # warm up to the steady clock the part settles at under this load
+        for _ in range(30):
             fn()
         torch.cuda.synchronize()
         t = time_kernel(torch, fn, iters)
@@ -342,7 +343,7 @@ def main():
                 "kernel_ms": round(t_kernel * 1e3, 4), "algorithmic_flop_per_launch": p.flops,
                 "algorithmic_bytes_per_launch": algorithmic_bytes(p)}
 
-    sec = None if args.no_secondary else secondary(torch, dev, 20)
+    sec = None if args.no_secondary else secondary(torch, dev, 30)
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(p, A, B, C0)

@@ -523,17 +523,19 @@ struct RegPath {
 
 // ===========================================================================
 // DmaPath: interior tiles.  Global -> LDS with buffer_load_dwordx4 ... lds
-// (no registers in between), a ring of 4 LDS stages of BK = BKR/2 elements
-// (32 for 16-bit, 16 for fp32), loads issued 3 slabs ahead.  One barrier per
-// slab, placed before the MFMAs of the slab's second k-group so that the
-// next slab's first fragment reads overlap them.
+// (no registers in between) into a ring of NS LDS stages of BK elements,
+// loads issued NS-1 slabs ahead.  DEPTH 1: BK = BKR/2 (32 for 16-bit, 16 for
+// fp32), NS = 4; DEPTH 2: BK = BKR, NS = 2.  One barrier per slab, placed
+// before the MFMAs of the slab's last k-group so that the next slab's first
+// fragment reads overlap them.
 //
 // LDS layouts (bank-conflict free for every access of this path):
-//   KC  operand K-contiguous in memory: rows of BK elements = 64 bytes, a
-//       quarter of a bank line; physical row order as phys_row; chunk c of
-//       physical row p at c ^ ((p >> 2) & 3).  A fragment read touches 16
-//       consecutive physical rows per 16 lanes: 4 rows per line position x
-//       4 distinct chunks.
+//   KC  operand K-contiguous in memory: rows of BK elements (RB = 64 or 128
+//       bytes, a quarter or half of a 256-byte bank line); physical row order
+//       as phys_row; chunk c of physical row p at c ^ swz(p), with
+//       swz(p) = (p >> 2) & 3 for 64-byte rows and (p >> 1) & 7 for 128-byte
+//       rows.  A fragment read touches 16 consecutive physical rows per 16
+//       lanes, which then cover the 16 distinct 16-byte slots of a line.
 //   MC  operand MN-contiguous in memory: BK rows of MN elements, stored as
 //       in memory but with its 64-byte pieces permuted per row
 //       (piece ^ key(k)), so the 4 rows read together land in 4 distinct
@@ -544,7 +546,7 @@ struct RegPath {
 //       16-bit MC operand therefore index consecutive (not interleaved)
 //       rows/columns (interleave 1).
 // ===========================================================================
-template <typename T, int BM, int BN, int BKR, int WM, int WN, bool TA, bool TB>
+template <typename T, int BM, int BN, int BKR, int WM, int WN, bool TA, bool TB, int DEPTH>
 struct DmaPath {
     static constexpr int NT = WM * WN * 64;
     static constexpr int NW = WM * WN;
@@ -552,9 +554,12 @@ struct DmaPath {
     static constexpr bool F32 = (ES == 4);
     static constexpr int WTM = BM / WM, WTN = BN / WN;
     static constexpr int TM = WTM / 32, TN = WTN / 32;
-    static constexpr int BK = BKR / 2;
-    static constexpr int NS = 4;
-    static_assert(BK * ES == 64, "64-byte K-contiguous rows");
+    static constexpr int BK = DEPTH == 2 ? BKR : BKR / 2;
+    static constexpr int NS = DEPTH == 2 ? 2 : 4;
+    static constexpr int RB = BK * ES;          // K-contiguous row bytes
+    static_assert(RB == 64 || RB == 128, "64- or 128-byte K-contiguous rows");
+    static constexpr int CPR = RB / 16;         // 16-byte chunks per row
+    static constexpr int G = F32 ? BK / 8 : BK / 16;  // k-groups per slab
     static constexpr bool A_KC = !TA, B_KC = TB;
     static constexpr bool A_TR = TA && !F32, B_TR = !TB && !F32;
     static constexpr int IL_A = A_TR ? 1 : TM, IL_B = B_TR ? 1 : TN;
@@ -565,16 +570,18 @@ struct DmaPath {
     static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "DMA split");
     static constexpr int A_IPW = A_BYTES / 1024 / NW, B_IPW = B_BYTES / 1024 / NW;
     static constexpr int LPS = A_IPW + B_IPW;  // DMA loads per slab per thread
-    static_assert(3 * LPS <= 63, "vmcnt range");
+    static_assert((NS - 1) * LPS <= 63, "vmcnt range");
     static_assert(A_KC || A_ROWB >= 128, "MC rows of at least 128 bytes");
     static_assert(B_KC || B_ROWB >= 128, "MC rows of at least 128 bytes");
 
     using Fr = Frags<T, TM, TN>;
 
+    __device__ __forceinline__ static int swz(int p) { return RB == 64 ? ((p >> 2) & 3) : ((p >> 1) & 7); }
+
     __device__ __forceinline__ static int kc_off(int p, int kbyte)
     {
-        const int chunk = (kbyte >> 4) ^ ((p >> 2) & 3);
-        return p * 64 + (chunk << 4) + (kbyte & 15);
+        const int chunk = (kbyte >> 4) ^ swz(p);
+        return p * RB + (chunk << 4) + (kbyte & 15);
     }
 
     template <int ROWB>
@@ -589,32 +596,31 @@ struct DmaPath {
         return k * ROWB + (((byte >> 6) ^ mc_key<ROWB>(k)) << 6) + (byte & 63);
     }
 
-    // DMA of one operand's slab: wave `w` issues IPW 1 KB loads into the
-    // operand's region `dst` of a stage, from tile origin `src`.
+    // DMA instruction q (of IPW) of wave `w` for one operand's slab: 1 KB into
+    // the operand's region `dst` of a stage, from tile origin `src`.
     template <bool KC, int IL, int ROWB, int IPW>
-    __device__ __forceinline__ static void dma_operand(const char *src, char *dst, int ld_bytes, int w,
-                                                       int lane)
+    __device__ __forceinline__ static void dma_one(__amdgpu_buffer_rsrc_t rs, char *dst, int ld_bytes, int w,
+                                                   int lane, int q)
     {
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(src);
-#pragma unroll
-        for (int q = 0; q < IPW; ++q) {
-            const int ins = w * IPW + q;
-            if constexpr (KC) {
-                // 16 physical rows pb .. pb+15 (64 bytes each); lane -> row pb + lane/4,
-                // physical chunk lane%4, logical chunk (lane%4) ^ ((lane/16) & 3); the
-                // logical rows are logical_row(pb) + (lane/4)*IL.
-                const int pb = ins * 16;
-                const int voff = (lane >> 2) * IL * ld_bytes + (((lane & 3) ^ ((lane >> 4) & 3)) << 4);
-                const int soff = __builtin_amdgcn_readfirstlane(logical_row<IL>(pb) * ld_bytes);
-                dma16(rs, lds_addr_of(dst + pb * 64), voff, soff);
-            } else {
-                // bytes b = ins*1024 + 16*lane of the [BK][MN] region: row k = b / ROWB,
-                // physical piece (b % ROWB) / 64 holds logical piece ^ key(k)
-                const int b = ins * 1024 + 16 * lane;
-                const int k = b / ROWB, bb = b % ROWB;
-                const int lb = (((bb >> 6) ^ mc_key<ROWB>(k)) << 6) | (bb & 63);
-                dma16(rs, lds_addr_of(dst + ins * 1024), k * ld_bytes + lb, 0);
-            }
+        const int ins = w * IPW + q;
+        if constexpr (KC) {
+            // 1024/RB physical rows pb.. of RB bytes; lane -> row pb + lane/CPR, physical
+            // chunk lane%CPR holding logical chunk (lane%CPR) ^ swz(row); the logical
+            // rows are logical_row(pb) + (lane/CPR)*IL.
+            constexpr int RPI = 1024 / RB;
+            const int pb = ins * RPI;
+            const int j = lane / CPR;
+            const int c = (lane % CPR) ^ swz(pb + j);
+            const int voff = j * IL * ld_bytes + (c << 4);
+            const int soff = __builtin_amdgcn_readfirstlane(logical_row<IL>(pb) * ld_bytes);
+            dma16(rs, lds_addr_of(dst + pb * RB), voff, soff);
+        } else {
+            // bytes b = ins*1024 + 16*lane of the [BK][MN] region: row k = b / ROWB,
+            // physical piece (b % ROWB) / 64 holds logical piece ^ key(k)
+            const int b = ins * 1024 + 16 * lane;
+            const int k = b / ROWB, bb = b % ROWB;
+            const int lb = (((bb >> 6) ^ mc_key<ROWB>(k)) << 6) | (bb & 63);
+            dma16(rs, lds_addr_of(dst + ins * 1024), k * ld_bytes + lb, 0);
         }
     }
 
@@ -699,8 +705,14 @@ struct DmaPath {
     static constexpr int DSR = DSR_A + DSR_B;
     static constexpr int MF = F32 ? 4 * TM * TN : TM * TN;
 
+    template <int N>
+    __device__ __forceinline__ static void wait_ahead()
+    {
+        wait_counts<N * LPS, 0>();
+    }
+
     __device__ __forceinline__ static void run(const KernelArgs &p, char *smem, int bidx, int m0, int n0,
-                               f32x16 (&acc)[TM][TN])
+                                               f32x16 (&acc)[TM][TN])
     {
         const int tid = threadIdx.x;
         const int lane = tid & 63;
@@ -725,11 +737,15 @@ struct DmaPath {
         const int64_t b_kstep = (TB ? (int64_t)BK : (int64_t)BK * p.ldb) * ES;
         const int lda_b = (int)(p.lda * ES), ldb_b = (int)(p.ldb * ES);
 
-        auto stage = [&](int s) { return smem + (s & (NS - 1)) * STAGE; };
+        auto stage = [&](int s) { return smem + (s % NS) * STAGE; };
         auto issue = [&](int s) {
             char *st = stage(s);
-            dma_operand<A_KC, IL_A, A_ROWB, A_IPW>(Ap + (int64_t)s * a_kstep, st, lda_b, w, lane);
-            dma_operand<B_KC, IL_B, B_ROWB, B_IPW>(Bp + (int64_t)s * b_kstep, st + A_BYTES, ldb_b, w, lane);
+            const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ap + (int64_t)s * a_kstep);
+            const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bp + (int64_t)s * b_kstep);
+#pragma unroll
+            for (int q = 0; q < A_IPW; ++q) dma_one<A_KC, IL_A, A_ROWB, A_IPW>(ra, st, lda_b, w, lane, q);
+#pragma unroll
+            for (int q = 0; q < B_IPW; ++q) dma_one<B_KC, IL_B, B_ROWB, B_IPW>(rb, st + A_BYTES, ldb_b, w, lane, q);
         };
         auto frags = [&](int s, int g, Fr &f) {
             const char *st = stage(s);
@@ -737,46 +753,66 @@ struct DmaPath {
         };
 
         const int nk = p.K / BK;
-        // prologue: slabs 0..3 in flight, wait for slab 0
+        // prologue: slabs 0..NS-1 in flight, wait for slab 0
         issue(0);
-        if (nk > 1) issue(1);
-        if (nk > 2) issue(2);
-        if (nk > 3) issue(3);
-        if (nk > 3)      wait_counts<3 * LPS, 0>();
-        else if (nk > 2) wait_counts<2 * LPS, 0>();
-        else if (nk > 1) wait_counts<LPS, 0>();
-        else             wait_counts<0, 0>();
+#pragma unroll
+        for (int s = 1; s < NS; ++s)
+            if (s < nk) issue(s);
+        {
+            const int inflight = nk < NS ? nk : NS;  // slabs issued
+            if constexpr (NS == 4) {
+                if (inflight == 4)      wait_ahead<3>();
+                else if (inflight == 3) wait_ahead<2>();
+                else if (inflight == 2) wait_ahead<1>();
+                else                    wait_ahead<0>();
+            } else {
+                if (inflight == 2) wait_ahead<1>();
+                else               wait_ahead<0>();
+            }
+        }
         lds_barrier();
 
-        Fr f0, f1;
-        frags(0, 0, f0);
+        Fr f[2];
+        frags(0, 0, f[0]);
+        // one slab: groups 0..G-2 with the next group's fragments read under
+        // the MFMAs; then wait for slab kt+1 (my copies), barrier, refill the
+        // freed stage, read slab kt+1's first group under the last group's MFMAs
+        auto body_head = [&](int kt) {
+#pragma unroll
+            for (int g = 0; g + 1 < G; ++g) {
+                frags(kt, g + 1, f[(g + 1) & 1]);
+                f[g & 1].mfmas(acc);
+                sched_interleave<SG_MFMA, MF, SG_DS_READ, DSR>();
+            }
+        };
         int kt = 0;
-        // steady state: slab kt+4 exists; at the wait, slabs kt+2 and kt+3 may
-        // still be in flight
-        for (; kt + 4 < nk; ++kt) {
-            frags(kt, 1, f1);
-            f0.mfmas(acc);
-            sched_interleave<SG_MFMA, MF, SG_DS_READ, DSR>();
-            wait_counts<2 * LPS, 0>();
+        // steady state: slab kt+NS exists; at the wait, slabs kt+2 .. kt+NS-1
+        // may still be in flight
+        for (; kt + NS < nk; ++kt) {
+            body_head(kt);
+            wait_ahead<NS - 2>();
             lds_barrier();
-            issue(kt + 4);
-            frags(kt + 1, 0, f0);
-            f1.mfmas(acc);
+            issue(kt + NS);
+            frags(kt + 1, 0, f[G & 1]);
+            f[(G - 1) & 1].mfmas(acc);
             sched_interleave<SG_MFMA, MF, SG_DS_READ, DSR>();
         }
         // last slabs: everything already issued
         for (; kt < nk; ++kt) {
-            frags(kt, 1, f1);
-            f0.mfmas(acc);
+            body_head(kt);
             if (kt + 1 < nk) {
                 const int ahead = nk - kt - 2;  // slabs after kt+1 still possibly in flight
-                if (ahead >= 2)      wait_counts<2 * LPS, 0>();
-                else if (ahead == 1) wait_counts<LPS, 0>();
-                else                 wait_counts<0, 0>();
+                if constexpr (NS == 4) {
+                    if (ahead >= 2)      wait_ahead<2>();
+                    else if (ahead == 1) wait_ahead<1>();
+                    else                 wait_ahead<0>();
+                } else {
+                    wait_ahead<0>();
+                }
                 lds_barrier();
-                frags(kt + 1, 0, f0);
+                frags(kt + 1, 0, f[G & 1]);
             }
-            f1.mfmas(acc);
+            f[(G - 1) & 1].mfmas(acc);
         }
     }
 };
@@ -850,13 +886,14 @@ __device__ __forceinline__ void epilogue(const KernelArgs &p, int bidx, int m0, 
 //              made of TM x TN MFMA blocks of 32x32
 //   TA, TB     op(A) = A^T, op(B) = B^T
 //   VECOK      A and B allow 16-byte global accesses (enables DmaPath)
+//   DEPTH      DmaPath slab depth: 1 -> 4 stages of BK/2, 2 -> 2 stages of BK
 // ---------------------------------------------------------------------------
-template <typename T, int BM, int BN, int BK, int WM, int WN, bool TA, bool TB, bool VECOK>
+template <typename T, int BM, int BN, int BK, int WM, int WN, bool TA, bool TB, bool VECOK, int DEPTH>
 __global__ void __launch_bounds__(WM * WN * 64)
 gemm_kernel(KernelArgs p)
 {
     using R = RegPath<T, BM, BN, BK, WM, WN, TA, TB, VECOK>;
-    using D = DmaPath<T, BM, BN, BK, WM, WN, TA, TB>;
+    using D = DmaPath<T, BM, BN, BK, WM, WN, TA, TB, DEPTH>;
     constexpr int TM = R::TM, TN = R::TN, WTM = R::WTM, WTN = R::WTN;
     constexpr int LDS = (VECOK && D::LDS_BYTES > R::LDS_BYTES) ? D::LDS_BYTES : R::LDS_BYTES;
     __shared__ __attribute__((aligned(1024))) char smem[LDS];

@@ -15,25 +15,28 @@ struct Variant {
     int bm, bn, bk;       // workgroup tile and K-slab
     int wm, wn;           // wavefront grid
     bool vec;             // needs 16-byte aligned A/B rows (dwordx4 loads)
+    int depth;            // DMA-path slab depth (1: 4 stages of bk/2, 2: 2 stages of bk)
     const char *name;
     LaunchFn fn[2][2];    // [transA][transB]
 };
 
-template <typename T, int BM, int BN, int BK, int WM, int WN, bool TA, bool TB, bool V>
+template <typename T, int BM, int BN, int BK, int WM, int WN, bool TA, bool TB, bool V, int D>
 hipError_t launch_gemm(const KernelArgs &a, unsigned grid, hipStream_t s)
 {
     KernelArgs copy = a;
     void *args[] = {&copy};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&gemm_kernel<T, BM, BN, BK, WM, WN, TA, TB, V>),
+    return hipLaunchKernel(reinterpret_cast<const void *>(&gemm_kernel<T, BM, BN, BK, WM, WN, TA, TB, V, D>),
                            dim3(grid), dim3(WM * WN * 64), args, 0, s);
 }
 
-#define MGEMM_VARIANT(T, DT, BM, BN, BK, WM, WN, V, NAME)                                   \
-    {DT, BM, BN, BK, WM, WN, V, NAME,                                                        \
-     {{launch_gemm<T, BM, BN, BK, WM, WN, false, false, V>,                                  \
-       launch_gemm<T, BM, BN, BK, WM, WN, false, true, V>},                                  \
-      {launch_gemm<T, BM, BN, BK, WM, WN, true, false, V>,                                   \
-       launch_gemm<T, BM, BN, BK, WM, WN, true, true, V>}}}
+#define MGEMM_VARIANT_D(T, DT, BM, BN, BK, WM, WN, V, D, NAME)                               \
+    {DT, BM, BN, BK, WM, WN, V, D, NAME,                                                     \
+     {{launch_gemm<T, BM, BN, BK, WM, WN, false, false, V, D>,                               \
+       launch_gemm<T, BM, BN, BK, WM, WN, false, true, V, D>},                               \
+      {launch_gemm<T, BM, BN, BK, WM, WN, true, false, V, D>,                                \
+       launch_gemm<T, BM, BN, BK, WM, WN, true, true, V, D>}}}
+
+#define MGEMM_VARIANT(T, DT, BM, BN, BK, WM, WN, V, NAME) MGEMM_VARIANT_D(T, DT, BM, BN, BK, WM, WN, V, 1, NAME)
 
 // Host-side variant tables, one per input type (function-local statics, so
 // that the device compilation never sees the host launch pointers).

@@ -65,6 +65,19 @@ def sampled_check(p, exact=False, what="", n_random=20000):
     assert not np.isnan(got).any()
 
 
+def _round8(x):
+    return (x + 7) // 8 * 8
+
+
+def _assert_selected(p, v):
+    # a forced aligned-only variant falls back to the automatic choice on unaligned
+    # operands: make sure the case really runs the variant it is meant to cover
+    info, _ = mg.select(p.dtype, int(p.transA), int(p.transB), p.M, p.N, p.K, p.alpha,
+                        16, p.lda, p.strideA, 16, p.ldb, p.strideB, p.beta, 16, p.ldc,
+                        p.strideC, p.batch)
+    assert info["name"] == v["name"], (info["name"], v["name"])
+
+
 def variants_of(dtype):
     code = {"f32": 0, "f16": 1, "bf16": 2}[dtype]
     return [v for v in mg.variants() if v["dtype"] == code] if torch.cuda.is_available() else []
@@ -78,12 +91,54 @@ def test_every_variant_every_transpose_ragged(dtype):
         mg.force_variant(dtype, v["id"])
         bm, bn, bk = v["block_m"], v["block_n"], v["block_k"]
         M, N, K = 2 * bm + 17, 2 * bn + 9, 3 * bk + 5
+        aligned = not v["name"].endswith("_u")
         for tA, tB in itertools.product((False, True), repeat=2):
+            a_cols = M if tA else K
+            b_cols = K if tB else N
+            # the aligned builds need 16-byte rows; the others get the tight, odd ones
             base = wl.Problem(dtype, M, N, K, transA=tA, transB=tB, alpha=1.5, beta=0.5,
+                              lda=_round8(a_cols) if aligned else a_cols,
+                              ldb=_round8(b_cols) if aligned else b_cols,
                               dist="uniform" if dtype == "f32" else "normal",
-                              c_dist="uniform", seed=11)
+                              c_dist="uniform", pad_value=float("nan"), seed=11)
+            _assert_selected(base, v)
             full_check(base, what=f"{v['name']} float")
             full_check(wl.int_shadow(base, -8, 8), exact=True, what=f"{v['name']} int")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_dma_path_every_variant_every_transpose(dtype):
+    # K a multiple of every slab depth, so interior tiles take the LDS-DMA path while
+    # the ragged last tile row/column takes the range-checked path; leading dimensions
+    # padded by 8 elements (16-byte rows stay aligned) with NaN in the padding.
+    for v in variants_of(dtype):
+        if v["name"].endswith("_u"):
+            continue
+        mg.force_variant(dtype, v["id"])
+        bm, bn, bk = v["block_m"], v["block_n"], v["block_k"]
+        M, N, K = 2 * bm + 17, 2 * bn + 9, 4 * bk
+        for tA, tB in itertools.product((False, True), repeat=2):
+            a_cols = M if tA else K
+            b_cols = K if tB else N
+            base = wl.Problem(dtype, M, N, K, transA=tA, transB=tB, lda=_round8(a_cols) + 8,
+                              ldb=_round8(b_cols) + 8, ldc=N + 4, alpha=1.5, beta=0.5,
+                              dist="uniform" if dtype == "f32" else "normal", c_dist="uniform",
+                              pad_value=float("nan"), seed=31)
+            _assert_selected(base, v)
+            full_check(base, what=f"{v['name']} DMA float")
+            full_check(wl.int_shadow(base, -8, 8), exact=True, what=f"{v['name']} DMA int")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_dma_path_batched_and_broadcast(dtype):
+    # interior tiles in several batch entries, B shared by all entries (stride 0)
+    v = variants_of(dtype)[0]
+    mg.force_variant(dtype, v["id"])
+    K = 2 * v["block_k"]
+    p = wl.Problem(dtype, v["block_m"], v["block_n"], K, batch=3, strideB=0, transB=True,
+                   dist="int", int_lo=-8, int_hi=8, seed=32)
+    _assert_selected(p, v)
+    full_check(p, exact=True, what=f"{v['name']} DMA batched, strideB=0")
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
