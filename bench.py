@@ -113,9 +113,9 @@ def summarize_profiles(d):
                         p.beta, 1 << 20, p.ldc, 0, 1)
     kname = info["name"]
     # kernel names appear demangled in the rocprofv3 CSVs
-    depth = 2 if kname.endswith("_d2") else 1
     inst = "gemm_kernel<float, %d, %d, %d, %d, %d, false, false, true, %d>" % (
-        info["block_m"], info["block_n"], info["block_k"], info["waves_m"], info["waves_n"], depth)
+        info["block_m"], info["block_n"], info["block_k"], info["waves_m"], info["waves_n"],
+        info["pipe"])
     stats = _kernel_stats(os.path.join(d, "trace"), inst)
     durs = _dispatch_durations(os.path.join(d, "trace"), inst)
     timed = durs[5:]  # the traced command ran 5 warmup steps, then the timed ones

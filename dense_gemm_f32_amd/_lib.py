@@ -36,7 +36,7 @@ class VariantInfo(ctypes.Structure):
     _fields_ = [("id", ctypes.c_int), ("dtype", ctypes.c_int), ("block_m", ctypes.c_int),
                 ("block_n", ctypes.c_int), ("block_k", ctypes.c_int), ("waves_m", ctypes.c_int),
                 ("waves_n", ctypes.c_int), ("threads", ctypes.c_int), ("lds_bytes", ctypes.c_int),
-                ("name", ctypes.c_char * 64)]
+                ("pipe", ctypes.c_int), ("name", ctypes.c_char * 64)]
 
     def as_dict(self):
         d = {f: getattr(self, f) for f, _ in self._fields_}

@@ -523,11 +523,13 @@ struct RegPath {
 
 // ===========================================================================
 // DmaPath: interior tiles.  Global -> LDS with buffer_load_dwordx4 ... lds
-// (no registers in between) into a ring of NS LDS stages of BK elements,
-// loads issued NS-1 slabs ahead.  DEPTH 1: BK = BKR/2 (32 for 16-bit, 16 for
-// fp32), NS = 4; DEPTH 2: BK = BKR, NS = 2.  One barrier per slab, placed
-// before the MFMAs of the slab's last k-group so that the next slab's first
-// fragment reads overlap them.
+// (no registers in between) into a ring of NS LDS stages of BK elements.
+// Two schedules (PIPE):
+//   1  BK = BKR/2 (32 for 16-bit, 16 for fp32), NS = 4, loads issued 3 slabs
+//      ahead; every wave reads and multiplies each slab, with one barrier per
+//      slab placed before the MFMAs of its last k-group so that the next
+//      slab's first fragment reads overlap them.
+//   2  the same with BK = BKR, NS = 2 (one slab ahead, half the barriers).
 //
 // LDS layouts (bank-conflict free for every access of this path):
 //   KC  operand K-contiguous in memory: rows of BK elements (RB = 64 or 128
@@ -546,7 +548,7 @@ struct RegPath {
 //       16-bit MC operand therefore index consecutive (not interleaved)
 //       rows/columns (interleave 1).
 // ===========================================================================
-template <typename T, int BM, int BN, int BKR, int WM, int WN, bool TA, bool TB, int DEPTH>
+template <typename T, int BM, int BN, int BKR, int WM, int WN, bool TA, bool TB, int PIPE>
 struct DmaPath {
     static constexpr int NT = WM * WN * 64;
     static constexpr int NW = WM * WN;
@@ -554,8 +556,8 @@ struct DmaPath {
     static constexpr bool F32 = (ES == 4);
     static constexpr int WTM = BM / WM, WTN = BN / WN;
     static constexpr int TM = WTM / 32, TN = WTN / 32;
-    static constexpr int BK = DEPTH == 2 ? BKR : BKR / 2;
-    static constexpr int NS = DEPTH == 2 ? 2 : 4;
+    static constexpr int BK = PIPE == 2 ? BKR : BKR / 2;
+    static constexpr int NS = PIPE == 2 ? 2 : 4;
     static constexpr int RB = BK * ES;          // K-contiguous row bytes
     static_assert(RB == 64 || RB == 128, "64- or 128-byte K-contiguous rows");
     static constexpr int CPR = RB / 16;         // 16-byte chunks per row
@@ -886,14 +888,14 @@ __device__ __forceinline__ void epilogue(const KernelArgs &p, int bidx, int m0, 
 //              made of TM x TN MFMA blocks of 32x32
 //   TA, TB     op(A) = A^T, op(B) = B^T
 //   VECOK      A and B allow 16-byte global accesses (enables DmaPath)
-//   DEPTH      DmaPath slab depth: 1 -> 4 stages of BK/2, 2 -> 2 stages of BK
+//   PIPE       DmaPath schedule: 1 -> 4 stages of BK/2, 2 -> 2 stages of BK
 // ---------------------------------------------------------------------------
-template <typename T, int BM, int BN, int BK, int WM, int WN, bool TA, bool TB, bool VECOK, int DEPTH>
+template <typename T, int BM, int BN, int BK, int WM, int WN, bool TA, bool TB, bool VECOK, int PIPE>
 __global__ void __launch_bounds__(WM * WN * 64)
 gemm_kernel(KernelArgs p)
 {
     using R = RegPath<T, BM, BN, BK, WM, WN, TA, TB, VECOK>;
-    using D = DmaPath<T, BM, BN, BK, WM, WN, TA, TB, DEPTH>;
+    using D = DmaPath<T, BM, BN, BK, WM, WN, TA, TB, PIPE>;
     constexpr int TM = R::TM, TN = R::TN, WTM = R::WTM, WTN = R::WTN;
     constexpr int LDS = (VECOK && D::LDS_BYTES > R::LDS_BYTES) ? D::LDS_BYTES : R::LDS_BYTES;
     __shared__ __attribute__((aligned(1024))) char smem[LDS];

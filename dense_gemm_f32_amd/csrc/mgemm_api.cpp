@@ -189,6 +189,7 @@ void fill_info(const Variant &v, int id, mgemm_variant_info *out)
     out->waves_n = v.wn;
     out->threads = v.wm * v.wn * 64;
     out->lds_bytes = 2 * (v.bm + v.bn) * v.bk * elem_size(v.dtype);
+    out->pipe = v.pipe;
     std::snprintf(out->name, sizeof(out->name), "%s", v.name);
 }
 

@@ -15,7 +15,7 @@ struct Variant {
     int bm, bn, bk;       // workgroup tile and K-slab
     int wm, wn;           // wavefront grid
     bool vec;             // needs 16-byte aligned A/B rows (dwordx4 loads)
-    int depth;            // DMA-path slab depth (1: 4 stages of bk/2, 2: 2 stages of bk)
+    int pipe;             // DMA-path schedule (1: 4 stages of bk/2, 2: 2 stages of bk)
     const char *name;
     LaunchFn fn[2][2];    // [transA][transB]
 };

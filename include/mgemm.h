@@ -140,6 +140,8 @@ typedef struct {
     int waves_n;       /* wavefronts along N */
     int threads;       /* workgroup size */
     int lds_bytes;     /* LDS per workgroup */
+    int pipe;          /* interior-tile schedule: 1 = four LDS stages of
+                          block_k/2, 2 = two stages of block_k */
     char name[64];     /* kernel family name, e.g. "mgemm_f32_256x256x32_w2x2" */
 } mgemm_variant_info;
 

@@ -129,6 +129,24 @@ def test_dma_path_every_variant_every_transpose(dtype):
             full_check(wl.int_shadow(base, -8, 8), exact=True, what=f"{v['name']} DMA int")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_dma_path_short_k(dtype):
+    # one to four LDS slabs: the prologue and the drain of every schedule,
+    # with interior tiles (M, N multiples of the tile) and a ragged edge
+    for v in variants_of(dtype):
+        if v["name"].endswith("_u"):
+            continue
+        mg.force_variant(dtype, v["id"])
+        half = v["block_k"] // 2
+        for nslab in (1, 2, 3, 4, 5):
+            K = nslab * half
+            base = wl.Problem(dtype, v["block_m"] + 40, 2 * v["block_n"], K, transB=nslab % 2 == 1,
+                              dist="int", int_lo=-8, int_hi=8, alpha=1.0, beta=-1.0,
+                              c_dist="int", seed=40 + nslab)
+            _assert_selected(base, v)
+            full_check(base, exact=True, what=f"{v['name']} K={K}")
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_dma_path_batched_and_broadcast(dtype):
     # interior tiles in several batch entries, B shared by all entries (stride 0)
