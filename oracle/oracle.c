@@ -40,6 +40,7 @@
  * computed by exactly the loop above, so the thread count cannot change a bit.
  */
 #include <math.h>
+#include <omp.h>
 #include <stddef.h>
 #include <stdint.h>
 #include <string.h>
@@ -201,3 +202,12 @@ int oracle_gemm_elems(int dtype, int transA, int transB,
     }
     return ORACLE_OK;
 }
+
+/* Thread count of the OpenMP loops above (timing only: results do not
+ * depend on it, since threads split whole output elements). */
+void oracle_set_threads(int n)
+{
+    if (n > 0) omp_set_num_threads(n);
+}
+
+int oracle_max_threads(void) { return omp_get_max_threads(); }

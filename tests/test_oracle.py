@@ -256,6 +256,24 @@ def test_elems_matches_full_output_bitwise():
     assert np.array_equal(el, full[b, i, j])
 
 
+def test_thread_count_changes_no_bit():
+    p = wl.Problem("bf16", 67, 45, 129, transA=True, alpha=0.75, beta=-2.0, dist="normal",
+                   c_dist="uniform", seed=9)
+    A, B, C = wl.make_inputs(p)
+    An, Bn = wl.to_numpy_operand(A), wl.to_numpy_operand(B)
+    args = ("bf16", True, False, p.M, p.N, p.K, p.alpha, An, p.lda, Bn, p.ldb, p.beta,
+            C.numpy(), p.ldc)
+    before = oracle.max_threads()
+    try:
+        oracle.set_threads(1)
+        one = oracle.gemm(*args)
+        oracle.set_threads(max(4, before))
+        many = oracle.gemm(*args)
+    finally:
+        oracle.set_threads(before)
+    assert np.array_equal(one, many)
+
+
 def test_bad_arguments_rejected():
     a = f32(np.ones(4))
     with pytest.raises(ValueError):
