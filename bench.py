@@ -49,8 +49,8 @@ PROFILES = os.path.join(ROOT, "profiles")
 COPY_PROBE_BYTES = 256 << 20
 PRIMARY = "sgemm_4096"
 CASES = ("sgemm_256", "sgemm_4096", "sgemm_ragged", "gemm_bf16_8192", "gemm_f16_8192",
-         "qkt_batched")
-HBM_BOUND = ("qkt_batched",)
+         "qkt_batched", "qkt_batched_f16_out")
+HBM_BOUND = ("qkt_batched", "qkt_batched_f16_out")
 MOPS_COUNTER = {"f32": "SQ_INSTS_VALU_MFMA_MOPS_F32", "f16": "SQ_INSTS_VALU_MFMA_MOPS_F16",
                 "bf16": "SQ_INSTS_VALU_MFMA_MOPS_BF16"}
 UTIL_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE",
@@ -257,12 +257,18 @@ def make_device_problem(p, torch, dev):
     from dense_gemm_f32_amd import workloads as wl
     A, B, C0 = wl.make_inputs(p)
     dA, dB = A.to(dev), B.to(dev)
-    dC = C0.to(dev) if C0 is not None else torch.zeros(p.c_elems, dtype=torch.float32, device=dev)
+    dC = (C0.to(dev) if C0 is not None
+          else torch.zeros(p.c_elems, dtype=wl.TORCH_DTYPE[p.c_dtype], device=dev))
     return dA, dB, dC
 
 
 def launcher(p, dA, dB, dC):
     import dense_gemm_f32_amd as mg
+    if p.c_dtype != "f32":
+        return lambda: mg.gemm_strided_batched_ex(p.dtype, p.c_dtype, int(p.transA), int(p.transB),
+                                                  p.M, p.N, p.K, p.alpha, dA, p.lda, p.strideA, dB,
+                                                  p.ldb, p.strideB, p.beta, dC, p.ldc, p.strideC,
+                                                  p.batch)
     if p.batch == 1:
         fn = {"f32": mg.gemm_f32, "f16": mg.gemm_f16, "bf16": mg.gemm_bf16}[p.dtype]
         return lambda: fn(int(p.transA), int(p.transB), p.M, p.N, p.K, p.alpha, dA, p.lda, dB,
@@ -305,8 +311,8 @@ def time_each(torch, fn, iters, between=None):
 def algorithmic_bytes(p):
     """Compulsory HBM traffic: A and B once, C written (and read when beta != 0)."""
     from dense_gemm_f32_amd import workloads as wl
-    es = wl.ELEM_SIZE[p.dtype]
-    per = (p.M * p.K + p.K * p.N) * es + p.M * p.N * 4 * (2 if p.beta != 0 else 1)
+    es, ces = wl.ELEM_SIZE[p.dtype], wl.ELEM_SIZE[p.c_dtype]
+    per = (p.M * p.K + p.K * p.N) * es + p.M * p.N * ces * (2 if p.beta != 0 else 1)
     return per * p.batch
 
 
@@ -329,7 +335,7 @@ def per_config(torch, dev, iters):
         each = time_each(torch, fn, iters)
         info, grid = select_for(mg, p, (dA.data_ptr(), dB.data_ptr(), dC.data_ptr()))
         tf = p.flops / t / 1e12
-        rec = {"dtype": p.dtype, "M": p.M, "N": p.N, "K": p.K, "batch": p.batch,
+        rec = {"dtype": p.dtype, "c_dtype": p.c_dtype, "M": p.M, "N": p.N, "K": p.K, "batch": p.batch,
                "transA": int(p.transA), "transB": int(p.transB), "alpha": p.alpha,
                "beta": p.beta, "kernel": info["name"], "grid": grid,
                "ms": round(t * 1e3, 4), "median_ms": round(statistics.median(each) * 1e3, 4),

@@ -1,6 +1,7 @@
 """MI355X-native dense row-major GEMM.
 
-    C = alpha * op(A) * op(B) + beta * C      (fp32 C; fp32, f16 or bf16 A/B)
+    C = alpha * op(A) * op(B) + beta * C      (fp32, f16 or bf16 A/B; fp32 accumulate;
+                                               fp32 C, or 16-bit C of the inputs' type)
 
 Python binding over the C-ABI library libmgemm.so (include/mgemm.h): the
 functions below forward to the C entry points of the same names.  All the
@@ -8,8 +9,10 @@ arithmetic runs in the library's HIP kernels for gfx950; PyTorch only
 provides device memory and streams.
 """
 from ._lib import (BF16, F16, F32, OP_N, OP_T, MgemmError, force_variant, gemm_bf16, gemm_f16,
-                   gemm_f32, gemm_strided_batched, load, select, status_string, variants)
+                   gemm_f32, gemm_strided_batched, gemm_strided_batched_ex, load, select,
+                   status_string, variants)
 
-__all__ = ["gemm_f32", "gemm_f16", "gemm_bf16", "gemm_strided_batched", "select", "variants",
+__all__ = ["gemm_f32", "gemm_f16", "gemm_bf16", "gemm_strided_batched", "gemm_strided_batched_ex",
+           "select", "variants",
            "force_variant", "status_string", "load", "MgemmError", "OP_N", "OP_T", "F32", "F16",
            "BF16"]

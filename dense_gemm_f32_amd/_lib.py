@@ -66,6 +66,9 @@ def load():
     lib.gemm_strided_batched.restype = i32
     lib.gemm_strided_batched.argtypes = [i32, i32, i32, i64, i64, i64, f32, vp, i64, i64, vp, i64,
                                          i64, f32, vp, i64, i64, i64, vp]
+    lib.gemm_strided_batched_ex.restype = i32
+    lib.gemm_strided_batched_ex.argtypes = [i32, i32, i32, i32, i64, i64, i64, f32, vp, i64, i64, vp,
+                                            i64, i64, f32, vp, i64, i64, i64, vp]
     lib.mgemm_status_string.restype = ctypes.c_char_p
     lib.mgemm_status_string.argtypes = [i32]
     lib.mgemm_num_variants.restype = i32
@@ -175,6 +178,24 @@ def gemm_strided_batched(in_dtype, transA, transB, M, N, K, alpha, A, lda, strid
                                      strideA, pb, ldb, strideB, beta, pc, ldc, strideC, batch,
                                      _stream(stream, dev))
     _check(st, "gemm_strided_batched")
+
+
+def gemm_strided_batched_ex(in_dtype, c_dtype, transA, transB, M, N, K, alpha, A, lda, strideA, B,
+                            ldb, strideB, beta, C, ldc, strideC, batch, stream=None):
+    """Strided-batched GEMM with C of type c_dtype: fp32, or the inputs' 16-bit type."""
+    dt = DTYPE_CODES.get(in_dtype, in_dtype)
+    ct = DTYPE_CODES.get(c_dtype, c_dtype)
+    es = ELEM_SIZE[dt]
+    a_rows, a_cols = (K, M) if transA else (M, K)
+    b_rows, b_cols = (N, K) if transB else (K, N)
+    reads = M > 0 and N > 0 and K > 0 and alpha != 0.0 and batch > 0
+    pa, _ = _addr(A, _extent(a_rows, a_cols, lda, strideA, batch) if reads else 0, es, "A")
+    pb, _ = _addr(B, _extent(b_rows, b_cols, ldb, strideB, batch) if reads else 0, es, "B")
+    pc, dev = _addr(C, _extent(M, N, ldc, strideC, batch), ELEM_SIZE.get(ct, 4), "C")
+    st = load().gemm_strided_batched_ex(dt, ct, int(transA), int(transB), M, N, K, alpha, pa, lda,
+                                        strideA, pb, ldb, strideB, beta, pc, ldc, strideC, batch,
+                                        _stream(stream, dev))
+    _check(st, "gemm_strided_batched_ex")
 
 
 # --------------------------------------------------------------------------- introspection

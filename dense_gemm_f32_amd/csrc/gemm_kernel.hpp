@@ -63,14 +63,14 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 struct KernelArgs {
     const void *A;
     const void *B;
-    float *C;
+    void *C;          // fp32, or the inputs' 16-bit type
     int64_t lda, ldb, ldc;
     int64_t strideA, strideB, strideC;
     int M, N, K;
     int tiles_m, tiles_n;
     int group_m;      // tile rows per raster group
     float alpha, beta;
-    int c_vec;        // C pointer/ldc/strideC allow 16-byte accesses
+    int c_vec;        // C pointer/ldc/strideC allow one vector access per 4 elements
     int fast_ok;      // operand tiles addressable with 32-bit byte offsets
 };
 
@@ -829,7 +829,36 @@ struct DmaPath {
 // (attention scores, K = 64) from 5.6 to 6.5 TB/s, with no change on the
 // compute-bound shapes.
 // ---------------------------------------------------------------------------
-template <bool EDGE, int IL_A, int IL_B, int TM, int TN, int WTM, int WTN, int WN>
+template <typename CT, int N>
+struct CVec {
+    typedef CT type __attribute__((ext_vector_type(N)));
+};
+
+// N adjacent elements of C at cp (aligned to N elements when N > 1):
+// v + beta * C_old, rounded to CT (round to nearest even), stored as one
+// non-temporal vector.
+template <typename CT, int N>
+__device__ __forceinline__ void store_c(CT *cp, const float *v, bool use_beta, float beta)
+{
+    if constexpr (N == 1) {
+        const float o = use_beta ? v[0] + beta * (float)*cp : v[0];
+        __builtin_nontemporal_store((CT)o, cp);
+    } else {
+        using V = typename CVec<CT, N>::type;
+        V o;
+        if (use_beta) {
+            const V old = *reinterpret_cast<const V *>(cp);
+#pragma unroll
+            for (int u = 0; u < N; ++u) o[u] = (CT)(v[u] + beta * (float)old[u]);
+        } else {
+#pragma unroll
+            for (int u = 0; u < N; ++u) o[u] = (CT)v[u];
+        }
+        __builtin_nontemporal_store(o, reinterpret_cast<V *>(cp));
+    }
+}
+
+template <bool EDGE, int IL_A, int IL_B, int TM, int TN, int WTM, int WTN, int WN, typename CT>
 __device__ __forceinline__ void epilogue(const KernelArgs &p, int bidx, int m0, int n0,
                                          const f32x16 (&acc)[TM][TN])
 {
@@ -837,7 +866,7 @@ __device__ __forceinline__ void epilogue(const KernelArgs &p, int bidx, int m0, 
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
     const int li = lane & 31, lh = lane >> 5;
-    float *Cb = p.C + (int64_t)bidx * p.strideC;
+    CT *Cb = static_cast<CT *>(p.C) + (int64_t)bidx * p.strideC;
     const bool use_beta = p.beta != 0.0f;
     constexpr bool VCOL = IL_B > 1;  // TN adjacent columns per lane
     const int colv = n0 + wn * WTN + TN * li;
@@ -849,27 +878,18 @@ __device__ __forceinline__ void epilogue(const KernelArgs &p, int bidx, int m0, 
         for (int t = 0; t < TM; ++t) {
             const int row = m0 + wm * WTM + (IL_A == 1 ? 32 * t + ip : TM * ip + t);
             if (EDGE && row >= p.M) continue;
-            float *crow = Cb + (int64_t)row * p.ldc;
+            CT *crow = Cb + (int64_t)row * p.ldc;
             if constexpr (VCOL) {
                 float v[TN];
 #pragma unroll
                 for (int u = 0; u < TN; ++u) v[u] = p.alpha * acc[t][u][r];
-                float *cp = crow + colv;
+                CT *cp = crow + colv;
                 if (vec_store) {
-                    if constexpr (TN == 4) {
-                        f32x4 o = {v[0], v[1], v[2], v[3]};
-                        if (use_beta) o += p.beta * *reinterpret_cast<const f32x4 *>(cp);
-                        __builtin_nontemporal_store(o, reinterpret_cast<f32x4 *>(cp));
-                    } else if constexpr (TN == 2) {
-                        f32x2 o = {v[0], v[1]};
-                        if (use_beta) o += p.beta * *reinterpret_cast<const f32x2 *>(cp);
-                        __builtin_nontemporal_store(o, reinterpret_cast<f32x2 *>(cp));
-                    }
+                    store_c<CT, TN>(cp, v, use_beta, p.beta);
                 } else {
 #pragma unroll
                     for (int u = 0; u < TN; ++u)
-                        if (!EDGE || colv + u < p.N)
-                            __builtin_nontemporal_store(use_beta ? v[u] + p.beta * cp[u] : v[u], cp + u);
+                        if (!EDGE || colv + u < p.N) store_c<CT, 1>(cp + u, v + u, use_beta, p.beta);
                 }
             } else {
 #pragma unroll
@@ -877,7 +897,7 @@ __device__ __forceinline__ void epilogue(const KernelArgs &p, int bidx, int m0, 
                     const int col = n0 + wn * WTN + 32 * u + li;
                     if (EDGE && col >= p.N) continue;
                     const float v = p.alpha * acc[t][u][r];
-                    __builtin_nontemporal_store(use_beta ? v + p.beta * crow[col] : v, crow + col);
+                    store_c<CT, 1>(crow + col, &v, use_beta, p.beta);
                 }
             }
         }
@@ -894,8 +914,10 @@ __device__ __forceinline__ void epilogue(const KernelArgs &p, int bidx, int m0, 
 //   TA, TB     op(A) = A^T, op(B) = B^T
 //   VECOK      A and B allow 16-byte global accesses (enables DmaPath)
 //   PIPE       DmaPath schedule: 1 -> 4 stages of BK/2, 2 -> 2 stages of BK
+//   CT         C element type: float, or T itself (16-bit output)
 // ---------------------------------------------------------------------------
-template <typename T, int BM, int BN, int BK, int WM, int WN, bool TA, bool TB, bool VECOK, int PIPE>
+template <typename T, int BM, int BN, int BK, int WM, int WN, bool TA, bool TB, bool VECOK, int PIPE,
+          typename CT>
 __global__ void __launch_bounds__(WM * WN * 64)
 gemm_kernel(KernelArgs p)
 {
@@ -917,17 +939,18 @@ gemm_kernel(KernelArgs p)
         const bool interior = p.fast_ok && m0 + BM <= p.M && n0 + BN <= p.N && p.K % D::BK == 0;
         if (interior) {
             D::run(p, smem, bidx, m0, n0, acc);
-            epilogue<false, D::IL_A, D::IL_B, TM, TN, WTM, WTN, WN>(p, bidx, m0, n0, acc);
+            epilogue<false, D::IL_A, D::IL_B, TM, TN, WTM, WTN, WN, CT>(p, bidx, m0, n0, acc);
             return;
         }
     }
     R::run(p, smem, bidx, m0, n0, acc);
-    epilogue<true, R::IL_A, R::IL_B, TM, TN, WTM, WTN, WN>(p, bidx, m0, n0, acc);
+    epilogue<true, R::IL_A, R::IL_B, TM, TN, WTM, WTN, WN, CT>(p, bidx, m0, n0, acc);
 }
 
-// C = beta * C over a strided batch (alpha == 0 or K == 0).  beta == 0 writes
-// zeros without reading C.
-__global__ void __launch_bounds__(256) scale_c_kernel(float *C, int M, int N, int64_t ldc,
+// C = beta * C over a strided batch (alpha == 0 or K == 0), in C's own type.
+// beta == 0 writes zeros without reading C.
+template <typename CT>
+__global__ void __launch_bounds__(256) scale_c_kernel(CT *C, int M, int N, int64_t ldc,
                                                       int64_t strideC, int batch, float beta);
 
 }  // namespace mgemm

@@ -8,12 +8,12 @@ const Variant *f32_variants(int *count)
     // Preference order: the first variant that gives at least one workgroup
     // per CU is taken (see the selection in mgemm_api.cpp).
     static const Variant table[] = {
-        MGEMM_VARIANT(float, 0, 256, 256, 32, 4, 2, true, "mgemm_f32_256x256x32_w4x2"),
-        MGEMM_VARIANT(float, 0, 256, 256, 32, 2, 2, true, "mgemm_f32_256x256x32_w2x2"),
-        MGEMM_VARIANT(float, 0, 128, 128, 32, 2, 2, true, "mgemm_f32_128x128x32_w2x2"),
-        MGEMM_VARIANT(float, 0, 128, 128, 32, 2, 2, false, "mgemm_f32_128x128x32_w2x2_u"),
-        MGEMM_VARIANT(float, 0, 64, 64, 32, 2, 2, true, "mgemm_f32_64x64x32_w2x2"),
-        MGEMM_VARIANT(float, 0, 64, 64, 32, 2, 2, false, "mgemm_f32_64x64x32_w2x2_u"),
+        MGEMM_VARIANT_F32(256, 256, 32, 4, 2, true, "mgemm_f32_256x256x32_w4x2"),
+        MGEMM_VARIANT_F32(256, 256, 32, 2, 2, true, "mgemm_f32_256x256x32_w2x2"),
+        MGEMM_VARIANT_F32(128, 128, 32, 2, 2, true, "mgemm_f32_128x128x32_w2x2"),
+        MGEMM_VARIANT_F32(128, 128, 32, 2, 2, false, "mgemm_f32_128x128x32_w2x2_u"),
+        MGEMM_VARIANT_F32(64, 64, 32, 2, 2, true, "mgemm_f32_64x64x32_w2x2"),
+        MGEMM_VARIANT_F32(64, 64, 32, 2, 2, false, "mgemm_f32_64x64x32_w2x2_u"),
     };
     *count = sizeof(table) / sizeof(table[0]);
     return table;

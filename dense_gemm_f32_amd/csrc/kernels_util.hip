@@ -1,9 +1,10 @@
-// C = beta * C for the alpha == 0 and K == 0 cases.
+// C = beta * C for the alpha == 0 and K == 0 cases (fp32 or 16-bit C).
 #include "variants.hpp"
 
 namespace mgemm {
 
-__global__ void __launch_bounds__(256) scale_c_kernel(float *C, int M, int N, int64_t ldc,
+template <typename CT>
+__global__ void __launch_bounds__(256) scale_c_kernel(CT *C, int M, int N, int64_t ldc,
                                                       int64_t strideC, int batch, float beta)
 {
     const int64_t total = (int64_t)batch * M * N;
@@ -12,20 +13,22 @@ __global__ void __launch_bounds__(256) scale_c_kernel(float *C, int M, int N, in
         const int64_t b = e / ((int64_t)M * N);
         const int64_t rem = e - b * M * N;
         const int64_t i = rem / N, j = rem - i * N;
-        float *c = C + b * strideC + i * ldc + j;
-        __builtin_nontemporal_store(beta == 0.0f ? 0.0f : beta * *c, c);
+        CT *c = C + b * strideC + i * ldc + j;
+        __builtin_nontemporal_store((CT)(beta == 0.0f ? 0.0f : beta * (float)*c), c);
     }
 }
 
-hipError_t launch_scale_c(float *C, int M, int N, int64_t ldc, int64_t strideC, int batch,
+hipError_t launch_scale_c(int c_dtype, void *C, int M, int N, int64_t ldc, int64_t strideC, int batch,
                           float beta, hipStream_t s)
 {
     const int64_t total = (int64_t)batch * M * N;
     int64_t blocks = (total + 255) / 256;
     if (blocks > 4096) blocks = 4096;
     void *args[] = {&C, &M, &N, &ldc, &strideC, &batch, &beta};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&scale_c_kernel), dim3((unsigned)blocks),
-                           dim3(256), args, 0, s);
+    const void *fn = c_dtype == 1   ? reinterpret_cast<const void *>(&scale_c_kernel<_Float16>)
+                     : c_dtype == 2 ? reinterpret_cast<const void *>(&scale_c_kernel<__bf16>)
+                                    : reinterpret_cast<const void *>(&scale_c_kernel<float>);
+    return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(256), args, 0, s);
 }
 
 }  // namespace mgemm

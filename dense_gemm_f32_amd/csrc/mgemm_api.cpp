@@ -63,13 +63,14 @@ bool aligned(const void *p, int64_t bytes) { return (reinterpret_cast<uintptr_t>
 // Smallest element span one stored matrix occupies: (rows-1)*ld + cols.
 int64_t span(int64_t rows, int64_t cols, int64_t ld) { return rows == 0 || cols == 0 ? 0 : (rows - 1) * ld + cols; }
 
-mgemm_status validate_and_plan(int dtype, int transA, int transB, int64_t M, int64_t N, int64_t K,
-                               float alpha, const void *A, int64_t lda, int64_t strideA,
+mgemm_status validate_and_plan(int dtype, int c_dtype, int transA, int transB, int64_t M, int64_t N,
+                               int64_t K, float alpha, const void *A, int64_t lda, int64_t strideA,
                                const void *B, int64_t ldb, int64_t strideB, float beta,
-                               const float *C, int64_t ldc, int64_t strideC, int64_t batch,
+                               const void *C, int64_t ldc, int64_t strideC, int64_t batch,
                                Plan *plan)
 {
     if (dtype != MGEMM_F32 && dtype != MGEMM_F16 && dtype != MGEMM_BF16) return MGEMM_INVALID_ARG;
+    if (c_dtype != MGEMM_F32 && c_dtype != dtype) return MGEMM_INVALID_ARG;  // fp32 C, or the inputs' type
     if ((transA != MGEMM_OP_N && transA != MGEMM_OP_T) || (transB != MGEMM_OP_N && transB != MGEMM_OP_T))
         return MGEMM_INVALID_ARG;
     if (M < 0 || N < 0 || K < 0 || batch < 0) return MGEMM_INVALID_ARG;
@@ -87,7 +88,8 @@ mgemm_status validate_and_plan(int dtype, int transA, int transB, int64_t M, int
     const int es = elem_size(dtype);
     const bool writes_c = M > 0 && N > 0 && batch > 0;
     const bool reads_ab = writes_c && K > 0 && alpha != 0.0f;
-    if (writes_c && (C == nullptr || !aligned(C, 4))) return MGEMM_INVALID_ARG;
+    const int ces = elem_size(c_dtype);
+    if (writes_c && (C == nullptr || !aligned(C, ces))) return MGEMM_INVALID_ARG;
     if (reads_ab && (A == nullptr || B == nullptr || !aligned(A, es) || !aligned(B, es)))
         return MGEMM_INVALID_ARG;
 
@@ -99,7 +101,7 @@ mgemm_status validate_and_plan(int dtype, int transA, int transB, int64_t M, int
     KernelArgs &a = plan->args;
     a.A = A;
     a.B = B;
-    a.C = const_cast<float *>(C);
+    a.C = const_cast<void *>(C);
     a.lda = lda;
     a.ldb = ldb;
     a.ldc = ldc;
@@ -111,7 +113,8 @@ mgemm_status validate_and_plan(int dtype, int transA, int transB, int64_t M, int
     a.K = (int)K;
     a.alpha = alpha;
     a.beta = beta;
-    a.c_vec = aligned(C, 16) && ldc % 4 == 0 && (batch == 1 || strideC % 4 == 0);
+    // a lane stores up to 4 adjacent C elements as one vector
+    a.c_vec = aligned(C, 4 * ces) && ldc % 4 == 0 && (batch == 1 || strideC % 4 == 0);
     // Interior tiles address their operands with 32-bit byte offsets from the
     // tile origin: at most 256 rows of the larger leading dimension.
     const int64_t max_ld = lda > ldb ? lda : ldb;
@@ -193,20 +196,22 @@ void fill_info(const Variant &v, int id, mgemm_variant_info *out)
     std::snprintf(out->name, sizeof(out->name), "%s", v.name);
 }
 
-mgemm_status run(int dtype, int transA, int transB, int64_t M, int64_t N, int64_t K, float alpha,
-                 const void *A, int64_t lda, int64_t strideA, const void *B, int64_t ldb,
-                 int64_t strideB, float beta, float *C, int64_t ldc, int64_t strideC,
+mgemm_status run(int dtype, int c_dtype, int transA, int transB, int64_t M, int64_t N, int64_t K,
+                 float alpha, const void *A, int64_t lda, int64_t strideA, const void *B,
+                 int64_t ldb, int64_t strideB, float beta, void *C, int64_t ldc, int64_t strideC,
                  int64_t batch, hipStream_t stream)
 {
     Plan plan;
-    mgemm_status st = validate_and_plan(dtype, transA, transB, M, N, K, alpha, A, lda, strideA, B,
-                                        ldb, strideB, beta, C, ldc, strideC, batch, &plan);
+    mgemm_status st = validate_and_plan(dtype, c_dtype, transA, transB, M, N, K, alpha, A, lda,
+                                        strideA, B, ldb, strideB, beta, C, ldc, strideC, batch, &plan);
     if (st != MGEMM_OK || plan.kind == Plan::NOTHING) return st;
     hipError_t err;
     if (plan.kind == Plan::SCALE) {
-        err = launch_scale_c(C, (int)M, (int)N, ldc, strideC, (int)batch, beta, stream);
+        err = launch_scale_c(c_dtype, C, (int)M, (int)N, ldc, strideC, (int)batch, beta, stream);
     } else {
-        err = plan.var->fn[transA][transB](plan.args, (unsigned)plan.grid, stream);
+        const LaunchFn fn = c_dtype == MGEMM_F32 ? plan.var->fn[transA][transB] : plan.var->fn16[transA][transB];
+        if (fn == nullptr) return MGEMM_INVALID_ARG;
+        err = fn(plan.args, (unsigned)plan.grid, stream);
     }
     return err == hipSuccess ? MGEMM_OK : MGEMM_HIP_ERROR;
 }
@@ -222,24 +227,24 @@ mgemm_status gemm_f32(mgemm_op transA, mgemm_op transB, int64_t M, int64_t N, in
                       float alpha, const float *A, int64_t lda, const float *B, int64_t ldb,
                       float beta, float *C, int64_t ldc, hipStream_t stream)
 {
-    return run(MGEMM_F32, transA, transB, M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C, ldc, 0, 1,
-               stream);
+    return run(MGEMM_F32, MGEMM_F32, transA, transB, M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C,
+               ldc, 0, 1, stream);
 }
 
 mgemm_status gemm_f16(mgemm_op transA, mgemm_op transB, int64_t M, int64_t N, int64_t K,
                       float alpha, const mgemm_f16 *A, int64_t lda, const mgemm_f16 *B,
                       int64_t ldb, float beta, float *C, int64_t ldc, hipStream_t stream)
 {
-    return run(MGEMM_F16, transA, transB, M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C, ldc, 0, 1,
-               stream);
+    return run(MGEMM_F16, MGEMM_F32, transA, transB, M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C,
+               ldc, 0, 1, stream);
 }
 
 mgemm_status gemm_bf16(mgemm_op transA, mgemm_op transB, int64_t M, int64_t N, int64_t K,
                        float alpha, const mgemm_bf16 *A, int64_t lda, const mgemm_bf16 *B,
                        int64_t ldb, float beta, float *C, int64_t ldc, hipStream_t stream)
 {
-    return run(MGEMM_BF16, transA, transB, M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C, ldc, 0, 1,
-               stream);
+    return run(MGEMM_BF16, MGEMM_F32, transA, transB, M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C,
+               ldc, 0, 1, stream);
 }
 
 mgemm_status gemm_strided_batched(mgemm_dtype in_dtype, mgemm_op transA, mgemm_op transB,
@@ -248,8 +253,18 @@ mgemm_status gemm_strided_batched(mgemm_dtype in_dtype, mgemm_op transA, mgemm_o
                                   int64_t strideB, float beta, float *C, int64_t ldc,
                                   int64_t strideC, int64_t batch, hipStream_t stream)
 {
-    return run(in_dtype, transA, transB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C,
-               ldc, strideC, batch, stream);
+    return run(in_dtype, MGEMM_F32, transA, transB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB,
+               beta, C, ldc, strideC, batch, stream);
+}
+
+mgemm_status gemm_strided_batched_ex(mgemm_dtype in_dtype, mgemm_dtype c_dtype, mgemm_op transA,
+                                     mgemm_op transB, int64_t M, int64_t N, int64_t K, float alpha,
+                                     const void *A, int64_t lda, int64_t strideA, const void *B,
+                                     int64_t ldb, int64_t strideB, float beta, void *C, int64_t ldc,
+                                     int64_t strideC, int64_t batch, hipStream_t stream)
+{
+    return run(in_dtype, c_dtype, transA, transB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB,
+               beta, C, ldc, strideC, batch, stream);
 }
 
 const char *mgemm_status_string(mgemm_status s)
@@ -279,8 +294,8 @@ mgemm_status mgemm_select(mgemm_dtype in_dtype, mgemm_op transA, mgemm_op transB
                           int64_t batch, mgemm_variant_info *out, int64_t *grid)
 {
     Plan plan;
-    mgemm_status st = validate_and_plan(in_dtype, transA, transB, M, N, K, alpha, A, lda, strideA,
-                                        B, ldb, strideB, beta, C, ldc, strideC, batch, &plan);
+    mgemm_status st = validate_and_plan(in_dtype, MGEMM_F32, transA, transB, M, N, K, alpha, A, lda,
+                                        strideA, B, ldb, strideB, beta, C, ldc, strideC, batch, &plan);
     if (st != MGEMM_OK) return st;
     if (out) {
         if (plan.kind == Plan::GEMM) {

@@ -17,24 +17,34 @@ struct Variant {
     bool vec;             // needs 16-byte aligned A/B rows (dwordx4 loads)
     int pipe;             // DMA-path schedule (1: 4 stages of bk/2, 2: 2 stages of bk)
     const char *name;
-    LaunchFn fn[2][2];    // [transA][transB]
+    LaunchFn fn[2][2];    // [transA][transB], fp32 C
+    LaunchFn fn16[2][2];  // [transA][transB], C in the inputs' 16-bit type (16-bit tables only)
 };
 
-template <typename T, int BM, int BN, int BK, int WM, int WN, bool TA, bool TB, bool V, int D>
+template <typename T, int BM, int BN, int BK, int WM, int WN, bool TA, bool TB, bool V, int D, typename CT>
 hipError_t launch_gemm(const KernelArgs &a, unsigned grid, hipStream_t s)
 {
     KernelArgs copy = a;
     void *args[] = {&copy};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&gemm_kernel<T, BM, BN, BK, WM, WN, TA, TB, V, D>),
+    return hipLaunchKernel(reinterpret_cast<const void *>(&gemm_kernel<T, BM, BN, BK, WM, WN, TA, TB, V, D, CT>),
                            dim3(grid), dim3(WM * WN * 64), args, 0, s);
 }
 
+#define MGEMM_LAUNCHERS(T, BM, BN, BK, WM, WN, V, D, CT)                                     \
+    {{launch_gemm<T, BM, BN, BK, WM, WN, false, false, V, D, CT>,                            \
+      launch_gemm<T, BM, BN, BK, WM, WN, false, true, V, D, CT>},                            \
+     {launch_gemm<T, BM, BN, BK, WM, WN, true, false, V, D, CT>,                             \
+      launch_gemm<T, BM, BN, BK, WM, WN, true, true, V, D, CT>}}
+
+// fp32 inputs: fp32 C only
+#define MGEMM_VARIANT_F32(BM, BN, BK, WM, WN, V, NAME)                                       \
+    {0, BM, BN, BK, WM, WN, V, 1, NAME, MGEMM_LAUNCHERS(float, BM, BN, BK, WM, WN, V, 1, float), \
+     {{nullptr, nullptr}, {nullptr, nullptr}}}
+
+// 16-bit inputs: fp32 C or C of the input type
 #define MGEMM_VARIANT_D(T, DT, BM, BN, BK, WM, WN, V, D, NAME)                               \
-    {DT, BM, BN, BK, WM, WN, V, D, NAME,                                                     \
-     {{launch_gemm<T, BM, BN, BK, WM, WN, false, false, V, D>,                               \
-       launch_gemm<T, BM, BN, BK, WM, WN, false, true, V, D>},                               \
-      {launch_gemm<T, BM, BN, BK, WM, WN, true, false, V, D>,                                \
-       launch_gemm<T, BM, BN, BK, WM, WN, true, true, V, D>}}}
+    {DT, BM, BN, BK, WM, WN, V, D, NAME, MGEMM_LAUNCHERS(T, BM, BN, BK, WM, WN, V, D, float), \
+     MGEMM_LAUNCHERS(T, BM, BN, BK, WM, WN, V, D, T)}
 
 #define MGEMM_VARIANT(T, DT, BM, BN, BK, WM, WN, V, NAME) MGEMM_VARIANT_D(T, DT, BM, BN, BK, WM, WN, V, 1, NAME)
 
@@ -44,7 +54,7 @@ const Variant *f32_variants(int *count);
 const Variant *f16_variants(int *count);
 const Variant *bf16_variants(int *count);
 
-hipError_t launch_scale_c(float *C, int M, int N, int64_t ldc, int64_t strideC, int batch,
+hipError_t launch_scale_c(int c_dtype, void *C, int M, int N, int64_t ldc, int64_t strideC, int batch,
                           float beta, hipStream_t s);
 
 }  // namespace mgemm

@@ -13,14 +13,16 @@ draw A, then B, then C, each over its whole stored buffer (padding included).
   in the operand type.
 
 The named workloads follow the shapes the pages measure on:
-- 256^3, 4096^3 and 6144^3 SGEMM ("Sgemm [128,128,8]" harness; "cuda11/matmul"
+- 256^3 and 4096^3 SGEMM ("Sgemm [128,128,8]" harness; "cuda11/matmul"
   timing tables);
 - a ragged SGEMM whose sizes are no multiple of any tile, with integer-valued
   operands in {0..99} (the residual-tile example of the CSDN tile-algorithm
   page, which fills with ``rand() % 100``);
 - 16-bit inputs with a float accumulator (WMMA API page, type table);
 - strided-batched QK^T with B stored [n, d] ("cuda11/matmul", section
-  "Pytorch", the einsum 'bhqd,bhkd->bhqk' example).
+  "Pytorch", the einsum 'bhqd,bhkd->bhqk' example), with fp32 C and, as the
+  tutorial's Triton kernel stores its accumulator in C's own type, with a
+  binary16 C.
 """
 from __future__ import annotations
 
@@ -37,7 +39,7 @@ ELEM_SIZE = {"f32": 4, "f16": 2, "bf16": 2}
 
 @dataclasses.dataclass
 class Problem:
-    dtype: str                 # "f32" | "f16" | "bf16" (operand type; C is always fp32)
+    dtype: str                 # "f32" | "f16" | "bf16" (operand type)
     M: int
     N: int
     K: int
@@ -58,6 +60,7 @@ class Problem:
     strideB: Optional[int] = None
     strideC: Optional[int] = None
     pad_value: Optional[float] = None  # fill for padding beyond the logical matrix
+    c_dtype: str = "f32"       # C's type: "f32", or the operand type for 16-bit output
 
     def __post_init__(self):
         a_rows, a_cols = (self.K, self.M) if self.transA else (self.M, self.K)
@@ -103,6 +106,11 @@ class Problem:
         """c in max|err| <= c * sqrt(K) * max|ref| (fp32: 1e-5, 16-bit: 2e-3)."""
         return 1e-5 if self.dtype == "f32" else 2e-3
 
+    def output_rounding(self) -> float:
+        """Relative rounding of the stored C: half an ulp of its type (0 for fp32,
+        which the accumulator itself is)."""
+        return {"f32": 0.0, "f16": 2.0 ** -11, "bf16": 2.0 ** -8}[self.c_dtype]
+
 
 def _draw(gen, n, dist, lo, hi):
     if dist == "uniform":
@@ -126,7 +134,7 @@ def _logical_mask(total, batch, rows, cols, ld, stride):
 
 
 def make_inputs(p: Problem):
-    """CPU torch tensors (flat) A, B (operand dtype) and C0 (fp32, or None when beta == 0
+    """CPU torch tensors (flat) A, B (operand dtype) and C0 (C's type, or None when beta == 0
     and no C distribution was asked for)."""
     gen = torch.Generator()
     gen.manual_seed(p.seed)
@@ -143,6 +151,8 @@ def make_inputs(p: Problem):
     if p.beta != 0.0 or p.c_dist is not None:
         cd = p.c_dist or p.dist
         C0 = _draw(gen, p.c_elems, cd, p.int_lo, p.int_hi)
+        if p.c_dtype != "f32":
+            C0 = C0.to(TORCH_DTYPE[p.c_dtype])
     return bufs[0], bufs[1], C0
 
 
@@ -185,6 +195,14 @@ def qkt_batched() -> Problem:
                    dist="normal", seed=1005)
 
 
+def qkt_batched_f16_out() -> Problem:
+    """The attention-score batch with a binary16 C (fp32 accumulate, rounded on store)."""
+    p = qkt_batched()
+    p.c_dtype = "f16"
+    p.seed = 1006
+    return p
+
+
 WORKLOADS = {
     "sgemm_256": sgemm_256,
     "sgemm_4096": sgemm_4096,
@@ -192,6 +210,7 @@ WORKLOADS = {
     "gemm_bf16_8192": lambda: gemm16_8192("bf16"),
     "gemm_f16_8192": lambda: gemm16_8192("f16"),
     "qkt_batched": qkt_batched,
+    "qkt_batched_f16_out": qkt_batched_f16_out,
 }
 
 

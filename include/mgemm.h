@@ -121,6 +121,29 @@ mgemm_status gemm_strided_batched(mgemm_dtype in_dtype, mgemm_op transA, mgemm_o
                                   float beta, float *C, int64_t ldc, int64_t strideC,
                                   int64_t batch, hipStream_t stream);
 
+/*
+ * Strided-batched GEMM with a choice of C type: as gemm_strided_batched, but
+ * C (read when beta != 0, and written) has type c_dtype, which is either
+ * MGEMM_F32 or the inputs' own 16-bit type (f16 -> f16, bf16 -> bf16; fp32
+ * inputs take fp32 C only).  Accumulation stays fp32; alpha*acc + beta*C is
+ * formed in fp32 and rounded to c_dtype to nearest, ties to even.
+ * The "cuda11/matmul" tutorial (dlog.com.cn), section "Triton", converts its
+ * fp32 accumulator to C's element type when storing; the WMMA API page's
+ * fragment description lets the C/D matrices be __half.  A 16-bit C halves
+ * the output traffic of store-bound shapes (attention scores with K = 64).
+ *   C      device pointer, aligned to c_dtype's size; ldc, strideC in
+ *          elements of c_dtype.
+ * Errors: as gemm_strided_batched, plus MGEMM_INVALID_ARG for any other
+ * c_dtype.
+ */
+mgemm_status gemm_strided_batched_ex(mgemm_dtype in_dtype, mgemm_dtype c_dtype,
+                                     mgemm_op transA, mgemm_op transB,
+                                     int64_t M, int64_t N, int64_t K, float alpha,
+                                     const void *A, int64_t lda, int64_t strideA,
+                                     const void *B, int64_t ldb, int64_t strideB,
+                                     float beta, void *C, int64_t ldc, int64_t strideC,
+                                     int64_t batch, hipStream_t stream);
+
 /* Human-readable text for a status code (static storage). */
 const char *mgemm_status_string(mgemm_status s);
 

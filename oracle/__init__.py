@@ -68,12 +68,50 @@ def _load():
     lib.oracle_f16_to_double.argtypes = [ctypes.c_uint16]
     lib.oracle_bf16_to_double.restype = dbl
     lib.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
+    lib.oracle_double_to_f16.restype = ctypes.c_uint16
+    lib.oracle_double_to_f16.argtypes = [dbl]
+    lib.oracle_double_to_bf16.restype = ctypes.c_uint16
+    lib.oracle_double_to_bf16.argtypes = [dbl]
+    lib.oracle_round16.restype = ctypes.c_int
+    lib.oracle_round16.argtypes = [ctypes.c_int, vp, vp, i64]
     lib.oracle_set_threads.restype = None
     lib.oracle_set_threads.argtypes = [ctypes.c_int]
     lib.oracle_max_threads.restype = ctypes.c_int
     lib.oracle_max_threads.argtypes = []
     _lib = lib
     return lib
+
+
+def round16(dtype, x):
+    """Round float64 values to binary16 ("f16") or bfloat16 ("bf16"), to nearest
+    with ties to even; returns the uint16 bit patterns (same shape)."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(x.shape, dtype=np.uint16)
+    if _load().oracle_round16(DTYPES[dtype], x.ctypes.data, out.ctypes.data, x.size) != 0:
+        raise ValueError("round16: dtype must be f16 or bf16")
+    return out
+
+
+def decode16(dtype, bits):
+    """float64 values of 16-bit patterns (binary16 or bfloat16)."""
+    bits = np.ascontiguousarray(bits, dtype=np.uint16)
+    fn = f16_to_double if dtype == "f16" else bf16_to_double
+    flat = np.array([fn(int(b)) for b in bits.ravel()], dtype=np.float64) if bits.size < 4096 else None
+    if flat is None:
+        # vectorised through a lookup table of all 65536 patterns
+        table = _decode_table(dtype)
+        return table[bits]
+    return flat.reshape(bits.shape)
+
+
+_TABLES = {}
+
+
+def _decode_table(dtype):
+    if dtype not in _TABLES:
+        fn = f16_to_double if dtype == "f16" else bf16_to_double
+        _TABLES[dtype] = np.array([fn(b) for b in range(65536)], dtype=np.float64)
+    return _TABLES[dtype]
 
 
 def set_threads(n: int) -> None:

@@ -87,6 +87,44 @@ double oracle_bf16_to_double(uint16_t h)
     return sign ? -v : v;
 }
 
+/* Nearest value of a binary format with `fbits` fraction bits, minimum
+ * normal exponent `emin` and maximum exponent `emax` (IEEE 754
+ * roundTiesToEven), as its bit pattern.  Values past the largest finite
+ * number by half an ulp or more become infinity; NaN becomes a quiet NaN.
+ * Used for 16-bit C: the result alpha*acc + beta*C converted to C's element
+ * type on store ("cuda11/matmul" tutorial, section "Triton"). */
+static uint16_t round_to_format(double x, int fbits, int ebits, int emin, int emax)
+{
+    const uint16_t sign = signbit(x) ? 0x8000 : 0;
+    const uint16_t inf = (uint16_t)(((1u << ebits) - 1) << fbits);
+    if (isnan(x)) return (uint16_t)(inf | (1u << (fbits - 1)));
+    const double a = fabs(x);
+    if (a == 0.0) return sign;
+    int e;
+    frexp(a, &e);                          /* a in [2^(e-1), 2^e) */
+    const int q = (e - 1 < emin ? emin : e - 1) - fbits;  /* exponent of one ulp there */
+    const double v = ldexp(rint(ldexp(a, -q)), q);        /* rint: nearest, ties to even */
+    if (v >= ldexp(1.0, emax + 1)) return (uint16_t)(sign | inf);
+    if (v < ldexp(1.0, emin))              /* subnormal: fraction = v / 2^(emin - fbits) */
+        return (uint16_t)(sign | (uint16_t)ldexp(v, fbits - emin));
+    frexp(v, &e);                          /* v = 1.f * 2^(e-1) */
+    const uint16_t frac = (uint16_t)(ldexp(v, fbits - (e - 1)) - ldexp(1.0, fbits));
+    return (uint16_t)(sign | (uint16_t)((e - 1 + emax) << fbits) | frac);  /* bias = emax */
+}
+
+uint16_t oracle_double_to_f16(double x) { return round_to_format(x, 10, 5, -14, 15); }
+
+uint16_t oracle_double_to_bf16(double x) { return round_to_format(x, 7, 8, -126, 127); }
+
+/* Element-wise rounding of n values to dtype (ORACLE_F16 or ORACLE_BF16). */
+int oracle_round16(int dtype, const double *in, uint16_t *out, int64_t n)
+{
+    if (dtype != ORACLE_F16 && dtype != ORACLE_BF16) return ORACLE_BAD_ARG;
+    for (int64_t e = 0; e < n; ++e)
+        out[e] = dtype == ORACLE_F16 ? oracle_double_to_f16(in[e]) : oracle_double_to_bf16(in[e]);
+    return ORACLE_OK;
+}
+
 /* Element (r, c) of a row-major matrix with leading dimension ld, widened. */
 static double load_elem(int dtype, const void *base, int64_t r, int64_t c, int64_t ld)
 {

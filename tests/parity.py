@@ -13,7 +13,7 @@ from dense_gemm_f32_amd import workloads as wl
 
 DEV = torch.device("cuda:0")
 GUARD = 64                    # sentinel elements before and after C
-SENTINEL = -12345.5
+SENTINEL = -1920.0            # exact in fp32, binary16 and bfloat16
 
 
 def log(msg):
@@ -30,18 +30,23 @@ class Run:
         self.dA = self.A.to(DEV)
         self.dB = self.B.to(DEV)
         n = p.c_elems
-        c = torch.full((n + 2 * GUARD,), SENTINEL, dtype=torch.float32)
+        c = torch.full((n + 2 * GUARD,), SENTINEL, dtype=wl.TORCH_DTYPE[p.c_dtype])
         if self.C0 is not None:
             c[GUARD:GUARD + n] = self.C0
         elif c_fill is not None:
             c[GUARD:GUARD + n] = c_fill
-        self.c_init = c.numpy().copy()
+        self.c_init = c.float().numpy().copy()
         self.dCbuf = c.to(DEV)
         self.dC = self.dCbuf[GUARD:GUARD + n]
 
     def launch(self, stream=None):
         p = self.p
-        if p.batch == 1 and p.strideA == p.a_rows * p.lda and not getattr(p, "force_batched", False):
+        if p.c_dtype != "f32":
+            mg.gemm_strided_batched_ex(p.dtype, p.c_dtype, int(p.transA), int(p.transB), p.M, p.N,
+                                       p.K, p.alpha, self.dA, p.lda, p.strideA, self.dB, p.ldb,
+                                       p.strideB, p.beta, self.dC, p.ldc, p.strideC, p.batch,
+                                       stream=stream)
+        elif p.batch == 1 and p.strideA == p.a_rows * p.lda and not getattr(p, "force_batched", False):
             fn = {"f32": mg.gemm_f32, "f16": mg.gemm_f16, "bf16": mg.gemm_bf16}[p.dtype]
             fn(int(p.transA), int(p.transB), p.M, p.N, p.K, p.alpha, self.dA, p.lda, self.dB,
                p.ldb, p.beta, self.dC, p.ldc, stream=stream)
@@ -54,7 +59,7 @@ class Run:
         """(batch, M, N) fp32 result, after checking the guard band and padding."""
         torch.cuda.synchronize()
         p = self.p
-        buf = self.dCbuf.cpu().numpy()
+        buf = self.dCbuf.float().cpu().numpy()
         assert np.all(buf[:GUARD] == SENTINEL) and np.all(buf[GUARD + p.c_elems:] == SENTINEL), \
             "write outside C"
         c = buf[GUARD:GUARD + p.c_elems]
@@ -74,7 +79,7 @@ class Run:
         p = self.p
         return (p.dtype, p.transA, p.transB, p.M, p.N, p.K, p.alpha, wl.to_numpy_operand(self.A),
                 p.lda, wl.to_numpy_operand(self.B), p.ldb, p.beta,
-                None if self.C0 is None else self.C0.numpy(), p.ldc)
+                None if self.C0 is None else self.C0.float().numpy(), p.ldc)
 
     def oracle_full(self):
         p = self.p
@@ -104,13 +109,22 @@ def sample_positions(p: wl.Problem, n_random=20000, seed=0, tile=256):
     return np.concatenate(bs), np.concatenate(is_), np.concatenate(js)
 
 
+def expected_exact(p: wl.Problem, ref):
+    """What an exact accumulation stores: the oracle's value, rounded to C's type
+    (to nearest, ties to even) when C is 16-bit."""
+    if p.c_dtype == "f32":
+        return ref
+    return oracle.decode16(p.c_dtype, oracle.round16(p.c_dtype, ref))
+
+
 def check_tolerance(got, ref, p: wl.Problem, what=""):
-    """max|err| <= c*sqrt(K)*max|ref| with c = 1e-5 (fp32) or 2e-3 (16-bit)."""
+    """max|err| <= (c*sqrt(K) + u)*max|ref| with c = 1e-5 (fp32 inputs) or 2e-3
+    (16-bit inputs) and u the rounding of a 16-bit C (half an ulp; 0 for fp32 C)."""
     got = np.asarray(got, np.float64)
     assert not np.isnan(got).any(), f"{what}: NaN in output"
     err = float(np.max(np.abs(got - ref))) if ref.size else 0.0
     scale = float(np.max(np.abs(ref))) if ref.size else 0.0
-    tol = p.tolerance_coeff() * np.sqrt(max(p.K, 1)) * scale
+    tol = (p.tolerance_coeff() * np.sqrt(max(p.K, 1)) + p.output_rounding()) * scale
     log(f"  {what}: max|err|={err:.3e} tol={tol:.3e} err/tol={err / tol if tol else 0:.2e}")
     assert err <= tol, f"{what}: max|err| {err} > {tol}"
     return err, tol

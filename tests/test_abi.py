@@ -33,7 +33,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ("gemm_f32", "gemm_f16", "gemm_bf16", "gemm_strided_batched",
-                 "mgemm_status_string", "mgemm_select", "mgemm_force_variant"):
+                 "gemm_strided_batched_ex", "mgemm_status_string", "mgemm_select",
+                 "mgemm_force_variant"):
         assert want in names
 
 
@@ -171,6 +172,24 @@ def test_entry_points_reject_bad_arguments_without_a_gpu():
                                     ALIGNED, 4, 15, 2, None) == 1
     # nothing to do: OK with no launch
     assert lib.gemm_f32(0, 0, 0, 4, 4, 1.0, None, 4, None, 4, 0.0, None, 4, None) == 0
+
+
+def test_c_type_rules_without_a_gpu():
+    lib = mg.load()
+    ex = lib.gemm_strided_batched_ex
+
+    def call(in_dt, c_dt, C=ALIGNED, ldc=4, M=4):
+        return ex(in_dt, c_dt, 0, 0, M, 4, 4, 1.0, ALIGNED, 8, 0, ALIGNED, 8, 0, 0.0, C, ldc, 0, 1,
+                  None)
+    # C is fp32 or the inputs' own 16-bit type; nothing else
+    assert call(0, 1) == 1 and call(0, 2) == 1          # fp32 inputs -> 16-bit C
+    assert call(1, 2) == 1 and call(2, 1) == 1          # f16 <-> bf16 mix
+    assert call(1, 7) == 1
+    # a 16-bit C needs 2-byte alignment only; an odd address is rejected
+    assert call(1, 1, C=ALIGNED + 1) == 1
+    # empty problems return OK without touching the GPU, for every legal pairing
+    for in_dt, c_dt in ((0, 0), (1, 0), (1, 1), (2, 0), (2, 2)):
+        assert call(in_dt, c_dt, M=0) == 0
 
 
 def test_binding_refuses_host_tensors_and_short_buffers():

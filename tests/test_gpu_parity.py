@@ -20,7 +20,7 @@ pytestmark = pytest.mark.gpu
 
 if torch.cuda.is_available():
     import dense_gemm_f32_amd as mg
-    from parity import Run, check_exact, check_tolerance, log, sample_positions
+    from parity import Run, check_exact, check_tolerance, expected_exact, log, sample_positions
 
 
 @pytest.fixture(autouse=True)
@@ -31,23 +31,24 @@ def _auto_variant():
 
 
 def full_check(p, exact=False, c_fill=None, what=""):
-    log(f"[{what}] {p.dtype} tA={int(p.transA)} tB={int(p.transB)} M={p.M} N={p.N} K={p.K} "
-        f"batch={p.batch} lda={p.lda} ldb={p.ldb} ldc={p.ldc} alpha={p.alpha} beta={p.beta} "
-        f"dist={p.dist} seed={p.seed}")
+    log(f"[{what}] {p.dtype}->{p.c_dtype} tA={int(p.transA)} tB={int(p.transB)} M={p.M} N={p.N} "
+        f"K={p.K} batch={p.batch} lda={p.lda} ldb={p.ldb} ldc={p.ldc} alpha={p.alpha} "
+        f"beta={p.beta} dist={p.dist} seed={p.seed}")
     r = Run(p, c_fill=c_fill)
     r.launch()
     got = r.result()
     ref = r.oracle_full()
     if exact:
-        check_exact(got, ref, what)
+        check_exact(got, expected_exact(p, ref), what)
     else:
         check_tolerance(got, ref, p, what)
     return got
 
 
 def sampled_check(p, exact=False, what="", n_random=20000):
-    log(f"[{what}] {p.dtype} tA={int(p.transA)} tB={int(p.transB)} M={p.M} N={p.N} K={p.K} "
-        f"batch={p.batch} alpha={p.alpha} beta={p.beta} dist={p.dist} seed={p.seed} (sampled)")
+    log(f"[{what}] {p.dtype}->{p.c_dtype} tA={int(p.transA)} tB={int(p.transB)} M={p.M} N={p.N} "
+        f"K={p.K} batch={p.batch} alpha={p.alpha} beta={p.beta} dist={p.dist} seed={p.seed} "
+        f"(sampled)")
     info, grid = mg.select(p.dtype, int(p.transA), int(p.transB), p.M, p.N, p.K, p.alpha,
                            16, p.lda, p.strideA, 16, p.ldb, p.strideB, p.beta, 16, p.ldc,
                            p.strideC, p.batch)
@@ -59,7 +60,7 @@ def sampled_check(p, exact=False, what="", n_random=20000):
     ref = r.oracle_elems(b, i, j)
     vals = got[b, i, j]
     if exact:
-        check_exact(vals, ref, what)
+        check_exact(vals, expected_exact(p, ref), what)
     else:
         check_tolerance(vals, ref, p, what)
     assert not np.isnan(got).any()
@@ -214,6 +215,56 @@ def test_qkt_batched():
     p = wl.qkt_batched()
     sampled_check(p, what="QK^T 128 x 1024x1024x64 fp16")
     sampled_check(wl.int_shadow(p, -8, 8), exact=True, what="QK^T int shadow")
+
+
+def test_qkt_batched_f16_out():
+    p = wl.qkt_batched_f16_out()
+    sampled_check(p, what="QK^T 128 x 1024x1024x64 fp16 -> fp16 C")
+    sampled_check(wl.int_shadow(p, -8, 8), exact=True, what="QK^T -> fp16 C, int shadow")
+
+
+# ------------------------------------------------------------------ 16-bit C output
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_c16_every_variant_every_transpose(dtype):
+    # C in the inputs' 16-bit type: interior (LDS-DMA) and edge tiles; integer
+    # inputs accumulate exactly in fp32, so the stored value is that exact sum
+    # rounded to nearest-even, bit for bit (most sums are not representable)
+    for v in variants_of(dtype):
+        mg.force_variant(dtype, v["id"])
+        aligned = not v["name"].endswith("_u")
+        bm, bn, bk = v["block_m"], v["block_n"], v["block_k"]
+        M, N, K = 2 * bm + 17, 2 * bn + 9, 4 * bk
+        for tA, tB in itertools.product((False, True), repeat=2):
+            a_cols = M if tA else K
+            b_cols = K if tB else N
+            base = wl.Problem(dtype, M, N, K, transA=tA, transB=tB, c_dtype=dtype,
+                              lda=_round8(a_cols) if aligned else a_cols + 1,
+                              ldb=_round8(b_cols) if aligned else b_cols + 1,
+                              alpha=1.5, beta=0.5, dist="normal", c_dist="uniform", seed=51)
+            _assert_selected(base, v)
+            full_check(base, what=f"{v['name']} -> {dtype} C, float")
+            full_check(wl.int_shadow(base, -20, 20), exact=True, what=f"{v['name']} -> {dtype} C, int")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_c16_odd_ldc_padding_untouched(dtype):
+    # ldc not a multiple of 4: element stores; the padding keeps its NaNs
+    for tA, tB in itertools.product((False, True), repeat=2):
+        p = wl.Problem(dtype, 300, 277, 192, transA=tA, transB=tB, c_dtype=dtype, ldc=277 + 3,
+                       dist="int", int_lo=-20, int_hi=20, pad_value=float("nan"), seed=52)
+        full_check(p, exact=True, c_fill=float("nan"), what=f"-> {dtype} C, ldc odd")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_c16_quick_returns_scale_c(dtype):
+    for alpha, K in ((0.0, 64), (1.0, 0)):
+        p = wl.Problem(dtype, 70, 90, K, alpha=alpha, beta=-1.25, c_dtype=dtype, dist="int",
+                       int_lo=-30, int_hi=30, c_dist="uniform", seed=53)
+        full_check(p, exact=True, what=f"-> {dtype} C, alpha={alpha} K={K}")
+    p = wl.Problem(dtype, 70, 90, 0, beta=0.0, c_dtype=dtype, seed=54)
+    got = full_check(p, exact=True, c_fill=float("nan"), what=f"-> {dtype} C, beta=0 K=0")
+    assert not np.isnan(got).any()
 
 
 # ------------------------------------------------------------------ shapes from the pages

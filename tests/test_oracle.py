@@ -256,6 +256,74 @@ def test_elems_matches_full_output_bitwise():
     assert np.array_equal(el, full[b, i, j])
 
 
+def _finite_positive(decoded):
+    """Sorted positive finite values of a 16-bit format and their bit patterns."""
+    bits = np.arange(1, 0x8000, dtype=np.uint16)
+    vals = decoded(bits)
+    keep = np.isfinite(vals)
+    return vals[keep], bits[keep]
+
+
+def _round_cases(vals, rng):
+    mids = (vals[:-1] + vals[1:]) / 2          # exact ties
+    return np.concatenate([
+        vals, -vals, mids, -mids, np.nextafter(mids, 0), np.nextafter(mids, np.inf),
+        rng.standard_normal(20000) * 10.0 ** rng.integers(-45, 40, 20000),
+        [0.0, -0.0, vals[-1] * 1.001, vals[-1] * 2, vals[0] / 2, vals[0] / 2 * 1.0001, vals[0] / 3]])
+
+
+def test_round_to_f16_matches_numpy_conversion():
+    # binary16 output rounding: numpy's float64 -> float16 conversion rounds to nearest even
+    rng = np.random.default_rng(21)
+    vals, _ = _finite_positive(lambda b: b.view(np.float16).astype(np.float64))
+    x = _round_cases(vals, rng)
+    x = x[np.abs(x) < 1e6]
+    got = oracle.round16("f16", x)
+    with np.errstate(over="ignore"):
+        want = x.astype(np.float16).view(np.uint16)
+    assert np.array_equal(got, want)
+    # the ties include both directions, so truncation would fail this pin
+    mids = (vals[:-1] + vals[1:]) / 2
+    assert np.any(oracle.round16("f16", mids) == np.arange(2, 0x7c00, dtype=np.uint16)[:mids.size])
+
+
+def test_round_to_bf16_matches_brute_force_nearest():
+    # bfloat16 output rounding against the nearest representable value found by
+    # search over every finite pattern (decoded by torch), ties to the even pattern
+    rng = np.random.default_rng(22)
+    dec = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).double().numpy()
+    vals, bits = _finite_positive(dec)
+    order = np.argsort(vals)
+    vals, bits = vals[order], bits[order]
+    x = _round_cases(vals, rng)
+    a = np.abs(x)
+    ulp_top = vals[-1] - vals[-2]
+    hi = np.searchsorted(vals, a)               # first value >= a
+    want = np.empty(x.size, np.uint16)
+    for e, (ae, h) in enumerate(zip(a, hi)):
+        if ae == 0:
+            w = 0
+        elif ae >= vals[-1] + ulp_top / 2:
+            w = 0x7f80                           # past the top by half an ulp: infinity
+        elif h == 0:                             # below the smallest subnormal
+            w = bits[0] if ae > vals[0] / 2 else (bits[0] if (ae == vals[0] / 2 and bits[0] % 2 == 0) else 0)
+        elif h == vals.size:
+            w = bits[-1]
+        else:
+            lo_v, hi_v = vals[h - 1], vals[h]
+            d_lo, d_hi = ae - lo_v, hi_v - ae
+            if d_lo < d_hi:
+                w = bits[h - 1]
+            elif d_hi < d_lo:
+                w = bits[h]
+            else:
+                w = bits[h - 1] if bits[h - 1] % 2 == 0 else bits[h]
+        want[e] = w | (0x8000 if np.signbit(x[e]) else 0)
+    got = oracle.round16("bf16", x)
+    bad = np.flatnonzero(got != want)
+    assert bad.size == 0, (x[bad[:5]], got[bad[:5]], want[bad[:5]])
+
+
 def test_thread_count_changes_no_bit():
     p = wl.Problem("bf16", 67, 45, 129, transA=True, alpha=0.75, beta=-2.0, dist="normal",
                    c_dist="uniform", seed=9)
