@@ -8,8 +8,8 @@ max of single launches as well), and the CPU oracle timed on bounded samples.
 
 Usage:
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-secondary]
-  python bench.py --profile-case NAME [--launches N] [--warmup W]
-                                   (launches of one workload, for rocprofv3)
+  python bench.py --profile-case NAME [--launches N]
+                                   (30 warm-up + N launches of one workload, for rocprofv3)
   python bench.py --copy-probe     (plain 256 MiB copies: FETCH/WRITE_SIZE calibration)
   python bench.py --summarize-profiles DIR   (profiles/ summaries from rocprofv3 CSVs)
 
@@ -57,6 +57,7 @@ UTIL_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX
                  "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
 N_SIMD = 256 * 4
 N_XCD = 8
+PROFILE_WARMUP = 30   # launches before the profiled ones, as in the timed bench
 
 
 def log(msg):
@@ -144,7 +145,7 @@ def summarize_case(case, d, copy_dir):
     kname = info["name"]
     filt = "gemm_kernel"   # demangled for fp32; 16-bit instances stay mangled
     durs = _dispatch_durations(os.path.join(d, "trace"), filt)
-    timed = durs[5:] if len(durs) > 5 else durs   # --profile-case runs 5 warmup launches first
+    timed = durs[PROFILE_WARMUP:] if len(durs) > PROFILE_WARMUP else durs  # after the warm-up
     fetch_v, _ = _counters(os.path.join(d, "fetch"), filt)
     write_v, _ = _counters(os.path.join(d, "write"), filt)
     util_v, util_d = _counters(os.path.join(d, "util"), filt)
@@ -465,7 +466,8 @@ def main():
         summarize_profiles(args.summarize_profiles)
         return
     if args.profile_case:
-        profile_case(args.profile_case, args.launches, 5 if args.warmup is None else args.warmup)
+        profile_case(args.profile_case, args.launches,
+                     PROFILE_WARMUP if args.warmup is None else args.warmup)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); a GEMM shards by "
