@@ -20,6 +20,7 @@ pytestmark = pytest.mark.gpu
 
 if torch.cuda.is_available():
     import dense_gemm_f32_amd as mg
+    import oracle
     from parity import Run, check_exact, check_tolerance, expected_exact, log, sample_positions
 
 
@@ -318,6 +319,50 @@ def test_minimum_sizes():
         for dt in ("f32", "f16", "bf16"):
             full_check(wl.Problem(dt, M, N, K, dist="int", int_lo=-9, int_hi=9, seed=23),
                        exact=True, what="tiny")
+
+
+def test_leading_dimensions_beyond_32bit_tile_offsets():
+    # with a leading dimension past 2^31 / (257 * element size), 257 rows no longer
+    # fit 32-bit byte offsets from a tile origin: interior tiles must take the
+    # 64-bit-addressed register path and still be exact
+    p = wl.Problem("f32", 300, 260, 48, ldb=(1 << 21) + 64, dist="int", int_lo=-9, int_hi=9,
+                   seed=27)
+    full_check(p, exact=True, what="fp32, ldb 2^21+64")
+    p = wl.Problem("bf16", 300, 260, 32, transA=True, lda=(1 << 22) + 64, dist="int", int_lo=-9,
+                   int_hi=9, seed=28)
+    full_check(p, exact=True, what="bf16, A^T, lda 2^22+64")
+
+
+def test_output_beyond_2_31_elements():
+    # C with more than 2^31 elements (8.6 GB): row * ldc and batch * strideC offsets
+    # must be 64-bit; checked on every element of the rows past index 2^31 that we
+    # sample, against the oracle element by element
+    for (M, N, K, batch) in ((65600, 32768, 32, 1), (32768, 32768, 16, 3)):
+        p = wl.Problem("bf16", M, N, K, transB=True, batch=batch, dist="int", int_lo=-4, int_hi=4,
+                       seed=29)
+        log(f"[>2^31 C] bf16 M={M} N={N} K={K} batch={batch} C elements {p.c_elems}")
+        A, B, _ = wl.make_inputs(p)
+        dA, dB = A.cuda(), B.cuda()
+        dC = torch.full((p.c_elems,), float("nan"), device="cuda")
+        mg.gemm_strided_batched("bf16", 0, 1, M, N, K, 1.0, dA, p.lda, p.strideA, dB, p.ldb,
+                                p.strideB, 0.0, dC, p.ldc, p.strideC, batch)
+        torch.cuda.synchronize()
+        rng = np.random.default_rng(5)
+        last = batch - 1
+        rows = np.array([M - 1, M - 2, (1 << 31) // N if batch == 1 else M // 2])
+        bs = np.concatenate([np.full(N, last)] * 3 + [rng.integers(0, batch, 4000)])
+        is_ = np.concatenate([np.full(N, r) for r in rows] + [rng.integers(0, M, 4000)])
+        js = np.concatenate([np.arange(N)] * 3 + [rng.integers(0, N, 4000)])
+        flat = torch.from_numpy(bs * p.strideC + is_ * p.ldc + js).cuda()
+        got = dC[flat].cpu().numpy().astype(np.float64)
+        assert (bs * p.strideC + is_ * p.ldc + js).max() >= (1 << 31)
+        ref = oracle.gemm_elems("bf16", False, True, M, N, K, 1.0, wl.to_numpy_operand(A), p.lda,
+                                wl.to_numpy_operand(B), p.ldb, 0.0, None, p.ldc, bs, is_, js,
+                                batch=batch, strideA=p.strideA, strideB=p.strideB,
+                                strideC=p.strideC)
+        check_exact(got, ref, f"C past 2^31 elements, batch={batch}")
+        del dA, dB, dC
+        torch.cuda.empty_cache()
 
 
 def test_broadcast_operands_in_batches():
