@@ -43,16 +43,17 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-PEAK_TFLOPS = {"f32": 157.3, "f16": 2516.6, "bf16": 2516.6}   # MI355X dense matrix peaks
+PEAK_TFLOPS = {"f32": 157.3, "f16": 2516.6, "bf16": 2516.6,     # MI355X dense matrix peaks
+               "i8": 5000.0}                                     # (int8: TOP/s)
 PEAK_HBM_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 COPY_PROBE_BYTES = 256 << 20
 PRIMARY = "sgemm_4096"
 CASES = ("sgemm_256", "sgemm_4096", "sgemm_ragged", "gemm_bf16_8192", "gemm_f16_8192",
-         "qkt_batched", "qkt_batched_f16_out")
+         "qkt_batched", "qkt_batched_f16_out", "gemm_i8_8192")
 HBM_BOUND = ("qkt_batched", "qkt_batched_f16_out")
 MOPS_COUNTER = {"f32": "SQ_INSTS_VALU_MFMA_MOPS_F32", "f16": "SQ_INSTS_VALU_MFMA_MOPS_F16",
-                "bf16": "SQ_INSTS_VALU_MFMA_MOPS_BF16"}
+                "bf16": "SQ_INSTS_VALU_MFMA_MOPS_BF16", "i8": "SQ_INSTS_VALU_MFMA_MOPS_I8"}
 UTIL_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE",
                  "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
 N_SIMD = 256 * 4
@@ -404,7 +405,8 @@ def cpu_baseline(budget_s=15.0):
            "sample": f"first {r2} of {p.M} output rows of the same {p.M}x{p.N}x{p.K} fp32 GEMM "
                      f"({flop / 1e9:.1f} GFLOP, fp64 accumulation, {t2:.1f} s)"}
     samples = {"sgemm_256": {}, "sgemm_ragged": {}, "gemm_bf16_8192": {"rows": threads},
-               "gemm_f16_8192": {"rows": threads}, "qkt_batched": {"batches": 2}}
+               "gemm_f16_8192": {"rows": threads}, "qkt_batched": {"batches": 2},
+               "qkt_batched_f16_out": {"batches": 2}, "gemm_i8_8192": {"rows": threads}}
     per = {}
     for name, kw in samples.items():
         q = wl.WORKLOADS[name]()

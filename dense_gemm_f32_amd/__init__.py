@@ -10,7 +10,7 @@ provides device memory and streams.  ``torch_ops`` maps torch tensors
 (row-major or transposed views, batch strides) onto the same entry points:
 mm, bmm, matmul and attention_scores.
 """
-from ._lib import (BF16, F16, F32, OP_N, OP_T, MgemmError, force_variant, gemm_bf16, gemm_f16,
+from ._lib import (BF16, F16, F32, I8, I32, OP_N, OP_T, MgemmError, force_variant, gemm_bf16, gemm_f16,
                    gemm_f32, gemm_strided_batched, gemm_strided_batched_ex, load, select,
                    status_string, variants)
 from . import torch_ops
@@ -18,4 +18,4 @@ from . import torch_ops
 __all__ = ["gemm_f32", "gemm_f16", "gemm_bf16", "gemm_strided_batched", "gemm_strided_batched_ex",
            "select", "variants",
            "force_variant", "status_string", "load", "MgemmError", "OP_N", "OP_T", "F32", "F16",
-           "BF16", "torch_ops"]
+           "BF16", "I8", "I32", "torch_ops"]

@@ -19,9 +19,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libmgemm.so")
 
 OP_N, OP_T = 0, 1
-F32, F16, BF16 = 0, 1, 2
-DTYPE_CODES = {"f32": F32, "f16": F16, "bf16": BF16}
-ELEM_SIZE = {F32: 4, F16: 2, BF16: 2}
+F32, F16, BF16, I8, I32 = 0, 1, 2, 3, 4
+DTYPE_CODES = {"f32": F32, "f16": F16, "bf16": BF16, "i8": I8, "i32": I32}
+ELEM_SIZE = {F32: 4, F16: 2, BF16: 2, I8: 1, I32: 4}
 
 STATUS = {0: "MGEMM_OK", 1: "MGEMM_INVALID_ARG", 2: "MGEMM_HIP_ERROR"}
 

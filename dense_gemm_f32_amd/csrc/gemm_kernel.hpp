@@ -56,6 +56,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
@@ -70,6 +72,7 @@ struct KernelArgs {
     int tiles_m, tiles_n;
     int group_m;      // tile rows per raster group
     float alpha, beta;
+    int alpha_i, beta_i;  // integral alpha and beta for int8 inputs (int32 C)
     int c_vec;        // C pointer/ldc/strideC allow one vector access per 4 elements
     int fast_ok;      // operand tiles addressable with 32-bit byte offsets
 };
@@ -106,6 +109,7 @@ template <> struct RawOf<16> { using type = u32x4; };
 template <> struct RawOf<8> { using type = u32x2; };
 template <> struct RawOf<4> { using type = uint32_t; };
 template <> struct RawOf<2> { using type = uint16_t; };
+template <> struct RawOf<1> { using type = uint8_t; };
 
 // Buffer resource over [base, base + 2 GiB): raw addressing, no swizzle.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base)
@@ -215,7 +219,9 @@ __device__ __forceinline__ void lds_floats(const char *ptr, float (&out)[N])
 // ---------------------------------------------------------------------------
 // Operand fragments of one k-group and the MFMAs that consume them.
 // fp32: 4 k-slots per operand row (k = 8g + 4h + s); 16-bit: one 8-element
-// vector per row (k = 16g + 8h + 0..7).
+// vector per row (k = 16g + 8h + 0..7); int8: one 16-element vector per row
+// (k = 32g + 16h + 0..15), v_mfma_i32_32x32x32_i8 with int32 accumulators
+// kept in the same registers (the f32x16 type only names 16 dwords).
 // ---------------------------------------------------------------------------
 template <typename T, int TM, int TN>
 struct Frags {
@@ -238,7 +244,11 @@ struct Frags {
             for (int t = 0; t < TM; ++t)
 #pragma unroll
                 for (int u = 0; u < TN; ++u) {
-                    if constexpr (__is_same(T, _Float16))
+                    if constexpr (__is_same(T, int8_t))
+                        acc[t][u] = __builtin_bit_cast(f32x16, __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                            __builtin_bit_cast(i32x4, a16[t]), __builtin_bit_cast(i32x4, b16[u]),
+                            __builtin_bit_cast(i32x16, acc[t][u]), 0, 0, 0));
+                    else if constexpr (__is_same(T, _Float16))
                         acc[t][u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
                             __builtin_bit_cast(f16x8, a16[t]), __builtin_bit_cast(f16x8, b16[u]), acc[t][u], 0, 0, 0);
                     else
@@ -342,6 +352,10 @@ struct RegOperand {
 #pragma unroll
             for (int e = 0; e < V; ++e)
                 if (e < n) v[e] = reinterpret_cast<const uint32_t *>(ptr)[e];
+        } else if constexpr (ES == 1) {
+#pragma unroll
+            for (int e = 0; e < V; ++e)
+                if (e < n) v[e >> 2] |= (uint32_t)reinterpret_cast<const uint8_t *>(ptr)[e] << (8 * (e & 3));
         } else {
 #pragma unroll
             for (int e = 0; e < V; ++e)
@@ -409,7 +423,7 @@ struct RegPath {
     static constexpr int A_BYTES = BM * BK * ES, B_BYTES = BN * BK * ES;
     static constexpr int STAGE = A_BYTES + B_BYTES;
     static constexpr int LDS_BYTES = 2 * STAGE;
-    static constexpr int G = F32 ? BK / 8 : BK / 16;
+    static constexpr int G = F32 ? BK / 8 : BK * ES / 32;  // k-groups of 32 bytes per slab
     static constexpr int IL_A = TM, IL_B = TN;  // C mapping: interleaved rows and columns
 
     using OpA = RegOperand<ES, NT, BM, BK, TM, TA, VECOK>;
@@ -561,7 +575,7 @@ struct DmaPath {
     static constexpr int RB = BK * ES;          // K-contiguous row bytes
     static_assert(RB == 64 || RB == 128, "64- or 128-byte K-contiguous rows");
     static constexpr int CPR = RB / 16;         // 16-byte chunks per row
-    static constexpr int G = F32 ? BK / 8 : BK / 16;  // k-groups per slab
+    static constexpr int G = F32 ? BK / 8 : BK * ES / 32;  // k-groups (32 bytes of k) per slab
     static constexpr bool A_KC = !TA, B_KC = TB;
     static constexpr bool A_TR = TA && !F32, B_TR = !TB && !F32;
     static constexpr int IL_A = A_TR ? 1 : TM, IL_B = B_TR ? 1 : TN;
@@ -837,6 +851,29 @@ struct CVec {
 // N adjacent elements of C at cp (aligned to N elements when N > 1):
 // v + beta * C_old, rounded to CT (round to nearest even), stored as one
 // non-temporal vector.
+// int32 C of int8 inputs: alpha*acc + beta*C in 32-bit two's-complement
+// arithmetic (wrapping), stored as N adjacent ints.
+template <int N>
+__device__ __forceinline__ void store_c_int(int32_t *cp, const uint32_t *v, bool use_beta, uint32_t beta)
+{
+    if constexpr (N == 1) {
+        const uint32_t o = use_beta ? v[0] + beta * (uint32_t)*cp : v[0];
+        __builtin_nontemporal_store((int32_t)o, cp);
+    } else {
+        using V = typename CVec<int32_t, N>::type;
+        V o;
+        if (use_beta) {
+            const V old = *reinterpret_cast<const V *>(cp);
+#pragma unroll
+            for (int u = 0; u < N; ++u) o[u] = (int32_t)(v[u] + beta * (uint32_t)old[u]);
+        } else {
+#pragma unroll
+            for (int u = 0; u < N; ++u) o[u] = (int32_t)v[u];
+        }
+        __builtin_nontemporal_store(o, reinterpret_cast<V *>(cp));
+    }
+}
+
 template <typename CT, int N>
 __device__ __forceinline__ void store_c(CT *cp, const float *v, bool use_beta, float beta)
 {
@@ -859,8 +896,78 @@ __device__ __forceinline__ void store_c(CT *cp, const float *v, bool use_beta, f
 }
 
 template <bool EDGE, int IL_A, int IL_B, int TM, int TN, int WTM, int WTN, int WN, typename CT>
+__device__ __forceinline__ void epilogue_fp(const KernelArgs &p, int bidx, int m0, int n0,
+                                            const f32x16 (&acc)[TM][TN]);
+
+// Register r of an int32 accumulator held in an f32x16.  The whole vector is
+// reinterpreted before indexing: a bit cast applied to one element of an
+// ext_vector lvalue compiled to a read of element 0 whatever the index.
+__device__ __forceinline__ uint32_t acc_u32(const f32x16 &v, int r)
+{
+    return (uint32_t)__builtin_bit_cast(i32x16, v)[r];
+}
+
+// The same mapping for int32 accumulators (int8 inputs) and int32 C.
+template <bool EDGE, int IL_A, int IL_B, int TM, int TN, int WTM, int WTN, int WN>
+__device__ __forceinline__ void epilogue_int(const KernelArgs &p, int bidx, int m0, int n0,
+                                             const f32x16 (&acc)[TM][TN])
+{
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    const int li = lane & 31, lh = lane >> 5;
+    int32_t *Cb = static_cast<int32_t *>(p.C) + (int64_t)bidx * p.strideC;
+    const bool use_beta = p.beta_i != 0;
+    const uint32_t alpha = (uint32_t)p.alpha_i, beta = (uint32_t)p.beta_i;
+    constexpr bool VCOL = IL_B > 1;
+    const int colv = n0 + wn * WTN + TN * li;
+    const bool vec_store = VCOL && p.c_vec && (!EDGE || colv + TN <= p.N);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int ip = 8 * (r >> 2) + 4 * lh + (r & 3);
+#pragma unroll
+        for (int t = 0; t < TM; ++t) {
+            const int row = m0 + wm * WTM + (IL_A == 1 ? 32 * t + ip : TM * ip + t);
+            if (EDGE && row >= p.M) continue;
+            int32_t *crow = Cb + (int64_t)row * p.ldc;
+            if constexpr (VCOL) {
+                uint32_t v[TN];
+#pragma unroll
+                for (int u = 0; u < TN; ++u) v[u] = alpha * acc_u32(acc[t][u], r);
+                int32_t *cp = crow + colv;
+                if (vec_store) {
+                    store_c_int<TN>(cp, v, use_beta, beta);
+                } else {
+#pragma unroll
+                    for (int u = 0; u < TN; ++u)
+                        if (!EDGE || colv + u < p.N) store_c_int<1>(cp + u, v + u, use_beta, beta);
+                }
+            } else {
+#pragma unroll
+                for (int u = 0; u < TN; ++u) {
+                    const int col = n0 + wn * WTN + 32 * u + li;
+                    if (EDGE && col >= p.N) continue;
+                    const uint32_t v = alpha * acc_u32(acc[t][u], r);
+                    store_c_int<1>(crow + col, &v, use_beta, beta);
+                }
+            }
+        }
+    }
+}
+
+template <bool EDGE, int IL_A, int IL_B, int TM, int TN, int WTM, int WTN, int WN, typename CT>
 __device__ __forceinline__ void epilogue(const KernelArgs &p, int bidx, int m0, int n0,
                                          const f32x16 (&acc)[TM][TN])
+{
+    if constexpr (__is_same(CT, int32_t))
+        epilogue_int<EDGE, IL_A, IL_B, TM, TN, WTM, WTN, WN>(p, bidx, m0, n0, acc);
+    else
+        epilogue_fp<EDGE, IL_A, IL_B, TM, TN, WTM, WTN, WN, CT>(p, bidx, m0, n0, acc);
+}
+
+template <bool EDGE, int IL_A, int IL_B, int TM, int TN, int WTM, int WTN, int WN, typename CT>
+__device__ __forceinline__ void epilogue_fp(const KernelArgs &p, int bidx, int m0, int n0,
+                                            const f32x16 (&acc)[TM][TN])
 {
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -906,7 +1013,7 @@ __device__ __forceinline__ void epilogue(const KernelArgs &p, int bidx, int m0, 
 
 // ---------------------------------------------------------------------------
 // The kernel.
-//   T          float, _Float16 or __bf16 (A and B element type)
+//   T          float, _Float16, __bf16 or int8_t (A and B element type)
 //   BM, BN     workgroup tile
 //   BK         K-slab of the register path (the DMA path uses BK/2)
 //   WM, WN     wavefront grid; each wave owns a (BM/WM) x (BN/WN) sub-tile
@@ -914,7 +1021,8 @@ __device__ __forceinline__ void epilogue(const KernelArgs &p, int bidx, int m0, 
 //   TA, TB     op(A) = A^T, op(B) = B^T
 //   VECOK      A and B allow 16-byte global accesses (enables DmaPath)
 //   PIPE       DmaPath schedule: 1 -> 4 stages of BK/2, 2 -> 2 stages of BK
-//   CT         C element type: float, or T itself (16-bit output)
+//   CT         C element type: float, T itself (16-bit output), or int32_t
+//              (int8 inputs)
 // ---------------------------------------------------------------------------
 template <typename T, int BM, int BN, int BK, int WM, int WN, bool TA, bool TB, bool VECOK, int PIPE,
           typename CT>
@@ -951,6 +1059,7 @@ gemm_kernel(KernelArgs p)
 // beta == 0 writes zeros without reading C.
 template <typename CT>
 __global__ void __launch_bounds__(256) scale_c_kernel(CT *C, int M, int N, int64_t ldc,
-                                                      int64_t strideC, int batch, float beta);
+                                                      int64_t strideC, int batch, float beta,
+                                                      int beta_i);
 
 }  // namespace mgemm

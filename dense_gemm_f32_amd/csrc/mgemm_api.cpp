@@ -22,32 +22,43 @@ struct Table {
 
 Table table_for(int dtype)
 {
-    int n32, n16, nb16;
+    int n32, n16, nb16, n8;
     const Variant *v32 = f32_variants(&n32);
     const Variant *v16 = f16_variants(&n16);
     const Variant *vb16 = bf16_variants(&nb16);
+    const Variant *v8 = i8_variants(&n8);
     switch (dtype) {
     case MGEMM_F32: return {v32, n32, 0};
     case MGEMM_F16: return {v16, n16, n32};
     case MGEMM_BF16: return {vb16, nb16, n32 + n16};
+    case MGEMM_I8: return {v8, n8, n32 + n16 + nb16};
     default: return {nullptr, 0, 0};
     }
 }
 
-std::atomic<int> g_forced[3] = {{-1}, {-1}, {-1}};
+constexpr int N_IN_TYPES = 4;  // input types with a variant table: f32, f16, bf16, i8
+std::atomic<int> g_forced[N_IN_TYPES] = {{-1}, {-1}, {-1}, {-1}};
 
-int total_variants() { return table_for(MGEMM_BF16).first_id + table_for(MGEMM_BF16).n; }
+bool is_input_type(int dtype) { return dtype >= MGEMM_F32 && dtype <= MGEMM_I8; }
+
+int total_variants() { return table_for(MGEMM_I8).first_id + table_for(MGEMM_I8).n; }
 
 const Variant *variant_by_id(int id)
 {
-    for (int d = 0; d < 3; ++d) {
+    for (int d = 0; d < N_IN_TYPES; ++d) {
         Table t = table_for(d);
         if (id >= t.first_id && id < t.first_id + t.n) return &t.v[id - t.first_id];
     }
     return nullptr;
 }
 
-int elem_size(int dtype) { return dtype == MGEMM_F32 ? 4 : 2; }
+int elem_size(int dtype)
+{
+    return dtype == MGEMM_F32 || dtype == MGEMM_I32 ? 4 : dtype == MGEMM_I8 ? 1 : 2;
+}
+
+// alpha or beta usable as an int32 multiplier (int8 inputs): integral and in range
+bool int32_scalar(float x) { return x == (float)(int64_t)x && x >= -2147483648.0f && x < 2147483648.0f; }
 
 // What a validated call will do.
 struct Plan {
@@ -69,8 +80,14 @@ mgemm_status validate_and_plan(int dtype, int c_dtype, int transA, int transB, i
                                const void *C, int64_t ldc, int64_t strideC, int64_t batch,
                                Plan *plan)
 {
-    if (dtype != MGEMM_F32 && dtype != MGEMM_F16 && dtype != MGEMM_BF16) return MGEMM_INVALID_ARG;
-    if (c_dtype != MGEMM_F32 && c_dtype != dtype) return MGEMM_INVALID_ARG;  // fp32 C, or the inputs' type
+    if (!is_input_type(dtype)) return MGEMM_INVALID_ARG;
+    if (dtype == MGEMM_I8) {
+        // int32 C; A and B K-contiguous; integral alpha and beta
+        if (c_dtype != MGEMM_I32 || transA != MGEMM_OP_N || transB != MGEMM_OP_T) return MGEMM_INVALID_ARG;
+        if (!int32_scalar(alpha) || !int32_scalar(beta)) return MGEMM_INVALID_ARG;
+    } else if (c_dtype != MGEMM_F32 && c_dtype != dtype) {
+        return MGEMM_INVALID_ARG;  // fp32 C, or the inputs' own 16-bit type
+    }
     if ((transA != MGEMM_OP_N && transA != MGEMM_OP_T) || (transB != MGEMM_OP_N && transB != MGEMM_OP_T))
         return MGEMM_INVALID_ARG;
     if (M < 0 || N < 0 || K < 0 || batch < 0) return MGEMM_INVALID_ARG;
@@ -113,6 +130,8 @@ mgemm_status validate_and_plan(int dtype, int c_dtype, int transA, int transB, i
     a.K = (int)K;
     a.alpha = alpha;
     a.beta = beta;
+    a.alpha_i = dtype == MGEMM_I8 ? (int)(int64_t)alpha : 0;
+    a.beta_i = dtype == MGEMM_I8 ? (int)(int64_t)beta : 0;
     // a lane stores up to 4 adjacent C elements as one vector
     a.c_vec = aligned(C, 4 * ces) && ldc % 4 == 0 && (batch == 1 || strideC % 4 == 0);
     // Interior tiles address their operands with 32-bit byte offsets from the
@@ -207,9 +226,11 @@ mgemm_status run(int dtype, int c_dtype, int transA, int transB, int64_t M, int6
     if (st != MGEMM_OK || plan.kind == Plan::NOTHING) return st;
     hipError_t err;
     if (plan.kind == Plan::SCALE) {
-        err = launch_scale_c(c_dtype, C, (int)M, (int)N, ldc, strideC, (int)batch, beta, stream);
+        err = launch_scale_c(c_dtype, C, (int)M, (int)N, ldc, strideC, (int)batch, beta,
+                             plan.args.beta_i, stream);
     } else {
-        const LaunchFn fn = c_dtype == MGEMM_F32 ? plan.var->fn[transA][transB] : plan.var->fn16[transA][transB];
+        const LaunchFn fn = c_dtype == MGEMM_F32 || c_dtype == MGEMM_I32 ? plan.var->fn[transA][transB]
+                                                                          : plan.var->fn16[transA][transB];
         if (fn == nullptr) return MGEMM_INVALID_ARG;
         err = fn(plan.args, (unsigned)plan.grid, stream);
     }
@@ -294,7 +315,9 @@ mgemm_status mgemm_select(mgemm_dtype in_dtype, mgemm_op transA, mgemm_op transB
                           int64_t batch, mgemm_variant_info *out, int64_t *grid)
 {
     Plan plan;
-    mgemm_status st = validate_and_plan(in_dtype, MGEMM_F32, transA, transB, M, N, K, alpha, A, lda,
+    // the C type does not change the choice: fp32 (int32 for int8 inputs)
+    const int c_dtype = in_dtype == MGEMM_I8 ? MGEMM_I32 : MGEMM_F32;
+    mgemm_status st = validate_and_plan(in_dtype, c_dtype, transA, transB, M, N, K, alpha, A, lda,
                                         strideA, B, ldb, strideB, beta, C, ldc, strideC, batch, &plan);
     if (st != MGEMM_OK) return st;
     if (out) {
@@ -313,7 +336,7 @@ mgemm_status mgemm_select(mgemm_dtype in_dtype, mgemm_op transA, mgemm_op transB
 
 mgemm_status mgemm_force_variant(mgemm_dtype dtype, int id)
 {
-    if (dtype != MGEMM_F32 && dtype != MGEMM_F16 && dtype != MGEMM_BF16) return MGEMM_INVALID_ARG;
+    if (!is_input_type(dtype)) return MGEMM_INVALID_ARG;
     if (id >= 0) {
         const Variant *v = variant_by_id(id);
         if (!v || v->dtype != dtype) return MGEMM_INVALID_ARG;

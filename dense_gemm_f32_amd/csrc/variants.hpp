@@ -17,7 +17,7 @@ struct Variant {
     bool vec;             // needs 16-byte aligned A/B rows (dwordx4 loads)
     int pipe;             // DMA-path schedule (1: 4 stages of bk/2, 2: 2 stages of bk)
     const char *name;
-    LaunchFn fn[2][2];    // [transA][transB], fp32 C
+    LaunchFn fn[2][2];    // [transA][transB], fp32 C (int32 C for int8 inputs)
     LaunchFn fn16[2][2];  // [transA][transB], C in the inputs' 16-bit type (16-bit tables only)
 };
 
@@ -41,6 +41,13 @@ hipError_t launch_gemm(const KernelArgs &a, unsigned grid, hipStream_t s)
     {0, BM, BN, BK, WM, WN, V, 1, NAME, MGEMM_LAUNCHERS(float, BM, BN, BK, WM, WN, V, 1, float), \
      {{nullptr, nullptr}, {nullptr, nullptr}}}
 
+// int8 inputs: int32 C, A K-contiguous (op N) and B K-contiguous (op T) only
+#define MGEMM_VARIANT_I8(BM, BN, BK, WM, WN, V, D, NAME)                                     \
+    {3, BM, BN, BK, WM, WN, V, D, NAME,                                                      \
+     {{nullptr, launch_gemm<int8_t, BM, BN, BK, WM, WN, false, true, V, D, int32_t>},         \
+      {nullptr, nullptr}},                                                                   \
+     {{nullptr, nullptr}, {nullptr, nullptr}}}
+
 // 16-bit inputs: fp32 C or C of the input type
 #define MGEMM_VARIANT_D(T, DT, BM, BN, BK, WM, WN, V, D, NAME)                               \
     {DT, BM, BN, BK, WM, WN, V, D, NAME, MGEMM_LAUNCHERS(T, BM, BN, BK, WM, WN, V, D, float), \
@@ -53,8 +60,9 @@ hipError_t launch_gemm(const KernelArgs &a, unsigned grid, hipStream_t s)
 const Variant *f32_variants(int *count);
 const Variant *f16_variants(int *count);
 const Variant *bf16_variants(int *count);
+const Variant *i8_variants(int *count);
 
 hipError_t launch_scale_c(int c_dtype, void *C, int M, int N, int64_t ldc, int64_t strideC, int batch,
-                          float beta, hipStream_t s);
+                          float beta, int beta_i, hipStream_t s);
 
 }  // namespace mgemm

@@ -33,13 +33,14 @@ from typing import Optional
 import numpy as np
 import torch
 
-TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
-ELEM_SIZE = {"f32": 4, "f16": 2, "bf16": 2}
+TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
+               "i8": torch.int8, "i32": torch.int32}
+ELEM_SIZE = {"f32": 4, "f16": 2, "bf16": 2, "i8": 1, "i32": 4}
 
 
 @dataclasses.dataclass
 class Problem:
-    dtype: str                 # "f32" | "f16" | "bf16" (operand type)
+    dtype: str                 # "f32" | "f16" | "bf16" | "i8" (operand type)
     M: int
     N: int
     K: int
@@ -60,7 +61,7 @@ class Problem:
     strideB: Optional[int] = None
     strideC: Optional[int] = None
     pad_value: Optional[float] = None  # fill for padding beyond the logical matrix
-    c_dtype: str = "f32"       # C's type: "f32", or the operand type for 16-bit output
+    c_dtype: str = "f32"       # C's type: "f32", the operand type for 16-bit output, "i32" for i8
 
     def __post_init__(self):
         a_rows, a_cols = (self.K, self.M) if self.transA else (self.M, self.K)
@@ -103,13 +104,13 @@ class Problem:
         return self.buffer_elems(self.M, self.ldc, self.strideC)
 
     def tolerance_coeff(self) -> float:
-        """c in max|err| <= c * sqrt(K) * max|ref| (fp32: 1e-5, 16-bit: 2e-3)."""
-        return 1e-5 if self.dtype == "f32" else 2e-3
+        """c in max|err| <= c * sqrt(K) * max|ref| (fp32: 1e-5, 16-bit: 2e-3, int8: 0)."""
+        return {"f32": 1e-5, "f16": 2e-3, "bf16": 2e-3, "i8": 0.0}[self.dtype]
 
     def output_rounding(self) -> float:
         """Relative rounding of the stored C: half an ulp of its type (0 for fp32,
         which the accumulator itself is)."""
-        return {"f32": 0.0, "f16": 2.0 ** -11, "bf16": 2.0 ** -8}[self.c_dtype]
+        return {"f32": 0.0, "f16": 2.0 ** -11, "bf16": 2.0 ** -8, "i32": 0.0}[self.c_dtype]
 
 
 def _draw(gen, n, dist, lo, hi):
@@ -150,16 +151,20 @@ def make_inputs(p: Problem):
     C0 = None
     if p.beta != 0.0 or p.c_dist is not None:
         cd = p.c_dist or p.dist
-        C0 = _draw(gen, p.c_elems, cd, p.int_lo, p.int_hi)
-        if p.c_dtype != "f32":
+        if p.c_dtype == "i32":   # integer C: drawn as int64, stored exactly
+            C0 = torch.randint(p.int_lo, p.int_hi + 1, (p.c_elems,), generator=gen).to(torch.int32)
+        else:
+            C0 = _draw(gen, p.c_elems, cd, p.int_lo, p.int_hi)
+        if p.c_dtype not in ("f32", "i32"):
             C0 = C0.to(TORCH_DTYPE[p.c_dtype])
     return bufs[0], bufs[1], C0
 
 
 def to_numpy_operand(x: torch.Tensor) -> np.ndarray:
-    """Operand buffer as numpy: float32 values, or uint16 bit patterns for 16-bit types."""
+    """Operand buffer as numpy: float32 or int8 values, or uint16 bit patterns for 16-bit
+    types."""
     x = x.detach().cpu().contiguous()
-    if x.dtype == torch.float32:
+    if x.dtype in (torch.float32, torch.int8, torch.int32):
         return x.numpy()
     return x.view(torch.int16).numpy().view(np.uint16)
 
@@ -195,6 +200,13 @@ def qkt_batched() -> Problem:
                    dist="normal", seed=1005)
 
 
+def gemm_i8_8192() -> Problem:
+    """8192^3 with int8 operands in [-128, 127], int32 accumulate and int32 C; A and B
+    both K-contiguous (B stored [n, k])."""
+    return Problem("i8", 8192, 8192, 8192, transB=True, dist="int", int_lo=-128, int_hi=127,
+                   c_dtype="i32", seed=1007)
+
+
 def qkt_batched_f16_out() -> Problem:
     """The attention-score batch with a binary16 C (fp32 accumulate, rounded on store)."""
     p = qkt_batched()
@@ -211,6 +223,7 @@ WORKLOADS = {
     "gemm_f16_8192": lambda: gemm16_8192("f16"),
     "qkt_batched": qkt_batched,
     "qkt_batched_f16_out": qkt_batched_f16_out,
+    "gemm_i8_8192": gemm_i8_8192,
 }
 
 

@@ -64,7 +64,13 @@ typedef enum {
 
 typedef enum { MGEMM_OP_N = 0, MGEMM_OP_T = 1 } mgemm_op;
 
-typedef enum { MGEMM_F32 = 0, MGEMM_F16 = 1, MGEMM_BF16 = 2 } mgemm_dtype;
+typedef enum {
+    MGEMM_F32 = 0,
+    MGEMM_F16 = 1,
+    MGEMM_BF16 = 2,
+    MGEMM_I8 = 3,   /* int8 inputs (gemm_strided_batched_ex only) */
+    MGEMM_I32 = 4   /* int32 C of int8 inputs */
+} mgemm_dtype;
 
 /* Raw 16-bit storage: IEEE 754 binary16 and bfloat16 bit patterns. */
 typedef uint16_t mgemm_f16;
@@ -135,6 +141,15 @@ mgemm_status gemm_strided_batched(mgemm_dtype in_dtype, mgemm_op transA, mgemm_o
  *          elements of c_dtype.
  * Errors: as gemm_strided_batched, plus MGEMM_INVALID_ARG for any other
  * c_dtype.
+ *
+ * int8 inputs (in_dtype = MGEMM_I8, the other precision row of the WMMA
+ * page's type table, "1. 概述": 8-bit integer A/B with an int
+ * accumulator): c_dtype must be MGEMM_I32; products accumulate exactly in
+ * int32 and alpha*acc + beta*C is formed in 32-bit two's-complement
+ * arithmetic (wrapping on overflow).  alpha and beta must be integers that
+ * fit int32, and only transA = MGEMM_OP_N, transB = MGEMM_OP_T (both
+ * operands K-contiguous) is built; anything else is MGEMM_INVALID_ARG.
+ * lda, ldb, strides in elements (bytes); C aligned to 4 bytes.
  */
 mgemm_status gemm_strided_batched_ex(mgemm_dtype in_dtype, mgemm_dtype c_dtype,
                                      mgemm_op transA, mgemm_op transB,
@@ -178,7 +193,8 @@ mgemm_status mgemm_variant(int id, mgemm_variant_info *out);
  * The variant (and launch grid size) a call with these arguments would use,
  * after the same validation the entry points perform.  Returns the
  * validation status; *out and *grid are set on MGEMM_OK (id = -1 and grid = 0
- * when the call would launch no GEMM kernel).
+ * when the call would launch no GEMM kernel).  C is taken as fp32 (int32
+ * for MGEMM_I8 inputs); a 16-bit C selects the same variant.
  */
 mgemm_status mgemm_select(mgemm_dtype in_dtype, mgemm_op transA, mgemm_op transB,
                           int64_t M, int64_t N, int64_t K, float alpha,

@@ -15,7 +15,8 @@ the CPU sgemm of section "什么是矩阵乘法"; WMMA API page (adg.csdn.net),
 "1. 概述" type table (16-bit inputs, float accumulator).
 
 16-bit operands are passed as ``numpy.uint16`` arrays holding the raw
-binary16 / bfloat16 bit patterns; fp32 operands as ``numpy.float32``.
+binary16 / bfloat16 bit patterns; fp32 operands as ``numpy.float32``;
+int8 operands as ``numpy.int8`` (C then ``numpy.int32``).
 """
 from __future__ import annotations
 
@@ -29,7 +30,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
-DTYPES = {"f32": 0, "f16": 1, "bf16": 2}
+DTYPES = {"f32": 0, "f16": 1, "bf16": 2, "i8": 3}
 
 _lib = None
 
@@ -74,6 +75,8 @@ def _load():
     lib.oracle_double_to_bf16.argtypes = [dbl]
     lib.oracle_round16.restype = ctypes.c_int
     lib.oracle_round16.argtypes = [ctypes.c_int, vp, vp, i64]
+    lib.oracle_wrap_i32.restype = ctypes.c_int
+    lib.oracle_wrap_i32.argtypes = [vp, vp, i64]
     lib.oracle_set_threads.restype = None
     lib.oracle_set_threads.argtypes = [ctypes.c_int]
     lib.oracle_max_threads.restype = ctypes.c_int
@@ -128,11 +131,26 @@ def _ptr(a):
 
 
 def _check_operand(x, dtype):
-    want = np.float32 if dtype == "f32" else np.uint16
+    want = {"f32": np.float32, "i8": np.int8}.get(dtype, np.uint16)
     if x.dtype != want:
         raise TypeError(f"{dtype} operand must be {np.dtype(want).name}, got {x.dtype}")
     if not x.flags.c_contiguous:
         raise ValueError("operands must be C-contiguous buffers")
+
+
+def _check_c(C, dtype):
+    want = np.int32 if dtype == "i8" else np.float32
+    if C is not None and (C.dtype != want or not C.flags.c_contiguous):
+        raise TypeError(f"C must be a C-contiguous {np.dtype(want).name} buffer")
+
+
+def wrap_i32(x):
+    """int32 C of int8 inputs: exact integer results (float64) modulo 2^32, as int32."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(x.shape, dtype=np.int32)
+    if _load().oracle_wrap_i32(x.ctypes.data, out.ctypes.data, x.size) != 0:
+        raise ValueError("wrap_i32: values must be integers below 2^53 in magnitude")
+    return out
 
 
 def gemm(dtype, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
@@ -145,8 +163,7 @@ def gemm(dtype, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
     """
     _check_operand(A, dtype)
     _check_operand(B, dtype)
-    if C is not None and (C.dtype != np.float32 or not C.flags.c_contiguous):
-        raise TypeError("C must be a C-contiguous float32 buffer")
+    _check_c(C, dtype)
     out = np.empty((batch, M, N), dtype=np.float64)
     rc = _load().oracle_gemm(DTYPES[dtype], int(bool(transA)), int(bool(transB)), M, N, K,
                              float(alpha), _ptr(A), lda, strideA, _ptr(B), ldb, strideB,
@@ -162,8 +179,7 @@ def gemm_elems(dtype, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, l
     """Selected output elements (bidx[e], iidx[e], jidx[e]) as float64."""
     _check_operand(A, dtype)
     _check_operand(B, dtype)
-    if C is not None and (C.dtype != np.float32 or not C.flags.c_contiguous):
-        raise TypeError("C must be a C-contiguous float32 buffer")
+    _check_c(C, dtype)
     bidx = np.ascontiguousarray(bidx, dtype=np.int64)
     iidx = np.ascontiguousarray(iidx, dtype=np.int64)
     jidx = np.ascontiguousarray(jidx, dtype=np.int64)

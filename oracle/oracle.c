@@ -21,7 +21,8 @@
  *   - op(A)/op(B) with an explicit stride per matrix ("matrices may be
  *     non-contiguous"): same tutorial, section "Triton", the wrapper that
  *     passes strides;
- *   - half and bfloat16 operands with a float accumulator:
+ *   - half and bfloat16 operands with a float accumulator, and 8-bit
+ *     integer operands with an int accumulator:
  *     WMMA API page (adg.csdn.net), "1. 概述", the element-type table.
  *
  * Readings taken where the pages are silent (each listed in the design doc):
@@ -48,6 +49,7 @@
 #define ORACLE_F32 0
 #define ORACLE_F16 1
 #define ORACLE_BF16 2
+#define ORACLE_I8 3   /* int8 A/B; C (when read) is int32 */
 
 #define ORACLE_OK 0
 #define ORACLE_BAD_ARG 1
@@ -133,7 +135,16 @@ static double load_elem(int dtype, const void *base, int64_t r, int64_t c, int64
         return (double)((const float *)base)[off];
     if (dtype == ORACLE_F16)
         return oracle_f16_to_double(((const uint16_t *)base)[off]);
+    if (dtype == ORACLE_I8)
+        return (double)((const int8_t *)base)[off];
     return oracle_bf16_to_double(((const uint16_t *)base)[off]);
+}
+
+/* Element of C (fp32, or int32 for int8 inputs); both are 4 bytes wide. */
+static double load_c(int dtype, const void *C, int64_t off)
+{
+    if (dtype == ORACLE_I8) return (double)((const int32_t *)C)[off];
+    return (double)((const float *)C)[off];
 }
 
 /* op(A)[i][k]: A is stored M x K (transA == 0) or K x M (transA == 1). */
@@ -148,12 +159,12 @@ static double op_b(int dtype, const void *B, int transB, int64_t k, int64_t j, i
     return transB ? load_elem(dtype, B, j, k, ldb) : load_elem(dtype, B, k, j, ldb);
 }
 
-static size_t elem_size(int dtype) { return dtype == ORACLE_F32 ? 4 : 2; }
+static size_t elem_size(int dtype) { return dtype == ORACLE_F32 ? 4 : dtype == ORACLE_I8 ? 1 : 2; }
 
 /* One output element, exactly as the definition at the top of this file. */
 static double one_element(int dtype, int transA, int transB, int64_t K, double alpha,
                           const void *A, int64_t lda, const void *B, int64_t ldb,
-                          double beta, const float *C, int64_t ldc,
+                          double beta, const void *C, int64_t ldc,
                           int64_t i, int64_t j)
 {
     double acc = 0.0;
@@ -161,14 +172,14 @@ static double one_element(int dtype, int transA, int transB, int64_t K, double a
         acc += op_a(dtype, A, transA, i, k, lda) * op_b(dtype, B, transB, k, j, ldb);
     double out = alpha * acc;
     if (beta != 0.0)
-        out = out + beta * (double)C[i * ldc + j];
+        out = out + beta * load_c(dtype, C, i * ldc + j);
     return out;
 }
 
 static int check_args(int dtype, int transA, int transB, int64_t M, int64_t N, int64_t K,
                       int64_t lda, int64_t ldb, int64_t ldc, int64_t batch)
 {
-    if (dtype < ORACLE_F32 || dtype > ORACLE_BF16) return ORACLE_BAD_ARG;
+    if (dtype < ORACLE_F32 || dtype > ORACLE_I8) return ORACLE_BAD_ARG;
     if ((transA != 0 && transA != 1) || (transB != 0 && transB != 1)) return ORACLE_BAD_ARG;
     if (M < 0 || N < 0 || K < 0 || batch < 0) return ORACLE_BAD_ARG;
     if (lda < (transA ? M : K) || ldb < (transB ? K : N) || ldc < N) return ORACLE_BAD_ARG;
@@ -184,7 +195,7 @@ int oracle_gemm(int dtype, int transA, int transB,
                 int64_t M, int64_t N, int64_t K, double alpha,
                 const void *A, int64_t lda, int64_t strideA,
                 const void *B, int64_t ldb, int64_t strideB,
-                double beta, const float *C, int64_t ldc, int64_t strideC,
+                double beta, const void *C, int64_t ldc, int64_t strideC,
                 int64_t batch, double *out, int64_t ldo, int64_t strideO)
 {
     if (check_args(dtype, transA, transB, M, N, K, lda, ldb, ldc, batch) != ORACLE_OK)
@@ -198,7 +209,7 @@ int oracle_gemm(int dtype, int transA, int transB,
         int64_t b = row / M, i = row % M;
         const char *Ab = (const char *)A + (size_t)(b * strideA) * es;
         const char *Bb = (const char *)B + (size_t)(b * strideB) * es;
-        const float *Cb = C ? C + b * strideC : NULL;
+        const char *Cb = C ? (const char *)C + (size_t)(b * strideC) * 4 : NULL;
         for (int64_t j = 0; j < N; ++j)
             out[b * strideO + i * ldo + j] =
                 one_element(dtype, transA, transB, K, alpha, Ab, lda, Bb, ldb,
@@ -216,7 +227,7 @@ int oracle_gemm_elems(int dtype, int transA, int transB,
                       int64_t M, int64_t N, int64_t K, double alpha,
                       const void *A, int64_t lda, int64_t strideA,
                       const void *B, int64_t ldb, int64_t strideB,
-                      double beta, const float *C, int64_t ldc, int64_t strideC,
+                      double beta, const void *C, int64_t ldc, int64_t strideC,
                       int64_t batch, int64_t count,
                       const int64_t *bidx, const int64_t *iidx, const int64_t *jidx,
                       double *out)
@@ -234,9 +245,23 @@ int oracle_gemm_elems(int dtype, int transA, int transB,
         int64_t b = bidx[e];
         const char *Ab = (const char *)A + (size_t)(b * strideA) * es;
         const char *Bb = (const char *)B + (size_t)(b * strideB) * es;
-        const float *Cb = C ? C + b * strideC : NULL;
+        const char *Cb = C ? (const char *)C + (size_t)(b * strideC) * 4 : NULL;
         out[e] = one_element(dtype, transA, transB, K, alpha, Ab, lda, Bb, ldb,
                              beta, Cb, ldc, iidx[e], jidx[e]);
+    }
+    return ORACLE_OK;
+}
+
+/* int32 C of int8 inputs: the exact integer result taken modulo 2^32 into
+ * [-2^31, 2^31) (two's-complement wrapping).  Each input must be an integer
+ * of magnitude below 2^53 (exact in fp64); otherwise ORACLE_BAD_ARG. */
+int oracle_wrap_i32(const double *in, int32_t *out, int64_t n)
+{
+    for (int64_t e = 0; e < n; ++e) {
+        const double x = in[e];
+        if (!(fabs(x) < 9007199254740992.0) || x != floor(x)) return ORACLE_BAD_ARG;
+        const int64_t v = (int64_t)x;
+        out[e] = (int32_t)(uint32_t)((uint64_t)v & 0xffffffffu);
     }
     return ORACLE_OK;
 }

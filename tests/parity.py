@@ -35,7 +35,7 @@ class Run:
             c[GUARD:GUARD + n] = self.C0
         elif c_fill is not None:
             c[GUARD:GUARD + n] = c_fill
-        self.c_init = c.float().numpy().copy()
+        self.c_init = c.double().numpy().copy()
         self.dCbuf = c.to(DEV)
         self.dC = self.dCbuf[GUARD:GUARD + n]
 
@@ -56,10 +56,11 @@ class Run:
                                     self.dC, p.ldc, p.strideC, p.batch, stream=stream)
 
     def result(self):
-        """(batch, M, N) fp32 result, after checking the guard band and padding."""
+        """(batch, M, N) result as float64 (exact for every C type), after checking the
+        guard band and padding."""
         torch.cuda.synchronize()
         p = self.p
-        buf = self.dCbuf.float().cpu().numpy()
+        buf = self.dCbuf.double().cpu().numpy()
         assert np.all(buf[:GUARD] == SENTINEL) and np.all(buf[GUARD + p.c_elems:] == SENTINEL), \
             "write outside C"
         c = buf[GUARD:GUARD + p.c_elems]
@@ -68,10 +69,10 @@ class Run:
             init = self.c_init[GUARD:GUARD + p.c_elems]
             same = (c[~logical] == init[~logical]) | (np.isnan(c[~logical]) & np.isnan(init[~logical]))
             assert same.all(), "write into C padding"
-        out = np.empty((p.batch, p.M, p.N), np.float32)
+        out = np.empty((p.batch, p.M, p.N), np.float64)
         for b in range(p.batch):
             m = c[b * p.strideC:b * p.strideC + (p.M - 1) * p.ldc + p.N]
-            m = np.concatenate([m, np.zeros(p.M * p.ldc - m.size, np.float32)]).reshape(p.M, p.ldc)
+            m = np.concatenate([m, np.zeros(p.M * p.ldc - m.size, np.float64)]).reshape(p.M, p.ldc)
             out[b] = m[:, :p.N]
         return out
 
@@ -79,7 +80,8 @@ class Run:
         p = self.p
         return (p.dtype, p.transA, p.transB, p.M, p.N, p.K, p.alpha, wl.to_numpy_operand(self.A),
                 p.lda, wl.to_numpy_operand(self.B), p.ldb, p.beta,
-                None if self.C0 is None else self.C0.float().numpy(), p.ldc)
+                None if self.C0 is None else
+                (self.C0.numpy() if p.c_dtype == "i32" else self.C0.float().numpy()), p.ldc)
 
     def oracle_full(self):
         p = self.p
@@ -111,9 +113,11 @@ def sample_positions(p: wl.Problem, n_random=20000, seed=0, tile=256):
 
 def expected_exact(p: wl.Problem, ref):
     """What an exact accumulation stores: the oracle's value, rounded to C's type
-    (to nearest, ties to even) when C is 16-bit."""
+    (to nearest, ties to even) when C is 16-bit, wrapped to int32 for int8 inputs."""
     if p.c_dtype == "f32":
         return ref
+    if p.c_dtype == "i32":   # int8 inputs: the exact integer result wrapped to int32
+        return oracle.wrap_i32(ref).astype(np.float64)
     return oracle.decode16(p.c_dtype, oracle.round16(p.c_dtype, ref))
 
 

@@ -65,7 +65,7 @@ def test_variant_table():
         assert v["lds_bytes"] <= 160 * 1024
         assert v["pipe"] in (1, 2)
         assert v["name"].startswith("mgemm_")
-    assert {v["dtype"] for v in vs} == {0, 1, 2}
+    assert {v["dtype"] for v in vs} == {0, 1, 2, 3}
     info = _lib.VariantInfo()
     assert mg.load().mgemm_variant(len(vs), ctypes.byref(info)) == 1
 
@@ -144,6 +144,26 @@ def test_selection_for_the_named_workloads():
     info, g = sel("f16", 0, 1, M=1024, N=1024, K=64, lda=64, ldb=64, ldc=1024, batch=128,
                   strideA=65536, strideB=65536, strideC=1048576, alpha=0.125)
     assert info["dtype"] == 1 and g == 128 * (1024 // info["block_m"]) * (1024 // info["block_n"])
+
+
+def test_int8_rules_without_a_gpu():
+    lib = mg.load()
+    ex = lib.gemm_strided_batched_ex
+
+    def call(tA=0, tB=1, c_dt=4, alpha=1.0, beta=0.0, M=4, A=ALIGNED):
+        return ex(3, c_dt, tA, tB, M, 4, 16, alpha, A, 16, 0, ALIGNED, 16, 0, beta, ALIGNED, 4, 0,
+                  1, None)
+    # int32 C only; A and B K-contiguous only; integral alpha and beta only
+    assert call(c_dt=0) == 1 and call(c_dt=3) == 1
+    assert call(tA=1) == 1 and call(tB=0) == 1 and call(tA=1, tB=0) == 1
+    assert call(alpha=0.5) == 1 and call(beta=1.5) == 1 and call(alpha=3e9) == 1
+    # int32 C is for int8 inputs only
+    assert ex(0, 4, 0, 0, 4, 4, 4, 1.0, ALIGNED, 4, 0, ALIGNED, 4, 0, 0.0, ALIGNED, 4, 0, 1,
+              None) == 1
+    # legal calls with nothing to do return OK without touching the GPU
+    assert call(M=0) == 0 and call(M=0, alpha=-7.0, beta=2.0) == 0
+    info, grid = sel("i8", 0, 1, M=8192, N=8192, K=8192)
+    assert info["dtype"] == 3 and grid == 1024 and info["block_k"] == 128
 
 
 def test_force_variant_roundtrip():

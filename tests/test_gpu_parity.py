@@ -27,7 +27,7 @@ if torch.cuda.is_available():
 @pytest.fixture(autouse=True)
 def _auto_variant():
     yield
-    for dt in ("f32", "f16", "bf16"):
+    for dt in ("f32", "f16", "bf16", "i8"):
         mg.force_variant(dt, None)
 
 
@@ -81,7 +81,7 @@ def _assert_selected(p, v):
 
 
 def variants_of(dtype):
-    code = {"f32": 0, "f16": 1, "bf16": 2}[dtype]
+    code = {"f32": 0, "f16": 1, "bf16": 2, "i8": 3}[dtype]
     return [v for v in mg.variants() if v["dtype"] == code] if torch.cuda.is_available() else []
 
 
@@ -266,6 +266,46 @@ def test_c16_quick_returns_scale_c(dtype):
     p = wl.Problem(dtype, 70, 90, 0, beta=0.0, c_dtype=dtype, seed=54)
     got = full_check(p, exact=True, c_fill=float("nan"), what=f"-> {dtype} C, beta=0 K=0")
     assert not np.isnan(got).any()
+
+
+# ------------------------------------------------------------------ int8 inputs, int32 C
+
+def test_i8_every_variant():
+    # A and B K-contiguous (the layout built); interior (LDS-DMA) and edge tiles,
+    # aligned and odd leading dimensions, integral alpha and beta, exact
+    for v in variants_of("i8"):
+        mg.force_variant("i8", v["id"])
+        aligned = not v["name"].endswith("_u")
+        bm, bn, bk = v["block_m"], v["block_n"], v["block_k"]
+        for (M, N, K) in ((2 * bm + 17, 2 * bn + 9, 4 * bk), (bm + 3, bn + 40, 3 * bk + 29)):
+            for alpha, beta in ((1.0, 0.0), (-3.0, 2.0)):
+                p = wl.Problem("i8", M, N, K, transB=True, c_dtype="i32", alpha=alpha, beta=beta,
+                               lda=(K + 16 - K % 16 if aligned else K + 1),
+                               ldb=(K + 16 - K % 16 if aligned else K + 3),
+                               dist="int", int_lo=-128, int_hi=127, c_dist="int", seed=71,
+                               pad_value=77)
+                _assert_selected(p, v)
+                full_check(p, exact=True, what=f"{v['name']} i8 alpha={alpha} beta={beta}")
+
+
+def test_i8_wraps_like_int32():
+    # alpha * acc overflows int32: the stored value is the exact one modulo 2^32
+    p = wl.Problem("i8", 300, 260, 256, transB=True, c_dtype="i32", alpha=float(1 << 20),
+                   beta=-(1 << 30), dist="int", int_lo=-128, int_hi=127, c_dist="int", seed=72)
+    full_check(p, exact=True, what="i8 int32 wrap-around")
+    ref = Run(p).oracle_full()
+    assert np.abs(ref).max() > 2 ** 31          # the case really overflows
+
+
+def test_i8_quick_returns_and_empty():
+    for alpha, K in ((0.0, 128), (1.0, 0)):
+        p = wl.Problem("i8", 70, 90, K, transB=True, c_dtype="i32", alpha=alpha, beta=-5.0,
+                       dist="int", int_lo=-100, int_hi=100, c_dist="int", seed=73)
+        full_check(p, exact=True, what=f"i8 alpha={alpha} K={K}")
+
+
+def test_gemm_i8_8192():
+    sampled_check(wl.gemm_i8_8192(), exact=True, what="int8 8192^3 -> int32")
 
 
 # ------------------------------------------------------------------ shapes from the pages

@@ -324,6 +324,36 @@ def test_round_to_bf16_matches_brute_force_nearest():
     assert bad.size == 0, (x[bad[:5]], got[bad[:5]], want[bad[:5]])
 
 
+@pytest.mark.parametrize("tA,tB", [(False, False), (False, True), (True, False), (True, True)])
+def test_int8_products_match_numpy_int64(tA, tB):
+    # int8 inputs over their whole range, int32 C with integral alpha and beta
+    rng = np.random.default_rng(31)
+    M, N, K = 37, 29, 301
+    A = rng.integers(-128, 128, (K, M) if tA else (M, K)).astype(np.int8)
+    B = rng.integers(-128, 128, (N, K) if tB else (K, N)).astype(np.int8)
+    C = rng.integers(-2 ** 31, 2 ** 31, (M, N)).astype(np.int32)
+    out = oracle.gemm("i8", tA, tB, M, N, K, -3.0, A.ravel(), A.shape[1], B.ravel(), B.shape[1],
+                      5.0, C.ravel(), N)[0]
+    opA = (A.T if tA else A).astype(np.int64)
+    opB = (B.T if tB else B).astype(np.int64)
+    want = -3 * (opA @ opB) + 5 * C.astype(np.int64)
+    assert np.array_equal(out, want.astype(np.float64))
+    wrapped = oracle.wrap_i32(out)
+    assert np.array_equal(wrapped.astype(np.int64), ((want + 2 ** 31) % 2 ** 32) - 2 ** 31)
+
+
+def test_wrap_to_int32_closed_form():
+    x = np.array([0, 1, -1, 2 ** 31 - 1, 2 ** 31, -2 ** 31, -2 ** 31 - 1, 2 ** 32, 2 ** 32 + 7,
+                  -2 ** 40 - 3, 2 ** 52 + 1], dtype=np.float64)
+    want = np.array([0, 1, -1, 2 ** 31 - 1, -2 ** 31, -2 ** 31, 2 ** 31 - 1, 0, 7, -3, 1],
+                    dtype=np.int32)
+    assert np.array_equal(oracle.wrap_i32(x), want)
+    with pytest.raises(ValueError):
+        oracle.wrap_i32(np.array([0.5]))
+    with pytest.raises(ValueError):
+        oracle.wrap_i32(np.array([2.0 ** 60]))
+
+
 def test_thread_count_changes_no_bit():
     p = wl.Problem("bf16", 67, 45, 129, transA=True, alpha=0.75, beta=-2.0, dist="normal",
                    c_dist="uniform", seed=9)
