@@ -44,16 +44,17 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = {"f32": 157.3, "f16": 2516.6, "bf16": 2516.6,     # MI355X dense matrix peaks
-               "i8": 5000.0}                                     # (int8: TOP/s)
+               "i8": 5000.0, "f64": 78.6}                        # (int8: TOP/s)
 PEAK_HBM_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 COPY_PROBE_BYTES = 256 << 20
 PRIMARY = "sgemm_4096"
 CASES = ("sgemm_256", "sgemm_4096", "sgemm_ragged", "gemm_bf16_8192", "gemm_f16_8192",
-         "qkt_batched", "qkt_batched_f16_out", "gemm_i8_8192")
+         "qkt_batched", "qkt_batched_f16_out", "gemm_i8_8192", "dgemm_4096")
 HBM_BOUND = ("qkt_batched", "qkt_batched_f16_out")
 MOPS_COUNTER = {"f32": "SQ_INSTS_VALU_MFMA_MOPS_F32", "f16": "SQ_INSTS_VALU_MFMA_MOPS_F16",
-                "bf16": "SQ_INSTS_VALU_MFMA_MOPS_BF16", "i8": "SQ_INSTS_VALU_MFMA_MOPS_I8"}
+                "bf16": "SQ_INSTS_VALU_MFMA_MOPS_BF16", "i8": "SQ_INSTS_VALU_MFMA_MOPS_I8",
+                "f64": "SQ_INSTS_VALU_MFMA_MOPS_F64"}
 UTIL_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE",
                  "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
 N_SIMD = 256 * 4
@@ -71,7 +72,10 @@ def kernel_source_sha(dtype):
     """sha256 over the sources one dtype's kernels are built from."""
     csrc = os.path.join(ROOT, "dense_gemm_f32_amd", "csrc")
     h = hashlib.sha256()
-    for name in ("gemm_kernel.hpp", "variants.hpp", "kernels_%s.hip" % dtype):
+    names = ("gemm_kernel.hpp", "variants.hpp", "kernels_%s.hip" % dtype)
+    if dtype == "f64":
+        names += ("gemm_f64.hpp",)
+    for name in names:
         with open(os.path.join(csrc, name), "rb") as fh:
             h.update(name.encode())
             h.update(fh.read())
@@ -144,7 +148,8 @@ def summarize_case(case, d, copy_dir):
     p = wl.WORKLOADS[case]()
     info, grid = select_for(mg, p)
     kname = info["name"]
-    filt = "gemm_kernel"   # demangled for fp32; 16-bit instances stay mangled
+    # demangled for fp32; 16-bit instances stay mangled
+    filt = "gemm_f64_kernel" if p.dtype == "f64" else "gemm_kernel"
     durs = _dispatch_durations(os.path.join(d, "trace"), filt)
     timed = durs[PROFILE_WARMUP:] if len(durs) > PROFILE_WARMUP else durs  # after the warm-up
     fetch_v, _ = _counters(os.path.join(d, "fetch"), filt)
@@ -266,6 +271,14 @@ def make_device_problem(p, torch, dev):
 
 def launcher(p, dA, dB, dC):
     import dense_gemm_f32_amd as mg
+    if p.dtype == "f64":
+        if p.batch == 1:
+            return lambda: mg.gemm_f64(int(p.transA), int(p.transB), p.M, p.N, p.K, p.alpha, dA,
+                                       p.lda, dB, p.ldb, p.beta, dC, p.ldc)
+        return lambda: mg.gemm_f64_strided_batched(int(p.transA), int(p.transB), p.M, p.N, p.K,
+                                                   p.alpha, dA, p.lda, p.strideA, dB, p.ldb,
+                                                   p.strideB, p.beta, dC, p.ldc, p.strideC,
+                                                   p.batch)
     if p.c_dtype != "f32":
         return lambda: mg.gemm_strided_batched_ex(p.dtype, p.c_dtype, int(p.transA), int(p.transB),
                                                   p.M, p.N, p.K, p.alpha, dA, p.lda, p.strideA, dB,
@@ -406,7 +419,8 @@ def cpu_baseline(budget_s=15.0):
                      f"({flop / 1e9:.1f} GFLOP, fp64 accumulation, {t2:.1f} s)"}
     samples = {"sgemm_256": {}, "sgemm_ragged": {}, "gemm_bf16_8192": {"rows": threads},
                "gemm_f16_8192": {"rows": threads}, "qkt_batched": {"batches": 2},
-               "qkt_batched_f16_out": {"batches": 2}, "gemm_i8_8192": {"rows": threads}}
+               "qkt_batched_f16_out": {"batches": 2}, "gemm_i8_8192": {"rows": threads},
+               "dgemm_4096": {"rows": threads}}
     per = {}
     for name, kw in samples.items():
         q = wl.WORKLOADS[name]()

@@ -19,9 +19,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libmgemm.so")
 
 OP_N, OP_T = 0, 1
-F32, F16, BF16, I8, I32 = 0, 1, 2, 3, 4
-DTYPE_CODES = {"f32": F32, "f16": F16, "bf16": BF16, "i8": I8, "i32": I32}
-ELEM_SIZE = {F32: 4, F16: 2, BF16: 2, I8: 1, I32: 4}
+F32, F16, BF16, I8, I32, F64 = 0, 1, 2, 3, 4, 5
+DTYPE_CODES = {"f32": F32, "f16": F16, "bf16": BF16, "i8": I8, "i32": I32, "f64": F64}
+ELEM_SIZE = {F32: 4, F16: 2, BF16: 2, I8: 1, I32: 4, F64: 8}
 
 STATUS = {0: "MGEMM_OK", 1: "MGEMM_INVALID_ARG", 2: "MGEMM_HIP_ERROR"}
 
@@ -66,6 +66,12 @@ def load():
     lib.gemm_strided_batched.restype = i32
     lib.gemm_strided_batched.argtypes = [i32, i32, i32, i64, i64, i64, f32, vp, i64, i64, vp, i64,
                                          i64, f32, vp, i64, i64, i64, vp]
+    f64 = ctypes.c_double
+    lib.gemm_f64.restype = i32
+    lib.gemm_f64.argtypes = [i32, i32, i64, i64, i64, f64, vp, i64, vp, i64, f64, vp, i64, vp]
+    lib.gemm_f64_strided_batched.restype = i32
+    lib.gemm_f64_strided_batched.argtypes = [i32, i32, i64, i64, i64, f64, vp, i64, i64, vp, i64,
+                                             i64, f64, vp, i64, i64, i64, vp]
     lib.gemm_strided_batched_ex.restype = i32
     lib.gemm_strided_batched_ex.argtypes = [i32, i32, i32, i32, i64, i64, i64, f32, vp, i64, i64, vp,
                                             i64, i64, f32, vp, i64, i64, i64, vp]
@@ -134,12 +140,13 @@ def _check(status: int, what: str):
 
 def _single(name, dtype, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream):
     es = ELEM_SIZE[dtype]
+    ces = 8 if dtype == F64 else 4
     a_rows, a_cols = (K, M) if transA else (M, K)
     b_rows, b_cols = (N, K) if transB else (K, N)
     reads = M > 0 and N > 0 and K > 0 and alpha != 0.0
     pa, _ = _addr(A, _span(a_rows, a_cols, lda) if reads else 0, es, "A")
     pb, _ = _addr(B, _span(b_rows, b_cols, ldb) if reads else 0, es, "B")
-    pc, dev = _addr(C, _span(M, N, ldc), 4, "C")
+    pc, dev = _addr(C, _span(M, N, ldc), ces, "C")
     st = getattr(load(), name)(int(transA), int(transB), M, N, K, alpha, pa, lda, pb, ldb, beta,
                                pc, ldc, _stream(stream, dev))
     _check(st, name)
@@ -161,6 +168,26 @@ def gemm_bf16(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stre
     """bfloat16 A/B, fp32 accumulate and fp32 C."""
     _single("gemm_bf16", BF16, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
             stream)
+
+
+def gemm_f64(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None):
+    """double A, B, C, alpha and beta; fp64 matrix-core products."""
+    _single("gemm_f64", F64, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
+
+
+def gemm_f64_strided_batched(transA, transB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB,
+                             beta, C, ldc, strideC, batch, stream=None):
+    """Strided-batched fp64 GEMM (double alpha and beta)."""
+    a_rows, a_cols = (K, M) if transA else (M, K)
+    b_rows, b_cols = (N, K) if transB else (K, N)
+    reads = M > 0 and N > 0 and K > 0 and alpha != 0.0 and batch > 0
+    pa, _ = _addr(A, _extent(a_rows, a_cols, lda, strideA, batch) if reads else 0, 8, "A")
+    pb, _ = _addr(B, _extent(b_rows, b_cols, ldb, strideB, batch) if reads else 0, 8, "B")
+    pc, dev = _addr(C, _extent(M, N, ldc, strideC, batch), 8, "C")
+    st = load().gemm_f64_strided_batched(int(transA), int(transB), M, N, K, alpha, pa, lda, strideA,
+                                         pb, ldb, strideB, beta, pc, ldc, strideC, batch,
+                                         _stream(stream, dev))
+    _check(st, "gemm_f64_strided_batched")
 
 
 def gemm_strided_batched(in_dtype, transA, transB, M, N, K, alpha, A, lda, strideA, B, ldb,

@@ -1,0 +1,197 @@
+// fp64 GEMM on the CDNA4 matrix cores: C = alpha * op(A) * op(B) + beta * C
+// with double A, B, C, alpha and beta (the double x double -> double row of
+// the WMMA API page's type table, section "1. 概述").
+//
+// The instruction is v_mfma_f64_16x16x4_f64: a 16x16 block of D from 16x4 of
+// A and 4x16 of B.  Lane layout (pinned by an in-bounds one-wave probe):
+//   A[i][k] comes from lane 16k + i, B[k][j] from lane 16k + j, and register
+//   r of lane L holds D[4r + L/16][L%16].
+// The matrix cores run fp64 at the vector rate (78.6 TFLOP/s on MI355X,
+// 32 flop per clock per SIMD): one 16x16x4 block takes about 64 clocks, so
+// operand traffic per flop is small and a register-staged, double-buffered
+// tile keeps the matrix cores fed.  Every tile uses range-checked loads
+// (out-of-range elements read as zero), so edges and unaligned leading
+// dimensions need no second path.
+//
+// LDS holds both operands k-major, [BK][MN + 4] doubles: a fragment read has
+// lane (g = lane/16, i = lane%16) read row 4g + s, column i of its 16-wide
+// block.  The 4-double pad puts the two 16-lane groups of a 32-lane LDS
+// cycle 32 banks apart (row stride = 8 mod 64 dwords, rows 4 apart), so the
+// 8-byte reads are conflict-free.  The k-slot 4g + s of MFMA step s is the
+// same for A and B, which is all the dot product needs.
+#pragma once
+
+#include "gemm_kernel.hpp"
+
+namespace mgemm {
+
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+typedef double f64x2 __attribute__((ext_vector_type(2)));
+
+// One operand's tile for one K-slab: memory tile [R][CC] (CC contiguous);
+// KROW: memory rows are k (R = BK, CC = MN), else memory rows are m or n
+// (R = MN, CC = BK).  VEC doubles per global load (2 when 16-byte aligned).
+template <int MN, int BK, int NT, bool KROW, int VEC>
+struct F64Operand {
+    static constexpr int R = KROW ? BK : MN;
+    static constexpr int CC = KROW ? MN : BK;
+    static constexpr int VPR = CC / VEC;        // vectors per memory row
+    static constexpr int NPT = R * VPR / NT;    // vectors per thread
+    static_assert(NPT * NT == R * VPR, "tile not divisible among threads");
+    static constexpr int P = MN + 4;            // padded LDS row (doubles)
+    f64x2 regs[NPT];
+
+    __device__ __forceinline__ static int row_of(int tid, int q) { return (tid + q * NT) / VPR; }
+    __device__ __forceinline__ static int col_of(int tid, int q) { return ((tid + q * NT) % VPR) * VEC; }
+
+    // rows < rlim and columns < clim of the memory tile at `base` are in range.
+    __device__ __forceinline__ void load(const double *base, int64_t ld, int rlim, int clim, int tid)
+    {
+#pragma unroll
+        for (int q = 0; q < NPT; ++q) {
+            const int r = row_of(tid, q), c = col_of(tid, q);
+            const double *ptr = base + (int64_t)r * ld + c;
+            f64x2 v = {0.0, 0.0};
+            if (r < rlim) {
+                if constexpr (VEC == 2) {
+                    if (c + 1 < clim)
+                        v = *reinterpret_cast<const f64x2 *>(ptr);
+                    else if (c < clim)
+                        v[0] = ptr[0];
+                } else {
+                    if (c < clim) v[0] = ptr[0];
+                }
+            }
+            regs[q] = v;
+        }
+    }
+
+    // registers -> k-major LDS tile s[BK][P]
+    __device__ __forceinline__ void store(double *s, int tid) const
+    {
+#pragma unroll
+        for (int q = 0; q < NPT; ++q) {
+            const int r = row_of(tid, q), c = col_of(tid, q);
+            if constexpr (KROW) {          // memory row = k: already k-major
+                if constexpr (VEC == 2)
+                    *reinterpret_cast<f64x2 *>(s + r * P + c) = regs[q];
+                else
+                    s[r * P + c] = regs[q][0];
+            } else {                       // memory row = m/n: transpose into k rows
+                s[c * P + r] = regs[q][0];
+                if constexpr (VEC == 2) s[(c + 1) * P + r] = regs[q][1];
+            }
+        }
+    }
+};
+
+// BM x BN workgroup tile, WM x WN waves, each owning a (BM/WM) x (BN/WN)
+// sub-tile of TM x TN blocks of 16x16; BK-deep K-slabs (a multiple of 16).
+// V2: A and B allow 16-byte loads.
+template <int BM, int BN, int BK, int WM, int WN, bool TA, bool TB, bool V2>
+__global__ void __launch_bounds__(WM * WN * 64)
+gemm_f64_kernel(KernelArgs p)
+{
+    static_assert(BK % 16 == 0, "K-slab");
+    constexpr int NT = WM * WN * 64;
+    constexpr int WTM = BM / WM, WTN = BN / WN, TM = WTM / 16, TN = WTN / 16;
+    static_assert(TM * 16 * WM == BM && TN * 16 * WN == BN, "tile");
+    constexpr int VEC = V2 ? 2 : 1;
+    using OpA = F64Operand<BM, BK, NT, TA, VEC>;    // A^T in memory: rows are k
+    using OpB = F64Operand<BN, BK, NT, !TB, VEC>;   // B in memory: rows are k
+    constexpr int A_ELEMS = BK * OpA::P, B_ELEMS = BK * OpB::P, STAGE = A_ELEMS + B_ELEMS;
+    __shared__ __attribute__((aligned(16))) double smem[2 * STAGE];
+
+    int bidx, tm, tn;
+    map_tile(p, bidx, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    const int g = lane >> 4, li = lane & 15;
+
+    const double *Ap = static_cast<const double *>(p.A) + (int64_t)bidx * p.strideA +
+                       (TA ? (int64_t)m0 : (int64_t)m0 * p.lda);
+    const double *Bp = static_cast<const double *>(p.B) + (int64_t)bidx * p.strideB +
+                       (TB ? (int64_t)n0 * p.ldb : (int64_t)n0);
+    const int64_t a_kstep = TA ? (int64_t)BK * p.lda : (int64_t)BK;
+    const int64_t b_kstep = TB ? (int64_t)BK : (int64_t)BK * p.ldb;
+    const int mrem = p.M - m0, nrem = p.N - n0;
+
+    f64x4 acc[TM][TN];
+#pragma unroll
+    for (int t = 0; t < TM; ++t)
+#pragma unroll
+        for (int u = 0; u < TN; ++u)
+            acc[t][u] = f64x4{0.0, 0.0, 0.0, 0.0};
+
+    OpA la;
+    OpB lb;
+    auto load_slab = [&](int kt) {
+        const int krem = p.K - kt * BK;
+        const double *a = Ap + (int64_t)kt * a_kstep;
+        const double *b = Bp + (int64_t)kt * b_kstep;
+        if constexpr (TA) la.load(a, p.lda, krem, mrem, tid);
+        else              la.load(a, p.lda, mrem, krem, tid);
+        if constexpr (TB) lb.load(b, p.ldb, nrem, krem, tid);
+        else              lb.load(b, p.ldb, krem, nrem, tid);
+    };
+    // MFMA steps of k = 4; in each 16-deep group h of the slab, lane group g
+    // takes k = 16h + 4g + s at step s
+    auto compute = [&](int stage) {
+        const double *sa = smem + stage * STAGE + wm * WTM + li;
+        const double *sb = smem + stage * STAGE + A_ELEMS + wn * WTN + li;
+#pragma unroll
+        for (int hs = 0; hs < BK / 4; ++hs) {
+            const int kr = 16 * (hs >> 2) + 4 * g + (hs & 3);
+            double a[TM], b[TN];
+#pragma unroll
+            for (int t = 0; t < TM; ++t) a[t] = sa[kr * OpA::P + 16 * t];
+#pragma unroll
+            for (int u = 0; u < TN; ++u) b[u] = sb[kr * OpB::P + 16 * u];
+#pragma unroll
+            for (int t = 0; t < TM; ++t)
+#pragma unroll
+                for (int u = 0; u < TN; ++u)
+                    acc[t][u] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[t], b[u], acc[t][u], 0, 0, 0);
+        }
+    };
+
+    // two LDS stages; the next slab is fetched to registers during the current one
+    const int nk = (p.K + BK - 1) / BK;
+    load_slab(0);
+    la.store(smem, tid);
+    lb.store(smem + A_ELEMS, tid);
+    __syncthreads();
+    for (int kt = 0; kt + 1 < nk; ++kt) {
+        load_slab(kt + 1);
+        compute(kt & 1);
+        double *st = smem + ((kt + 1) & 1) * STAGE;
+        la.store(st, tid);
+        lb.store(st + A_ELEMS, tid);
+        __syncthreads();
+    }
+    compute((nk - 1) & 1);
+
+    // epilogue: C = alpha*acc + beta*C (C read only when beta != 0)
+    double *Cb = static_cast<double *>(p.C) + (int64_t)bidx * p.strideC;
+    const bool use_beta = p.beta_d != 0.0;
+#pragma unroll
+    for (int t = 0; t < TM; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = m0 + wm * WTM + 16 * t + 4 * r + g;
+            if (row >= p.M) continue;
+            double *crow = Cb + (int64_t)row * p.ldc;
+#pragma unroll
+            for (int u = 0; u < TN; ++u) {
+                const int col = n0 + wn * WTN + 16 * u + li;
+                if (col >= p.N) continue;
+                double v = p.alpha_d * acc[t][u][r];
+                if (use_beta) v += p.beta_d * crow[col];
+                __builtin_nontemporal_store(v, crow + col);
+            }
+        }
+}
+
+}  // namespace mgemm

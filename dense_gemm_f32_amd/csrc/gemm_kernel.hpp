@@ -65,7 +65,7 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 struct KernelArgs {
     const void *A;
     const void *B;
-    void *C;          // fp32, or the inputs' 16-bit type
+    void *C;          // fp32, the inputs' 16-bit type, int32 (int8 inputs) or double
     int64_t lda, ldb, ldc;
     int64_t strideA, strideB, strideC;
     int M, N, K;
@@ -75,6 +75,7 @@ struct KernelArgs {
     int alpha_i, beta_i;  // integral alpha and beta for int8 inputs (int32 C)
     int c_vec;        // C pointer/ldc/strideC allow one vector access per 4 elements
     int fast_ok;      // operand tiles addressable with 32-bit byte offsets
+    double alpha_d, beta_d;  // alpha and beta of fp64 GEMM
 };
 
 // ---------------------------------------------------------------------------
@@ -1059,7 +1060,7 @@ gemm_kernel(KernelArgs p)
 // beta == 0 writes zeros without reading C.
 template <typename CT>
 __global__ void __launch_bounds__(256) scale_c_kernel(CT *C, int M, int N, int64_t ldc,
-                                                      int64_t strideC, int batch, float beta,
+                                                      int64_t strideC, int batch, double beta,
                                                       int beta_i);
 
 }  // namespace mgemm

@@ -1,11 +1,13 @@
-// C = beta * C for the alpha == 0 and K == 0 cases (fp32, 16-bit or int32 C).
+// C = beta * C for the alpha == 0 and K == 0 cases (fp32, 16-bit, int32 or
+// double C).  beta arrives as a double; for fp32 and 16-bit C it is a float
+// widened on the host, and the product is formed in fp32 as before.
 #include "variants.hpp"
 
 namespace mgemm {
 
 template <typename CT>
 __global__ void __launch_bounds__(256) scale_c_kernel(CT *C, int M, int N, int64_t ldc,
-                                                      int64_t strideC, int batch, float beta,
+                                                      int64_t strideC, int batch, double beta,
                                                       int beta_i)
 {
     const int64_t total = (int64_t)batch * M * N;
@@ -17,13 +19,15 @@ __global__ void __launch_bounds__(256) scale_c_kernel(CT *C, int M, int N, int64
         CT *c = C + b * strideC + i * ldc + j;
         if constexpr (__is_same(CT, int32_t))  // int32 C: wrapping integer product
             __builtin_nontemporal_store(beta_i == 0 ? 0 : (int32_t)((uint32_t)beta_i * (uint32_t)*c), c);
+        else if constexpr (__is_same(CT, double))
+            __builtin_nontemporal_store(beta == 0.0 ? 0.0 : beta * *c, c);
         else
-            __builtin_nontemporal_store((CT)(beta == 0.0f ? 0.0f : beta * (float)*c), c);
+            __builtin_nontemporal_store((CT)(beta == 0.0 ? 0.0f : (float)beta * (float)*c), c);
     }
 }
 
 hipError_t launch_scale_c(int c_dtype, void *C, int M, int N, int64_t ldc, int64_t strideC, int batch,
-                          float beta, int beta_i, hipStream_t s)
+                          double beta, int beta_i, hipStream_t s)
 {
     const int64_t total = (int64_t)batch * M * N;
     int64_t blocks = (total + 255) / 256;
@@ -32,6 +36,7 @@ hipError_t launch_scale_c(int c_dtype, void *C, int M, int N, int64_t ldc, int64
     const void *fn = c_dtype == 1   ? reinterpret_cast<const void *>(&scale_c_kernel<_Float16>)
                      : c_dtype == 2 ? reinterpret_cast<const void *>(&scale_c_kernel<__bf16>)
                      : c_dtype == 4 ? reinterpret_cast<const void *>(&scale_c_kernel<int32_t>)
+                     : c_dtype == 5 ? reinterpret_cast<const void *>(&scale_c_kernel<double>)
                                     : reinterpret_cast<const void *>(&scale_c_kernel<float>);
     return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(256), args, 0, s);
 }

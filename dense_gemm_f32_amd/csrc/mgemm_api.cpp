@@ -22,30 +22,34 @@ struct Table {
 
 Table table_for(int dtype)
 {
-    int n32, n16, nb16, n8;
+    int n32, n16, nb16, n8, n64;
     const Variant *v32 = f32_variants(&n32);
     const Variant *v16 = f16_variants(&n16);
     const Variant *vb16 = bf16_variants(&nb16);
     const Variant *v8 = i8_variants(&n8);
+    const Variant *v64 = f64_variants(&n64);
     switch (dtype) {
     case MGEMM_F32: return {v32, n32, 0};
     case MGEMM_F16: return {v16, n16, n32};
     case MGEMM_BF16: return {vb16, nb16, n32 + n16};
     case MGEMM_I8: return {v8, n8, n32 + n16 + nb16};
+    case MGEMM_F64: return {v64, n64, n32 + n16 + nb16 + n8};
     default: return {nullptr, 0, 0};
     }
 }
 
-constexpr int N_IN_TYPES = 4;  // input types with a variant table: f32, f16, bf16, i8
-std::atomic<int> g_forced[N_IN_TYPES] = {{-1}, {-1}, {-1}, {-1}};
+// input types with a variant table: f32, f16, bf16, i8 and f64 (codes 0-3 and 5)
+constexpr int N_CODES = MGEMM_F64 + 1;
+std::atomic<int> g_forced[N_CODES] = {{-1}, {-1}, {-1}, {-1}, {-1}, {-1}};
 
-bool is_input_type(int dtype) { return dtype >= MGEMM_F32 && dtype <= MGEMM_I8; }
+bool is_input_type(int dtype) { return (dtype >= MGEMM_F32 && dtype <= MGEMM_I8) || dtype == MGEMM_F64; }
 
-int total_variants() { return table_for(MGEMM_I8).first_id + table_for(MGEMM_I8).n; }
+int total_variants() { return table_for(MGEMM_F64).first_id + table_for(MGEMM_F64).n; }
 
 const Variant *variant_by_id(int id)
 {
-    for (int d = 0; d < N_IN_TYPES; ++d) {
+    for (int d = 0; d < N_CODES; ++d) {
+        if (!is_input_type(d)) continue;
         Table t = table_for(d);
         if (id >= t.first_id && id < t.first_id + t.n) return &t.v[id - t.first_id];
     }
@@ -54,11 +58,11 @@ const Variant *variant_by_id(int id)
 
 int elem_size(int dtype)
 {
-    return dtype == MGEMM_F32 || dtype == MGEMM_I32 ? 4 : dtype == MGEMM_I8 ? 1 : 2;
+    return dtype == MGEMM_F64 ? 8 : dtype == MGEMM_F32 || dtype == MGEMM_I32 ? 4 : dtype == MGEMM_I8 ? 1 : 2;
 }
 
 // alpha or beta usable as an int32 multiplier (int8 inputs): integral and in range
-bool int32_scalar(float x) { return x == (float)(int64_t)x && x >= -2147483648.0f && x < 2147483648.0f; }
+bool int32_scalar(double x) { return x == (double)(int64_t)x && x >= -2147483648.0 && x < 2147483648.0; }
 
 // What a validated call will do.
 struct Plan {
@@ -75,13 +79,15 @@ bool aligned(const void *p, int64_t bytes) { return (reinterpret_cast<uintptr_t>
 int64_t span(int64_t rows, int64_t cols, int64_t ld) { return rows == 0 || cols == 0 ? 0 : (rows - 1) * ld + cols; }
 
 mgemm_status validate_and_plan(int dtype, int c_dtype, int transA, int transB, int64_t M, int64_t N,
-                               int64_t K, float alpha, const void *A, int64_t lda, int64_t strideA,
-                               const void *B, int64_t ldb, int64_t strideB, float beta,
+                               int64_t K, double alpha, const void *A, int64_t lda, int64_t strideA,
+                               const void *B, int64_t ldb, int64_t strideB, double beta,
                                const void *C, int64_t ldc, int64_t strideC, int64_t batch,
                                Plan *plan)
 {
     if (!is_input_type(dtype)) return MGEMM_INVALID_ARG;
-    if (dtype == MGEMM_I8) {
+    if (dtype == MGEMM_F64) {
+        if (c_dtype != MGEMM_F64) return MGEMM_INVALID_ARG;  // double C only
+    } else if (dtype == MGEMM_I8) {
         // int32 C; A and B K-contiguous; integral alpha and beta
         if (c_dtype != MGEMM_I32 || transA != MGEMM_OP_N || transB != MGEMM_OP_T) return MGEMM_INVALID_ARG;
         if (!int32_scalar(alpha) || !int32_scalar(beta)) return MGEMM_INVALID_ARG;
@@ -104,7 +110,7 @@ mgemm_status validate_and_plan(int dtype, int c_dtype, int transA, int transB, i
     }
     const int es = elem_size(dtype);
     const bool writes_c = M > 0 && N > 0 && batch > 0;
-    const bool reads_ab = writes_c && K > 0 && alpha != 0.0f;
+    const bool reads_ab = writes_c && K > 0 && alpha != 0.0;
     const int ces = elem_size(c_dtype);
     if (writes_c && (C == nullptr || !aligned(C, ces))) return MGEMM_INVALID_ARG;
     if (reads_ab && (A == nullptr || B == nullptr || !aligned(A, es) || !aligned(B, es)))
@@ -128,10 +134,12 @@ mgemm_status validate_and_plan(int dtype, int c_dtype, int transA, int transB, i
     a.M = (int)M;
     a.N = (int)N;
     a.K = (int)K;
-    a.alpha = alpha;
-    a.beta = beta;
+    a.alpha = (float)alpha;  // exact: the fp32/16-bit/int8 entry points take float scalars
+    a.beta = (float)beta;
     a.alpha_i = dtype == MGEMM_I8 ? (int)(int64_t)alpha : 0;
     a.beta_i = dtype == MGEMM_I8 ? (int)(int64_t)beta : 0;
+    a.alpha_d = alpha;
+    a.beta_d = beta;
     // a lane stores up to 4 adjacent C elements as one vector
     a.c_vec = aligned(C, 4 * ces) && ldc % 4 == 0 && (batch == 1 || strideC % 4 == 0);
     // Interior tiles address their operands with 32-bit byte offsets from the
@@ -210,14 +218,16 @@ void fill_info(const Variant &v, int id, mgemm_variant_info *out)
     out->waves_m = v.wm;
     out->waves_n = v.wn;
     out->threads = v.wm * v.wn * 64;
-    out->lds_bytes = 2 * (v.bm + v.bn) * v.bk * elem_size(v.dtype);
+    // two stages; fp64 rows carry a 4-element pad (gemm_f64.hpp)
+    const int pad = v.dtype == MGEMM_F64 ? 4 : 0;
+    out->lds_bytes = 2 * (v.bm + v.bn + 2 * pad) * v.bk * elem_size(v.dtype);
     out->pipe = v.pipe;
     std::snprintf(out->name, sizeof(out->name), "%s", v.name);
 }
 
 mgemm_status run(int dtype, int c_dtype, int transA, int transB, int64_t M, int64_t N, int64_t K,
-                 float alpha, const void *A, int64_t lda, int64_t strideA, const void *B,
-                 int64_t ldb, int64_t strideB, float beta, void *C, int64_t ldc, int64_t strideC,
+                 double alpha, const void *A, int64_t lda, int64_t strideA, const void *B,
+                 int64_t ldb, int64_t strideB, double beta, void *C, int64_t ldc, int64_t strideC,
                  int64_t batch, hipStream_t stream)
 {
     Plan plan;
@@ -229,8 +239,8 @@ mgemm_status run(int dtype, int c_dtype, int transA, int transB, int64_t M, int6
         err = launch_scale_c(c_dtype, C, (int)M, (int)N, ldc, strideC, (int)batch, beta,
                              plan.args.beta_i, stream);
     } else {
-        const LaunchFn fn = c_dtype == MGEMM_F32 || c_dtype == MGEMM_I32 ? plan.var->fn[transA][transB]
-                                                                          : plan.var->fn16[transA][transB];
+        const bool wide_c = c_dtype == MGEMM_F32 || c_dtype == MGEMM_I32 || c_dtype == MGEMM_F64;
+        const LaunchFn fn = wide_c ? plan.var->fn[transA][transB] : plan.var->fn16[transA][transB];
         if (fn == nullptr) return MGEMM_INVALID_ARG;
         err = fn(plan.args, (unsigned)plan.grid, stream);
     }
@@ -274,6 +284,7 @@ mgemm_status gemm_strided_batched(mgemm_dtype in_dtype, mgemm_op transA, mgemm_o
                                   int64_t strideB, float beta, float *C, int64_t ldc,
                                   int64_t strideC, int64_t batch, hipStream_t stream)
 {
+    if (in_dtype == MGEMM_F64) return MGEMM_INVALID_ARG;  // fp64 has its own entry points
     return run(in_dtype, MGEMM_F32, transA, transB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB,
                beta, C, ldc, strideC, batch, stream);
 }
@@ -284,8 +295,27 @@ mgemm_status gemm_strided_batched_ex(mgemm_dtype in_dtype, mgemm_dtype c_dtype, 
                                      int64_t ldb, int64_t strideB, float beta, void *C, int64_t ldc,
                                      int64_t strideC, int64_t batch, hipStream_t stream)
 {
+    if (in_dtype == MGEMM_F64) return MGEMM_INVALID_ARG;  // fp64 has its own entry points
     return run(in_dtype, c_dtype, transA, transB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB,
                beta, C, ldc, strideC, batch, stream);
+}
+
+mgemm_status gemm_f64(mgemm_op transA, mgemm_op transB, int64_t M, int64_t N, int64_t K,
+                      double alpha, const double *A, int64_t lda, const double *B, int64_t ldb,
+                      double beta, double *C, int64_t ldc, hipStream_t stream)
+{
+    return run(MGEMM_F64, MGEMM_F64, transA, transB, M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C,
+               ldc, 0, 1, stream);
+}
+
+mgemm_status gemm_f64_strided_batched(mgemm_op transA, mgemm_op transB, int64_t M, int64_t N,
+                                      int64_t K, double alpha, const double *A, int64_t lda,
+                                      int64_t strideA, const double *B, int64_t ldb,
+                                      int64_t strideB, double beta, double *C, int64_t ldc,
+                                      int64_t strideC, int64_t batch, hipStream_t stream)
+{
+    return run(MGEMM_F64, MGEMM_F64, transA, transB, M, N, K, alpha, A, lda, strideA, B, ldb,
+               strideB, beta, C, ldc, strideC, batch, stream);
 }
 
 const char *mgemm_status_string(mgemm_status s)
@@ -315,8 +345,8 @@ mgemm_status mgemm_select(mgemm_dtype in_dtype, mgemm_op transA, mgemm_op transB
                           int64_t batch, mgemm_variant_info *out, int64_t *grid)
 {
     Plan plan;
-    // the C type does not change the choice: fp32 (int32 for int8 inputs)
-    const int c_dtype = in_dtype == MGEMM_I8 ? MGEMM_I32 : MGEMM_F32;
+    // the C type does not change the choice: fp32 (int32 for int8, double for fp64 inputs)
+    const int c_dtype = in_dtype == MGEMM_I8 ? MGEMM_I32 : in_dtype == MGEMM_F64 ? MGEMM_F64 : MGEMM_F32;
     mgemm_status st = validate_and_plan(in_dtype, c_dtype, transA, transB, M, N, K, alpha, A, lda,
                                         strideA, B, ldb, strideB, beta, C, ldc, strideC, batch, &plan);
     if (st != MGEMM_OK) return st;

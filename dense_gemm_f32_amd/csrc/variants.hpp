@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include "gemm_f64.hpp"
 #include "gemm_kernel.hpp"
 
 namespace mgemm {
@@ -17,7 +18,7 @@ struct Variant {
     bool vec;             // needs 16-byte aligned A/B rows (dwordx4 loads)
     int pipe;             // DMA-path schedule (1: 4 stages of bk/2, 2: 2 stages of bk)
     const char *name;
-    LaunchFn fn[2][2];    // [transA][transB], fp32 C (int32 C for int8 inputs)
+    LaunchFn fn[2][2];    // [transA][transB], fp32 C (int32 C for int8, double C for fp64 inputs)
     LaunchFn fn16[2][2];  // [transA][transB], C in the inputs' 16-bit type (16-bit tables only)
 };
 
@@ -29,6 +30,24 @@ hipError_t launch_gemm(const KernelArgs &a, unsigned grid, hipStream_t s)
     return hipLaunchKernel(reinterpret_cast<const void *>(&gemm_kernel<T, BM, BN, BK, WM, WN, TA, TB, V, D, CT>),
                            dim3(grid), dim3(WM * WN * 64), args, 0, s);
 }
+
+template <int BM, int BN, int BK, int WM, int WN, bool TA, bool TB, bool V>
+hipError_t launch_gemm_f64(const KernelArgs &a, unsigned grid, hipStream_t s)
+{
+    KernelArgs copy = a;
+    void *args[] = {&copy};
+    return hipLaunchKernel(reinterpret_cast<const void *>(&gemm_f64_kernel<BM, BN, BK, WM, WN, TA, TB, V>),
+                           dim3(grid), dim3(WM * WN * 64), args, 0, s);
+}
+
+// fp64 inputs: double C
+#define MGEMM_VARIANT_F64(BM, BN, BK, WM, WN, V, NAME)                                       \
+    {5, BM, BN, BK, WM, WN, V, 1, NAME,                                                      \
+     {{launch_gemm_f64<BM, BN, BK, WM, WN, false, false, V>,                                \
+       launch_gemm_f64<BM, BN, BK, WM, WN, false, true, V>},                                \
+      {launch_gemm_f64<BM, BN, BK, WM, WN, true, false, V>,                                 \
+       launch_gemm_f64<BM, BN, BK, WM, WN, true, true, V>}},                                \
+     {{nullptr, nullptr}, {nullptr, nullptr}}}
 
 #define MGEMM_LAUNCHERS(T, BM, BN, BK, WM, WN, V, D, CT)                                     \
     {{launch_gemm<T, BM, BN, BK, WM, WN, false, false, V, D, CT>,                            \
@@ -61,8 +80,9 @@ const Variant *f32_variants(int *count);
 const Variant *f16_variants(int *count);
 const Variant *bf16_variants(int *count);
 const Variant *i8_variants(int *count);
+const Variant *f64_variants(int *count);
 
 hipError_t launch_scale_c(int c_dtype, void *C, int M, int N, int64_t ldc, int64_t strideC, int batch,
-                          float beta, int beta_i, hipStream_t s);
+                          double beta, int beta_i, hipStream_t s);
 
 }  // namespace mgemm

@@ -6,9 +6,10 @@ inputs from it.
 
 Recipe (one ``torch.Generator`` on the CPU per problem, seeded explicitly):
 draw A, then B, then C, each over its whole stored buffer (padding included).
-- ``"uniform"``: U[-1, 1) as ``2*rand - 1`` in fp32;
-- ``"normal"``:  N(0, 1) as ``randn`` in fp32, then rounded to the operand
-  type (round-to-nearest-even for bf16 / fp16);
+- ``"uniform"``: U[-1, 1) as ``2*rand - 1`` in fp32 (in fp64 for double
+  operands, so that every significand bit is drawn);
+- ``"normal"``:  N(0, 1) as ``randn`` in fp32 (fp64 for double operands),
+  then rounded to the operand type (round-to-nearest-even for bf16 / fp16);
 - ``"int"``:     integers uniform in [lo, hi] (``randint``), stored exactly
   in the operand type.
 
@@ -18,7 +19,9 @@ The named workloads follow the shapes the pages measure on:
 - a ragged SGEMM whose sizes are no multiple of any tile, with integer-valued
   operands in {0..99} (the residual-tile example of the CSDN tile-algorithm
   page, which fills with ``rand() % 100``);
-- 16-bit inputs with a float accumulator (WMMA API page, type table);
+- 16-bit inputs with a float accumulator, int8 inputs with an int32
+  accumulator and double inputs with a double accumulator (WMMA API page,
+  type table);
 - strided-batched QK^T with B stored [n, d] ("cuda11/matmul", section
   "Pytorch", the einsum 'bhqd,bhkd->bhqk' example), with fp32 C and, as the
   tutorial's Triton kernel stores its accumulator in C's own type, with a
@@ -34,13 +37,13 @@ import numpy as np
 import torch
 
 TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
-               "i8": torch.int8, "i32": torch.int32}
-ELEM_SIZE = {"f32": 4, "f16": 2, "bf16": 2, "i8": 1, "i32": 4}
+               "i8": torch.int8, "i32": torch.int32, "f64": torch.float64}
+ELEM_SIZE = {"f32": 4, "f16": 2, "bf16": 2, "i8": 1, "i32": 4, "f64": 8}
 
 
 @dataclasses.dataclass
 class Problem:
-    dtype: str                 # "f32" | "f16" | "bf16" | "i8" (operand type)
+    dtype: str                 # "f32" | "f16" | "bf16" | "i8" | "f64" (operand type)
     M: int
     N: int
     K: int
@@ -61,9 +64,12 @@ class Problem:
     strideB: Optional[int] = None
     strideC: Optional[int] = None
     pad_value: Optional[float] = None  # fill for padding beyond the logical matrix
-    c_dtype: str = "f32"       # C's type: "f32", the operand type for 16-bit output, "i32" for i8
+    c_dtype: str = "f32"       # C's type: "f32", the operand type for 16-bit output, "i32" for
+                               # i8; double operands always take "f64"
 
     def __post_init__(self):
+        if self.dtype == "f64":
+            self.c_dtype = "f64"
         a_rows, a_cols = (self.K, self.M) if self.transA else (self.M, self.K)
         b_rows, b_cols = (self.N, self.K) if self.transB else (self.K, self.N)
         self.a_rows, self.a_cols = a_rows, a_cols
@@ -104,22 +110,25 @@ class Problem:
         return self.buffer_elems(self.M, self.ldc, self.strideC)
 
     def tolerance_coeff(self) -> float:
-        """c in max|err| <= c * sqrt(K) * max|ref| (fp32: 1e-5, 16-bit: 2e-3, int8: 0)."""
-        return {"f32": 1e-5, "f16": 2e-3, "bf16": 2e-3, "i8": 0.0}[self.dtype]
+        """c in max|err| <= c * sqrt(K) * max|ref| (fp32: 1e-5, 16-bit: 2e-3, int8: 0;
+        fp64: the fp32 constant scaled by the ratio of unit roundoffs, 1e-5 * 2^-29)."""
+        return {"f32": 1e-5, "f16": 2e-3, "bf16": 2e-3, "i8": 0.0,
+                "f64": 1e-5 * 2.0 ** -29}[self.dtype]
 
     def output_rounding(self) -> float:
         """Relative rounding of the stored C: half an ulp of its type (0 for fp32,
         which the accumulator itself is)."""
-        return {"f32": 0.0, "f16": 2.0 ** -11, "bf16": 2.0 ** -8, "i32": 0.0}[self.c_dtype]
+        return {"f32": 0.0, "f16": 2.0 ** -11, "bf16": 2.0 ** -8, "i32": 0.0,
+                "f64": 0.0}[self.c_dtype]
 
 
-def _draw(gen, n, dist, lo, hi):
+def _draw(gen, n, dist, lo, hi, fdt=torch.float32):
     if dist == "uniform":
-        return 2.0 * torch.rand(n, generator=gen, dtype=torch.float32) - 1.0
+        return 2.0 * torch.rand(n, generator=gen, dtype=fdt) - 1.0
     if dist == "normal":
-        return torch.randn(n, generator=gen, dtype=torch.float32)
+        return torch.randn(n, generator=gen, dtype=fdt)
     if dist == "int":
-        return torch.randint(lo, hi + 1, (n,), generator=gen).to(torch.float32)
+        return torch.randint(lo, hi + 1, (n,), generator=gen).to(fdt)
     raise ValueError(f"unknown distribution {dist!r}")
 
 
@@ -140,10 +149,11 @@ def make_inputs(p: Problem):
     gen = torch.Generator()
     gen.manual_seed(p.seed)
     tdt = TORCH_DTYPE[p.dtype]
+    fdt = torch.float64 if p.dtype == "f64" else torch.float32
     bufs = []
     for elems, rows, cols, ld, stride in ((p.a_elems, p.a_rows, p.a_cols, p.lda, p.strideA),
                                           (p.b_elems, p.b_rows, p.b_cols, p.ldb, p.strideB)):
-        x = _draw(gen, elems, p.dist, p.int_lo, p.int_hi).to(tdt)
+        x = _draw(gen, elems, p.dist, p.int_lo, p.int_hi, fdt).to(tdt)
         if p.pad_value is not None and elems:
             mask = torch.from_numpy(_logical_mask(elems, p.batch, rows, cols, ld, stride))
             x[~mask] = p.pad_value
@@ -154,17 +164,17 @@ def make_inputs(p: Problem):
         if p.c_dtype == "i32":   # integer C: drawn as int64, stored exactly
             C0 = torch.randint(p.int_lo, p.int_hi + 1, (p.c_elems,), generator=gen).to(torch.int32)
         else:
-            C0 = _draw(gen, p.c_elems, cd, p.int_lo, p.int_hi)
-        if p.c_dtype not in ("f32", "i32"):
+            C0 = _draw(gen, p.c_elems, cd, p.int_lo, p.int_hi, fdt)
+        if p.c_dtype not in ("f32", "i32", "f64"):
             C0 = C0.to(TORCH_DTYPE[p.c_dtype])
     return bufs[0], bufs[1], C0
 
 
 def to_numpy_operand(x: torch.Tensor) -> np.ndarray:
-    """Operand buffer as numpy: float32 or int8 values, or uint16 bit patterns for 16-bit
-    types."""
+    """Operand buffer as numpy: float32, float64 or int8 values, or uint16 bit patterns for
+    16-bit types."""
     x = x.detach().cpu().contiguous()
-    if x.dtype in (torch.float32, torch.int8, torch.int32):
+    if x.dtype in (torch.float32, torch.float64, torch.int8, torch.int32):
         return x.numpy()
     return x.view(torch.int16).numpy().view(np.uint16)
 
@@ -207,6 +217,12 @@ def gemm_i8_8192() -> Problem:
                    c_dtype="i32", seed=1007)
 
 
+def dgemm_4096() -> Problem:
+    """DGEMM fp64 4096^3, A, B, C ~ U[-1,1) drawn in fp64, alpha=1.5, beta=0.5 (the SGEMM
+    workload's shape and scalars in the double row of the type table)."""
+    return Problem("f64", 4096, 4096, 4096, alpha=1.5, beta=0.5, dist="uniform", seed=1008)
+
+
 def qkt_batched_f16_out() -> Problem:
     """The attention-score batch with a binary16 C (fp32 accumulate, rounded on store)."""
     p = qkt_batched()
@@ -224,6 +240,7 @@ WORKLOADS = {
     "qkt_batched": qkt_batched,
     "qkt_batched_f16_out": qkt_batched_f16_out,
     "gemm_i8_8192": gemm_i8_8192,
+    "dgemm_4096": dgemm_4096,
 }
 
 

@@ -69,7 +69,8 @@ typedef enum {
     MGEMM_F16 = 1,
     MGEMM_BF16 = 2,
     MGEMM_I8 = 3,   /* int8 inputs (gemm_strided_batched_ex only) */
-    MGEMM_I32 = 4   /* int32 C of int8 inputs */
+    MGEMM_I32 = 4,  /* int32 C of int8 inputs */
+    MGEMM_F64 = 5   /* double A, B and C (gemm_f64* only) */
 } mgemm_dtype;
 
 /* Raw 16-bit storage: IEEE 754 binary16 and bfloat16 bit patterns. */
@@ -159,6 +160,38 @@ mgemm_status gemm_strided_batched_ex(mgemm_dtype in_dtype, mgemm_dtype c_dtype,
                                      float beta, void *C, int64_t ldc, int64_t strideC,
                                      int64_t batch, hipStream_t stream);
 
+/*
+ * DGEMM: double A, B, C, alpha and beta; double products and accumulation
+ * on the matrix cores (v_mfma_f64_16x16x4_f64).  The double x double ->
+ * double row of the WMMA API page's type table ("1. 概述").  Arguments,
+ * layouts, quick returns, ownership and errors as gemm_f32, with elements of
+ * 8 bytes (A, B, C aligned to 8; lda, ldb, ldc in elements).  Any leading
+ * dimension works; 16-byte aligned operand rows (A and B aligned to 16 and
+ * even lda, ldb) take the 16-byte load build.  The sum order differs from a
+ * sequential loop, so results match an exact evaluation to within rounding,
+ * and exactly whenever every partial sum is an integer below 2^53.
+ */
+mgemm_status gemm_f64(mgemm_op transA, mgemm_op transB,
+                      int64_t M, int64_t N, int64_t K, double alpha,
+                      const double *A, int64_t lda,
+                      const double *B, int64_t ldb,
+                      double beta, double *C, int64_t ldc,
+                      hipStream_t stream);
+
+/*
+ * Strided-batched DGEMM: gemm_strided_batched's batch rules (int64 element
+ * strides; strideA or strideB may be 0 to share the operand; strideC covers
+ * one M x N matrix) with gemm_f64's types.  gemm_strided_batched and
+ * gemm_strided_batched_ex, whose alpha and beta are float, refuse MGEMM_F64
+ * with MGEMM_INVALID_ARG.
+ */
+mgemm_status gemm_f64_strided_batched(mgemm_op transA, mgemm_op transB,
+                                      int64_t M, int64_t N, int64_t K, double alpha,
+                                      const double *A, int64_t lda, int64_t strideA,
+                                      const double *B, int64_t ldb, int64_t strideB,
+                                      double beta, double *C, int64_t ldc, int64_t strideC,
+                                      int64_t batch, hipStream_t stream);
+
 /* Human-readable text for a status code (static storage). */
 const char *mgemm_status_string(mgemm_status s);
 
@@ -194,7 +227,8 @@ mgemm_status mgemm_variant(int id, mgemm_variant_info *out);
  * after the same validation the entry points perform.  Returns the
  * validation status; *out and *grid are set on MGEMM_OK (id = -1 and grid = 0
  * when the call would launch no GEMM kernel).  C is taken as fp32 (int32
- * for MGEMM_I8 inputs); a 16-bit C selects the same variant.
+ * for MGEMM_I8 inputs, double for MGEMM_F64); a 16-bit C selects the same
+ * variant.
  */
 mgemm_status mgemm_select(mgemm_dtype in_dtype, mgemm_op transA, mgemm_op transB,
                           int64_t M, int64_t N, int64_t K, float alpha,

@@ -6,17 +6,20 @@ shares no code with it.
 
 The arithmetic lives in ``oracle.c`` (plain C, built with gcc): the textbook
 triple loop with an fp64 accumulator, summing over k in ascending order, then
-``alpha*acc + beta*C`` in fp64 (C unread when beta == 0).  This module only
-marshals numpy arrays into that library.
+``alpha*acc + beta*C`` in fp64 (C unread when beta == 0).  Double operands
+take the same loop in binary128 (``__float128``), rounded once to double at
+the end.  This module only marshals numpy arrays into that library.
 
 Sources: "Sgemm [128,128,8]" (jianshu), host_gemm and the kernel's design
 comment (C = alpha*A*B + beta*C, row-major); "cuda11/matmul" (dlog.com.cn),
 the CPU sgemm of section "什么是矩阵乘法"; WMMA API page (adg.csdn.net),
-"1. 概述" type table (16-bit inputs, float accumulator).
+"1. 概述" type table (16-bit inputs with a float accumulator, 8-bit integers
+with an int accumulator, doubles with a double accumulator).
 
 16-bit operands are passed as ``numpy.uint16`` arrays holding the raw
 binary16 / bfloat16 bit patterns; fp32 operands as ``numpy.float32``;
-int8 operands as ``numpy.int8`` (C then ``numpy.int32``).
+int8 operands as ``numpy.int8`` (C then ``numpy.int32``); double operands as
+``numpy.float64`` (C then ``numpy.float64``).
 """
 from __future__ import annotations
 
@@ -30,7 +33,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
-DTYPES = {"f32": 0, "f16": 1, "bf16": 2, "i8": 3}
+DTYPES = {"f32": 0, "f16": 1, "bf16": 2, "i8": 3, "f64": 5}
 
 _lib = None
 
@@ -131,7 +134,7 @@ def _ptr(a):
 
 
 def _check_operand(x, dtype):
-    want = {"f32": np.float32, "i8": np.int8}.get(dtype, np.uint16)
+    want = {"f32": np.float32, "i8": np.int8, "f64": np.float64}.get(dtype, np.uint16)
     if x.dtype != want:
         raise TypeError(f"{dtype} operand must be {np.dtype(want).name}, got {x.dtype}")
     if not x.flags.c_contiguous:
@@ -139,7 +142,7 @@ def _check_operand(x, dtype):
 
 
 def _check_c(C, dtype):
-    want = np.int32 if dtype == "i8" else np.float32
+    want = {"i8": np.int32, "f64": np.float64}.get(dtype, np.float32)
     if C is not None and (C.dtype != want or not C.flags.c_contiguous):
         raise TypeError(f"C must be a C-contiguous {np.dtype(want).name} buffer")
 

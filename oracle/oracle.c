@@ -21,8 +21,9 @@
  *   - op(A)/op(B) with an explicit stride per matrix ("matrices may be
  *     non-contiguous"): same tutorial, section "Triton", the wrapper that
  *     passes strides;
- *   - half and bfloat16 operands with a float accumulator, and 8-bit
- *     integer operands with an int accumulator:
+ *   - half and bfloat16 operands with a float accumulator, 8-bit integer
+ *     operands with an int accumulator, and double operands with a double
+ *     accumulator:
  *     WMMA API page (adg.csdn.net), "1. 概述", the element-type table.
  *
  * Readings taken where the pages are silent (each listed in the design doc):
@@ -37,6 +38,12 @@
  * ascending order.  The file must be built with -ffp-contract=off so that
  * the epilogue alpha*acc + beta*c is never fused.
  *
+ * Double operands (ORACLE_F64) take the same loop one precision up: the
+ * products and the sum are formed in IEEE binary128 (gcc's __float128, 113
+ * significand bits, where a product of two doubles is exact as a product of
+ * two floats is exact in fp64), then alpha*acc + beta*C in binary128, and
+ * the result is rounded once to double.  C is then double as well.
+ *
  * Parallelism: OpenMP over output rows only.  Each output element is still
  * computed by exactly the loop above, so the thread count cannot change a bit.
  */
@@ -50,6 +57,7 @@
 #define ORACLE_F16 1
 #define ORACLE_BF16 2
 #define ORACLE_I8 3   /* int8 A/B; C (when read) is int32 */
+#define ORACLE_F64 5  /* double A/B/C; accumulation in binary128 */
 
 #define ORACLE_OK 0
 #define ORACLE_BAD_ARG 1
@@ -159,7 +167,37 @@ static double op_b(int dtype, const void *B, int transB, int64_t k, int64_t j, i
     return transB ? load_elem(dtype, B, j, k, ldb) : load_elem(dtype, B, k, j, ldb);
 }
 
-static size_t elem_size(int dtype) { return dtype == ORACLE_F32 ? 4 : dtype == ORACLE_I8 ? 1 : 2; }
+static size_t elem_size(int dtype)
+{
+    return dtype == ORACLE_F64 ? 8 : dtype == ORACLE_F32 ? 4 : dtype == ORACLE_I8 ? 1 : 2;
+}
+
+/* C's element size: double for double inputs, otherwise 4 (fp32 or int32). */
+static size_t c_elem_size(int dtype) { return dtype == ORACLE_F64 ? 8 : 4; }
+
+/* Element (r, c) of a row-major double matrix, widened to binary128 (exact). */
+static __float128 load_f64(const void *base, int64_t r, int64_t c, int64_t ld)
+{
+    return (__float128)((const double *)base)[r * ld + c];
+}
+
+/* One output element for double operands: the definition in binary128,
+ * rounded to double at the end. */
+static double one_element_f64(int transA, int transB, int64_t K, double alpha,
+                              const void *A, int64_t lda, const void *B, int64_t ldb,
+                              double beta, const void *C, int64_t ldc, int64_t i, int64_t j)
+{
+    __float128 acc = 0;
+    for (int64_t k = 0; k < K; ++k) {
+        const __float128 a = transA ? load_f64(A, k, i, lda) : load_f64(A, i, k, lda);
+        const __float128 b = transB ? load_f64(B, j, k, ldb) : load_f64(B, k, j, ldb);
+        acc += a * b;
+    }
+    __float128 out = (__float128)alpha * acc;
+    if (beta != 0.0)
+        out = out + (__float128)beta * (__float128)((const double *)C)[i * ldc + j];
+    return (double)out;
+}
 
 /* One output element, exactly as the definition at the top of this file. */
 static double one_element(int dtype, int transA, int transB, int64_t K, double alpha,
@@ -167,6 +205,8 @@ static double one_element(int dtype, int transA, int transB, int64_t K, double a
                           double beta, const void *C, int64_t ldc,
                           int64_t i, int64_t j)
 {
+    if (dtype == ORACLE_F64)
+        return one_element_f64(transA, transB, K, alpha, A, lda, B, ldb, beta, C, ldc, i, j);
     double acc = 0.0;
     for (int64_t k = 0; k < K; ++k)
         acc += op_a(dtype, A, transA, i, k, lda) * op_b(dtype, B, transB, k, j, ldb);
@@ -179,7 +219,7 @@ static double one_element(int dtype, int transA, int transB, int64_t K, double a
 static int check_args(int dtype, int transA, int transB, int64_t M, int64_t N, int64_t K,
                       int64_t lda, int64_t ldb, int64_t ldc, int64_t batch)
 {
-    if (dtype < ORACLE_F32 || dtype > ORACLE_I8) return ORACLE_BAD_ARG;
+    if ((dtype < ORACLE_F32 || dtype > ORACLE_I8) && dtype != ORACLE_F64) return ORACLE_BAD_ARG;
     if ((transA != 0 && transA != 1) || (transB != 0 && transB != 1)) return ORACLE_BAD_ARG;
     if (M < 0 || N < 0 || K < 0 || batch < 0) return ORACLE_BAD_ARG;
     if (lda < (transA ? M : K) || ldb < (transB ? K : N) || ldc < N) return ORACLE_BAD_ARG;
@@ -209,7 +249,7 @@ int oracle_gemm(int dtype, int transA, int transB,
         int64_t b = row / M, i = row % M;
         const char *Ab = (const char *)A + (size_t)(b * strideA) * es;
         const char *Bb = (const char *)B + (size_t)(b * strideB) * es;
-        const char *Cb = C ? (const char *)C + (size_t)(b * strideC) * 4 : NULL;
+        const char *Cb = C ? (const char *)C + (size_t)(b * strideC) * c_elem_size(dtype) : NULL;
         for (int64_t j = 0; j < N; ++j)
             out[b * strideO + i * ldo + j] =
                 one_element(dtype, transA, transB, K, alpha, Ab, lda, Bb, ldb,
@@ -245,7 +285,7 @@ int oracle_gemm_elems(int dtype, int transA, int transB,
         int64_t b = bidx[e];
         const char *Ab = (const char *)A + (size_t)(b * strideA) * es;
         const char *Bb = (const char *)B + (size_t)(b * strideB) * es;
-        const char *Cb = C ? (const char *)C + (size_t)(b * strideC) * 4 : NULL;
+        const char *Cb = C ? (const char *)C + (size_t)(b * strideC) * c_elem_size(dtype) : NULL;
         out[e] = one_element(dtype, transA, transB, K, alpha, Ab, lda, Bb, ldb,
                              beta, Cb, ldc, iidx[e], jidx[e]);
     }

@@ -41,7 +41,16 @@ class Run:
 
     def launch(self, stream=None):
         p = self.p
-        if p.c_dtype != "f32":
+        if p.dtype == "f64":
+            if p.batch == 1 and p.strideA == p.a_rows * p.lda and not getattr(p, "force_batched", False):
+                mg.gemm_f64(int(p.transA), int(p.transB), p.M, p.N, p.K, p.alpha, self.dA, p.lda,
+                            self.dB, p.ldb, p.beta, self.dC, p.ldc, stream=stream)
+            else:
+                mg.gemm_f64_strided_batched(int(p.transA), int(p.transB), p.M, p.N, p.K, p.alpha,
+                                            self.dA, p.lda, p.strideA, self.dB, p.ldb, p.strideB,
+                                            p.beta, self.dC, p.ldc, p.strideC, p.batch,
+                                            stream=stream)
+        elif p.c_dtype != "f32":
             mg.gemm_strided_batched_ex(p.dtype, p.c_dtype, int(p.transA), int(p.transB), p.M, p.N,
                                        p.K, p.alpha, self.dA, p.lda, p.strideA, self.dB, p.ldb,
                                        p.strideB, p.beta, self.dC, p.ldc, p.strideC, p.batch,
@@ -81,7 +90,7 @@ class Run:
         return (p.dtype, p.transA, p.transB, p.M, p.N, p.K, p.alpha, wl.to_numpy_operand(self.A),
                 p.lda, wl.to_numpy_operand(self.B), p.ldb, p.beta,
                 None if self.C0 is None else
-                (self.C0.numpy() if p.c_dtype == "i32" else self.C0.float().numpy()), p.ldc)
+                (self.C0.numpy() if p.c_dtype in ("i32", "f64") else self.C0.float().numpy()), p.ldc)
 
     def oracle_full(self):
         p = self.p
@@ -114,7 +123,7 @@ def sample_positions(p: wl.Problem, n_random=20000, seed=0, tile=256):
 def expected_exact(p: wl.Problem, ref):
     """What an exact accumulation stores: the oracle's value, rounded to C's type
     (to nearest, ties to even) when C is 16-bit, wrapped to int32 for int8 inputs."""
-    if p.c_dtype == "f32":
+    if p.c_dtype in ("f32", "f64"):
         return ref
     if p.c_dtype == "i32":   # int8 inputs: the exact integer result wrapped to int32
         return oracle.wrap_i32(ref).astype(np.float64)
@@ -122,8 +131,9 @@ def expected_exact(p: wl.Problem, ref):
 
 
 def check_tolerance(got, ref, p: wl.Problem, what=""):
-    """max|err| <= (c*sqrt(K) + u)*max|ref| with c = 1e-5 (fp32 inputs) or 2e-3
-    (16-bit inputs) and u the rounding of a 16-bit C (half an ulp; 0 for fp32 C)."""
+    """max|err| <= (c*sqrt(K) + u)*max|ref| with c = 1e-5 (fp32 inputs), 2e-3 (16-bit
+    inputs) or 1e-5 * 2^-29 (fp64 inputs) and u the rounding of a 16-bit C (half an ulp;
+    0 for fp32 and double C)."""
     got = np.asarray(got, np.float64)
     assert not np.isnan(got).any(), f"{what}: NaN in output"
     err = float(np.max(np.abs(got - ref))) if ref.size else 0.0

@@ -32,9 +32,9 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for want in ("gemm_f32", "gemm_f16", "gemm_bf16", "gemm_strided_batched",
-                 "gemm_strided_batched_ex", "mgemm_status_string", "mgemm_select",
-                 "mgemm_force_variant"):
+    for want in ("gemm_f32", "gemm_f16", "gemm_bf16", "gemm_f64", "gemm_strided_batched",
+                 "gemm_strided_batched_ex", "gemm_f64_strided_batched", "mgemm_status_string",
+                 "mgemm_select", "mgemm_force_variant"):
         assert want in names
 
 
@@ -65,7 +65,7 @@ def test_variant_table():
         assert v["lds_bytes"] <= 160 * 1024
         assert v["pipe"] in (1, 2)
         assert v["name"].startswith("mgemm_")
-    assert {v["dtype"] for v in vs} == {0, 1, 2, 3}
+    assert {v["dtype"] for v in vs} == {0, 1, 2, 3, 5}
     info = _lib.VariantInfo()
     assert mg.load().mgemm_variant(len(vs), ctypes.byref(info)) == 1
 
@@ -164,6 +164,35 @@ def test_int8_rules_without_a_gpu():
     assert call(M=0) == 0 and call(M=0, alpha=-7.0, beta=2.0) == 0
     info, grid = sel("i8", 0, 1, M=8192, N=8192, K=8192)
     assert info["dtype"] == 3 and grid == 1024 and info["block_k"] == 128
+
+
+def test_fp64_rules_without_a_gpu():
+    lib = mg.load()
+    # fp64 has its own entry points (double scalars): the float-scalar ones refuse it
+    assert lib.gemm_strided_batched(5, 0, 0, 4, 4, 4, 1.0, ALIGNED, 4, 0, ALIGNED, 4, 0, 0.0,
+                                    ALIGNED, 4, 0, 1, None) == 1
+    assert lib.gemm_strided_batched_ex(5, 5, 0, 0, 4, 4, 4, 1.0, ALIGNED, 4, 0, ALIGNED, 4, 0,
+                                       0.0, ALIGNED, 4, 0, 1, None) == 1
+    f64 = lib.gemm_f64
+    # C aligned to 8 bytes; A and B to 8 bytes; the usual shape checks
+    assert f64(0, 0, 4, 4, 4, 1.0, ALIGNED, 4, ALIGNED, 4, 0.0, ALIGNED + 4, 4, None) == 1
+    assert f64(0, 0, 4, 4, 4, 1.0, ALIGNED + 4, 4, ALIGNED, 4, 0.0, ALIGNED, 4, None) == 1
+    assert f64(0, 0, 4, 4, 4, 1.0, ALIGNED, 3, ALIGNED, 4, 0.0, ALIGNED, 4, None) == 1
+    assert f64(0, 2, 4, 4, 4, 1.0, ALIGNED, 4, ALIGNED, 4, 0.0, ALIGNED, 4, None) == 1
+    # a non-float alpha (not representable in fp32) is fine: nothing to do returns OK
+    assert f64(0, 0, 0, 4, 4, 1.0 + 2 ** -40, None, 4, None, 4, 0.0, None, 4, None) == 0
+    bat = lib.gemm_f64_strided_batched
+    assert bat(0, 0, 4, 4, 4, 1.0, ALIGNED, 4, 16, ALIGNED, 4, 16, 0.0, ALIGNED, 4, 15, 2,
+               None) == 1                                      # C entries would overlap
+    assert bat(0, 0, 4, 4, 4, 1.0, ALIGNED, 4, 0, ALIGNED, 4, 0, 0.0, ALIGNED, 4, 16, 0,
+               None) == 0                                      # batch 0: nothing to do
+    info, grid = sel("f64", M=4096, N=4096, K=4096)
+    assert info["dtype"] == 5 and grid >= 256 and info["block_k"] == 16
+    # odd leading dimensions take the 8-byte-load build
+    info, _ = sel("f64", M=1000, N=1027, K=999, lda=999, ldb=1027, ldc=1027)
+    assert info["name"].endswith("_u")
+    info, _ = sel("f64", 1, 1, M=512, N=512, K=512)
+    assert not info["name"].endswith("_u")
 
 
 def test_force_variant_roundtrip():

@@ -1,8 +1,9 @@
 """GPU parity: the HIP path (through the C ABI) against the CPU oracle.
 
 Bar: bit-exact on integer-valued inputs whose partial sums stay below 2^24
-(the result is then unique); otherwise max|err| <= c*sqrt(K)*max|ref|, with
-c = 1e-5 for fp32 inputs and 2e-3 for f16/bf16 inputs.
+(2^53 for fp64 inputs; the result is then unique) and for int8; otherwise
+max|err| <= c*sqrt(K)*max|ref|, with c = 1e-5 for fp32 inputs, 2e-3 for
+f16/bf16 inputs and 1e-5 * 2^-29 for fp64 inputs.
 Small problems are compared element by element over the whole output; the
 full-size workloads, in the launch configuration the benchmark times, on
 sampled elements (whole boundary rows/columns plus random positions).
@@ -27,7 +28,7 @@ if torch.cuda.is_available():
 @pytest.fixture(autouse=True)
 def _auto_variant():
     yield
-    for dt in ("f32", "f16", "bf16", "i8"):
+    for dt in ("f32", "f16", "bf16", "i8", "f64"):
         mg.force_variant(dt, None)
 
 
@@ -81,7 +82,7 @@ def _assert_selected(p, v):
 
 
 def variants_of(dtype):
-    code = {"f32": 0, "f16": 1, "bf16": 2, "i8": 3}[dtype]
+    code = {"f32": 0, "f16": 1, "bf16": 2, "i8": 3, "f64": 5}[dtype]
     return [v for v in mg.variants() if v["dtype"] == code] if torch.cuda.is_available() else []
 
 
@@ -306,6 +307,70 @@ def test_i8_quick_returns_and_empty():
 
 def test_gemm_i8_8192():
     sampled_check(wl.gemm_i8_8192(), exact=True, what="int8 8192^3 -> int32")
+
+
+# ------------------------------------------------------------------ fp64 inputs
+
+def test_f64_every_variant_every_transpose():
+    # integer-valued doubles (every partial sum exact): bit-exact, with several
+    # tiles plus a ragged tail, padded (NaN) or odd leading dimensions
+    for v in variants_of("f64"):
+        mg.force_variant("f64", v["id"])
+        aligned = not v["name"].endswith("_u")
+        bm, bn = v["block_m"], v["block_n"]
+        for tA, tB in itertools.product((False, True), repeat=2):
+            M, N, K = 2 * bm + 19, bn + 37, 3 * 16 + 7
+            a_cols = M if tA else K
+            b_cols = K if tB else N
+            p = wl.Problem("f64", M, N, K, transA=tA, transB=tB, alpha=-1.5, beta=0.25,
+                           lda=_round8(a_cols) if aligned else a_cols + 1,
+                           ldb=_round8(b_cols) if aligned else b_cols + 3,
+                           ldc=N + 5, dist="int", int_lo=-1000, int_hi=1000, c_dist="int",
+                           seed=81, pad_value=float("nan"))
+            _assert_selected(p, v)
+            full_check(p, exact=True, what=f"{v['name']} f64 tA={int(tA)} tB={int(tB)}")
+
+
+def test_f64_float_inputs_within_tolerance():
+    for v in variants_of("f64"):
+        mg.force_variant("f64", v["id"])
+        aligned = not v["name"].endswith("_u")
+        for tA, tB in ((False, False), (True, True)):
+            M, N, K = 300, 221, 515
+            a_cols, b_cols = (M if tA else K), (K if tB else N)
+            p = wl.Problem("f64", M, N, K, transA=tA, transB=tB, alpha=1.5, beta=0.5,
+                           lda=_round8(a_cols) if aligned else a_cols + 1,
+                           ldb=_round8(b_cols) if aligned else b_cols + 1,
+                           dist="uniform", seed=82)
+            _assert_selected(p, v)
+            full_check(p, what=f"{v['name']} f64 uniform tA={int(tA)} tB={int(tB)}")
+
+
+def test_f64_batched_and_broadcast():
+    p = wl.Problem("f64", 130, 70, 90, transB=True, batch=5, alpha=2.0, beta=-1.0,
+                   dist="int", int_lo=-500, int_hi=500, c_dist="int", seed=83)
+    full_check(p, exact=True, what="f64 batched")
+    q = dataclasses.replace(p, strideA=0, seed=84)
+    q.force_batched = True
+    full_check(q, exact=True, what="f64 batched, A shared (stride 0)")
+
+
+def test_f64_quick_returns_and_nan_c():
+    for alpha, K in ((0.0, 64), (1.0, 0)):
+        p = wl.Problem("f64", 70, 90, K, alpha=alpha, beta=-0.75, dist="uniform", seed=85)
+        full_check(p, exact=True, what=f"f64 alpha={alpha} K={K}")
+    # beta == 0: C is never read, so NaN in C does not leak
+    p = wl.Problem("f64", 100, 80, 40, dist="int", int_lo=-9, int_hi=9, seed=86)
+    full_check(p, exact=True, c_fill=float("nan"), what="f64 beta=0 over NaN C")
+
+
+def test_dgemm_4096():
+    sampled_check(wl.dgemm_4096(), what="DGEMM 4096^3 alpha=1.5 beta=0.5")
+
+
+def test_dgemm_4096_integer_shadow():
+    sampled_check(wl.int_shadow(wl.dgemm_4096(), -1000, 1000), exact=True,
+                  what="DGEMM 4096^3 integer shadow")
 
 
 # ------------------------------------------------------------------ shapes from the pages

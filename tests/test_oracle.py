@@ -429,3 +429,142 @@ def test_workload_generators_are_seeded_and_shaped():
     assert (q.strideA, q.strideB, q.strideC, q.lda, q.ldb, q.ldc) == (
         65536, 65536, 1048576, 64, 64, 1024)
     assert q.alpha == 0.125
+
+
+# ---------------------------------------------------------------- double operands
+
+def _exact_f64(A, B, C, alpha, beta, tA, tB):
+    """alpha * op(A) op(B) + beta * C in exact rational arithmetic, rounded once to double."""
+    opA = A.T if tA else A
+    opB = B.T if tB else B
+    M, K = opA.shape
+    N = opB.shape[1]
+    out = np.empty((M, N))
+    for i in range(M):
+        for j in range(N):
+            acc = sum(Fraction(float(opA[i, k])) * Fraction(float(opB[k, j])) for k in range(K))
+            v = Fraction(alpha) * acc
+            if beta != 0.0:
+                v += Fraction(beta) * Fraction(float(C[i, j]))
+            out[i, j] = float(v)        # Fraction -> float rounds to nearest
+    return out
+
+
+@pytest.mark.parametrize("tA,tB", list(itertools.product((False, True), repeat=2)))
+def test_f64_equals_exact_rational_rounded_once(tA, tB):
+    # full 53-bit significands of mixed magnitude, alpha/beta not representable in fp32
+    rng = np.random.default_rng(41)
+    M, N, K = 9, 7, 33
+    A = rng.standard_normal((K, M) if tA else (M, K)) * np.exp2(rng.integers(-20, 20, (K, M) if tA else (M, K)))
+    B = rng.standard_normal((N, K) if tB else (K, N))
+    C = rng.standard_normal((M, N))
+    alpha, beta = 1.0 + 2.0 ** -40, -0.3
+    got = oracle.gemm("f64", tA, tB, M, N, K, alpha, A.ravel(), A.shape[1], B.ravel(), B.shape[1],
+                      beta, C.ravel(), N)[0]
+    assert np.array_equal(got, _exact_f64(A, B, C, alpha, beta, tA, tB))
+
+
+def test_f64_accumulates_beyond_double_precision():
+    # 2^60 + 1 - 2^60: a double accumulator loses the 1, the definition keeps it
+    A = np.array([[2.0 ** 60, 1.0, -(2.0 ** 60)]])
+    B = np.ones((3, 1))
+    got = oracle.gemm("f64", False, False, 1, 1, 3, 1.0, A.ravel(), 3, B.ravel(), 1, 0.0, None, 1)
+    assert got[0, 0, 0] == 1.0
+    # a product whose low half lies below a double's ulp: (1 + 2^-30)^2 - 1 - 2^-29 = 2^-60
+    x = 1.0 + 2.0 ** -30
+    A = np.array([[x, -1.0, -(2.0 ** -29)]])
+    B = np.array([[x], [1.0], [1.0]])
+    got = oracle.gemm("f64", False, False, 1, 1, 3, 1.0, A.ravel(), 3, B.ravel(), 1, 0.0, None, 1)
+    assert got[0, 0, 0] == 2.0 ** -60
+
+
+@pytest.mark.parametrize("tA,tB", list(itertools.product((False, True), repeat=2)))
+def test_f64_integer_products_match_numpy_int64(tA, tB):
+    rng = np.random.default_rng(43)
+    M, N, K = 23, 31, 77
+    Ai = rng.integers(-2 ** 20, 2 ** 20, (K, M) if tA else (M, K))
+    Bi = rng.integers(-2 ** 20, 2 ** 20, (N, K) if tB else (K, N))
+    Ci = rng.integers(-2 ** 40, 2 ** 40, (M, N))
+    got = oracle.gemm("f64", tA, tB, M, N, K, 3.0, Ai.astype(np.float64).ravel(), Ai.shape[1],
+                      Bi.astype(np.float64).ravel(), Bi.shape[1], -2.0,
+                      Ci.astype(np.float64).ravel(), N)[0]
+    want = 3 * ((Ai.T if tA else Ai) @ (Bi.T if tB else Bi)) - 2 * Ci   # |want| < 2^53
+    assert np.abs(want).max() < 2 ** 53
+    assert np.array_equal(got, want.astype(np.float64))
+
+
+def test_f64_batched_strides_padding_and_elems():
+    rng = np.random.default_rng(45)
+    M, N, K, batch, lda, ldb, ldc = 6, 5, 11, 3, 13, 7, 9
+    sA, sB, sC = M * lda + 4, K * ldb + 2, M * ldc + 1
+    A = np.full(batch * sA, np.nan)
+    B = np.full(batch * sB, np.nan)
+    C = np.full(batch * sC, np.nan)
+    Al = rng.integers(-9, 9, (batch, M, K)).astype(np.float64)
+    Bl = rng.integers(-9, 9, (batch, K, N)).astype(np.float64)
+    Cl = rng.integers(-9, 9, (batch, M, N)).astype(np.float64)
+    for b in range(batch):
+        for i in range(M):
+            A[b * sA + i * lda:b * sA + i * lda + K] = Al[b, i]
+            C[b * sC + i * ldc:b * sC + i * ldc + N] = Cl[b, i]
+        for k in range(K):
+            B[b * sB + k * ldb:b * sB + k * ldb + N] = Bl[b, k]
+    out = oracle.gemm("f64", False, False, M, N, K, 0.5, A, lda, B, ldb, 2.0, C, ldc,
+                      batch=batch, strideA=sA, strideB=sB, strideC=sC)
+    want = 0.5 * np.einsum("bik,bkj->bij", Al, Bl) + 2.0 * Cl     # small integers: exact
+    assert np.array_equal(out, want)
+    bi = rng.integers(0, batch, 40)
+    ii = rng.integers(0, M, 40)
+    jj = rng.integers(0, N, 40)
+    el = oracle.gemm_elems("f64", False, False, M, N, K, 0.5, A, lda, B, ldb, 2.0, C, ldc,
+                           bi, ii, jj, batch=batch, strideA=sA, strideB=sB, strideC=sC)
+    assert np.array_equal(el, out[bi, ii, jj])
+
+
+def test_f64_operands_must_be_float64():
+    a = np.zeros(4, np.float32)
+    with pytest.raises(TypeError):
+        oracle.gemm("f64", False, False, 2, 2, 2, 1.0, a, 2, a, 2, 0.0, None, 2)
+    d = np.zeros(4)
+    with pytest.raises(TypeError):
+        oracle.gemm("f64", False, False, 2, 2, 2, 1.0, d, 2, d, 2, 1.0, np.zeros(4, np.float32), 2)
+
+
+def _f64_pins_hold(gemm):
+    """The fp64 pins above against a given oracle callable."""
+    try:
+        rng = np.random.default_rng(47)
+        for tA, tB in itertools.product((False, True), repeat=2):
+            A = rng.standard_normal((6, 5) if tA else (5, 6))
+            B = rng.standard_normal((4, 6) if tB else (6, 4))
+            C = rng.standard_normal((5, 4))
+            got = gemm("f64", tA, tB, 5, 4, 6, 0.7, A.ravel(), A.shape[1], B.ravel(), B.shape[1],
+                       1.5, C.ravel(), 4)[0]
+            if not np.array_equal(got, _exact_f64(A, B, C, 0.7, 1.5, tA, tB)):
+                return False
+        A = np.array([2.0 ** 60, 1.0, -(2.0 ** 60)])
+        if gemm("f64", False, False, 1, 1, 3, 1.0, A, 3, np.ones(3), 1, 0.0, None, 1)[0, 0, 0] != 1.0:
+            return False
+    except Exception:
+        return False
+    return True
+
+
+def test_f64_pins_catch_planted_mistakes():
+    assert _f64_pins_hold(oracle.gemm)
+
+    def double_accumulator(dtype, tA, tB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, **kw):
+        opA = A.reshape(-1, lda)[:, :(M if tA else K)]
+        opA = opA.T if tA else opA
+        opB = B.reshape(-1, ldb)[:, :(K if tB else N)]
+        opB = opB.T if tB else opB
+        out = alpha * (opA @ opB)
+        if beta != 0.0:
+            out = out + beta * C.reshape(-1, ldc)[:, :N]
+        return out[None]
+
+    def ignore_trans_b(dtype, tA, tB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, **kw):
+        return oracle.gemm(dtype, tA, False, M, N, K, alpha, A, lda, B, N, beta, C, ldc, **kw)
+
+    for broken in (double_accumulator, ignore_trans_b):
+        assert not _f64_pins_hold(broken), broken.__name__
