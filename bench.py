@@ -49,8 +49,8 @@ PEAK_HBM_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 COPY_PROBE_BYTES = 256 << 20
 PRIMARY = "sgemm_4096"
-CASES = ("sgemm_256", "sgemm_4096", "sgemm_ragged", "gemm_bf16_8192", "gemm_f16_8192",
-         "qkt_batched", "qkt_batched_f16_out", "gemm_i8_8192", "dgemm_4096")
+CASES = ("sgemm_256", "sgemm_4096", "sgemm_ragged", "sgemm_ragged_splitk", "gemm_bf16_8192",
+         "gemm_f16_8192", "qkt_batched", "qkt_batched_f16_out", "gemm_i8_8192", "dgemm_4096")
 HBM_BOUND = ("qkt_batched", "qkt_batched_f16_out")
 MOPS_COUNTER = {"f32": "SQ_INSTS_VALU_MFMA_MOPS_F32", "f16": "SQ_INSTS_VALU_MFMA_MOPS_F16",
                 "bf16": "SQ_INSTS_VALU_MFMA_MOPS_BF16", "i8": "SQ_INSTS_VALU_MFMA_MOPS_I8",
@@ -203,6 +203,14 @@ def summarize_case(case, d, copy_dir):
         "tflops_at_average: " + _fmt(tflops, "%.2f"),
         "frac_matrix_peak: " + _fmt(tflops / PEAK_TFLOPS[dt] if tflops else None, "%.4f"),
     ]
+    if p.splitk is not None:   # the chunk products above, then one reduction kernel
+        red = _dispatch_durations(os.path.join(d, "trace"), "splitk_reduce")
+        red = red[PROFILE_WARMUP:] if len(red) > PROFILE_WARMUP else red
+        ravg = _mean(red)
+        both = p.flops / ((avg + ravg) * 1e-9) / 1e12 if avg and ravg else None
+        lines += ["splitk_chunks: %d" % mg.splitk_chunks(dt, p.M, p.N, p.K, p.splitk),
+                  "reduce_kernel_average_ns: " + _fmt(ravg, "%.0f"),
+                  "tflops_both_kernels: " + _fmt(both, "%.2f")]
     if case in HBM_BOUND and avg:
         gbs = algo / (avg * 1e-9) / 1e9
         lines += ["algorithmic_gbs_at_average: %.1f" % gbs,
@@ -255,6 +263,12 @@ def copy_probe():
 # ---------------------------------------------------------------------------- timing
 
 def select_for(mg, p, ptrs=(1 << 20, 1 << 20, 1 << 20)):
+    """(variant info, grid) of the GEMM kernel a workload launches (for split-K: the
+    partial-product kernel)."""
+    if p.splitk is not None:
+        info, grid, _, _ = mg.splitk_select(p.dtype, int(p.transA), int(p.transB), p.M, p.N, p.K,
+                                            ptrs[0], p.lda, ptrs[1], p.ldb, p.splitk)
+        return info, grid
     return mg.select(p.dtype, int(p.transA), int(p.transB), p.M, p.N, p.K, p.alpha, ptrs[0],
                      p.lda, p.strideA, ptrs[1], p.ldb, p.strideB, p.beta, ptrs[2], p.ldc,
                      p.strideC, p.batch)
@@ -271,6 +285,13 @@ def make_device_problem(p, torch, dev):
 
 def launcher(p, dA, dB, dC):
     import dense_gemm_f32_amd as mg
+    if p.splitk is not None:
+        import torch
+        ws = torch.empty(max(mg.splitk_workspace_bytes(p.dtype, p.M, p.N, p.K, p.splitk), 16),
+                         dtype=torch.uint8, device=dA.device)   # allocated once, outside the timing
+        return lambda: mg.gemm_splitk(p.dtype, p.c_dtype, int(p.transA), int(p.transB), p.M, p.N,
+                                      p.K, p.alpha, dA, p.lda, dB, p.ldb, p.beta, dC, p.ldc,
+                                      splits=p.splitk, workspace=ws)
     if p.dtype == "f64":
         if p.batch == 1:
             return lambda: mg.gemm_f64(int(p.transA), int(p.transB), p.M, p.N, p.K, p.alpha, dA,

@@ -72,6 +72,17 @@ def load():
     lib.gemm_f64_strided_batched.restype = i32
     lib.gemm_f64_strided_batched.argtypes = [i32, i32, i64, i64, i64, f64, vp, i64, i64, vp, i64,
                                              i64, f64, vp, i64, i64, i64, vp]
+    lib.gemm_splitk.restype = i32
+    lib.gemm_splitk.argtypes = [i32, i32, i32, i32, i64, i64, i64, f64, vp, i64, vp, i64, f64, vp,
+                                i64, i64, vp, i64, vp]
+    lib.mgemm_splitk_chunks.restype = i64
+    lib.mgemm_splitk_chunks.argtypes = [i32, i64, i64, i64, i64]
+    lib.mgemm_splitk_select.restype = i32
+    lib.mgemm_splitk_select.argtypes = [i32, i32, i32, i64, i64, i64, vp, i64, vp, i64, i64,
+                                        ctypes.POINTER(VariantInfo), ctypes.POINTER(i64),
+                                        ctypes.POINTER(i64), ctypes.POINTER(i64)]
+    lib.mgemm_splitk_workspace_bytes.restype = i64
+    lib.mgemm_splitk_workspace_bytes.argtypes = [i32, i64, i64, i64, i64]
     lib.gemm_strided_batched_ex.restype = i32
     lib.gemm_strided_batched_ex.argtypes = [i32, i32, i32, i32, i64, i64, i64, f32, vp, i64, i64, vp,
                                             i64, i64, f32, vp, i64, i64, i64, vp]
@@ -223,6 +234,66 @@ def gemm_strided_batched_ex(in_dtype, c_dtype, transA, transB, M, N, K, alpha, A
                                         strideA, pb, ldb, strideB, beta, pc, ldc, strideC, batch,
                                         _stream(stream, dev))
     _check(st, "gemm_strided_batched_ex")
+
+
+def splitk_chunks(in_dtype, M, N, K, splits=0):
+    """K-chunks gemm_splitk runs (1: the plain kernel)."""
+    n = load().mgemm_splitk_chunks(DTYPE_CODES.get(in_dtype, in_dtype), M, N, K, splits)
+    if n < 0:
+        raise MgemmError(1, "mgemm_splitk_chunks")
+    return n
+
+
+def splitk_workspace_bytes(in_dtype, M, N, K, splits=0):
+    """Workspace bytes gemm_splitk needs (0 when one chunk runs)."""
+    n = load().mgemm_splitk_workspace_bytes(DTYPE_CODES.get(in_dtype, in_dtype), M, N, K, splits)
+    if n < 0:
+        raise MgemmError(1, "mgemm_splitk_workspace_bytes")
+    return n
+
+
+def splitk_select(in_dtype, transA, transB, M, N, K, A=1 << 20, lda=None, B=1 << 20, ldb=None,
+                  splits=0):
+    """(variant info of the partial-product launch, grid, chunks, chunk length)."""
+    dt = DTYPE_CODES.get(in_dtype, in_dtype)
+    lda = lda if lda is not None else (M if transA else K)
+    ldb = ldb if ldb is not None else (K if transB else N)
+    info = VariantInfo()
+    grid, chunks, ks = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    st = load().mgemm_splitk_select(dt, int(transA), int(transB), M, N, K, A, lda, B, ldb, splits,
+                                    ctypes.byref(info), ctypes.byref(grid), ctypes.byref(chunks),
+                                    ctypes.byref(ks))
+    _check(st, "mgemm_splitk_select")
+    return info.as_dict(), grid.value, chunks.value, ks.value
+
+
+def gemm_splitk(in_dtype, c_dtype, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                splits=0, workspace=None, stream=None):
+    """Split-K GEMM (single matrix).  `workspace` is a device tensor (or int address) of at
+    least splitk_workspace_bytes(...) bytes; None allocates one with torch on C's device."""
+    dt = DTYPE_CODES.get(in_dtype, in_dtype)
+    ct = DTYPE_CODES.get(c_dtype, c_dtype)
+    es = ELEM_SIZE[dt]
+    a_rows, a_cols = (K, M) if transA else (M, K)
+    b_rows, b_cols = (N, K) if transB else (K, N)
+    reads = M > 0 and N > 0 and K > 0 and alpha != 0.0
+    pa, _ = _addr(A, _span(a_rows, a_cols, lda) if reads else 0, es, "A")
+    pb, _ = _addr(B, _span(b_rows, b_cols, ldb) if reads else 0, es, "B")
+    pc, dev = _addr(C, _span(M, N, ldc), ELEM_SIZE.get(ct, 4), "C")
+    need = splitk_workspace_bytes(dt, M, N, K, splits) if splits >= 0 else 0
+    if workspace is None and need > 0:
+        import torch
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace is None:
+        pw, wbytes = None, 0
+    elif isinstance(workspace, int):
+        pw, wbytes = workspace, need
+    else:
+        pw, _ = _addr(workspace, 0, workspace.element_size(), "workspace")
+        wbytes = workspace.numel() * workspace.element_size()
+    st = load().gemm_splitk(dt, ct, int(transA), int(transB), M, N, K, alpha, pa, lda, pb, ldb, beta,
+                            pc, ldc, splits, pw, wbytes, _stream(stream, dev))
+    _check(st, "gemm_splitk")
 
 
 # --------------------------------------------------------------------------- introspection

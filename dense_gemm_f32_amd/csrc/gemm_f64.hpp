@@ -117,6 +117,7 @@ gemm_f64_kernel(KernelArgs p)
     const int64_t a_kstep = TA ? (int64_t)BK * p.lda : (int64_t)BK;
     const int64_t b_kstep = TB ? (int64_t)BK : (int64_t)BK * p.ldb;
     const int mrem = p.M - m0, nrem = p.N - n0;
+    const int K = bidx == p.tail_batch ? p.k_tail : p.K;  // split-K's last chunk may be shorter
 
     f64x4 acc[TM][TN];
 #pragma unroll
@@ -128,7 +129,7 @@ gemm_f64_kernel(KernelArgs p)
     OpA la;
     OpB lb;
     auto load_slab = [&](int kt) {
-        const int krem = p.K - kt * BK;
+        const int krem = K - kt * BK;
         const double *a = Ap + (int64_t)kt * a_kstep;
         const double *b = Bp + (int64_t)kt * b_kstep;
         if constexpr (TA) la.load(a, p.lda, krem, mrem, tid);
@@ -158,7 +159,7 @@ gemm_f64_kernel(KernelArgs p)
     };
 
     // two LDS stages; the next slab is fetched to registers during the current one
-    const int nk = (p.K + BK - 1) / BK;
+    const int nk = (K + BK - 1) / BK;
     load_slab(0);
     la.store(smem, tid);
     lb.store(smem + A_ELEMS, tid);

@@ -76,6 +76,7 @@ struct KernelArgs {
     int c_vec;        // C pointer/ldc/strideC allow one vector access per 4 elements
     int fast_ok;      // operand tiles addressable with 32-bit byte offsets
     double alpha_d, beta_d;  // alpha and beta of fp64 GEMM
+    int k_tail, tail_batch;  // batch entry tail_batch runs K = k_tail (split-K's last chunk); -1: none
 };
 
 // ---------------------------------------------------------------------------
@@ -1038,6 +1039,8 @@ gemm_kernel(KernelArgs p)
     int bidx, tm, tn;
     map_tile(p, bidx, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
+    KernelArgs pk = p;  // this workgroup's K: split-K's last chunk may be shorter
+    if (bidx == p.tail_batch) pk.K = p.k_tail;
     f32x16 acc[TM][TN];
 #pragma unroll
     for (int t = 0; t < TM; ++t)
@@ -1045,15 +1048,15 @@ gemm_kernel(KernelArgs p)
         for (int u = 0; u < TN; ++u)
             acc[t][u] = f32x16{};
     if constexpr (VECOK) {
-        const bool interior = p.fast_ok && m0 + BM <= p.M && n0 + BN <= p.N && p.K % D::BK == 0;
+        const bool interior = pk.fast_ok && m0 + BM <= pk.M && n0 + BN <= pk.N && pk.K % D::BK == 0;
         if (interior) {
-            D::run(p, smem, bidx, m0, n0, acc);
-            epilogue<false, D::IL_A, D::IL_B, TM, TN, WTM, WTN, WN, CT>(p, bidx, m0, n0, acc);
+            D::run(pk, smem, bidx, m0, n0, acc);
+            epilogue<false, D::IL_A, D::IL_B, TM, TN, WTM, WTN, WN, CT>(pk, bidx, m0, n0, acc);
             return;
         }
     }
-    R::run(p, smem, bidx, m0, n0, acc);
-    epilogue<true, R::IL_A, R::IL_B, TM, TN, WTM, WTN, WN, CT>(p, bidx, m0, n0, acc);
+    R::run(pk, smem, bidx, m0, n0, acc);
+    epilogue<true, R::IL_A, R::IL_B, TM, TN, WTM, WTN, WN, CT>(pk, bidx, m0, n0, acc);
 }
 
 // C = beta * C over a strided batch (alpha == 0 or K == 0), in C's own type.

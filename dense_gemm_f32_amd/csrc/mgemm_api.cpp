@@ -78,11 +78,14 @@ bool aligned(const void *p, int64_t bytes) { return (reinterpret_cast<uintptr_t>
 // Smallest element span one stored matrix occupies: (rows-1)*ld + cols.
 int64_t span(int64_t rows, int64_t cols, int64_t ld) { return rows == 0 || cols == 0 ? 0 : (rows - 1) * ld + cols; }
 
+// k_chunks: the batch entries are K-chunks of one operand pair (split-K's
+// partial products), so strideA/strideB step along K inside one matrix and
+// are not required to cover a whole matrix.
 mgemm_status validate_and_plan(int dtype, int c_dtype, int transA, int transB, int64_t M, int64_t N,
                                int64_t K, double alpha, const void *A, int64_t lda, int64_t strideA,
                                const void *B, int64_t ldb, int64_t strideB, double beta,
                                const void *C, int64_t ldc, int64_t strideC, int64_t batch,
-                               Plan *plan)
+                               Plan *plan, bool k_chunks = false)
 {
     if (!is_input_type(dtype)) return MGEMM_INVALID_ARG;
     if (dtype == MGEMM_F64) {
@@ -103,9 +106,11 @@ mgemm_status validate_and_plan(int dtype, int c_dtype, int transA, int transB, i
     if (lda < (a_cols > 1 ? a_cols : 1) || ldb < (b_cols > 1 ? b_cols : 1) || ldc < (N > 1 ? N : 1))
         return MGEMM_INVALID_ARG;
     if (strideA < 0 || strideB < 0 || strideC < 0) return MGEMM_INVALID_ARG;
-    if (batch > 1) {
+    if (batch > 1 && !k_chunks) {
         if (strideA != 0 && strideA < span(a_rows, a_cols, lda)) return MGEMM_INVALID_ARG;
         if (strideB != 0 && strideB < span(b_rows, b_cols, ldb)) return MGEMM_INVALID_ARG;
+    }
+    if (batch > 1) {
         if (M > 0 && N > 0 && strideC < span(M, N, ldc)) return MGEMM_INVALID_ARG;
     }
     const int es = elem_size(dtype);
@@ -140,6 +145,8 @@ mgemm_status validate_and_plan(int dtype, int c_dtype, int transA, int transB, i
     a.beta_i = dtype == MGEMM_I8 ? (int)(int64_t)beta : 0;
     a.alpha_d = alpha;
     a.beta_d = beta;
+    a.k_tail = a.K;
+    a.tail_batch = -1;
     // a lane stores up to 4 adjacent C elements as one vector
     a.c_vec = aligned(C, 4 * ces) && ldc % 4 == 0 && (batch == 1 || strideC % 4 == 0);
     // Interior tiles address their operands with 32-bit byte offsets from the
@@ -206,6 +213,105 @@ mgemm_status validate_and_plan(int dtype, int c_dtype, int transA, int transB, i
     plan->id = t.first_id + pick;
     plan->grid = grid;
     return MGEMM_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Split-K.  K is cut into chunks of ks (a multiple of the type's K-slab); the
+// partial products of the chunks go to the caller's workspace as a batch
+// ([splits][M][N], fp32 / int32 / double), then one reduction kernel forms
+// C = alpha * sum of the chunks (ascending) + beta * C.
+// ---------------------------------------------------------------------------
+int64_t k_granule(int dtype)
+{
+    return dtype == MGEMM_F32 ? 32 : dtype == MGEMM_I8 ? 128 : dtype == MGEMM_F64 ? 16 : 64;
+}
+
+int partial_dtype(int dtype) { return dtype == MGEMM_I8 ? MGEMM_I32 : dtype == MGEMM_F64 ? MGEMM_F64 : MGEMM_F32; }
+
+// chunk length for `splits` requested chunks, and the number of chunks it gives
+int64_t k_chunk(int dtype, int64_t K, int64_t splits, int64_t *used)
+{
+    const int64_t g = k_granule(dtype);
+    int64_t ks = (K + splits - 1) / splits;
+    ks = (ks + g - 1) / g * g;
+    if (ks < g) ks = g;
+    *used = (K + ks - 1) / ks;
+    return ks;
+}
+
+// Automatic split count, for deep-K shapes that leave the device idle: when
+// 128x128 tiles give fewer than 256 workgroups and K >= 2 max(M, N), enough
+// chunks for one workgroup per CU, each at least 512 deep; otherwise 1.
+// (Measured: 512x512x4096 fp32 91 -> 28 us with 8 chunks, 256x256x8192
+// 176 -> 24 us with 16; on 1024^3 and 256^3 the extra pass and the
+// workspace traffic cost more than the fuller grid gives.)
+int64_t auto_splits(int dtype, int64_t M, int64_t N, int64_t K)
+{
+    (void)dtype;
+    const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
+    if (tiles >= 256 || tiles == 0 || K < 2 * (M > N ? M : N)) return 1;
+    int64_t s = (256 + tiles - 1) / tiles;
+    const int64_t by_k = K / 512;
+    if (s > by_k) s = by_k;
+    return s < 1 ? 1 : s;
+}
+
+// The partial-product launch: `used` chunks of ks (the last K - (used-1)*ks)
+// as a batch over the workspace W = [used][M][N].
+mgemm_status plan_chunks(int dtype, int transA, int transB, int64_t M, int64_t N, int64_t K, int64_t ks,
+                         int64_t used, const void *A, int64_t lda, const void *B, int64_t ldb,
+                         const void *W, Plan *part)
+{
+    const int64_t sA = transA ? ks * lda : ks;  // chunk z starts at column (or row) z*ks
+    const int64_t sB = transB ? ks : ks * ldb;
+    mgemm_status st = validate_and_plan(dtype, partial_dtype(dtype), transA, transB, M, N, ks, 1.0, A,
+                                        lda, sA, B, ldb, sB, 0.0, W, N, M * N, used, part, true);
+    if (st != MGEMM_OK) return st;
+    if (part->kind != Plan::GEMM) return MGEMM_INVALID_ARG;
+    part->args.k_tail = (int)(K - (used - 1) * ks);
+    part->args.tail_batch = (int)(used - 1);
+    return MGEMM_OK;
+}
+
+mgemm_status run_splitk(int dtype, int c_dtype, int transA, int transB, int64_t M, int64_t N,
+                        int64_t K, double alpha, const void *A, int64_t lda, const void *B,
+                        int64_t ldb, double beta, void *C, int64_t ldc, int64_t splits,
+                        void *workspace, int64_t workspace_bytes, hipStream_t stream)
+{
+    if (splits < 0) return MGEMM_INVALID_ARG;
+    Plan full;
+    mgemm_status st = validate_and_plan(dtype, c_dtype, transA, transB, M, N, K, alpha, A, lda, 0, B,
+                                        ldb, 0, beta, C, ldc, 0, 1, &full);
+    if (st != MGEMM_OK || full.kind == Plan::NOTHING) return st;
+    int64_t used = 1, ks = K;
+    if (full.kind == Plan::GEMM) {
+        if (splits == 0) splits = auto_splits(dtype, M, N, K);
+        if (splits > 1) ks = k_chunk(dtype, K, splits, &used);
+    }
+    hipError_t err;
+    if (full.kind == Plan::SCALE) {
+        err = launch_scale_c(c_dtype, C, (int)M, (int)N, ldc, 0, 1, beta, full.args.beta_i, stream);
+        return err == hipSuccess ? MGEMM_OK : MGEMM_HIP_ERROR;
+    }
+    if (used <= 1) {  // one chunk: the plain kernel, no workspace
+        const bool wide_c = c_dtype == MGEMM_F32 || c_dtype == MGEMM_I32 || c_dtype == MGEMM_F64;
+        const LaunchFn fn = wide_c ? full.var->fn[transA][transB] : full.var->fn16[transA][transB];
+        if (fn == nullptr) return MGEMM_INVALID_ARG;
+        err = fn(full.args, (unsigned)full.grid, stream);
+        return err == hipSuccess ? MGEMM_OK : MGEMM_HIP_ERROR;
+    }
+    const int64_t need = used * M * N * elem_size(partial_dtype(dtype));
+    if (workspace == nullptr || !aligned(workspace, 16) || workspace_bytes < need) return MGEMM_INVALID_ARG;
+    Plan part;
+    st = plan_chunks(dtype, transA, transB, M, N, K, ks, used, A, lda, B, ldb, workspace, &part);
+    if (st != MGEMM_OK) return st;
+    const LaunchFn fn = part.var->fn[transA][transB];
+    if (fn == nullptr) return MGEMM_INVALID_ARG;
+    err = fn(part.args, (unsigned)part.grid, stream);
+    if (err == hipSuccess)
+        err = launch_splitk_reduce(c_dtype, workspace, (int)used, (int)M, (int)N, C, ldc, alpha, beta,
+                                   full.args.alpha_i, full.args.beta_i, stream);
+    return err == hipSuccess ? MGEMM_OK : MGEMM_HIP_ERROR;
 }
 
 void fill_info(const Variant &v, int id, mgemm_variant_info *out)
@@ -316,6 +422,75 @@ mgemm_status gemm_f64_strided_batched(mgemm_op transA, mgemm_op transB, int64_t 
 {
     return run(MGEMM_F64, MGEMM_F64, transA, transB, M, N, K, alpha, A, lda, strideA, B, ldb,
                strideB, beta, C, ldc, strideC, batch, stream);
+}
+
+mgemm_status gemm_splitk(mgemm_dtype in_dtype, mgemm_dtype c_dtype, mgemm_op transA,
+                         mgemm_op transB, int64_t M, int64_t N, int64_t K, double alpha,
+                         const void *A, int64_t lda, const void *B, int64_t ldb, double beta,
+                         void *C, int64_t ldc, int64_t splits, void *workspace,
+                         int64_t workspace_bytes, hipStream_t stream)
+{
+    // 32-bit, 16-bit and int8 paths take float scalars: refuse what a float cannot hold
+    if (in_dtype != MGEMM_F64 && ((double)(float)alpha != alpha || (double)(float)beta != beta))
+        return MGEMM_INVALID_ARG;
+    return run_splitk(in_dtype, c_dtype, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                      splits, workspace, workspace_bytes, stream);
+}
+
+int64_t mgemm_splitk_chunks(mgemm_dtype in_dtype, int64_t M, int64_t N, int64_t K, int64_t splits)
+{
+    if (!is_input_type(in_dtype) || M < 0 || N < 0 || K < 0 || splits < 0) return -1;
+    if (M == 0 || N == 0 || K == 0) return 1;
+    if (splits == 0) splits = auto_splits(in_dtype, M, N, K);
+    if (splits <= 1) return 1;
+    int64_t used;
+    k_chunk(in_dtype, K, splits, &used);
+    return used;
+}
+
+mgemm_status mgemm_splitk_select(mgemm_dtype in_dtype, mgemm_op transA, mgemm_op transB, int64_t M,
+                                 int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
+                                 int64_t ldb, int64_t splits, mgemm_variant_info *out, int64_t *grid,
+                                 int64_t *chunks, int64_t *chunk_len)
+{
+    const int64_t used = mgemm_splitk_chunks(in_dtype, M, N, K, splits);
+    if (used < 0) return MGEMM_INVALID_ARG;
+    Plan plan;
+    mgemm_status st;
+    int64_t ks = K;
+    if (used <= 1) {
+        const int c_dtype = partial_dtype(in_dtype);
+        st = validate_and_plan(in_dtype, c_dtype, transA, transB, M, N, K, 1.0, A, lda, 0, B, ldb, 0,
+                               0.0, A, N, 0, 1, &plan);
+    } else {
+        int64_t u;
+        ks = k_chunk(in_dtype, K, splits == 0 ? auto_splits(in_dtype, M, N, K) : splits, &u);
+        // any 16-byte aligned address stands in for the workspace
+        st = plan_chunks(in_dtype, transA, transB, M, N, K, ks, used, A, lda, B, ldb,
+                         reinterpret_cast<const void *>((uintptr_t)256), &plan);
+    }
+    if (st != MGEMM_OK) return st;
+    if (out) {
+        if (plan.kind == Plan::GEMM) {
+            fill_info(*plan.var, plan.id, out);
+        } else {
+            std::memset(out, 0, sizeof(*out));
+            out->id = -1;
+            std::snprintf(out->name, sizeof(out->name), "%s", "none");
+        }
+    }
+    if (grid) *grid = plan.kind == Plan::GEMM ? plan.grid : 0;
+    if (chunks) *chunks = used;
+    if (chunk_len) *chunk_len = used <= 1 ? K : ks;
+    return MGEMM_OK;
+}
+
+int64_t mgemm_splitk_workspace_bytes(mgemm_dtype in_dtype, int64_t M, int64_t N, int64_t K,
+                                     int64_t splits)
+{
+    const int64_t used = mgemm_splitk_chunks(in_dtype, M, N, K, splits);
+    if (used < 0) return -1;
+    return used <= 1 ? 0 : used * M * N * elem_size(partial_dtype(in_dtype));
 }
 
 const char *mgemm_status_string(mgemm_status s)

@@ -66,6 +66,7 @@ class Problem:
     pad_value: Optional[float] = None  # fill for padding beyond the logical matrix
     c_dtype: str = "f32"       # C's type: "f32", the operand type for 16-bit output, "i32" for
                                # i8; double operands always take "f64"
+    splitk: Optional[int] = None   # None: one-pass kernels; n: split-K with n chunks (0: automatic)
 
     def __post_init__(self):
         if self.dtype == "f64":
@@ -198,6 +199,14 @@ def sgemm_ragged() -> Problem:
     return Problem("f32", 1000, 1027, 999, dist="int", int_lo=0, int_hi=99, seed=1003)
 
 
+def sgemm_ragged_splitk() -> Problem:
+    """The ragged SGEMM through split-K with 3 chunks of 352 (the last 295): 216
+    workgroups of 128x128 instead of 272 of 64x64."""
+    p = sgemm_ragged()
+    p.splitk = 3
+    return p
+
+
 def gemm16_8192(dtype: str = "bf16") -> Problem:
     """8192^3 with bf16 (or fp16) N(0,1) operands, fp32 accumulate and fp32 C."""
     return Problem(dtype, 8192, 8192, 8192, dist="normal", seed=1004)
@@ -235,6 +244,7 @@ WORKLOADS = {
     "sgemm_256": sgemm_256,
     "sgemm_4096": sgemm_4096,
     "sgemm_ragged": sgemm_ragged,
+    "sgemm_ragged_splitk": sgemm_ragged_splitk,
     "gemm_bf16_8192": lambda: gemm16_8192("bf16"),
     "gemm_f16_8192": lambda: gemm16_8192("f16"),
     "qkt_batched": qkt_batched,

@@ -192,6 +192,54 @@ mgemm_status gemm_f64_strided_batched(mgemm_op transA, mgemm_op transB,
                                       double beta, double *C, int64_t ldc, int64_t strideC,
                                       int64_t batch, hipStream_t stream);
 
+/*
+ * Split-K GEMM for under-filled shapes (few output tiles, long K): the same
+ * C = alpha * op(A) * op(B) + beta * C as the entry points above (the form
+ * of "Sgemm [128,128,8]" (jianshu), design comment and host_gemm), computed
+ * as `splits` K-chunks whose partial products fill more of the device, then
+ * summed.  The pages size their tiles per kernel through template
+ * parameters ("cuda11/matmul" tutorial, sections V1-V3); a tile grid that
+ * leaves most of the 256 CUs idle is the case this entry point is for.
+ *   in_dtype, c_dtype  as gemm_strided_batched_ex (fp32/f16/bf16 inputs with
+ *          fp32 or the inputs' 16-bit C; int8 with int32 C), or MGEMM_F64
+ *          for both.
+ *   alpha, beta  double; for every in_dtype but MGEMM_F64 they must be
+ *          exactly representable as float (else MGEMM_INVALID_ARG).
+ *   splits  requested chunk count; 0 picks one automatically, 1 runs the
+ *          plain kernel.  Chunks are whole K-slabs, so fewer chunks than
+ *          requested may run (mgemm_splitk_chunks tells how many).
+ *   workspace, workspace_bytes  device scratch owned by the caller, 16-byte
+ *          aligned, at least mgemm_splitk_workspace_bytes(...) bytes (0 when
+ *          one chunk runs; then workspace may be NULL).  It holds
+ *          [chunks][M][N] partial products (fp32; int32 for int8; double
+ *          for fp64) and is overwritten.  Calls that share a workspace must
+ *          be ordered on one stream.
+ * Two kernels run on `stream`: the chunked products, then a reduction that
+ * adds the chunks in ascending order (deterministic), applies alpha and
+ * beta (C read only when beta != 0) and rounds to C's type.  Results differ
+ * from the one-pass kernels only by fp32 (fp64) summation order, and are
+ * identical for integer-valued inputs whose partial sums are exact.
+ * Errors: as gemm_strided_batched_ex, plus MGEMM_INVALID_ARG for splits < 0
+ * or a missing, misaligned or short workspace.
+ */
+mgemm_status gemm_splitk(mgemm_dtype in_dtype, mgemm_dtype c_dtype,
+                         mgemm_op transA, mgemm_op transB,
+                         int64_t M, int64_t N, int64_t K, double alpha,
+                         const void *A, int64_t lda,
+                         const void *B, int64_t ldb,
+                         double beta, void *C, int64_t ldc,
+                         int64_t splits, void *workspace, int64_t workspace_bytes,
+                         hipStream_t stream);
+
+/* Chunks gemm_splitk runs for these sizes and `splits` (0 = automatic);
+ * 1 means the plain kernel; -1 for invalid arguments.  Pure host. */
+int64_t mgemm_splitk_chunks(mgemm_dtype in_dtype, int64_t M, int64_t N, int64_t K, int64_t splits);
+
+/* Workspace bytes gemm_splitk needs for these sizes and `splits`; -1 for
+ * invalid arguments.  Pure host. */
+int64_t mgemm_splitk_workspace_bytes(mgemm_dtype in_dtype, int64_t M, int64_t N, int64_t K,
+                                     int64_t splits);
+
 /* Human-readable text for a status code (static storage). */
 const char *mgemm_status_string(mgemm_status s);
 
@@ -243,6 +291,16 @@ mgemm_status mgemm_select(mgemm_dtype in_dtype, mgemm_op transA, mgemm_op transB
  * MGEMM_INVALID_ARG if the variant does not exist or has another dtype.
  */
 mgemm_status mgemm_force_variant(mgemm_dtype dtype, int id);
+
+/* The kernel variant and grid of gemm_splitk's partial-product launch (of
+ * the plain kernel when one chunk runs), the chunk count and the chunk
+ * length (the last chunk takes the rest of K).  A and B stand for the
+ * operand addresses (their alignment matters).  Pure host. */
+mgemm_status mgemm_splitk_select(mgemm_dtype in_dtype, mgemm_op transA, mgemm_op transB,
+                                 int64_t M, int64_t N, int64_t K,
+                                 const void *A, int64_t lda, const void *B, int64_t ldb,
+                                 int64_t splits, mgemm_variant_info *out, int64_t *grid,
+                                 int64_t *chunks, int64_t *chunk_len);
 
 #ifdef __cplusplus
 }

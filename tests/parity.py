@@ -39,9 +39,14 @@ class Run:
         self.dCbuf = c.to(DEV)
         self.dC = self.dCbuf[GUARD:GUARD + n]
 
-    def launch(self, stream=None):
+    def launch(self, stream=None, workspace=None):
         p = self.p
-        if p.dtype == "f64":
+        if p.splitk is not None:
+            assert p.batch == 1
+            mg.gemm_splitk(p.dtype, p.c_dtype, int(p.transA), int(p.transB), p.M, p.N, p.K, p.alpha,
+                           self.dA, p.lda, self.dB, p.ldb, p.beta, self.dC, p.ldc, splits=p.splitk,
+                           workspace=workspace, stream=stream)
+        elif p.dtype == "f64":
             if p.batch == 1 and p.strideA == p.a_rows * p.lda and not getattr(p, "force_batched", False):
                 mg.gemm_f64(int(p.transA), int(p.transB), p.M, p.N, p.K, p.alpha, self.dA, p.lda,
                             self.dB, p.ldb, p.beta, self.dC, p.ldc, stream=stream)

@@ -246,3 +246,38 @@ def test_binding_refuses_host_tensors_and_short_buffers():
     a = torch.zeros(16)
     with pytest.raises(ValueError):
         mg.gemm_f32(0, 0, 4, 4, 4, 1.0, a, 4, a, 4, 0.0, a, 4)
+
+
+def test_splitk_rules_without_a_gpu():
+    lib = mg.load()
+    sk = lib.gemm_splitk
+
+    def call(in_dt=0, c_dt=0, M=64, N=64, K=1024, alpha=1.0, beta=0.0, splits=4, ws=ALIGNED,
+             wbytes=1 << 30):
+        return sk(in_dt, c_dt, 0, 0, M, N, K, alpha, ALIGNED, K, ALIGNED, N, beta, ALIGNED, N,
+                  splits, ws, wbytes, None)
+    assert call(splits=-1) == 1
+    assert call(ws=None) == 1                                  # chunks > 1 need a workspace
+    assert call(ws=ALIGNED + 8) == 1                           # 16-byte alignment
+    need = mg.splitk_workspace_bytes("f32", 64, 64, 1024, 4)
+    assert need == 4 * 64 * 64 * 4
+    assert call(wbytes=need - 1) == 1
+    assert call(alpha=1.0 + 2 ** -40) == 1                     # not a float: refused for fp32
+    assert call(in_dt=1, c_dt=2) == 1                          # C type rules as the _ex entry point
+    assert call(in_dt=3, c_dt=0) == 1                          # int8 needs int32 C
+    # nothing to do: OK without a workspace, for every input type
+    for in_dt, c_dt in ((0, 0), (1, 1), (2, 0), (5, 5)):
+        assert call(in_dt, c_dt, M=0, ws=None, wbytes=0) == 0
+    assert call(5, 5, M=0, alpha=1.0 + 2 ** -40, ws=None, wbytes=0) == 0   # fp64 takes doubles
+    # chunk planning: whole K-slabs, the automatic count fills the device
+    assert mg.splitk_chunks("f32", 1000, 1027, 999, 0) == 1    # K not deep enough: one pass
+    assert mg.splitk_chunks("f32", 512, 512, 4096, 0) == 8     # 16 tiles, chunks >= 512 deep
+    assert mg.splitk_chunks("f32", 256, 256, 8192, 0) == 16
+    assert mg.splitk_chunks("f32", 4096, 4096, 4096, 0) == 1   # already fills 256 CUs
+    assert mg.splitk_chunks("f32", 64, 64, 100, 8) == 4        # 32-deep slabs: 100 -> 4 chunks
+    assert mg.splitk_chunks("bf16", 64, 64, 1000, 3) == 3
+    assert mg.splitk_chunks("i8", 64, 64, 1000, 16) == 8       # 128-byte slabs
+    assert mg.splitk_workspace_bytes("f64", 100, 50, 1000, 4) == 4 * 100 * 50 * 8
+    assert mg.splitk_workspace_bytes("i8", 100, 50, 1024, 2) == 2 * 100 * 50 * 4
+    assert mg.splitk_workspace_bytes("f32", 100, 50, 1000, 1) == 0
+    assert lib.mgemm_splitk_chunks(0, -1, 4, 4, 0) == -1

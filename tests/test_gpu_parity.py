@@ -373,6 +373,74 @@ def test_dgemm_4096_integer_shadow():
                   what="DGEMM 4096^3 integer shadow")
 
 
+# ------------------------------------------------------------------ split-K
+
+SPLITK_TYPES = [("f32", "f32", 1000), ("f16", "f32", 8), ("bf16", "bf16", 8), ("i8", "i32", 127),
+                ("f64", "f64", 1000)]
+
+
+@pytest.mark.parametrize("dtype,c_dtype,hi", SPLITK_TYPES)
+def test_splitk_every_type_and_transpose_exact(dtype, c_dtype, hi):
+    # integer-valued inputs: the chunked sum is exact, so bit-exact; K is no
+    # multiple of the chunk, so the last chunk is short (and takes the edge path)
+    lo = -128 if dtype == "i8" else -hi
+    trans = [(False, True)] if dtype == "i8" else list(itertools.product((False, True), repeat=2))
+    for tA, tB in trans:
+        for splits, (M, N, K) in ((2, (150, 133, 700)), (5, (70, 300, 1111)), (0, (200, 190, 2050))):
+            ab = (3.0, -2.0) if dtype == "i8" else (1.5, 0.5)
+            p = wl.Problem(dtype, M, N, K, transA=tA, transB=tB, alpha=ab[0], beta=ab[1],
+                           dist="int", int_lo=lo, int_hi=hi, c_dist="int", c_dtype=c_dtype,
+                           seed=91, splitk=splits)
+            if dtype == "f32":   # keep every partial sum below 2^24
+                p = dataclasses.replace(p, int_lo=-20, int_hi=20)
+            if dtype in ("f16", "bf16") and c_dtype != "f32":
+                p = dataclasses.replace(p, int_lo=-4, int_hi=4)
+            n = mg.splitk_chunks(dtype, M, N, K, splits)
+            assert n > 1
+            full_check(p, exact=True, what=f"split-K {dtype}->{c_dtype} x{n} tA={int(tA)} tB={int(tB)}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f64"])
+def test_splitk_float_inputs_within_tolerance(dtype):
+    p = wl.Problem(dtype, 257, 190, 3000, transA=True, alpha=0.75, beta=-1.25,
+                   dist="normal" if dtype == "bf16" else "uniform", c_dist="uniform", seed=92,
+                   splitk=6)
+    full_check(p, what=f"split-K {dtype} x{mg.splitk_chunks(dtype, 257, 190, 3000, 6)}")
+
+
+def test_splitk_workspace_reused_by_a_smaller_call():
+    p = wl.Problem("f32", 300, 260, 1500, dist="int", int_lo=-9, int_hi=9, seed=93, splitk=4)
+    ws = torch.empty(mg.splitk_workspace_bytes("f32", 300, 260, 1500, 4), dtype=torch.uint8,
+                     device="cuda")
+    for q in (p, dataclasses.replace(p, M=120, N=77, K=900, seed=94)):
+        r = Run(q)
+        r.launch(workspace=ws)
+        check_exact(r.result(), r.oracle_full(), f"split-K {q.M}x{q.N}x{q.K} in a shared workspace")
+
+
+def test_splitk_quick_returns_and_one_chunk():
+    for alpha, K in ((0.0, 512), (1.0, 0)):
+        p = wl.Problem("f32", 90, 70, K, alpha=alpha, beta=-0.5, dist="uniform", seed=95, splitk=4)
+        full_check(p, exact=True, what=f"split-K alpha={alpha} K={K} (no chunks)")
+    # a request that gives one chunk runs the plain kernel, with no workspace
+    p = wl.Problem("f32", 64, 64, 32, dist="int", int_lo=-9, int_hi=9, seed=96, splitk=8)
+    assert mg.splitk_chunks("f32", 64, 64, 32, 8) == 1
+    full_check(p, exact=True, what="split-K with one chunk")
+
+
+def test_sgemm_ragged_splitk_bit_exact():
+    p = wl.sgemm_ragged_splitk()
+    assert mg.splitk_chunks("f32", p.M, p.N, p.K, p.splitk) == 3
+    full_check(p, exact=True, what="ragged 1000x1027x999 through split-K")
+
+
+def test_splitk_auto_on_a_deep_k_shape():
+    p = wl.Problem("f32", 256, 256, 8192, alpha=2.0, dist="int", int_lo=-9, int_hi=9, seed=97,
+                   splitk=0)
+    assert mg.splitk_chunks("f32", 256, 256, 8192, 0) == 16
+    full_check(p, exact=True, what="256x256x8192 automatic split-K")
+
+
 # ------------------------------------------------------------------ shapes from the pages
 
 def test_csdn_ragged_integer_example():
