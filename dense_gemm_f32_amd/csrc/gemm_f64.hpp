@@ -13,12 +13,18 @@
 // (out-of-range elements read as zero), so edges and unaligned leading
 // dimensions need no second path.
 //
-// LDS holds both operands k-major, [BK][MN + 4] doubles: a fragment read has
-// lane (g = lane/16, i = lane%16) read row 4g + s, column i of its 16-wide
-// block.  The 4-double pad puts the two 16-lane groups of a 32-lane LDS
-// cycle 32 banks apart (row stride = 8 mod 64 dwords, rows 4 apart), so the
-// 8-byte reads are conflict-free.  The k-slot 4g + s of MFMA step s is the
-// same for A and B, which is all the dot product needs.
+// LDS holds both operands k-major, [BK][MN + 2] doubles.  At MFMA step s of a
+// 16-deep group, lane (g = lane/16, i = lane%16) reads row
+// 8(g&1) + 4(g>>1) + s, column i of its 16-wide block: the four steps cover
+// the 16 rows once, and A and B use the same k-slot, which is all the dot
+// product needs.  Bank arithmetic (64 banks of 4 bytes, a 32-lane half-wave
+// per LDS cycle): with the row stride P = MN + 2 doubles,
+//   - fragment reads: the half-wave's two 16-lane groups read rows 8 apart,
+//     16P = 32 mod 64 dwords apart, so their 32 consecutive dwords interleave;
+//   - transposing stores (memory rows along m/n): 8 lanes of one memory row
+//     write rows 2j of one column, 4P = 8 mod 64 dwords apart, and 4 memory
+//     rows fill the gaps;
+// so both are conflict-free (a pad of 4 left the stores 2-way conflicted).
 #pragma once
 
 #include "gemm_kernel.hpp"
@@ -38,7 +44,7 @@ struct F64Operand {
     static constexpr int VPR = CC / VEC;        // vectors per memory row
     static constexpr int NPT = R * VPR / NT;    // vectors per thread
     static_assert(NPT * NT == R * VPR, "tile not divisible among threads");
-    static constexpr int P = MN + 4;            // padded LDS row (doubles)
+    static constexpr int P = MN + 2;            // padded LDS row (doubles)
     f64x2 regs[NPT];
 
     __device__ __forceinline__ static int row_of(int tid, int q) { return (tid + q * NT) / VPR; }
@@ -138,13 +144,14 @@ gemm_f64_kernel(KernelArgs p)
         else              lb.load(b, p.ldb, krem, nrem, tid);
     };
     // MFMA steps of k = 4; in each 16-deep group h of the slab, lane group g
-    // takes k = 16h + 4g + s at step s
+    // takes k = 16h + 8(g&1) + 4(g>>1) + s at step s
+    const int g_row = 8 * (g & 1) + 4 * (g >> 1);
     auto compute = [&](int stage) {
         const double *sa = smem + stage * STAGE + wm * WTM + li;
         const double *sb = smem + stage * STAGE + A_ELEMS + wn * WTN + li;
 #pragma unroll
         for (int hs = 0; hs < BK / 4; ++hs) {
-            const int kr = 16 * (hs >> 2) + 4 * g + (hs & 3);
+            const int kr = 16 * (hs >> 2) + g_row + (hs & 3);
             double a[TM], b[TN];
 #pragma unroll
             for (int t = 0; t < TM; ++t) a[t] = sa[kr * OpA::P + 16 * t];

@@ -324,8 +324,8 @@ void fill_info(const Variant &v, int id, mgemm_variant_info *out)
     out->waves_m = v.wm;
     out->waves_n = v.wn;
     out->threads = v.wm * v.wn * 64;
-    // two stages; fp64 rows carry a 4-element pad (gemm_f64.hpp)
-    const int pad = v.dtype == MGEMM_F64 ? 4 : 0;
+    // two stages; fp64 rows carry a 2-element pad (gemm_f64.hpp)
+    const int pad = v.dtype == MGEMM_F64 ? 2 : 0;
     out->lds_bytes = 2 * (v.bm + v.bn + 2 * pad) * v.bk * elem_size(v.dtype);
     out->pipe = v.pipe;
     std::snprintf(out->name, sizeof(out->name), "%s", v.name);
