@@ -11,6 +11,13 @@ The calls mirror the PyTorch forms of the "cuda11/matmul" tutorial
 (dlog.com.cn), section "Pytorch": torch.mm, torch.bmm, matmul broadcasting a
 (10,3,4) batch against a (4,5) matrix, and einsum('bhqd,bhkd->bhqk') for
 attention scores.
+
+Input types: float32, float16, bfloat16 (fp32 accumulate; fp32 output, or
+the inputs' own 16-bit type), float64 (float64 output) and int8 (int32
+output, wrapping; A is used as a row-major [M][K] matrix and B as [N][K],
+the one int8 layout the library builds, so other views are copied into it).
+mm splits K over the device for deep-K shapes that would leave it idle
+(the library's automatic split count), with a torch-allocated workspace.
 """
 from __future__ import annotations
 
@@ -25,11 +32,19 @@ def _dtype_name(t):
     global _DTYPES
     if _DTYPES is None:
         import torch
-        _DTYPES = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}
+        _DTYPES = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16",
+                   torch.float64: "f64", torch.int8: "i8", torch.int32: "i32"}
     name = _DTYPES.get(t)
-    if name is None:
-        raise TypeError(f"unsupported dtype {t}: fp32, fp16 or bf16 inputs")
+    if name is None or name == "i32":
+        raise TypeError(f"unsupported dtype {t}: fp32, fp16, bf16, fp64 or int8 inputs")
     return name
+
+
+def _default_out(name):
+    """C's type when none is asked for: fp32 (16-bit and fp32 inputs), the
+    inputs' type for fp64, int32 for int8."""
+    import torch
+    return {"f64": torch.float64, "i8": torch.int32}.get(name, torch.float32)
 
 
 def _matrix_layout(x):
@@ -81,7 +96,7 @@ def _check_pair(a, b):
     return name
 
 
-def _out(shape, out_dtype, a, out, beta=0.0):
+def _out(shape, out_dtype, a, out, beta=0.0, in_name="f32"):
     import torch
     if beta != 0.0 and out is None:
         raise ValueError("beta != 0 needs out (the C that beta scales)")
@@ -89,19 +104,62 @@ def _out(shape, out_dtype, a, out, beta=0.0):
         if tuple(out.shape) != tuple(shape) or not out.is_contiguous():
             raise ValueError(f"out must be a contiguous tensor of shape {tuple(shape)}")
         return out
-    return torch.empty(shape, dtype=out_dtype or torch.float32, device=a.device)
+    return torch.empty(shape, dtype=out_dtype or _default_out(in_name), device=a.device)
 
 
 def _c_name(c, in_name):
+    import torch
+    if in_name == "i8":
+        if c.dtype != torch.int32:
+            raise TypeError(f"output dtype {c.dtype}: int8 inputs give int32")
+        return "i32"
+    if in_name == "f64":
+        if c.dtype != torch.float64:
+            raise TypeError(f"output dtype {c.dtype}: fp64 inputs give fp64")
+        return "f64"
     name = _dtype_name(c.dtype)
     if name not in ("f32", in_name):
         raise TypeError(f"output dtype {c.dtype}: fp32 or the inputs' own type")
     return name
 
 
-def mm(a, b, *, alpha=1.0, beta=0.0, out=None, out_dtype=None):
-    """alpha * a @ b (+ beta * out): a (M, K), b (K, N), fp32 accumulate; the
-    result is fp32 unless out_dtype (or out) is the inputs' own 16-bit type."""
+def _int8_layout(x, op, ld, want_op, b_stride=None):
+    """int8 operands must be K-contiguous: A (logical M x K) stored row-major
+    (op N), B (logical K x N) stored as its transpose, [N][K] (op T).  x is
+    the operand's logical view; a copy is made when its storage differs."""
+    if op == want_op:
+        return x, op, ld, b_stride
+    if x.dim() == 2:
+        y = x.contiguous() if want_op == 0 else x.t().contiguous()
+        return y, want_op, y.shape[1], b_stride
+    y = x.contiguous() if want_op == 0 else x.transpose(1, 2).contiguous()
+    return y, want_op, y.shape[2], (y.stride(0) if y.shape[0] > 1 else 0)
+
+
+def _launch(name, c_name, op_a, op_b, M, N, K, alpha, a, lda, sa, b, ldb, sb, beta, c, ldc, sc,
+            batch, splitk=None):
+    """One library call: fp64 through its own entry points, a single matrix
+    through split-K when that pays (or is asked for), the rest through
+    gemm_strided_batched_ex."""
+    if batch == 1 and splitk != 1:
+        chunks = _lib.splitk_chunks(name, M, N, K, splitk or 0)
+        if chunks > 1:
+            _lib.gemm_splitk(name, c_name, op_a, op_b, M, N, K, alpha, a.data_ptr(), lda,
+                             b.data_ptr(), ldb, beta, c, ldc, splits=splitk or 0)
+            return
+    if name == "f64":
+        _lib.gemm_f64_strided_batched(op_a, op_b, M, N, K, alpha, a.data_ptr(), lda, sa,
+                                      b.data_ptr(), ldb, sb, beta, c, ldc, sc, batch)
+    else:
+        _lib.gemm_strided_batched_ex(name, c_name, op_a, op_b, M, N, K, alpha, a.data_ptr(), lda,
+                                     sa, b.data_ptr(), ldb, sb, beta, c, ldc, sc, batch)
+
+
+def mm(a, b, *, alpha=1.0, beta=0.0, out=None, out_dtype=None, splitk=None):
+    """alpha * a @ b (+ beta * out): a (M, K), b (K, N).  fp32 accumulate and
+    fp32 result for fp32/16-bit inputs (or out_dtype = the inputs' 16-bit
+    type); fp64 for fp64; int32 for int8.  splitk: None chooses split-K
+    automatically for deep-K shapes, 1 turns it off, n asks for n chunks."""
     if a.dim() != 2 or b.dim() != 2 or a.shape[1] != b.shape[0]:
         raise ValueError(f"mm: shapes {tuple(a.shape)} and {tuple(b.shape)} do not chain")
     name = _check_pair(a, b)
@@ -109,10 +167,12 @@ def mm(a, b, *, alpha=1.0, beta=0.0, out=None, out_dtype=None):
     N = b.shape[1]
     a, op_a, lda = _operand(a)
     b, op_b, ldb = _operand(b)
-    c = _out((M, N), out_dtype, a, out, beta)
-    _lib.gemm_strided_batched_ex(name, _c_name(c, name), op_a, op_b, M, N, K, alpha,
-                                 a.data_ptr(), lda, 0, b.data_ptr(), ldb, 0, beta, c, max(N, 1),
-                                 M * N, 1)
+    if name == "i8":
+        a, op_a, lda, _ = _int8_layout(a, op_a, lda, 0)
+        b, op_b, ldb, _ = _int8_layout(b, op_b, ldb, 1)
+    c = _out((M, N), out_dtype, a, out, beta, name)
+    _launch(name, _c_name(c, name), op_a, op_b, M, N, K, alpha, a, lda, 0, b, ldb, 0, beta, c,
+            max(N, 1), M * N, 1, splitk)
     return c
 
 
@@ -129,10 +189,12 @@ def bmm(a, b, *, alpha=1.0, beta=0.0, out=None, out_dtype=None):
     M, K, N = a.shape[1], a.shape[2], b.shape[2]
     a, op_a, lda, sa = _batched_operand(a)
     b, op_b, ldb, sb = _batched_operand(b)
-    c = _out((batch, M, N), out_dtype, a, out, beta)
-    _lib.gemm_strided_batched_ex(name, _c_name(c, name), op_a, op_b, M, N, K, alpha,
-                                 a.data_ptr(), lda, sa, b.data_ptr(), ldb, sb, beta, c,
-                                 max(N, 1), M * N, batch)
+    if name == "i8":
+        a, op_a, lda, sa = _int8_layout(a, op_a, lda, 0, sa)
+        b, op_b, ldb, sb = _int8_layout(b, op_b, ldb, 1, sb)
+    c = _out((batch, M, N), out_dtype, a, out, beta, name)
+    _launch(name, _c_name(c, name), op_a, op_b, M, N, K, alpha, a, lda, sa, b, ldb, sb, beta, c,
+            max(N, 1), M * N, batch, splitk=1)
     return c
 
 
@@ -159,19 +221,26 @@ def matmul(a, b, *, out_dtype=None):
 def attention_scores(q, k, scale=None, *, out_dtype=None):
     """scale * q @ k^T per (batch, head): q (B, H, S, D), k (B, H, T, D) ->
     (B, H, S, T), i.e. einsum('bhqd,bhkd->bhqk') scaled; scale defaults to
-    1/sqrt(D).  k is read in place as the transposed operand."""
+    1/sqrt(D) (1 for int8 inputs, whose scale must be an integer).  k is read
+    in place as the transposed operand (int8: copied when stored D-major)."""
     if q.dim() != 4 or k.dim() != 4 or q.shape[:2] != k.shape[:2] or q.shape[3] != k.shape[3]:
         raise ValueError(f"attention_scores: shapes {tuple(q.shape)} and {tuple(k.shape)}")
     name = _check_pair(q, k)
     B, H, S, D = q.shape
     T = k.shape[2]
     if scale is None:
-        scale = 1.0 / math.sqrt(D)
+        scale = 1.0 if name == "i8" else 1.0 / math.sqrt(D)
+    if name == "i8" and float(scale) != int(scale):
+        raise ValueError("attention_scores: int8 inputs take an integer scale")
     q3, op_q, ldq, sq = _batched_operand(q.reshape(B * H, S, D))
     k3, op_k, ldk, sk = _batched_operand(k.reshape(B * H, T, D))
-    c = _out((B, H, S, T), out_dtype, q, None)
     # scores = q k^T: op(B) = k^T, so k's own layout flips
-    _lib.gemm_strided_batched_ex(name, _c_name(c, name), op_q, 1 - op_k, S, T, D, float(scale),
-                                 q3.data_ptr(), ldq, sq, k3.data_ptr(), ldk, sk, 0.0, c,
-                                 max(T, 1), S * T, B * H)
+    op_kt = 1 - op_k
+    if name == "i8":
+        q3, op_q, ldq, sq = _int8_layout(q3, op_q, ldq, 0, sq)
+        # the library's B is k^T, logical (D, T); int8 wants it stored [T][D]
+        k3, op_kt, ldk, sk = _int8_layout(k3.transpose(1, 2), op_kt, ldk, 1, sk)
+    c = _out((B, H, S, T), out_dtype, q, None, 0.0, name)
+    _launch(name, _c_name(c, name), op_q, op_kt, S, T, D, float(scale), q3, ldq, sq, k3, ldk, sk,
+            0.0, c, max(T, 1), S * T, B * H, splitk=1)
     return c

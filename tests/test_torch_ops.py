@@ -63,7 +63,7 @@ def test_shape_errors_before_any_gpu_work():
     with pytest.raises(ValueError):
         torch_ops.attention_scores(torch.zeros(1, 2, 3, 4), torch.zeros(1, 2, 3, 5))
     with pytest.raises(TypeError):
-        torch_ops.mm(torch.zeros(3, 4, dtype=torch.float64), torch.zeros(4, 5, dtype=torch.float64))
+        torch_ops.mm(torch.zeros(3, 4, dtype=torch.int32), torch.zeros(4, 5, dtype=torch.int32))
     with pytest.raises(ValueError):                            # CPU tensors are refused
         torch_ops.mm(torch.zeros(3, 4), torch.zeros(4, 5))
 
@@ -163,3 +163,78 @@ def test_attention_scores_match_einsum_definition(dtype):
             ref = ref_mm(qf[b, h], kf[b, h].t(), 0.3)
             tol = (2e-3 * math.sqrt(D) + (2.0 ** -11 if dtype == torch.float16 else 2.0 ** -8))
             assert np.max(np.abs(got[b, h] - ref)) <= tol * np.max(np.abs(ref))
+
+
+def test_int8_layout_copies_only_when_needed():
+    x = torch.zeros(6, 10, dtype=torch.int8)
+    assert torch_ops._int8_layout(x, 0, 10, 0)[0] is x                    # A row-major: as is
+    y, op, ld, _ = torch_ops._int8_layout(x.t(), 1, 10, 0)                # A given transposed
+    assert op == 0 and ld == 6 and y.is_contiguous() and torch.equal(y, x.t())
+    b = torch.zeros(10, 4, dtype=torch.int8)                              # B (K, N) row-major
+    y, op, ld, _ = torch_ops._int8_layout(b, 0, 4, 1)
+    assert op == 1 and ld == 10 and tuple(y.shape) == (4, 10) and torch.equal(y.t(), b)
+    z = torch.zeros(3, 10, 4, dtype=torch.int8)
+    y, op, ld, st = torch_ops._int8_layout(z, 0, 4, 1, 40)
+    assert op == 1 and ld == 10 and st == 40 and tuple(y.shape) == (3, 4, 10)
+
+
+def test_dtype_names_and_default_outputs():
+    assert torch_ops._dtype_name(torch.float64) == "f64"
+    assert torch_ops._dtype_name(torch.int8) == "i8"
+    assert torch_ops._default_out("f64") == torch.float64
+    assert torch_ops._default_out("i8") == torch.int32
+    assert torch_ops._default_out("bf16") == torch.float32
+    with pytest.raises(TypeError):
+        torch_ops._dtype_name(torch.int32)
+
+
+@pytest.mark.gpu
+def test_mm_f64_views_and_alpha_beta():
+    gen = torch.Generator().manual_seed(66)
+    for (M, K, N) in ((70, 45, 33), (200, 130, 150)):
+        a = torch.randn(M, K, generator=gen, dtype=torch.float64).cuda()
+        b = torch.randn(N, K, generator=gen, dtype=torch.float64).cuda().t()   # transposed view
+        c0 = torch.randn(M, N, generator=gen, dtype=torch.float64).cuda()
+        out = c0.clone()
+        torch_ops.mm(a, b, alpha=0.3, beta=1.7, out=out)
+        ref = oracle.gemm("f64", False, False, M, N, K, 0.3, a.cpu().numpy().ravel(), K,
+                          b.cpu().contiguous().numpy().ravel(), N, 1.7, c0.cpu().numpy().ravel(), N)[0]
+        tol = 1e-5 * 2.0 ** -29 * math.sqrt(K) * np.max(np.abs(ref))
+        assert out.dtype == torch.float64
+        assert np.max(np.abs(out.cpu().numpy() - ref)) <= tol
+
+
+@pytest.mark.gpu
+def test_mm_and_bmm_int8_any_view():
+    gen = torch.Generator().manual_seed(67)
+    M, K, N = 70, 160, 50
+    a = torch.randint(-128, 128, (M, K), generator=gen).to(torch.int8)
+    b = torch.randint(-128, 128, (K, N), generator=gen).to(torch.int8)
+    want = (a.long() @ b.long()).numpy()
+    for x, y in ((a.cuda(), b.cuda()), (a.t().contiguous().cuda().t(), b.t().contiguous().cuda().t())):
+        got = torch_ops.mm(x, y)
+        assert got.dtype == torch.int32
+        assert np.array_equal(got.cpu().numpy(), want)
+    a3 = torch.randint(-128, 128, (3, M, K), generator=gen).to(torch.int8)
+    b3 = torch.randint(-128, 128, (3, K, N), generator=gen).to(torch.int8)
+    got = torch_ops.bmm(a3.cuda(), b3.cuda(), alpha=2.0)
+    assert np.array_equal(got.cpu().numpy(), 2 * (a3.long() @ b3.long()).numpy())
+    with pytest.raises(Exception):
+        torch_ops.mm(a.cuda(), b.cuda(), alpha=0.5)                    # int8: integral alpha only
+
+
+@pytest.mark.gpu
+def test_mm_takes_split_k_on_deep_k_and_matches():
+    gen = torch.Generator().manual_seed(68)
+    M, K, N = 256, 8192, 256
+    assert torch_ops._lib.splitk_chunks("f32", M, N, K, 0) > 1          # auto split applies
+    a = ints((M, K), torch.float32, gen).cuda()
+    b = ints((K, N), torch.float32, gen).cuda()
+    got = torch_ops.mm(a, b).double().cpu().numpy()
+    assert np.array_equal(got, ref_mm(a, b))
+    off = torch_ops.mm(a, b, splitk=1).double().cpu().numpy()           # one pass, same result
+    assert np.array_equal(off, got)
+    h = torch_ops.mm(a.to(torch.bfloat16), b.to(torch.bfloat16), out_dtype=torch.bfloat16)
+    want = oracle.decode16("bf16", oracle.round16("bf16", ref_mm(a.to(torch.bfloat16),
+                                                                 b.to(torch.bfloat16))))
+    assert np.array_equal(h.double().cpu().numpy(), want)
