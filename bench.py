@@ -208,7 +208,9 @@ def summarize_case(case, d, copy_dir):
         red = red[PROFILE_WARMUP:] if len(red) > PROFILE_WARMUP else red
         ravg = _mean(red)
         both = p.flops / ((avg + ravg) * 1e-9) / 1e12 if avg and ravg else None
-        lines += ["splitk_chunks: %d" % mg.splitk_chunks(dt, p.M, p.N, p.K, p.splitk),
+        plan = mg.splitk_plan(dt, p.M, p.N, p.K, p.splitk, transA=int(p.transA),
+                              transB=int(p.transB), lda=p.lda, ldb=p.ldb)
+        lines += ["splitk_chunks: %d of %d" % (plan["chunks"], plan["chunk_len"]),
                   "reduce_kernel_average_ns: " + _fmt(ravg, "%.0f"),
                   "tflops_both_kernels: " + _fmt(both, "%.2f")]
     if case in HBM_BOUND and avg:
@@ -266,9 +268,9 @@ def select_for(mg, p, ptrs=(1 << 20, 1 << 20, 1 << 20)):
     """(variant info, grid) of the GEMM kernel a workload launches (for split-K: the
     partial-product kernel)."""
     if p.splitk is not None:
-        info, grid, _, _ = mg.splitk_select(p.dtype, int(p.transA), int(p.transB), p.M, p.N, p.K,
-                                            ptrs[0], p.lda, ptrs[1], p.ldb, p.splitk)
-        return info, grid
+        plan = mg.splitk_plan(p.dtype, p.M, p.N, p.K, p.splitk, transA=int(p.transA),
+                              transB=int(p.transB), A=ptrs[0], lda=p.lda, B=ptrs[1], ldb=p.ldb)
+        return plan["variant"], plan["grid"]
     return mg.select(p.dtype, int(p.transA), int(p.transB), p.M, p.N, p.K, p.alpha, ptrs[0],
                      p.lda, p.strideA, ptrs[1], p.ldb, p.strideB, p.beta, ptrs[2], p.ldc,
                      p.strideC, p.batch)
@@ -287,8 +289,9 @@ def launcher(p, dA, dB, dC):
     import dense_gemm_f32_amd as mg
     if p.splitk is not None:
         import torch
-        ws = torch.empty(max(mg.splitk_workspace_bytes(p.dtype, p.M, p.N, p.K, p.splitk), 16),
-                         dtype=torch.uint8, device=dA.device)   # allocated once, outside the timing
+        need = mg.splitk_workspace_bytes(p.dtype, p.M, p.N, p.K, p.splitk, transA=int(p.transA),
+                                         transB=int(p.transB), A=dA, lda=p.lda, B=dB, ldb=p.ldb)
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dA.device)  # outside the timing
         return lambda: mg.gemm_splitk(p.dtype, p.c_dtype, int(p.transA), int(p.transB), p.M, p.N,
                                       p.K, p.alpha, dA, p.lda, dB, p.ldb, p.beta, dC, p.ldc,
                                       splits=p.splitk, workspace=ws)

@@ -44,6 +44,16 @@ class VariantInfo(ctypes.Structure):
         return d
 
 
+class SplitkPlanInfo(ctypes.Structure):
+    _fields_ = [("workspace_bytes", ctypes.c_int64), ("chunks", ctypes.c_int64),
+                ("chunk_len", ctypes.c_int64), ("variant", VariantInfo), ("grid", ctypes.c_int64)]
+
+    def as_dict(self):
+        d = {f: getattr(self, f) for f, _ in self._fields_}
+        d["variant"] = self.variant.as_dict()
+        return d
+
+
 _lib = None
 
 
@@ -75,14 +85,9 @@ def load():
     lib.gemm_splitk.restype = i32
     lib.gemm_splitk.argtypes = [i32, i32, i32, i32, i64, i64, i64, f64, vp, i64, vp, i64, f64, vp,
                                 i64, i64, vp, i64, vp]
-    lib.mgemm_splitk_chunks.restype = i64
-    lib.mgemm_splitk_chunks.argtypes = [i32, i64, i64, i64, i64]
-    lib.mgemm_splitk_select.restype = i32
-    lib.mgemm_splitk_select.argtypes = [i32, i32, i32, i64, i64, i64, vp, i64, vp, i64, i64,
-                                        ctypes.POINTER(VariantInfo), ctypes.POINTER(i64),
-                                        ctypes.POINTER(i64), ctypes.POINTER(i64)]
-    lib.mgemm_splitk_workspace_bytes.restype = i64
-    lib.mgemm_splitk_workspace_bytes.argtypes = [i32, i64, i64, i64, i64]
+    lib.mgemm_splitk_plan.restype = i32
+    lib.mgemm_splitk_plan.argtypes = [i32, i32, i32, i64, i64, i64, vp, i64, vp, i64, i64,
+                                      ctypes.POINTER(SplitkPlanInfo)]
     lib.gemm_strided_batched_ex.restype = i32
     lib.gemm_strided_batched_ex.argtypes = [i32, i32, i32, i32, i64, i64, i64, f32, vp, i64, i64, vp,
                                             i64, i64, f32, vp, i64, i64, i64, vp]
@@ -236,35 +241,30 @@ def gemm_strided_batched_ex(in_dtype, c_dtype, transA, transB, M, N, K, alpha, A
     _check(st, "gemm_strided_batched_ex")
 
 
-def splitk_chunks(in_dtype, M, N, K, splits=0):
-    """K-chunks gemm_splitk runs (1: the plain kernel)."""
-    n = load().mgemm_splitk_chunks(DTYPE_CODES.get(in_dtype, in_dtype), M, N, K, splits)
-    if n < 0:
-        raise MgemmError(1, "mgemm_splitk_chunks")
-    return n
-
-
-def splitk_workspace_bytes(in_dtype, M, N, K, splits=0):
-    """Workspace bytes gemm_splitk needs (0 when one chunk runs)."""
-    n = load().mgemm_splitk_workspace_bytes(DTYPE_CODES.get(in_dtype, in_dtype), M, N, K, splits)
-    if n < 0:
-        raise MgemmError(1, "mgemm_splitk_workspace_bytes")
-    return n
-
-
-def splitk_select(in_dtype, transA, transB, M, N, K, A=1 << 20, lda=None, B=1 << 20, ldb=None,
-                  splits=0):
-    """(variant info of the partial-product launch, grid, chunks, chunk length)."""
+def splitk_plan(in_dtype, M, N, K, splits=0, transA=0, transB=0, A=1 << 20, lda=None, B=1 << 20,
+                ldb=None):
+    """What gemm_splitk will do (a dict: workspace_bytes, chunks, chunk_len, and the GEMM
+    kernel's variant and grid).  A and B are addresses (ints) or tensors: only their
+    alignment matters."""
     dt = DTYPE_CODES.get(in_dtype, in_dtype)
     lda = lda if lda is not None else (M if transA else K)
     ldb = ldb if ldb is not None else (K if transB else N)
-    info = VariantInfo()
-    grid, chunks, ks = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
-    st = load().mgemm_splitk_select(dt, int(transA), int(transB), M, N, K, A, lda, B, ldb, splits,
-                                    ctypes.byref(info), ctypes.byref(grid), ctypes.byref(chunks),
-                                    ctypes.byref(ks))
-    _check(st, "mgemm_splitk_select")
-    return info.as_dict(), grid.value, chunks.value, ks.value
+    pa = A if isinstance(A, int) else A.data_ptr()
+    pb = B if isinstance(B, int) else B.data_ptr()
+    info = SplitkPlanInfo()
+    _check(load().mgemm_splitk_plan(dt, int(transA), int(transB), M, N, K, pa, lda, pb, ldb, splits,
+                                    ctypes.byref(info)), "mgemm_splitk_plan")
+    return info.as_dict()
+
+
+def splitk_chunks(in_dtype, M, N, K, splits=0, **operands):
+    """K-chunks gemm_splitk runs (1: the plain kernel)."""
+    return splitk_plan(in_dtype, M, N, K, splits, **operands)["chunks"]
+
+
+def splitk_workspace_bytes(in_dtype, M, N, K, splits=0, **operands):
+    """Workspace bytes gemm_splitk needs (0 when nothing is chunked)."""
+    return splitk_plan(in_dtype, M, N, K, splits, **operands)["workspace_bytes"]
 
 
 def gemm_splitk(in_dtype, c_dtype, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
@@ -280,7 +280,8 @@ def gemm_splitk(in_dtype, c_dtype, transA, transB, M, N, K, alpha, A, lda, B, ld
     pa, _ = _addr(A, _span(a_rows, a_cols, lda) if reads else 0, es, "A")
     pb, _ = _addr(B, _span(b_rows, b_cols, ldb) if reads else 0, es, "B")
     pc, dev = _addr(C, _span(M, N, ldc), ELEM_SIZE.get(ct, 4), "C")
-    need = splitk_workspace_bytes(dt, M, N, K, splits) if splits >= 0 else 0
+    need = (splitk_workspace_bytes(dt, M, N, K, splits, transA=transA, transB=transB,
+                                   A=pa or 0, lda=lda, B=pb or 0, ldb=ldb) if splits >= 0 else 0)
     if workspace is None and need > 0:
         import torch
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)

@@ -427,6 +427,13 @@ struct RegPath {
     static constexpr int LDS_BYTES = 2 * STAGE;
     static constexpr int G = F32 ? BK / 8 : BK * ES / 32;  // k-groups of 32 bytes per slab
     static constexpr int IL_A = TM, IL_B = TN;  // C mapping: interleaved rows and columns
+    // 64x64 tiles keep two register sets in flight: a grid of them is often
+    // about one workgroup per CU, with little else to hide the load latency
+    // behind.  Larger tiles keep one, and so do the element-wise 8/16-bit
+    // builds: a second set would cost them occupancy (128x128 unaligned fp32
+    // would go from 244 to 308 registers, 64x64 unaligned 16-bit past 256:
+    // one wave per SIMD instead of two).
+    static constexpr bool REG2 = BM * BN <= 64 * 64 && (F32 || VECOK);
 
     using OpA = RegOperand<ES, NT, BM, BK, TM, TA, VECOK>;
     using OpB = RegOperand<ES, NT, BN, BK, TN, !TB, VECOK>;
@@ -497,9 +504,7 @@ struct RegPath {
         const int a_row0 = wm * WTM + TM * li, b_row0 = wn * WTN + TN * li;
         const int a_prow0 = wm * WTM + li, b_prow0 = wn * WTN + li;
 
-        OpA la;
-        OpB lb;
-        auto load_slab = [&](int kt) {
+        auto load_slab = [&](int kt, OpA &la, OpB &lb) {
             const int krem = p.K - kt * BK;
             const char *a = Ap + (int64_t)kt * a_kstep;
             const char *b = Bp + (int64_t)kt * b_kstep;
@@ -519,28 +524,63 @@ struct RegPath {
                 f[g & 1].mfmas(acc);
             }
         };
-        // two LDS stages, the next slab fetched to registers during the current one
         const int nk = (p.K + BK - 1) / BK;
-        load_slab(0);
-        la.store(smem, tid);
-        lb.store(smem + A_BYTES, tid);
-        __syncthreads();
-        for (int kt = 0; kt + 1 < nk; ++kt) {
-            load_slab(kt + 1);
-            compute(kt & 1);
-            char *st = smem + ((kt + 1) & 1) * STAGE;
-            la.store(st, tid);
-            lb.store(st + A_BYTES, tid);
+        if constexpr (!REG2) {
+            // two LDS stages, the next slab fetched to registers during the current one
+            OpA la;
+            OpB lb;
+            load_slab(0, la, lb);
+            la.store(smem, tid);
+            lb.store(smem + A_BYTES, tid);
             __syncthreads();
+            for (int kt = 0; kt + 1 < nk; ++kt) {
+                load_slab(kt + 1, la, lb);
+                compute(kt & 1);
+                char *st = smem + ((kt + 1) & 1) * STAGE;
+                la.store(st, tid);
+                lb.store(st + A_BYTES, tid);
+                __syncthreads();
+            }
+            compute((nk - 1) & 1);
+        } else {
+            // Two LDS stages and two register sets: the loads of slab kt+2 are
+            // issued before slab kt is computed and written to LDS only after
+            // slab kt+1 has been, so each load has two slabs of compute to
+            // arrive.  At step kt, LDS stage kt&1 holds slab kt and register
+            // set (kt+1)&1 holds slab kt+1; set kt&1 (stored one step ago) is
+            // free.  The loop is unrolled by two so that the register sets are
+            // distinct variables.
+            OpA la0, la1;
+            OpB lb0, lb1;
+            load_slab(0, la0, lb0);
+            if (nk > 1) load_slab(1, la1, lb1);
+            la0.store(smem, tid);
+            lb0.store(smem + A_BYTES, tid);
+            __syncthreads();
+            auto step = [&](int kt, OpA &free_a, OpB &free_b, const OpA &next_a, const OpB &next_b) {
+                if (kt + 2 < nk) load_slab(kt + 2, free_a, free_b);
+                compute(kt & 1);
+                if (kt + 1 < nk) {
+                    char *st = smem + ((kt + 1) & 1) * STAGE;
+                    next_a.store(st, tid);
+                    next_b.store(st + A_BYTES, tid);
+                    __syncthreads();
+                }
+            };
+            int kt = 0;
+            for (; kt + 1 < nk; kt += 2) {
+                step(kt, la0, lb0, la1, lb1);
+                step(kt + 1, la1, lb1, la0, lb0);
+            }
+            if (kt < nk) step(kt, la0, lb0, la1, lb1);
         }
-        compute((nk - 1) & 1);
     }
 };
 
 // ===========================================================================
 // DmaPath: interior tiles.  Global -> LDS with buffer_load_dwordx4 ... lds
 // (no registers in between) into a ring of NS LDS stages of BK elements.
-// Two schedules (PIPE):
+// Schedules (PIPE):
 //   1  BK = BKR/2 (32 for 16-bit, 16 for fp32), NS = 4, loads issued 3 slabs
 //      ahead; every wave reads and multiplies each slab, with one barrier per
 //      slab placed before the MFMAs of its last k-group so that the next
@@ -729,6 +769,18 @@ struct DmaPath {
         wait_counts<N * LPS, 0>();
     }
 
+    // wait_ahead<n> for a run-time n in [0, N] (n above N waits as N)
+    template <int N>
+    __device__ __forceinline__ static void wait_ahead_upto(int n)
+    {
+        if constexpr (N == 0) {
+            wait_ahead<0>();
+        } else {
+            if (n >= N) wait_ahead<N>();
+            else        wait_ahead_upto<N - 1>(n);
+        }
+    }
+
     __device__ __forceinline__ static void run(const KernelArgs &p, char *smem, int bidx, int m0, int n0,
                                                f32x16 (&acc)[TM][TN])
     {
@@ -778,15 +830,7 @@ struct DmaPath {
             if (s < nk) issue(s);
         {
             const int inflight = nk < NS ? nk : NS;  // slabs issued
-            if constexpr (NS == 4) {
-                if (inflight == 4)      wait_ahead<3>();
-                else if (inflight == 3) wait_ahead<2>();
-                else if (inflight == 2) wait_ahead<1>();
-                else                    wait_ahead<0>();
-            } else {
-                if (inflight == 2) wait_ahead<1>();
-                else               wait_ahead<0>();
-            }
+            wait_ahead_upto<NS - 1>(inflight - 1);
         }
         lds_barrier();
 
@@ -820,13 +864,7 @@ struct DmaPath {
             body_head(kt);
             if (kt + 1 < nk) {
                 const int ahead = nk - kt - 2;  // slabs after kt+1 still possibly in flight
-                if constexpr (NS == 4) {
-                    if (ahead >= 2)      wait_ahead<2>();
-                    else if (ahead == 1) wait_ahead<1>();
-                    else                 wait_ahead<0>();
-                } else {
-                    wait_ahead<0>();
-                }
+                wait_ahead_upto<NS - 2>(ahead);
                 lds_barrier();
                 frags(kt + 1, 0, f[G & 1]);
             }

@@ -273,6 +273,69 @@ mgemm_status plan_chunks(int dtype, int transA, int transB, int64_t M, int64_t N
     return MGEMM_OK;
 }
 
+// What gemm_splitk does for one call: the plain kernel (chunks == 1), or all
+// of C in `chunks` K-chunks of ks (the last chunk takes the rest of K).
+struct SplitPlan {
+    int64_t chunks, ks;
+    int64_t workspace_bytes;
+};
+
+// stands in for C or the workspace when only the variant choice is wanted
+const void *const kAnyAligned = reinterpret_cast<const void *>((uintptr_t)256);
+
+// Small grids of unaligned tiles: when the plain grid is at most two rounds
+// of 256 workgroups and its tile is an unaligned build (the range-checked
+// register path only), about one workgroup per CU leaves that path's load
+// latency exposed.  Three chunks of all of C triple the
+// workgroups per CU.  Applied only where one tile's MFMA work is at least
+// 5 us at the matrix peak, so that the two extra launches stay small beside
+// it.  (Measured, plain -> 3 chunks: ragged 1000x1027x999 fp32 56 -> 46 us,
+// 1100^3 fp32 58 -> 42, the ragged shape in fp64 94 -> 66; the rule leaves
+// alone bf16 ragged (31 -> 34), aligned fp32 1024^3 (26 -> 28) and aligned
+// fp64 1024^3 (65 -> 70).)
+int64_t small_grid_splits(int dtype, int transA, int transB, int64_t M, int64_t N, int64_t K,
+                          const void *A, int64_t lda, const void *B, int64_t ldb)
+{
+    Plan full;
+    if (validate_and_plan(dtype, partial_dtype(dtype), transA, transB, M, N, K, 1.0, A, lda, 0, B, ldb,
+                          0, 0.0, kAnyAligned, N, 0, 1, &full) != MGEMM_OK ||
+        full.kind != Plan::GEMM)
+        return 1;
+    if (full.grid > 512 || full.var->vec) return 1;
+    // matrix peak per CU, flop/s: fp32 157.3 T, fp64 78.6 T, 16-bit 2516.6 T, int8 5000 T over 256 CUs
+    const double per_cu = dtype == MGEMM_F32 ? 157.3e12 / 256 : dtype == MGEMM_F64 ? 78.6e12 / 256
+                        : dtype == MGEMM_I8 ? 5000e12 / 256 : 2516.6e12 / 256;
+    const double tile_s = 2.0 * full.var->bm * full.var->bn * (double)K / per_cu;
+    if (tile_s < 5e-6) return 1;
+    return K >= 6 * k_granule(dtype) ? 3 : 1;
+}
+
+mgemm_status make_split_plan(int dtype, int transA, int transB, int64_t M, int64_t N, int64_t K,
+                             const void *A, int64_t lda, const void *B, int64_t ldb, int64_t splits,
+                             SplitPlan *sp)
+{
+    *sp = SplitPlan{1, K, 0};
+    if (splits < 0) return MGEMM_INVALID_ARG;
+    if (M == 0 || N == 0 || K == 0) return MGEMM_OK;
+    const int64_t wes = elem_size(partial_dtype(dtype));
+    if (splits == 0) {
+        splits = auto_splits(dtype, M, N, K);
+        if (splits <= 1) splits = small_grid_splits(dtype, transA, transB, M, N, K, A, lda, B, ldb);
+    }
+    if (splits > 1) {
+        int64_t used;
+        const int64_t ks = k_chunk(dtype, K, splits, &used);
+        if (used > 1) *sp = SplitPlan{used, ks, used * M * N * wes};
+    }
+    return MGEMM_OK;
+}
+
+LaunchFn launcher_for(const Plan &p, int c_dtype, int transA, int transB)
+{
+    const bool wide_c = c_dtype == MGEMM_F32 || c_dtype == MGEMM_I32 || c_dtype == MGEMM_F64;
+    return wide_c ? p.var->fn[transA][transB] : p.var->fn16[transA][transB];
+}
+
 mgemm_status run_splitk(int dtype, int c_dtype, int transA, int transB, int64_t M, int64_t N,
                         int64_t K, double alpha, const void *A, int64_t lda, const void *B,
                         int64_t ldb, double beta, void *C, int64_t ldc, int64_t splits,
@@ -283,33 +346,30 @@ mgemm_status run_splitk(int dtype, int c_dtype, int transA, int transB, int64_t 
     mgemm_status st = validate_and_plan(dtype, c_dtype, transA, transB, M, N, K, alpha, A, lda, 0, B,
                                         ldb, 0, beta, C, ldc, 0, 1, &full);
     if (st != MGEMM_OK || full.kind == Plan::NOTHING) return st;
-    int64_t used = 1, ks = K;
-    if (full.kind == Plan::GEMM) {
-        if (splits == 0) splits = auto_splits(dtype, M, N, K);
-        if (splits > 1) ks = k_chunk(dtype, K, splits, &used);
-    }
     hipError_t err;
     if (full.kind == Plan::SCALE) {
         err = launch_scale_c(c_dtype, C, (int)M, (int)N, ldc, 0, 1, beta, full.args.beta_i, stream);
         return err == hipSuccess ? MGEMM_OK : MGEMM_HIP_ERROR;
     }
-    if (used <= 1) {  // one chunk: the plain kernel, no workspace
-        const bool wide_c = c_dtype == MGEMM_F32 || c_dtype == MGEMM_I32 || c_dtype == MGEMM_F64;
-        const LaunchFn fn = wide_c ? full.var->fn[transA][transB] : full.var->fn16[transA][transB];
+    SplitPlan sp;
+    st = make_split_plan(dtype, transA, transB, M, N, K, A, lda, B, ldb, splits, &sp);
+    if (st != MGEMM_OK) return st;
+    if (sp.chunks == 1) {  // one kernel, no workspace
+        const LaunchFn fn = launcher_for(full, c_dtype, transA, transB);
         if (fn == nullptr) return MGEMM_INVALID_ARG;
         err = fn(full.args, (unsigned)full.grid, stream);
         return err == hipSuccess ? MGEMM_OK : MGEMM_HIP_ERROR;
     }
-    const int64_t need = used * M * N * elem_size(partial_dtype(dtype));
-    if (workspace == nullptr || !aligned(workspace, 16) || workspace_bytes < need) return MGEMM_INVALID_ARG;
+    if (workspace == nullptr || !aligned(workspace, 16) || workspace_bytes < sp.workspace_bytes)
+        return MGEMM_INVALID_ARG;
     Plan part;
-    st = plan_chunks(dtype, transA, transB, M, N, K, ks, used, A, lda, B, ldb, workspace, &part);
+    st = plan_chunks(dtype, transA, transB, M, N, K, sp.ks, sp.chunks, A, lda, B, ldb, workspace, &part);
     if (st != MGEMM_OK) return st;
-    const LaunchFn fn = part.var->fn[transA][transB];
-    if (fn == nullptr) return MGEMM_INVALID_ARG;
-    err = fn(part.args, (unsigned)part.grid, stream);
+    const LaunchFn pfn = part.var->fn[transA][transB];
+    if (pfn == nullptr) return MGEMM_INVALID_ARG;
+    err = pfn(part.args, (unsigned)part.grid, stream);
     if (err == hipSuccess)
-        err = launch_splitk_reduce(c_dtype, workspace, (int)used, (int)M, (int)N, C, ldc, alpha, beta,
+        err = launch_splitk_reduce(c_dtype, workspace, (int)sp.chunks, (int)M, (int)N, C, ldc, alpha, beta,
                                    full.args.alpha_i, full.args.beta_i, stream);
     return err == hipSuccess ? MGEMM_OK : MGEMM_HIP_ERROR;
 }
@@ -324,7 +384,8 @@ void fill_info(const Variant &v, int id, mgemm_variant_info *out)
     out->waves_m = v.wm;
     out->waves_n = v.wn;
     out->threads = v.wm * v.wn * 64;
-    // two stages; fp64 rows carry a 2-element pad (gemm_f64.hpp)
+    // two stages of bk in either path (fp64 rows carry a 2-element pad,
+    // gemm_f64.hpp; the DMA path's PIPE 1 has four of bk/2)
     const int pad = v.dtype == MGEMM_F64 ? 2 : 0;
     out->lds_bytes = 2 * (v.bm + v.bn + 2 * pad) * v.bk * elem_size(v.dtype);
     out->pipe = v.pipe;
@@ -437,60 +498,32 @@ mgemm_status gemm_splitk(mgemm_dtype in_dtype, mgemm_dtype c_dtype, mgemm_op tra
                       splits, workspace, workspace_bytes, stream);
 }
 
-int64_t mgemm_splitk_chunks(mgemm_dtype in_dtype, int64_t M, int64_t N, int64_t K, int64_t splits)
+mgemm_status mgemm_splitk_plan(mgemm_dtype in_dtype, mgemm_op transA, mgemm_op transB, int64_t M,
+                               int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
+                               int64_t ldb, int64_t splits, mgemm_splitk_plan_info *out)
 {
-    if (!is_input_type(in_dtype) || M < 0 || N < 0 || K < 0 || splits < 0) return -1;
-    if (M == 0 || N == 0 || K == 0) return 1;
-    if (splits == 0) splits = auto_splits(in_dtype, M, N, K);
-    if (splits <= 1) return 1;
-    int64_t used;
-    k_chunk(in_dtype, K, splits, &used);
-    return used;
-}
-
-mgemm_status mgemm_splitk_select(mgemm_dtype in_dtype, mgemm_op transA, mgemm_op transB, int64_t M,
-                                 int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
-                                 int64_t ldb, int64_t splits, mgemm_variant_info *out, int64_t *grid,
-                                 int64_t *chunks, int64_t *chunk_len)
-{
-    const int64_t used = mgemm_splitk_chunks(in_dtype, M, N, K, splits);
-    if (used < 0) return MGEMM_INVALID_ARG;
-    Plan plan;
-    mgemm_status st;
-    int64_t ks = K;
-    if (used <= 1) {
-        const int c_dtype = partial_dtype(in_dtype);
-        st = validate_and_plan(in_dtype, c_dtype, transA, transB, M, N, K, 1.0, A, lda, 0, B, ldb, 0,
-                               0.0, A, N, 0, 1, &plan);
-    } else {
-        int64_t u;
-        ks = k_chunk(in_dtype, K, splits == 0 ? auto_splits(in_dtype, M, N, K) : splits, &u);
-        // any 16-byte aligned address stands in for the workspace
-        st = plan_chunks(in_dtype, transA, transB, M, N, K, ks, used, A, lda, B, ldb,
-                         reinterpret_cast<const void *>((uintptr_t)256), &plan);
-    }
+    if (!out) return MGEMM_INVALID_ARG;
+    std::memset(out, 0, sizeof(*out));
+    out->variant.id = -1;
+    SplitPlan sp;
+    mgemm_status st = make_split_plan(in_dtype, transA, transB, M, N, K, A, lda, B, ldb, splits, &sp);
     if (st != MGEMM_OK) return st;
-    if (out) {
-        if (plan.kind == Plan::GEMM) {
-            fill_info(*plan.var, plan.id, out);
-        } else {
-            std::memset(out, 0, sizeof(*out));
-            out->id = -1;
-            std::snprintf(out->name, sizeof(out->name), "%s", "none");
-        }
+    out->workspace_bytes = sp.workspace_bytes;
+    out->chunks = sp.chunks;
+    out->chunk_len = sp.ks;
+    if (M == 0 || N == 0 || K == 0) return MGEMM_OK;
+    Plan p;
+    if (sp.chunks > 1)
+        st = plan_chunks(in_dtype, transA, transB, M, N, K, sp.ks, sp.chunks, A, lda, B, ldb, kAnyAligned, &p);
+    else
+        st = validate_and_plan(in_dtype, partial_dtype(in_dtype), transA, transB, M, N, K, 1.0, A, lda, 0, B,
+                               ldb, 0, 0.0, kAnyAligned, N, 0, 1, &p);
+    if (st != MGEMM_OK) return st;
+    if (p.kind == Plan::GEMM) {
+        fill_info(*p.var, p.id, &out->variant);
+        out->grid = p.grid;
     }
-    if (grid) *grid = plan.kind == Plan::GEMM ? plan.grid : 0;
-    if (chunks) *chunks = used;
-    if (chunk_len) *chunk_len = used <= 1 ? K : ks;
     return MGEMM_OK;
-}
-
-int64_t mgemm_splitk_workspace_bytes(mgemm_dtype in_dtype, int64_t M, int64_t N, int64_t K,
-                                     int64_t splits)
-{
-    const int64_t used = mgemm_splitk_chunks(in_dtype, M, N, K, splits);
-    if (used < 0) return -1;
-    return used <= 1 ? 0 : used * M * N * elem_size(partial_dtype(in_dtype));
 }
 
 const char *mgemm_status_string(mgemm_status s)

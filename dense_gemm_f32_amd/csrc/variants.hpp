@@ -56,9 +56,10 @@ hipError_t launch_gemm_f64(const KernelArgs &a, unsigned grid, hipStream_t s)
       launch_gemm<T, BM, BN, BK, WM, WN, true, true, V, D, CT>}}
 
 // fp32 inputs: fp32 C only
-#define MGEMM_VARIANT_F32(BM, BN, BK, WM, WN, V, NAME)                                       \
-    {0, BM, BN, BK, WM, WN, V, 1, NAME, MGEMM_LAUNCHERS(float, BM, BN, BK, WM, WN, V, 1, float), \
+#define MGEMM_VARIANT_F32_D(BM, BN, BK, WM, WN, V, D, NAME)                                  \
+    {0, BM, BN, BK, WM, WN, V, D, NAME, MGEMM_LAUNCHERS(float, BM, BN, BK, WM, WN, V, D, float), \
      {{nullptr, nullptr}, {nullptr, nullptr}}}
+#define MGEMM_VARIANT_F32(BM, BN, BK, WM, WN, V, NAME) MGEMM_VARIANT_F32_D(BM, BN, BK, WM, WN, V, 1, NAME)
 
 // int8 inputs: int32 C, A K-contiguous (op N) and B K-contiguous (op T) only
 #define MGEMM_VARIANT_I8(BM, BN, BK, WM, WN, V, D, NAME)                                     \

@@ -142,7 +142,8 @@ def _launch(name, c_name, op_a, op_b, M, N, K, alpha, a, lda, sa, b, ldb, sb, be
     through split-K when that pays (or is asked for), the rest through
     gemm_strided_batched_ex."""
     if batch == 1 and splitk != 1:
-        chunks = _lib.splitk_chunks(name, M, N, K, splitk or 0)
+        chunks = _lib.splitk_chunks(name, M, N, K, splitk or 0, transA=op_a, transB=op_b, A=a,
+                                    lda=lda, B=b, ldb=ldb)
         if chunks > 1:
             _lib.gemm_splitk(name, c_name, op_a, op_b, M, N, K, alpha, a.data_ptr(), lda,
                              b.data_ptr(), ldb, beta, c, ldc, splits=splitk or 0)

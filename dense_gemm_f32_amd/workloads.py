@@ -200,10 +200,10 @@ def sgemm_ragged() -> Problem:
 
 
 def sgemm_ragged_splitk() -> Problem:
-    """The ragged SGEMM through split-K with 3 chunks of 352 (the last 295): 216
-    workgroups of 128x128 instead of 272 of 64x64."""
+    """The ragged SGEMM through split-K with the automatic chunk count (3 chunks of 352,
+    the last 295: 816 workgroups of 64x64 instead of 272)."""
     p = sgemm_ragged()
-    p.splitk = 3
+    p.splitk = 0
     return p
 
 

@@ -193,32 +193,41 @@ mgemm_status gemm_f64_strided_batched(mgemm_op transA, mgemm_op transB,
                                       int64_t batch, hipStream_t stream);
 
 /*
- * Split-K GEMM for under-filled shapes (few output tiles, long K): the same
+ * Split-K GEMM for under-filled shapes: the same
  * C = alpha * op(A) * op(B) + beta * C as the entry points above (the form
  * of "Sgemm [128,128,8]" (jianshu), design comment and host_gemm), computed
- * as `splits` K-chunks whose partial products fill more of the device, then
- * summed.  The pages size their tiles per kernel through template
- * parameters ("cuda11/matmul" tutorial, sections V1-V3); a tile grid that
- * leaves most of the 256 CUs idle is the case this entry point is for.
+ * as K-chunks whose partial products spread over more of the device and
+ * are then summed.  The pages size their tiles per
+ * kernel through template parameters ("cuda11/matmul" tutorial, sections
+ * V1-V3); a tile grid that leaves most of the 256 CUs idle, or holds too
+ * few workgroups per CU to hide its loads, is the case this entry point is
+ * for.
  *   in_dtype, c_dtype  as gemm_strided_batched_ex (fp32/f16/bf16 inputs with
  *          fp32 or the inputs' 16-bit C; int8 with int32 C), or MGEMM_F64
  *          for both.
  *   alpha, beta  double; for every in_dtype but MGEMM_F64 they must be
  *          exactly representable as float (else MGEMM_INVALID_ARG).
- *   splits  requested chunk count; 0 picks one automatically, 1 runs the
- *          plain kernel.  Chunks are whole K-slabs, so fewer chunks than
- *          requested may run (mgemm_splitk_chunks tells how many).
+ *   splits  n > 1: about n chunks (whole K-slabs, so possibly fewer);
+ *          1: the plain kernel; 0: automatic, which chunks
+ *            - deep-K shapes (K >= 2 max(M, N)) whose 128x128 tiles leave
+ *              CUs idle: enough chunks for 256 workgroups, each >= 512 deep;
+ *            - grids of at most two rounds of 256 workgroups of an
+ *              unaligned build (operand rows not 16-byte aligned) whose
+ *              tile holds at least 5 us of matrix-core work: 3 chunks;
+ *          and runs the plain kernel otherwise.  mgemm_splitk_plan reports
+ *          which.
  *   workspace, workspace_bytes  device scratch owned by the caller, 16-byte
- *          aligned, at least mgemm_splitk_workspace_bytes(...) bytes (0 when
- *          one chunk runs; then workspace may be NULL).  It holds
- *          [chunks][M][N] partial products (fp32; int32 for int8; double
- *          for fp64) and is overwritten.  Calls that share a workspace must
- *          be ordered on one stream.
- * Two kernels run on `stream`: the chunked products, then a reduction that
- * adds the chunks in ascending order (deterministic), applies alpha and
- * beta (C read only when beta != 0) and rounds to C's type.  Results differ
- * from the one-pass kernels only by fp32 (fp64) summation order, and are
- * identical for integer-valued inputs whose partial sums are exact.
+ *          aligned, at least mgemm_splitk_plan(...).workspace_bytes (0 when
+ *          nothing is chunked; then workspace may be NULL).  It holds the
+ *          chunks' partial products ([chunks][M][N]: fp32; int32 for int8;
+ *          double for fp64) and is overwritten.  Calls that share a
+ *          workspace must be ordered on one stream.
+ * With chunks, two kernels run on `stream`: the chunked products, then a
+ * reduction that adds the chunks in ascending order (deterministic),
+ * applies alpha and beta (C read only when beta != 0) and rounds to C's
+ * type.  Results differ from the one-pass kernels
+ * only by fp32 (fp64) summation order, and are identical for
+ * integer-valued inputs whose partial sums are exact.
  * Errors: as gemm_strided_batched_ex, plus MGEMM_INVALID_ARG for splits < 0
  * or a missing, misaligned or short workspace.
  */
@@ -230,15 +239,6 @@ mgemm_status gemm_splitk(mgemm_dtype in_dtype, mgemm_dtype c_dtype,
                          double beta, void *C, int64_t ldc,
                          int64_t splits, void *workspace, int64_t workspace_bytes,
                          hipStream_t stream);
-
-/* Chunks gemm_splitk runs for these sizes and `splits` (0 = automatic);
- * 1 means the plain kernel; -1 for invalid arguments.  Pure host. */
-int64_t mgemm_splitk_chunks(mgemm_dtype in_dtype, int64_t M, int64_t N, int64_t K, int64_t splits);
-
-/* Workspace bytes gemm_splitk needs for these sizes and `splits`; -1 for
- * invalid arguments.  Pure host. */
-int64_t mgemm_splitk_workspace_bytes(mgemm_dtype in_dtype, int64_t M, int64_t N, int64_t K,
-                                     int64_t splits);
 
 /* Human-readable text for a status code (static storage). */
 const char *mgemm_status_string(mgemm_status s);
@@ -292,15 +292,23 @@ mgemm_status mgemm_select(mgemm_dtype in_dtype, mgemm_op transA, mgemm_op transB
  */
 mgemm_status mgemm_force_variant(mgemm_dtype dtype, int id);
 
-/* The kernel variant and grid of gemm_splitk's partial-product launch (of
- * the plain kernel when one chunk runs), the chunk count and the chunk
- * length (the last chunk takes the rest of K).  A and B stand for the
- * operand addresses (their alignment matters).  Pure host. */
-mgemm_status mgemm_splitk_select(mgemm_dtype in_dtype, mgemm_op transA, mgemm_op transB,
-                                 int64_t M, int64_t N, int64_t K,
-                                 const void *A, int64_t lda, const void *B, int64_t ldb,
-                                 int64_t splits, mgemm_variant_info *out, int64_t *grid,
-                                 int64_t *chunks, int64_t *chunk_len);
+/* What gemm_splitk will do for these arguments. */
+typedef struct {
+    int64_t workspace_bytes;   /* workspace the call needs (0: nothing chunked) */
+    int64_t chunks;            /* K-chunks (1: the plain kernel) */
+    int64_t chunk_len;         /* K per chunk; the last chunk takes the rest */
+    mgemm_variant_info variant;  /* GEMM kernel launched: the chunked products or the
+                                    plain kernel (id -1: none) */
+    int64_t grid;              /* its workgroups */
+} mgemm_splitk_plan_info;
+
+/* Fill *out with gemm_splitk's plan for these arguments (A and B stand for
+ * the operand addresses: their alignment matters, their contents do not).
+ * Pure host; MGEMM_INVALID_ARG for splits < 0 or out == NULL. */
+mgemm_status mgemm_splitk_plan(mgemm_dtype in_dtype, mgemm_op transA, mgemm_op transB,
+                               int64_t M, int64_t N, int64_t K,
+                               const void *A, int64_t lda, const void *B, int64_t ldb,
+                               int64_t splits, mgemm_splitk_plan_info *out);
 
 #ifdef __cplusplus
 }

@@ -270,14 +270,38 @@ def test_splitk_rules_without_a_gpu():
         assert call(in_dt, c_dt, M=0, ws=None, wbytes=0) == 0
     assert call(5, 5, M=0, alpha=1.0 + 2 ** -40, ws=None, wbytes=0) == 0   # fp64 takes doubles
     # chunk planning: whole K-slabs, the automatic count fills the device
-    assert mg.splitk_chunks("f32", 1000, 1027, 999, 0) == 1    # K not deep enough: one pass
     assert mg.splitk_chunks("f32", 512, 512, 4096, 0) == 8     # 16 tiles, chunks >= 512 deep
     assert mg.splitk_chunks("f32", 256, 256, 8192, 0) == 16
     assert mg.splitk_chunks("f32", 4096, 4096, 4096, 0) == 1   # already fills 256 CUs
     assert mg.splitk_chunks("f32", 64, 64, 100, 8) == 4        # 32-deep slabs: 100 -> 4 chunks
     assert mg.splitk_chunks("bf16", 64, 64, 1000, 3) == 3
-    assert mg.splitk_chunks("i8", 64, 64, 1000, 16) == 8       # 128-byte slabs
+    assert mg.splitk_chunks("i8", 64, 64, 1000, 16, transB=1) == 8   # 128-byte slabs
     assert mg.splitk_workspace_bytes("f64", 100, 50, 1000, 4) == 4 * 100 * 50 * 8
-    assert mg.splitk_workspace_bytes("i8", 100, 50, 1024, 2) == 2 * 100 * 50 * 4
+    assert mg.splitk_workspace_bytes("i8", 100, 50, 1024, 2, transB=1) == 2 * 100 * 50 * 4
     assert mg.splitk_workspace_bytes("f32", 100, 50, 1000, 1) == 0
-    assert lib.mgemm_splitk_chunks(0, -1, 4, 4, 0) == -1
+    info = _lib.SplitkPlanInfo()
+    assert lib.mgemm_splitk_plan(0, 0, 0, 4, 4, 4, ALIGNED, 4, ALIGNED, 4, -1, ctypes.byref(info)) == 1
+    assert lib.mgemm_splitk_plan(0, 0, 0, 4, 4, 4, ALIGNED, 4, ALIGNED, 4, 0, None) == 1
+
+
+def test_splitk_automatic_plans():
+    # a small grid of unaligned tiles: three chunks of all of C
+    p = mg.splitk_plan("f32", 1000, 1027, 999, 0, lda=999, ldb=1027)
+    assert p["chunks"] == 3 and p["chunk_len"] == 352
+    assert p["variant"]["name"].endswith("_u") and p["grid"] == 3 * 16 * 17
+    assert p["workspace_bytes"] == 3 * 1000 * 1027 * 4
+    # the same shape with aligned rows stays one pass (the DMA path hides its loads)
+    assert mg.splitk_plan("f32", 1024, 1024, 1024, 0)["chunks"] == 1
+    assert mg.splitk_plan("f64", 1024, 1024, 1024, 0)["chunks"] == 1
+    # short tiles (16-bit) are not worth two extra launches
+    assert mg.splitk_plan("bf16", 1000, 1027, 999, 0, lda=999, ldb=1027)["chunks"] == 1
+    # deep K: enough chunks for 256 workgroups
+    d = mg.splitk_plan("f32", 256, 256, 8192, 0)
+    assert d["chunks"] == 16 and d["grid"] == 256
+    # big grids stay one pass; the plan then names the plain kernel
+    b = mg.splitk_plan("f32", 4096, 4096, 4096, 0)
+    assert b["chunks"] == 1 and b["workspace_bytes"] == 0
+    assert b["variant"]["name"] == "mgemm_f32_256x256x32_w4x2" and b["grid"] == 256
+    # explicit counts; 1 is the plain kernel
+    assert mg.splitk_plan("f32", 1000, 1027, 999, 4)["chunks"] == 4
+    assert mg.splitk_plan("f32", 1000, 1027, 999, 1)["chunks"] == 1

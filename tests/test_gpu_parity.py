@@ -395,7 +395,8 @@ def test_splitk_every_type_and_transpose_exact(dtype, c_dtype, hi):
                 p = dataclasses.replace(p, int_lo=-20, int_hi=20)
             if dtype in ("f16", "bf16") and c_dtype != "f32":
                 p = dataclasses.replace(p, int_lo=-4, int_hi=4)
-            n = mg.splitk_chunks(dtype, M, N, K, splits)
+            n = mg.splitk_chunks(dtype, M, N, K, splits, transA=int(tA), transB=int(tB),
+                                 lda=p.lda, ldb=p.ldb)
             assert n > 1
             full_check(p, exact=True, what=f"split-K {dtype}->{c_dtype} x{n} tA={int(tA)} tB={int(tB)}")
 
@@ -405,7 +406,7 @@ def test_splitk_float_inputs_within_tolerance(dtype):
     p = wl.Problem(dtype, 257, 190, 3000, transA=True, alpha=0.75, beta=-1.25,
                    dist="normal" if dtype == "bf16" else "uniform", c_dist="uniform", seed=92,
                    splitk=6)
-    full_check(p, what=f"split-K {dtype} x{mg.splitk_chunks(dtype, 257, 190, 3000, 6)}")
+    full_check(p, what=f"split-K {dtype} x{mg.splitk_chunks(dtype, 257, 190, 3000, 6, transA=1)}")
 
 
 def test_splitk_workspace_reused_by_a_smaller_call():
@@ -430,8 +431,24 @@ def test_splitk_quick_returns_and_one_chunk():
 
 def test_sgemm_ragged_splitk_bit_exact():
     p = wl.sgemm_ragged_splitk()
-    assert mg.splitk_chunks("f32", p.M, p.N, p.K, p.splitk) == 3
+    assert mg.splitk_chunks("f32", p.M, p.N, p.K, p.splitk, lda=p.lda, ldb=p.ldb) == 3
     full_check(p, exact=True, what="ragged 1000x1027x999 through split-K")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64"])
+def test_splitk_auto_small_unaligned_grid(dtype):
+    # odd leading dimensions, a grid of 16 x 17 tiles: the automatic plan
+    # chunks all of C in three; integer data bit-exact, float data in tolerance
+    for tA, tB in itertools.product((False, True), repeat=2):
+        p = wl.Problem(dtype, 1000, 1027, 999, transA=tA, transB=tB, alpha=2.0, beta=-1.0,
+                       dist="int", int_lo=-20, int_hi=20, c_dist="int", seed=98, splitk=0)
+        plan = mg.splitk_plan(dtype, 1000, 1027, 999, 0, transA=int(tA), transB=int(tB),
+                              lda=p.lda, ldb=p.ldb)
+        assert plan["chunks"] == 3, plan
+        full_check(p, exact=True, what=f"automatic split-K {dtype} tA={int(tA)} tB={int(tB)}")
+    q = wl.Problem(dtype, 1000, 1027, 999, alpha=0.5, beta=0.25, dist="uniform", c_dist="uniform",
+                   seed=99, splitk=0)
+    full_check(q, what=f"automatic split-K {dtype} uniform")
 
 
 def test_splitk_auto_on_a_deep_k_shape():
