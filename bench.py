@@ -52,6 +52,7 @@ PRIMARY = "sgemm_4096"
 CASES = ("sgemm_256", "sgemm_4096", "sgemm_ragged", "sgemm_ragged_splitk", "gemm_bf16_8192",
          "gemm_f16_8192", "qkt_batched", "qkt_batched_f16_out", "gemm_i8_8192", "dgemm_4096")
 HBM_BOUND = ("qkt_batched", "qkt_batched_f16_out")
+GRAPH_CASES = ("sgemm_256", "sgemm_ragged_splitk")   # launch-bound: also timed from a HIP graph
 MOPS_COUNTER = {"f32": "SQ_INSTS_VALU_MFMA_MOPS_F32", "f16": "SQ_INSTS_VALU_MFMA_MOPS_F16",
                 "bf16": "SQ_INSTS_VALU_MFMA_MOPS_BF16", "i8": "SQ_INSTS_VALU_MFMA_MOPS_I8",
                 "f64": "SQ_INSTS_VALU_MFMA_MOPS_F64"}
@@ -347,6 +348,30 @@ def time_each(torch, fn, iters, between=None):
     return [e0.elapsed_time(e1) * 1e-3 for e0, e1 in evs]
 
 
+def time_graph(torch, fn, calls=20, replays=10):
+    """Per-call time of `calls` library calls captured into one HIP graph (torch's graph
+    capture records the kernels the calls enqueue) and replayed `replays` times."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            for _ in range(calls):
+                fn()
+    torch.cuda.current_stream().wait_stream(side)
+    g.replay()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record(s)
+    for _ in range(replays):
+        g.replay()
+    stop.record(s)
+    stop.synchronize()
+    return start.elapsed_time(stop) / (calls * replays) * 1e-3
+
+
 def algorithmic_bytes(p):
     """Compulsory HBM traffic: A and B once, C written (and read when beta != 0)."""
     from dense_gemm_f32_amd import workloads as wl
@@ -387,6 +412,10 @@ def per_config(torch, dev, iters):
             gbs = algorithmic_bytes(p) / t / 1e9
             rec["hbm_gbs"] = round(gbs, 1)
             rec["frac_hbm_peak"] = round(gbs / PEAK_HBM_GBS, 4)
+        if name in GRAPH_CASES:
+            tg = time_graph(torch, fn)
+            rec["graph_ms"] = round(tg * 1e3, 4)
+            rec["graph_tflops"] = round(p.flops / tg / 1e12, 2)
         if name == PRIMARY:
             scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
             cold = time_each(torch, fn, 10, between=lambda: scratch.fill_(1))

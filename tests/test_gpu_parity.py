@@ -593,3 +593,42 @@ def test_runs_on_a_side_stream():
     s.synchronize()
     got = r.result()
     check_tolerance(got, r.oracle_full(), p, "side stream")
+
+
+# ------------------------------------------------------------------ HIP graph capture
+
+def test_launches_replay_in_a_hip_graph():
+    # The library only enqueues kernels on the caller's stream, so a capture
+    # records them.  Each replay is checked against the eager result, with
+    # eager work and synchronisation between replays.
+    p = wl.Problem("f32", 256, 256, 256, alpha=1.5, beta=0.5, dist="int", int_lo=-8, int_hi=8,
+                   c_dist="int", seed=120)
+    r = Run(p)
+    c0 = r.dCbuf.clone()
+    r.launch()
+    eager = r.result()
+    check_exact(eager, r.oracle_full(), "eager 256^3")
+    q = wl.Problem("f32", 256, 256, 8192, dist="int", int_lo=-8, int_hi=8, seed=121, splitk=0)
+    rq = Run(q)
+    ws = torch.empty(mg.splitk_workspace_bytes("f32", 256, 256, 8192, 0), dtype=torch.uint8,
+                     device="cuda")
+    rq.launch(workspace=ws)
+    eager_q = rq.result()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):          # capture on a side stream, as torch requires
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            r.launch()
+            rq.launch(workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    for rep in range(3):
+        r.dCbuf.copy_(c0)                  # beta = 0.5 reads C: restore it eagerly
+        rq.dC.fill_(float("nan"))          # beta = 0: C is overwritten (guard bands kept)
+        junk = torch.randn(1 << 20, device="cuda").sum()      # unrelated eager work
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert float(junk) == float(junk)
+        check_exact(r.result(), eager, f"graph replay {rep} (256^3)")
+        check_exact(rq.result(), eager_q, f"graph replay {rep} (split-K 256x256x8192)")
