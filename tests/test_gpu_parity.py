@@ -506,9 +506,28 @@ def test_empty_problems_touch_nothing():
 
 def test_minimum_sizes():
     for M, N, K in ((1, 1, 1), (1, 7, 3), (5, 1, 9), (3, 3, 1), (33, 65, 2)):
-        for dt in ("f32", "f16", "bf16"):
+        for dt in ("f32", "f16", "bf16", "f64"):
             full_check(wl.Problem(dt, M, N, K, dist="int", int_lo=-9, int_hi=9, seed=23),
-                       exact=True, what="tiny")
+                       exact=True, what=f"tiny {dt}")
+        full_check(wl.Problem("i8", M, N, K, transB=True, c_dtype="i32", dist="int", int_lo=-128,
+                              int_hi=127, seed=24), exact=True, what="tiny i8")
+        # split-K on tiny shapes: one chunk (plain kernel) or a few short ones
+        full_check(wl.Problem("f32", M, N, K, dist="int", int_lo=-9, int_hi=9, seed=25, splitk=4),
+                   exact=True, what="tiny split-K")
+
+
+def test_empty_problems_for_every_entry_point():
+    # M, N or batch == 0: OK, nothing launched, nothing written
+    c = torch.full((64,), 3.0, device="cuda", dtype=torch.float64)
+    mg.gemm_f64(0, 0, 0, 4, 4, 1.0, c, 4, c, 4, 0.0, c, 4)
+    mg.gemm_f64_strided_batched(0, 0, 4, 4, 4, 1.0, c, 4, 16, c, 4, 16, 0.0, c, 4, 16, 0)
+    ci = torch.full((64,), 3, device="cuda", dtype=torch.int32)
+    a8 = torch.zeros(64, device="cuda", dtype=torch.int8)
+    mg.gemm_strided_batched_ex("i8", "i32", 0, 1, 4, 0, 4, 1.0, a8, 4, 0, a8, 4, 0, 0.0, ci, 1, 0, 1)
+    cf = torch.full((64,), 3.0, device="cuda")
+    mg.gemm_splitk("f32", "f32", 0, 0, 0, 4, 64, 1.0, cf, 64, cf, 4, 0.0, cf, 4, splits=4)
+    torch.cuda.synchronize()
+    assert torch.all(c == 3.0) and torch.all(ci == 3) and torch.all(cf == 3.0)
 
 
 def test_leading_dimensions_beyond_32bit_tile_offsets():
