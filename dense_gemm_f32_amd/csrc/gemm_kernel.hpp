@@ -133,6 +133,18 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, uint32_t lds_ad
                  :: "s"(lds_addr), "v"(voff), "s"(rs), "s"(soff) : "memory");
 }
 
+// 4-byte global -> LDS copy: lane l's 4 bytes from rsrc[voff] land at LDS byte
+// lds_addr + 4*l.  A lane whose voff is past the buffer's range (kOutOfRange)
+// is masked by the hardware's range check: no memory is read and a zero is
+// written to its LDS word (checked with a one-wave probe).
+constexpr int kOutOfRange = 0x7fffffff;
+
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t rs, uint32_t lds_addr, int voff)
+{
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                 :: "s"(lds_addr), "v"(voff), "s"(rs) : "memory");
+}
+
 __device__ __forceinline__ uint32_t lds_addr_of(const char *p)
 {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p;
@@ -586,6 +598,11 @@ struct RegPath {
 //      slab placed before the MFMAs of its last k-group so that the next
 //      slab's first fragment reads overlap them.
 //   2  the same with BK = BKR, NS = 2 (one slab ahead, half the barriers).
+//   4  fp32 with 4-byte copies, BK = BKR, NS = 2, for every tile of any
+//      4-byte aligned problem: each lane copies one element, and lanes whose
+//      element lies past the matrix (row, column or k) are masked to zero by
+//      the buffer range check, so edges and odd leading dimensions need no
+//      register path.
 //
 // LDS layouts (bank-conflict free for every access of this path):
 //   KC  operand K-contiguous in memory: rows of BK elements (RB = 64 or 128
@@ -612,8 +629,10 @@ struct DmaPath {
     static constexpr bool F32 = (ES == 4);
     static constexpr int WTM = BM / WM, WTN = BN / WN;
     static constexpr int TM = WTM / 32, TN = WTN / 32;
-    static constexpr int BK = PIPE == 2 ? BKR : BKR / 2;
-    static constexpr int NS = PIPE == 2 ? 2 : 4;
+    static constexpr bool DW = PIPE == 4;  // 4-byte copies, every tile (fp32)
+    static_assert(!DW || sizeof(T) == 4, "4-byte copies are for fp32");
+    static constexpr int BK = PIPE == 2 || DW ? BKR : BKR / 2;
+    static constexpr int NS = PIPE == 1 ? 4 : 2;
     static constexpr int RB = BK * ES;          // K-contiguous row bytes
     static_assert(RB == 64 || RB == 128, "64- or 128-byte K-contiguous rows");
     static constexpr int CPR = RB / 16;         // 16-byte chunks per row
@@ -625,8 +644,9 @@ struct DmaPath {
     static constexpr int STAGE = A_BYTES + B_BYTES;
     static constexpr int LDS_BYTES = NS * STAGE;
     static constexpr int A_ROWB = BM * ES, B_ROWB = BN * ES;  // MC row bytes
-    static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "DMA split");
-    static constexpr int A_IPW = A_BYTES / 1024 / NW, B_IPW = B_BYTES / 1024 / NW;
+    static constexpr int CPY = DW ? 256 : 1024;  // LDS bytes one copy instruction fills
+    static_assert(A_BYTES % (CPY * NW) == 0 && B_BYTES % (CPY * NW) == 0, "DMA split");
+    static constexpr int A_IPW = A_BYTES / CPY / NW, B_IPW = B_BYTES / CPY / NW;
     static constexpr int LPS = A_IPW + B_IPW;  // DMA loads per slab per thread
     static_assert((NS - 1) * LPS <= 63, "vmcnt range");
     static_assert(A_KC || A_ROWB >= 128, "MC rows of at least 128 bytes");
@@ -680,6 +700,31 @@ struct DmaPath {
             const int lb = (((bb >> 6) ^ mc_key<ROWB>(k)) << 6) | (bb & 63);
             dma16(rs, lds_addr_of(dst + ins * 1024), k * ld_bytes + lb, 0);
         }
+    }
+
+    // 4-byte copy instruction q (of IPW) of wave `w`: 256 bytes of the
+    // operand's region `dst`, laid out exactly as dma_one lays them (KC rows
+    // with swizzled chunks, or MC rows with permuted pieces).  Memory tile
+    // rows < rows_ok and columns < cols_ok exist; any other element reads as
+    // zero through an out-of-range offset.
+    template <bool KC, int IL, int ROWB, int IPW>
+    __device__ __forceinline__ static void dma_dw(__amdgpu_buffer_rsrc_t rs, char *dst, int ld_bytes, int w,
+                                                  int lane, int q, int rows_ok, int cols_ok)
+    {
+        const int ins = w * IPW + q;
+        const int b = ins * 256 + 4 * lane;  // byte of the operand's LDS region
+        int r, c;                            // memory row and column (elements) of the tile
+        if constexpr (KC) {
+            const int pr = b / RB, within = b % RB;   // physical row, byte within it
+            r = logical_row<IL>(pr);
+            c = ((((within >> 4) ^ swz(pr)) << 4) | (within & 15)) >> 2;
+        } else {
+            const int k = b / ROWB, bb = b % ROWB;
+            r = k;
+            c = ((((bb >> 6) ^ mc_key<ROWB>(k)) << 6) | (bb & 63)) >> 2;
+        }
+        const int voff = (r < rows_ok && c < cols_ok) ? r * ld_bytes + 4 * c : kOutOfRange;
+        dma4(rs, lds_addr_of(dst + ins * 256), voff);
     }
 
     // Fragment of one MC 16-bit operand (rows k, columns mn): the 8 k-values
@@ -808,21 +853,34 @@ struct DmaPath {
         const int lda_b = (int)(p.lda * ES), ldb_b = (int)(p.ldb * ES);
 
         auto stage = [&](int s) { return smem + (s % NS) * STAGE; };
+        const int mrem = p.M - m0, nrem = p.N - n0;
         auto issue = [&](int s) {
             char *st = stage(s);
             const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ap + (int64_t)s * a_kstep);
             const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bp + (int64_t)s * b_kstep);
+            if constexpr (DW) {
+                const int krem = p.K - s * BK;
 #pragma unroll
-            for (int q = 0; q < A_IPW; ++q) dma_one<A_KC, IL_A, A_ROWB, A_IPW>(ra, st, lda_b, w, lane, q);
+                for (int q = 0; q < A_IPW; ++q)
+                    dma_dw<A_KC, IL_A, A_ROWB, A_IPW>(ra, st, lda_b, w, lane, q, A_KC ? mrem : krem,
+                                                      A_KC ? krem : mrem);
 #pragma unroll
-            for (int q = 0; q < B_IPW; ++q) dma_one<B_KC, IL_B, B_ROWB, B_IPW>(rb, st + A_BYTES, ldb_b, w, lane, q);
+                for (int q = 0; q < B_IPW; ++q)
+                    dma_dw<B_KC, IL_B, B_ROWB, B_IPW>(rb, st + A_BYTES, ldb_b, w, lane, q,
+                                                      B_KC ? nrem : krem, B_KC ? krem : nrem);
+            } else {
+#pragma unroll
+                for (int q = 0; q < A_IPW; ++q) dma_one<A_KC, IL_A, A_ROWB, A_IPW>(ra, st, lda_b, w, lane, q);
+#pragma unroll
+                for (int q = 0; q < B_IPW; ++q) dma_one<B_KC, IL_B, B_ROWB, B_IPW>(rb, st + A_BYTES, ldb_b, w, lane, q);
+            }
         };
         auto frags = [&](int s, int g, Fr &f) {
             const char *st = stage(s);
             load_frags(st, st + A_BYTES, g, L, f);
         };
 
-        const int nk = p.K / BK;
+        const int nk = DW ? (p.K + BK - 1) / BK : p.K / BK;  // 4-byte copies zero-fill the last slab
         // prologue: slabs 0..NS-1 in flight, wait for slab 0
         issue(0);
 #pragma unroll
@@ -1072,7 +1130,9 @@ gemm_kernel(KernelArgs p)
     using R = RegPath<T, BM, BN, BK, WM, WN, TA, TB, VECOK>;
     using D = DmaPath<T, BM, BN, BK, WM, WN, TA, TB, PIPE>;
     constexpr int TM = R::TM, TN = R::TN, WTM = R::WTM, WTN = R::WTN;
-    constexpr int LDS = (VECOK && D::LDS_BYTES > R::LDS_BYTES) ? D::LDS_BYTES : R::LDS_BYTES;
+    constexpr bool ALL_DMA = D::DW;  // 4-byte copies serve every tile: no register path
+    constexpr int LDS = ALL_DMA ? D::LDS_BYTES
+                        : (VECOK && D::LDS_BYTES > R::LDS_BYTES) ? D::LDS_BYTES : R::LDS_BYTES;
     __shared__ __attribute__((aligned(1024))) char smem[LDS];
     int bidx, tm, tn;
     map_tile(p, bidx, tm, tn);
@@ -1085,16 +1145,24 @@ gemm_kernel(KernelArgs p)
 #pragma unroll
         for (int u = 0; u < TN; ++u)
             acc[t][u] = f32x16{};
-    if constexpr (VECOK) {
-        const bool interior = pk.fast_ok && m0 + BM <= pk.M && n0 + BN <= pk.N && pk.K % D::BK == 0;
-        if (interior) {
-            D::run(pk, smem, bidx, m0, n0, acc);
+    if constexpr (ALL_DMA) {
+        D::run(pk, smem, bidx, m0, n0, acc);
+        if (m0 + BM <= pk.M && n0 + BN <= pk.N)
             epilogue<false, D::IL_A, D::IL_B, TM, TN, WTM, WTN, WN, CT>(pk, bidx, m0, n0, acc);
-            return;
+        else
+            epilogue<true, D::IL_A, D::IL_B, TM, TN, WTM, WTN, WN, CT>(pk, bidx, m0, n0, acc);
+    } else {
+        if constexpr (VECOK) {
+            const bool interior = pk.fast_ok && m0 + BM <= pk.M && n0 + BN <= pk.N && pk.K % D::BK == 0;
+            if (interior) {
+                D::run(pk, smem, bidx, m0, n0, acc);
+                epilogue<false, D::IL_A, D::IL_B, TM, TN, WTM, WTN, WN, CT>(pk, bidx, m0, n0, acc);
+                return;
+            }
         }
+        R::run(pk, smem, bidx, m0, n0, acc);
+        epilogue<true, R::IL_A, R::IL_B, TM, TN, WTM, WTN, WN, CT>(pk, bidx, m0, n0, acc);
     }
-    R::run(pk, smem, bidx, m0, n0, acc);
-    epilogue<true, R::IL_A, R::IL_B, TM, TN, WTM, WTN, WN, CT>(pk, bidx, m0, n0, acc);
 }
 
 // C = beta * C over a strided batch (alpha == 0 or K == 0), in C's own type.

@@ -163,13 +163,15 @@ mgemm_status validate_and_plan(int dtype, int c_dtype, int transA, int transB, i
     const bool vec_ok = aligned(A, 16) && aligned(B, 16) && lda % vec == 0 && ldb % vec == 0 &&
                         strideA % vec == 0 && strideB % vec == 0;
 
+    // builds with 4-byte copies (pipe 4) address their tiles with 32-bit offsets too
+    auto offsets_ok = [&](const Variant &v) { return v.pipe != 4 || a.fast_ok; };
     Table t = table_for(dtype);
     const int forced = g_forced[dtype].load();
     int pick = -1;
     if (forced >= 0) {
         const Variant *v = variant_by_id(forced);
-        if (v && (!v->vec || vec_ok)) pick = forced - t.first_id;
-        // a forced aligned-only variant on unaligned data falls back to the automatic choice
+        if (v && (!v->vec || vec_ok) && offsets_ok(*v)) pick = forced - t.first_id;
+        // a forced variant the operands do not allow falls back to the automatic choice
     }
     if (pick < 0) {
         // The table is in order of preference (measured on the large square
@@ -181,7 +183,7 @@ mgemm_status validate_and_plan(int dtype, int c_dtype, int transA, int transB, i
         // with 4x2 wavefronts measured best, so it moves to the front.
         const int64_t min_wgs = 256;
         int best = -1, smallest = -1;
-        auto eligible = [&](const Variant &v) { return v.vec == vec_ok; };  // aligned build when allowed
+        auto eligible = [&](const Variant &v) { return v.vec == vec_ok && offsets_ok(v); };
         auto wgs_of = [&](const Variant &v) {
             return ((M + v.bm - 1) / v.bm) * ((N + v.bn - 1) / v.bn) * batch;
         };

@@ -150,6 +150,32 @@ def test_dma_path_short_k(dtype):
             full_check(base, exact=True, what=f"{v['name']} K={K}")
 
 
+def test_four_byte_copy_variants():
+    # fp32 builds whose every tile copies 4-byte elements into LDS, with
+    # out-of-matrix lanes masked to zero: odd leading dimensions with NaN in
+    # the padding, K tails of every length mod the slab, slab counts through
+    # the steady state, every transpose, a batch with a shared operand
+    for v in variants_of("f32"):
+        if v["pipe"] != 4:
+            continue
+        mg.force_variant("f32", v["id"])
+        bm, bn, bk = v["block_m"], v["block_n"], v["block_k"]
+        for i, K in enumerate((1, bk - 1, bk, bk + 1, 3 * bk + 17, 9 * bk + 5)):
+            tA, tB = bool(i & 1), bool(i & 2)
+            M, N = bm + 3 + i, 2 * bn - 7
+            p = wl.Problem("f32", M, N, K, transA=tA, transB=tB, alpha=1.5, beta=0.5,
+                           lda=(M if tA else K) + 1, ldb=(K if tB else N) + 3, ldc=N + 1,
+                           dist="int", int_lo=-20, int_hi=20, c_dist="int", seed=70 + i,
+                           pad_value=float("nan"))
+            _assert_selected(p, v)
+            full_check(p, exact=True, what=f"{v['name']} K={K} tA={int(tA)} tB={int(tB)}")
+        q = wl.Problem("f32", bm + 5, bn + 9, 2 * bk + 3, transB=True, batch=3, strideB=0,
+                       lda=2 * bk + 4, ldb=2 * bk + 5, dist="uniform", seed=77)
+        q.force_batched = True
+        _assert_selected(q, v)
+        full_check(q, what=f"{v['name']} batched, B shared")
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_dma_path_batched_and_broadcast(dtype):
     # interior tiles in several batch entries, B shared by all entries (stride 0)
