@@ -5,20 +5,31 @@ namespace mgemm {
 
 const Variant *f32_variants(int *count)
 {
-    // Preference order: the first variant that gives at least one workgroup
-    // per CU is taken (see the selection in mgemm_api.cpp).
+    // Chosen by the lowest estimated time (Cost in variants.hpp: t0 us, tk us
+    // per unit of K, register-path factor, one-round factor); a build without
+    // an estimate runs only when forced or when no estimated build fits.
+    // Rounds: 256x256 0.234 us per K (0.91 of the matrix peak per CU),
+    // 128x128 0.0605 (0.88), 64x64 two-stage 0.0166 (0.80), the 4-byte-copy
+    // builds 0.0658 and 0.0185.  The 64x64 tiles lose per flop but win where
+    // the larger tiles leave a last round mostly empty (4608^3: 324 tiles of
+    // 256x256 are two rounds, 5184 of 64x64 twenty-one).  The 64x64 two-stage
+    // build's register factor is its one-round figure (1000^3: 39 us against
+    // 26 us for 1024^3 on the DMA path); over several rounds it measured 1.2
+    // to 1.3, where the 4-byte-copy build is faster still.
     static const Variant table[] = {
-        MGEMM_VARIANT_F32(256, 256, 32, 4, 2, true, "mgemm_f32_256x256x32_w4x2"),
-        MGEMM_VARIANT_F32(256, 256, 32, 2, 2, true, "mgemm_f32_256x256x32_w2x2"),
-        MGEMM_VARIANT_F32(128, 128, 32, 2, 2, true, "mgemm_f32_128x128x32_w2x2"),
-        MGEMM_VARIANT_F32_D(128, 128, 32, 2, 2, false, 4, "mgemm_f32_128x128x32_w2x2_d4_u"),
-        MGEMM_VARIANT_F32(128, 128, 32, 2, 2, false, "mgemm_f32_128x128x32_w2x2_u"),
+        MGEMM_VARIANT_F32(256, 256, 32, 4, 2, true, "mgemm_f32_256x256x32_w4x2", {13.9f, 0.2344f, 1.10f, 1.0f}),
+        MGEMM_VARIANT_F32(256, 256, 32, 2, 2, true, "mgemm_f32_256x256x32_w2x2", {}),
+        MGEMM_VARIANT_F32(128, 128, 32, 2, 2, true, "mgemm_f32_128x128x32_w2x2", {6.6f, 0.0605f, 1.15f, 1.25f}),
+        MGEMM_VARIANT_F32_D(128, 128, 32, 2, 2, false, 4, "mgemm_f32_128x128x32_w2x2_d4_u",
+                            {9.9f, 0.0658f, 1.0f, 1.25f}),
+        MGEMM_VARIANT_F32(128, 128, 32, 2, 2, false, "mgemm_f32_128x128x32_w2x2_u", {}),
         // 64x64: two stages of 32 (one barrier per 16 MFMAs) measured 9-14%
         // faster than four of 16 at 512^3 to 2048^3 (deeper rings of 8 or 16
         // stages gained nothing)
-        MGEMM_VARIANT_F32_D(64, 64, 32, 2, 2, true, 2, "mgemm_f32_64x64x32_w2x2_d2"),
-        MGEMM_VARIANT_F32_D(64, 64, 32, 2, 2, false, 4, "mgemm_f32_64x64x32_w2x2_d4_u"),
-        MGEMM_VARIANT_F32(64, 64, 32, 2, 2, false, "mgemm_f32_64x64x32_w2x2_u"),
+        MGEMM_VARIANT_F32_D(64, 64, 32, 2, 2, true, 2, "mgemm_f32_64x64x32_w2x2_d2", {2.1f, 0.0166f, 1.5f, 1.4f}),
+        MGEMM_VARIANT_F32_D(64, 64, 32, 2, 2, false, 4, "mgemm_f32_64x64x32_w2x2_d4_u",
+                            {2.9f, 0.0185f, 1.0f, 1.6f}),
+        MGEMM_VARIANT_F32(64, 64, 32, 2, 2, false, "mgemm_f32_64x64x32_w2x2_u", {}),
     };
     *count = sizeof(table) / sizeof(table[0]);
     return table;

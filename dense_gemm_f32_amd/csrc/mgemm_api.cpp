@@ -173,20 +173,44 @@ mgemm_status validate_and_plan(int dtype, int c_dtype, int transA, int transB, i
         if (v && (!v->vec || vec_ok) && offsets_ok(*v)) pick = forced - t.first_id;
         // a forced variant the operands do not allow falls back to the automatic choice
     }
+    auto wgs_of = [&](const Variant &v) {
+        return ((M + v.bm - 1) / v.bm) * ((N + v.bn - 1) / v.bn) * batch;
+    };
     if (pick < 0) {
-        // The table is in order of preference (measured on the large square
-        // problems): take the first variant that still gives at least one
-        // workgroup per CU (256 CUs); if none does, the smallest tile, to spread
-        // a small problem over more CUs.  A shallow K (the whole product is a
-        // couple of slabs, e.g. attention scores with a 64-wide head) is bound
-        // by the C store rather than the matrix cores: there the 256x256 tile
-        // with 4x2 wavefronts measured best, so it moves to the front.
+        // Builds with a time estimate (Cost in variants.hpp): the lowest one.
+        // Builds without 16-byte loads serve aligned operands too.  A build
+        // with a DMA path and a register path pays the register factor when
+        // any tile takes the latter (the 4-byte-copy builds have no second
+        // path); a grid of one round pays the one-round factor.
+        double best_us = 0.0;
+        for (int i = 0; i < t.n; ++i) {
+            const Variant &v = t.v[i];
+            if (v.cost.tk <= 0.0f || (v.vec && !vec_ok) || !offsets_ok(v)) continue;
+            const int64_t rounds = (wgs_of(v) + 255) / 256;
+            const int64_t dma_slab = v.pipe == 1 ? v.bk / 2 : v.bk;
+            const bool reg_tiles = v.pipe != 4 && (!a.fast_ok || K % dma_slab != 0 || M % v.bm != 0 ||
+                                                   N % v.bn != 0);
+            double us = (double)rounds * (v.cost.t0 + v.cost.tk * (double)K);
+            if (reg_tiles) us *= v.cost.reg;
+            if (rounds == 1) us *= v.cost.solo;
+            if (pick < 0 || us < best_us) {
+                pick = i;
+                best_us = us;
+            }
+        }
+    }
+    if (pick < 0) {
+        // Types without estimates: the table is in order of preference
+        // (measured on the large square problems): take the first variant
+        // that still gives at least one workgroup per CU (256 CUs); if none
+        // does, the smallest tile, to spread a small problem over more CUs.
+        // A shallow K (the whole product is a couple of slabs, e.g. attention
+        // scores with a 64-wide head) is bound by the C store rather than the
+        // matrix cores: there the 256x256 tile with 4x2 wavefronts measured
+        // best, so it moves to the front.
         const int64_t min_wgs = 256;
         int best = -1, smallest = -1;
         auto eligible = [&](const Variant &v) { return v.vec == vec_ok && offsets_ok(v); };
-        auto wgs_of = [&](const Variant &v) {
-            return ((M + v.bm - 1) / v.bm) * ((N + v.bn - 1) / v.bn) * batch;
-        };
         if (dtype != MGEMM_F32 && K <= 128) {
             for (int i = 0; i < t.n && best < 0; ++i)
                 if (eligible(t.v[i]) && t.v[i].bm == 256 && t.v[i].bn == 256 && t.v[i].wm == 4 &&
@@ -285,10 +309,10 @@ struct SplitPlan {
 // stands in for C or the workspace when only the variant choice is wanted
 const void *const kAnyAligned = reinterpret_cast<const void *>((uintptr_t)256);
 
-// Small grids of unaligned tiles: when the plain grid is at most two rounds
-// of 256 workgroups and its tile is an unaligned build (the range-checked
-// register path only), about one workgroup per CU leaves that path's load
-// latency exposed.  Three chunks of all of C triple the
+// Small grids of builds without 16-byte loads: when the plain grid is at most
+// two rounds of 256 workgroups and its build copies 4 bytes per lane (or has
+// only the range-checked register path), about one workgroup per CU leaves
+// the load latency exposed.  Three chunks of all of C triple the
 // workgroups per CU.  Applied only where one tile's MFMA work is at least
 // 5 us at the matrix peak, so that the two extra launches stay small beside
 // it.  (Measured, plain -> 3 chunks: ragged 1000x1027x999 fp32 56 -> 46 us,

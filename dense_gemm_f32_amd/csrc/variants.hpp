@@ -11,15 +11,32 @@ namespace mgemm {
 
 using LaunchFn = hipError_t (*)(const KernelArgs &, unsigned grid, hipStream_t);
 
+// Time model of one build, for the automatic choice: a CU runs its share of the
+// workgroups one after another, so a launch of W workgroups takes ceil(W/256)
+// "rounds" of t0 + tk*K microseconds on 256 CUs.  reg multiplies the round when
+// some tiles take the range-checked register path (edge tiles, a K that is no
+// multiple of the DMA slab, or offsets past 32 bits).  solo multiplies a
+// launch of one round: a CU holding a single workgroup cannot hide one
+// workgroup's load latency behind another's MFMAs.  Measured on MI355X by
+// forcing each build over square and oblong shapes from 512 to 8192 (t0, tk:
+// least squares over the launches of at least two rounds; solo: launches of
+// 256 workgroups).  tk == 0: no estimate; such a build runs only when asked
+// for by name or when no estimated build fits.
+struct Cost {
+    float t0, tk, reg, solo;
+};
+
 struct Variant {
     int dtype;            // mgemm_dtype of A and B
     int bm, bn, bk;       // workgroup tile and K-slab
     int wm, wn;           // wavefront grid
     bool vec;             // needs 16-byte aligned A/B rows (dwordx4 loads)
-    int pipe;             // DMA-path schedule (1: 4 stages of bk/2, 2: 2 stages of bk)
+    int pipe;             // DMA-path schedule (1: 4 stages of bk/2, 2: 2 stages of bk,
+                          // 4: 4-byte copies, 2 stages of bk, every tile)
     const char *name;
     LaunchFn fn[2][2];    // [transA][transB], fp32 C (int32 C for int8, double C for fp64 inputs)
     LaunchFn fn16[2][2];  // [transA][transB], C in the inputs' 16-bit type (16-bit tables only)
+    Cost cost;            // zero unless the build's table is chosen by estimate
 };
 
 template <typename T, int BM, int BN, int BK, int WM, int WN, bool TA, bool TB, bool V, int D, typename CT>
@@ -55,11 +72,12 @@ hipError_t launch_gemm_f64(const KernelArgs &a, unsigned grid, hipStream_t s)
      {launch_gemm<T, BM, BN, BK, WM, WN, true, false, V, D, CT>,                             \
       launch_gemm<T, BM, BN, BK, WM, WN, true, true, V, D, CT>}}
 
-// fp32 inputs: fp32 C only
-#define MGEMM_VARIANT_F32_D(BM, BN, BK, WM, WN, V, D, NAME)                                  \
+// fp32 inputs: fp32 C only; COST: the build's Cost, {t0, tk, reg, solo} ({}: no estimate)
+#define MGEMM_VARIANT_F32_D(BM, BN, BK, WM, WN, V, D, NAME, ...)                              \
     {0, BM, BN, BK, WM, WN, V, D, NAME, MGEMM_LAUNCHERS(float, BM, BN, BK, WM, WN, V, D, float), \
-     {{nullptr, nullptr}, {nullptr, nullptr}}}
-#define MGEMM_VARIANT_F32(BM, BN, BK, WM, WN, V, NAME) MGEMM_VARIANT_F32_D(BM, BN, BK, WM, WN, V, 1, NAME)
+     {{nullptr, nullptr}, {nullptr, nullptr}}, __VA_ARGS__}
+#define MGEMM_VARIANT_F32(BM, BN, BK, WM, WN, V, NAME, ...) \
+    MGEMM_VARIANT_F32_D(BM, BN, BK, WM, WN, V, 1, NAME, __VA_ARGS__)
 
 // int8 inputs: int32 C, A K-contiguous (op N) and B K-contiguous (op T) only
 #define MGEMM_VARIANT_I8(BM, BN, BK, WM, WN, V, D, NAME)                                     \

@@ -146,6 +146,35 @@ def test_selection_for_the_named_workloads():
     assert info["dtype"] == 1 and g == 128 * (1024 // info["block_m"]) * (1024 // info["block_n"])
 
 
+def test_fp32_choice_by_estimated_time():
+    """fp32 builds carry a measured time model (rounds of 256 workgroups, a
+    register-path factor, a one-round factor); the lowest estimate wins."""
+    def name(M, N, K, **kw):
+        return sel(M=M, N=N, K=K, **kw)[0]["name"]
+    # whole rounds of the large tile stay there
+    assert name(4096, 4096, 4096) == "mgemm_f32_256x256x32_w4x2"
+    assert name(8192, 8192, 8192) == "mgemm_f32_256x256x32_w4x2"
+    # 324 tiles of 256x256 are two rounds, the second a quarter full (measured
+    # 2172 us against 1568 for 64x64); 576 of them are three (4392 against 3383)
+    assert name(4608, 4608, 4608) == "mgemm_f32_64x64x32_w2x2_d2"
+    assert name(6144, 6144, 6144) == "mgemm_f32_128x128x32_w2x2"
+    assert name(3072, 3072, 3072) == "mgemm_f32_64x64x32_w2x2_d2"
+    # aligned rows but K no multiple of the slab: every tile of the 16-byte
+    # builds would take the register path; the 4-byte-copy builds keep the DMA
+    assert name(3000, 3000, 3000).endswith("_d4_u")
+    assert name(1000, 1000, 1000) == "mgemm_f32_64x64x32_w2x2_d4_u"
+    assert name(1024, 1024, 1024) == "mgemm_f32_64x64x32_w2x2_d2"
+    # offsets past 32 bits: no 4-byte-copy build; aligned rows keep the
+    # 16-byte builds (their register path), unaligned ones the plain builds
+    big = 2_100_000
+    n = name(1024, 1024, 1000, lda=big, ldb=big)
+    assert n == "mgemm_f32_64x64x32_w2x2_d2"
+    n = name(1024, 1024, 1000, lda=big + 1, ldb=big + 1)
+    assert n.endswith("_u") and "_d4" not in n
+    # types without a time model keep the preference order
+    assert sel("bf16", M=8192, N=8192, K=8192)[0]["block_m"] == 256
+
+
 def test_int8_rules_without_a_gpu():
     lib = mg.load()
     ex = lib.gemm_strided_batched_ex
