@@ -35,8 +35,8 @@
 // layout.
 //
 // Each workgroup takes one of two paths (uniform branch):
-//   DmaPath  interior tiles of 16-byte aligned problems with K a multiple of
-//            the slab: global -> LDS by buffer_load ... lds, 4-stage ring;
+//   DmaPath  every tile of 16-byte aligned problems with K a multiple of 16
+//            bytes: global -> LDS by buffer_load ... lds, a ring of stages;
 //   RegPath  everything else: range-checked loads through registers,
 //            out-of-range elements read as zero, 2 LDS stages.
 #pragma once
@@ -590,8 +590,12 @@ struct RegPath {
 };
 
 // ===========================================================================
-// DmaPath: interior tiles.  Global -> LDS with buffer_load_dwordx4 ... lds
-// (no registers in between) into a ring of NS LDS stages of BK elements.
+// DmaPath: every tile of a 16-byte aligned problem whose K is a multiple of
+// the 16-byte chunk (CH elements).  Global -> LDS with buffer_load_dwordx4
+// ... lds (no registers in between) into a ring of NS LDS stages of BK
+// elements.  Chunks past K, and rows past the matrix, are masked to zero by
+// the buffer range check, so edge tiles and the slab past the last whole one
+// take the same copies.
 // Schedules (PIPE):
 //   1  BK = BKR/2 (32 for 16-bit, 16 for fp32), NS = 4, loads issued 3 slabs
 //      ahead; every wave reads and multiplies each slab, with one barrier per
@@ -636,6 +640,7 @@ struct DmaPath {
     static constexpr int RB = BK * ES;          // K-contiguous row bytes
     static_assert(RB == 64 || RB == 128, "64- or 128-byte K-contiguous rows");
     static constexpr int CPR = RB / 16;         // 16-byte chunks per row
+    static constexpr int CH = 16 / ES;          // elements per 16-byte chunk: K % CH == 0 on this path
     static constexpr int G = F32 ? BK / 8 : BK * ES / 32;  // k-groups (32 bytes of k) per slab
     static constexpr bool A_KC = !TA, B_KC = TB;
     static constexpr bool A_TR = TA && !F32, B_TR = !TB && !F32;
@@ -675,10 +680,18 @@ struct DmaPath {
     }
 
     // DMA instruction q (of IPW) of wave `w` for one operand's slab: 1 KB into
-    // the operand's region `dst` of a stage, from tile origin `src`.
+    // the operand's region `dst` of a stage, from tile origin `src`.  Memory
+    // tile rows < rows_ok and columns < cols_ok exist (rows k and columns m/n
+    // for an MC operand, rows m/n and columns k for a KC one).  A chunk of a
+    // row past rows_ok, or starting at or past cols_ok, gets an out-of-range
+    // offset: the copy writes zeros to its 16 LDS bytes and reads no memory.
+    // K is a multiple of CH, so no KC chunk straddles the end of K.  An MC
+    // chunk that straddles the m/n edge is read whole: it is 16-byte aligned
+    // and holds a valid element, so it lies inside a mapped page, and its
+    // values past the edge feed only rows or columns of C that are not stored.
     template <bool KC, int IL, int ROWB, int IPW>
     __device__ __forceinline__ static void dma_one(__amdgpu_buffer_rsrc_t rs, char *dst, int ld_bytes, int w,
-                                                   int lane, int q)
+                                                   int lane, int q, int rows_ok, int cols_ok)
     {
         const int ins = w * IPW + q;
         if constexpr (KC) {
@@ -689,8 +702,10 @@ struct DmaPath {
             const int pb = ins * RPI;
             const int j = lane / CPR;
             const int c = (lane % CPR) ^ swz(pb + j);
-            const int voff = j * IL * ld_bytes + (c << 4);
-            const int soff = __builtin_amdgcn_readfirstlane(logical_row<IL>(pb) * ld_bytes);
+            const int row0 = logical_row<IL>(pb);
+            int voff = j * IL * ld_bytes + (c << 4);
+            if (row0 + j * IL >= rows_ok || c * CH >= cols_ok) voff = kOutOfRange;
+            const int soff = __builtin_amdgcn_readfirstlane(row0 * ld_bytes);
             dma16(rs, lds_addr_of(dst + pb * RB), voff, soff);
         } else {
             // bytes b = ins*1024 + 16*lane of the [BK][MN] region: row k = b / ROWB,
@@ -698,7 +713,8 @@ struct DmaPath {
             const int b = ins * 1024 + 16 * lane;
             const int k = b / ROWB, bb = b % ROWB;
             const int lb = (((bb >> 6) ^ mc_key<ROWB>(k)) << 6) | (bb & 63);
-            dma16(rs, lds_addr_of(dst + ins * 1024), k * ld_bytes + lb, 0);
+            const int voff = (k >= rows_ok || lb >= cols_ok * ES) ? kOutOfRange : k * ld_bytes + lb;
+            dma16(rs, lds_addr_of(dst + ins * 1024), voff, 0);
         }
     }
 
@@ -869,10 +885,18 @@ struct DmaPath {
                     dma_dw<B_KC, IL_B, B_ROWB, B_IPW>(rb, st + A_BYTES, ldb_b, w, lane, q,
                                                       B_KC ? nrem : krem, B_KC ? krem : nrem);
             } else {
+                // every copy is checked (two compares and a select; a branch
+                // to unchecked copies for interior slabs cost the LDS address
+                // its scalar register)
+                const int krem = p.K - s * BK;
 #pragma unroll
-                for (int q = 0; q < A_IPW; ++q) dma_one<A_KC, IL_A, A_ROWB, A_IPW>(ra, st, lda_b, w, lane, q);
+                for (int q = 0; q < A_IPW; ++q)
+                    dma_one<A_KC, IL_A, A_ROWB, A_IPW>(ra, st, lda_b, w, lane, q, A_KC ? mrem : krem,
+                                                       A_KC ? krem : mrem);
 #pragma unroll
-                for (int q = 0; q < B_IPW; ++q) dma_one<B_KC, IL_B, B_ROWB, B_IPW>(rb, st + A_BYTES, ldb_b, w, lane, q);
+                for (int q = 0; q < B_IPW; ++q)
+                    dma_one<B_KC, IL_B, B_ROWB, B_IPW>(rb, st + A_BYTES, ldb_b, w, lane, q,
+                                                       B_KC ? nrem : krem, B_KC ? krem : nrem);
             }
         };
         auto frags = [&](int s, int g, Fr &f) {
@@ -880,7 +904,7 @@ struct DmaPath {
             load_frags(st, st + A_BYTES, g, L, f);
         };
 
-        const int nk = DW ? (p.K + BK - 1) / BK : p.K / BK;  // 4-byte copies zero-fill the last slab
+        const int nk = (p.K + BK - 1) / BK;  // a K tail is one more slab, zero-filled past K
         // prologue: slabs 0..NS-1 in flight, wait for slab 0
         issue(0);
 #pragma unroll
@@ -1153,10 +1177,12 @@ gemm_kernel(KernelArgs p)
             epilogue<true, D::IL_A, D::IL_B, TM, TN, WTM, WTN, WN, CT>(pk, bidx, m0, n0, acc);
     } else {
         if constexpr (VECOK) {
-            const bool interior = pk.fast_ok && m0 + BM <= pk.M && n0 + BN <= pk.N && pk.K % D::BK == 0;
-            if (interior) {
+            if (pk.fast_ok && pk.K % D::CH == 0) {
                 D::run(pk, smem, bidx, m0, n0, acc);
-                epilogue<false, D::IL_A, D::IL_B, TM, TN, WTM, WTN, WN, CT>(pk, bidx, m0, n0, acc);
+                if (m0 + BM <= pk.M && n0 + BN <= pk.N)
+                    epilogue<false, D::IL_A, D::IL_B, TM, TN, WTM, WTN, WN, CT>(pk, bidx, m0, n0, acc);
+                else
+                    epilogue<true, D::IL_A, D::IL_B, TM, TN, WTM, WTN, WN, CT>(pk, bidx, m0, n0, acc);
                 return;
             }
         }

@@ -180,16 +180,16 @@ mgemm_status validate_and_plan(int dtype, int c_dtype, int transA, int transB, i
         // Builds with a time estimate (Cost in variants.hpp): the lowest one.
         // Builds without 16-byte loads serve aligned operands too.  A build
         // with a DMA path and a register path pays the register factor when
-        // any tile takes the latter (the 4-byte-copy builds have no second
-        // path); a grid of one round pays the one-round factor.
+        // its tiles take the latter (K not a multiple of 16 bytes, or offsets
+        // past 32 bits; the 4-byte-copy builds have no second path); a grid
+        // of one round pays the one-round factor.
         double best_us = 0.0;
         for (int i = 0; i < t.n; ++i) {
             const Variant &v = t.v[i];
             if (v.cost.tk <= 0.0f || (v.vec && !vec_ok) || !offsets_ok(v)) continue;
             const int64_t rounds = (wgs_of(v) + 255) / 256;
-            const int64_t dma_slab = v.pipe == 1 ? v.bk / 2 : v.bk;
-            const bool reg_tiles = v.pipe != 4 && (!a.fast_ok || K % dma_slab != 0 || M % v.bm != 0 ||
-                                                   N % v.bn != 0);
+            // the 16-byte DMA path takes every tile when K is a multiple of 16 bytes
+            const bool reg_tiles = v.pipe != 4 && (!a.fast_ok || K % (16 / es) != 0);
             double us = (double)rounds * (v.cost.t0 + v.cost.tk * (double)K);
             if (reg_tiles) us *= v.cost.reg;
             if (rounds == 1) us *= v.cost.solo;

@@ -14,8 +14,8 @@ using LaunchFn = hipError_t (*)(const KernelArgs &, unsigned grid, hipStream_t);
 // Time model of one build, for the automatic choice: a CU runs its share of the
 // workgroups one after another, so a launch of W workgroups takes ceil(W/256)
 // "rounds" of t0 + tk*K microseconds on 256 CUs.  reg multiplies the round when
-// some tiles take the range-checked register path (edge tiles, a K that is no
-// multiple of the DMA slab, or offsets past 32 bits).  solo multiplies a
+// the tiles take the range-checked register path (a K that is no multiple of
+// 16 bytes, or offsets past 32 bits).  solo multiplies a
 // launch of one round: a CU holding a single workgroup cannot hide one
 // workgroup's load latency behind another's MFMAs.  Measured on MI355X by
 // forcing each build over square and oblong shapes from 512 to 8192 (t0, tk:

@@ -159,11 +159,15 @@ def test_fp32_choice_by_estimated_time():
     assert name(4608, 4608, 4608) == "mgemm_f32_64x64x32_w2x2_d2"
     assert name(6144, 6144, 6144) == "mgemm_f32_128x128x32_w2x2"
     assert name(3072, 3072, 3072) == "mgemm_f32_64x64x32_w2x2_d2"
-    # aligned rows but K no multiple of the slab: every tile of the 16-byte
-    # builds would take the register path; the 4-byte-copy builds keep the DMA
-    assert name(3000, 3000, 3000).endswith("_d4_u")
-    assert name(1000, 1000, 1000) == "mgemm_f32_64x64x32_w2x2_d4_u"
+    # aligned rows, K a multiple of 16 bytes: the 16-byte builds copy every
+    # tile by DMA, edges and K tails included
+    assert name(3000, 3000, 3000) == "mgemm_f32_64x64x32_w2x2_d2"
+    assert name(1000, 1000, 1000) == "mgemm_f32_64x64x32_w2x2_d2"
     assert name(1024, 1024, 1024) == "mgemm_f32_64x64x32_w2x2_d2"
+    # aligned rows but K no multiple of 4: the 16-byte builds would take the
+    # register path for every tile; the 4-byte-copy builds keep the DMA
+    assert name(1000, 1000, 1001, lda=1004) == "mgemm_f32_64x64x32_w2x2_d4_u"
+    assert name(3000, 3000, 3001, lda=3004).endswith("_d4_u")
     # offsets past 32 bits: no 4-byte-copy build; aligned rows keep the
     # 16-byte builds (their register path), unaligned ones the plain builds
     big = 2_100_000

@@ -150,6 +150,42 @@ def test_dma_path_short_k(dtype):
             full_check(base, exact=True, what=f"{v['name']} K={K}")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "i8"])
+def test_dma_path_k_tails(dtype):
+    # K a multiple of the 16-byte chunk but not of the slab: interior tiles
+    # stay on the LDS-DMA path and copy one more slab whose chunks past K are
+    # masked to zero.  NaN fills the row padding past K, so a chunk read
+    # past K would show; a K shorter than one slab, and a tail after several.
+    es = {"f32": 4, "f16": 2, "bf16": 2, "i8": 1}[dtype]
+    ch = 16 // es
+    for v in variants_of(dtype):
+        if v["name"].endswith("_u"):
+            continue
+        mg.force_variant(dtype, v["id"])
+        bm, bn = v["block_m"], v["block_n"]
+        slab = v["block_k"] // 2 if v["pipe"] == 1 else v["block_k"]
+        combos = [(False, True)] if dtype == "i8" else list(itertools.product((False, True), repeat=2))
+        M, N = 2 * bm + 17, 2 * bn + 9
+        pad = 16 if dtype == "i8" else 8
+        padded = lambda cols: -(-cols // pad) * pad + pad   # 16-byte rows, padding after
+        for K in (ch, 3 * slab + slab - ch, slab + slab // 2 + ch):
+            for tA, tB in combos:
+                kw = dict(c_dtype="i32", int_lo=-100, int_hi=100, pad_value=77) if dtype == "i8" else \
+                    dict(int_lo=-8, int_hi=8, pad_value=float("nan"))
+                p = wl.Problem(dtype, M, N, K, transA=tA, transB=tB, lda=padded(M if tA else K),
+                               ldb=padded(K if tB else N), alpha=1.0, beta=-1.0, dist="int",
+                               c_dist="int", seed=90 + K % 7, **kw)
+                _assert_selected(p, v)
+                full_check(p, exact=True, what=f"{v['name']} K={K} tA={tA} tB={tB}")
+        if dtype in ("f32", "bf16"):
+            K = 2 * slab + ch
+            p = wl.Problem(dtype, M, N, K, alpha=1.5, beta=0.5, lda=padded(K), ldb=padded(N),
+                           dist="uniform" if dtype == "f32" else "normal", c_dist="uniform",
+                           pad_value=float("nan"), seed=97)
+            _assert_selected(p, v)
+            full_check(p, what=f"{v['name']} float K tail")
+
+
 def test_four_byte_copy_variants():
     # fp32 builds whose every tile copies 4-byte elements into LDS, with
     # out-of-matrix lanes masked to zero: odd leading dimensions with NaN in
