@@ -56,6 +56,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef u32x4 u32x4_a4 __attribute__((aligned(4)));  // 16 bytes at a 4-byte aligned address
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
 
@@ -288,23 +289,24 @@ __device__ __forceinline__ int kc128_off(int p, int kbyte)
 }
 
 // One operand (A or B) of one K-slab: global -> registers -> LDS.
-//   ES    element size (4: fp32, 2: f16/bf16)
+//   ES    element size (4: fp32, 2: f16/bf16, 1: int8)
 //   MN    tile extent along M (for A) or N (for B)
 //   KROW  memory rows run along k (A^T or B), i.e. MN is the contiguous dim
 //   IL    the operand's sub-tile interleave
+//   VECOK 16-byte aligned rows; otherwise every 16-byte vector is assembled
+//         from the aligned dwords around it (realigned_vec)
 // Modes:
 //   vector   (!KROW, or fp32): memory vectors copied as is; LDS rows are
 //            K-contiguous (!KROW) or the fp32 [BK][MN] layout (KROW).
-//   block    (16-bit KROW, aligned): KB x 8 blocks transposed in registers
-//            so LDS rows stay K-contiguous (the MFMA wants 8 k per lane).
-//   scalar   (16-bit KROW, unaligned): element by element.
+//   block    (8/16-bit KROW): KB x 8 blocks transposed in registers so LDS
+//            rows stay K-contiguous (the MFMA wants 8 k per lane).
 template <int ES, int NT, int MN, int BK, int IL, bool KROW, bool VECOK>
 struct RegOperand {
     static constexpr bool F32 = ES == 4;
     static constexpr int ROWB = BK * ES;
     static_assert(ROWB == 128, "K-contiguous rows are 128 bytes");
-    static constexpr bool BLOCK = KROW && !F32 && VECOK;
-    static constexpr int VEC = VECOK ? 16 / ES : 1;
+    static constexpr bool BLOCK = KROW && !F32;
+    static constexpr int VEC = 16 / ES;
     static constexpr int R = KROW ? BK : MN;   // memory rows of the tile
     static constexpr int CC = KROW ? MN : BK;  // contiguous elements per memory row
     static constexpr int VPR = CC / VEC;
@@ -336,24 +338,63 @@ struct RegOperand {
 #pragma unroll
                 for (int r = 0; r < KB; ++r) {
                     const int row = bkg(tid) * KB + r, col = bng(tid, q) * 8;
-                    regs[q * KB + r] = masked_vec(base + ((int64_t)row * ld + col) * ES,
-                                                  row < rlim ? clim - col : 0);
+                    regs[q * KB + r] = load_vec(base + ((int64_t)row * ld + col) * ES,
+                                                row < rlim ? clim - col : 0);
                 }
         } else {
 #pragma unroll
             for (int q = 0; q < NPT; ++q) {
                 const int r = mem_row(vrow(tid, q)), c = vcol(tid, q);
-                const char *ptr = base + ((int64_t)r * ld + c) * ES;
-                if constexpr (VEC == 1) {
-                    if (r < rlim && c < clim)
-                        regs[q] = *reinterpret_cast<const Raw *>(ptr);
-                    else
-                        regs[q] = 0;
-                } else {
-                    regs[q] = masked_vec(ptr, r < rlim ? clim - c : 0);
-                }
+                regs[q] = load_vec(base + ((int64_t)r * ld + c) * ES, r < rlim ? clim - c : 0);
             }
         }
+    }
+
+    __device__ __forceinline__ static u32x4 load_vec(const char *ptr, int n)
+    {
+        if constexpr (VECOK) return masked_vec(ptr, n);
+        else                 return realigned_vec(ptr, n);
+    }
+
+    // masked_vec for an address aligned only to the element size (rows of
+    // any length).  The 4-byte aligned dwords that hold in-range bytes are
+    // loaded -- four as one 16-byte load, a fifth when the address is not
+    // 4-byte aligned -- and shifted into place with v_alignbyte.  A dword
+    // holding an in-range byte lies in that byte's page, so no load can
+    // fault; bytes past the n elements are cleared.
+    __device__ __forceinline__ static u32x4 realigned_vec(const char *ptr, int n)
+    {
+        constexpr int V = 16 / ES;
+        if (n <= 0) return u32x4{0, 0, 0, 0};
+        const uintptr_t addr = reinterpret_cast<uintptr_t>(ptr);
+        const int o = ES == 4 ? 0 : (int)(addr & 3);
+        const uint32_t *p0 = reinterpret_cast<const uint32_t *>(addr - (uintptr_t)o);
+        const int nb = (n < V ? n : V) * ES;  // in-range bytes from ptr
+        const int end = o + nb;               // in-range bytes end here, from p0
+        u32x4 lo = {0, 0, 0, 0};
+        uint32_t hi = 0;
+        if (end > 12) {
+            lo = *reinterpret_cast<const u32x4_a4 *>(p0);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 3; ++j)
+                if (4 * j < end) lo[j] = p0[j];
+        }
+        if (end > 16) hi = p0[4];
+        u32x4 v;
+        v[0] = __builtin_amdgcn_alignbyte(lo[1], lo[0], o);
+        v[1] = __builtin_amdgcn_alignbyte(lo[2], lo[1], o);
+        v[2] = __builtin_amdgcn_alignbyte(lo[3], lo[2], o);
+        v[3] = __builtin_amdgcn_alignbyte(hi, lo[3], o);
+        if (nb < 16) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int keep = nb - 4 * i;  // in-range bytes of dword i
+                if (keep <= 0) v[i] = 0;
+                else if (keep < 4) v[i] &= (1u << (8 * keep)) - 1u;
+            }
+        }
+        return v;
     }
 
     // A 16-byte vector of which only the first `n` elements are in range.
@@ -413,10 +454,8 @@ struct RegOperand {
                 const int r = vrow(tid, q), c = vcol(tid, q);
                 if constexpr (!KROW) {          // memory row = mn, contiguous = k; r is physical
                     *reinterpret_cast<Raw *>(s + kc128_off(r, c * ES)) = regs[q];
-                } else if constexpr (F32) {     // memory row = k, contiguous = mn -> [BK][MN]
+                } else {                        // fp32, memory row = k, contiguous = mn -> [BK][MN]
                     *reinterpret_cast<Raw *>(s + (r * MN + c) * 4) = regs[q];
-                } else {                        // 16-bit, unaligned: one element
-                    *reinterpret_cast<uint16_t *>(s + kc128_off(phys_row<IL>(c), r * 2)) = regs[q];
                 }
             }
         }
@@ -441,11 +480,9 @@ struct RegPath {
     static constexpr int IL_A = TM, IL_B = TN;  // C mapping: interleaved rows and columns
     // 64x64 tiles keep two register sets in flight: a grid of them is often
     // about one workgroup per CU, with little else to hide the load latency
-    // behind.  Larger tiles keep one, and so do the element-wise 8/16-bit
-    // builds: a second set would cost them occupancy (128x128 unaligned fp32
-    // would go from 244 to 308 registers, 64x64 unaligned 16-bit past 256:
-    // one wave per SIMD instead of two).
-    static constexpr bool REG2 = BM * BN <= 64 * 64 && (F32 || VECOK);
+    // behind.  Larger tiles keep one: a second set would cost them occupancy
+    // (128x128 unaligned fp32 would go from 244 to 308 registers).
+    static constexpr bool REG2 = BM * BN <= 64 * 64;
 
     using OpA = RegOperand<ES, NT, BM, BK, TM, TA, VECOK>;
     using OpB = RegOperand<ES, NT, BN, BK, TN, !TB, VECOK>;
@@ -602,11 +639,12 @@ struct RegPath {
 //      slab placed before the MFMAs of its last k-group so that the next
 //      slab's first fragment reads overlap them.
 //   2  the same with BK = BKR, NS = 2 (one slab ahead, half the barriers).
-//   4  fp32 with 4-byte copies, BK = BKR, NS = 2, for every tile of any
-//      4-byte aligned problem: each lane copies one element, and lanes whose
-//      element lies past the matrix (row, column or k) are masked to zero by
-//      the buffer range check, so edges and odd leading dimensions need no
-//      register path.
+//   4  4-byte copies, BK = BKR, NS = 2, for every tile of a problem whose
+//      rows are 4-byte aligned (and, for 8/16-bit elements, whose K is a
+//      multiple of the 4-byte piece): each lane copies one piece, and lanes
+//      whose piece lies past the matrix (row, column or k) are masked to
+//      zero by the buffer range check, so edges and leading dimensions that
+//      are no multiple of 16 bytes need no register path.
 //
 // LDS layouts (bank-conflict free for every access of this path):
 //   KC  operand K-contiguous in memory: rows of BK elements (RB = 64 or 128
@@ -633,8 +671,7 @@ struct DmaPath {
     static constexpr bool F32 = (ES == 4);
     static constexpr int WTM = BM / WM, WTN = BN / WN;
     static constexpr int TM = WTM / 32, TN = WTN / 32;
-    static constexpr bool DW = PIPE == 4;  // 4-byte copies, every tile (fp32)
-    static_assert(!DW || sizeof(T) == 4, "4-byte copies are for fp32");
+    static constexpr bool DW = PIPE == 4;  // 4-byte copies, every tile
     static constexpr int BK = PIPE == 2 || DW ? BKR : BKR / 2;
     static constexpr int NS = PIPE == 1 ? 4 : 2;
     static constexpr int RB = BK * ES;          // K-contiguous row bytes
@@ -720,26 +757,30 @@ struct DmaPath {
 
     // 4-byte copy instruction q (of IPW) of wave `w`: 256 bytes of the
     // operand's region `dst`, laid out exactly as dma_one lays them (KC rows
-    // with swizzled chunks, or MC rows with permuted pieces).  Memory tile
-    // rows < rows_ok and columns < cols_ok exist; any other element reads as
-    // zero through an out-of-range offset.
+    // with swizzled chunks, or MC rows with permuted pieces).  Each lane
+    // copies one 4-byte piece (1, 2 or 4 elements) of 4-byte aligned rows.
+    // Memory tile rows < rows_ok and columns < cols_ok exist; a piece in a
+    // row past rows_ok, or starting at or past cols_ok, reads as zero through
+    // an out-of-range offset.  For KC operands K is a multiple of the piece;
+    // an MC piece that straddles the m/n edge is read whole (it lies in the
+    // page of its first element and feeds only C elements that are not stored).
     template <bool KC, int IL, int ROWB, int IPW>
     __device__ __forceinline__ static void dma_dw(__amdgpu_buffer_rsrc_t rs, char *dst, int ld_bytes, int w,
                                                   int lane, int q, int rows_ok, int cols_ok)
     {
         const int ins = w * IPW + q;
         const int b = ins * 256 + 4 * lane;  // byte of the operand's LDS region
-        int r, c;                            // memory row and column (elements) of the tile
+        int r, cb;                           // memory row and byte column of the tile
         if constexpr (KC) {
             const int pr = b / RB, within = b % RB;   // physical row, byte within it
             r = logical_row<IL>(pr);
-            c = ((((within >> 4) ^ swz(pr)) << 4) | (within & 15)) >> 2;
+            cb = (((within >> 4) ^ swz(pr)) << 4) | (within & 15);
         } else {
             const int k = b / ROWB, bb = b % ROWB;
             r = k;
-            c = ((((bb >> 6) ^ mc_key<ROWB>(k)) << 6) | (bb & 63)) >> 2;
+            cb = (((bb >> 6) ^ mc_key<ROWB>(k)) << 6) | (bb & 63);
         }
-        const int voff = (r < rows_ok && c < cols_ok) ? r * ld_bytes + 4 * c : kOutOfRange;
+        const int voff = (r < rows_ok && cb < cols_ok * ES) ? r * ld_bytes + cb : kOutOfRange;
         dma4(rs, lds_addr_of(dst + ins * 256), voff);
     }
 

@@ -14,8 +14,11 @@ const Variant *f16_variants(int *count)
         MGEMM_VARIANT(_Float16, 1, 256, 256, 64, 2, 2, true, "mgemm_f16_256x256x64_w2x2"),
         MGEMM_VARIANT_D(_Float16, 1, 256, 256, 64, 2, 2, true, 2, "mgemm_f16_256x256x64_w2x2_d2"),
         MGEMM_VARIANT(_Float16, 1, 128, 128, 64, 2, 2, true, "mgemm_f16_128x128x64_w2x2"),
+        // rows 4-byte aligned (and K even): 4-byte copies into LDS, every tile
+        MGEMM_VARIANT_D(_Float16, 1, 128, 128, 64, 2, 2, false, 4, "mgemm_f16_128x128x64_w2x2_d4_u"),
         MGEMM_VARIANT(_Float16, 1, 128, 128, 64, 2, 2, false, "mgemm_f16_128x128x64_w2x2_u"),
         MGEMM_VARIANT(_Float16, 1, 64, 64, 64, 2, 2, true, "mgemm_f16_64x64x64_w2x2"),
+        MGEMM_VARIANT_D(_Float16, 1, 64, 64, 64, 2, 2, false, 4, "mgemm_f16_64x64x64_w2x2_d4_u"),
         MGEMM_VARIANT(_Float16, 1, 64, 64, 64, 2, 2, false, "mgemm_f16_64x64x64_w2x2_u"),
     };
     *count = sizeof(table) / sizeof(table[0]);

@@ -78,15 +78,17 @@ bool aligned(const void *p, int64_t bytes) { return (reinterpret_cast<uintptr_t>
 // Smallest element span one stored matrix occupies: (rows-1)*ld + cols.
 int64_t span(int64_t rows, int64_t cols, int64_t ld) { return rows == 0 || cols == 0 ? 0 : (rows - 1) * ld + cols; }
 
-// k_chunks: the batch entries are K-chunks of one operand pair (split-K's
-// partial products), so strideA/strideB step along K inside one matrix and
-// are not required to cover a whole matrix.
+// k_total >= 0: the batch entries are K-chunks of one operand pair of depth
+// k_total (split-K's partial products), so strideA/strideB step along K
+// inside one matrix and are not required to cover a whole matrix; the last
+// chunk is shorter than K.
 mgemm_status validate_and_plan(int dtype, int c_dtype, int transA, int transB, int64_t M, int64_t N,
                                int64_t K, double alpha, const void *A, int64_t lda, int64_t strideA,
                                const void *B, int64_t ldb, int64_t strideB, double beta,
                                const void *C, int64_t ldc, int64_t strideC, int64_t batch,
-                               Plan *plan, bool k_chunks = false)
+                               Plan *plan, int64_t k_total = -1)
 {
+    const bool k_chunks = k_total >= 0;
     if (!is_input_type(dtype)) return MGEMM_INVALID_ARG;
     if (dtype == MGEMM_F64) {
         if (c_dtype != MGEMM_F64) return MGEMM_INVALID_ARG;  // double C only
@@ -163,8 +165,14 @@ mgemm_status validate_and_plan(int dtype, int c_dtype, int transA, int transB, i
     const bool vec_ok = aligned(A, 16) && aligned(B, 16) && lda % vec == 0 && ldb % vec == 0 &&
                         strideA % vec == 0 && strideB % vec == 0;
 
-    // builds with 4-byte copies (pipe 4) address their tiles with 32-bit offsets too
-    auto offsets_ok = [&](const Variant &v) { return v.pipe != 4 || a.fast_ok; };
+    // Builds with 4-byte copies (pipe 4) address their tiles with 32-bit
+    // offsets too, and copy 4-byte pieces: 8/16-bit operands need 4-byte
+    // aligned rows and a K (every chunk's, under split-K) that is a multiple
+    // of the piece.
+    const int64_t piece = es >= 4 ? 1 : 4 / es, k_all = k_chunks ? k_total : K;
+    const bool dw_rows = es >= 4 || (aligned(A, 4) && aligned(B, 4) && lda % piece == 0 && ldb % piece == 0 &&
+                                     strideA % piece == 0 && strideB % piece == 0 && k_all % piece == 0);
+    auto offsets_ok = [&](const Variant &v) { return v.pipe != 4 || (a.fast_ok && dw_rows); };
     Table t = table_for(dtype);
     const int forced = g_forced[dtype].load();
     int pick = -1;
@@ -291,7 +299,7 @@ mgemm_status plan_chunks(int dtype, int transA, int transB, int64_t M, int64_t N
     const int64_t sA = transA ? ks * lda : ks;  // chunk z starts at column (or row) z*ks
     const int64_t sB = transB ? ks : ks * ldb;
     mgemm_status st = validate_and_plan(dtype, partial_dtype(dtype), transA, transB, M, N, ks, 1.0, A,
-                                        lda, sA, B, ldb, sB, 0.0, W, N, M * N, used, part, true);
+                                        lda, sA, B, ldb, sB, 0.0, W, N, M * N, used, part, K);
     if (st != MGEMM_OK) return st;
     if (part->kind != Plan::GEMM) return MGEMM_INVALID_ARG;
     part->args.k_tail = (int)(K - (used - 1) * ks);

@@ -72,6 +72,24 @@ def _round8(x):
     return (x + 7) // 8 * 8
 
 
+ES = {"f32": 4, "f16": 2, "bf16": 2, "i8": 1, "f64": 8}
+
+
+def _narrow_dw(v, dtype):
+    """An 8/16-bit build with 4-byte copies: rows 4-byte aligned, K a multiple of the piece."""
+    return v["pipe"] == 4 and ES[dtype] < 4
+
+
+def _ld_unaligned(v, dtype, cols):
+    """A leading dimension with no 16-byte rows that the unaligned build v accepts: odd,
+    or (8/16-bit 4-byte-copy builds) a multiple of the 4-byte piece."""
+    if _narrow_dw(v, dtype):
+        piece = 4 // ES[dtype]
+        ld = -(-cols // piece) * piece
+        return ld + piece if (ld * ES[dtype]) % 16 == 0 else ld
+    return cols + 1
+
+
 def _assert_selected(p, v):
     # a forced aligned-only variant falls back to the automatic choice on unaligned
     # operands: make sure the case really runs the variant it is meant to cover
@@ -91,6 +109,8 @@ def variants_of(dtype):
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 def test_every_variant_every_transpose_ragged(dtype):
     for v in variants_of(dtype):
+        if _narrow_dw(v, dtype):
+            continue    # needs an even K: test_four_byte_copy_variants covers it
         mg.force_variant(dtype, v["id"])
         bm, bn, bk = v["block_m"], v["block_n"], v["block_k"]
         M, N, K = 2 * bm + 17, 2 * bn + 9, 3 * bk + 5
@@ -186,30 +206,42 @@ def test_dma_path_k_tails(dtype):
             full_check(p, what=f"{v['name']} float K tail")
 
 
-def test_four_byte_copy_variants():
-    # fp32 builds whose every tile copies 4-byte elements into LDS, with
-    # out-of-matrix lanes masked to zero: odd leading dimensions with NaN in
-    # the padding, K tails of every length mod the slab, slab counts through
-    # the steady state, every transpose, a batch with a shared operand
-    for v in variants_of("f32"):
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "i8"])
+def test_four_byte_copy_variants(dtype):
+    # builds whose every tile copies 4-byte pieces into LDS (1 fp32, 2 16-bit
+    # or 4 int8 elements), with out-of-matrix lanes masked to zero: leading
+    # dimensions with no 16-byte rows and filler in the padding, K tails of
+    # every length mod the slab (whole pieces), slab counts through the steady
+    # state, every transpose, a batch with a shared operand
+    es = ES[dtype]
+    piece = 4 // es
+    up = lambda x: -(-x // piece) * piece
+    i8 = dtype == "i8"
+    for v in variants_of(dtype):
         if v["pipe"] != 4:
             continue
-        mg.force_variant("f32", v["id"])
+        mg.force_variant(dtype, v["id"])
         bm, bn, bk = v["block_m"], v["block_n"], v["block_k"]
         for i, K in enumerate((1, bk - 1, bk, bk + 1, 3 * bk + 17, 9 * bk + 5)):
-            tA, tB = bool(i & 1), bool(i & 2)
+            K = up(K)
+            tA, tB = (False, True) if i8 else (bool(i & 1), bool(i & 2))
             M, N = bm + 3 + i, 2 * bn - 7
-            p = wl.Problem("f32", M, N, K, transA=tA, transB=tB, alpha=1.5, beta=0.5,
-                           lda=(M if tA else K) + 1, ldb=(K if tB else N) + 3, ldc=N + 1,
-                           dist="int", int_lo=-20, int_hi=20, c_dist="int", seed=70 + i,
-                           pad_value=float("nan"))
+            kw = dict(c_dtype="i32", alpha=2.0, beta=-1.0, int_lo=-100, int_hi=100, pad_value=77) if i8 \
+                else dict(alpha=1.5, beta=0.5, int_lo=-20, int_hi=20, pad_value=float("nan"))
+            p = wl.Problem(dtype, M, N, K, transA=tA, transB=tB,
+                           lda=_ld_unaligned(v, dtype, M if tA else K),
+                           ldb=_ld_unaligned(v, dtype, K if tB else N), ldc=N + 1,
+                           dist="int", c_dist="int", seed=70 + i, **kw)
             _assert_selected(p, v)
             full_check(p, exact=True, what=f"{v['name']} K={K} tA={int(tA)} tB={int(tB)}")
-        q = wl.Problem("f32", bm + 5, bn + 9, 2 * bk + 3, transB=True, batch=3, strideB=0,
-                       lda=2 * bk + 4, ldb=2 * bk + 5, dist="uniform", seed=77)
+        K = up(2 * bk + 3)
+        q = wl.Problem(dtype, bm + 5, bn + 9, K, transB=True, batch=3, strideB=0,
+                       lda=_ld_unaligned(v, dtype, K), ldb=_ld_unaligned(v, dtype, K + 1),
+                       dist="int" if i8 else "uniform", int_lo=-100, int_hi=100,
+                       c_dtype="i32" if i8 else "f32", seed=77)
         q.force_batched = True
         _assert_selected(q, v)
-        full_check(q, what=f"{v['name']} batched, B shared")
+        full_check(q, exact=i8, what=f"{v['name']} batched, B shared")
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -303,8 +335,8 @@ def test_c16_every_variant_every_transpose(dtype):
             a_cols = M if tA else K
             b_cols = K if tB else N
             base = wl.Problem(dtype, M, N, K, transA=tA, transB=tB, c_dtype=dtype,
-                              lda=_round8(a_cols) if aligned else a_cols + 1,
-                              ldb=_round8(b_cols) if aligned else b_cols + 1,
+                              lda=_round8(a_cols) if aligned else _ld_unaligned(v, dtype, a_cols),
+                              ldb=_round8(b_cols) if aligned else _ld_unaligned(v, dtype, b_cols),
                               alpha=1.5, beta=0.5, dist="normal", c_dist="uniform", seed=51)
             _assert_selected(base, v)
             full_check(base, what=f"{v['name']} -> {dtype} C, float")
@@ -341,10 +373,12 @@ def test_i8_every_variant():
         aligned = not v["name"].endswith("_u")
         bm, bn, bk = v["block_m"], v["block_n"], v["block_k"]
         for (M, N, K) in ((2 * bm + 17, 2 * bn + 9, 4 * bk), (bm + 3, bn + 40, 3 * bk + 29)):
+            if _narrow_dw(v, "i8"):
+                K -= K % 4      # 4-byte pieces of k
             for alpha, beta in ((1.0, 0.0), (-3.0, 2.0)):
                 p = wl.Problem("i8", M, N, K, transB=True, c_dtype="i32", alpha=alpha, beta=beta,
-                               lda=(K + 16 - K % 16 if aligned else K + 1),
-                               ldb=(K + 16 - K % 16 if aligned else K + 3),
+                               lda=(K + 16 - K % 16 if aligned else _ld_unaligned(v, "i8", K)),
+                               ldb=(K + 16 - K % 16 if aligned else _ld_unaligned(v, "i8", K + 2)),
                                dist="int", int_lo=-128, int_hi=127, c_dist="int", seed=71,
                                pad_value=77)
                 _assert_selected(p, v)
