@@ -184,6 +184,17 @@ mgemm_status validate_and_plan(int dtype, int c_dtype, int transA, int transB, i
     auto wgs_of = [&](const Variant &v) {
         return ((M + v.bm - 1) / v.bm) * ((N + v.bn - 1) / v.bn) * batch;
     };
+    auto eligible = [&](const Variant &v) { return v.vec == vec_ok && offsets_ok(v); };
+    if (pick < 0 && (dtype == MGEMM_F16 || dtype == MGEMM_BF16) && K <= 128) {
+        // A shallow K (the whole product is a couple of slabs, e.g. attention
+        // scores with a 64-wide head) is bound by the C store rather than the
+        // matrix cores: there the 256x256 tile with 4x2 wavefronts measured
+        // best while it still gives one workgroup per CU.
+        for (int i = 0; i < t.n && pick < 0; ++i)
+            if (eligible(t.v[i]) && t.v[i].bm == 256 && t.v[i].bn == 256 && t.v[i].wm == 4 &&
+                wgs_of(t.v[i]) >= 256)
+                pick = i;
+    }
     if (pick < 0) {
         // Builds with a time estimate (Cost in variants.hpp): the lowest one.
         // Builds without 16-byte loads serve aligned operands too.  A build
@@ -208,23 +219,12 @@ mgemm_status validate_and_plan(int dtype, int c_dtype, int transA, int transB, i
         }
     }
     if (pick < 0) {
-        // Types without estimates: the table is in order of preference
-        // (measured on the large square problems): take the first variant
-        // that still gives at least one workgroup per CU (256 CUs); if none
-        // does, the smallest tile, to spread a small problem over more CUs.
-        // A shallow K (the whole product is a couple of slabs, e.g. attention
-        // scores with a 64-wide head) is bound by the C store rather than the
-        // matrix cores: there the 256x256 tile with 4x2 wavefronts measured
-        // best, so it moves to the front.
+        // No estimated build fits (unaligned rows, or offsets past 32 bits):
+        // the table is in order of preference; take the first variant that
+        // still gives at least one workgroup per CU (256 CUs); if none does,
+        // the smallest tile, to spread a small problem over more CUs.
         const int64_t min_wgs = 256;
         int best = -1, smallest = -1;
-        auto eligible = [&](const Variant &v) { return v.vec == vec_ok && offsets_ok(v); };
-        if (dtype != MGEMM_F32 && K <= 128) {
-            for (int i = 0; i < t.n && best < 0; ++i)
-                if (eligible(t.v[i]) && t.v[i].bm == 256 && t.v[i].bn == 256 && t.v[i].wm == 4 &&
-                    wgs_of(t.v[i]) >= min_wgs)
-                    best = i;
-        }
         for (int i = 0; i < t.n; ++i) {
             const Variant &v = t.v[i];
             if (!eligible(v)) continue;

@@ -36,7 +36,7 @@ struct Variant {
     const char *name;
     LaunchFn fn[2][2];    // [transA][transB], fp32 C (int32 C for int8, double C for fp64 inputs)
     LaunchFn fn16[2][2];  // [transA][transB], C in the inputs' 16-bit type (16-bit tables only)
-    Cost cost;            // zero unless the build's table is chosen by estimate
+    Cost cost;            // zero: no estimate
 };
 
 template <typename T, int BM, int BN, int BK, int WM, int WN, bool TA, bool TB, bool V, int D, typename CT>
@@ -58,13 +58,13 @@ hipError_t launch_gemm_f64(const KernelArgs &a, unsigned grid, hipStream_t s)
 }
 
 // fp64 inputs: double C
-#define MGEMM_VARIANT_F64(BM, BN, BK, WM, WN, V, NAME)                                       \
+#define MGEMM_VARIANT_F64(BM, BN, BK, WM, WN, V, NAME, ...)                                  \
     {5, BM, BN, BK, WM, WN, V, 1, NAME,                                                      \
      {{launch_gemm_f64<BM, BN, BK, WM, WN, false, false, V>,                                \
        launch_gemm_f64<BM, BN, BK, WM, WN, false, true, V>},                                \
       {launch_gemm_f64<BM, BN, BK, WM, WN, true, false, V>,                                 \
        launch_gemm_f64<BM, BN, BK, WM, WN, true, true, V>}},                                \
-     {{nullptr, nullptr}, {nullptr, nullptr}}}
+     {{nullptr, nullptr}, {nullptr, nullptr}}, __VA_ARGS__}
 
 #define MGEMM_LAUNCHERS(T, BM, BN, BK, WM, WN, V, D, CT)                                     \
     {{launch_gemm<T, BM, BN, BK, WM, WN, false, false, V, D, CT>,                            \
@@ -72,7 +72,9 @@ hipError_t launch_gemm_f64(const KernelArgs &a, unsigned grid, hipStream_t s)
      {launch_gemm<T, BM, BN, BK, WM, WN, true, false, V, D, CT>,                             \
       launch_gemm<T, BM, BN, BK, WM, WN, true, true, V, D, CT>}}
 
-// fp32 inputs: fp32 C only; COST: the build's Cost, {t0, tk, reg, solo} ({}: no estimate)
+// The trailing argument of each macro is the build's Cost, {t0, tk, reg, solo}
+// ({}: no estimate).
+// fp32 inputs: fp32 C only
 #define MGEMM_VARIANT_F32_D(BM, BN, BK, WM, WN, V, D, NAME, ...)                              \
     {0, BM, BN, BK, WM, WN, V, D, NAME, MGEMM_LAUNCHERS(float, BM, BN, BK, WM, WN, V, D, float), \
      {{nullptr, nullptr}, {nullptr, nullptr}}, __VA_ARGS__}
@@ -80,18 +82,19 @@ hipError_t launch_gemm_f64(const KernelArgs &a, unsigned grid, hipStream_t s)
     MGEMM_VARIANT_F32_D(BM, BN, BK, WM, WN, V, 1, NAME, __VA_ARGS__)
 
 // int8 inputs: int32 C, A K-contiguous (op N) and B K-contiguous (op T) only
-#define MGEMM_VARIANT_I8(BM, BN, BK, WM, WN, V, D, NAME)                                     \
+#define MGEMM_VARIANT_I8(BM, BN, BK, WM, WN, V, D, NAME, ...)                                \
     {3, BM, BN, BK, WM, WN, V, D, NAME,                                                      \
      {{nullptr, launch_gemm<int8_t, BM, BN, BK, WM, WN, false, true, V, D, int32_t>},         \
       {nullptr, nullptr}},                                                                   \
-     {{nullptr, nullptr}, {nullptr, nullptr}}}
+     {{nullptr, nullptr}, {nullptr, nullptr}}, __VA_ARGS__}
 
 // 16-bit inputs: fp32 C or C of the input type
-#define MGEMM_VARIANT_D(T, DT, BM, BN, BK, WM, WN, V, D, NAME)                               \
+#define MGEMM_VARIANT_D(T, DT, BM, BN, BK, WM, WN, V, D, NAME, ...)                          \
     {DT, BM, BN, BK, WM, WN, V, D, NAME, MGEMM_LAUNCHERS(T, BM, BN, BK, WM, WN, V, D, float), \
-     MGEMM_LAUNCHERS(T, BM, BN, BK, WM, WN, V, D, T)}
+     MGEMM_LAUNCHERS(T, BM, BN, BK, WM, WN, V, D, T), __VA_ARGS__}
 
-#define MGEMM_VARIANT(T, DT, BM, BN, BK, WM, WN, V, NAME) MGEMM_VARIANT_D(T, DT, BM, BN, BK, WM, WN, V, 1, NAME)
+#define MGEMM_VARIANT(T, DT, BM, BN, BK, WM, WN, V, NAME, ...) \
+    MGEMM_VARIANT_D(T, DT, BM, BN, BK, WM, WN, V, 1, NAME, __VA_ARGS__)
 
 // Host-side variant tables, one per input type (function-local statics, so
 // that the device compilation never sees the host launch pointers).

@@ -175,8 +175,32 @@ def test_fp32_choice_by_estimated_time():
     assert n == "mgemm_f32_64x64x32_w2x2_d2"
     n = name(1024, 1024, 1000, lda=big + 1, ldb=big + 1)
     assert n.endswith("_u") and "_d4" not in n
-    # types without a time model keep the preference order
+    # the 16-bit, int8 and fp64 tables carry estimates too (below)
     assert sel("bf16", M=8192, N=8192, K=8192)[0]["block_m"] == 256
+
+
+def test_other_types_choice_by_estimated_time():
+    def name(dtype, M, N, K, tB=0, **kw):
+        return sel(dtype, 0, tB, M=M, N=N, K=K, **kw)[0]["name"]
+    # the headline shapes keep their builds
+    assert name("bf16", 8192, 8192, 8192) == "mgemm_bf16_256x256x64_w2x4_d2"
+    assert name("i8", 8192, 8192, 8192, tB=1) == "mgemm_i8_256x256x128_w2x4_d2"
+    assert name("f64", 4096, 4096, 4096) == "mgemm_f64_128x128x16_w4x2"
+    # 144 tiles of 256x256 beat 576 of 128x128 (three rounds; measured bf16
+    # 3072^3 66 us against 81, int8 43 against 50)
+    assert name("bf16", 3072, 3072, 3072) == "mgemm_bf16_256x256x64_w2x4_d2"
+    assert name("i8", 3072, 3072, 3072, tB=1) == "mgemm_i8_256x256x128_w2x4_d2"
+    # fp64: 2304 tiles of 64x64 beat 576 of 128x128 (1043 us against 1207)
+    assert name("f64", 3072, 3072, 3072) == "mgemm_f64_64x64x16_w2x2"
+    # a shallow K stays on the store-bound rule: the attention-score batch
+    assert name("f16", 1024, 1024, 64, tB=1, lda=64, ldb=64, batch=128, strideA=65536,
+                strideB=65536, strideC=1048576) == "mgemm_f16_256x256x64_w4x2"
+    # rows with no 16-byte alignment: the preference order, 4-byte copies first
+    assert name("i8", 3000, 3000, 3000, tB=1) == "mgemm_i8_128x128x128_w2x2_d4_u"
+    assert name("bf16", 1000, 1030, 1000, lda=1002, ldb=1030) == "mgemm_bf16_64x64x64_w2x2_d4_u"
+    assert name("bf16", 1000, 1027, 999, lda=999, ldb=1027) == "mgemm_bf16_64x64x64_w2x2_u"
+    # 4-byte copies of 16-bit elements need an even K
+    assert name("bf16", 1000, 1030, 999, lda=1002, ldb=1030) == "mgemm_bf16_64x64x64_w2x2_u"
 
 
 def test_int8_rules_without_a_gpu():
