@@ -726,7 +726,9 @@ struct DmaPath {
     // chunk that straddles the m/n edge is read whole: it is 16-byte aligned
     // and holds a valid element, so it lies inside a mapped page, and its
     // values past the edge feed only rows or columns of C that are not stored.
-    template <bool KC, int IL, int ROWB, int IPW>
+    // CHECK false (interior tiles with whole slabs): no masking, and the
+    // offsets do not depend on the slab.
+    template <bool KC, int IL, int ROWB, int IPW, bool CHECK>
     __device__ __forceinline__ static void dma_one(__amdgpu_buffer_rsrc_t rs, char *dst, int ld_bytes, int w,
                                                    int lane, int q, int rows_ok, int cols_ok)
     {
@@ -741,7 +743,7 @@ struct DmaPath {
             const int c = (lane % CPR) ^ swz(pb + j);
             const int row0 = logical_row<IL>(pb);
             int voff = j * IL * ld_bytes + (c << 4);
-            if (row0 + j * IL >= rows_ok || c * CH >= cols_ok) voff = kOutOfRange;
+            if (CHECK && (row0 + j * IL >= rows_ok || c * CH >= cols_ok)) voff = kOutOfRange;
             const int soff = __builtin_amdgcn_readfirstlane(row0 * ld_bytes);
             dma16(rs, lds_addr_of(dst + pb * RB), voff, soff);
         } else {
@@ -750,7 +752,7 @@ struct DmaPath {
             const int b = ins * 1024 + 16 * lane;
             const int k = b / ROWB, bb = b % ROWB;
             const int lb = (((bb >> 6) ^ mc_key<ROWB>(k)) << 6) | (bb & 63);
-            const int voff = (k >= rows_ok || lb >= cols_ok * ES) ? kOutOfRange : k * ld_bytes + lb;
+            const int voff = (CHECK && (k >= rows_ok || lb >= cols_ok * ES)) ? kOutOfRange : k * ld_bytes + lb;
             dma16(rs, lds_addr_of(dst + ins * 1024), voff, 0);
         }
     }
@@ -883,6 +885,9 @@ struct DmaPath {
         }
     }
 
+    // CHECK: mask copies against the matrix edges and K (edge tiles, a K
+    // tail); without it the tile must be interior with whole slabs.
+    template <bool CHECK>
     __device__ __forceinline__ static void run(const KernelArgs &p, char *smem, int bidx, int m0, int n0,
                                                f32x16 (&acc)[TM][TN])
     {
@@ -926,18 +931,18 @@ struct DmaPath {
                     dma_dw<B_KC, IL_B, B_ROWB, B_IPW>(rb, st + A_BYTES, ldb_b, w, lane, q,
                                                       B_KC ? nrem : krem, B_KC ? krem : nrem);
             } else {
-                // every copy is checked (two compares and a select; a branch
-                // to unchecked copies for interior slabs cost the LDS address
-                // its scalar register)
+                // CHECK is fixed for the whole tile: a branch between checked
+                // and unchecked copies inside one loop cost the LDS address
+                // its scalar register
                 const int krem = p.K - s * BK;
 #pragma unroll
                 for (int q = 0; q < A_IPW; ++q)
-                    dma_one<A_KC, IL_A, A_ROWB, A_IPW>(ra, st, lda_b, w, lane, q, A_KC ? mrem : krem,
-                                                       A_KC ? krem : mrem);
+                    dma_one<A_KC, IL_A, A_ROWB, A_IPW, CHECK>(ra, st, lda_b, w, lane, q, A_KC ? mrem : krem,
+                                                              A_KC ? krem : mrem);
 #pragma unroll
                 for (int q = 0; q < B_IPW; ++q)
-                    dma_one<B_KC, IL_B, B_ROWB, B_IPW>(rb, st + A_BYTES, ldb_b, w, lane, q,
-                                                       B_KC ? nrem : krem, B_KC ? krem : nrem);
+                    dma_one<B_KC, IL_B, B_ROWB, B_IPW, CHECK>(rb, st + A_BYTES, ldb_b, w, lane, q,
+                                                              B_KC ? nrem : krem, B_KC ? krem : nrem);
             }
         };
         auto frags = [&](int s, int g, Fr &f) {
@@ -1211,7 +1216,7 @@ gemm_kernel(KernelArgs p)
         for (int u = 0; u < TN; ++u)
             acc[t][u] = f32x16{};
     if constexpr (ALL_DMA) {
-        D::run(pk, smem, bidx, m0, n0, acc);
+        D::template run<true>(pk, smem, bidx, m0, n0, acc);
         if (m0 + BM <= pk.M && n0 + BN <= pk.N)
             epilogue<false, D::IL_A, D::IL_B, TM, TN, WTM, WTN, WN, CT>(pk, bidx, m0, n0, acc);
         else
@@ -1219,8 +1224,12 @@ gemm_kernel(KernelArgs p)
     } else {
         if constexpr (VECOK) {
             if (pk.fast_ok && pk.K % D::CH == 0) {
-                D::run(pk, smem, bidx, m0, n0, acc);
-                if (m0 + BM <= pk.M && n0 + BN <= pk.N)
+                const bool full = m0 + BM <= pk.M && n0 + BN <= pk.N;
+                if (full && pk.K % D::BK == 0)
+                    D::template run<false>(pk, smem, bidx, m0, n0, acc);
+                else
+                    D::template run<true>(pk, smem, bidx, m0, n0, acc);
+                if (full)
                     epilogue<false, D::IL_A, D::IL_B, TM, TN, WTM, WTN, WN, CT>(pk, bidx, m0, n0, acc);
                 else
                     epilogue<true, D::IL_A, D::IL_B, TM, TN, WTM, WTN, WN, CT>(pk, bidx, m0, n0, acc);
