@@ -8,22 +8,31 @@ const Variant *f16_variants(int *count)
     // Chosen by the lowest estimated time (Cost in variants.hpp: t0 us, tk us
     // per unit of K, register-path factor, one-round factor), fitted on bf16
     // (the two 16-bit types run the same kernels at the same rates): the
-    // 256x256 two-stage tile 0.0236 us per K per round (0.57 of the matrix
-    // peak per CU), 128x128 0.0085 (0.39), 64x64 0.0040 (0.21).  K <= 128
-    // (store-bound) takes the 256x256 4x2-wave tile first.  Builds without
-    // an estimate run when forced, or by preference order when no estimated
-    // build fits (unaligned rows: 4-byte copies first).
+    // 256x256 two-stage tile 0.0228 us per K per round (0.58 of the matrix
+    // peak per CU), 128x128 0.0083 to 0.0096 (0.35 to 0.40), 64x64 0.0034 to
+    // 0.0039 (0.21 to 0.25).  The 128x128 slopes are set 10% above their fit:
+    // their rounds slow down on large problems (twice the operand traffic of
+    // the 256x256 tile), and without it the choice took them at 3000^3 and
+    // 7000^3 where the large tile is faster.  K <= 128 (store-bound) takes the
+    // 256x256 4x2-wave tile first.  Builds without an estimate run when
+    // forced, or by preference order when no estimated build fits (unaligned
+    // rows: 4-byte copies first).
     static const Variant table[] = {
-        MGEMM_VARIANT_D(_Float16, 1, 256, 256, 64, 2, 4, true, 2, "mgemm_f16_256x256x64_w2x4_d2", {11.1f, 0.02356f, 1.6f, 1.0f}),
+        MGEMM_VARIANT_D(_Float16, 1, 256, 256, 64, 2, 4, true, 2, "mgemm_f16_256x256x64_w2x4_d2", {11.13f, 0.02283f, 1.6f, 1.0f}),
         MGEMM_VARIANT(_Float16, 1, 256, 256, 64, 2, 4, true, "mgemm_f16_256x256x64_w2x4", {}),
         MGEMM_VARIANT(_Float16, 1, 256, 256, 64, 4, 2, true, "mgemm_f16_256x256x64_w4x2", {}),
         MGEMM_VARIANT(_Float16, 1, 256, 256, 64, 2, 2, true, "mgemm_f16_256x256x64_w2x2", {}),
         MGEMM_VARIANT_D(_Float16, 1, 256, 256, 64, 2, 2, true, 2, "mgemm_f16_256x256x64_w2x2_d2", {}),
-        MGEMM_VARIANT(_Float16, 1, 128, 128, 64, 2, 2, true, "mgemm_f16_128x128x64_w2x2", {2.34f, 0.00852f, 1.5f, 1.27f}),
+        // 128x128 with eight waves: four stages of 32 for one-round grids (the
+        // deeper ring hides the loads of a lone workgroup), two of 64 when a CU
+        // holds several workgroups
+        MGEMM_VARIANT(_Float16, 1, 128, 128, 64, 2, 4, true, "mgemm_f16_128x128x64_w2x4", {2.35f, 0.00964f, 1.5f, 1.07f}),
+        MGEMM_VARIANT_D(_Float16, 1, 128, 128, 64, 2, 4, true, 2, "mgemm_f16_128x128x64_w2x4_d2", {2.46f, 0.00829f, 1.5f, 1.39f}),
         // rows 4-byte aligned (and K even): 4-byte copies into LDS, every tile
         MGEMM_VARIANT_D(_Float16, 1, 128, 128, 64, 2, 2, false, 4, "mgemm_f16_128x128x64_w2x2_d4_u", {}),
         MGEMM_VARIANT(_Float16, 1, 128, 128, 64, 2, 2, false, "mgemm_f16_128x128x64_w2x2_u", {}),
-        MGEMM_VARIANT(_Float16, 1, 64, 64, 64, 2, 2, true, "mgemm_f16_64x64x64_w2x2", {0.41f, 0.00402f, 1.1f, 2.28f}),
+        MGEMM_VARIANT(_Float16, 1, 64, 64, 64, 2, 2, true, "mgemm_f16_64x64x64_w2x2", {0.44f, 0.00391f, 1.1f, 1.73f}),
+        MGEMM_VARIANT_D(_Float16, 1, 64, 64, 64, 2, 2, true, 2, "mgemm_f16_64x64x64_w2x2_d2", {0.45f, 0.00335f, 1.1f, 2.32f}),
         MGEMM_VARIANT_D(_Float16, 1, 64, 64, 64, 2, 2, false, 4, "mgemm_f16_64x64x64_w2x2_d4_u", {}),
         MGEMM_VARIANT(_Float16, 1, 64, 64, 64, 2, 2, false, "mgemm_f16_64x64x64_w2x2_u", {}),
     };

@@ -7,20 +7,26 @@ namespace mgemm {
 const Variant *i8_variants(int *count)
 {
     // Chosen by the lowest estimated time (Cost in variants.hpp): the 256x256
-    // two-stage tile 0.0131 us per K per round (0.51 of the matrix peak per
-    // CU), 128x128 0.0045 (0.37), 64x64 0.0021 (0.20); the register-path
-    // factor (16-byte rows, K no multiple of 16) is a round estimate.  Builds
-    // without an estimate run when forced, or by preference order when no
-    // estimated build fits (unaligned rows: 4-byte copies first).
+    // two-stage tile 0.0121 us per K per round (0.55 of the matrix peak per
+    // CU; its t0 is set from a K = 256 launch, the fit over whole-K rounds
+    // having too few points), 128x128 with eight waves 0.0034 (two stages of
+    // 128, several workgroups per CU) or 0.0044 (four of 64, better for one
+    // round), 64x64 0.0014 to 0.0020.  The register-path factor (16-byte
+    // rows, K no multiple of 16) is a round estimate.  Builds without an
+    // estimate run when forced, or by preference order when no estimated
+    // build fits (unaligned rows: 4-byte copies first).
     static const Variant table[] = {
-        MGEMM_VARIANT_I8(256, 256, 128, 2, 4, true, 2, "mgemm_i8_256x256x128_w2x4_d2", {0.0f, 0.01308f, 1.5f, 1.18f}),
+        MGEMM_VARIANT_I8(256, 256, 128, 2, 4, true, 2, "mgemm_i8_256x256x128_w2x4_d2", {8.0f, 0.0121f, 1.5f, 1.15f}),
         MGEMM_VARIANT_I8(256, 256, 128, 2, 4, true, 1, "mgemm_i8_256x256x128_w2x4", {}),
         MGEMM_VARIANT_I8(256, 256, 128, 4, 2, true, 1, "mgemm_i8_256x256x128_w4x2", {}),
-        MGEMM_VARIANT_I8(128, 128, 128, 2, 2, true, 1, "mgemm_i8_128x128x128_w2x2", {3.83f, 0.00448f, 1.5f, 1.13f}),
+        // 128x128 with eight waves (four waves measured 3-20% slower)
+        MGEMM_VARIANT_I8(128, 128, 128, 2, 4, true, 1, "mgemm_i8_128x128x128_w2x4", {3.39f, 0.00441f, 1.5f, 1.15f}),
+        MGEMM_VARIANT_I8(128, 128, 128, 2, 4, true, 2, "mgemm_i8_128x128x128_w2x4_d2", {3.59f, 0.00336f, 1.5f, 1.35f}),
         // rows 4-byte aligned (and K a multiple of 4): 4-byte copies into LDS, every tile
         MGEMM_VARIANT_I8(128, 128, 128, 2, 2, false, 4, "mgemm_i8_128x128x128_w2x2_d4_u", {}),
         MGEMM_VARIANT_I8(128, 128, 128, 2, 2, false, 1, "mgemm_i8_128x128x128_w2x2_u", {}),
-        MGEMM_VARIANT_I8(64, 64, 128, 2, 2, true, 1, "mgemm_i8_64x64x128_w2x2", {0.59f, 0.00207f, 1.5f, 3.51f}),
+        MGEMM_VARIANT_I8(64, 64, 128, 2, 2, true, 1, "mgemm_i8_64x64x128_w2x2", {0.64f, 0.00195f, 1.5f, 2.6f}),
+        MGEMM_VARIANT_I8(64, 64, 128, 2, 2, true, 2, "mgemm_i8_64x64x128_w2x2_d2", {0.82f, 0.00139f, 1.5f, 3.16f}),
         MGEMM_VARIANT_I8(64, 64, 128, 2, 2, false, 4, "mgemm_i8_64x64x128_w2x2_d4_u", {}),
         MGEMM_VARIANT_I8(64, 64, 128, 2, 2, false, 1, "mgemm_i8_64x64x128_w2x2_u", {}),
     };

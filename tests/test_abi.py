@@ -187,9 +187,14 @@ def test_other_types_choice_by_estimated_time():
     assert name("i8", 8192, 8192, 8192, tB=1) == "mgemm_i8_256x256x128_w2x4_d2"
     assert name("f64", 4096, 4096, 4096) == "mgemm_f64_128x128x16_w4x2"
     # 144 tiles of 256x256 beat 576 of 128x128 (three rounds; measured bf16
-    # 3072^3 66 us against 81, int8 43 against 50)
+    # 3072^3 66 us against 78)
     assert name("bf16", 3072, 3072, 3072) == "mgemm_bf16_256x256x64_w2x4_d2"
-    assert name("i8", 3072, 3072, 3072, tB=1) == "mgemm_i8_256x256x128_w2x4_d2"
+    # 128x128 with eight waves: one round of 256 tiles takes the four-stage
+    # build, several rounds the two-stage one (bf16 2048^3 22 us, 2560^3 38;
+    # int8 4608^3 104 us against 116 for 256x256)
+    assert name("bf16", 2048, 2048, 2048) == "mgemm_bf16_128x128x64_w2x4"
+    assert name("bf16", 2560, 2560, 2560) == "mgemm_bf16_128x128x64_w2x4_d2"
+    assert name("i8", 4608, 4608, 4608, tB=1) == "mgemm_i8_128x128x128_w2x4_d2"
     # fp64: 2304 tiles of 64x64 beat 576 of 128x128 (1043 us against 1207)
     assert name("f64", 3072, 3072, 3072) == "mgemm_f64_64x64x16_w2x2"
     # a shallow K stays on the store-bound rule: the attention-score batch
