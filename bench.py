@@ -274,7 +274,7 @@ def select_for(mg, p, ptrs=(1 << 20, 1 << 20, 1 << 20)):
         return plan["variant"], plan["grid"]
     return mg.select(p.dtype, int(p.transA), int(p.transB), p.M, p.N, p.K, p.alpha, ptrs[0],
                      p.lda, p.strideA, ptrs[1], p.ldb, p.strideB, p.beta, ptrs[2], p.ldc,
-                     p.strideC, p.batch)
+                     p.strideC, p.batch, c_dtype=p.c_dtype)
 
 
 def make_device_problem(p, torch, dev):

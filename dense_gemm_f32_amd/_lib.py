@@ -101,6 +101,10 @@ def load():
     lib.mgemm_select.argtypes = [i32, i32, i32, i64, i64, i64, f32, vp, i64, i64, vp, i64, i64,
                                  f32, vp, i64, i64, i64, ctypes.POINTER(VariantInfo),
                                  ctypes.POINTER(i64)]
+    lib.mgemm_select_ex.restype = i32
+    lib.mgemm_select_ex.argtypes = [i32, i32, i32, i32, i64, i64, i64, ctypes.c_double, vp, i64, i64,
+                                    vp, i64, i64, ctypes.c_double, vp, i64, i64, i64,
+                                    ctypes.POINTER(VariantInfo), ctypes.POINTER(i64)]
     lib.mgemm_force_variant.restype = i32
     lib.mgemm_force_variant.argtypes = [i32, i32]
     _lib = lib
@@ -314,19 +318,27 @@ def variants():
 
 
 def select(in_dtype, transA, transB, M, N, K, alpha=1.0, A=0, lda=None, strideA=0, B=0,
-           ldb=None, strideB=0, beta=0.0, C=0, ldc=None, strideC=0, batch=1):
+           ldb=None, strideB=0, beta=0.0, C=0, ldc=None, strideC=0, batch=1, c_dtype=None):
     """(variant info dict, grid size) for a call with these arguments; raises on invalid ones.
-    Pointers are plain integers here (alignment matters, contents do not)."""
+    Pointers are plain integers here (alignment matters, contents do not).  c_dtype: C's type
+    (mgemm_select_ex); None takes fp32 (int32 for int8, double for fp64 inputs)."""
     dt = DTYPE_CODES.get(in_dtype, in_dtype)
     lda = lda if lda is not None else (M if transA else K)
     ldb = ldb if ldb is not None else (K if transB else N)
     ldc = ldc if ldc is not None else N
     info = VariantInfo()
     grid = ctypes.c_int64()
-    st = load().mgemm_select(dt, int(transA), int(transB), M, N, K, alpha, A, lda, strideA, B, ldb,
-                             strideB, beta, C, ldc, strideC, batch, ctypes.byref(info),
-                             ctypes.byref(grid))
-    _check(st, "mgemm_select")
+    if c_dtype is None:
+        st = load().mgemm_select(dt, int(transA), int(transB), M, N, K, alpha, A, lda, strideA, B,
+                                 ldb, strideB, beta, C, ldc, strideC, batch, ctypes.byref(info),
+                                 ctypes.byref(grid))
+        _check(st, "mgemm_select")
+    else:
+        ct = DTYPE_CODES.get(c_dtype, c_dtype)
+        st = load().mgemm_select_ex(dt, ct, int(transA), int(transB), M, N, K, alpha, A, lda,
+                                    strideA, B, ldb, strideB, beta, C, ldc, strideC, batch,
+                                    ctypes.byref(info), ctypes.byref(grid))
+        _check(st, "mgemm_select_ex")
     return info.as_dict(), grid.value
 
 

@@ -275,8 +275,7 @@ mgemm_status mgemm_variant(int id, mgemm_variant_info *out);
  * after the same validation the entry points perform.  Returns the
  * validation status; *out and *grid are set on MGEMM_OK (id = -1 and grid = 0
  * when the call would launch no GEMM kernel).  C is taken as fp32 (int32
- * for MGEMM_I8 inputs, double for MGEMM_F64); a 16-bit C selects the same
- * variant.
+ * for MGEMM_I8 inputs, double for MGEMM_F64).
  */
 mgemm_status mgemm_select(mgemm_dtype in_dtype, mgemm_op transA, mgemm_op transB,
                           int64_t M, int64_t N, int64_t K, float alpha,
@@ -284,6 +283,20 @@ mgemm_status mgemm_select(mgemm_dtype in_dtype, mgemm_op transA, mgemm_op transB
                           const void *B, int64_t ldb, int64_t strideB,
                           float beta, const float *C, int64_t ldc, int64_t strideC,
                           int64_t batch, mgemm_variant_info *out, int64_t *grid);
+
+/*
+ * mgemm_select for a C of type c_dtype, with the pairs gemm_strided_batched_ex
+ * accepts (fp32 or the inputs' own 16-bit type for 16-bit inputs, int32 for
+ * MGEMM_I8, double for MGEMM_F64).  The choice can depend on C's type: with
+ * a shallow K the C stores dominate, and a 16-bit C takes a tile whose lanes
+ * store four adjacent elements.  C is aligned to its own element size.
+ */
+mgemm_status mgemm_select_ex(mgemm_dtype in_dtype, mgemm_dtype c_dtype, mgemm_op transA,
+                             mgemm_op transB, int64_t M, int64_t N, int64_t K, double alpha,
+                             const void *A, int64_t lda, int64_t strideA,
+                             const void *B, int64_t ldb, int64_t strideB,
+                             double beta, const void *C, int64_t ldc, int64_t strideC,
+                             int64_t batch, mgemm_variant_info *out, int64_t *grid);
 
 /*
  * Force every later call of dtype `dtype` onto variant `id` (-1 restores the

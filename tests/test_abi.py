@@ -197,9 +197,18 @@ def test_other_types_choice_by_estimated_time():
     assert name("i8", 4608, 4608, 4608, tB=1) == "mgemm_i8_128x128x128_w2x4_d2"
     # fp64: 2304 tiles of 64x64 beat 576 of 128x128 (1043 us against 1207)
     assert name("f64", 3072, 3072, 3072) == "mgemm_f64_64x64x16_w2x2"
-    # a shallow K stays on the store-bound rule: the attention-score batch
-    assert name("f16", 1024, 1024, 64, tB=1, lda=64, ldb=64, batch=128, strideA=65536,
-                strideB=65536, strideC=1048576) == "mgemm_f16_256x256x64_w4x2"
+    # a shallow K is store-bound: the attention-score batch takes two 128x128
+    # workgroups per CU with an fp32 C, and the 256x256 tile whose lanes store
+    # four adjacent elements with a binary16 C
+    qkt = dict(tB=1, lda=64, ldb=64, batch=128, strideA=65536, strideB=65536, strideC=1048576)
+    assert name("f16", 1024, 1024, 64, **qkt) == "mgemm_f16_128x128x64_w2x4_d2"
+    assert name("f16", 1024, 1024, 64, c_dtype="f16", **qkt) == "mgemm_f16_256x256x64_w4x2"
+    assert name("f16", 1024, 1024, 64, c_dtype="f32", **qkt) == "mgemm_f16_128x128x64_w2x4_d2"
+    # mgemm_select_ex checks C's type like the entry points do
+    with pytest.raises(mg.MgemmError):
+        sel("f16", M=64, N=64, K=64, c_dtype="bf16")
+    with pytest.raises(mg.MgemmError):
+        sel("f32", M=64, N=64, K=64, c_dtype="f16")
     # rows with no 16-byte alignment: the preference order, 4-byte copies first
     assert name("i8", 3000, 3000, 3000, tB=1) == "mgemm_i8_128x128x128_w2x2_d4_u"
     assert name("bf16", 1000, 1030, 1000, lda=1002, ldb=1030) == "mgemm_bf16_64x64x64_w2x2_d4_u"
