@@ -188,19 +188,15 @@ mgemm_status validate_and_plan(int dtype, int c_dtype, int transA, int transB, i
     if (pick < 0 && (dtype == MGEMM_F16 || dtype == MGEMM_BF16) && K <= 128) {
         // A shallow K (the whole product is a couple of slabs, e.g. attention
         // scores with a 64-wide head) is bound by the C store rather than the
-        // matrix cores.  A 16-bit C: the 256x256 tile with 4x2 wavefronts,
-        // whose lanes store four adjacent elements, while it still gives one
-        // workgroup per CU.  An fp32 C: the 128x128 eight-wave two-stage
-        // tile, two workgroups per CU, so that one's stores overlap the
-        // other's loads, while it gives two rounds (measured: the
-        // attention-score batch 85 us against 89, 8192^2 x 128 51 against 63).
-        const bool c16 = c_dtype == MGEMM_F16 || c_dtype == MGEMM_BF16;
+        // matrix cores: the 256x256 tile with 4x2 wavefronts, whose lanes
+        // store four adjacent elements, while it still gives one workgroup
+        // per CU.  (Two 128x128 workgroups per CU ran 4% faster on the
+        // attention-score batch with an fp32 C from a cool start, but slowed
+        // from 82 to 120 us per launch over 50 back-to-back launches, where
+        // this tile goes from 86 to 99.)
         for (int i = 0; i < t.n && pick < 0; ++i) {
             const Variant &v = t.v[i];
-            if (!eligible(v)) continue;
-            if (c16 ? (v.bm == 256 && v.bn == 256 && v.wm == 4 && wgs_of(v) >= 256)
-                    : (v.bm == 128 && v.bn == 128 && v.wn == 4 && v.pipe == 2 && wgs_of(v) >= 512))
-                pick = i;
+            if (eligible(v) && v.bm == 256 && v.bn == 256 && v.wm == 4 && wgs_of(v) >= 256) pick = i;
         }
     }
     if (pick < 0) {

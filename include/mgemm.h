@@ -285,11 +285,11 @@ mgemm_status mgemm_select(mgemm_dtype in_dtype, mgemm_op transA, mgemm_op transB
                           int64_t batch, mgemm_variant_info *out, int64_t *grid);
 
 /*
- * mgemm_select for a C of type c_dtype, with the pairs gemm_strided_batched_ex
- * accepts (fp32 or the inputs' own 16-bit type for 16-bit inputs, int32 for
- * MGEMM_I8, double for MGEMM_F64).  The choice can depend on C's type: with
- * a shallow K the C stores dominate, and a 16-bit C takes a tile whose lanes
- * store four adjacent elements.  C is aligned to its own element size.
+ * mgemm_select for a C of type c_dtype, validated exactly as the entry points
+ * validate that call: the pairs gemm_strided_batched_ex accepts (fp32 or the
+ * inputs' own 16-bit type for 16-bit inputs, int32 for MGEMM_I8, double for
+ * MGEMM_F64), C aligned to its own element size, alpha and beta as doubles
+ * (integral for int8).  The variant chosen does not depend on C's type.
  */
 mgemm_status mgemm_select_ex(mgemm_dtype in_dtype, mgemm_dtype c_dtype, mgemm_op transA,
                              mgemm_op transB, int64_t M, int64_t N, int64_t K, double alpha,

@@ -197,13 +197,11 @@ def test_other_types_choice_by_estimated_time():
     assert name("i8", 4608, 4608, 4608, tB=1) == "mgemm_i8_128x128x128_w2x4_d2"
     # fp64: 2304 tiles of 64x64 beat 576 of 128x128 (1043 us against 1207)
     assert name("f64", 3072, 3072, 3072) == "mgemm_f64_64x64x16_w2x2"
-    # a shallow K is store-bound: the attention-score batch takes two 128x128
-    # workgroups per CU with an fp32 C, and the 256x256 tile whose lanes store
-    # four adjacent elements with a binary16 C
+    # a shallow K is store-bound: the attention-score batch takes the 256x256
+    # tile whose lanes store four adjacent elements, with either C type
     qkt = dict(tB=1, lda=64, ldb=64, batch=128, strideA=65536, strideB=65536, strideC=1048576)
-    assert name("f16", 1024, 1024, 64, **qkt) == "mgemm_f16_128x128x64_w2x4_d2"
+    assert name("f16", 1024, 1024, 64, **qkt) == "mgemm_f16_256x256x64_w4x2"
     assert name("f16", 1024, 1024, 64, c_dtype="f16", **qkt) == "mgemm_f16_256x256x64_w4x2"
-    assert name("f16", 1024, 1024, 64, c_dtype="f32", **qkt) == "mgemm_f16_128x128x64_w2x4_d2"
     # mgemm_select_ex checks C's type like the entry points do
     with pytest.raises(mg.MgemmError):
         sel("f16", M=64, N=64, K=64, c_dtype="bf16")
