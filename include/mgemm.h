@@ -259,8 +259,9 @@ typedef struct {
     int waves_n;       /* wavefronts along N */
     int threads;       /* workgroup size */
     int lds_bytes;     /* LDS per workgroup */
-    int pipe;          /* interior-tile schedule: 1 = four LDS stages of
-                          block_k/2, 2 = two stages of block_k */
+    int pipe;          /* DMA-path schedule: 1 = four LDS stages of
+                          block_k/2, 2 = two stages of block_k, 4 = 4-byte
+                          copies in two stages of block_k (every tile) */
     char name[64];     /* kernel family name, e.g. "mgemm_f32_256x256x32_w2x2" */
 } mgemm_variant_info;
 

@@ -131,9 +131,10 @@ def test_every_variant_every_transpose_ragged(dtype):
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 def test_dma_path_every_variant_every_transpose(dtype):
-    # K a multiple of every slab depth, so interior tiles take the LDS-DMA path while
-    # the ragged last tile row/column takes the range-checked path; leading dimensions
-    # padded by 8 elements (16-byte rows stay aligned) with NaN in the padding.
+    # K a multiple of every slab depth: interior tiles take the unchecked LDS-DMA
+    # copies, the ragged last tile row/column the range-checked ones; leading
+    # dimensions padded by 8 elements (16-byte rows stay aligned) with NaN in the
+    # padding.
     for v in variants_of(dtype):
         if v["name"].endswith("_u"):
             continue
@@ -628,7 +629,7 @@ def test_empty_problems_for_every_entry_point():
 
 def test_leading_dimensions_beyond_32bit_tile_offsets():
     # with a leading dimension past 2^31 / (257 * element size), 257 rows no longer
-    # fit 32-bit byte offsets from a tile origin: interior tiles must take the
+    # fit 32-bit byte offsets from a tile origin: every tile must take the
     # 64-bit-addressed register path and still be exact
     p = wl.Problem("f32", 300, 260, 48, ldb=(1 << 21) + 64, dist="int", int_lo=-9, int_hi=9,
                    seed=27)
