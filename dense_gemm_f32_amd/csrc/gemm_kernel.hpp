@@ -682,7 +682,7 @@ struct DmaPath {
     static constexpr int G = F32 ? BK / 8 : BK * ES / 32;  // k-groups (32 bytes of k) per slab
     static constexpr bool A_KC = !TA, B_KC = TB;
     static constexpr bool A_TR = TA && !F32, B_TR = !TB && !F32;
-    static constexpr bool PRIO = F32 || (ES == 2 && B_KC);  // raised priority while multiplying
+    static constexpr bool PRIO = F32 || B_KC;  // raised priority while multiplying
     static constexpr int IL_A = A_TR ? 1 : TM, IL_B = B_TR ? 1 : TN;
     static constexpr int A_BYTES = BM * BK * ES, B_BYTES = BN * BK * ES;
     static constexpr int STAGE = A_BYTES + B_BYTES;
@@ -983,9 +983,9 @@ struct DmaPath {
         for (; kt + NS < nk; ++kt) {
             // A wave multiplying a slab outranks one at its copies and waits
             // (two waves share each SIMD).  Measured in a same-box A/B: fp32
-            // 4096^3 -0.8%, 16-bit with a K-contiguous B -1.5%, while 16-bit
-            // with an MN-contiguous B (transposing reads) lost 0.6%: it is
-            // left at the default priority there.
+            // 4096^3 within 0.8%, 16-bit with a K-contiguous B -1.5%, int8
+            // -1.5 to -2.5%, while 16-bit with an MN-contiguous B
+            // (transposing reads) lost 0.6%: it keeps the default priority.
             if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
             body_head(kt);
             if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
