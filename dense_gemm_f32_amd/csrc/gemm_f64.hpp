@@ -173,7 +173,11 @@ gemm_f64_kernel(KernelArgs p)
     __syncthreads();
     for (int kt = 0; kt + 1 < nk; ++kt) {
         load_slab(kt + 1);
+        // a wave multiplying outranks one at its stores and barrier (four
+        // waves share each SIMD): about 1% in a same-box A/B
+        __builtin_amdgcn_s_setprio(1);
         compute(kt & 1);
+        __builtin_amdgcn_s_setprio(0);
         double *st = smem + ((kt + 1) & 1) * STAGE;
         la.store(st, tid);
         lb.store(st + A_ELEMS, tid);
