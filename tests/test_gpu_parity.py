@@ -748,3 +748,47 @@ def test_launches_replay_in_a_hip_graph():
         assert float(junk) == float(junk)
         check_exact(r.result(), eager, f"graph replay {rep} (256^3)")
         check_exact(rq.result(), eager_q, f"graph replay {rep} (split-K 256x256x8192)")
+
+
+# ------------------------------------------------------------------ seeded random problems
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "i8", "f64"])
+def test_random_problems_exact(dtype):
+    # Seeded random shapes, transposes, leading-dimension padding (aligned and
+    # not), C types, batches and split-K plans through the automatic choice:
+    # whatever build and path (unchecked or checked DMA copies, 4-byte copies,
+    # the realigning register path) the choice lands on must be exact on
+    # integer-valued inputs, with NaN (or a filler) in every padding element.
+    rng = np.random.default_rng({"f32": 11, "f16": 12, "bf16": 13, "i8": 14, "f64": 15}[dtype])
+    i8 = dtype == "i8"
+    for case in range(16):
+        small = rng.random() < 0.4
+        M = int(rng.integers(1, 70 if small else 400))
+        N = int(rng.integers(1, 70 if small else 400))
+        K = int(rng.integers(1, 64)) if rng.random() < 0.3 else int(rng.integers(64, 500))
+        if rng.random() < 0.3:
+            K = -(-K // 32) * 32          # whole slabs now and then
+        tA, tB = (False, True) if i8 else (bool(rng.integers(2)), bool(rng.integers(2)))
+        batch = int(rng.integers(1, 4)) if rng.random() < 0.3 else 1
+        splitk = None
+        if batch == 1 and rng.random() < 0.25:
+            splitk = int(rng.choice([0, 2, 3, 5]))
+        pads = [0, 1, 2, 3, 4, 8, 16, 64]
+        a_cols, b_cols = (M if tA else K), (K if tB else N)
+        lda = max(a_cols, 1) + int(rng.choice(pads))
+        ldb = max(b_cols, 1) + int(rng.choice(pads))
+        ldc = max(N, 1) + int(rng.choice(pads))
+        if i8:
+            kw = dict(c_dtype="i32", int_lo=-128, int_hi=127, pad_value=77,
+                      alpha=float(rng.choice([1, -3, 2])), beta=float(rng.choice([0, 1, -2])))
+        else:
+            c16 = dtype in ("f16", "bf16") and rng.random() < 0.4
+            kw = dict(c_dtype=dtype if c16 else "f32", int_lo=-8, int_hi=8, pad_value=float("nan"),
+                      alpha=float(rng.choice([1.0, -1.0, 2.0, 0.5])),
+                      beta=float(rng.choice([0.0, 1.0, -1.0, 0.5])))
+        p = wl.Problem(dtype, M, N, K, transA=tA, transB=tB, batch=batch, lda=lda, ldb=ldb, ldc=ldc,
+                       dist="int", c_dist="int", seed=1000 * case + 7, splitk=splitk, **kw)
+        info, _ = mg.select(p.dtype, int(tA), int(tB), M, N, K, A=16, lda=lda,
+                            strideA=p.strideA, B=16, ldb=ldb, strideB=p.strideB, C=16, ldc=ldc,
+                            strideC=p.strideC, batch=batch, alpha=p.alpha, beta=p.beta)
+        full_check(p, exact=True, what=f"random {dtype} #{case} ({info['name']}, splitk={splitk})")
