@@ -8,8 +8,9 @@ const Variant *f16_variants(int *count)
     // Chosen by the lowest estimated time (Cost in variants.hpp: t0 us, tk us
     // per unit of K, register-path factor, one-round factor), fitted on bf16
     // (the two 16-bit types run the same kernels at the same rates): the
-    // 256x256 two-stage tile 0.0228 us per K per round (0.58 of the matrix
-    // peak per CU), 128x128 0.0083 to 0.0096 (0.35 to 0.40), 64x64 0.0034 to
+    // 256x256 two-stage tile 0.0219 us per K per round (0.61 of the matrix
+    // peak per CU; its fit scaled by the 4% that spreading its copies among
+    // the MFMAs gained), 128x128 0.0083 to 0.0096 (0.35 to 0.40), 64x64 0.0034 to
     // 0.0039 (0.21 to 0.25).  The 128x128 slopes are set 10% above their fit:
     // their rounds slow down on large problems (twice the operand traffic of
     // the 256x256 tile), and without it the choice took them at 3000^3 and
@@ -18,7 +19,7 @@ const Variant *f16_variants(int *count)
     // forced, or by preference order when no estimated build fits (unaligned
     // rows: 4-byte copies first).
     static const Variant table[] = {
-        MGEMM_VARIANT_D(_Float16, 1, 256, 256, 64, 2, 4, true, 2, "mgemm_f16_256x256x64_w2x4_d2", {11.13f, 0.02283f, 1.6f, 1.0f}),
+        MGEMM_VARIANT_D(_Float16, 1, 256, 256, 64, 2, 4, true, 2, "mgemm_f16_256x256x64_w2x4_d2", {10.7f, 0.0219f, 1.6f, 1.0f}),
         MGEMM_VARIANT(_Float16, 1, 256, 256, 64, 2, 4, true, "mgemm_f16_256x256x64_w2x4", {}),
         MGEMM_VARIANT(_Float16, 1, 256, 256, 64, 4, 2, true, "mgemm_f16_256x256x64_w4x2", {}),
         MGEMM_VARIANT(_Float16, 1, 256, 256, 64, 2, 2, true, "mgemm_f16_256x256x64_w2x2", {}),
