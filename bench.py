@@ -49,10 +49,11 @@ PEAK_HBM_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 COPY_PROBE_BYTES = 256 << 20
 PRIMARY = "sgemm_4096"
-CASES = ("sgemm_256", "sgemm_4096", "sgemm_ragged", "sgemm_ragged_splitk", "gemm_bf16_8192",
+CASES = ("sgemm_256", "sgemm_4096", "sgemm_ragged", "sgemm_ragged_splitk", "sgemm_ragged_streamk",
+         "gemm_bf16_8192",
          "gemm_f16_8192", "qkt_batched", "qkt_batched_f16_out", "gemm_i8_8192", "dgemm_4096")
 HBM_BOUND = ("qkt_batched", "qkt_batched_f16_out")
-GRAPH_CASES = ("sgemm_256", "sgemm_ragged_splitk")   # launch-bound: also timed from a HIP graph
+GRAPH_CASES = ("sgemm_256", "sgemm_ragged_splitk", "sgemm_ragged_streamk")  # also timed from a HIP graph
 MOPS_COUNTER = {"f32": "SQ_INSTS_VALU_MFMA_MOPS_F32", "f16": "SQ_INSTS_VALU_MFMA_MOPS_F16",
                 "bf16": "SQ_INSTS_VALU_MFMA_MOPS_BF16", "i8": "SQ_INSTS_VALU_MFMA_MOPS_I8",
                 "f64": "SQ_INSTS_VALU_MFMA_MOPS_F64"}
@@ -150,7 +151,8 @@ def summarize_case(case, d, copy_dir):
     info, grid = select_for(mg, p)
     kname = info["name"]
     # demangled for fp32; 16-bit instances stay mangled
-    filt = "gemm_f64_kernel" if p.dtype == "f64" else "gemm_kernel"
+    filt = ("gemm_f64_kernel" if p.dtype == "f64" else
+            "gemm_sk_kernel" if p.streamk is not None else "gemm_kernel")
     durs = _dispatch_durations(os.path.join(d, "trace"), filt)
     timed = durs[PROFILE_WARMUP:] if len(durs) > PROFILE_WARMUP else durs  # after the warm-up
     fetch_v, _ = _counters(os.path.join(d, "fetch"), filt)
@@ -214,6 +216,17 @@ def summarize_case(case, d, copy_dir):
         lines += ["splitk_chunks: %d of %d" % (plan["chunks"], plan["chunk_len"]),
                   "reduce_kernel_average_ns: " + _fmt(ravg, "%.0f"),
                   "tflops_both_kernels: " + _fmt(both, "%.2f")]
+    if p.streamk is not None:   # the stream-K launch above, then the fix-up of split tiles
+        fix = _dispatch_durations(os.path.join(d, "trace"), "sk_fixup")
+        fix = fix[PROFILE_WARMUP:] if len(fix) > PROFILE_WARMUP else fix
+        favg = _mean(fix)
+        both = p.flops / ((avg + favg) * 1e-9) / 1e12 if avg and favg else None
+        plan = mg.streamk_plan(dt, p.M, p.N, p.K, p.streamk, transA=int(p.transA),
+                               transB=int(p.transB), lda=p.lda, ldb=p.ldb)
+        lines += ["streamk: %d workgroups over %d tiles of %d iterations of %d" %
+                  (plan["workgroups"], plan["tiles"], plan["iterations"], plan["k_per_iteration"]),
+                  "fixup_kernel_average_ns: " + _fmt(favg, "%.0f"),
+                  "tflops_both_kernels: " + _fmt(both, "%.2f")]
     if case in HBM_BOUND and avg:
         gbs = algo / (avg * 1e-9) / 1e9
         lines += ["algorithmic_gbs_at_average: %.1f" % gbs,
@@ -267,7 +280,11 @@ def copy_probe():
 
 def select_for(mg, p, ptrs=(1 << 20, 1 << 20, 1 << 20)):
     """(variant info, grid) of the GEMM kernel a workload launches (for split-K: the
-    partial-product kernel)."""
+    partial-product kernel; for stream-K: the stream-K kernel)."""
+    if p.streamk is not None:
+        plan = mg.streamk_plan(p.dtype, p.M, p.N, p.K, p.streamk, transA=int(p.transA),
+                               transB=int(p.transB), A=ptrs[0], lda=p.lda, B=ptrs[1], ldb=p.ldb)
+        return plan["variant"], plan["workgroups"]
     if p.splitk is not None:
         plan = mg.splitk_plan(p.dtype, p.M, p.N, p.K, p.splitk, transA=int(p.transA),
                               transB=int(p.transB), A=ptrs[0], lda=p.lda, B=ptrs[1], ldb=p.ldb)
@@ -288,6 +305,14 @@ def make_device_problem(p, torch, dev):
 
 def launcher(p, dA, dB, dC):
     import dense_gemm_f32_amd as mg
+    if p.streamk is not None:
+        import torch
+        need = mg.streamk_plan(p.dtype, p.M, p.N, p.K, p.streamk, transA=int(p.transA),
+                               transB=int(p.transB), A=dA, lda=p.lda, B=dB, ldb=p.ldb)["workspace_bytes"]
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dA.device)  # outside the timing
+        return lambda: mg.gemm_streamk(p.dtype, p.c_dtype, int(p.transA), int(p.transB), p.M, p.N,
+                                       p.K, p.alpha, dA, p.lda, dB, p.ldb, p.beta, dC, p.ldc,
+                                       workgroups=p.streamk, workspace=ws)
     if p.splitk is not None:
         import torch
         need = mg.splitk_workspace_bytes(p.dtype, p.M, p.N, p.K, p.splitk, transA=int(p.transA),

@@ -54,6 +54,17 @@ class SplitkPlanInfo(ctypes.Structure):
         return d
 
 
+class StreamkPlanInfo(ctypes.Structure):
+    _fields_ = [("workspace_bytes", ctypes.c_int64), ("workgroups", ctypes.c_int64),
+                ("tiles", ctypes.c_int64), ("iterations", ctypes.c_int64),
+                ("k_per_iteration", ctypes.c_int64), ("variant", VariantInfo)]
+
+    def as_dict(self):
+        d = {f: getattr(self, f) for f, _ in self._fields_}
+        d["variant"] = self.variant.as_dict()
+        return d
+
+
 _lib = None
 
 
@@ -88,6 +99,12 @@ def load():
     lib.mgemm_splitk_plan.restype = i32
     lib.mgemm_splitk_plan.argtypes = [i32, i32, i32, i64, i64, i64, vp, i64, vp, i64, i64,
                                       ctypes.POINTER(SplitkPlanInfo)]
+    lib.gemm_streamk.restype = i32
+    lib.gemm_streamk.argtypes = [i32, i32, i32, i32, i64, i64, i64, f64, vp, i64, vp, i64, f64, vp,
+                                 i64, i64, vp, i64, vp]
+    lib.mgemm_streamk_plan.restype = i32
+    lib.mgemm_streamk_plan.argtypes = [i32, i32, i32, i64, i64, i64, vp, i64, vp, i64, i64,
+                                       ctypes.POINTER(StreamkPlanInfo)]
     lib.gemm_strided_batched_ex.restype = i32
     lib.gemm_strided_batched_ex.argtypes = [i32, i32, i32, i32, i64, i64, i64, f32, vp, i64, i64, vp,
                                             i64, i64, f32, vp, i64, i64, i64, vp]
@@ -299,6 +316,53 @@ def gemm_splitk(in_dtype, c_dtype, transA, transB, M, N, K, alpha, A, lda, B, ld
     st = load().gemm_splitk(dt, ct, int(transA), int(transB), M, N, K, alpha, pa, lda, pb, ldb, beta,
                             pc, ldc, splits, pw, wbytes, _stream(stream, dev))
     _check(st, "gemm_splitk")
+
+
+def streamk_plan(in_dtype, M, N, K, workgroups=0, transA=0, transB=0, A=1 << 20, lda=None,
+                 B=1 << 20, ldb=None):
+    """What gemm_streamk will do (a dict: workspace_bytes, workgroups, tiles, iterations,
+    k_per_iteration and the tile build's variant).  A and B are addresses (ints) or tensors:
+    only their alignment matters."""
+    dt = DTYPE_CODES.get(in_dtype, in_dtype)
+    lda = lda if lda is not None else (M if transA else K)
+    ldb = ldb if ldb is not None else (K if transB else N)
+    pa = A if isinstance(A, int) else A.data_ptr()
+    pb = B if isinstance(B, int) else B.data_ptr()
+    info = StreamkPlanInfo()
+    _check(load().mgemm_streamk_plan(dt, int(transA), int(transB), M, N, K, pa, lda, pb, ldb,
+                                     workgroups, ctypes.byref(info)), "mgemm_streamk_plan")
+    return info.as_dict()
+
+
+def gemm_streamk(in_dtype, c_dtype, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                 workgroups=0, workspace=None, stream=None):
+    """Stream-K GEMM (single matrix).  `workspace` is a device tensor (or int address) of at
+    least streamk_plan(...)["workspace_bytes"] bytes; None allocates one with torch on C's
+    device."""
+    dt = DTYPE_CODES.get(in_dtype, in_dtype)
+    ct = DTYPE_CODES.get(c_dtype, c_dtype)
+    es = ELEM_SIZE[dt]
+    a_rows, a_cols = (K, M) if transA else (M, K)
+    b_rows, b_cols = (N, K) if transB else (K, N)
+    reads = M > 0 and N > 0 and K > 0 and alpha != 0.0
+    pa, _ = _addr(A, _span(a_rows, a_cols, lda) if reads else 0, es, "A")
+    pb, _ = _addr(B, _span(b_rows, b_cols, ldb) if reads else 0, es, "B")
+    pc, dev = _addr(C, _span(M, N, ldc), ELEM_SIZE.get(ct, 4), "C")
+    need = (streamk_plan(dt, M, N, K, workgroups, transA=transA, transB=transB, A=pa or 0, lda=lda,
+                         B=pb or 0, ldb=ldb)["workspace_bytes"] if workgroups >= 0 else 0)
+    if workspace is None and need > 0:
+        import torch
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace is None:
+        pw, wbytes = None, 0
+    elif isinstance(workspace, int):
+        pw, wbytes = workspace, need
+    else:
+        pw, _ = _addr(workspace, 0, workspace.element_size(), "workspace")
+        wbytes = workspace.numel() * workspace.element_size()
+    st = load().gemm_streamk(dt, ct, int(transA), int(transB), M, N, K, alpha, pa, lda, pb, ldb, beta,
+                             pc, ldc, workgroups, pw, wbytes, _stream(stream, dev))
+    _check(st, "gemm_streamk")
 
 
 # --------------------------------------------------------------------------- introspection

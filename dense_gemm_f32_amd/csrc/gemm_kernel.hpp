@@ -78,6 +78,14 @@ struct KernelArgs {
     int fast_ok;      // operand tiles addressable with 32-bit byte offsets
     double alpha_d, beta_d;  // alpha and beta of fp64 GEMM
     int k_tail, tail_batch;  // batch entry tail_batch runs K = k_tail (split-K's last chunk); -1: none
+    // stream-K launches (gemm_sk_kernel, sk_fixup_kernel): every tile is
+    // sk_iters K-iterations of sk_unit elements (the last one may be
+    // shorter); the sk_total = tiles * sk_iters iterations, tile-major, are
+    // shared out evenly over sk_grid workgroups; sk_part holds two partial
+    // tiles per workgroup
+    int sk_iters, sk_unit, sk_grid;
+    int64_t sk_total;
+    void *sk_part;
 };
 
 // ---------------------------------------------------------------------------
@@ -88,13 +96,18 @@ struct KernelArgs {
 // `group_m` tile rows, so the tiles resident on one XCD share A rows and B
 // columns in its L2.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void map_tile(const KernelArgs &p, int &b, int &tm, int &tn)
+__device__ __forceinline__ int logical_wg()
 {
     const int nwg = gridDim.x;
     const int w = blockIdx.x;
     const int q = nwg >> 3, rem = nwg & 7;
     const int x = w & 7, i = w >> 3;
-    const int L = x * q + min(x, rem) + i;
+    return x * q + min(x, rem) + i;
+}
+
+// logical tile L -> (batch, tile row, tile column), grouped order
+__device__ __forceinline__ void tile_coords(const KernelArgs &p, int L, int &b, int &tm, int &tn)
+{
     const int per_b = p.tiles_m * p.tiles_n;
     b = L / per_b;
     const int t = L - b * per_b;
@@ -105,6 +118,11 @@ __device__ __forceinline__ void map_tile(const KernelArgs &p, int &b, int &tm, i
     const int w2 = t - g * width;
     tm = first + w2 % gsz;
     tn = w2 / gsz;
+}
+
+__device__ __forceinline__ void map_tile(const KernelArgs &p, int &b, int &tm, int &tn)
+{
+    tile_coords(p, logical_wg(), b, tm, tn);
 }
 
 template <int BYTES> struct RawOf;
@@ -1332,6 +1350,97 @@ gemm_kernel(KernelArgs p)
         }
         R::run(pk, smem, bidx, m0, n0, acc);
         epilogue<true, R::IL_A, R::IL_B, TM, TN, WTM, WTN, WN, CT>(pk, bidx, m0, n0, acc);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Stream-K: a grid of sk_grid workgroups shares one GEMM evenly, whatever
+// the tile count.  The work is the list of (tile, K-iteration) pairs in
+// tile-major order; logical workgroup L takes pairs [T*L/G, T*(L+1)/G)
+// (T = sk_total, G = sk_grid) and walks them as segments, each within one
+// tile.  A segment that covers a whole tile writes C as gemm_kernel does;
+// any other writes its sums (fp32; int32 for int8 inputs) to one of the
+// workgroup's two partial tiles in sk_part, slot 0 for its first segment
+// and slot 1 for its last, and sk_fixup_kernel then adds the partials of
+// each split tile in K order.  The host keeps G <= T, so every workgroup
+// has at least one pair; nothing waits on another workgroup.
+// ---------------------------------------------------------------------------
+template <typename T, int BM, int BN, int BK, int WM, int WN, bool TA, bool TB, bool VECOK, int PIPE,
+          typename CT>
+__global__ void __launch_bounds__(WM * WN * 64)
+gemm_sk_kernel(KernelArgs p)
+{
+    using R = RegPath<T, BM, BN, BK, WM, WN, TA, TB, VECOK>;
+    using D = DmaPath<T, BM, BN, BK, WM, WN, TA, TB, PIPE>;
+    using PT = typename std::conditional<__is_same(T, int8_t), int32_t, float>::type;
+    constexpr int TM = R::TM, TN = R::TN, WTM = R::WTM, WTN = R::WTN;
+    constexpr bool ALL_DMA = D::DW;
+    constexpr int LDS = ALL_DMA ? D::LDS_BYTES
+                        : (VECOK && D::LDS_BYTES > R::LDS_BYTES) ? D::LDS_BYTES : R::LDS_BYTES;
+    __shared__ __attribute__((aligned(1024))) char smem[LDS];
+    const int L = logical_wg();
+    const int iters = p.sk_iters;
+    const int64_t beg = p.sk_total * L / p.sk_grid, end = p.sk_total * (L + 1) / p.sk_grid;
+    for (int64_t it = beg; it < end;) {
+        const int tile = (int)(it / iters);
+        const int k0 = (int)(it - (int64_t)tile * iters);
+        const int k1 = end - it < iters - k0 ? k0 + (int)(end - it) : iters;
+        int bidx, tm, tn;
+        tile_coords(p, tile, bidx, tm, tn);
+        const int m0 = tm * BM, n0 = tn * BN;
+        const int64_t ko = (int64_t)k0 * p.sk_unit;  // first k of the segment
+        KernelArgs pk = p;
+        pk.A = static_cast<const T *>(p.A) + (TA ? ko * p.lda : ko);
+        pk.B = static_cast<const T *>(p.B) + (TB ? ko : ko * p.ldb);
+        pk.K = k1 == iters ? p.K - (int)ko : (k1 - k0) * p.sk_unit;
+        pk.tail_batch = -1;
+        f32x16 acc[TM][TN];
+#pragma unroll
+        for (int t = 0; t < TM; ++t)
+#pragma unroll
+            for (int u = 0; u < TN; ++u)
+                acc[t][u] = f32x16{};
+        const bool full = m0 + BM <= p.M && n0 + BN <= p.N;
+        bool dma = ALL_DMA;
+        if constexpr (ALL_DMA) {
+            D::template run<true>(pk, smem, bidx, m0, n0, acc);
+        } else {
+            if constexpr (VECOK) {
+                if (pk.fast_ok && pk.K % D::CH == 0) {
+                    dma = true;
+                    if (full && pk.K % D::BK == 0)
+                        D::template run<false>(pk, smem, bidx, m0, n0, acc);
+                    else
+                        D::template run<true>(pk, smem, bidx, m0, n0, acc);
+                }
+            }
+            if (!dma) R::run(pk, smem, bidx, m0, n0, acc);
+        }
+        if (k0 == 0 && k1 == iters) {
+            if (dma) {
+                if (full) epilogue<false, D::IL_A, D::IL_B, TM, TN, WTM, WTN, WN, CT>(pk, bidx, m0, n0, acc);
+                else      epilogue<true, D::IL_A, D::IL_B, TM, TN, WTM, WTN, WN, CT>(pk, bidx, m0, n0, acc);
+            } else {
+                epilogue<true, R::IL_A, R::IL_B, TM, TN, WTM, WTN, WN, CT>(pk, bidx, m0, n0, acc);
+            }
+        } else {
+            // the whole BM x BN tile, row-major, into partial slot (L, first or last)
+            KernelArgs q = p;
+            q.C = static_cast<PT *>(p.sk_part) + ((int64_t)L * 2 + (it == beg ? 0 : 1)) * (BM * BN);
+            q.ldc = BN;
+            q.strideC = 0;
+            q.M = BM;
+            q.N = BN;
+            q.alpha = 1.0f;
+            q.beta = 0.0f;
+            q.alpha_i = 1;
+            q.beta_i = 0;
+            q.c_vec = 1;
+            if (dma) epilogue<false, D::IL_A, D::IL_B, TM, TN, WTM, WTN, WN, PT>(q, 0, 0, 0, acc);
+            else     epilogue<false, R::IL_A, R::IL_B, TM, TN, WTM, WTN, WN, PT>(q, 0, 0, 0, acc);
+        }
+        it += k1 - k0;
+        __syncthreads();  // the next segment refills the LDS stages
     }
 }
 

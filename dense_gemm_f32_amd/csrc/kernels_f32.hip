@@ -19,17 +19,21 @@ const Variant *f32_variants(int *count)
     static const Variant table[] = {
         MGEMM_VARIANT_F32(256, 256, 32, 4, 2, true, "mgemm_f32_256x256x32_w4x2", {13.9f, 0.2344f, 1.10f, 1.0f}),
         MGEMM_VARIANT_F32(256, 256, 32, 2, 2, true, "mgemm_f32_256x256x32_w2x2", {}),
-        MGEMM_VARIANT_F32(128, 128, 32, 2, 2, true, "mgemm_f32_128x128x32_w2x2", {6.6f, 0.0605f, 1.15f, 1.25f}),
+        MGEMM_VARIANT_F32(128, 128, 32, 2, 2, true, "mgemm_f32_128x128x32_w2x2", {6.6f, 0.0605f, 1.15f, 1.25f},
+                          MGEMM_SK(float, 128, 128, 32, 2, 2, true, 1)),
         MGEMM_VARIANT_F32_D(128, 128, 32, 2, 2, false, 4, "mgemm_f32_128x128x32_w2x2_d4_u",
-                            {9.9f, 0.0658f, 1.0f, 1.25f}),
-        MGEMM_VARIANT_F32(128, 128, 32, 2, 2, false, "mgemm_f32_128x128x32_w2x2_u", {}),
+                            {9.9f, 0.0658f, 1.0f, 1.25f}, MGEMM_SK(float, 128, 128, 32, 2, 2, false, 4)),
+        MGEMM_VARIANT_F32(128, 128, 32, 2, 2, false, "mgemm_f32_128x128x32_w2x2_u", {},
+                          MGEMM_SK(float, 128, 128, 32, 2, 2, false, 1)),
         // 64x64: two stages of 32 (one barrier per 16 MFMAs) measured 9-14%
         // faster than four of 16 at 512^3 to 2048^3 (deeper rings of 8 or 16
         // stages gained nothing)
-        MGEMM_VARIANT_F32_D(64, 64, 32, 2, 2, true, 2, "mgemm_f32_64x64x32_w2x2_d2", {2.1f, 0.0166f, 1.5f, 1.4f}),
+        MGEMM_VARIANT_F32_D(64, 64, 32, 2, 2, true, 2, "mgemm_f32_64x64x32_w2x2_d2", {2.1f, 0.0166f, 1.5f, 1.4f},
+                            MGEMM_SK(float, 64, 64, 32, 2, 2, true, 2)),
         MGEMM_VARIANT_F32_D(64, 64, 32, 2, 2, false, 4, "mgemm_f32_64x64x32_w2x2_d4_u",
-                            {2.9f, 0.0185f, 1.0f, 1.6f}),
-        MGEMM_VARIANT_F32(64, 64, 32, 2, 2, false, "mgemm_f32_64x64x32_w2x2_u", {}),
+                            {2.9f, 0.0185f, 1.0f, 1.6f}, MGEMM_SK(float, 64, 64, 32, 2, 2, false, 4)),
+        MGEMM_VARIANT_F32(64, 64, 32, 2, 2, false, "mgemm_f32_64x64x32_w2x2_u", {},
+                          MGEMM_SK(float, 64, 64, 32, 2, 2, false, 1)),
     };
     *count = sizeof(table) / sizeof(table[0]);
     return table;

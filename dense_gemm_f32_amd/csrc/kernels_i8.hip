@@ -20,15 +20,23 @@ const Variant *i8_variants(int *count)
         MGEMM_VARIANT_I8(256, 256, 128, 2, 4, true, 1, "mgemm_i8_256x256x128_w2x4", {}),
         MGEMM_VARIANT_I8(256, 256, 128, 4, 2, true, 1, "mgemm_i8_256x256x128_w4x2", {}),
         // 128x128 with eight waves (four waves measured 3-20% slower)
-        MGEMM_VARIANT_I8(128, 128, 128, 2, 4, true, 1, "mgemm_i8_128x128x128_w2x4", {3.39f, 0.00441f, 1.5f, 1.15f}),
-        MGEMM_VARIANT_I8(128, 128, 128, 2, 4, true, 2, "mgemm_i8_128x128x128_w2x4_d2", {3.59f, 0.00336f, 1.5f, 1.35f}),
+        MGEMM_VARIANT_I8(128, 128, 128, 2, 4, true, 1, "mgemm_i8_128x128x128_w2x4", {3.39f, 0.00441f, 1.5f, 1.15f},
+                         MGEMM_SK_I8(128, 128, 128, 2, 4, true, 1)),
+        MGEMM_VARIANT_I8(128, 128, 128, 2, 4, true, 2, "mgemm_i8_128x128x128_w2x4_d2", {3.59f, 0.00336f, 1.5f, 1.35f},
+                         MGEMM_SK_I8(128, 128, 128, 2, 4, true, 2)),
         // rows 4-byte aligned (and K a multiple of 4): 4-byte copies into LDS, every tile
-        MGEMM_VARIANT_I8(128, 128, 128, 2, 2, false, 4, "mgemm_i8_128x128x128_w2x2_d4_u", {}),
-        MGEMM_VARIANT_I8(128, 128, 128, 2, 2, false, 1, "mgemm_i8_128x128x128_w2x2_u", {}),
-        MGEMM_VARIANT_I8(64, 64, 128, 2, 2, true, 1, "mgemm_i8_64x64x128_w2x2", {0.64f, 0.00195f, 1.5f, 2.6f}),
-        MGEMM_VARIANT_I8(64, 64, 128, 2, 2, true, 2, "mgemm_i8_64x64x128_w2x2_d2", {0.82f, 0.00139f, 1.5f, 3.16f}),
-        MGEMM_VARIANT_I8(64, 64, 128, 2, 2, false, 4, "mgemm_i8_64x64x128_w2x2_d4_u", {}),
-        MGEMM_VARIANT_I8(64, 64, 128, 2, 2, false, 1, "mgemm_i8_64x64x128_w2x2_u", {}),
+        MGEMM_VARIANT_I8(128, 128, 128, 2, 2, false, 4, "mgemm_i8_128x128x128_w2x2_d4_u", {},
+                         MGEMM_SK_I8(128, 128, 128, 2, 2, false, 4)),
+        MGEMM_VARIANT_I8(128, 128, 128, 2, 2, false, 1, "mgemm_i8_128x128x128_w2x2_u", {},
+                         MGEMM_SK_I8(128, 128, 128, 2, 2, false, 1)),
+        MGEMM_VARIANT_I8(64, 64, 128, 2, 2, true, 1, "mgemm_i8_64x64x128_w2x2", {0.64f, 0.00195f, 1.5f, 2.6f},
+                         MGEMM_SK_I8(64, 64, 128, 2, 2, true, 1)),
+        MGEMM_VARIANT_I8(64, 64, 128, 2, 2, true, 2, "mgemm_i8_64x64x128_w2x2_d2", {0.82f, 0.00139f, 1.5f, 3.16f},
+                         MGEMM_SK_I8(64, 64, 128, 2, 2, true, 2)),
+        MGEMM_VARIANT_I8(64, 64, 128, 2, 2, false, 4, "mgemm_i8_64x64x128_w2x2_d4_u", {},
+                         MGEMM_SK_I8(64, 64, 128, 2, 2, false, 4)),
+        MGEMM_VARIANT_I8(64, 64, 128, 2, 2, false, 1, "mgemm_i8_64x64x128_w2x2_u", {},
+                         MGEMM_SK_I8(64, 64, 128, 2, 2, false, 1)),
     };
     *count = sizeof(table) / sizeof(table[0]);
     return table;

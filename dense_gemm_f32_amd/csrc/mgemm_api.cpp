@@ -86,7 +86,7 @@ mgemm_status validate_and_plan(int dtype, int c_dtype, int transA, int transB, i
                                int64_t K, double alpha, const void *A, int64_t lda, int64_t strideA,
                                const void *B, int64_t ldb, int64_t strideB, double beta,
                                const void *C, int64_t ldc, int64_t strideC, int64_t batch,
-                               Plan *plan, int64_t k_total = -1)
+                               Plan *plan, int64_t k_total = -1, bool need_sk = false)
 {
     const bool k_chunks = k_total >= 0;
     if (!is_input_type(dtype)) return MGEMM_INVALID_ARG;
@@ -178,14 +178,17 @@ mgemm_status validate_and_plan(int dtype, int c_dtype, int transA, int transB, i
     int pick = -1;
     if (forced >= 0) {
         const Variant *v = variant_by_id(forced);
-        if (v && (!v->vec || vec_ok) && offsets_ok(*v)) pick = forced - t.first_id;
+        if (v && (!v->vec || vec_ok) && offsets_ok(*v) && (!need_sk || v->sk[transA][transB]))
+            pick = forced - t.first_id;
         // a forced variant the operands do not allow falls back to the automatic choice
     }
     auto wgs_of = [&](const Variant &v) {
         return ((M + v.bm - 1) / v.bm) * ((N + v.bn - 1) / v.bn) * batch;
     };
-    auto eligible = [&](const Variant &v) { return v.vec == vec_ok && offsets_ok(v); };
-    if (pick < 0 && (dtype == MGEMM_F16 || dtype == MGEMM_BF16) && K <= 128) {
+    // need_sk: only builds with a stream-K launch for this transpose
+    auto has_sk = [&](const Variant &v) { return !need_sk || v.sk[transA][transB] != nullptr; };
+    auto eligible = [&](const Variant &v) { return v.vec == vec_ok && offsets_ok(v) && has_sk(v); };
+    if (pick < 0 && !need_sk && (dtype == MGEMM_F16 || dtype == MGEMM_BF16) && K <= 128) {
         // A shallow K (the whole product is a couple of slabs, e.g. attention
         // scores with a 64-wide head) is bound by the C store rather than the
         // matrix cores: the 256x256 tile with 4x2 wavefronts, whose lanes
@@ -209,7 +212,7 @@ mgemm_status validate_and_plan(int dtype, int c_dtype, int transA, int transB, i
         double best_us = 0.0;
         for (int i = 0; i < t.n; ++i) {
             const Variant &v = t.v[i];
-            if (v.cost.tk <= 0.0f || (v.vec && !vec_ok) || !offsets_ok(v)) continue;
+            if (v.cost.tk <= 0.0f || (v.vec && !vec_ok) || !offsets_ok(v) || !has_sk(v)) continue;
             const int64_t rounds = (wgs_of(v) + 255) / 256;
             // the 16-byte DMA path takes every tile when K is a multiple of 16 bytes
             const bool reg_tiles = v.pipe != 4 && (!a.fast_ok || K % (16 / es) != 0);
@@ -412,6 +415,79 @@ mgemm_status run_splitk(int dtype, int c_dtype, int transA, int transB, int64_t 
     return err == hipSuccess ? MGEMM_OK : MGEMM_HIP_ERROR;
 }
 
+// ---------------------------------------------------------------------------
+// Stream-K.  One launch of G workgroups shares the (tile, K-iteration) pairs
+// of the whole product evenly (gemm_sk_kernel), so a tile count that leaves
+// the last round of CUs part-empty costs no idle round; a fix-up launch of
+// one workgroup per tile then completes the tiles that were split between
+// workgroups, from the partial tiles in the caller's workspace
+// ([G][2][bm*bn], fp32; int32 for int8).  Iterations are the split-K
+// granule of K (whole slabs of every build).
+// ---------------------------------------------------------------------------
+constexpr int64_t kStreamkWorkgroups = 512;  // default: two per CU
+
+struct StreamPlan {
+    Plan plan;  // the stream-K launch (kind GEMM), or SCALE / NOTHING
+    int64_t tiles, workspace_bytes;
+};
+
+mgemm_status make_streamk_plan(int dtype, int c_dtype, int transA, int transB, int64_t M, int64_t N,
+                               int64_t K, double alpha, const void *A, int64_t lda, const void *B,
+                               int64_t ldb, double beta, const void *C, int64_t ldc, int64_t workgroups,
+                               void *W, StreamPlan *sp)
+{
+    sp->tiles = 0;
+    sp->workspace_bytes = 0;
+    if (workgroups < 0 || dtype == MGEMM_F64 || c_dtype != partial_dtype(dtype)) return MGEMM_INVALID_ARG;
+    mgemm_status st = validate_and_plan(dtype, c_dtype, transA, transB, M, N, K, alpha, A, lda, 0, B, ldb,
+                                        0, beta, C, ldc, 0, 1, &sp->plan, -1, true);
+    if (st != MGEMM_OK || sp->plan.kind != Plan::GEMM) return st;
+    KernelArgs &a = sp->plan.args;
+    const Variant &v = *sp->plan.var;
+    const int64_t unit = k_granule(dtype);
+    const int64_t iters = (K + unit - 1) / unit;
+    const int64_t tiles = (int64_t)a.tiles_m * a.tiles_n;
+    const int64_t total = tiles * iters;
+    int64_t g = workgroups > 0 ? workgroups : kStreamkWorkgroups;
+    if (g > total) g = total;  // every workgroup gets at least one iteration
+    // the kernels form total * (workgroup + 1) in 64 bits
+    if (g > INT_MAX || iters > INT_MAX || total > ((int64_t)1 << 62) / g) return MGEMM_INVALID_ARG;
+    a.sk_iters = (int)iters;
+    a.sk_unit = (int)unit;
+    a.sk_grid = (int)g;
+    a.sk_total = total;
+    a.sk_part = W;
+    sp->plan.grid = g;
+    sp->tiles = tiles;
+    sp->workspace_bytes = g * 2 * (int64_t)v.bm * v.bn * elem_size(partial_dtype(dtype));
+    return MGEMM_OK;
+}
+
+mgemm_status run_streamk(int dtype, int c_dtype, int transA, int transB, int64_t M, int64_t N, int64_t K,
+                         double alpha, const void *A, int64_t lda, const void *B, int64_t ldb, double beta,
+                         void *C, int64_t ldc, int64_t workgroups, void *workspace, int64_t workspace_bytes,
+                         hipStream_t stream)
+{
+    StreamPlan sp;
+    mgemm_status st = make_streamk_plan(dtype, c_dtype, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta,
+                                        C, ldc, workgroups, workspace, &sp);
+    if (st != MGEMM_OK || sp.plan.kind == Plan::NOTHING) return st;
+    hipError_t err;
+    if (sp.plan.kind == Plan::SCALE) {
+        err = launch_scale_c(c_dtype, C, (int)M, (int)N, ldc, 0, 1, beta, sp.plan.args.beta_i, stream);
+        return err == hipSuccess ? MGEMM_OK : MGEMM_HIP_ERROR;
+    }
+    if (workspace == nullptr || !aligned(workspace, 16) || workspace_bytes < sp.workspace_bytes)
+        return MGEMM_INVALID_ARG;
+    const LaunchFn fn = sp.plan.var->sk[transA][transB];
+    if (fn == nullptr) return MGEMM_INVALID_ARG;
+    err = fn(sp.plan.args, (unsigned)sp.plan.grid, stream);
+    if (err == hipSuccess)
+        err = launch_sk_fixup(c_dtype, sp.plan.args, sp.plan.var->bm, sp.plan.var->bn, (unsigned)sp.tiles,
+                              stream);
+    return err == hipSuccess ? MGEMM_OK : MGEMM_HIP_ERROR;
+}
+
 void fill_info(const Variant &v, int id, mgemm_variant_info *out)
 {
     out->id = id;
@@ -560,6 +636,39 @@ mgemm_status mgemm_splitk_plan(mgemm_dtype in_dtype, mgemm_op transA, mgemm_op t
     if (p.kind == Plan::GEMM) {
         fill_info(*p.var, p.id, &out->variant);
         out->grid = p.grid;
+    }
+    return MGEMM_OK;
+}
+
+mgemm_status gemm_streamk(mgemm_dtype in_dtype, mgemm_dtype c_dtype, mgemm_op transA,
+                          mgemm_op transB, int64_t M, int64_t N, int64_t K, double alpha,
+                          const void *A, int64_t lda, const void *B, int64_t ldb, double beta,
+                          void *C, int64_t ldc, int64_t workgroups, void *workspace,
+                          int64_t workspace_bytes, hipStream_t stream)
+{
+    if ((double)(float)alpha != alpha || (double)(float)beta != beta) return MGEMM_INVALID_ARG;
+    return run_streamk(in_dtype, c_dtype, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                       workgroups, workspace, workspace_bytes, stream);
+}
+
+mgemm_status mgemm_streamk_plan(mgemm_dtype in_dtype, mgemm_op transA, mgemm_op transB, int64_t M,
+                                int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
+                                int64_t ldb, int64_t workgroups, mgemm_streamk_plan_info *out)
+{
+    if (!out) return MGEMM_INVALID_ARG;
+    std::memset(out, 0, sizeof(*out));
+    out->variant.id = -1;
+    StreamPlan sp;
+    const mgemm_status st = make_streamk_plan(in_dtype, partial_dtype(in_dtype), transA, transB, M, N, K, 1.0,
+                                              A, lda, B, ldb, 0.0, kAnyAligned, N, workgroups, nullptr, &sp);
+    if (st != MGEMM_OK) return st;
+    if (sp.plan.kind == Plan::GEMM) {
+        fill_info(*sp.plan.var, sp.plan.id, &out->variant);
+        out->workspace_bytes = sp.workspace_bytes;
+        out->workgroups = sp.plan.grid;
+        out->tiles = sp.tiles;
+        out->iterations = sp.plan.args.sk_iters;
+        out->k_per_iteration = sp.plan.args.sk_unit;
     }
     return MGEMM_OK;
 }

@@ -37,6 +37,7 @@ struct Variant {
     LaunchFn fn[2][2];    // [transA][transB], fp32 C (int32 C for int8, double C for fp64 inputs)
     LaunchFn fn16[2][2];  // [transA][transB], C in the inputs' 16-bit type (16-bit tables only)
     Cost cost;            // zero: no estimate
+    LaunchFn sk[2][2];    // stream-K launch of the same tile, fp32 C (int32 for int8); null: none
 };
 
 template <typename T, int BM, int BN, int BK, int WM, int WN, bool TA, bool TB, bool V, int D, typename CT>
@@ -45,6 +46,15 @@ hipError_t launch_gemm(const KernelArgs &a, unsigned grid, hipStream_t s)
     KernelArgs copy = a;
     void *args[] = {&copy};
     return hipLaunchKernel(reinterpret_cast<const void *>(&gemm_kernel<T, BM, BN, BK, WM, WN, TA, TB, V, D, CT>),
+                           dim3(grid), dim3(WM * WN * 64), args, 0, s);
+}
+
+template <typename T, int BM, int BN, int BK, int WM, int WN, bool TA, bool TB, bool V, int D, typename CT>
+hipError_t launch_gemm_sk(const KernelArgs &a, unsigned grid, hipStream_t s)
+{
+    KernelArgs copy = a;
+    void *args[] = {&copy};
+    return hipLaunchKernel(reinterpret_cast<const void *>(&gemm_sk_kernel<T, BM, BN, BK, WM, WN, TA, TB, V, D, CT>),
                            dim3(grid), dim3(WM * WN * 64), args, 0, s);
 }
 
@@ -73,7 +83,16 @@ hipError_t launch_gemm_f64(const KernelArgs &a, unsigned grid, hipStream_t s)
       launch_gemm<T, BM, BN, BK, WM, WN, true, true, V, D, CT>}}
 
 // The trailing argument of each macro is the build's Cost, {t0, tk, reg, solo}
-// ({}: no estimate).
+// ({}: no estimate), optionally followed by its stream-K launchers
+// (MGEMM_SK or MGEMM_SK_I8; omitted: none).
+#define MGEMM_SK(T, BM, BN, BK, WM, WN, V, D)                                                \
+    {{launch_gemm_sk<T, BM, BN, BK, WM, WN, false, false, V, D, float>,                      \
+      launch_gemm_sk<T, BM, BN, BK, WM, WN, false, true, V, D, float>},                      \
+     {launch_gemm_sk<T, BM, BN, BK, WM, WN, true, false, V, D, float>,                       \
+      launch_gemm_sk<T, BM, BN, BK, WM, WN, true, true, V, D, float>}}
+#define MGEMM_SK_I8(BM, BN, BK, WM, WN, V, D)                                                 \
+    {{nullptr, launch_gemm_sk<int8_t, BM, BN, BK, WM, WN, false, true, V, D, int32_t>},       \
+     {nullptr, nullptr}}
 // fp32 inputs: fp32 C only
 #define MGEMM_VARIANT_F32_D(BM, BN, BK, WM, WN, V, D, NAME, ...)                              \
     {0, BM, BN, BK, WM, WN, V, D, NAME, MGEMM_LAUNCHERS(float, BM, BN, BK, WM, WN, V, D, float), \
@@ -106,6 +125,8 @@ const Variant *f64_variants(int *count);
 
 hipError_t launch_scale_c(int c_dtype, void *C, int M, int N, int64_t ldc, int64_t strideC, int batch,
                           double beta, int beta_i, hipStream_t s);
+
+hipError_t launch_sk_fixup(int c_dtype, const KernelArgs &a, int bm, int bn, unsigned tiles, hipStream_t s);
 
 hipError_t launch_splitk_reduce(int c_dtype, const void *W, int splits, int M, int N, void *C,
                                 int64_t ldc, double alpha, double beta, int alpha_i, int beta_i,

@@ -67,6 +67,7 @@ class Problem:
     c_dtype: str = "f32"       # C's type: "f32", the operand type for 16-bit output, "i32" for
                                # i8; double operands always take "f64"
     splitk: Optional[int] = None   # None: one-pass kernels; n: split-K with n chunks (0: automatic)
+    streamk: Optional[int] = None  # None: not stream-K; n: stream-K over n workgroups (0: default)
 
     def __post_init__(self):
         if self.dtype == "f64":
@@ -207,6 +208,14 @@ def sgemm_ragged_splitk() -> Problem:
     return p
 
 
+def sgemm_ragged_streamk() -> Problem:
+    """The ragged SGEMM through stream-K with the default 512 workgroups (two per CU) sharing
+    the 272 tiles' 32 K-iterations each, then the fix-up of the split tiles."""
+    p = sgemm_ragged()
+    p.streamk = 0
+    return p
+
+
 def gemm16_8192(dtype: str = "bf16") -> Problem:
     """8192^3 with bf16 (or fp16) N(0,1) operands, fp32 accumulate and fp32 C."""
     return Problem(dtype, 8192, 8192, 8192, dist="normal", seed=1004)
@@ -245,6 +254,7 @@ WORKLOADS = {
     "sgemm_4096": sgemm_4096,
     "sgemm_ragged": sgemm_ragged,
     "sgemm_ragged_splitk": sgemm_ragged_splitk,
+    "sgemm_ragged_streamk": sgemm_ragged_streamk,
     "gemm_bf16_8192": lambda: gemm16_8192("bf16"),
     "gemm_f16_8192": lambda: gemm16_8192("f16"),
     "qkt_batched": qkt_batched,

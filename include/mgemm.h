@@ -324,6 +324,69 @@ mgemm_status mgemm_splitk_plan(mgemm_dtype in_dtype, mgemm_op transA, mgemm_op t
                                const void *A, int64_t lda, const void *B, int64_t ldb,
                                int64_t splits, mgemm_splitk_plan_info *out);
 
+/*
+ * Stream-K GEMM: the same C = alpha * op(A) * op(B) + beta * C ("Sgemm
+ * [128,128,8]" (jianshu), design comment and host_gemm), with the work cut
+ * so that every workgroup gets an equal share whatever the tile count.  The
+ * pages fix a tile per kernel ("cuda11/matmul" tutorial, sections V1-V3);
+ * on 256 CUs a tile grid that is not a multiple of the CU count leaves the
+ * last round part-empty (1000x1027: 272 tiles of 64x64), which is the case
+ * this entry point is for.  The product is the list of (output tile, K
+ * iteration) pairs; one launch of `workgroups` workgroups takes equal
+ * consecutive ranges of it, writing whole tiles straight to C and the tiles
+ * it splits as partial sums to the workspace; a second launch adds each
+ * split tile's partials in ascending K (deterministic), applies alpha and
+ * beta and writes C.  Nothing waits on another workgroup.
+ *   in_dtype  MGEMM_F32, MGEMM_F16, MGEMM_BF16 (then c_dtype MGEMM_F32) or
+ *          MGEMM_I8 (c_dtype MGEMM_I32, transA N, transB T); other pairs
+ *          and MGEMM_F64 give MGEMM_INVALID_ARG.
+ *   alpha, beta  double, exactly representable as float (int8: integral,
+ *          as gemm_strided_batched_ex).
+ *   workgroups  n > 0: n workgroups (at most one per (tile, iteration)
+ *          pair); 0: 512, two per CU.
+ *   workspace, workspace_bytes  device scratch owned by the caller, 16-byte
+ *          aligned, at least mgemm_streamk_plan(...).workspace_bytes (0 when
+ *          nothing is launched, e.g. M, N or K zero or alpha zero; then it
+ *          may be NULL).  Two partial tiles per workgroup, fp32 (int32 for
+ *          int8), overwritten.  Calls that share a workspace must be ordered
+ *          on one stream.
+ * A and B are read, C is read only when beta != 0; layouts, leading
+ * dimensions and quick returns are those of gemm_strided_batched_ex with
+ * batch 1.  Results differ from the one-pass kernels only by fp32 summation
+ * order where a tile is split, and are identical for integer-valued inputs
+ * whose sums are exact.
+ * Errors: as gemm_strided_batched_ex, plus MGEMM_INVALID_ARG for
+ * workgroups < 0 or a missing, misaligned or short workspace; nothing is
+ * launched then.
+ */
+mgemm_status gemm_streamk(mgemm_dtype in_dtype, mgemm_dtype c_dtype,
+                          mgemm_op transA, mgemm_op transB,
+                          int64_t M, int64_t N, int64_t K, double alpha,
+                          const void *A, int64_t lda,
+                          const void *B, int64_t ldb,
+                          double beta, void *C, int64_t ldc,
+                          int64_t workgroups, void *workspace, int64_t workspace_bytes,
+                          hipStream_t stream);
+
+/* What gemm_streamk will do for these arguments. */
+typedef struct {
+    int64_t workspace_bytes;   /* workspace the call needs (0: nothing launched) */
+    int64_t workgroups;        /* workgroups of the stream-K launch */
+    int64_t tiles;             /* output tiles (the fix-up launch's workgroups) */
+    int64_t iterations;        /* K-iterations per tile */
+    int64_t k_per_iteration;   /* K elements per iteration (the last may be shorter) */
+    mgemm_variant_info variant;  /* tile build (id -1: none) */
+} mgemm_streamk_plan_info;
+
+/* Fill *out with gemm_streamk's plan (A and B stand for the operand
+ * addresses: their alignment matters, their contents do not).  Pure host;
+ * MGEMM_INVALID_ARG for workgroups < 0, an in_dtype without stream-K, or
+ * out == NULL. */
+mgemm_status mgemm_streamk_plan(mgemm_dtype in_dtype, mgemm_op transA, mgemm_op transB,
+                                int64_t M, int64_t N, int64_t K,
+                                const void *A, int64_t lda, const void *B, int64_t ldb,
+                                int64_t workgroups, mgemm_streamk_plan_info *out);
+
 #ifdef __cplusplus
 }
 #endif

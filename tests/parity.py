@@ -41,7 +41,12 @@ class Run:
 
     def launch(self, stream=None, workspace=None):
         p = self.p
-        if p.splitk is not None:
+        if p.streamk is not None:
+            assert p.batch == 1
+            mg.gemm_streamk(p.dtype, p.c_dtype, int(p.transA), int(p.transB), p.M, p.N, p.K,
+                            p.alpha, self.dA, p.lda, self.dB, p.ldb, p.beta, self.dC, p.ldc,
+                            workgroups=p.streamk, workspace=workspace, stream=stream)
+        elif p.splitk is not None:
             assert p.batch == 1
             mg.gemm_splitk(p.dtype, p.c_dtype, int(p.transA), int(p.transB), p.M, p.N, p.K, p.alpha,
                            self.dA, p.lda, self.dB, p.ldb, p.beta, self.dC, p.ldc, splits=p.splitk,

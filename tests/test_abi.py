@@ -353,6 +353,37 @@ def test_splitk_rules_without_a_gpu():
     assert lib.mgemm_splitk_plan(0, 0, 0, 4, 4, 4, ALIGNED, 4, ALIGNED, 4, 0, None) == 1
 
 
+def test_streamk_plans():
+    # the ragged shape: 16 x 17 tiles of the 4-byte-copy 64x64 build, 32 iterations of 32,
+    # shared by 512 workgroups (two per CU), two fp32 partial tiles each
+    p = mg.streamk_plan("f32", 1000, 1027, 999, lda=999, ldb=1027)
+    assert p["variant"]["name"] == "mgemm_f32_64x64x32_w2x2_d4_u"
+    assert (p["tiles"], p["iterations"], p["k_per_iteration"], p["workgroups"]) == (272, 32, 32, 512)
+    assert p["workspace_bytes"] == 512 * 2 * 64 * 64 * 4
+    # an explicit count, and the cap of one workgroup per (tile, iteration) pair
+    assert mg.streamk_plan("f32", 1000, 1027, 999, 37, lda=999, ldb=1027)["workgroups"] == 37
+    one = mg.streamk_plan("f32", 64, 64, 300, 1000)
+    assert (one["tiles"], one["iterations"], one["workgroups"]) == (1, 10, 10)
+    # the K-iteration is the type's K granule; int8 takes N x T only
+    assert mg.streamk_plan("bf16", 500, 500, 500)["k_per_iteration"] == 64
+    i8 = mg.streamk_plan("i8", 1000, 1027, 999, transB=1)
+    assert i8["k_per_iteration"] == 128 and i8["workspace_bytes"] == 512 * 2 * i8["variant"]["block_m"] * i8["variant"]["block_n"] * 4
+    # rows of any alignment have a stream-K build (the register path)
+    assert mg.streamk_plan("bf16", 1000, 1027, 999, lda=999, ldb=1027)["variant"]["name"].endswith("_u")
+    # no tile of 256x256 takes stream-K: a large aligned problem gets a smaller build
+    assert mg.streamk_plan("f32", 4096, 4096, 4096)["variant"]["block_m"] <= 128
+    # nothing launched: no workspace
+    for M, K in ((0, 64), (64, 0)):
+        z = mg.streamk_plan("f32", M, 64, K, lda=max(K, 1))
+        assert z["workspace_bytes"] == 0 and z["variant"]["id"] == -1
+    with pytest.raises(mg.MgemmError):
+        mg.streamk_plan("f64", 100, 100, 100)
+    with pytest.raises(mg.MgemmError):
+        mg.streamk_plan("f32", 100, 100, 100, -1)
+    with pytest.raises(mg.MgemmError):
+        mg.streamk_plan("i8", 100, 100, 128)   # int8 needs transB
+
+
 def test_splitk_automatic_plans():
     # a small grid of unaligned tiles: three chunks of all of C
     p = mg.splitk_plan("f32", 1000, 1027, 999, 0, lda=999, ldb=1027)

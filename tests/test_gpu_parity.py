@@ -555,6 +555,53 @@ def test_splitk_auto_on_a_deep_k_shape():
     full_check(p, exact=True, what="256x256x8192 automatic split-K")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "i8"])
+def test_streamk_exact(dtype):
+    # integer-valued inputs: bit-exact however the tiles are split between
+    # workgroups; shapes with edge tiles and K tails, the 4-byte-copy builds
+    # (odd leading dimensions), one workgroup, and one workgroup per
+    # (tile, iteration) pair
+    i8 = dtype == "i8"
+    trans = [(False, True)] if i8 else [(False, False), (False, True), (True, False), (True, True)]
+    cases = [((1000, 1027, 999), 0), ((1000, 1027, 999), 37), ((150, 133, 700), 0),
+             ((70, 300, 1111), 5), ((200, 190, 2050), 1), ((64, 64, 300), None)]
+    for n, (tA, tB) in enumerate(trans):
+        for (M, N, K), wgs in cases[n % 2::2] if not i8 else cases:
+            plan = mg.streamk_plan(dtype, M, N, K, 0, transA=int(tA), transB=int(tB))
+            if wgs is None:   # one workgroup per (tile, iteration) pair
+                wgs = plan["tiles"] * plan["iterations"]
+            ab = (3.0, -2.0) if i8 else (1.5, 0.5)
+            p = wl.Problem(dtype, M, N, K, transA=tA, transB=tB, alpha=ab[0], beta=ab[1], dist="int",
+                           int_lo=-128 if i8 else -20, int_hi=127 if i8 else 20, c_dist="int",
+                           c_dtype="i32" if i8 else "f32", seed=131 + n, streamk=wgs)
+            plan = mg.streamk_plan(dtype, M, N, K, wgs, transA=int(tA), transB=int(tB), lda=p.lda,
+                                   ldb=p.ldb)
+            full_check(p, exact=True, what=f"stream-K {dtype} tA={int(tA)} tB={int(tB)} "
+                       f"{plan['variant']['name']} x{plan['workgroups']} over {plan['tiles']} tiles "
+                       f"of {plan['iterations']} iterations")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_streamk_float_inputs_within_tolerance(dtype):
+    p = wl.Problem(dtype, 1000, 1027, 999, alpha=0.75, beta=-1.25,
+                   dist="normal" if dtype == "bf16" else "uniform", c_dist="uniform", seed=141,
+                   streamk=0)
+    full_check(p, what=f"stream-K {dtype} 1000x1027x999")
+
+
+def test_streamk_quick_returns_and_shared_workspace():
+    for alpha, K in ((0.0, 512), (1.0, 0)):
+        p = wl.Problem("f32", 90, 70, K, alpha=alpha, beta=-0.5, dist="uniform", seed=142, streamk=0)
+        full_check(p, exact=True, what=f"stream-K alpha={alpha} K={K} (nothing but beta*C)")
+    ws = torch.empty(mg.streamk_plan("f32", 300, 260, 1500, 100)["workspace_bytes"],
+                     dtype=torch.uint8, device="cuda")
+    for q in (wl.Problem("f32", 300, 260, 1500, dist="int", int_lo=-9, int_hi=9, seed=143, streamk=100),
+              wl.Problem("f32", 120, 77, 900, dist="int", int_lo=-9, int_hi=9, seed=144, streamk=60)):
+        r = Run(q)
+        r.launch(workspace=ws)
+        check_exact(r.result(), r.oracle_full(), f"stream-K {q.M}x{q.N}x{q.K} in a shared workspace")
+
+
 # ------------------------------------------------------------------ shapes from the pages
 
 def test_csdn_ragged_integer_example():
