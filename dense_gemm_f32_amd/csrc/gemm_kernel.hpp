@@ -693,6 +693,9 @@ struct RegPath {
 //      slab placed before the MFMAs of its last k-group so that the next
 //      slab's first fragment reads overlap them.
 //   2  the same with BK = BKR, NS = 2 (one slab ahead, half the barriers).
+//   3  one stage of BK = BKR, for K <= BKR only (one slab, e.g. attention
+//      scores over a 64-wide head): half the LDS, so that two workgroups
+//      share a CU and one's C stores overlap the other's loads;
 //   4  4-byte copies, BK = BKR, NS = 2, for every tile of a problem whose
 //      rows are 4-byte aligned (and, for 8/16-bit elements, whose K is a
 //      multiple of the 4-byte piece): each lane copies one piece, and lanes
@@ -726,8 +729,9 @@ struct DmaPath {
     static constexpr int WTM = BM / WM, WTN = BN / WN;
     static constexpr int TM = WTM / 32, TN = WTN / 32;
     static constexpr bool DW = PIPE == 4;  // 4-byte copies, every tile
-    static constexpr int BK = PIPE == 2 || DW ? BKR : BKR / 2;
-    static constexpr int NS = PIPE == 1 ? 4 : 2;
+    static constexpr bool ONE = PIPE == 3;  // one stage, one slab (K <= BKR)
+    static constexpr int BK = PIPE == 2 || DW || ONE ? BKR : BKR / 2;
+    static constexpr int NS = PIPE == 1 ? 4 : ONE ? 1 : 2;
     static constexpr int RB = BK * ES;          // K-contiguous row bytes
     static_assert(RB == 64 || RB == 128, "64- or 128-byte K-contiguous rows");
     static constexpr int CPR = RB / 16;         // 16-byte chunks per row
@@ -1069,7 +1073,8 @@ struct DmaPath {
         };
         int kt = 0;
         // steady state: slab kt+NS exists; at the wait, slabs kt+2 .. kt+NS-1
-        // may still be in flight
+        // may still be in flight (a one-stage build has a single slab)
+        if constexpr (NS >= 2)
         for (; kt + NS < nk; ++kt) {
             // A wave multiplying a slab outranks one at its copies and waits
             // (two waves share each SIMD).  Measured in a same-box A/B: fp32
@@ -1102,11 +1107,13 @@ struct DmaPath {
         // last slabs: everything already issued
         for (; kt < nk; ++kt) {
             body_head(kt);
-            if (kt + 1 < nk) {
-                const int ahead = nk - kt - 2;  // slabs after kt+1 still possibly in flight
-                wait_ahead_upto<NS - 2>(ahead);
-                lds_barrier();
-                frags(kt + 1, 0, f[G & 1]);
+            if constexpr (NS >= 2) {
+                if (kt + 1 < nk) {
+                    const int ahead = nk - kt - 2;  // slabs after kt+1 still possibly in flight
+                    wait_ahead_upto<NS - 2>(ahead);
+                    lds_barrier();
+                    frags(kt + 1, 0, f[G & 1]);
+                }
             }
             f[(G - 1) & 1].mfmas(acc);
         }
@@ -1312,7 +1319,9 @@ gemm_kernel(KernelArgs p)
     using R = RegPath<T, BM, BN, BK, WM, WN, TA, TB, VECOK>;
     using D = DmaPath<T, BM, BN, BK, WM, WN, TA, TB, PIPE>;
     constexpr int TM = R::TM, TN = R::TN, WTM = R::WTM, WTN = R::WTN;
-    constexpr bool ALL_DMA = D::DW;  // 4-byte copies serve every tile: no register path
+    // 4-byte copies serve every tile, and one-stage builds run only where the
+    // DMA path serves every tile: no register path
+    constexpr bool ALL_DMA = D::DW || D::ONE;
     constexpr int LDS = ALL_DMA ? D::LDS_BYTES
                         : (VECOK && D::LDS_BYTES > R::LDS_BYTES) ? D::LDS_BYTES : R::LDS_BYTES;
     __shared__ __attribute__((aligned(1024))) char smem[LDS];
@@ -1328,8 +1337,14 @@ gemm_kernel(KernelArgs p)
         for (int u = 0; u < TN; ++u)
             acc[t][u] = f32x16{};
     if constexpr (ALL_DMA) {
-        D::template run<true>(pk, smem, bidx, m0, n0, acc);
-        if (m0 + BM <= pk.M && n0 + BN <= pk.N)
+        const bool full = m0 + BM <= pk.M && n0 + BN <= pk.N;
+        if constexpr (D::ONE) {
+            if (full && pk.K == D::BK) D::template run<false>(pk, smem, bidx, m0, n0, acc);
+            else                       D::template run<true>(pk, smem, bidx, m0, n0, acc);
+        } else {
+            D::template run<true>(pk, smem, bidx, m0, n0, acc);
+        }
+        if (full)
             epilogue<false, D::IL_A, D::IL_B, TM, TN, WTM, WTN, WN, CT>(pk, bidx, m0, n0, acc);
         else
             epilogue<true, D::IL_A, D::IL_B, TM, TN, WTM, WTN, WN, CT>(pk, bidx, m0, n0, acc);

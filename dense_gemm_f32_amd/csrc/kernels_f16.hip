@@ -21,6 +21,8 @@ const Variant *f16_variants(int *count)
     static const Variant table[] = {
         MGEMM_VARIANT_D(_Float16, 1, 256, 256, 64, 2, 4, true, 2, "mgemm_f16_256x256x64_w2x4_d2", {10.7f, 0.0219f, 1.6f, 1.0f}),
         MGEMM_VARIANT(_Float16, 1, 256, 256, 64, 2, 4, true, "mgemm_f16_256x256x64_w2x4", {}),
+        // one LDS stage for K <= 64 (attention scores): two workgroups per CU
+        MGEMM_VARIANT_D(_Float16, 1, 256, 256, 64, 4, 2, true, 3, "mgemm_f16_256x256x64_w4x2_s1", {}),
         MGEMM_VARIANT(_Float16, 1, 256, 256, 64, 4, 2, true, "mgemm_f16_256x256x64_w4x2", {}),
         MGEMM_VARIANT(_Float16, 1, 256, 256, 64, 2, 2, true, "mgemm_f16_256x256x64_w2x2", {}),
         MGEMM_VARIANT_D(_Float16, 1, 256, 256, 64, 2, 2, true, 2, "mgemm_f16_256x256x64_w2x2_d2", {}),

@@ -172,7 +172,12 @@ mgemm_status validate_and_plan(int dtype, int c_dtype, int transA, int transB, i
     const int64_t piece = es >= 4 ? 1 : 4 / es, k_all = k_chunks ? k_total : K;
     const bool dw_rows = es >= 4 || (aligned(A, 4) && aligned(B, 4) && lda % piece == 0 && ldb % piece == 0 &&
                                      strideA % piece == 0 && strideB % piece == 0 && k_all % piece == 0);
-    auto offsets_ok = [&](const Variant &v) { return v.pipe != 4 || (a.fast_ok && dw_rows); };
+    // One-stage builds (pipe 3) hold a single K-slab and have no register
+    // path: K at most their slab, a multiple of 16 bytes, 32-bit offsets.
+    auto offsets_ok = [&](const Variant &v) {
+        return (v.pipe != 4 || (a.fast_ok && dw_rows)) &&
+               (v.pipe != 3 || (a.fast_ok && K <= v.bk && K % (16 / es) == 0));
+    };
     Table t = table_for(dtype);
     const int forced = g_forced[dtype].load();
     int pick = -1;
@@ -501,7 +506,7 @@ void fill_info(const Variant &v, int id, mgemm_variant_info *out)
     // two stages of bk in either path (fp64 rows carry a 2-element pad,
     // gemm_f64.hpp; the DMA path's PIPE 1 has four of bk/2)
     const int pad = v.dtype == MGEMM_F64 ? 2 : 0;
-    out->lds_bytes = 2 * (v.bm + v.bn + 2 * pad) * v.bk * elem_size(v.dtype);
+    out->lds_bytes = (v.pipe == 3 ? 1 : 2) * (v.bm + v.bn + 2 * pad) * v.bk * elem_size(v.dtype);
     out->pipe = v.pipe;
     std::snprintf(out->name, sizeof(out->name), "%s", v.name);
 }

@@ -32,7 +32,8 @@ struct Variant {
     int wm, wn;           // wavefront grid
     bool vec;             // needs 16-byte aligned A/B rows (dwordx4 loads)
     int pipe;             // DMA-path schedule (1: 4 stages of bk/2, 2: 2 stages of bk,
-                          // 4: 4-byte copies, 2 stages of bk, every tile)
+                          // 3: 1 stage of bk, K <= bk only, 4: 4-byte copies, 2 stages
+                          // of bk, every tile)
     const char *name;
     LaunchFn fn[2][2];    // [transA][transB], fp32 C (int32 C for int8, double C for fp64 inputs)
     LaunchFn fn16[2][2];  // [transA][transB], C in the inputs' 16-bit type (16-bit tables only)

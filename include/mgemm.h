@@ -260,7 +260,8 @@ typedef struct {
     int threads;       /* workgroup size */
     int lds_bytes;     /* LDS per workgroup */
     int pipe;          /* DMA-path schedule: 1 = four LDS stages of
-                          block_k/2, 2 = two stages of block_k, 4 = 4-byte
+                          block_k/2, 2 = two stages of block_k, 3 = one
+                          stage of block_k (K <= block_k only), 4 = 4-byte
                           copies in two stages of block_k (every tile) */
     char name[64];     /* kernel family name, e.g. "mgemm_f32_256x256x32_w2x2" */
 } mgemm_variant_info;

@@ -63,7 +63,7 @@ def test_variant_table():
         assert v["id"] == i
         assert v["threads"] == v["waves_m"] * v["waves_n"] * 64
         assert v["lds_bytes"] <= 160 * 1024
-        assert v["pipe"] in (1, 2, 4)
+        assert v["pipe"] in (1, 2, 3, 4)
         assert v["name"].startswith("mgemm_")
     assert {v["dtype"] for v in vs} == {0, 1, 2, 3, 5}
     info = _lib.VariantInfo()
@@ -200,8 +200,11 @@ def test_other_types_choice_by_estimated_time():
     # a shallow K is store-bound: the attention-score batch takes the 256x256
     # tile whose lanes store four adjacent elements, with either C type
     qkt = dict(tB=1, lda=64, ldb=64, batch=128, strideA=65536, strideB=65536, strideC=1048576)
-    assert name("f16", 1024, 1024, 64, **qkt) == "mgemm_f16_256x256x64_w4x2"
-    assert name("f16", 1024, 1024, 64, c_dtype="f16", **qkt) == "mgemm_f16_256x256x64_w4x2"
+    # the attention-score batch (K = 64, one slab): the one-stage build; K = 128: two stages
+    assert name("f16", 1024, 1024, 64, **qkt) == "mgemm_f16_256x256x64_w4x2_s1"
+    assert name("f16", 1024, 1024, 64, c_dtype="f16", **qkt) == "mgemm_f16_256x256x64_w4x2_s1"
+    qkt128 = dict(qkt, lda=128, ldb=128, strideA=131072, strideB=131072)
+    assert name("f16", 1024, 1024, 128, **qkt128) == "mgemm_f16_256x256x64_w4x2"
     # mgemm_select_ex checks C's type like the entry points do
     with pytest.raises(mg.MgemmError):
         sel("f16", M=64, N=64, K=64, c_dtype="bf16")

@@ -99,9 +99,12 @@ def _assert_selected(p, v):
     assert info["name"] == v["name"], (info["name"], v["name"])
 
 
-def variants_of(dtype):
+def variants_of(dtype, one_stage=False):
+    """The dtype's builds; the one-stage ones (pipe 3, K of one slab only) when asked."""
     code = {"f32": 0, "f16": 1, "bf16": 2, "i8": 3, "f64": 5}[dtype]
-    return [v for v in mg.variants() if v["dtype"] == code] if torch.cuda.is_available() else []
+    if not torch.cuda.is_available():
+        return []
+    return [v for v in mg.variants() if v["dtype"] == code and (v["pipe"] == 3) == one_stage]
 
 
 # ------------------------------------------------------------------ every variant, every op
@@ -600,6 +603,36 @@ def test_streamk_quick_returns_and_shared_workspace():
         r = Run(q)
         r.launch(workspace=ws)
         check_exact(r.result(), r.oracle_full(), f"stream-K {q.M}x{q.N}x{q.K} in a shared workspace")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_one_stage_builds_shallow_k_exact(dtype):
+    # the one-stage 256x256 builds (K of one slab at most): full and edge tiles, a K tail
+    # inside the slab, every transpose, fp32 and 16-bit C, batches; integer data, so each
+    # result is the exact sum rounded once to C's type
+    builds = variants_of(dtype, one_stage=True)
+    assert builds
+    for v in builds:
+        mg.force_variant(dtype, v["id"])
+        for n, (M, N, K, batch) in enumerate(((512, 768, 64, 2), (300, 260, 40, 3), (256, 256, 8, 1),
+                                              (1000, 520, 56, 1))):
+            for tA, tB in itertools.product((False, True), repeat=2):
+                for c_dtype in ("f32", dtype):
+                    a_cols = M if tA else K
+                    b_cols = K if tB else N
+                    p = wl.Problem(dtype, M, N, K, transA=tA, transB=tB, batch=batch, alpha=0.5,
+                                   beta=0.0 if n % 2 else 2.0, lda=_round8(a_cols), ldb=_round8(b_cols),
+                                   dist="int", int_lo=-4, int_hi=4, c_dist="int", c_dtype=c_dtype,
+                                   pad_value=float("nan"), seed=151 + n)
+                    _assert_selected(p, v)
+                    full_check(p, exact=True, what=f"{v['name']} -> {c_dtype}")
+    # the automatic choice takes it for the attention-score batch, and not past one slab
+    info, _ = mg.select(dtype, 0, 1, 1024, 1024, 64, 0.125, 1 << 20, 64, 65536, 1 << 20, 64, 65536,
+                        0.0, 1 << 20, 1024, 1 << 20, 128)
+    assert info["name"].endswith("_w4x2_s1"), info["name"]
+    info, _ = mg.select(dtype, 0, 1, 1024, 1024, 128, 0.125, 1 << 20, 128, 131072, 1 << 20, 128,
+                        131072, 0.0, 1 << 20, 1024, 1 << 20, 128)
+    assert info["name"].endswith("_w4x2"), info["name"]
 
 
 # ------------------------------------------------------------------ shapes from the pages
