@@ -320,6 +320,29 @@ def test_binding_refuses_host_tensors_and_short_buffers():
         mg.gemm_f32(0, 0, 4, 4, 4, 1.0, a, 4, a, 4, 0.0, a, 4)
 
 
+def test_streamk_rules_without_a_gpu():
+    lib = mg.load()
+    sk = lib.gemm_streamk
+
+    def call(in_dt=0, c_dt=0, M=64, N=64, K=1024, alpha=1.0, beta=0.0, wgs=0, ws=ALIGNED,
+             wbytes=1 << 30, tB=0):
+        return sk(in_dt, c_dt, 0, tB, M, N, K, alpha, ALIGNED, K, ALIGNED, K if tB else N, beta,
+                  ALIGNED, N, wgs, ws, wbytes, None)
+    assert call(wgs=-1) == 1
+    assert call(ws=None) == 1                                  # a launch needs the workspace
+    assert call(ws=ALIGNED + 8) == 1                           # 16-byte alignment
+    need = mg.streamk_plan("f32", 64, 64, 1024)["workspace_bytes"]
+    assert need == 32 * 2 * 64 * 64 * 4                        # 1 tile x 32 iterations: 32 workgroups
+    assert call(wbytes=need - 1) == 1
+    assert call(alpha=1.0 + 2 ** -40) == 1                     # not a float
+    assert call(in_dt=1, c_dt=1) == 1                          # fp32 C only for 16-bit inputs
+    assert call(in_dt=3, c_dt=4) == 1                          # int8 takes N x T only
+    assert call(in_dt=5, c_dt=5) == 1                          # no fp64 stream-K
+    # nothing to do: OK without a workspace
+    for in_dt, c_dt, tB in ((0, 0, 0), (2, 0, 0), (3, 4, 1)):
+        assert call(in_dt, c_dt, M=0, ws=None, wbytes=0, tB=tB) == 0
+
+
 def test_splitk_rules_without_a_gpu():
     lib = mg.load()
     sk = lib.gemm_splitk
