@@ -795,7 +795,7 @@ def test_runs_on_a_side_stream():
 
 def test_launches_replay_in_a_hip_graph():
     # The library only enqueues kernels on the caller's stream, so a capture
-    # records them.  Each replay is checked against the eager result, with
+    # records them (split-K's and stream-K's two kernels included).  Each replay is checked against the eager result, with
     # eager work and synchronisation between replays.
     p = wl.Problem("f32", 256, 256, 256, alpha=1.5, beta=0.5, dist="int", int_lo=-8, int_hi=8,
                    c_dist="int", seed=120)
@@ -810,6 +810,13 @@ def test_launches_replay_in_a_hip_graph():
                      device="cuda")
     rq.launch(workspace=ws)
     eager_q = rq.result()
+    z = wl.Problem("f32", 1000, 1027, 999, dist="int", int_lo=-8, int_hi=8, seed=122, streamk=0)
+    rz = Run(z)
+    wz = torch.empty(mg.streamk_plan("f32", 1000, 1027, 999, 0, lda=z.lda, ldb=z.ldb)["workspace_bytes"],
+                     dtype=torch.uint8, device="cuda")
+    rz.launch(workspace=wz)
+    eager_z = rz.result()
+    check_exact(eager_z, rz.oracle_full(), "eager stream-K 1000x1027x999")
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):          # capture on a side stream, as torch requires
@@ -817,10 +824,12 @@ def test_launches_replay_in_a_hip_graph():
         with torch.cuda.graph(g, stream=side):
             r.launch()
             rq.launch(workspace=ws)
+            rz.launch(workspace=wz)
     torch.cuda.current_stream().wait_stream(side)
     for rep in range(3):
         r.dCbuf.copy_(c0)                  # beta = 0.5 reads C: restore it eagerly
         rq.dC.fill_(float("nan"))          # beta = 0: C is overwritten (guard bands kept)
+        rz.dC.fill_(float("nan"))
         junk = torch.randn(1 << 20, device="cuda").sum()      # unrelated eager work
         torch.cuda.synchronize()
         g.replay()
@@ -828,6 +837,7 @@ def test_launches_replay_in_a_hip_graph():
         assert float(junk) == float(junk)
         check_exact(r.result(), eager, f"graph replay {rep} (256^3)")
         check_exact(rq.result(), eager_q, f"graph replay {rep} (split-K 256x256x8192)")
+        check_exact(rz.result(), eager_z, f"graph replay {rep} (stream-K 1000x1027x999)")
 
 
 # ------------------------------------------------------------------ seeded random problems
