@@ -39,6 +39,9 @@
 //            bytes: global -> LDS by buffer_load ... lds, a ring of stages;
 //   RegPath  everything else: range-checked loads through registers,
 //            out-of-range elements read as zero, 2 LDS stages.
+// gemm_kernel gives each workgroup one tile; gemm_sk_kernel (stream-K)
+// gives each an equal share of the (tile, K-iteration) pairs and runs the
+// same paths over K ranges.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -1307,7 +1310,8 @@ __device__ __forceinline__ void epilogue_fp(const KernelArgs &p, int bidx, int m
 //              made of TM x TN MFMA blocks of 32x32
 //   TA, TB     op(A) = A^T, op(B) = B^T
 //   VECOK      A and B allow 16-byte global accesses (enables DmaPath)
-//   PIPE       DmaPath schedule: 1 -> 4 stages of BK/2, 2 -> 2 stages of BK
+//   PIPE       DmaPath schedule: 1 -> 4 stages of BK/2, 2 -> 2 stages of BK,
+//              3 -> 1 stage of BK (K <= BK), 4 -> 4-byte copies, 2 stages of BK
 //   CT         C element type: float, T itself (16-bit output), or int32_t
 //              (int8 inputs)
 // ---------------------------------------------------------------------------
