@@ -377,7 +377,7 @@ mgemm_status gemm_streamk(mgemm_dtype in_dtype, mgemm_dtype c_dtype,
 typedef struct {
     int64_t workspace_bytes;   /* workspace the call needs (0: no product formed) */
     int64_t workgroups;        /* workgroups of the stream-K launch */
-    int64_t tiles;             /* output tiles (the fix-up launch's workgroups) */
+    int64_t tiles;             /* output tiles (the fix-up launch covers the split ones) */
     int64_t iterations;        /* K-iterations per tile */
     int64_t k_per_iteration;   /* K elements per iteration (the last may be shorter) */
     mgemm_variant_info variant;  /* tile build (id -1: none) */
