@@ -11,8 +11,8 @@ provides device memory and streams.  ``torch_ops`` maps torch tensors
 (row-major or transposed views, batch strides) onto the same entry points:
 mm, bmm, matmul and attention_scores.
 """
-from ._lib import (BF16, F16, F32, F64, I8, I32, OP_N, OP_T, MgemmError, force_variant, gemm_bf16,
-                   gemm_f16, gemm_f32, gemm_f64, gemm_f64_strided_batched, gemm_splitk,
+from ._lib import (BF16, F16, F32, F64, I8, I32, OP_N, OP_T, MgemmError, force_variant,
+                   gemm_bf16, gemm_f16, gemm_f32, gemm_f64, gemm_f64_strided_batched, gemm_splitk,
                    gemm_streamk, gemm_strided_batched, gemm_strided_batched_ex, load, select,
                    splitk_chunks, splitk_plan, splitk_workspace_bytes, status_string, streamk_plan,
                    variants)

@@ -170,6 +170,18 @@ def _stream(stream, device):
     return torch.cuda.current_stream(device).cuda_stream
 
 
+def _workspace_on(nbytes, device, stream, launch):
+    """A torch-allocated workspace for a call launched on stream handle `launch`.  It is
+    allocated on that stream, so that torch's caching allocator, once the tensor is
+    dropped, hands the block only to work ordered after the call's kernels (allocated on
+    another stream, the block could be reused while they still write it)."""
+    import torch
+    if stream is None:   # the launch stream is torch's current stream
+        return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    with torch.cuda.stream(torch.cuda.ExternalStream(launch, device=device)):
+        return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
 def _check(status: int, what: str):
     if status != 0:
         raise MgemmError(status, what)
@@ -303,9 +315,9 @@ def gemm_splitk(in_dtype, c_dtype, transA, transB, M, N, K, alpha, A, lda, B, ld
     pc, dev = _addr(C, _span(M, N, ldc), ELEM_SIZE.get(ct, 4), "C")
     need = (splitk_workspace_bytes(dt, M, N, K, splits, transA=transA, transB=transB,
                                    A=pa or 0, lda=lda, B=pb or 0, ldb=ldb) if splits >= 0 else 0)
+    launch = _stream(stream, dev)
     if workspace is None and need > 0:
-        import torch
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        workspace = _workspace_on(need, dev, stream, launch)
     if workspace is None:
         pw, wbytes = None, 0
     elif isinstance(workspace, int):
@@ -314,7 +326,7 @@ def gemm_splitk(in_dtype, c_dtype, transA, transB, M, N, K, alpha, A, lda, B, ld
         pw, _ = _addr(workspace, 0, workspace.element_size(), "workspace")
         wbytes = workspace.numel() * workspace.element_size()
     st = load().gemm_splitk(dt, ct, int(transA), int(transB), M, N, K, alpha, pa, lda, pb, ldb, beta,
-                            pc, ldc, splits, pw, wbytes, _stream(stream, dev))
+                            pc, ldc, splits, pw, wbytes, launch)
     _check(st, "gemm_splitk")
 
 
@@ -350,9 +362,9 @@ def gemm_streamk(in_dtype, c_dtype, transA, transB, M, N, K, alpha, A, lda, B, l
     pc, dev = _addr(C, _span(M, N, ldc), ELEM_SIZE.get(ct, 4), "C")
     need = (streamk_plan(dt, M, N, K, workgroups, transA=transA, transB=transB, A=pa or 0, lda=lda,
                          B=pb or 0, ldb=ldb)["workspace_bytes"] if workgroups >= 0 else 0)
+    launch = _stream(stream, dev)
     if workspace is None and need > 0:
-        import torch
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        workspace = _workspace_on(need, dev, stream, launch)
     if workspace is None:
         pw, wbytes = None, 0
     elif isinstance(workspace, int):
@@ -361,7 +373,7 @@ def gemm_streamk(in_dtype, c_dtype, transA, transB, M, N, K, alpha, A, lda, B, l
         pw, _ = _addr(workspace, 0, workspace.element_size(), "workspace")
         wbytes = workspace.numel() * workspace.element_size()
     st = load().gemm_streamk(dt, ct, int(transA), int(transB), M, N, K, alpha, pa, lda, pb, ldb, beta,
-                             pc, ldc, workgroups, pw, wbytes, _stream(stream, dev))
+                             pc, ldc, workgroups, pw, wbytes, launch)
     _check(st, "gemm_streamk")
 
 

@@ -147,12 +147,23 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base)
 // memory-counter tracking does not see it: it would otherwise wait for every
 // outstanding copy before any LDS read it cannot prove disjoint (the
 // transposing reads among them), serialising the ring.  Callers order these
-// copies with explicit vmcnt waits.  M0 is written here; nothing else in the
-// copy loop keeps a value in M0 (it is reserved and set before each use).
+// copies with explicit vmcnt waits.  The LDS destination goes in M0 through
+// an "{m0}" operand: the compiler writes M0 itself before the copy, and so
+// knows that M0 changes there (M0 is a reserved register, which a clobber
+// list cannot name).
+// The compiler inserts the wait states a memory instruction needs after the
+// writes of its scalar operands only for instructions it can see, not for
+// inline asm, so the copy opens with s_nop 4 (five wait states): a vector
+// instruction that writes an SGPR (v_readfirstlane, which forms soff and may
+// form M0 or the resource) must be five wait states ahead of a vector-memory
+// instruction that reads it, and a scalar write of M0 one ahead of an LDS-DMA
+// read of M0.  Without them a copy can take the SGPR's previous value: an
+// interior-tile prologue whose soff came from v_readfirstlane one wait state
+// earlier loaded 1 KB of B from a wrong address.
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, uint32_t lds_addr, int voff, int soff)
 {
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                 :: "s"(lds_addr), "v"(voff), "s"(rs), "s"(soff) : "memory");
+    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                 :: "v"(voff), "s"(rs), "s"(soff), "{m0}"(lds_addr) : "memory");
 }
 
 // 4-byte global -> LDS copy: lane l's 4 bytes from rsrc[voff] land at LDS byte
@@ -163,8 +174,9 @@ constexpr int kOutOfRange = 0x7fffffff;
 
 __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t rs, uint32_t lds_addr, int voff)
 {
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
-                 :: "s"(lds_addr), "v"(voff), "s"(rs) : "memory");
+    // s_nop 4: the wait states of dma16
+    asm volatile("s_nop 4\n\tbuffer_load_dword %0, %1, 0 offen lds"
+                 :: "v"(voff), "s"(rs), "{m0}"(lds_addr) : "memory");
 }
 
 __device__ __forceinline__ uint32_t lds_addr_of(const char *p)

@@ -173,10 +173,13 @@ mgemm_status validate_and_plan(int dtype, int c_dtype, int transA, int transB, i
     const bool dw_rows = es >= 4 || (aligned(A, 4) && aligned(B, 4) && lda % piece == 0 && ldb % piece == 0 &&
                                      strideA % piece == 0 && strideB % piece == 0 && k_all % piece == 0);
     // One-stage builds (pipe 3) hold a single K-slab and have no register
-    // path: K at most their slab, a multiple of 16 bytes, 32-bit offsets.
+    // path: K at most their slab, every workgroup's K a multiple of 16 bytes,
+    // 32-bit offsets.  Under split-K, K is the chunk length (a multiple of the
+    // slab) and the last chunk takes the rest of k_all, so the chunk multiple
+    // is checked on k_all: the last chunk's remainder is k_all's.
     auto offsets_ok = [&](const Variant &v) {
         return (v.pipe != 4 || (a.fast_ok && dw_rows)) &&
-               (v.pipe != 3 || (a.fast_ok && K <= v.bk && K % (16 / es) == 0));
+               (v.pipe != 3 || (a.fast_ok && K <= v.bk && k_all % (16 / es) == 0));
     };
     Table t = table_for(dtype);
     const int forced = g_forced[dtype].load();

@@ -31,11 +31,18 @@
  * alpha == 0 or K == 0: C = beta * C; A and B are not read.
  * M == 0, N == 0 or batch == 0: nothing is launched; MGEMM_OK.
  * Ownership.  The caller owns A, B and C (device memory, e.g. from PyTorch).
- *   The library allocates, frees and keeps nothing; it needs no handle and
- *   no workspace, and may be called from several host threads at once.
- * Asynchrony.  Each call validates its arguments on the host, enqueues one
- *   kernel on `stream` (NULL = the default stream) and returns.  Results are
- *   ready after the stream is synchronised.
+ *   The library allocates, frees and keeps nothing and needs no handle; it
+ *   may be called from several host threads at once.  gemm_splitk and
+ *   gemm_streamk also take a caller-owned device workspace for their partial
+ *   sums (its size comes from mgemm_splitk_plan / mgemm_streamk_plan); no
+ *   other entry point uses memory beyond A, B and C.
+ * Asynchrony.  Each call validates its arguments on the host, enqueues its
+ *   kernels on `stream` (NULL = the default stream) and returns: one kernel,
+ *   except gemm_splitk with more than one chunk (the chunk products, then a
+ *   reduction kernel) and gemm_streamk (the stream-K kernel, then a fix-up
+ *   kernel for the tiles split between workgroups).  Results are ready after
+ *   the stream is synchronised; a workspace must not be reused by another
+ *   call until the first call's kernels have finished (same stream: always).
  * Errors.  Invalid arguments are reported synchronously and nothing is
  *   launched: negative sizes, a leading dimension or stride below its
  *   minimum, a NULL pointer for an operand that will be read or written,

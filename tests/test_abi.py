@@ -431,3 +431,50 @@ def test_splitk_automatic_plans():
     # explicit counts; 1 is the plain kernel
     assert mg.splitk_plan("f32", 1000, 1027, 999, 4)["chunks"] == 4
     assert mg.splitk_plan("f32", 1000, 1027, 999, 1)["chunks"] == 1
+
+
+def test_splitk_one_stage_needs_whole_chunks_of_k():
+    # The one-stage (pipe 3) builds have no register path, so every chunk's K must be a
+    # multiple of the 16-byte piece.  Chunks are whole 64-deep slabs and the last takes the
+    # rest: with K = 196 the last chunk is 4 deep, and the plan must not pick them.
+    p = mg.splitk_plan("f16", 2048, 2048, 196, 4, transB=1, lda=200, ldb=200)
+    assert p["chunks"] == 4 and p["chunk_len"] == 64
+    assert not p["variant"]["name"].endswith("_s1")
+    # with K a multiple of 8 every chunk, the last one included, is whole pieces
+    q = mg.splitk_plan("f16", 2048, 2048, 200, 4, transB=1, lda=200, ldb=200)
+    assert q["chunks"] == 4 and q["chunk_len"] == 64
+    assert q["variant"]["name"].endswith("_s1")
+
+
+def test_every_lds_copy_in_the_library_opens_with_its_wait_states(built_library):
+    # The copies global -> LDS are inline asm, where the compiler inserts no wait states:
+    # each must open with s_nop 4, so that a v_readfirstlane that formed one of its scalar
+    # operands (the row offset, M0, the buffer resource) is five wait states behind it.
+    # Without them an interior-tile prologue loaded 1 KB of B from a stale offset.  The
+    # check disassembles the built library's gfx950 code objects (our own build).
+    import shutil
+    import tempfile
+    objdump = "/opt/rocm/llvm/bin/llvm-objdump"
+    if not os.path.exists(objdump):
+        pytest.skip("llvm-objdump not installed")
+    with tempfile.TemporaryDirectory() as d:
+        lib = os.path.join(d, "libmgemm.so")
+        shutil.copy(_lib.LIB_PATH, lib)
+        subprocess.run([objdump, "--offloading", lib], capture_output=True, check=True, cwd=d)
+        objs = sorted(f for f in os.listdir(d) if "amdgcn" in f)
+        assert objs, "no device code objects in the library"
+        copies = 0
+        for o in objs:
+            text = subprocess.run([objdump, "-d", "--no-show-raw-insn", os.path.join(d, o)],
+                                  capture_output=True, text=True, check=True).stdout
+            prev = ""
+            for line in text.splitlines():
+                ins = line.strip()
+                if not ins or ins.endswith(":") or ins.startswith(("/", ";", "Disassembly")):
+                    continue
+                ins = ins.split("//")[0].strip()
+                if ins.startswith("buffer_load") and ins.endswith(" lds"):
+                    copies += 1
+                    assert prev == "s_nop 4", f"{o}: '{ins}' follows '{prev}'"
+                prev = ins
+    assert copies > 1000

@@ -551,6 +551,31 @@ def test_splitk_auto_small_unaligned_grid(dtype):
     full_check(q, what=f"automatic split-K {dtype} uniform")
 
 
+@pytest.mark.parametrize("K", [196, 200])
+def test_splitk_attention_layout_with_padded_rows(K):
+    # QK^T layout (16-bit, B stored [n][k]) with rows padded to 200 elements of NaN-free
+    # data and NaN in the padding, four 64-deep chunks, 256 workgroups.  With K = 196 the
+    # last chunk is 4 deep: the one-stage builds (no register path) must not take it,
+    # else the row padding past K would be multiplied in.  K = 200 keeps them.
+    p = wl.Problem("f16", 2048, 2048, K, transB=True, lda=200, ldb=200, dist="int", int_lo=-8,
+                   int_hi=8, seed=120 + K, splitk=4, pad_value=float("nan"))
+    plan = mg.splitk_plan("f16", 2048, 2048, K, 4, transB=1, lda=200, ldb=200)
+    assert plan["chunks"] == 4 and plan["grid"] >= 256, plan
+    assert plan["variant"]["name"].endswith("_s1") == (K % 8 == 0), plan
+    full_check(p, exact=True, what=f"split-K QK^T layout K={K} ({plan['variant']['name']})")
+
+
+def test_splitk_own_workspace_on_an_explicit_stream():
+    # no workspace given: the binding allocates it on the launch stream, here a side stream
+    # passed by handle while torch's current stream is another one
+    p = wl.Problem("f32", 300, 260, 1500, dist="int", int_lo=-9, int_hi=9, seed=125, splitk=4)
+    r = Run(p)
+    s = torch.cuda.Stream()
+    r.launch(stream=s.cuda_stream)
+    s.synchronize()
+    check_exact(r.result(), r.oracle_full(), "split-K, binding-allocated workspace, side stream")
+
+
 def test_splitk_auto_on_a_deep_k_shape():
     p = wl.Problem("f32", 256, 256, 8192, alpha=2.0, dist="int", int_lo=-9, int_hi=9, seed=97,
                    splitk=0)
