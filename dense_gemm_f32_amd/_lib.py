@@ -23,7 +23,9 @@ F32, F16, BF16, I8, I32, F64 = 0, 1, 2, 3, 4, 5
 DTYPE_CODES = {"f32": F32, "f16": F16, "bf16": BF16, "i8": I8, "i32": I32, "f64": F64}
 ELEM_SIZE = {F32: 4, F16: 2, BF16: 2, I8: 1, I32: 4, F64: 8}
 
-STATUS = {0: "MGEMM_OK", 1: "MGEMM_INVALID_ARG", 2: "MGEMM_HIP_ERROR"}
+STATUS = {0: "MGEMM_OK", 1: "MGEMM_INVALID_ARG", 2: "MGEMM_HIP_ERROR", 3: "MGEMM_SCRATCH_TOO_SMALL"}
+# fixed device scratch of gemm_splitk_noalloc (MGEMM_NOALLOC_SCRATCH_BYTES in include/mgemm.h)
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class MgemmError(RuntimeError):
@@ -96,6 +98,9 @@ def load():
     lib.gemm_splitk.restype = i32
     lib.gemm_splitk.argtypes = [i32, i32, i32, i32, i64, i64, i64, f64, vp, i64, vp, i64, f64, vp,
                                 i64, i64, vp, i64, vp]
+    lib.gemm_splitk_noalloc.restype = i32
+    lib.gemm_splitk_noalloc.argtypes = [i32, i32, i32, i32, i64, i64, i64, f64, vp, i64, vp, i64, f64,
+                                        vp, i64, i64, vp]
     lib.mgemm_splitk_plan.restype = i32
     lib.mgemm_splitk_plan.argtypes = [i32, i32, i32, i64, i64, i64, vp, i64, vp, i64, i64,
                                       ctypes.POINTER(SplitkPlanInfo)]
@@ -328,6 +333,25 @@ def gemm_splitk(in_dtype, c_dtype, transA, transB, M, N, K, alpha, A, lda, B, ld
     st = load().gemm_splitk(dt, ct, int(transA), int(transB), M, N, K, alpha, pa, lda, pb, ldb, beta,
                             pc, ldc, splits, pw, wbytes, launch)
     _check(st, "gemm_splitk")
+
+
+def gemm_splitk_noalloc(in_dtype, c_dtype, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta,
+                        C, ldc, splits=0, stream=None):
+    """Split-K GEMM whose partial sums go to the library's fixed per-GPU scratch
+    (NOALLOC_SCRATCH_BYTES): nothing is allocated, here or in the library.  Calls that may
+    overlap on one GPU race on that scratch; order them on one stream."""
+    dt = DTYPE_CODES.get(in_dtype, in_dtype)
+    ct = DTYPE_CODES.get(c_dtype, c_dtype)
+    es = ELEM_SIZE[dt]
+    a_rows, a_cols = (K, M) if transA else (M, K)
+    b_rows, b_cols = (N, K) if transB else (K, N)
+    reads = M > 0 and N > 0 and K > 0 and alpha != 0.0
+    pa, _ = _addr(A, _span(a_rows, a_cols, lda) if reads else 0, es, "A")
+    pb, _ = _addr(B, _span(b_rows, b_cols, ldb) if reads else 0, es, "B")
+    pc, dev = _addr(C, _span(M, N, ldc), ELEM_SIZE.get(ct, 4), "C")
+    st = load().gemm_splitk_noalloc(dt, ct, int(transA), int(transB), M, N, K, alpha, pa, lda, pb,
+                                    ldb, beta, pc, ldc, splits, _stream(stream, dev))
+    _check(st, "gemm_splitk_noalloc")
 
 
 def streamk_plan(in_dtype, M, N, K, workgroups=0, transA=0, transB=0, A=1 << 20, lda=None,

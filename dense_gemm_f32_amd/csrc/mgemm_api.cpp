@@ -4,6 +4,7 @@
 // introspection functions work on machines without a GPU.
 #include <atomic>
 #include <climits>
+#include <mutex>
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
@@ -496,6 +497,67 @@ mgemm_status run_streamk(int dtype, int c_dtype, int transA, int transB, int64_t
     return err == hipSuccess ? MGEMM_OK : MGEMM_HIP_ERROR;
 }
 
+// ---------------------------------------------------------------------------
+// Fixed scratch for gemm_splitk_noalloc: split-K's partial products on a GPU
+// whose caller cannot allocate.  The array's host-side name is not a device
+// address: the device address is looked up once per device, with that device
+// current, and only that address is handed to kernels.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) char scratch[MGEMM_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of this GPU's scratch for work on `stream` (which must
+// belong to the current device).
+mgemm_status scratch_for(hipStream_t stream, void **out)
+{
+    int cur = -1;
+    hipDevice_t sdev = -1;
+    if (hipGetDevice(&cur) != hipSuccess || hipStreamGetDevice(stream, &sdev) != hipSuccess)
+        return MGEMM_HIP_ERROR;
+    if (sdev != cur) return MGEMM_INVALID_ARG;
+    if (cur < 0 || cur >= kMaxDevices) return MGEMM_HIP_ERROR;
+    void *p = g_scratch_ptr[cur].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_ptr[cur].load(std::memory_order_acquire);
+        if (p == nullptr) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+                return MGEMM_HIP_ERROR;
+            g_scratch_ptr[cur].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return MGEMM_OK;
+}
+
+mgemm_status run_splitk_noalloc(int dtype, int c_dtype, int transA, int transB, int64_t M, int64_t N,
+                                int64_t K, double alpha, const void *A, int64_t lda, const void *B,
+                                int64_t ldb, double beta, void *C, int64_t ldc, int64_t splits,
+                                hipStream_t stream)
+{
+    // argument errors and the size limit first, before any device call
+    Plan full;
+    mgemm_status st = validate_and_plan(dtype, c_dtype, transA, transB, M, N, K, alpha, A, lda, 0, B,
+                                        ldb, 0, beta, C, ldc, 0, 1, &full);
+    if (st != MGEMM_OK) return st;
+    void *ws = nullptr;
+    if (full.kind == Plan::GEMM) {
+        SplitPlan sp;
+        st = make_split_plan(dtype, transA, transB, M, N, K, A, lda, B, ldb, splits, &sp);
+        if (st != MGEMM_OK) return st;
+        if (sp.workspace_bytes > MGEMM_NOALLOC_SCRATCH_BYTES) return MGEMM_SCRATCH_TOO_SMALL;
+        if (sp.chunks > 1) {
+            st = scratch_for(stream, &ws);
+            if (st != MGEMM_OK) return st;
+        }
+    }
+    return run_splitk(dtype, c_dtype, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, splits,
+                      ws, ws ? MGEMM_NOALLOC_SCRATCH_BYTES : 0, stream);
+}
+
 void fill_info(const Variant &v, int id, mgemm_variant_info *out)
 {
     out->id = id;
@@ -620,6 +682,17 @@ mgemm_status gemm_splitk(mgemm_dtype in_dtype, mgemm_dtype c_dtype, mgemm_op tra
                       splits, workspace, workspace_bytes, stream);
 }
 
+mgemm_status gemm_splitk_noalloc(mgemm_dtype in_dtype, mgemm_dtype c_dtype, mgemm_op transA,
+                                 mgemm_op transB, int64_t M, int64_t N, int64_t K, double alpha,
+                                 const void *A, int64_t lda, const void *B, int64_t ldb, double beta,
+                                 void *C, int64_t ldc, int64_t splits, hipStream_t stream)
+{
+    if (in_dtype != MGEMM_F64 && ((double)(float)alpha != alpha || (double)(float)beta != beta))
+        return MGEMM_INVALID_ARG;
+    return run_splitk_noalloc(in_dtype, c_dtype, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C,
+                              ldc, splits, stream);
+}
+
 mgemm_status mgemm_splitk_plan(mgemm_dtype in_dtype, mgemm_op transA, mgemm_op transB, int64_t M,
                                int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
                                int64_t ldb, int64_t splits, mgemm_splitk_plan_info *out)
@@ -687,6 +760,9 @@ const char *mgemm_status_string(mgemm_status s)
     case MGEMM_OK: return "MGEMM_OK";
     case MGEMM_INVALID_ARG: return "MGEMM_INVALID_ARG: an argument failed validation; nothing was launched";
     case MGEMM_HIP_ERROR: return "MGEMM_HIP_ERROR: the HIP runtime refused the kernel launch";
+    case MGEMM_SCRATCH_TOO_SMALL:
+        return "MGEMM_SCRATCH_TOO_SMALL: the split-K partial sums need more than the fixed "
+               "scratch of gemm_splitk_noalloc (MGEMM_NOALLOC_SCRATCH_BYTES); nothing was launched";
     default: return "unknown mgemm_status";
     }
 }

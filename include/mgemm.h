@@ -66,7 +66,8 @@ extern "C" {
 typedef enum {
     MGEMM_OK = 0,
     MGEMM_INVALID_ARG = 1,
-    MGEMM_HIP_ERROR = 2
+    MGEMM_HIP_ERROR = 2,
+    MGEMM_SCRATCH_TOO_SMALL = 3  /* gemm_splitk_noalloc: partial sums exceed its fixed scratch */
 } mgemm_status;
 
 typedef enum { MGEMM_OP_N = 0, MGEMM_OP_T = 1 } mgemm_op;
@@ -246,6 +247,33 @@ mgemm_status gemm_splitk(mgemm_dtype in_dtype, mgemm_dtype c_dtype,
                          double beta, void *C, int64_t ldc,
                          int64_t splits, void *workspace, int64_t workspace_bytes,
                          hipStream_t stream);
+
+/* gemm_splitk_noalloc -- gemm_splitk for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid allocation.  Same arguments, plan, kernels and
+ * results as gemm_splitk, minus the workspace: the partial products go to a
+ * fixed scratch array of MGEMM_NOALLOC_SCRATCH_BYTES in the library's own
+ * device memory, one per GPU, held from the first call on that GPU until the
+ * process ends.  The first call on a GPU looks the array's address up
+ * (hipGetSymbolAddress); no call allocates or frees anything.
+ *   stream  must belong to the calling thread's current device
+ *          (MGEMM_INVALID_ARG otherwise).
+ * Every call on one GPU shares that GPU's scratch, which keeps the last
+ * call's partial sums (each call overwrites what it reads; nothing needs to
+ * start at zero).  Calls that may run at the same time on one GPU (other
+ * streams, other host threads) race on it: order them on one stream.
+ * Errors: as gemm_splitk, plus MGEMM_SCRATCH_TOO_SMALL, before any device
+ * call, when the plan's workspace_bytes (mgemm_splitk_plan) exceeds
+ * MGEMM_NOALLOC_SCRATCH_BYTES; MGEMM_HIP_ERROR when the address lookup
+ * fails. */
+#define MGEMM_NOALLOC_SCRATCH_BYTES ((int64_t)64 << 20)
+mgemm_status gemm_splitk_noalloc(mgemm_dtype in_dtype, mgemm_dtype c_dtype,
+                                 mgemm_op transA, mgemm_op transB,
+                                 int64_t M, int64_t N, int64_t K, double alpha,
+                                 const void *A, int64_t lda,
+                                 const void *B, int64_t ldb,
+                                 double beta, void *C, int64_t ldc,
+                                 int64_t splits, hipStream_t stream);
 
 /* Human-readable text for a status code (static storage). */
 const char *mgemm_status_string(mgemm_status s);

@@ -446,6 +446,25 @@ def test_splitk_one_stage_needs_whole_chunks_of_k():
     assert q["variant"]["name"].endswith("_s1")
 
 
+def test_noalloc_refuses_sizes_beyond_its_scratch_without_a_gpu():
+    # the plan is checked before any device call: 4 chunks of 4096 x 4096 fp32 partial sums
+    # (256 MiB) exceed the fixed scratch, bad arguments are refused as in gemm_splitk
+    lib = mg.load()
+    na = lib.gemm_splitk_noalloc
+    M = N = K = 4096
+    assert 4 * M * N * 4 > mg.NOALLOC_SCRATCH_BYTES
+    assert na(0, 0, 0, 0, M, N, K, 1.0, ALIGNED, K, ALIGNED, N, 0.0, ALIGNED, N, 4, None) == 3
+    assert na(0, 0, 0, 0, M, N, K, 1.0, ALIGNED, K - 1, ALIGNED, N, 0.0, ALIGNED, N, 4, None) == 1
+    assert na(0, 0, 0, 0, 64, 64, 1024, 1.0 + 2 ** -40, ALIGNED, 1024, ALIGNED, 64, 0.0, ALIGNED,
+              64, 4, None) == 1
+    assert na(0, 0, 0, 0, 0, 64, 1024, 1.0, ALIGNED, 1024, ALIGNED, 64, 0.0, ALIGNED, 64, 4,
+              None) == 0                                       # nothing to do
+    assert "SCRATCH" in mg.status_string(3)
+    with open(HEADER) as f:
+        assert "#define MGEMM_NOALLOC_SCRATCH_BYTES ((int64_t)64 << 20)" in f.read()
+    assert mg.NOALLOC_SCRATCH_BYTES == 64 << 20
+
+
 def test_every_lds_copy_in_the_library_opens_with_its_wait_states(built_library):
     # The copies global -> LDS are inline asm, where the compiler inserts no wait states:
     # each must open with s_nop 4, so that a v_readfirstlane that formed one of its scalar
