@@ -4,7 +4,12 @@ A step is one gemm_f32 call, C = 1.5*A*B + 0.5*C at M = N = K = 4096 (fp32,
 operands ~ U[-1,1), already resident in HBM).  The JSON line reports its
 TFLOP/s (2*M*N*K per step), the kernel's fraction of the fp32 matrix-core
 peak, every workload of the scope table timed the same way (median, min and
-max of single launches as well), and the CPU oracle timed on bounded samples.
+max of single launches as well) with its sustained clock and socket power and
+a parity check of one fresh launch against the oracle on sampled elements
+(max|err|, tolerance, bit-exactness; run in the CPU leg, outside every timed
+region), the register-only 16-bit matrix-core rate on N(0,1) data (the
+power-limited ceiling on this board), and the CPU oracle timed on bounded
+samples.
 
 Usage:
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-secondary]
@@ -397,6 +402,138 @@ def time_graph(torch, fn, calls=20, replays=10):
     return start.elapsed_time(stop) / (calls * replays) * 1e-3
 
 
+class Telemetry:
+    """GPU clock (mean over the XCDs) and socket power from the SMU's metrics
+    table through amdsmi.  The table refreshes about once a second (measured),
+    so readings come from a sustained run of a few seconds, after its first
+    second.  Without amdsmi every reading is None."""
+
+    def __init__(self):
+        self.h = None
+        self.error = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self.amdsmi = amdsmi
+            self.h = amdsmi.amdsmi_get_processor_handles()[0]
+        except Exception as e:  # no amdsmi, no permission: no readings
+            self.error = repr(e)
+
+    def read(self):
+        if self.h is None:
+            return None
+        try:
+            m = self.amdsmi.amdsmi_get_gpu_metrics_info(self.h)
+            clks = [c for c in m.get("current_gfxclks", []) if isinstance(c, (int, float)) and c > 0]
+            clk = statistics.mean(clks) if clks else m.get("current_gfxclk")
+            pw = m.get("current_socket_power")
+            return (float(clk) if isinstance(clk, (int, float)) else None,
+                    float(pw) if isinstance(pw, (int, float)) else None)
+        except Exception:
+            return None
+
+    def sustained(self, torch, fn, launch_s, seconds=2.5, settle=1.2):
+        """Run fn back to back for about `seconds`, sampling every 20 ms; the
+        medians of the samples taken after `settle` seconds (the table has
+        refreshed at least once under the load)."""
+        if self.h is None:
+            return None
+        import threading
+        samples, stop = [], threading.Event()
+        t_start = time.perf_counter()
+
+        def poll():
+            while not stop.is_set():
+                r = self.read()
+                if r is not None and time.perf_counter() - t_start >= settle:
+                    samples.append(r)
+                time.sleep(0.02)
+
+        th = threading.Thread(target=poll)
+        th.start()
+        batch = max(1, int(0.02 / max(launch_s, 1e-7)))
+        t0 = time.perf_counter()
+        try:
+            while time.perf_counter() - t0 < seconds:
+                for _ in range(batch):
+                    fn()
+                torch.cuda.synchronize()
+        finally:
+            stop.set()
+            th.join()
+        clks = [c for c, _ in samples if c is not None]
+        pws = [w for _, w in samples if w is not None]
+        return {"clock_mhz": round(statistics.median(clks)) if clks else None,
+                "socket_power_w": round(statistics.median(pws)) if pws else None,
+                "window_s": seconds, "readings": len(set(samples))}
+
+
+def mfma_ceiling(torch, dev, tel):
+    """Register-only matrix-core rate (libmgemm_diag.so) on N(0,1) operand values,
+    bf16 and binary16: the power-limited ceiling no 16-bit GEMM on this board
+    and data can exceed.  None when the diagnostic library is not built."""
+    import ctypes
+    path = os.path.join(ROOT, "dense_gemm_f32_amd", "libmgemm_diag.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.mgemm_diag_mfma_ceiling.restype = ctypes.c_int
+    lib.mgemm_diag_mfma_ceiling.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_int, ctypes.c_void_p]
+    lib.mgemm_diag_ceiling_operand_bytes.restype = ctypes.c_int64
+    lib.mgemm_diag_ceiling_out_floats.restype = ctypes.c_int64
+    lib.mgemm_diag_ceiling_flop.restype = ctypes.c_double
+    lib.mgemm_diag_ceiling_flop.argtypes = [ctypes.c_int]
+    n16 = lib.mgemm_diag_ceiling_operand_bytes() // 2
+    out = torch.empty(lib.mgemm_diag_ceiling_out_floats(), dtype=torch.float32, device=dev)
+    iters = 40000
+    res = {}
+    for name, tdt in (("bf16", torch.bfloat16), ("f16", torch.float16)):
+        g = torch.Generator().manual_seed(1004)
+        ops = torch.randn(n16, generator=g).to(tdt).to(dev)
+        st = torch.cuda.current_stream()
+        fn = lambda: lib.mgemm_diag_mfma_ceiling(int(name == "bf16"), ops.data_ptr(), out.data_ptr(),
+                                                 iters, ctypes.c_void_p(st.cuda_stream))
+        for _ in range(3):
+            assert fn() == 0
+        each = time_each(torch, fn, 5)
+        t = statistics.median(each)
+        tf = lib.mgemm_diag_ceiling_flop(iters) / t / 1e12
+        rec = {"tflops": round(tf, 1), "frac_matrix_peak": round(tf / PEAK_TFLOPS[name], 4),
+               "data": "N(0,1) rounded to %s" % name, "ms": round(t * 1e3, 3)}
+        tel_r = tel.sustained(torch, fn, t) if tel else None
+        if tel_r:
+            rec.update(tel_r)
+        res[name] = rec
+        log(f"mfma ceiling {name}: {rec}")
+        del ops
+    return res
+
+
+def sample_positions(p, n_random=4096, seed=7):
+    """Output elements the parity check compares: the first and last row and
+    column of the first and last batch entry, and random ones."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    bs, is_, js = [], [], []
+    for b in sorted({0, p.batch - 1}):
+        for i in sorted({0, p.M - 1}):
+            bs.append(np.full(p.N, b)); is_.append(np.full(p.N, i)); js.append(np.arange(p.N))
+        for j in sorted({0, p.N - 1}):
+            bs.append(np.full(p.M, b)); is_.append(np.arange(p.M)); js.append(np.full(p.M, j))
+    bs.append(rng.integers(0, p.batch, n_random))
+    is_.append(rng.integers(0, p.M, n_random))
+    js.append(rng.integers(0, p.N, n_random))
+    return np.concatenate(bs), np.concatenate(is_), np.concatenate(js)
+
+
+def gather_c(torch, p, dC, pos):
+    """C's sampled elements (float64 on the host) after a launch."""
+    b, i, j = pos
+    idx = torch.as_tensor(b * p.strideC + i * p.ldc + j, dtype=torch.int64, device=dC.device)
+    return dC[idx].double().cpu().numpy()
+
+
 def algorithmic_bytes(p):
     """Compulsory HBM traffic: A and B once, C written (and read when beta != 0)."""
     from dense_gemm_f32_amd import workloads as wl
@@ -405,17 +542,22 @@ def algorithmic_bytes(p):
     return per * p.batch
 
 
-def per_config(torch, dev, iters):
+def per_config(torch, dev, iters, tel=None, checks=None):
     """Every workload: 30 warm-up launches (the part settles at its power-limited
     clock), then `iters` back-to-back launches (mean) and `iters` single
-    launches (median / min / max).  The fp32 4096^3 step is also timed with a
-    cold cache: 512 MiB written between launches, outside the timed bracket."""
+    launches (median / min / max), then 2.5 s of back-to-back launches with the
+    clock and socket power sampled.  The fp32 4096^3 step is
+    also timed with a cold cache: 512 MiB written between launches, outside the
+    timed bracket.  Last, C is restored and one fresh launch is made whose
+    sampled output elements go to `checks` (compared with the oracle in the CPU
+    leg, outside every timed region)."""
     import dense_gemm_f32_amd as mg
     from dense_gemm_f32_amd import workloads as wl
     out = {}
     for name in CASES:
         p = wl.WORKLOADS[name]()
         dA, dB, dC = make_device_problem(p, torch, dev)
+        dC_init = dC.clone()
         fn = launcher(p, dA, dB, dC)
         for _ in range(30):
             fn()
@@ -448,11 +590,55 @@ def per_config(torch, dev, iters):
             rec["cold_cache_median_ms"] = round(cm * 1e3, 4)
             rec["cold_cache_tflops"] = round(p.flops / cm / 1e12, 2)
             del scratch
+        if tel is not None:
+            rec["telemetry"] = tel.sustained(torch, fn, t)
+        if checks is not None:
+            dC.copy_(dC_init)
+            fn()
+            torch.cuda.synchronize()
+            pos = sample_positions(p)
+            checks[name] = (pos, gather_c(torch, p, dC, pos))
         out[name] = rec
         log(f"{name}: {rec}")
-        del dA, dB, dC
+        del dA, dB, dC, dC_init
         torch.cuda.empty_cache()
     return out
+
+
+def parity_checks(per, checks):
+    """CPU leg: the oracle's values at each workload's sampled elements against
+    the fresh launch's (max|err|, the workload's tolerance, bit-exactness)."""
+    import numpy as np
+    import oracle
+    from dense_gemm_f32_amd import workloads as wl
+    for name, (pos, got) in checks.items():
+        p = wl.WORKLOADS[name]()
+        A, B, C0 = wl.make_inputs(p)
+        Cn = None if C0 is None else (C0.numpy() if p.c_dtype in ("i32", "f64") else C0.float().numpy())
+        t0 = time.perf_counter()
+        ref = oracle.gemm_elems(p.dtype, p.transA, p.transB, p.M, p.N, p.K, p.alpha,
+                                wl.to_numpy_operand(A), p.lda, wl.to_numpy_operand(B), p.ldb,
+                                p.beta, Cn, p.ldc, *pos, batch=p.batch, strideA=p.strideA,
+                                strideB=p.strideB, strideC=p.strideC)
+        secs = time.perf_counter() - t0
+        if p.c_dtype in ("f16", "bf16"):   # what an exact accumulation stores in C's type
+            exp = oracle.decode16(p.c_dtype, oracle.round16(p.c_dtype, ref))
+        elif p.c_dtype == "i32":
+            exp = oracle.wrap_i32(ref).astype(np.float64)
+        else:
+            exp = ref
+        err = float(np.max(np.abs(got - ref)))
+        scale = float(np.max(np.abs(ref)))
+        tol = (p.tolerance_coeff() * np.sqrt(max(p.K, 1)) + p.output_rounding()) * scale
+        exact = bool(np.array_equal(got, exp))
+        must_be_exact = p.dist == "int"
+        per[name]["check"] = {
+            "elements": int(got.size), "max_abs_err": err, "tol": tol,
+            "err_over_tol": (err / tol) if tol else None, "bit_exact": exact,
+            "exact_required": must_be_exact,
+            "pass": bool(exact if must_be_exact else (err <= tol and not np.isnan(got).any())),
+            "oracle_seconds": round(secs, 2)}
+        log(f"check {name}: {per[name]['check']}")
 
 
 # ---------------------------------------------------------------------------- CPU oracle
@@ -479,6 +665,17 @@ def _oracle_rate(p, rows=None, batches=None):
     return time.perf_counter() - t0, 2.0 * r * p.N * p.K
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(budget_s=15.0):
     """The oracle, as it stands, on the host cores: the bench workload on its first
     R output rows (R sized for about `budget_s`), and every other workload on a
@@ -493,6 +690,8 @@ def cpu_baseline(budget_s=15.0):
     r2 = max(threads, (r2 // threads) * threads)
     t2, flop = _oracle_rate(p, rows=r2)
     res = {"value": flop / t2 / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+           "cpu_model": _cpu_model(), "nproc": os.cpu_count(),
+           "affinity_cpus": len(os.sched_getaffinity(0)),
            "sample": f"first {r2} of {p.M} output rows of the same {p.M}x{p.N}x{p.K} fp32 GEMM "
                      f"({flop / 1e9:.1f} GFLOP, fp64 accumulation, {t2:.1f} s)"}
     samples = {"sgemm_256": {}, "sgemm_ragged": {}, "gemm_bf16_8192": {"rows": threads},
@@ -617,11 +816,25 @@ def main():
     del dA, dB, dC
     torch.cuda.empty_cache()
 
-    per = None if args.no_secondary else per_config(torch, dev, 30)
+    tel = Telemetry()
+    if tel.h is None:
+        log(f"no GPU telemetry: {tel.error}")
+    ceiling = None if args.no_secondary else mfma_ceiling(torch, dev, tel)
+    checks = {}
+    per = None if args.no_secondary else per_config(torch, dev, 30, tel, checks)
+    if per and (per[PRIMARY].get("telemetry") or {}).get("clock_mhz"):
+        # the same kernel, sustained: the clock the roofline fraction was reached at
+        roofline["clock_mhz"] = per[PRIMARY]["telemetry"]["clock_mhz"]
+    if per and ceiling:
+        for name in ("gemm_bf16_8192", "gemm_f16_8192"):
+            c = ceiling[per[name]["dtype"]]["tflops"]
+            per[name]["frac_of_mfma_ceiling"] = round(per[name]["tflops"] / c, 4)
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline()
         log(f"cpu_baseline: {cpu}")
+        if per:   # the oracle is used in this leg only
+            parity_checks(per, checks)
 
     line = {
         "metric": "GEMM TFLOP/s + % of MI355X matrix peak (fp32 4096^3, bf16 8192^3)",
@@ -641,6 +854,7 @@ def main():
                    "grid": grid},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "mfma_ceiling": ceiling,
         "per_config": per,
     }
     print(json.dumps(line), flush=True)

@@ -1,7 +1,8 @@
 """Build libmgemm.so (HIP, gfx950) in-tree.
 
 Every translation unit under csrc/ is compiled with hipcc for gfx950 into
-_build/, in parallel, then linked into dense_gemm_f32_amd/libmgemm.so.
+_build/, in parallel, then linked into dense_gemm_f32_amd/libmgemm.so.  The
+benchmark's measurement aids under diag/ go into libmgemm_diag.so.
 """
 from __future__ import annotations
 
@@ -14,6 +15,8 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
+DIAG = os.path.join(PKG, "diag")
+DIAG_LIB = os.path.join(PKG, "libmgemm_diag.so")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmgemm.so")
 ARCH = "gfx950"
@@ -41,19 +44,27 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
-def build(extra_flags=(), jobs: int | None = None) -> str:
-    """Compile and link libmgemm.so; returns its path.  Always rebuilds."""
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
-    jobs = jobs or min(len(srcs), os.cpu_count() or 4, 16)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, list(extra_flags)), srcs))
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(objs, out):
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(extra_flags=(), jobs: int | None = None) -> str:
+    """Compile and link libmgemm.so (and libmgemm_diag.so); returns the former's
+    path.  Always rebuilds."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
+    diag = sorted(glob.glob(os.path.join(DIAG, "*.hip")))
+    jobs = jobs or min(len(srcs) + len(diag), os.cpu_count() or 4, 16)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(lambda s: _compile(s, list(extra_flags)), srcs + diag))
+    _link(objs[:len(srcs)], LIB)
+    if diag:
+        _link(objs[len(srcs):], DIAG_LIB)
     return LIB
 
 

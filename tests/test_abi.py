@@ -49,6 +49,29 @@ def test_library_exports_every_declared_symbol():
         assert getattr(lib, n) is not None
 
 
+def test_diag_library_exports_its_header():
+    # the benchmark's measurement aid: built beside libmgemm.so, loaded by bench.py only
+    diag_header = os.path.join(ROOT, "include", "mgemm_diag.h")
+    diag_lib = os.path.join(os.path.dirname(_lib.LIB_PATH), "libmgemm_diag.so")
+    if not os.path.exists(diag_lib):
+        from dense_gemm_f32_amd import build
+        build.build()
+    text = re.sub(r"/\*.*?\*/", "", open(diag_header).read(), flags=re.S)
+    names = sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+    assert "mgemm_diag_mfma_ceiling" in names
+    out = subprocess.run(["nm", "-D", "--defined-only", diag_lib], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
+    assert not [n for n in names if n not in exported]
+    lib = ctypes.CDLL(diag_lib)
+    lib.mgemm_diag_ceiling_flop.restype = ctypes.c_double
+    lib.mgemm_diag_ceiling_flop.argtypes = [ctypes.c_int]
+    assert lib.mgemm_diag_ceiling_flop(1) == 256 * 4 * 64 * 32768.0
+    lib.mgemm_diag_mfma_ceiling.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_int, ctypes.c_void_p]
+    assert lib.mgemm_diag_mfma_ceiling(1, None, None, 10, None) == 1   # refused, no launch
+
+
 def test_status_strings():
     assert mg.status_string(0) == "MGEMM_OK"
     assert "INVALID_ARG" in mg.status_string(1)
