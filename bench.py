@@ -82,6 +82,8 @@ def kernel_source_sha(dtype):
     names = ("gemm_kernel.hpp", "variants.hpp", "kernels_%s.hip" % dtype)
     if dtype == "f64":
         names += ("gemm_f64.hpp",)
+    if dtype == "f32":
+        names += ("gemm_small.hpp",)
     for name in names:
         with open(os.path.join(csrc, name), "rb") as fh:
             h.update(name.encode())
@@ -157,7 +159,8 @@ def summarize_case(case, d, copy_dir):
     kname = info["name"]
     # demangled for fp32; 16-bit instances stay mangled
     filt = ("gemm_f64_kernel" if p.dtype == "f64" else
-            "gemm_sk_kernel" if p.streamk is not None else "gemm_kernel")
+            "gemm_sk_kernel" if p.streamk is not None else
+            "gemm_small_kernel" if info["pipe"] == 6 else "gemm_kernel")
     durs = _dispatch_durations(os.path.join(d, "trace"), filt)
     timed = durs[PROFILE_WARMUP:] if len(durs) > PROFILE_WARMUP else durs  # after the warm-up
     fetch_v, _ = _counters(os.path.join(d, "fetch"), filt)

@@ -34,6 +34,15 @@ const Variant *f32_variants(int *count)
                             {2.9f, 0.0185f, 1.0f, 1.6f}, MGEMM_SK(float, 64, 64, 32, 2, 2, false, 4)),
         MGEMM_VARIANT_F32(64, 64, 32, 2, 2, false, "mgemm_f32_64x64x32_w2x2_u", {},
                           MGEMM_SK(float, 64, 64, 32, 2, 2, false, 1)),
+        // small problems: 16x16 tiles, the waves of a workgroup sharing K
+        // (t0 + max(tk*K, tw*W*K) us).  Measured per call from HIP-graph
+        // replays, against the 64x64 build the model picked before: 256^3 4.2
+        // against 7.5 us, 128^3 3.2 against 5.1, 256x256x1024 10.0 against
+        // 21.8; the 64x64 build stays ahead at 512^3 (12.3 against 17.3) and
+        // 512x512x256 (7.6 against 9.7), where the 16x16 grid is four times
+        // larger than one CU-filling round
+        MGEMM_VARIANT_F32_SMALL(4, 2, "mgemm_f32_16x16_k4w_256", {2.2f, 0.0076f, 1.0f, 1.0f, 3.05e-5f}),
+        MGEMM_VARIANT_F32_SMALL(8, 4, "mgemm_f32_16x16_k8w_1024", {2.2f, 0.0076f, 1.0f, 1.0f, 3.05e-5f}),
     };
     *count = sizeof(table) / sizeof(table[0]);
     return table;

@@ -180,7 +180,10 @@ mgemm_status validate_and_plan(int dtype, int c_dtype, int transA, int transB, i
     // is checked on k_all: the last chunk's remainder is k_all's.
     auto offsets_ok = [&](const Variant &v) {
         return (v.pipe != 4 || (a.fast_ok && dw_rows)) &&
-               (v.pipe != 3 || (a.fast_ok && K <= v.bk && k_all % (16 / es) == 0));
+               (v.pipe != 3 || (a.fast_ok && K <= v.bk && k_all % (16 / es) == 0)) &&
+               // the small-problem kernel: its waves share at most bk of K, and it
+               // has no shorter last chunk (split-K) of its own
+               (v.pipe != 6 || (K <= v.bk && !k_chunks));
     };
     Table t = table_for(dtype);
     const int forced = g_forced[dtype].load();
@@ -218,21 +221,42 @@ mgemm_status validate_and_plan(int dtype, int c_dtype, int transA, int transB, i
         // its tiles take the latter (K not a multiple of 16 bytes, or offsets
         // past 32 bits; the 4-byte-copy builds have no second path); a grid
         // of one round pays the one-round factor.
-        double best_us = 0.0;
+        // The small-problem builds (pipe 6) load one element at a time and
+        // take any alignment; where no estimated build fits the operands, the
+        // unestimated ones below run the register path, and a small build
+        // must beat that path's estimate (the 16-byte builds' times with the
+        // register factor) rather than nothing.
+        double best_us = 0.0, small_us = 0.0, reg_us = -1.0;
+        int small = -1;
         for (int i = 0; i < t.n; ++i) {
             const Variant &v = t.v[i];
-            if (v.cost.tk <= 0.0f || (v.vec && !vec_ok) || !offsets_ok(v) || !has_sk(v)) continue;
+            if (v.cost.tk <= 0.0f || !has_sk(v)) continue;
             const int64_t rounds = (wgs_of(v) + 255) / 256;
+            double us = (double)rounds * (v.cost.t0 + v.cost.tk * (double)K);
+            if (rounds == 1) us *= v.cost.solo;
+            if (v.pipe == 6) {  // workgroups share CUs: no rounds (Cost in variants.hpp)
+                const double chain = v.cost.tk * (double)K;
+                const double rate = v.cost.tw * (double)wgs_of(v) * (double)K;
+                us = v.cost.t0 + (chain > rate ? chain : rate);
+                if (offsets_ok(v) && (small < 0 || us < small_us)) {
+                    small = i;
+                    small_us = us;
+                }
+                continue;
+            }
+            if ((v.vec && !vec_ok) || !offsets_ok(v)) {
+                if (v.pipe != 4 && (reg_us < 0.0 || us * v.cost.reg < reg_us)) reg_us = us * v.cost.reg;
+                continue;
+            }
             // the 16-byte DMA path takes every tile when K is a multiple of 16 bytes
             const bool reg_tiles = v.pipe != 4 && (!a.fast_ok || K % (16 / es) != 0);
-            double us = (double)rounds * (v.cost.t0 + v.cost.tk * (double)K);
             if (reg_tiles) us *= v.cost.reg;
-            if (rounds == 1) us *= v.cost.solo;
             if (pick < 0 || us < best_us) {
                 pick = i;
                 best_us = us;
             }
         }
+        if (small >= 0 && (pick >= 0 ? small_us < best_us : (reg_us < 0.0 || small_us < reg_us))) pick = small;
     }
     if (pick < 0) {
         // No estimated build fits (unaligned rows, or offsets past 32 bits):
@@ -571,7 +595,8 @@ void fill_info(const Variant &v, int id, mgemm_variant_info *out)
     // two stages of bk in either path (fp64 rows carry a 2-element pad,
     // gemm_f64.hpp; the DMA path's PIPE 1 has four of bk/2)
     const int pad = v.dtype == MGEMM_F64 ? 2 : 0;
-    out->lds_bytes = (v.pipe == 3 ? 1 : 2) * (v.bm + v.bn + 2 * pad) * v.bk * elem_size(v.dtype);
+    out->lds_bytes = v.pipe == 6 ? v.wn * 16 * 20 * 4  // small builds: one padded partial tile per wave
+                                 : (v.pipe == 3 ? 1 : 2) * (v.bm + v.bn + 2 * pad) * v.bk * elem_size(v.dtype);
     out->pipe = v.pipe;
     std::snprintf(out->name, sizeof(out->name), "%s", v.name);
 }

@@ -6,6 +6,7 @@
 
 #include "gemm_f64.hpp"
 #include "gemm_kernel.hpp"
+#include "gemm_small.hpp"
 
 namespace mgemm {
 
@@ -22,8 +23,14 @@ using LaunchFn = hipError_t (*)(const KernelArgs &, unsigned grid, hipStream_t);
 // least squares over the launches of at least two rounds; solo: launches of
 // 256 workgroups).  tk == 0: no estimate; such a build runs only when asked
 // for by name or when no estimated build fits.
+// Small-problem builds (pipe 6) have workgroups of a few dozen registers that
+// share CUs, so rounds do not apply: their launch takes t0 + max(tk*K, tw*W*K)
+// us for W workgroups, the longer of one workgroup's load-then-multiply chain
+// and the whole launch's rate (measured from HIP-graph replays over shapes
+// from 64^3 to 1024x1024x256).
 struct Cost {
     float t0, tk, reg, solo;
+    float tw = 0.0f;  // us per workgroup per unit of K (pipe 6 only)
 };
 
 struct Variant {
@@ -33,7 +40,8 @@ struct Variant {
     bool vec;             // needs 16-byte aligned A/B rows (dwordx4 loads)
     int pipe;             // DMA-path schedule (1: 4 stages of bk/2, 2: 2 stages of bk,
                           // 3: 1 stage of bk, K <= bk only, 4: 4-byte copies, 2 stages
-                          // of bk, every tile)
+                          // of bk, every tile); 6: small-problem kernel (gemm_small.hpp,
+                          // registers only, K <= bk, wn waves sharing K)
     const char *name;
     LaunchFn fn[2][2];    // [transA][transB], fp32 C (int32 C for int8, double C for fp64 inputs)
     LaunchFn fn16[2][2];  // [transA][transB], C in the inputs' 16-bit type (16-bit tables only)
@@ -57,6 +65,15 @@ hipError_t launch_gemm_sk(const KernelArgs &a, unsigned grid, hipStream_t s)
     void *args[] = {&copy};
     return hipLaunchKernel(reinterpret_cast<const void *>(&gemm_sk_kernel<T, BM, BN, BK, WM, WN, TA, TB, V, D, CT>),
                            dim3(grid), dim3(WM * WN * 64), args, 0, s);
+}
+
+template <int W, int NCH, bool TA, bool TB>
+hipError_t launch_gemm_small(const KernelArgs &a, unsigned grid, hipStream_t s)
+{
+    KernelArgs copy = a;
+    void *args[] = {&copy};
+    return hipLaunchKernel(reinterpret_cast<const void *>(&gemm_small_kernel<W, NCH, TA, TB>), dim3(grid),
+                           dim3(W * 64), args, 0, s);
 }
 
 template <int BM, int BN, int BK, int WM, int WN, bool TA, bool TB, bool V>
@@ -94,6 +111,13 @@ hipError_t launch_gemm_f64(const KernelArgs &a, unsigned grid, hipStream_t s)
 #define MGEMM_SK_I8(BM, BN, BK, WM, WN, V, D)                                                 \
     {{nullptr, launch_gemm_sk<int8_t, BM, BN, BK, WM, WN, false, true, V, D, int32_t>},       \
      {nullptr, nullptr}}
+// small fp32 problems: 16x16 tiles, W waves sharing K <= W * NCH * 32 (pipe 6)
+#define MGEMM_VARIANT_F32_SMALL(W, NCH, NAME, ...)                                          \
+    {0, 16, 16, (W) * (NCH) * 32, 1, W, false, 6, NAME,                                      \
+     {{launch_gemm_small<W, NCH, false, false>, launch_gemm_small<W, NCH, false, true>},     \
+      {launch_gemm_small<W, NCH, true, false>, launch_gemm_small<W, NCH, true, true>}},      \
+     {{nullptr, nullptr}, {nullptr, nullptr}}, __VA_ARGS__}
+
 // fp32 inputs: fp32 C only
 #define MGEMM_VARIANT_F32_D(BM, BN, BK, WM, WN, V, D, NAME, ...)                              \
     {0, BM, BN, BK, WM, WN, V, D, NAME, MGEMM_LAUNCHERS(float, BM, BN, BK, WM, WN, V, D, float), \

@@ -86,7 +86,7 @@ def test_variant_table():
         assert v["id"] == i
         assert v["threads"] == v["waves_m"] * v["waves_n"] * 64
         assert v["lds_bytes"] <= 160 * 1024
-        assert v["pipe"] in (1, 2, 3, 4)
+        assert v["pipe"] in (1, 2, 3, 4, 6)
         assert v["name"].startswith("mgemm_")
     assert {v["dtype"] for v in vs} == {0, 1, 2, 3, 5}
     info = _lib.VariantInfo()
@@ -153,10 +153,14 @@ def test_broadcast_strides_allowed():
 def test_unaligned_operands_get_unaligned_variant():
     info, _ = sel(M=1000, N=1027, K=999, lda=999, ldb=1027, ldc=1027)
     assert info["name"].endswith("_u")
-    info, _ = sel(A=ALIGNED + 4)
+    big = dict(M=1024, N=1024, K=1024, lda=1024, ldb=1024, ldc=1024)
+    info, _ = sel(A=ALIGNED + 4, **big)
     assert info["name"].endswith("_u")
-    info, _ = sel()
+    info, _ = sel(**big)
     assert not info["name"].endswith("_u")
+    # the small-problem build loads one element at a time: any 4-byte alignment
+    info, _ = sel(A=ALIGNED + 4)
+    assert info["name"].startswith("mgemm_f32_16x16")
 
 
 def test_selection_for_the_named_workloads():
@@ -290,14 +294,41 @@ def test_fp64_rules_without_a_gpu():
     assert not info["name"].endswith("_u")
 
 
+def test_small_problem_choice():
+    # the 16x16 small-problem builds take small grids, and only those
+    name = lambda M, N, K, **kw: sel(M=M, N=N, K=K, **kw)[0]["name"]
+    assert name(256, 256, 256) == "mgemm_f32_16x16_k4w_256"
+    assert name(128, 128, 128) == "mgemm_f32_16x16_k4w_256"
+    assert name(256, 256, 1024) == "mgemm_f32_16x16_k8w_1024"
+    assert name(128, 128, 1024) == "mgemm_f32_16x16_k8w_1024"
+    for M, N, K in ((512, 512, 512), (512, 512, 256), (1024, 1024, 256), (256, 256, 2048),
+                    (4096, 4096, 4096)):
+        assert "16x16" not in name(M, N, K), (M, N, K)
+    # unaligned rows: the small build must beat the register path's estimate
+    assert "16x16" not in name(4096, 4096, 4096, lda=4097, ldb=4097)
+    assert "16x16" not in name(1024, 1024, 1000, lda=2_100_001, ldb=2_100_001)
+    assert name(256, 256, 256, lda=257, ldb=257) == "mgemm_f32_16x16_k4w_256"
+    # a batch multiplies the workgroups: 64 entries of 256^3 are a large launch
+    assert "16x16" not in name(256, 256, 256, batch=64, strideA=256 * 256, strideB=256 * 256,
+                               strideC=256 * 256)
+
+
 def test_force_variant_roundtrip():
     vs = mg.variants()
-    f32_ids = [v["id"] for v in vs if v["dtype"] == 0]
+    f32_ids = [v["id"] for v in vs if v["dtype"] == 0 and v["pipe"] != 6]
+    small = [v for v in vs if v["dtype"] == 0 and v["pipe"] == 6]
     bf16_ids = [v["id"] for v in vs if v["dtype"] == 2]
     try:
         mg.force_variant("f32", f32_ids[-1])
         info, _ = sel(M=4096, N=4096, K=4096)
         assert info["id"] == f32_ids[-1]
+        # a small-problem build runs forced while K fits its waves' share, not beyond
+        for v in small:
+            mg.force_variant("f32", v["id"])
+            assert sel(M=300, N=200, K=v["block_k"])[0]["id"] == v["id"]
+            assert sel(M=300, N=200, K=v["block_k"] + 1)[0]["id"] != v["id"]
+            # nor for split-K's chunks (no shorter last chunk of its own)
+            assert mg.splitk_plan("f32", 300, 200, 2 * v["block_k"], 4)["variant"]["id"] != v["id"]
         with pytest.raises(mg.MgemmError):
             mg.force_variant("f32", bf16_ids[0])
     finally:

@@ -99,12 +99,14 @@ def _assert_selected(p, v):
     assert info["name"] == v["name"], (info["name"], v["name"])
 
 
-def variants_of(dtype, one_stage=False):
-    """The dtype's builds; the one-stage ones (pipe 3, K of one slab only) when asked."""
+def variants_of(dtype, one_stage=False, small=False):
+    """The dtype's tile builds; the one-stage ones (pipe 3, K of one slab only) or the
+    small-problem ones (pipe 6, K at most their block_k) when asked."""
     code = {"f32": 0, "f16": 1, "bf16": 2, "i8": 3, "f64": 5}[dtype]
     if not torch.cuda.is_available():
         return []
-    return [v for v in mg.variants() if v["dtype"] == code and (v["pipe"] == 3) == one_stage]
+    return [v for v in mg.variants() if v["dtype"] == code and (v["pipe"] == 3) == one_stage
+            and (v["pipe"] == 6) == small]
 
 
 # ------------------------------------------------------------------ every variant, every op
@@ -661,6 +663,29 @@ def test_one_stage_builds_shallow_k_exact(dtype):
 
 
 # ------------------------------------------------------------------ shapes from the pages
+
+def test_small_problem_builds_exact_and_in_tolerance():
+    # 16x16 tiles whose waves share K: every transpose, edge tiles, K tails inside a
+    # wave's share and in the last chunk, a K that leaves waves empty, batches, NaN in
+    # the padding and in a beta = 0 C; integer data bit-exact, floats in tolerance
+    for v in variants_of("f32", small=True):
+        mg.force_variant("f32", v["id"])
+        kmax = v["block_k"]
+        for tA, tB in itertools.product((False, True), repeat=2):
+            for (M, N, K, batch) in ((256, 256, min(256, kmax), 1), (37, 45, kmax, 1),
+                                     (100, 130, kmax - 29, 2), (16, 16, 1, 1), (1, 1, 5, 3),
+                                     (70, 33, 40, 1)):
+                for dist, exact in (("int", True), ("uniform", False)):
+                    p = wl.Problem("f32", M, N, K, transA=tA, transB=tB, batch=batch,
+                                   alpha=1.5, beta=0.5 if dist == "int" else 0.0, dist=dist,
+                                   int_lo=-20, int_hi=20, c_dist=dist, seed=150 + K,
+                                   lda=(M if tA else K) + 3, ldb=(K if tB else N) + 5, ldc=N + 2,
+                                   pad_value=float("nan"))
+                    _assert_selected(p, v)
+                    full_check(p, exact=exact, c_fill=float("nan"),
+                               what=f"{v['name']} {dist} tA={int(tA)} tB={int(tB)}")
+    mg.force_variant("f32", None)
+
 
 def test_csdn_ragged_integer_example():
     # A 47 x 804, B 804 x 53, rand() % 100 values (CSDN tile-algorithm page, main)
