@@ -224,17 +224,11 @@ def summarize_case(case, d, copy_dir):
         lines += ["splitk_chunks: %d of %d" % (plan["chunks"], plan["chunk_len"]),
                   "reduce_kernel_average_ns: " + _fmt(ravg, "%.0f"),
                   "tflops_both_kernels: " + _fmt(both, "%.2f")]
-    if p.streamk is not None:   # the stream-K launch above, then the fix-up of split tiles
-        fix = _dispatch_durations(os.path.join(d, "trace"), "sk_fixup")
-        fix = fix[PROFILE_WARMUP:] if len(fix) > PROFILE_WARMUP else fix
-        favg = _mean(fix)
-        both = p.flops / ((avg + favg) * 1e-9) / 1e12 if avg and favg else None
+    if p.streamk is not None:   # one launch: split tiles are completed by their last contributor
         plan = mg.streamk_plan(dt, p.M, p.N, p.K, p.streamk, transA=int(p.transA),
                                transB=int(p.transB), lda=p.lda, ldb=p.ldb)
         lines += ["streamk: %d workgroups over %d tiles of %d iterations of %d" %
-                  (plan["workgroups"], plan["tiles"], plan["iterations"], plan["k_per_iteration"]),
-                  "fixup_kernel_average_ns: " + _fmt(favg, "%.0f"),
-                  "tflops_both_kernels: " + _fmt(both, "%.2f")]
+                  (plan["workgroups"], plan["tiles"], plan["iterations"], plan["k_per_iteration"])]
     if case in HBM_BOUND and avg:
         gbs = algo / (avg * 1e-9) / 1e9
         lines += ["algorithmic_gbs_at_average: %.1f" % gbs,
@@ -317,7 +311,8 @@ def launcher(p, dA, dB, dC):
         import torch
         need = mg.streamk_plan(p.dtype, p.M, p.N, p.K, p.streamk, transA=int(p.transA),
                                transB=int(p.transB), A=dA, lda=p.lda, B=dB, ldb=p.ldb)["workspace_bytes"]
-        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dA.device)  # outside the timing
+        # zero-filled once: the arrival counters at its start; every call leaves them zero
+        ws = torch.zeros(max(need, 16), dtype=torch.uint8, device=dA.device)  # outside the timing
         return lambda: mg.gemm_streamk(p.dtype, p.c_dtype, int(p.transA), int(p.transB), p.M, p.N,
                                        p.K, p.alpha, dA, p.lda, dB, p.ldb, p.beta, dC, p.ldc,
                                        workgroups=p.streamk, workspace=ws)

@@ -26,6 +26,10 @@ ELEM_SIZE = {F32: 4, F16: 2, BF16: 2, I8: 1, I32: 4, F64: 8}
 STATUS = {0: "MGEMM_OK", 1: "MGEMM_INVALID_ARG", 2: "MGEMM_HIP_ERROR", 3: "MGEMM_SCRATCH_TOO_SMALL"}
 # fixed device scratch of gemm_splitk_noalloc (MGEMM_NOALLOC_SCRATCH_BYTES in include/mgemm.h)
 NOALLOC_SCRATCH_BYTES = 64 << 20
+# zeroed prefix of a gemm_streamk workspace and the workgroup cap
+# (MGEMM_STREAMK_COUNTER_BYTES, MGEMM_STREAMK_MAX_WORKGROUPS in include/mgemm.h)
+STREAMK_COUNTER_BYTES = 64 << 10
+STREAMK_MAX_WORKGROUPS = 16384
 
 
 class MgemmError(RuntimeError):
@@ -175,16 +179,18 @@ def _stream(stream, device):
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def _workspace_on(nbytes, device, stream, launch):
+def _workspace_on(nbytes, device, stream, launch, zero=False):
     """A torch-allocated workspace for a call launched on stream handle `launch`.  It is
-    allocated on that stream, so that torch's caching allocator, once the tensor is
-    dropped, hands the block only to work ordered after the call's kernels (allocated on
-    another stream, the block could be reused while they still write it)."""
+    allocated (and, with `zero`, zero-filled) on that stream, so that the fill precedes the
+    call and torch's caching allocator, once the tensor is dropped, hands the block only to
+    work ordered after the call's kernels (allocated on another stream, the block could be
+    reused while they still write it)."""
     import torch
+    make = torch.zeros if zero else torch.empty
     if stream is None:   # the launch stream is torch's current stream
-        return torch.empty(nbytes, dtype=torch.uint8, device=device)
+        return make(nbytes, dtype=torch.uint8, device=device)
     with torch.cuda.stream(torch.cuda.ExternalStream(launch, device=device)):
-        return torch.empty(nbytes, dtype=torch.uint8, device=device)
+        return make(nbytes, dtype=torch.uint8, device=device)
 
 
 def _check(status: int, what: str):
@@ -373,8 +379,9 @@ def streamk_plan(in_dtype, M, N, K, workgroups=0, transA=0, transB=0, A=1 << 20,
 def gemm_streamk(in_dtype, c_dtype, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
                  workgroups=0, workspace=None, stream=None):
     """Stream-K GEMM (single matrix).  `workspace` is a device tensor (or int address) of at
-    least streamk_plan(...)["workspace_bytes"] bytes; None allocates one with torch on C's
-    device."""
+    least streamk_plan(...)["workspace_bytes"] bytes whose first STREAMK_COUNTER_BYTES are
+    zero (zero-fill it once; every call leaves them zero); None allocates a zero-filled one
+    with torch on C's device."""
     dt = DTYPE_CODES.get(in_dtype, in_dtype)
     ct = DTYPE_CODES.get(c_dtype, c_dtype)
     es = ELEM_SIZE[dt]
@@ -388,7 +395,7 @@ def gemm_streamk(in_dtype, c_dtype, transA, transB, M, N, K, alpha, A, lda, B, l
                          B=pb or 0, ldb=ldb)["workspace_bytes"] if workgroups >= 0 else 0)
     launch = _stream(stream, dev)
     if workspace is None and need > 0:
-        workspace = _workspace_on(need, dev, stream, launch)
+        workspace = _workspace_on(need, dev, stream, launch, zero=True)
     if workspace is None:
         pw, wbytes = None, 0
     elif isinstance(workspace, int):

@@ -62,6 +62,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef u32x4 u32x4_a4 __attribute__((aligned(4)));  // 16 bytes at a 4-byte aligned address
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
@@ -81,14 +82,16 @@ struct KernelArgs {
     int fast_ok;      // operand tiles addressable with 32-bit byte offsets
     double alpha_d, beta_d;  // alpha and beta of fp64 GEMM
     int k_tail, tail_batch;  // batch entry tail_batch runs K = k_tail (split-K's last chunk); -1: none
-    // stream-K launches (gemm_sk_kernel, sk_fixup_kernel): every tile is
-    // sk_iters K-iterations of sk_unit elements (the last one may be
-    // shorter); the sk_total = tiles * sk_iters iterations, tile-major, are
-    // shared out evenly over sk_grid workgroups; sk_part holds two partial
-    // tiles per workgroup
+    // stream-K launches (gemm_sk_kernel): every tile is sk_iters
+    // K-iterations of sk_unit elements (the last one may be shorter); the
+    // sk_total = tiles * sk_iters iterations, tile-major, are shared out
+    // evenly over sk_grid workgroups; sk_part holds two partial tiles per
+    // workgroup, sk_count one arrival counter per workgroup (zero between
+    // launches)
     int sk_iters, sk_unit, sk_grid;
     int64_t sk_total;
     void *sk_part;
+    unsigned *sk_count;
 };
 
 // ---------------------------------------------------------------------------
@@ -756,7 +759,7 @@ struct DmaPath {
     static constexpr bool A_TR = TA && !F32, B_TR = !TB && !F32;
     // raised priority while multiplying (not with 4-byte copies, whose four
     // times as many copy instructions lost 4% on the ragged fp32 shape)
-    static constexpr bool PRIO = !(PIPE == 4) && (F32 || B_KC);
+    static constexpr bool PRIO = !DW && (F32 || B_KC);
     // 256x256 16-bit tiles whose B is MN-contiguous (transposing fragment
     // reads): each group's fragment reads are issued at two per MFMA from
     // its start, and after the slab barrier the copies of the next slab
@@ -1392,10 +1395,138 @@ gemm_kernel(KernelArgs p)
 // tile.  A segment that covers a whole tile writes C as gemm_kernel does;
 // any other writes its sums (fp32; int32 for int8 inputs) to one of the
 // workgroup's two partial tiles in sk_part, slot 0 for its first segment
-// and slot 1 for its last, and sk_fixup_kernel then adds the partials of
-// each split tile in K order.  The host keeps G <= T, so every workgroup
-// has at least one pair; nothing waits on another workgroup.
+// and slot 1 for its last.  Only a workgroup's first and last segments can
+// be partial, so a split tile's contributors are the consecutive
+// workgroups g0..g1 that own its first and last iterations, and each
+// workgroup is g0 of at most one split tile (the one its range ends in).
+//
+// Completion without a second launch: a contributor writes its partial tile
+// with agent-scope stores, waits until they are acknowledged (then visible
+// to every XCD), and counts itself in at sk_count[g0] with a wrapping
+// increment (limit g1 - g0).  The contributor that reads g1 - g0 is the last
+// to arrive; the same increment has put the counter back to zero, ready for
+// the next launch.  That workgroup reads the partials with agent-scope loads,
+// adds them in ascending K order, g0 first, and writes C.  No workgroup
+// waits on another, and the sum order is fixed, whichever arrives last.
+// (Agent-scope fences instead cost an L2-wide write-back per contribution
+// and an L2 invalidate per tile: 1000x1027x999 fp32 took 108 us instead of
+// 33.)  The host keeps G <= T, so every workgroup has at least one pair.
 // ---------------------------------------------------------------------------
+
+// Agent-scope accesses (one 32-bit value, or two adjacent as one 64-bit
+// store): stores written through to the device-wide point of coherence and
+// loads served from it, so partial sums pass between XCDs (each with its own
+// L2) without an L2-wide write-back or invalidate.
+__device__ __forceinline__ void sk_put2(void *at, uint32_t lo, uint32_t hi)
+{
+    __hip_atomic_store(static_cast<uint64_t *>(at), (uint64_t)hi << 32 | lo, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void sk_put1(void *at, uint32_t v)
+{
+    __hip_atomic_store(static_cast<uint32_t *>(at), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// A split tile's partial sums (fp32 bits, or int32 for int8 inputs) into
+// `part`, the whole BM x BN tile row-major, with the C mapping of the
+// epilogue below (IL_A / IL_B as there).
+template <int IL_A, int IL_B, int TM, int TN, int WTM, int WTN, int WN, int BN>
+__device__ __forceinline__ void sk_store_partial(void *part, const f32x16 (&acc)[TM][TN])
+{
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    const int li = lane & 31, lh = lane >> 5;
+    uint32_t *P = static_cast<uint32_t *>(part);
+    constexpr bool VCOL = IL_B > 1;  // TN adjacent columns per lane
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int ip = 8 * (r >> 2) + 4 * lh + (r & 3);
+#pragma unroll
+        for (int t = 0; t < TM; ++t) {
+            uint32_t *prow = P + (wm * WTM + (IL_A == 1 ? 32 * t + ip : TM * ip + t)) * BN;
+            if constexpr (VCOL && TN % 2 == 0) {
+#pragma unroll
+                for (int u = 0; u < TN; u += 2)
+                    sk_put2(prow + wn * WTN + TN * li + u, acc_u32(acc[t][u], r), acc_u32(acc[t][u + 1], r));
+            } else {
+#pragma unroll
+                for (int u = 0; u < TN; ++u)
+                    sk_put1(prow + wn * WTN + (VCOL ? TN * li + u : 32 * u + li), acc_u32(acc[t][u], r));
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ uint32_t sk_get1(const uint32_t *at)
+{
+    return __hip_atomic_load(at, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The last contributor's share of stream-K: split tile (bidx, m0, n0), whose
+// iterations start at a0 and belong to workgroups g0..g1, this one (me)
+// among them.  Its own sums are still in `acc`; the others' partial tiles
+// are read at the same C positions (the epilogue's mapping), the terms are
+// added in ascending K order, g0 first (fp32, or wrapping int32 for int8
+// inputs), and the epilogue writes C.
+template <bool EDGE, int IL_A, int IL_B, int TM, int TN, int WTM, int WTN, int WN, int BM, int BN, typename PT,
+          typename CT>
+__device__ __forceinline__ void sk_finish(const KernelArgs &p, int bidx, int m0, int n0, int64_t a0, int64_t g0,
+                                          int64_t g1, int64_t me, const f32x16 (&acc)[TM][TN])
+{
+    constexpr int TSZ = BM * BN;
+    constexpr bool INT = __is_same(PT, int32_t);
+    constexpr bool VCOL = IL_B > 1;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    const int li = lane & 31, lh = lane >> 5;
+    const uint32_t *part = static_cast<const uint32_t *>(p.sk_part);
+    const int first_slot = p.sk_total * g0 / p.sk_grid == a0 ? 0 : 1;
+    f32x16 sum[TM][TN];
+    for (int64_t g = g0; g <= g1; ++g) {
+        const bool first = g == g0;
+        if (g == me) {
+#pragma unroll
+            for (int t = 0; t < TM; ++t)
+#pragma unroll
+                for (int u = 0; u < TN; ++u) {
+                    if (first) {
+                        sum[t][u] = acc[t][u];
+                    } else if constexpr (INT) {
+                        const u32x16 x = __builtin_bit_cast(u32x16, sum[t][u]) + __builtin_bit_cast(u32x16, acc[t][u]);
+                        sum[t][u] = __builtin_bit_cast(f32x16, x);
+                    } else {
+                        sum[t][u] = sum[t][u] + acc[t][u];
+                    }
+                }
+            continue;
+        }
+        const uint32_t *pg = part + (g * 2 + (first ? first_slot : 0)) * TSZ;
+#pragma unroll
+        for (int t = 0; t < TM; ++t)
+#pragma unroll
+            for (int u = 0; u < TN; ++u) {
+                const int col = wn * WTN + (VCOL ? TN * li + u : 32 * u + li);
+                u32x16 v;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int ip = 8 * (r >> 2) + 4 * lh + (r & 3);
+                    const int row = wm * WTM + (IL_A == 1 ? 32 * t + ip : TM * ip + t);
+                    v[r] = sk_get1(pg + row * BN + col);
+                }
+                if (first) {
+                    sum[t][u] = __builtin_bit_cast(f32x16, v);
+                } else if constexpr (INT) {
+                    sum[t][u] = __builtin_bit_cast(f32x16, __builtin_bit_cast(u32x16, sum[t][u]) + v);
+                } else {
+                    sum[t][u] = sum[t][u] + __builtin_bit_cast(f32x16, v);
+                }
+            }
+    }
+    epilogue<EDGE, IL_A, IL_B, TM, TN, WTM, WTN, WN, CT>(p, bidx, m0, n0, sum);
+}
+
 template <typename T, int BM, int BN, int BK, int WM, int WN, bool TA, bool TB, bool VECOK, int PIPE,
           typename CT>
 __global__ void __launch_bounds__(WM * WN * 64)
@@ -1409,6 +1540,7 @@ gemm_sk_kernel(KernelArgs p)
     constexpr int LDS = ALL_DMA ? D::LDS_BYTES
                         : (VECOK && D::LDS_BYTES > R::LDS_BYTES) ? D::LDS_BYTES : R::LDS_BYTES;
     __shared__ __attribute__((aligned(1024))) char smem[LDS];
+    __shared__ int last_arrival;
     const int L = logical_wg();
     const int iters = p.sk_iters;
     const int64_t beg = p.sk_total * L / p.sk_grid, end = p.sk_total * (L + 1) / p.sk_grid;
@@ -1455,20 +1587,46 @@ gemm_sk_kernel(KernelArgs p)
                 epilogue<true, R::IL_A, R::IL_B, TM, TN, WTM, WTN, WN, CT>(pk, bidx, m0, n0, acc);
             }
         } else {
-            // the whole BM x BN tile, row-major, into partial slot (L, first or last)
-            KernelArgs q = p;
-            q.C = static_cast<PT *>(p.sk_part) + ((int64_t)L * 2 + (it == beg ? 0 : 1)) * (BM * BN);
-            q.ldc = BN;
-            q.strideC = 0;
-            q.M = BM;
-            q.N = BN;
-            q.alpha = 1.0f;
-            q.beta = 0.0f;
-            q.alpha_i = 1;
-            q.beta_i = 0;
-            q.c_vec = 1;
-            if (dma) epilogue<false, D::IL_A, D::IL_B, TM, TN, WTM, WTN, WN, PT>(q, 0, 0, 0, acc);
-            else     epilogue<false, R::IL_A, R::IL_B, TM, TN, WTM, WTN, WN, PT>(q, 0, 0, 0, acc);
+            const int64_t a0 = (int64_t)tile * iters;
+            const int64_t g0 = ((a0 + 1) * p.sk_grid - 1) / p.sk_total;
+            const int64_t g1 = ((a0 + iters) * p.sk_grid - 1) / p.sk_total;
+            unsigned *count = p.sk_count + g0;
+            const unsigned others = (unsigned)(g1 - g0);
+            // Each contributor counts in once.  If all the others have, this
+            // workgroup is the last: it finishes from its registers without
+            // writing its partial tile, and clears the counter for the next launch.
+            if (threadIdx.x == 0)
+                last_arrival = __hip_atomic_load(count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == others;
+            __syncthreads();
+            // one value for the whole workgroup (read back from LDS): a uniform branch
+            bool last = __builtin_amdgcn_readfirstlane(last_arrival);
+            if (!last) {
+                // the whole BM x BN tile, row-major, into partial slot (L, first or last)
+                void *slot = static_cast<PT *>(p.sk_part) + ((int64_t)L * 2 + (it == beg ? 0 : 1)) * (BM * BN);
+                if (dma) sk_store_partial<D::IL_A, D::IL_B, TM, TN, WTM, WTN, WN, BN>(slot, acc);
+                else     sk_store_partial<R::IL_A, R::IL_B, TM, TN, WTM, WTN, WN, BN>(slot, acc);
+                // The agent-scope stores have reached the point of coherence once
+                // they are acknowledged: every wave waits for its own before the
+                // barrier, so the workgroup counts in only after all of its partial
+                // sums are visible to every XCD.
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                __syncthreads();
+                if (threadIdx.x == 0)
+                    last_arrival = __builtin_amdgcn_atomic_inc32(count, others, __ATOMIC_RELAXED, "agent") == others;
+                __syncthreads();
+                last = __builtin_amdgcn_readfirstlane(last_arrival);
+            } else if (threadIdx.x == 0) {
+                __hip_atomic_store(count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            // (the range-checked epilogue for every finished tile: one more
+            // instance of the unchecked one ran the 16-bit 4-byte-copy builds
+            // out of scalar registers for their copies' buffer resources)
+            if (last) {
+                if (dma) sk_finish<true, D::IL_A, D::IL_B, TM, TN, WTM, WTN, WN, BM, BN, PT, CT>(
+                             pk, bidx, m0, n0, a0, g0, g1, L, acc);
+                else     sk_finish<true, R::IL_A, R::IL_B, TM, TN, WTM, WTN, WN, BM, BN, PT, CT>(
+                             pk, bidx, m0, n0, a0, g0, g1, L, acc);
+            }
         }
         it += k1 - k0;
         __syncthreads();  // the next segment refills the LDS stages

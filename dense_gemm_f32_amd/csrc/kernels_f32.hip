@@ -30,6 +30,9 @@ const Variant *f32_variants(int *count)
         // stages gained nothing)
         MGEMM_VARIANT_F32_D(64, 64, 32, 2, 2, true, 2, "mgemm_f32_64x64x32_w2x2_d2", {2.1f, 0.0166f, 1.5f, 1.4f},
                             MGEMM_SK(float, 64, 64, 32, 2, 2, true, 2)),
+        // (four stages of 32 with 4-byte copies, ragged 1000x1027x999: one pass
+        // 49.0 against 50.6 us, stream-K 36.4 against 37.8, split-K 44.2
+        // against 39.9; not kept)
         MGEMM_VARIANT_F32_D(64, 64, 32, 2, 2, false, 4, "mgemm_f32_64x64x32_w2x2_d4_u",
                             {2.9f, 0.0185f, 1.0f, 1.6f}, MGEMM_SK(float, 64, 64, 32, 2, 2, false, 4)),
         MGEMM_VARIANT_F32(64, 64, 32, 2, 2, false, "mgemm_f32_64x64x32_w2x2_u", {},

@@ -57,6 +57,10 @@ const Variant *variant_by_id(int id)
     return nullptr;
 }
 
+// Builds whose tiles are copied 4 bytes at a time (pipe 4): one path for
+// every tile, rows only 4-byte aligned, offsets within 32 bits.
+bool dw_copies(const Variant &v) { return v.pipe == 4; }
+
 int elem_size(int dtype)
 {
     return dtype == MGEMM_F64 ? 8 : dtype == MGEMM_F32 || dtype == MGEMM_I32 ? 4 : dtype == MGEMM_I8 ? 1 : 2;
@@ -179,7 +183,7 @@ mgemm_status validate_and_plan(int dtype, int c_dtype, int transA, int transB, i
     // slab) and the last chunk takes the rest of k_all, so the chunk multiple
     // is checked on k_all: the last chunk's remainder is k_all's.
     auto offsets_ok = [&](const Variant &v) {
-        return (v.pipe != 4 || (a.fast_ok && dw_rows)) &&
+        return (!dw_copies(v) || (a.fast_ok && dw_rows)) &&
                (v.pipe != 3 || (a.fast_ok && K <= v.bk && k_all % (16 / es) == 0)) &&
                // the small-problem kernel: its waves share at most bk of K, and it
                // has no shorter last chunk (split-K) of its own
@@ -245,11 +249,11 @@ mgemm_status validate_and_plan(int dtype, int c_dtype, int transA, int transB, i
                 continue;
             }
             if ((v.vec && !vec_ok) || !offsets_ok(v)) {
-                if (v.pipe != 4 && (reg_us < 0.0 || us * v.cost.reg < reg_us)) reg_us = us * v.cost.reg;
+                if (!dw_copies(v) && (reg_us < 0.0 || us * v.cost.reg < reg_us)) reg_us = us * v.cost.reg;
                 continue;
             }
             // the 16-byte DMA path takes every tile when K is a multiple of 16 bytes
-            const bool reg_tiles = v.pipe != 4 && (!a.fast_ok || K % (16 / es) != 0);
+            const bool reg_tiles = !dw_copies(v) && (!a.fast_ok || K % (16 / es) != 0);
             if (reg_tiles) us *= v.cost.reg;
             if (pick < 0 || us < best_us) {
                 pick = i;
@@ -451,13 +455,17 @@ mgemm_status run_splitk(int dtype, int c_dtype, int transA, int transB, int64_t 
 // ---------------------------------------------------------------------------
 // Stream-K.  One launch of G workgroups shares the (tile, K-iteration) pairs
 // of the whole product evenly (gemm_sk_kernel), so a tile count that leaves
-// the last round of CUs part-empty costs no idle round; a fix-up launch of
-// one workgroup per tile then completes the tiles that were split between
-// workgroups, from the partial tiles in the caller's workspace
-// ([G][2][bm*bn], fp32; int32 for int8).  Iterations are the split-K
-// granule of K (whole slabs of every build).
+// the last round of CUs part-empty costs no idle round; the last workgroup
+// to finish its part of a split tile completes it in the same launch.  The
+// caller's workspace holds the arrival counters (MGEMM_STREAMK_COUNTER_BYTES
+// at its start, one 32-bit word per workgroup, zero between calls) and then
+// the partial tiles ([G][2][bm*bn], fp32; int32 for int8).  The counters
+// keep one place in every call, so calls of any size can share a workspace
+// without one call's partial tiles landing on another's counters.
+// Iterations are the split-K granule of K (whole slabs of every build).
 // ---------------------------------------------------------------------------
 constexpr int64_t kStreamkWorkgroups = 512;  // default: two per CU
+static_assert(MGEMM_STREAMK_MAX_WORKGROUPS * 4 <= MGEMM_STREAMK_COUNTER_BYTES, "one counter per workgroup");
 
 struct StreamPlan {
     Plan plan;  // the stream-K launch (kind GEMM), or SCALE / NOTHING
@@ -482,6 +490,7 @@ mgemm_status make_streamk_plan(int dtype, int c_dtype, int transA, int transB, i
     const int64_t tiles = (int64_t)a.tiles_m * a.tiles_n;
     const int64_t total = tiles * iters;
     int64_t g = workgroups > 0 ? workgroups : kStreamkWorkgroups;
+    if (g > MGEMM_STREAMK_MAX_WORKGROUPS) g = MGEMM_STREAMK_MAX_WORKGROUPS;
     if (g > total) g = total;  // every workgroup gets at least one iteration
     // the kernels form total * (workgroup + 1) in 64 bits
     if (g > INT_MAX || iters > INT_MAX || total > ((int64_t)1 << 62) / g) return MGEMM_INVALID_ARG;
@@ -489,10 +498,12 @@ mgemm_status make_streamk_plan(int dtype, int c_dtype, int transA, int transB, i
     a.sk_unit = (int)unit;
     a.sk_grid = (int)g;
     a.sk_total = total;
-    a.sk_part = W;
+    a.sk_count = static_cast<unsigned *>(W);
+    a.sk_part = W ? static_cast<char *>(W) + MGEMM_STREAMK_COUNTER_BYTES : nullptr;
     sp->plan.grid = g;
     sp->tiles = tiles;
-    sp->workspace_bytes = g * 2 * (int64_t)v.bm * v.bn * elem_size(partial_dtype(dtype));
+    sp->workspace_bytes =
+        MGEMM_STREAMK_COUNTER_BYTES + g * 2 * (int64_t)v.bm * v.bn * elem_size(partial_dtype(dtype));
     return MGEMM_OK;
 }
 
@@ -515,9 +526,6 @@ mgemm_status run_streamk(int dtype, int c_dtype, int transA, int transB, int64_t
     const LaunchFn fn = sp.plan.var->sk[transA][transB];
     if (fn == nullptr) return MGEMM_INVALID_ARG;
     err = fn(sp.plan.args, (unsigned)sp.plan.grid, stream);
-    if (err == hipSuccess)
-        err = launch_sk_fixup(c_dtype, sp.plan.args, sp.plan.var->bm, sp.plan.var->bn, (unsigned)sp.tiles,
-                              stream);
     return err == hipSuccess ? MGEMM_OK : MGEMM_HIP_ERROR;
 }
 

@@ -151,8 +151,6 @@ const Variant *f64_variants(int *count);
 hipError_t launch_scale_c(int c_dtype, void *C, int M, int N, int64_t ldc, int64_t strideC, int batch,
                           double beta, int beta_i, hipStream_t s);
 
-hipError_t launch_sk_fixup(int c_dtype, const KernelArgs &a, int bm, int bn, unsigned tiles, hipStream_t s);
-
 hipError_t launch_splitk_reduce(int c_dtype, const void *W, int splits, int M, int N, void *C,
                                 int64_t ldc, double alpha, double beta, int alpha_i, int beta_i,
                                 hipStream_t s);

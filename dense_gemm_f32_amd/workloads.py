@@ -210,7 +210,7 @@ def sgemm_ragged_splitk() -> Problem:
 
 def sgemm_ragged_streamk() -> Problem:
     """The ragged SGEMM through stream-K with the default 512 workgroups (two per CU) sharing
-    the 272 tiles' 32 K-iterations each, then the fix-up of the split tiles."""
+    the 272 tiles' 32 K-iterations each; split tiles are completed in the same launch."""
     p = sgemm_ragged()
     p.streamk = 0
     return p

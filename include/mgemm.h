@@ -31,16 +31,17 @@
  * alpha == 0 or K == 0: C = beta * C; A and B are not read.
  * M == 0, N == 0 or batch == 0: nothing is launched; MGEMM_OK.
  * Ownership.  The caller owns A, B and C (device memory, e.g. from PyTorch).
- *   The library allocates, frees and keeps nothing and needs no handle; it
+ *   The library allocates and frees nothing and needs no handle; it
  *   may be called from several host threads at once.  gemm_splitk and
  *   gemm_streamk also take a caller-owned device workspace for their partial
- *   sums (its size comes from mgemm_splitk_plan / mgemm_streamk_plan); no
+ *   sums (its size comes from mgemm_splitk_plan / mgemm_streamk_plan;
+ *   gemm_streamk's starts with arrival counters that must be zero), and
+ *   gemm_splitk_noalloc uses a fixed per-GPU scratch inside the library; no
  *   other entry point uses memory beyond A, B and C.
  * Asynchrony.  Each call validates its arguments on the host, enqueues its
  *   kernels on `stream` (NULL = the default stream) and returns: one kernel,
- *   except gemm_splitk with more than one chunk (the chunk products, then a
- *   reduction kernel) and gemm_streamk (the stream-K kernel, then a fix-up
- *   kernel for the tiles split between workgroups).  Results are ready after
+ *   except gemm_splitk and gemm_splitk_noalloc with more than one chunk
+ *   (the chunk products, then a reduction kernel).  Results are ready after
  *   the stream is synchronised; a workspace must not be reused by another
  *   call until the first call's kernels have finished (same stream: always).
  * Errors.  Invalid arguments are reported synchronously and nothing is
@@ -370,26 +371,35 @@ mgemm_status mgemm_splitk_plan(mgemm_dtype in_dtype, mgemm_op transA, mgemm_op t
  * this entry point is for.  The product is the list of (output tile, K
  * iteration) pairs; one launch of `workgroups` workgroups takes equal
  * consecutive ranges of it, writing whole tiles straight to C and the tiles
- * it splits as partial sums to the workspace; a second launch adds each
- * split tile's partials in ascending K (deterministic), applies alpha and
- * beta and writes C.  Nothing waits on another workgroup.  It pays where
- * the last round of tiles is mostly empty (measured: 1000x1027x999 fp32
- * 50 -> 38.5 us, 1100^3 44 -> 39 us); on grids that fill the device the
- * one-pass entry points are faster, and the automatic plan of gemm_splitk
- * does not choose it.
+ * it splits as partial sums to the workspace.  Each workgroup that wrote
+ * part of a split tile counts itself in on an arrival counter in the
+ * workspace; the last to arrive adds the tile's partials in ascending K
+ * (deterministic, whichever arrives last), applies alpha and beta, writes
+ * C and leaves the counter at zero.  One kernel; nothing waits on another
+ * workgroup.  It pays where the last round of tiles is mostly empty
+ * (1000x1027x999 fp32: 272 tiles of 64x64); on grids that fill the device
+ * the one-pass entry points are faster, and the automatic plan of
+ * gemm_splitk does not choose it.
  *   in_dtype  MGEMM_F32, MGEMM_F16, MGEMM_BF16 (then c_dtype MGEMM_F32) or
  *          MGEMM_I8 (c_dtype MGEMM_I32, transA N, transB T); other pairs
  *          and MGEMM_F64 give MGEMM_INVALID_ARG.
  *   alpha, beta  double, exactly representable as float (int8: integral,
  *          as gemm_strided_batched_ex).
- *   workgroups  n > 0: n workgroups, capped at the number of (tile,
- *          iteration) pairs; 0: 512 (two per CU), capped likewise.
- *   workspace, workspace_bytes  device scratch owned by the caller, 16-byte
+ *   workgroups  n > 0: n workgroups, capped at MGEMM_STREAMK_MAX_WORKGROUPS
+ *          and at the number of (tile, iteration) pairs; 0: 512 (two per
+ *          CU), capped likewise.
+ *   workspace, workspace_bytes  device memory owned by the caller, 16-byte
  *          aligned, at least mgemm_streamk_plan(...).workspace_bytes (0 when
  *          no product is formed: M, N or K zero, or alpha zero, where at
- *          most C = beta * C runs; then it may be NULL).  Two partial tiles per workgroup, fp32 (int32 for
- *          int8), overwritten.  Calls that share a workspace must be ordered
- *          on one stream.
+ *          most C = beta * C runs; then it may be NULL).  Its first
+ *          MGEMM_STREAMK_COUNTER_BYTES are arrival counters and MUST BE ZERO
+ *          when the call's kernel starts: zero-fill a new workspace once
+ *          (hipMemset, torch.zeros); every call leaves them zero when its
+ *          kernel ends, so a workspace is then reusable by calls of any
+ *          size without clearing.  Non-zero counters give wrong C for split
+ *          tiles (never a hang).  The rest holds two partial tiles per
+ *          workgroup, fp32 (int32 for int8), overwritten.  Calls that share
+ *          a workspace must be ordered on one stream.
  * A and B are read, C is read only when beta != 0; layouts, leading
  * dimensions and quick returns are those of gemm_strided_batched_ex with
  * batch 1.  Results differ from the one-pass kernels only by fp32 summation
@@ -399,6 +409,9 @@ mgemm_status mgemm_splitk_plan(mgemm_dtype in_dtype, mgemm_op transA, mgemm_op t
  * workgroups < 0 or a missing, misaligned or short workspace; nothing is
  * launched then.
  */
+#define MGEMM_STREAMK_COUNTER_BYTES ((int64_t)64 << 10)  /* zeroed prefix of a stream-K workspace */
+#define MGEMM_STREAMK_MAX_WORKGROUPS ((int64_t)16384)     /* one 32-bit counter each */
+
 mgemm_status gemm_streamk(mgemm_dtype in_dtype, mgemm_dtype c_dtype,
                           mgemm_op transA, mgemm_op transB,
                           int64_t M, int64_t N, int64_t K, double alpha,
@@ -412,7 +425,7 @@ mgemm_status gemm_streamk(mgemm_dtype in_dtype, mgemm_dtype c_dtype,
 typedef struct {
     int64_t workspace_bytes;   /* workspace the call needs (0: no product formed) */
     int64_t workgroups;        /* workgroups of the stream-K launch */
-    int64_t tiles;             /* output tiles (the fix-up launch covers the split ones) */
+    int64_t tiles;             /* output tiles */
     int64_t iterations;        /* K-iterations per tile */
     int64_t k_per_iteration;   /* K elements per iteration (the last may be shorter) */
     mgemm_variant_info variant;  /* tile build (id -1: none) */

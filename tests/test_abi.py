@@ -386,7 +386,7 @@ def test_streamk_rules_without_a_gpu():
     assert call(ws=None) == 1                                  # a launch needs the workspace
     assert call(ws=ALIGNED + 8) == 1                           # 16-byte alignment
     need = mg.streamk_plan("f32", 64, 64, 1024)["workspace_bytes"]
-    assert need == 32 * 2 * 64 * 64 * 4                        # 1 tile x 32 iterations: 32 workgroups
+    assert need == mg.STREAMK_COUNTER_BYTES + 32 * 2 * 64 * 64 * 4   # 1 tile x 32 iterations: 32 workgroups
     assert call(wbytes=need - 1) == 1
     assert call(alpha=1.0 + 2 ** -40) == 1                     # not a float
     assert call(in_dt=1, c_dt=1) == 1                          # fp32 C only for 16-bit inputs
@@ -439,15 +439,21 @@ def test_streamk_plans():
     p = mg.streamk_plan("f32", 1000, 1027, 999, lda=999, ldb=1027)
     assert p["variant"]["name"] == "mgemm_f32_64x64x32_w2x2_d4_u"
     assert (p["tiles"], p["iterations"], p["k_per_iteration"], p["workgroups"]) == (272, 32, 32, 512)
-    assert p["workspace_bytes"] == 512 * 2 * 64 * 64 * 4
-    # an explicit count, and the cap of one workgroup per (tile, iteration) pair
+    # the arrival counters first (a fixed prefix), then the partial tiles
+    assert mg.STREAMK_COUNTER_BYTES == 64 << 10 and mg.STREAMK_MAX_WORKGROUPS * 4 <= mg.STREAMK_COUNTER_BYTES
+    assert p["workspace_bytes"] == mg.STREAMK_COUNTER_BYTES + 512 * 2 * 64 * 64 * 4
+    # an explicit count, the cap of one workgroup per (tile, iteration) pair, and the cap
+    # of one arrival counter per workgroup
     assert mg.streamk_plan("f32", 1000, 1027, 999, 37, lda=999, ldb=1027)["workgroups"] == 37
+    assert mg.streamk_plan("f32", 4096, 4096, 4096, 10 ** 6)["workgroups"] == mg.STREAMK_MAX_WORKGROUPS
     one = mg.streamk_plan("f32", 64, 64, 300, 1000)
     assert (one["tiles"], one["iterations"], one["workgroups"]) == (1, 10, 10)
     # the K-iteration is the type's K granule; int8 takes N x T only
     assert mg.streamk_plan("bf16", 500, 500, 500)["k_per_iteration"] == 64
     i8 = mg.streamk_plan("i8", 1000, 1027, 999, transB=1)
-    assert i8["k_per_iteration"] == 128 and i8["workspace_bytes"] == 512 * 2 * i8["variant"]["block_m"] * i8["variant"]["block_n"] * 4
+    assert i8["k_per_iteration"] == 128
+    assert i8["workspace_bytes"] == (mg.STREAMK_COUNTER_BYTES +
+                                     512 * 2 * i8["variant"]["block_m"] * i8["variant"]["block_n"] * 4)
     # rows of any alignment have a stream-K build (the register path)
     assert mg.streamk_plan("bf16", 1000, 1027, 999, lda=999, ldb=1027)["variant"]["name"].endswith("_u")
     # no tile of 256x256 takes stream-K: a large aligned problem gets a smaller build
@@ -519,35 +525,60 @@ def test_noalloc_refuses_sizes_beyond_its_scratch_without_a_gpu():
     assert mg.NOALLOC_SCRATCH_BYTES == 64 << 20
 
 
+_DISASM = {}
+
+
+def device_instructions():
+    """{code object: [instruction, ...]} of the built library's gfx950 code (our own
+    build), disassembled once."""
+    if not _DISASM:
+        import shutil
+        import tempfile
+        objdump = "/opt/rocm/llvm/bin/llvm-objdump"
+        if not os.path.exists(objdump):
+            pytest.skip("llvm-objdump not installed")
+        with tempfile.TemporaryDirectory() as d:
+            lib = os.path.join(d, "libmgemm.so")
+            shutil.copy(_lib.LIB_PATH, lib)
+            subprocess.run([objdump, "--offloading", lib], capture_output=True, check=True, cwd=d)
+            objs = sorted(f for f in os.listdir(d) if "amdgcn" in f)
+            assert objs, "no device code objects in the library"
+            for o in objs:
+                text = subprocess.run([objdump, "-d", "--no-show-raw-insn", os.path.join(d, o)],
+                                      capture_output=True, text=True, check=True).stdout
+                ins = []
+                for line in text.splitlines():
+                    t = line.strip()
+                    if not t or t.endswith(":") or t.startswith(("/", ";", "Disassembly")):
+                        continue
+                    ins.append(t.split("//")[0].strip())
+                _DISASM[o] = ins
+    return _DISASM
+
+
 def test_every_lds_copy_in_the_library_opens_with_its_wait_states(built_library):
     # The copies global -> LDS are inline asm, where the compiler inserts no wait states:
     # each must open with s_nop 4, so that a v_readfirstlane that formed one of its scalar
     # operands (the row offset, M0, the buffer resource) is five wait states behind it.
-    # Without them an interior-tile prologue loaded 1 KB of B from a stale offset.  The
-    # check disassembles the built library's gfx950 code objects (our own build).
-    import shutil
-    import tempfile
-    objdump = "/opt/rocm/llvm/bin/llvm-objdump"
-    if not os.path.exists(objdump):
-        pytest.skip("llvm-objdump not installed")
-    with tempfile.TemporaryDirectory() as d:
-        lib = os.path.join(d, "libmgemm.so")
-        shutil.copy(_lib.LIB_PATH, lib)
-        subprocess.run([objdump, "--offloading", lib], capture_output=True, check=True, cwd=d)
-        objs = sorted(f for f in os.listdir(d) if "amdgcn" in f)
-        assert objs, "no device code objects in the library"
-        copies = 0
-        for o in objs:
-            text = subprocess.run([objdump, "-d", "--no-show-raw-insn", os.path.join(d, o)],
-                                  capture_output=True, text=True, check=True).stdout
-            prev = ""
-            for line in text.splitlines():
-                ins = line.strip()
-                if not ins or ins.endswith(":") or ins.startswith(("/", ";", "Disassembly")):
-                    continue
-                ins = ins.split("//")[0].strip()
-                if ins.startswith("buffer_load") and ins.endswith(" lds"):
-                    copies += 1
-                    assert prev == "s_nop 4", f"{o}: '{ins}' follows '{prev}'"
-                prev = ins
+    # Without them an interior-tile prologue loaded 1 KB of B from a stale offset.
+    copies = 0
+    for o, ins in device_instructions().items():
+        prev = ""
+        for i in ins:
+            if i.startswith("buffer_load") and i.endswith(" lds"):
+                copies += 1
+                assert prev == "s_nop 4", f"{o}: '{i}' follows '{prev}'"
+            prev = i
     assert copies > 1000
+
+
+def test_atomics_in_the_library_are_vector_memory_ones(built_library):
+    # stream-K's arrival counters are the library's only atomics: one wrapping increment
+    # per split-tile contribution, through the vector memory path
+    found = set()
+    for o, ins in device_instructions().items():
+        for i in ins:
+            op = i.split()[0]
+            if "atomic" in op:
+                found.add(op)
+    assert found == {"global_atomic_inc"}, found

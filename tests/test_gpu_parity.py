@@ -623,13 +623,29 @@ def test_streamk_quick_returns_and_shared_workspace():
     for alpha, K in ((0.0, 512), (1.0, 0)):
         p = wl.Problem("f32", 90, 70, K, alpha=alpha, beta=-0.5, dist="uniform", seed=142, streamk=0)
         full_check(p, exact=True, what=f"stream-K alpha={alpha} K={K} (nothing but beta*C)")
-    ws = torch.empty(mg.streamk_plan("f32", 300, 260, 1500, 100)["workspace_bytes"],
-                     dtype=torch.uint8, device="cuda")
-    for q in (wl.Problem("f32", 300, 260, 1500, dist="int", int_lo=-9, int_hi=9, seed=143, streamk=100),
-              wl.Problem("f32", 120, 77, 900, dist="int", int_lo=-9, int_hi=9, seed=144, streamk=60)):
+    # one zero-filled workspace for calls of different sizes, workgroup counts and tile
+    # counts, smaller after larger and larger after smaller: each call's last contributors
+    # put the arrival counters back to zero, and the partial tiles never reach them
+    shapes = ((300, 260, 1500, 100, 143), (120, 77, 900, 60, 144), (1000, 1027, 999, 0, 145),
+              (64, 64, 300, None, 146), (300, 260, 1500, 100, 147))
+    probs = []
+    for M, N, K, wgs, seed in shapes:
+        if wgs is None:   # one workgroup per (tile, iteration) pair
+            plan = mg.streamk_plan("f32", M, N, K, 0)
+            wgs = plan["tiles"] * plan["iterations"]
+        probs.append(wl.Problem("f32", M, N, K, dist="int", int_lo=-9, int_hi=9, seed=seed,
+                                streamk=wgs))
+    need = max(mg.streamk_plan("f32", q.M, q.N, q.K, q.streamk, lda=q.lda, ldb=q.ldb)["workspace_bytes"]
+               for q in probs)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for q in probs:
         r = Run(q)
+        ws[mg.STREAMK_COUNTER_BYTES:].fill_(0xA5)   # stale partial sums from anything before
         r.launch(workspace=ws)
-        check_exact(r.result(), r.oracle_full(), f"stream-K {q.M}x{q.N}x{q.K} in a shared workspace")
+        check_exact(r.result(), r.oracle_full(),
+                    f"stream-K {q.M}x{q.N}x{q.K} x{q.streamk} in a shared workspace")
+        left = int(torch.count_nonzero(ws[:mg.STREAMK_COUNTER_BYTES]))
+        assert left == 0, f"{left} counter bytes non-zero after stream-K {q.M}x{q.N}x{q.K}"
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
@@ -862,7 +878,7 @@ def test_launches_replay_in_a_hip_graph():
     eager_q = rq.result()
     z = wl.Problem("f32", 1000, 1027, 999, dist="int", int_lo=-8, int_hi=8, seed=122, streamk=0)
     rz = Run(z)
-    wz = torch.empty(mg.streamk_plan("f32", 1000, 1027, 999, 0, lda=z.lda, ldb=z.ldb)["workspace_bytes"],
+    wz = torch.zeros(mg.streamk_plan("f32", 1000, 1027, 999, 0, lda=z.lda, ldb=z.ldb)["workspace_bytes"],
                      dtype=torch.uint8, device="cuda")
     rz.launch(workspace=wz)
     eager_z = rz.result()
@@ -888,6 +904,7 @@ def test_launches_replay_in_a_hip_graph():
         check_exact(r.result(), eager, f"graph replay {rep} (256^3)")
         check_exact(rq.result(), eager_q, f"graph replay {rep} (split-K 256x256x8192)")
         check_exact(rz.result(), eager_z, f"graph replay {rep} (stream-K 1000x1027x999)")
+        assert int(torch.count_nonzero(wz[:mg.STREAMK_COUNTER_BYTES])) == 0, "stream-K counters left set"
 
 
 # ------------------------------------------------------------------ seeded random problems
