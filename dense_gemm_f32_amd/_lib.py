@@ -11,12 +11,15 @@ There is no fallback: if libmgemm.so is missing, the first call raises.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from typing import Optional
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libmgemm.so")
+POISON_LIB_PATH = os.path.join(PKG, "libmgemm_poison.so")   # LDS race-check build
+BUILD_LDS_POISON = 1   # MGEMM_BUILD_LDS_POISON
 
 OP_N, OP_T = 0, 1
 F32, F16, BF16, I8, I32, F64 = 0, 1, 2, 3, 4, 5
@@ -72,18 +75,46 @@ class StreamkPlanInfo(ctypes.Structure):
 
 
 _lib = None
+_override = None   # a library that using_library() routes every call to
 
 
 def load():
-    """Load libmgemm.so (raises if it has not been built)."""
+    """The library the calls go to: libmgemm.so (raises if it has not been built), or
+    the one a using_library() block selects."""
     global _lib
+    if _override is not None:
+        return _override
     if _lib is not None:
         return _lib
-    if not os.path.exists(LIB_PATH):
+    _lib = _open(LIB_PATH)
+    return _lib
+
+
+@contextlib.contextmanager
+def using_library(path):
+    """Route every call of this module to another build of the same sources inside the
+    block (e.g. POISON_LIB_PATH, the LDS race-check build); the product library is used
+    again afterwards."""
+    global _override
+    prev = _override
+    _override = _open(path)
+    try:
+        yield _override
+    finally:
+        _override = prev
+
+
+def build_flags():
+    """MGEMM_BUILD_* bits of the library in use (0: the product build)."""
+    return load().mgemm_build_flags()
+
+
+def _open(path):
+    if not os.path.exists(path):
         raise RuntimeError(
-            f"{LIB_PATH} is missing: build the HIP library first "
+            f"{path} is missing: build the HIP library first "
             "(python -c 'import __graft_entry__ as g; g.build()'). There is no fallback path.")
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(path)
     i64, i32, f32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_void_p
     single = [i32, i32, i64, i64, i64, f32, vp, i64, vp, i64, f32, vp, i64, vp]
     for name in ("gemm_f32", "gemm_f16", "gemm_bf16"):
@@ -133,7 +164,8 @@ def load():
                                     ctypes.POINTER(VariantInfo), ctypes.POINTER(i64)]
     lib.mgemm_force_variant.restype = i32
     lib.mgemm_force_variant.argtypes = [i32, i32]
-    _lib = lib
+    lib.mgemm_build_flags.restype = i32
+    lib.mgemm_build_flags.argtypes = []
     return lib
 
 

@@ -2,7 +2,9 @@
 
 Every translation unit under csrc/ is compiled with hipcc for gfx950 into
 _build/, in parallel, then linked into dense_gemm_f32_amd/libmgemm.so.  The
-benchmark's measurement aids under diag/ go into libmgemm_diag.so.
+benchmark's measurement aids under diag/ go into libmgemm_diag.so.  The same
+csrc/ sources built with -DMGEMM_DEBUG_POISON (objects in _build/poison/) make
+libmgemm_poison.so, the LDS race-check build that a GPU test runs.
 """
 from __future__ import annotations
 
@@ -19,6 +21,8 @@ DIAG = os.path.join(PKG, "diag")
 DIAG_LIB = os.path.join(PKG, "libmgemm_diag.so")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmgemm.so")
+POISON_LIB = os.path.join(PKG, "libmgemm_poison.so")
+POISON_FLAGS = ["-DMGEMM_DEBUG_POISON"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -31,8 +35,8 @@ FLAGS = [
 ]
 
 
-def _compile(src: str, extra) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+def _compile(src: str, extra, objdir: str = BUILD) -> str:
+    obj = os.path.join(objdir, os.path.basename(src) + ".o")
     cmd = [HIPCC, *FLAGS, *extra, "-x", "hip", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -53,18 +57,30 @@ def _link(objs, out):
     os.replace(tmp, out)
 
 
-def build(extra_flags=(), jobs: int | None = None) -> str:
-    """Compile and link libmgemm.so (and libmgemm_diag.so); returns the former's
-    path.  Always rebuilds."""
-    os.makedirs(BUILD, exist_ok=True)
+def build(extra_flags=(), jobs: int | None = None, poison: bool = True) -> str:
+    """Compile and link libmgemm.so, libmgemm_diag.so and (poison=True) the race-check
+    build libmgemm_poison.so; returns the first one's path.  Always rebuilds."""
+    poison_dir = os.path.join(BUILD, "poison")
+    os.makedirs(poison_dir, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
     diag = sorted(glob.glob(os.path.join(DIAG, "*.hip")))
-    jobs = jobs or min(len(srcs) + len(diag), os.cpu_count() or 4, 16)
+    units = [(s, list(extra_flags), BUILD) for s in srcs + diag]
+    if poison:
+        units += [(s, list(extra_flags) + POISON_FLAGS, poison_dir) for s in srcs]
+    # the largest translation units first, so that they do not finish last
+    order = sorted(range(len(units)), key=lambda i: -os.path.getsize(units[i][0]))
+    jobs = jobs or min(len(units), os.cpu_count() or 4, 16)
+    objs = [None] * len(units)
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, list(extra_flags)), srcs + diag))
-    _link(objs[:len(srcs)], LIB)
+        futs = {ex.submit(_compile, *units[i]): i for i in order}
+        for f in concurrent.futures.as_completed(futs):
+            objs[futs[f]] = f.result()
+    n, d = len(srcs), len(diag)
+    _link(objs[:n], LIB)
     if diag:
-        _link(objs[len(srcs):], DIAG_LIB)
+        _link(objs[n:n + d], DIAG_LIB)
+    if poison:
+        _link(objs[n + d:], POISON_LIB)
     return LIB
 
 

@@ -167,6 +167,7 @@ gemm_f64_kernel(KernelArgs p)
 
     // two LDS stages; the next slab is fetched to registers during the current one
     const int nk = (K + BK - 1) / BK;
+    lds_poison<2 * STAGE * 8>(smem);
     load_slab(0);
     la.store(smem, tid);
     lb.store(smem + A_ELEMS, tid);
@@ -182,6 +183,7 @@ gemm_f64_kernel(KernelArgs p)
         la.store(st, tid);
         lb.store(st + A_ELEMS, tid);
         __syncthreads();
+        lds_poison<STAGE * 8>(smem + (kt & 1) * STAGE);  // read by every wave
     }
     compute((nk - 1) & 1);
 

@@ -204,6 +204,31 @@ __device__ __forceinline__ void lds_barrier()
     asm volatile("" ::: "memory");
 }
 
+// Race check of the LDS rings (debug builds, -DMGEMM_DEBUG_POISON; a no-op
+// otherwise): every thread of the workgroup fills its share of LDS bytes
+// [p, p + BYTES) with 0xFF (NaN in every floating type, -1 in int8), waits
+// for its LDS writes and meets the others at a barrier.  Vector-memory
+// counters are not waited on, so copies in flight stay in flight.  Each ring
+// poisons all of its stages before its first copy and each stage again once
+// every wave has read it, before its refill is issued: a fragment read that
+// runs ahead of its slab's copies, or a stage refilled while a wave still
+// reads it, then takes poison instead of a plausible value.
+template <int BYTES>
+__device__ __forceinline__ void lds_poison(void *p)
+{
+#ifdef MGEMM_DEBUG_POISON
+    static_assert(BYTES % 4 == 0, "whole words");
+    uint32_t *w = static_cast<uint32_t *>(p);
+    for (int i = threadIdx.x; i < BYTES / 4; i += blockDim.x) w[i] = 0xffffffffu;
+    __builtin_amdgcn_s_waitcnt((63 & 15) | ((63 >> 4) << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+#else
+    (void)p;
+#endif
+}
+
 // Physical order of the rows of a K-contiguous LDS tile.  A wavefront's
 // 32*IL rows hold its IL interleaved MFMA sub-tiles (logical row IL*i' + t);
 // physical row 32*t + i' holds logical row IL*i' + t, so the lanes of one
@@ -646,6 +671,7 @@ struct RegPath {
             }
         };
         const int nk = (p.K + BK - 1) / BK;
+        lds_poison<2 * STAGE>(smem);
         if constexpr (!REG2) {
             // two LDS stages, the next slab fetched to registers during the current one
             OpA la;
@@ -661,6 +687,7 @@ struct RegPath {
                 la.store(st, tid);
                 lb.store(st + A_BYTES, tid);
                 __syncthreads();
+                lds_poison<STAGE>(smem + (kt & 1) * STAGE);  // read by every wave
             }
             compute((nk - 1) & 1);
         } else {
@@ -686,6 +713,7 @@ struct RegPath {
                     next_a.store(st, tid);
                     next_b.store(st + A_BYTES, tid);
                     __syncthreads();
+                    lds_poison<STAGE>(smem + (kt & 1) * STAGE);  // read by every wave
                 }
             };
             int kt = 0;
@@ -1064,6 +1092,7 @@ struct DmaPath {
         };
 
         const int nk = (p.K + BK - 1) / BK;  // a K tail is one more slab, zero-filled past K
+        lds_poison<LDS_BYTES>(smem);
         // prologue: slabs 0..NS-1 in flight, wait for slab 0
         issue(0);
 #pragma unroll
@@ -1104,6 +1133,7 @@ struct DmaPath {
             if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
             wait_ahead<NS - 2>();
             lds_barrier();
+            lds_poison<STAGE>(stage(kt));  // read by every wave; refilled below
             if constexpr (SPREAD) {
                 frags(kt + 1, 0, f[G & 1]);
                 __builtin_amdgcn_sched_barrier(0);

@@ -802,6 +802,15 @@ const char *mgemm_status_string(mgemm_status s)
 
 int mgemm_num_variants(void) { return total_variants(); }
 
+int mgemm_build_flags(void)
+{
+#ifdef MGEMM_DEBUG_POISON
+    return MGEMM_BUILD_LDS_POISON;
+#else
+    return 0;
+#endif
+}
+
 mgemm_status mgemm_variant(int id, mgemm_variant_info *out)
 {
     const Variant *v = variant_by_id(id);

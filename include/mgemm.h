@@ -298,12 +298,22 @@ typedef struct {
     int pipe;          /* DMA-path schedule: 1 = four LDS stages of
                           block_k/2, 2 = two stages of block_k, 3 = one
                           stage of block_k (K <= block_k only), 4 = 4-byte
-                          copies in two stages of block_k (every tile) */
+                          copies in two stages of block_k (every tile);
+                          6 = small-problem kernel: one 16x16 tile per
+                          workgroup, its waves_n waves sharing K, operands
+                          through registers, K <= block_k */
     char name[64];     /* kernel family name, e.g. "mgemm_f32_256x256x32_w2x2" */
 } mgemm_variant_info;
 
 /* Number of compiled variants (all dtypes). */
 int mgemm_num_variants(void);
+
+/* How this copy of the library was built: 0 for the product build, or a set
+ * of MGEMM_BUILD_* bits for a debug build of the same sources. */
+#define MGEMM_BUILD_LDS_POISON 1  /* every LDS stage is filled with 0xFF before
+                                     its first copy and after its last read
+                                     (race check; slower) */
+int mgemm_build_flags(void);
 
 /* Fill *out for variant `id`; MGEMM_INVALID_ARG if id is out of range. */
 mgemm_status mgemm_variant(int id, mgemm_variant_info *out);

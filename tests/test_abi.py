@@ -49,6 +49,20 @@ def test_library_exports_every_declared_symbol():
         assert getattr(lib, n) is not None
 
 
+def test_race_check_build_exports_the_header_and_says_what_it_is():
+    # libmgemm_poison.so: the same sources with -DMGEMM_DEBUG_POISON (a GPU test runs it)
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.POISON_LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
+    assert not [n for n in declared_functions() if n not in exported]
+    assert "mgemm_build_flags" in declared_functions()
+    assert _lib.build_flags() == 0
+    with _lib.using_library(_lib.POISON_LIB_PATH) as lib:
+        assert mg.load() is lib and _lib.build_flags() == _lib.BUILD_LDS_POISON
+        assert lib.mgemm_num_variants() == mg.load().mgemm_num_variants()
+    assert _lib.build_flags() == 0 and mg.load() is not lib
+
+
 def test_diag_library_exports_its_header():
     # the benchmark's measurement aid: built beside libmgemm.so, loaded by bench.py only
     diag_header = os.path.join(ROOT, "include", "mgemm_diag.h")
