@@ -13,18 +13,23 @@
 // (out-of-range elements read as zero), so edges and unaligned leading
 // dimensions need no second path.
 //
-// LDS holds both operands k-major, [BK][MN + 2] doubles.  At MFMA step s of a
+// LDS holds both operands k-major, [BK][P] doubles.  At MFMA step s of a
 // 16-deep group, lane (g = lane/16, i = lane%16) reads row
 // 8(g&1) + 4(g>>1) + s, column i of its 16-wide block: the four steps cover
 // the 16 rows once, and A and B use the same k-slot, which is all the dot
-// product needs.  Bank arithmetic (64 banks of 4 bytes, a 32-lane half-wave
-// per LDS cycle): with the row stride P = MN + 2 doubles,
-//   - fragment reads: the half-wave's two 16-lane groups read rows 8 apart,
-//     16P = 32 mod 64 dwords apart, so their 32 consecutive dwords interleave;
-//   - transposing stores (memory rows along m/n): 8 lanes of one memory row
-//     write rows 2j of one column, 4P = 8 mod 64 dwords apart, and 4 memory
-//     rows fill the gaps;
-// so both are conflict-free (a pad of 4 left the stores 2-way conflicted).
+// product needs.  Bank arithmetic, as the counters show it for 64-bit
+// accesses: 32 banks of 4 bytes, 16 lanes served together.
+//   - fragment reads: 16 lanes read 16 consecutive doubles of one row, 32
+//     distinct banks whatever the row pitch P;
+//   - transposing stores (memory rows along m/n): with P = MN + 2, LDS rows
+//     c and c' of one column are 2(c - c')P = 4(c - c') mod 32 dwords apart.
+//     A 16-lane group that covered 8 k-pairs of 2 memory rows (16-byte loads)
+//     put k-pairs j and j + 4 on the same banks: 2-way conflicts, 1/9 of the
+//     LDS cycles of 4096^3 NN.  Each 16-lane group now covers 4 k-pairs of 4
+//     memory rows (8 k of 2 rows for 8-byte loads): 8j + 2r' (+1), all 32
+//     banks; the two k-halves of a 32-lane half-wave land 32 dwords apart;
+//   - k-row operands are stored 16 bytes per lane, 16 consecutive doubles of
+//     one row per 8 lanes.
 #pragma once
 
 #include "gemm_kernel.hpp"
@@ -47,8 +52,28 @@ struct F64Operand {
     static constexpr int P = MN + 2;            // padded LDS row (doubles)
     f64x2 regs[NPT];
 
-    __device__ __forceinline__ static int row_of(int tid, int q) { return (tid + q * NT) / VPR; }
-    __device__ __forceinline__ static int col_of(int tid, int q) { return ((tid + q * NT) % VPR) * VEC; }
+    // Element (row, column) of vector q of thread tid.  A k-row operand walks
+    // the tile row by row.  A transposing one (memory rows m/n) gives each
+    // wave RW = 64/VPR whole memory rows (the same bytes either way) and its
+    // 16-lane groups a block of H = VPR/2 vectors by 16/H rows: group (h, g)
+    // takes vector columns h*H .. h*H+H-1 of rows g*16/H ...  See above for
+    // the banks.
+    static constexpr int RW = 64 / VPR, H = VPR / 2;
+    static_assert(KROW || (VPR == 8 || VPR == 16), "transposing tile: 8 or 16 vectors per row");
+    __device__ __forceinline__ static int row_of(int tid, int q)
+    {
+        const int idx = tid + q * NT;
+        if constexpr (KROW) return idx / VPR;
+        const int l = idx & 63, m = l & 15, qw = l >> 4;
+        return (idx >> 6) * RW + (qw >> 1) * (16 / H) + m / H;
+    }
+    __device__ __forceinline__ static int col_of(int tid, int q)
+    {
+        const int idx = tid + q * NT;
+        if constexpr (KROW) return (idx % VPR) * VEC;
+        const int l = idx & 63, m = l & 15, qw = l >> 4;
+        return ((qw & 1) * H + m % H) * VEC;
+    }
 
     // rows < rlim and columns < clim of the memory tile at `base` are in range.
     __device__ __forceinline__ void load(const double *base, int64_t ld, int rlim, int clim, int tid)
