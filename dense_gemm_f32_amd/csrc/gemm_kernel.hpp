@@ -65,6 +65,8 @@ typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 
 // Everything a GEMM launch needs; built on the host after validation.
 struct KernelArgs {
@@ -384,6 +386,42 @@ __device__ __forceinline__ int kc128_off(int p, int kbyte)
     return p * 128 + (chunk << 4) + (kbyte & 15);
 }
 
+// int8 operands whose memory rows are k (MN-contiguous, "MC"): LDS rows of
+// ROWB bytes (the tile's MN), 16-byte chunks permuted per row, chunk c of row
+// k at c ^ (k % 8) (k % 4 for 64-byte rows).  A transposing fragment read
+// (tr8_frag) takes one 16-byte chunk from each of 8 consecutive rows per 16
+// lanes; the permutation puts those in 8 distinct chunks, i.e. all 32 banks
+// of a 128-byte access.  The permutation is its own inverse: physical chunk
+// c of row k holds logical chunk c ^ (k % 8).
+template <int ROWB>
+__device__ __forceinline__ int mc8_chunk(int k, int c)
+{
+    static_assert(ROWB % 64 == 0, "whole 64-byte pieces");
+    return c ^ (k & (ROWB >= 128 ? 7 : 3));
+}
+template <int ROWB>
+__device__ __forceinline__ int mc8_off(int k, int byte)
+{
+    return k * ROWB + (mc8_chunk<ROWB>(k, byte >> 4) << 4) + (byte & 15);
+}
+
+// Fragment of one MC int8 operand: the 16 k-values 32g + 16h + 0..15 of column
+// (wave-local) col_base + lane % 32, for v_mfma_i32_32x32x32_i8, via two
+// ds_read_b64_tr_b8.  Within a 16-lane group, source lane j supplies 8 bytes
+// of row k0 + j/2, columns 8*(j%2) .. +7 of the group's 16, and lane i
+// receives column i of rows k0 .. k0+7 in its bytes 0..7 (pinned by an
+// in-bounds one-wave probe); the second read covers rows k0+8 .. k0+15.
+template <int ROWB>
+__device__ __forceinline__ u32x4 tr8_frag(const char *s, int g, int lh, int col_base, int lane)
+{
+    const int gi = lane & 15;
+    const int col = col_base + 16 * ((lane >> 4) & 1) + 8 * (gi & 1);
+    const int k0 = 32 * g + 16 * lh + (gi >> 1);
+    const i32x2 lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2 *)(s + mc8_off<ROWB>(k0, col)));
+    const i32x2 hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2 *)(s + mc8_off<ROWB>(k0 + 8, col)));
+    return u32x4{(uint32_t)lo[0], (uint32_t)lo[1], (uint32_t)hi[0], (uint32_t)hi[1]};
+}
+
 // One operand (A or B) of one K-slab: global -> registers -> LDS.
 //   ES    element size (4: fp32, 2: f16/bf16, 1: int8)
 //   MN    tile extent along M (for A) or N (for B)
@@ -392,16 +430,19 @@ __device__ __forceinline__ int kc128_off(int p, int kbyte)
 //   VECOK 16-byte aligned rows; otherwise every 16-byte vector is assembled
 //         from the aligned dwords around it (realigned_vec)
 // Modes:
-//   vector   (!KROW, or fp32): memory vectors copied as is; LDS rows are
-//            K-contiguous (!KROW) or the fp32 [BK][MN] layout (KROW).
-//   block    (8/16-bit KROW): KB x 8 blocks transposed in registers so LDS
+//   vector   (!KROW, fp32 or int8): memory vectors copied as is; LDS rows
+//            are K-contiguous (!KROW), the fp32 [BK][MN] layout (fp32 KROW)
+//            or the int8 MC layout of mc8_off (int8 KROW, read back with
+//            transposing reads).
+//   block    (16-bit KROW): KB x 8 blocks transposed in registers so LDS
 //            rows stay K-contiguous (the MFMA wants 8 k per lane).
 template <int ES, int NT, int MN, int BK, int IL, bool KROW, bool VECOK>
 struct RegOperand {
     static constexpr bool F32 = ES == 4;
     static constexpr int ROWB = BK * ES;
     static_assert(ROWB == 128, "K-contiguous rows are 128 bytes");
-    static constexpr bool BLOCK = KROW && !F32;
+    static constexpr bool BLOCK = KROW && ES == 2;
+    static constexpr bool MC8 = KROW && ES == 1;  // int8 rows of k: MC layout
     static constexpr int VEC = 16 / ES;
     static constexpr int R = KROW ? BK : MN;   // memory rows of the tile
     static constexpr int CC = KROW ? MN : BK;  // contiguous elements per memory row
@@ -551,6 +592,8 @@ struct RegOperand {
                 const int r = vrow(tid, q), c = vcol(tid, q);
                 if constexpr (!KROW) {          // memory row = mn, contiguous = k; r is physical
                     *reinterpret_cast<Raw *>(s + kc128_off(r, c * ES)) = regs[q];
+                } else if constexpr (MC8) {     // int8, memory row = k: one 16-byte chunk
+                    *reinterpret_cast<Raw *>(s + mc8_off<MN>(r, c)) = regs[q];
                 } else {                        // fp32, memory row = k, contiguous = mn -> [BK][MN]
                     *reinterpret_cast<Raw *>(s + (r * MN + c) * 4) = regs[q];
                 }
@@ -568,13 +611,18 @@ struct RegPath {
     static constexpr int TM = WTM / 32, TN = WTN / 32;
     static_assert(TM >= 1 && TN >= 1 && TM * 32 * WM == BM && TN * 32 * WN == BN, "tile");
     static_assert(TN == 1 || TN == 2 || TN == 4, "TN");
-    static constexpr bool A_KC = !TA || !F32;  // LDS layout of A is K-contiguous
-    static constexpr bool B_KC = TB || !F32;
+    // LDS layout of A (B) is K-contiguous; otherwise fp32 [BK][MN] or the int8
+    // MC layout (16-bit operands are always stored K-contiguous)
+    static constexpr bool A_KC = !TA || ES == 2;
+    static constexpr bool B_KC = TB || ES == 2;
+    static constexpr bool A_MC8 = !A_KC && ES == 1, B_MC8 = !B_KC && ES == 1;
     static constexpr int A_BYTES = BM * BK * ES, B_BYTES = BN * BK * ES;
     static constexpr int STAGE = A_BYTES + B_BYTES;
     static constexpr int LDS_BYTES = 2 * STAGE;
     static constexpr int G = F32 ? BK / 8 : BK * ES / 32;  // k-groups of 32 bytes per slab
-    static constexpr int IL_A = TM, IL_B = TN;  // C mapping: interleaved rows and columns
+    // C mapping: interleaved rows and columns, except that a transposing read
+    // (int8 MC) gives each lane consecutive ones
+    static constexpr int IL_A = A_MC8 ? 1 : TM, IL_B = B_MC8 ? 1 : TN;
     // 64x64 tiles keep two register sets in flight: a grid of them is often
     // about one workgroup per CU, with little else to hide the load latency
     // behind.  Larger tiles keep one: a second set would cost them occupancy
@@ -624,12 +672,22 @@ struct RegPath {
                 }
             }
         } else {
+            // int8 MC operands: transposing reads of the wave's consecutive columns
+            const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-            for (int t = 0; t < TM; ++t)
-                f.a16[t] = *reinterpret_cast<const u32x4 *>(sa + kc128_off(a_prow0 + 32 * t, (16 * g + 8 * lh) * 2));
+            for (int t = 0; t < TM; ++t) {
+                if constexpr (A_MC8)
+                    f.a16[t] = tr8_frag<BM>(sa, g, lh, (wave / WN) * WTM + 32 * t, lane);
+                else
+                    f.a16[t] = *reinterpret_cast<const u32x4 *>(sa + kc128_off(a_prow0 + 32 * t, (16 * g + 8 * lh) * 2));
+            }
 #pragma unroll
-            for (int u = 0; u < TN; ++u)
-                f.b16[u] = *reinterpret_cast<const u32x4 *>(sb + kc128_off(b_prow0 + 32 * u, (16 * g + 8 * lh) * 2));
+            for (int u = 0; u < TN; ++u) {
+                if constexpr (B_MC8)
+                    f.b16[u] = tr8_frag<BN>(sb, g, lh, (wave % WN) * WTN + 32 * u, lane);
+                else
+                    f.b16[u] = *reinterpret_cast<const u32x4 *>(sb + kc128_off(b_prow0 + 32 * u, (16 * g + 8 * lh) * 2));
+            }
         }
     }
 
@@ -829,7 +887,17 @@ struct DmaPath {
     template <int ROWB>
     __device__ __forceinline__ static int mc_off(int k, int byte)
     {
+        if constexpr (ES == 1) return mc8_off<ROWB>(k, byte);
         return k * ROWB + (((byte >> 6) ^ mc_key<ROWB>(k)) << 6) + (byte & 63);
+    }
+
+    // byte column of the memory tile that physical byte bb of MC row k holds
+    // (both permutations are their own inverses)
+    template <int ROWB>
+    __device__ __forceinline__ static int mc_logical(int k, int bb)
+    {
+        if constexpr (ES == 1) return (mc8_chunk<ROWB>(k, bb >> 4) << 4) | (bb & 15);
+        return (((bb >> 6) ^ mc_key<ROWB>(k)) << 6) | (bb & 63);
     }
 
     // DMA instruction q (of IPW) of wave `w` for one operand's slab: 1 KB into
@@ -864,10 +932,10 @@ struct DmaPath {
             dma16(rs, lds_addr_of(dst + pb * RB), voff, soff);
         } else {
             // bytes b = ins*1024 + 16*lane of the [BK][MN] region: row k = b / ROWB,
-            // physical piece (b % ROWB) / 64 holds logical piece ^ key(k)
+            // physical byte b % ROWB holds logical byte mc_logical(k, b % ROWB)
             const int b = ins * 1024 + 16 * lane;
             const int k = b / ROWB, bb = b % ROWB;
-            const int lb = (((bb >> 6) ^ mc_key<ROWB>(k)) << 6) | (bb & 63);
+            const int lb = mc_logical<ROWB>(k, bb);
             const int voff = (CHECK && (k >= rows_ok || lb >= cols_ok * ES)) ? kOutOfRange : k * ld_bytes + lb;
             dma16(rs, lds_addr_of(dst + ins * 1024), voff, 0);
         }
@@ -896,7 +964,7 @@ struct DmaPath {
         } else {
             const int k = b / ROWB, bb = b % ROWB;
             r = k;
-            cb = (((bb >> 6) ^ mc_key<ROWB>(k)) << 6) | (bb & 63);
+            cb = mc_logical<ROWB>(k, bb);
         }
         const int voff = (r < rows_ok && cb < cols_ok * ES) ? r * ld_bytes + cb : kOutOfRange;
         dma4(rs, lds_addr_of(dst + ins * 256), voff);
@@ -964,6 +1032,8 @@ struct DmaPath {
             for (int t = 0; t < TM; ++t) {
                 if constexpr (A_KC)
                     f.a16[t] = *reinterpret_cast<const u32x4 *>(sa + kc_off(L.a_prow0 + 32 * t, (16 * g + 8 * L.lh) * 2));
+                else if constexpr (ES == 1)
+                    f.a16[t] = tr8_frag<A_ROWB>(sa, g, L.lh, L.a_blk + 32 * t, L.lane);
                 else
                     f.a16[t] = tr_frag<A_ROWB>(sa, g, L.lh, L.a_blk + 32 * t, L.lane);
             }
@@ -971,6 +1041,8 @@ struct DmaPath {
             for (int u = 0; u < TN; ++u) {
                 if constexpr (B_KC)
                     f.b16[u] = *reinterpret_cast<const u32x4 *>(sb + kc_off(L.b_prow0 + 32 * u, (16 * g + 8 * L.lh) * 2));
+                else if constexpr (ES == 1)
+                    f.b16[u] = tr8_frag<B_ROWB>(sb, g, L.lh, L.b_blk + 32 * u, L.lane);
                 else
                     f.b16[u] = tr_frag<B_ROWB>(sb, g, L.lh, L.b_blk + 32 * u, L.lane);
             }

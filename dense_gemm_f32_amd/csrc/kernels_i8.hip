@@ -1,5 +1,7 @@
 // int8-input kernel variants: v_mfma_i32_32x32x32_i8, int32 accumulate and int32 C,
-// 128-element K-slabs; A K-contiguous and B K-contiguous (the only layout built).
+// 128-element K-slabs.  The 256x256 and 128x128 tiles take every transpose
+// (MN-contiguous operands through transposing LDS reads); the 64x64 ones take A
+// K-contiguous and B K-contiguous only.
 #include "variants.hpp"
 
 namespace mgemm {
@@ -16,19 +18,19 @@ const Variant *i8_variants(int *count)
     // estimate run when forced, or by preference order when no estimated
     // build fits (unaligned rows: 4-byte copies first).
     static const Variant table[] = {
-        MGEMM_VARIANT_I8(256, 256, 128, 2, 4, true, 2, "mgemm_i8_256x256x128_w2x4_d2", {8.0f, 0.0121f, 1.5f, 1.15f}),
-        MGEMM_VARIANT_I8(256, 256, 128, 2, 4, true, 1, "mgemm_i8_256x256x128_w2x4", {}),
-        MGEMM_VARIANT_I8(256, 256, 128, 4, 2, true, 1, "mgemm_i8_256x256x128_w4x2", {}),
+        MGEMM_VARIANT_I8_ALL(256, 256, 128, 2, 4, true, 2, "mgemm_i8_256x256x128_w2x4_d2", {8.0f, 0.0121f, 1.5f, 1.15f}),
+        MGEMM_VARIANT_I8_ALL(256, 256, 128, 2, 4, true, 1, "mgemm_i8_256x256x128_w2x4", {}),
+        MGEMM_VARIANT_I8_ALL(256, 256, 128, 4, 2, true, 1, "mgemm_i8_256x256x128_w4x2", {}),
         // 128x128 with eight waves (four waves measured 3-20% slower)
-        MGEMM_VARIANT_I8(128, 128, 128, 2, 4, true, 1, "mgemm_i8_128x128x128_w2x4", {3.39f, 0.00441f, 1.5f, 1.15f},
-                         MGEMM_SK_I8(128, 128, 128, 2, 4, true, 1)),
-        MGEMM_VARIANT_I8(128, 128, 128, 2, 4, true, 2, "mgemm_i8_128x128x128_w2x4_d2", {3.59f, 0.00336f, 1.5f, 1.35f},
-                         MGEMM_SK_I8(128, 128, 128, 2, 4, true, 2)),
+        MGEMM_VARIANT_I8_ALL(128, 128, 128, 2, 4, true, 1, "mgemm_i8_128x128x128_w2x4", {3.39f, 0.00441f, 1.5f, 1.15f},
+                         MGEMM_SK_I8_ALL(128, 128, 128, 2, 4, true, 1)),
+        MGEMM_VARIANT_I8_ALL(128, 128, 128, 2, 4, true, 2, "mgemm_i8_128x128x128_w2x4_d2", {3.59f, 0.00336f, 1.5f, 1.35f},
+                         MGEMM_SK_I8_ALL(128, 128, 128, 2, 4, true, 2)),
         // rows 4-byte aligned (and K a multiple of 4): 4-byte copies into LDS, every tile
-        MGEMM_VARIANT_I8(128, 128, 128, 2, 2, false, 4, "mgemm_i8_128x128x128_w2x2_d4_u", {},
-                         MGEMM_SK_I8(128, 128, 128, 2, 2, false, 4)),
-        MGEMM_VARIANT_I8(128, 128, 128, 2, 2, false, 1, "mgemm_i8_128x128x128_w2x2_u", {},
-                         MGEMM_SK_I8(128, 128, 128, 2, 2, false, 1)),
+        MGEMM_VARIANT_I8_ALL(128, 128, 128, 2, 2, false, 4, "mgemm_i8_128x128x128_w2x2_d4_u", {},
+                         MGEMM_SK_I8_ALL(128, 128, 128, 2, 2, false, 4)),
+        MGEMM_VARIANT_I8_ALL(128, 128, 128, 2, 2, false, 1, "mgemm_i8_128x128x128_w2x2_u", {},
+                         MGEMM_SK_I8_ALL(128, 128, 128, 2, 2, false, 1)),
         MGEMM_VARIANT_I8(64, 64, 128, 2, 2, true, 1, "mgemm_i8_64x64x128_w2x2", {0.64f, 0.00195f, 1.5f, 2.6f},
                          MGEMM_SK_I8(64, 64, 128, 2, 2, true, 1)),
         MGEMM_VARIANT_I8(64, 64, 128, 2, 2, true, 2, "mgemm_i8_64x64x128_w2x2_d2", {0.82f, 0.00139f, 1.5f, 3.16f},

@@ -98,8 +98,8 @@ mgemm_status validate_and_plan(int dtype, int c_dtype, int transA, int transB, i
     if (dtype == MGEMM_F64) {
         if (c_dtype != MGEMM_F64) return MGEMM_INVALID_ARG;  // double C only
     } else if (dtype == MGEMM_I8) {
-        // int32 C; A and B K-contiguous; integral alpha and beta
-        if (c_dtype != MGEMM_I32 || transA != MGEMM_OP_N || transB != MGEMM_OP_T) return MGEMM_INVALID_ARG;
+        // int32 C; integral alpha and beta
+        if (c_dtype != MGEMM_I32) return MGEMM_INVALID_ARG;
         if (!int32_scalar(alpha) || !int32_scalar(beta)) return MGEMM_INVALID_ARG;
     } else if (c_dtype != MGEMM_F32 && c_dtype != dtype) {
         return MGEMM_INVALID_ARG;  // fp32 C, or the inputs' own 16-bit type
@@ -182,8 +182,12 @@ mgemm_status validate_and_plan(int dtype, int c_dtype, int transA, int transB, i
     // 32-bit offsets.  Under split-K, K is the chunk length (a multiple of the
     // slab) and the last chunk takes the rest of k_all, so the chunk multiple
     // is checked on k_all: the last chunk's remainder is k_all's.
+    // (and a build of this transpose and C type: the 64x64 int8 tiles take
+    // A K-contiguous and B K-contiguous only)
+    const bool wide_c = c_dtype == MGEMM_F32 || c_dtype == MGEMM_I32 || c_dtype == MGEMM_F64;
     auto offsets_ok = [&](const Variant &v) {
-        return (!dw_copies(v) || (a.fast_ok && dw_rows)) &&
+        return (wide_c ? v.fn : v.fn16)[transA][transB] != nullptr &&
+               (!dw_copies(v) || (a.fast_ok && dw_rows)) &&
                (v.pipe != 3 || (a.fast_ok && K <= v.bk && k_all % (16 / es) == 0)) &&
                // the small-problem kernel: its waves share at most bk of K, and it
                // has no shorter last chunk (split-K) of its own

@@ -111,6 +111,11 @@ hipError_t launch_gemm_f64(const KernelArgs &a, unsigned grid, hipStream_t s)
 #define MGEMM_SK_I8(BM, BN, BK, WM, WN, V, D)                                                 \
     {{nullptr, launch_gemm_sk<int8_t, BM, BN, BK, WM, WN, false, true, V, D, int32_t>},       \
      {nullptr, nullptr}}
+#define MGEMM_SK_I8_ALL(BM, BN, BK, WM, WN, V, D)                                             \
+    {{launch_gemm_sk<int8_t, BM, BN, BK, WM, WN, false, false, V, D, int32_t>,                \
+      launch_gemm_sk<int8_t, BM, BN, BK, WM, WN, false, true, V, D, int32_t>},                \
+     {launch_gemm_sk<int8_t, BM, BN, BK, WM, WN, true, false, V, D, int32_t>,                 \
+      launch_gemm_sk<int8_t, BM, BN, BK, WM, WN, true, true, V, D, int32_t>}}
 // small fp32 problems: 16x16 tiles, W waves sharing K <= W * NCH * 32 (pipe 6)
 #define MGEMM_VARIANT_F32_SMALL(W, NCH, NAME, ...)                                          \
     {0, 16, 16, (W) * (NCH) * 32, 1, W, false, 6, NAME,                                      \
@@ -125,7 +130,12 @@ hipError_t launch_gemm_f64(const KernelArgs &a, unsigned grid, hipStream_t s)
 #define MGEMM_VARIANT_F32(BM, BN, BK, WM, WN, V, NAME, ...) \
     MGEMM_VARIANT_F32_D(BM, BN, BK, WM, WN, V, 1, NAME, __VA_ARGS__)
 
-// int8 inputs: int32 C, A K-contiguous (op N) and B K-contiguous (op T) only
+// int8 inputs: int32 C; every transpose (_ALL), or A K-contiguous (op N) and
+// B K-contiguous (op T) only (tiles whose MN-contiguous LDS rows, 64 bytes,
+// are too short for the transposing layout)
+#define MGEMM_VARIANT_I8_ALL(BM, BN, BK, WM, WN, V, D, NAME, ...)                            \
+    {3, BM, BN, BK, WM, WN, V, D, NAME, MGEMM_LAUNCHERS(int8_t, BM, BN, BK, WM, WN, V, D, int32_t), \
+     {{nullptr, nullptr}, {nullptr, nullptr}}, __VA_ARGS__}
 #define MGEMM_VARIANT_I8(BM, BN, BK, WM, WN, V, D, NAME, ...)                                \
     {3, BM, BN, BK, WM, WN, V, D, NAME,                                                      \
      {{nullptr, launch_gemm<int8_t, BM, BN, BK, WM, WN, false, true, V, D, int32_t>},         \

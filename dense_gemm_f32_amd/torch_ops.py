@@ -14,8 +14,7 @@ attention scores.
 
 Input types: float32, float16, bfloat16 (fp32 accumulate; fp32 output, or
 the inputs' own 16-bit type), float64 (float64 output) and int8 (int32
-output, wrapping; A is used as a row-major [M][K] matrix and B as [N][K],
-the one int8 layout the library builds, so other views are copied into it).
+output, wrapping).  Every type takes row-major and transposed views in place.
 mm splits K over the device for deep-K shapes that would leave it idle
 (the library's automatic split count), with a torch-allocated workspace.
 """
@@ -123,19 +122,6 @@ def _c_name(c, in_name):
     return name
 
 
-def _int8_layout(x, op, ld, want_op, b_stride=None):
-    """int8 operands must be K-contiguous: A (logical M x K) stored row-major
-    (op N), B (logical K x N) stored as its transpose, [N][K] (op T).  x is
-    the operand's logical view; a copy is made when its storage differs."""
-    if op == want_op:
-        return x, op, ld, b_stride
-    if x.dim() == 2:
-        y = x.contiguous() if want_op == 0 else x.t().contiguous()
-        return y, want_op, y.shape[1], b_stride
-    y = x.contiguous() if want_op == 0 else x.transpose(1, 2).contiguous()
-    return y, want_op, y.shape[2], (y.stride(0) if y.shape[0] > 1 else 0)
-
-
 def _launch(name, c_name, op_a, op_b, M, N, K, alpha, a, lda, sa, b, ldb, sb, beta, c, ldc, sc,
             batch, splitk=None):
     """One library call: fp64 through its own entry points, a single matrix
@@ -168,9 +154,6 @@ def mm(a, b, *, alpha=1.0, beta=0.0, out=None, out_dtype=None, splitk=None):
     N = b.shape[1]
     a, op_a, lda = _operand(a)
     b, op_b, ldb = _operand(b)
-    if name == "i8":
-        a, op_a, lda, _ = _int8_layout(a, op_a, lda, 0)
-        b, op_b, ldb, _ = _int8_layout(b, op_b, ldb, 1)
     c = _out((M, N), out_dtype, a, out, beta, name)
     _launch(name, _c_name(c, name), op_a, op_b, M, N, K, alpha, a, lda, 0, b, ldb, 0, beta, c,
             max(N, 1), M * N, 1, splitk)
@@ -190,9 +173,6 @@ def bmm(a, b, *, alpha=1.0, beta=0.0, out=None, out_dtype=None):
     M, K, N = a.shape[1], a.shape[2], b.shape[2]
     a, op_a, lda, sa = _batched_operand(a)
     b, op_b, ldb, sb = _batched_operand(b)
-    if name == "i8":
-        a, op_a, lda, sa = _int8_layout(a, op_a, lda, 0, sa)
-        b, op_b, ldb, sb = _int8_layout(b, op_b, ldb, 1, sb)
     c = _out((batch, M, N), out_dtype, a, out, beta, name)
     _launch(name, _c_name(c, name), op_a, op_b, M, N, K, alpha, a, lda, sa, b, ldb, sb, beta, c,
             max(N, 1), M * N, batch, splitk=1)
@@ -223,7 +203,7 @@ def attention_scores(q, k, scale=None, *, out_dtype=None):
     """scale * q @ k^T per (batch, head): q (B, H, S, D), k (B, H, T, D) ->
     (B, H, S, T), i.e. einsum('bhqd,bhkd->bhqk') scaled; scale defaults to
     1/sqrt(D) (1 for int8 inputs, whose scale must be an integer).  k is read
-    in place as the transposed operand (int8: copied when stored D-major)."""
+    in place as the transposed operand."""
     if q.dim() != 4 or k.dim() != 4 or q.shape[:2] != k.shape[:2] or q.shape[3] != k.shape[3]:
         raise ValueError(f"attention_scores: shapes {tuple(q.shape)} and {tuple(k.shape)}")
     name = _check_pair(q, k)
@@ -237,10 +217,6 @@ def attention_scores(q, k, scale=None, *, out_dtype=None):
     k3, op_k, ldk, sk = _batched_operand(k.reshape(B * H, T, D))
     # scores = q k^T: op(B) = k^T, so k's own layout flips
     op_kt = 1 - op_k
-    if name == "i8":
-        q3, op_q, ldq, sq = _int8_layout(q3, op_q, ldq, 0, sq)
-        # the library's B is k^T, logical (D, T); int8 wants it stored [T][D]
-        k3, op_kt, ldk, sk = _int8_layout(k3.transpose(1, 2), op_kt, ldk, 1, sk)
     c = _out((B, H, S, T), out_dtype, q, None, 0.0, name)
     _launch(name, _c_name(c, name), op_q, op_kt, S, T, D, float(scale), q3, ldq, sq, k3, ldk, sk,
             0.0, c, max(T, 1), S * T, B * H, splitk=1)

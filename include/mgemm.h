@@ -157,8 +157,9 @@ mgemm_status gemm_strided_batched(mgemm_dtype in_dtype, mgemm_op transA, mgemm_o
  * accumulator): c_dtype must be MGEMM_I32; products accumulate exactly in
  * int32 and alpha*acc + beta*C is formed in 32-bit two's-complement
  * arithmetic (wrapping on overflow).  alpha and beta must be integers that
- * fit int32, and only transA = MGEMM_OP_N, transB = MGEMM_OP_T (both
- * operands K-contiguous) is built; anything else is MGEMM_INVALID_ARG.
+ * fit int32 (else MGEMM_INVALID_ARG).  Every transpose is accepted; an
+ * MN-contiguous operand is read with transposing LDS reads, on tiles of
+ * 128x128 and up (the 64x64 tiles serve transA = N, transB = T only).
  * lda, ldb, strides in elements (bytes); C aligned to 4 bytes.
  */
 mgemm_status gemm_strided_batched_ex(mgemm_dtype in_dtype, mgemm_dtype c_dtype,
@@ -391,8 +392,8 @@ mgemm_status mgemm_splitk_plan(mgemm_dtype in_dtype, mgemm_op transA, mgemm_op t
  * the one-pass entry points are faster, and the automatic plan of
  * gemm_splitk does not choose it.
  *   in_dtype  MGEMM_F32, MGEMM_F16, MGEMM_BF16 (then c_dtype MGEMM_F32) or
- *          MGEMM_I8 (c_dtype MGEMM_I32, transA N, transB T); other pairs
- *          and MGEMM_F64 give MGEMM_INVALID_ARG.
+ *          MGEMM_I8 (c_dtype MGEMM_I32); other pairs and MGEMM_F64 give
+ *          MGEMM_INVALID_ARG.
  *   alpha, beta  double, exactly representable as float (int8: integral,
  *          as gemm_strided_batched_ex).
  *   workgroups  n > 0: n workgroups, capped at MGEMM_STREAMK_MAX_WORKGROUPS

@@ -266,10 +266,14 @@ def test_int8_rules_without_a_gpu():
     def call(tA=0, tB=1, c_dt=4, alpha=1.0, beta=0.0, M=4, A=ALIGNED):
         return ex(3, c_dt, tA, tB, M, 4, 16, alpha, A, 16, 0, ALIGNED, 16, 0, beta, ALIGNED, 4, 0,
                   1, None)
-    # int32 C only; A and B K-contiguous only; integral alpha and beta only
+    # int32 C only; integral alpha and beta only
     assert call(c_dt=0) == 1 and call(c_dt=3) == 1
-    assert call(tA=1) == 1 and call(tB=0) == 1 and call(tA=1, tB=0) == 1
     assert call(alpha=0.5) == 1 and call(beta=1.5) == 1 and call(alpha=3e9) == 1
+    for tA, tB in ((0, 0), (1, 0), (1, 1)):
+        assert call(tA=tA, tB=tB, alpha=0.5) == 1
+        assert call(tA=tA, tB=tB, M=0) == 0          # every transpose is legal (nothing to do)
+        info, _ = sel("i8", tA, tB, M=4, N=4, K=16, lda=4 if tA else 16, ldb=16 if tB else 4)
+        assert info["dtype"] == 3
     # int32 C is for int8 inputs only
     assert ex(0, 4, 0, 0, 4, 4, 4, 1.0, ALIGNED, 4, 0, ALIGNED, 4, 0, 0.0, ALIGNED, 4, 0, 1,
               None) == 1
@@ -306,6 +310,19 @@ def test_fp64_rules_without_a_gpu():
     assert info["name"].endswith("_u")
     info, _ = sel("f64", 1, 1, M=512, N=512, K=512)
     assert not info["name"].endswith("_u")
+
+
+def test_i8_every_transpose_has_builds():
+    # every transpose is accepted; an MN-contiguous operand rules out the 64x64 tiles
+    for tA, tB in ((0, 0), (0, 1), (1, 0), (1, 1)):
+        for M, N, K in ((64, 64, 256), (1000, 1027, 1024), (8192, 8192, 8192)):
+            lda = M if tA else K
+            ldb = K if tB else N
+            info, _ = sel("i8", tA, tB, M=M, N=N, K=K, lda=lda, ldb=ldb, ldc=N)
+            assert info["dtype"] == 3
+            if (tA, tB) != (0, 1):
+                assert info["block_m"] >= 128, (tA, tB, M, N, K, info["name"])
+    assert sel("i8", 0, 1, M=64, N=64, K=256, lda=256, ldb=256)[0]["block_m"] == 64
 
 
 def test_small_problem_choice():
@@ -404,7 +421,7 @@ def test_streamk_rules_without_a_gpu():
     assert call(wbytes=need - 1) == 1
     assert call(alpha=1.0 + 2 ** -40) == 1                     # not a float
     assert call(in_dt=1, c_dt=1) == 1                          # fp32 C only for 16-bit inputs
-    assert call(in_dt=3, c_dt=4) == 1                          # int8 takes N x T only
+    assert call(in_dt=3, c_dt=4, tB=1, alpha=1.5) == 1         # int8: integral alpha
     assert call(in_dt=5, c_dt=5) == 1                          # no fp64 stream-K
     # nothing to do: OK without a workspace
     for in_dt, c_dt, tB in ((0, 0, 0), (2, 0, 0), (3, 4, 1)):
@@ -480,8 +497,9 @@ def test_streamk_plans():
         mg.streamk_plan("f64", 100, 100, 100)
     with pytest.raises(mg.MgemmError):
         mg.streamk_plan("f32", 100, 100, 100, -1)
-    with pytest.raises(mg.MgemmError):
-        mg.streamk_plan("i8", 100, 100, 128)   # int8 needs transB
+    # int8 with an MN-contiguous operand: the 128x128 tiles (transposing LDS reads)
+    for tA, tB in ((0, 0), (1, 0), (1, 1)):
+        assert mg.streamk_plan("i8", 100, 100, 128, transA=tA, transB=tB)["variant"]["block_m"] == 128
 
 
 def test_splitk_automatic_plans():

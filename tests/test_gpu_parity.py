@@ -90,6 +90,14 @@ def _ld_unaligned(v, dtype, cols):
     return cols + 1
 
 
+def transposes_of(v, dtype):
+    """(transA, transB) pairs build v has launchers for: all four, except the 64x64 int8
+    tiles (A and B K-contiguous only)."""
+    if dtype == "i8" and v["block_m"] < 128:
+        return [(False, True)]
+    return list(itertools.product((False, True), repeat=2))
+
+
 def _assert_selected(p, v):
     # a forced aligned-only variant falls back to the automatic choice on unaligned
     # operands: make sure the case really runs the variant it is meant to cover
@@ -190,7 +198,7 @@ def test_dma_path_k_tails(dtype):
         mg.force_variant(dtype, v["id"])
         bm, bn = v["block_m"], v["block_n"]
         slab = v["block_k"] // 2 if v["pipe"] == 1 else v["block_k"]
-        combos = [(False, True)] if dtype == "i8" else list(itertools.product((False, True), repeat=2))
+        combos = transposes_of(v, dtype)
         M, N = 2 * bm + 17, 2 * bn + 9
         pad = 16 if dtype == "i8" else 8
         padded = lambda cols: -(-cols // pad) * pad + pad   # 16-byte rows, padding after
@@ -372,23 +380,26 @@ def test_c16_quick_returns_scale_c(dtype):
 # ------------------------------------------------------------------ int8 inputs, int32 C
 
 def test_i8_every_variant():
-    # A and B K-contiguous (the layout built); interior (LDS-DMA) and edge tiles,
-    # aligned and odd leading dimensions, integral alpha and beta, exact
+    # every transpose each build has (an MN-contiguous operand through transposing LDS
+    # reads); interior (LDS-DMA) and edge tiles, aligned and odd leading dimensions,
+    # integral alpha and beta, exact
     for v in variants_of("i8"):
         mg.force_variant("i8", v["id"])
         aligned = not v["name"].endswith("_u")
         bm, bn, bk = v["block_m"], v["block_n"], v["block_k"]
-        for (M, N, K) in ((2 * bm + 17, 2 * bn + 9, 4 * bk), (bm + 3, bn + 40, 3 * bk + 29)):
-            if _narrow_dw(v, "i8"):
-                K -= K % 4      # 4-byte pieces of k
-            for alpha, beta in ((1.0, 0.0), (-3.0, 2.0)):
-                p = wl.Problem("i8", M, N, K, transB=True, c_dtype="i32", alpha=alpha, beta=beta,
-                               lda=(K + 16 - K % 16 if aligned else _ld_unaligned(v, "i8", K)),
-                               ldb=(K + 16 - K % 16 if aligned else _ld_unaligned(v, "i8", K + 2)),
-                               dist="int", int_lo=-128, int_hi=127, c_dist="int", seed=71,
-                               pad_value=77)
-                _assert_selected(p, v)
-                full_check(p, exact=True, what=f"{v['name']} i8 alpha={alpha} beta={beta}")
+        ld = lambda cols: -(-cols // 16) * 16 + 16 if aligned else _ld_unaligned(v, "i8", cols)
+        for n, (tA, tB) in enumerate(transposes_of(v, "i8")):
+            for (M, N, K) in ((2 * bm + 17, 2 * bn + 9, 4 * bk), (bm + 3, bn + 40, 3 * bk + 29)):
+                if _narrow_dw(v, "i8"):
+                    K -= K % 4      # 4-byte pieces of k
+                for alpha, beta in ((1.0, 0.0), (-3.0, 2.0)):
+                    p = wl.Problem("i8", M, N, K, transA=tA, transB=tB, c_dtype="i32", alpha=alpha,
+                                   beta=beta, lda=ld(M if tA else K), ldb=ld(K if tB else N),
+                                   dist="int", int_lo=-128, int_hi=127, c_dist="int", seed=71 + n,
+                                   pad_value=77)
+                    _assert_selected(p, v)
+                    full_check(p, exact=True, what=f"{v['name']} i8 tA={int(tA)} tB={int(tB)} "
+                                                   f"alpha={alpha} beta={beta}")
 
 
 def test_i8_wraps_like_int32():
@@ -486,7 +497,7 @@ def test_splitk_every_type_and_transpose_exact(dtype, c_dtype, hi):
     # integer-valued inputs: the chunked sum is exact, so bit-exact; K is no
     # multiple of the chunk, so the last chunk is short (and takes the edge path)
     lo = -128 if dtype == "i8" else -hi
-    trans = [(False, True)] if dtype == "i8" else list(itertools.product((False, True), repeat=2))
+    trans = list(itertools.product((False, True), repeat=2))
     for tA, tB in trans:
         for splits, (M, N, K) in ((2, (150, 133, 700)), (5, (70, 300, 1111)), (0, (200, 190, 2050))):
             ab = (3.0, -2.0) if dtype == "i8" else (1.5, 0.5)
@@ -592,11 +603,11 @@ def test_streamk_exact(dtype):
     # (odd leading dimensions), one workgroup, and one workgroup per
     # (tile, iteration) pair
     i8 = dtype == "i8"
-    trans = [(False, True)] if i8 else [(False, False), (False, True), (True, False), (True, True)]
+    trans = [(False, False), (False, True), (True, False), (True, True)]
     cases = [((1000, 1027, 999), 0), ((1000, 1027, 999), 37), ((150, 133, 700), 0),
              ((70, 300, 1111), 5), ((200, 190, 2050), 1), ((64, 64, 300), None)]
     for n, (tA, tB) in enumerate(trans):
-        for (M, N, K), wgs in cases[n % 2::2] if not i8 else cases:
+        for (M, N, K), wgs in cases[n % 2::2]:
             plan = mg.streamk_plan(dtype, M, N, K, 0, transA=int(tA), transB=int(tB))
             if wgs is None:   # one workgroup per (tile, iteration) pair
                 wgs = plan["tiles"] * plan["iterations"]

@@ -15,7 +15,7 @@ covers every build of every type:
 - the one-stage builds (PIPE 3) and the 4-byte-copy builds (PIPE 4);
 - the SPREAD order of the 256x256 16-bit builds (MN-contiguous B, that is
   transB = N);
-- int8 and fp64;
+- int8 (transposing 8-bit reads for MN-contiguous operands) and fp64;
 - split-K chunks and stream-K segments, whose rings restart per segment.
 """
 import itertools
@@ -92,7 +92,7 @@ def lds(dtype, cols, aligned, narrow_dw):
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "i8", "f64"])
 def test_every_build_under_lds_poison(dtype):
-    combos = [(False, True)] if dtype == "i8" else list(itertools.product((False, True), repeat=2))
+    combos = list(itertools.product((False, True), repeat=2))
     seen = 0
     for v in builds(dtype):
         mg.force_variant(dtype, v["id"])
@@ -124,13 +124,13 @@ def test_every_build_under_lds_poison(dtype):
 
 
 # (K, lda, ldb) per type: fp32 with odd rows (the 4-byte-copy build), bf16 with
-# 16-byte rows (the DMA ring), int8 N x T
-STREAM_SHAPES = {"f32": (999, 999, 1027), "bf16": (1000, 1000, 1032), "i8": (1024, 1024, 1024)}
+# 16-byte rows (the DMA ring), int8 N x N with 16-byte rows
+STREAM_SHAPES = {"f32": (999, 999, 1027), "bf16": (1000, 1000, 1032), "i8": (1024, 1024, 1040)}
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "i8"])
 def test_streamk_and_splitk_under_lds_poison(dtype):
-    tB = dtype == "i8"
+    tB = False   # B MN-contiguous: int8 through its transposing reads
     K, lda, ldb = STREAM_SHAPES[dtype]
     for wgs in (0, 37):
         p = int_problem(dtype, 1000, 1027, K, False, tB, lda, ldb, seed=260 + wgs)

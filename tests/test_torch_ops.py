@@ -165,19 +165,6 @@ def test_attention_scores_match_einsum_definition(dtype):
             assert np.max(np.abs(got[b, h] - ref)) <= tol * np.max(np.abs(ref))
 
 
-def test_int8_layout_copies_only_when_needed():
-    x = torch.zeros(6, 10, dtype=torch.int8)
-    assert torch_ops._int8_layout(x, 0, 10, 0)[0] is x                    # A row-major: as is
-    y, op, ld, _ = torch_ops._int8_layout(x.t(), 1, 10, 0)                # A given transposed
-    assert op == 0 and ld == 6 and y.is_contiguous() and torch.equal(y, x.t())
-    b = torch.zeros(10, 4, dtype=torch.int8)                              # B (K, N) row-major
-    y, op, ld, _ = torch_ops._int8_layout(b, 0, 4, 1)
-    assert op == 1 and ld == 10 and tuple(y.shape) == (4, 10) and torch.equal(y.t(), b)
-    z = torch.zeros(3, 10, 4, dtype=torch.int8)
-    y, op, ld, st = torch_ops._int8_layout(z, 0, 4, 1, 40)
-    assert op == 1 and ld == 10 and st == 40 and tuple(y.shape) == (3, 4, 10)
-
-
 def test_dtype_names_and_default_outputs():
     assert torch_ops._dtype_name(torch.float64) == "f64"
     assert torch_ops._dtype_name(torch.int8) == "i8"
@@ -211,7 +198,10 @@ def test_mm_and_bmm_int8_any_view():
     a = torch.randint(-128, 128, (M, K), generator=gen).to(torch.int8)
     b = torch.randint(-128, 128, (K, N), generator=gen).to(torch.int8)
     want = (a.long() @ b.long()).numpy()
-    for x, y in ((a.cuda(), b.cuda()), (a.t().contiguous().cuda().t(), b.t().contiguous().cuda().t())):
+    # row-major or transposed storage of each operand, read in place (all four transposes)
+    at = a.t().contiguous().cuda().t()
+    bt = b.t().contiguous().cuda().t()
+    for x, y in ((a.cuda(), b.cuda()), (at, b.cuda()), (a.cuda(), bt), (at, bt)):
         got = torch_ops.mm(x, y)
         assert got.dtype == torch.int32
         assert np.array_equal(got.cpu().numpy(), want)
