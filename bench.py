@@ -168,6 +168,10 @@ def summarize_case(case, d, copy_dir):
     util_v, util_d = _counters(os.path.join(d, "util"), filt)
     cf = _mean(_counters(os.path.join(copy_dir, "fetch"), "copyBuffer")[0].get("FETCH_SIZE", []))
     cw = _mean(_counters(os.path.join(copy_dir, "write"), "copyBuffer")[0].get("WRITE_SIZE", []))
+    # read-only calibration: a reduction over the same number of bytes (its FETCH_SIZE
+    # should take the copy's scale if the counter's unit is the same for plain reads)
+    rf = _mean(_counters(os.path.join(copy_dir, "read"), "reduce")[0].get("FETCH_SIZE", []))
+    floor, floor_rounds = xcd_fetch_floor(p, info, grid)
     fetch = _mean(fetch_v.get("FETCH_SIZE", []))
     write = _mean(write_v.get("WRITE_SIZE", []))
     expect_kib = COPY_PROBE_BYTES / 1024.0
@@ -196,6 +200,8 @@ def summarize_case(case, d, copy_dir):
            "rocprofv3 --pmc {u} (same, -d DIR/{c}/util);  "
            "rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE --output-format csv -d DIR/copy/fetch, "
            "DIR/copy/write -o run -- python3 bench.py --copy-probe;  "
+           "rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/copy/read -o run -- "
+           "python3 bench.py --read-probe;  "
            "python3 bench.py --summarize-profiles DIR").format(
                c=case, u=" ".join(UTIL_COUNTERS[:4] + (MOPS_COUNTER[dt],) + UTIL_COUNTERS[4:]))
     lines = [
@@ -245,11 +251,19 @@ def summarize_case(case, d, copy_dir):
         "copy_probe_bytes: %d" % COPY_PROBE_BYTES,
         "copy_FETCH_SIZE_KiB: " + _fmt(cf, "%.1f"),
         "copy_WRITE_SIZE_KiB: " + _fmt(cw, "%.1f"),
+        "read_probe_FETCH_SIZE_KiB: " + _fmt(rf, "%.1f"),
         "fetch_scale: " + _fmt(sf, "%.4f"),
+        "fetch_scale_read_probe: " + _fmt(expect_kib / rf if rf else None, "%.4f"),
         "write_scale: " + _fmt(sw, "%.4f"),
         "traffic_bytes_per_launch: " + _fmt(traffic, "%d"),
         "algorithmic_bytes_per_launch: %d" % algo,
         "traffic_over_algorithmic: " + _fmt(traffic / algo if traffic else None, "%.3f"),
+        "fetch_bytes_per_launch: " + _fmt(fetch * sf * 1024 if fetch and sf else None, "%d"),
+        "xcd_fetch_floor_bytes: " + _fmt(floor, "%d"),
+        "xcd_round_fetch_bytes: " + _fmt(floor_rounds, "%d"),
+        "fetch_over_xcd_floor: " + _fmt(fetch * sf * 1024 / floor if fetch and sf and floor else None, "%.3f"),
+        "fetch_over_xcd_rounds: " + _fmt(fetch * sf * 1024 / floor_rounds
+                                         if fetch and sf and floor_rounds else None, "%.3f"),
     ]
     os.makedirs(PROFILES, exist_ok=True)
     path = summary_path(kname, case)
@@ -264,6 +278,18 @@ def summarize_profiles(d):
     for case in CASES:
         if os.path.isdir(os.path.join(d, case)):
             summarize_case(case, os.path.join(d, case), copy_dir)
+
+
+def read_probe():
+    """A device reduction over COPY_PROBE_BYTES (reads them once, writes a few bytes):
+    the read-only calibration of FETCH_SIZE beside the copy."""
+    import torch
+    x = torch.ones(COPY_PROBE_BYTES // 4, device="cuda:0")
+    for _ in range(5):
+        y = x.sum()
+    torch.cuda.synchronize()
+    assert float(y) == COPY_PROBE_BYTES // 4
+    print("read probe done", flush=True)
 
 
 def copy_probe():
@@ -540,6 +566,55 @@ def algorithmic_bytes(p):
     return per * p.batch
 
 
+def xcd_fetch_floor(p, info, grid):
+    """Operand bytes a plain launch must fetch from memory, two ways; (None, None) for
+    split-K and stream-K launches.  Each of the 8 XCDs has its own L2.  The kernels'
+    assignment: workgroup w runs on XCD w % 8, the ids are remapped to one contiguous range
+    of logical ids per XCD, and logical ids walk the tiles in groups of min(8, tile rows)
+    tile rows.
+      once: every A row panel and B column panel that the tiles on one XCD use, once per
+            XCD (a lower bound whatever the L2 holds);
+      rounds: the same per round of workgroups running together on an XCD (its 32 CUs
+            times the workgroups per CU that LDS allows), panels not kept from one round
+            to the next (an L2 too small for a round's panels).
+    C is added to both when it is read (beta != 0)."""
+    from dense_gemm_f32_amd import workloads as wl
+    if p.streamk is not None or p.splitk is not None or grid <= 0:
+        return None, None
+    bm, bn = info["block_m"], info["block_n"]
+    es = wl.ELEM_SIZE[p.dtype]
+    tiles_m, tiles_n = -(-p.M // bm), -(-p.N // bn)
+    group_m = max(1, min(tiles_m, 8))
+    per_b = tiles_m * tiles_n
+    per_cu = max(1, min(8, (160 << 10) // max(info["lds_bytes"], 1)))
+    round_size = 32 * per_cu
+    q, rem = grid // N_XCD, grid % N_XCD
+
+    def panels(ids):
+        a_pan, b_pan = set(), set()
+        for L in ids:
+            b = L // per_b
+            t = L - b * per_b
+            width = group_m * tiles_n
+            g = t // width
+            first = g * group_m
+            gsz = min(tiles_m - first, group_m)
+            w2 = t - g * width
+            a_pan.add((b if p.strideA else 0, first + w2 % gsz))
+            b_pan.add((b if p.strideB else 0, w2 // gsz))
+        return (sum(min(bm, p.M - tm * bm) for _, tm in a_pan) * p.K * es +
+                sum(min(bn, p.N - tn * bn) for _, tn in b_pan) * p.K * es)
+
+    once = rounds = 0
+    for x in range(N_XCD):
+        start = x * q + min(x, rem)
+        ids = range(start, start + q + (1 if x < rem else 0))
+        once += panels(ids)
+        rounds += sum(panels(ids[i:i + round_size]) for i in range(0, len(ids), round_size))
+    c_read = p.M * p.N * wl.ELEM_SIZE[p.c_dtype] * p.batch if p.beta != 0 else 0
+    return once + c_read, rounds + c_read
+
+
 def per_config(torch, dev, iters, tel=None, checks=None):
     """Every workload: 30 warm-up launches (the part settles at its power-limited
     clock), then `iters` back-to-back launches (mean) and `iters` single
@@ -746,12 +821,16 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--read-probe", action="store_true")
     ap.add_argument("--summarize-profiles", metavar="DIR")
     ap.add_argument("--profile-case", metavar="NAME", choices=CASES)
     ap.add_argument("--launches", type=int, default=20)
     args = ap.parse_args()
     if args.copy_probe:
         copy_probe()
+        return
+    if args.read_probe:
+        read_probe()
         return
     if args.summarize_profiles:
         summarize_profiles(args.summarize_profiles)
