@@ -493,9 +493,10 @@ class Telemetry:
 
 
 def mfma_ceiling(torch, dev, tel):
-    """Register-only matrix-core rate (libmgemm_diag.so) on N(0,1) operand values,
-    bf16 and binary16: the power-limited ceiling no 16-bit GEMM on this board
-    and data can exceed.  None when the diagnostic library is not built."""
+    """Register-only matrix-core rate (libmgemm_diag.so) on the operand values of the
+    workloads: N(0,1) rounded to bf16 and to binary16, and int8 uniform in -128..127.
+    The power-limited ceiling no GEMM of that type on this board and data can exceed.
+    None when the diagnostic library is not built."""
     import ctypes
     path = os.path.join(ROOT, "dense_gemm_f32_amd", "libmgemm_diag.so")
     if not os.path.exists(path):
@@ -506,25 +507,30 @@ def mfma_ceiling(torch, dev, tel):
                                             ctypes.c_int, ctypes.c_void_p]
     lib.mgemm_diag_ceiling_operand_bytes.restype = ctypes.c_int64
     lib.mgemm_diag_ceiling_out_floats.restype = ctypes.c_int64
-    lib.mgemm_diag_ceiling_flop.restype = ctypes.c_double
-    lib.mgemm_diag_ceiling_flop.argtypes = [ctypes.c_int]
-    n16 = lib.mgemm_diag_ceiling_operand_bytes() // 2
+    lib.mgemm_diag_ceiling_ops.restype = ctypes.c_double
+    lib.mgemm_diag_ceiling_ops.argtypes = [ctypes.c_int, ctypes.c_int]
+    nbytes = lib.mgemm_diag_ceiling_operand_bytes()
     out = torch.empty(lib.mgemm_diag_ceiling_out_floats(), dtype=torch.float32, device=dev)
     iters = 40000
     res = {}
-    for name, tdt in (("bf16", torch.bfloat16), ("f16", torch.float16)):
+    for name, kind in (("bf16", 1), ("f16", 0), ("i8", 2)):   # MGEMM_DIAG_* in mgemm_diag.h
         g = torch.Generator().manual_seed(1004)
-        ops = torch.randn(n16, generator=g).to(tdt).to(dev)
+        if name == "i8":
+            ops = torch.randint(-128, 128, (nbytes,), generator=g, dtype=torch.int8).to(dev)
+            data = "int8 uniform in -128..127"
+        else:
+            ops = torch.randn(nbytes // 2, generator=g).to(wl_dtype(torch, name)).to(dev)
+            data = "N(0,1) rounded to %s" % name
         st = torch.cuda.current_stream()
-        fn = lambda: lib.mgemm_diag_mfma_ceiling(int(name == "bf16"), ops.data_ptr(), out.data_ptr(),
+        fn = lambda: lib.mgemm_diag_mfma_ceiling(kind, ops.data_ptr(), out.data_ptr(),
                                                  iters, ctypes.c_void_p(st.cuda_stream))
         for _ in range(3):
             assert fn() == 0
         each = time_each(torch, fn, 5)
         t = statistics.median(each)
-        tf = lib.mgemm_diag_ceiling_flop(iters) / t / 1e12
+        tf = lib.mgemm_diag_ceiling_ops(kind, iters) / t / 1e12
         rec = {"tflops": round(tf, 1), "frac_matrix_peak": round(tf / PEAK_TFLOPS[name], 4),
-               "data": "N(0,1) rounded to %s" % name, "ms": round(t * 1e3, 3)}
+               "data": data, "ms": round(t * 1e3, 3)}
         tel_r = tel.sustained(torch, fn, t) if tel else None
         if tel_r:
             rec.update(tel_r)
@@ -532,6 +538,10 @@ def mfma_ceiling(torch, dev, tel):
         log(f"mfma ceiling {name}: {rec}")
         del ops
     return res
+
+
+def wl_dtype(torch, name):
+    return {"bf16": torch.bfloat16, "f16": torch.float16}[name]
 
 
 def sample_positions(p, n_random=4096, seed=7):
@@ -903,7 +913,7 @@ def main():
         # the same kernel, sustained: the clock the roofline fraction was reached at
         roofline["clock_mhz"] = per[PRIMARY]["telemetry"]["clock_mhz"]
     if per and ceiling:
-        for name in ("gemm_bf16_8192", "gemm_f16_8192"):
+        for name in ("gemm_bf16_8192", "gemm_f16_8192", "gemm_i8_8192"):
             c = ceiling[per[name]["dtype"]]["tflops"]
             per[name]["frac_of_mfma_ceiling"] = round(per[name]["tflops"] / c, 4)
     cpu = None

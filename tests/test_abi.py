@@ -84,6 +84,11 @@ def test_diag_library_exports_its_header():
     lib.mgemm_diag_mfma_ceiling.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                             ctypes.c_int, ctypes.c_void_p]
     assert lib.mgemm_diag_mfma_ceiling(1, None, None, 10, None) == 1   # refused, no launch
+    assert lib.mgemm_diag_mfma_ceiling(7, 16, 16, 10, None) == 1        # unknown kind, no launch
+    lib.mgemm_diag_ceiling_ops.restype = ctypes.c_double
+    lib.mgemm_diag_ceiling_ops.argtypes = [ctypes.c_int, ctypes.c_int]
+    assert lib.mgemm_diag_ceiling_ops(2, 1) == 2 * lib.mgemm_diag_ceiling_flop(1)   # int8: 32x32x32
+    assert lib.mgemm_diag_ceiling_ops(1, 3) == lib.mgemm_diag_ceiling_flop(3)
 
 
 def test_status_strings():
