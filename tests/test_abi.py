@@ -484,7 +484,7 @@ def test_streamk_plans():
     assert mg.streamk_plan("f32", 4096, 4096, 4096, 10 ** 6)["workgroups"] == mg.STREAMK_MAX_WORKGROUPS
     one = mg.streamk_plan("f32", 64, 64, 300, 1000)
     assert (one["tiles"], one["iterations"], one["workgroups"]) == (1, 10, 10)
-    # the K-iteration is the type's K granule; int8 takes N x T only
+    # the K-iteration is the type's K granule
     assert mg.streamk_plan("bf16", 500, 500, 500)["k_per_iteration"] == 64
     i8 = mg.streamk_plan("i8", 1000, 1027, 999, transB=1)
     assert i8["k_per_iteration"] == 128
