@@ -120,117 +120,247 @@ struct F64Operand {
 // sub-tile of TM x TN blocks of 16x16; BK-deep K-slabs (a multiple of 16).
 // V2: A and B allow 16-byte loads.
 template <int BM, int BN, int BK, int WM, int WN, bool TA, bool TB, bool V2>
+struct F64Tile {
+    static_assert(BK % 16 == 0, "K-slab");
+    static constexpr int NT = WM * WN * 64;
+    static constexpr int WTM = BM / WM, WTN = BN / WN, TM = WTM / 16, TN = WTN / 16;
+    static_assert(TM * 16 * WM == BM && TN * 16 * WN == BN, "tile");
+    static constexpr int VEC = V2 ? 2 : 1;
+    using OpA = F64Operand<BM, BK, NT, TA, VEC>;    // A^T in memory: rows are k
+    using OpB = F64Operand<BN, BK, NT, !TB, VEC>;   // B in memory: rows are k
+    static constexpr int A_ELEMS = BK * OpA::P, B_ELEMS = BK * OpB::P, STAGE = A_ELEMS + B_ELEMS;
+    static constexpr int SMEM = 2 * STAGE;          // doubles of LDS
+
+    // acc += op(A) x op(B) over K columns of A (rows of B) for the tile at
+    // (m0, n0) of batch entry bidx, starting `k_off` columns in; mrem, nrem:
+    // rows and columns of the tile inside C.
+    __device__ __forceinline__ static void run(const KernelArgs &p, double *smem, int bidx, int m0, int n0,
+                                               int64_t k_off, int K, f64x4 (&acc)[TM][TN])
+    {
+        const int tid = threadIdx.x;
+        const int lane = tid & 63, wave = tid >> 6;
+        const int wm = wave / WN, wn = wave % WN;
+        const int g = lane >> 4, li = lane & 15;
+        const double *Ap = static_cast<const double *>(p.A) + (int64_t)bidx * p.strideA +
+                           (TA ? (int64_t)m0 + k_off * p.lda : (int64_t)m0 * p.lda + k_off);
+        const double *Bp = static_cast<const double *>(p.B) + (int64_t)bidx * p.strideB +
+                           (TB ? (int64_t)n0 * p.ldb + k_off : (int64_t)n0 + k_off * p.ldb);
+        const int64_t a_kstep = TA ? (int64_t)BK * p.lda : (int64_t)BK;
+        const int64_t b_kstep = TB ? (int64_t)BK : (int64_t)BK * p.ldb;
+        const int mrem = p.M - m0, nrem = p.N - n0;
+
+        OpA la;
+        OpB lb;
+        auto load_slab = [&](int kt) {
+            const int krem = K - kt * BK;
+            const double *a = Ap + (int64_t)kt * a_kstep;
+            const double *b = Bp + (int64_t)kt * b_kstep;
+            if constexpr (TA) la.load(a, p.lda, krem, mrem, tid);
+            else              la.load(a, p.lda, mrem, krem, tid);
+            if constexpr (TB) lb.load(b, p.ldb, nrem, krem, tid);
+            else              lb.load(b, p.ldb, krem, nrem, tid);
+        };
+        // MFMA steps of k = 4; in each 16-deep group h of the slab, lane group g
+        // takes k = 16h + 8(g&1) + 4(g>>1) + s at step s
+        const int g_row = 8 * (g & 1) + 4 * (g >> 1);
+        auto compute = [&](int stage) {
+            const double *sa = smem + stage * STAGE + wm * WTM + li;
+            const double *sb = smem + stage * STAGE + A_ELEMS + wn * WTN + li;
+#pragma unroll
+            for (int hs = 0; hs < BK / 4; ++hs) {
+                const int kr = 16 * (hs >> 2) + g_row + (hs & 3);
+                double a[TM], b[TN];
+#pragma unroll
+                for (int t = 0; t < TM; ++t) a[t] = sa[kr * OpA::P + 16 * t];
+#pragma unroll
+                for (int u = 0; u < TN; ++u) b[u] = sb[kr * OpB::P + 16 * u];
+#pragma unroll
+                for (int t = 0; t < TM; ++t)
+#pragma unroll
+                    for (int u = 0; u < TN; ++u)
+                        acc[t][u] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[t], b[u], acc[t][u], 0, 0, 0);
+            }
+        };
+
+        // two LDS stages; the next slab is fetched to registers during the current one
+        const int nk = (K + BK - 1) / BK;
+        lds_poison<2 * STAGE * 8>(smem);
+        load_slab(0);
+        la.store(smem, tid);
+        lb.store(smem + A_ELEMS, tid);
+        __syncthreads();
+        for (int kt = 0; kt + 1 < nk; ++kt) {
+            load_slab(kt + 1);
+            // a wave multiplying outranks one at its stores and barrier (four
+            // waves share each SIMD): about 1% in a same-box A/B
+            __builtin_amdgcn_s_setprio(1);
+            compute(kt & 1);
+            __builtin_amdgcn_s_setprio(0);
+            double *st = smem + ((kt + 1) & 1) * STAGE;
+            la.store(st, tid);
+            lb.store(st + A_ELEMS, tid);
+            __syncthreads();
+            lds_poison<STAGE * 8>(smem + (kt & 1) * STAGE);  // read by every wave
+        }
+        compute((nk - 1) & 1);
+    }
+
+    // Element (row, column) of the tile that register r of block (t, u) of
+    // this lane holds: register r of lane L is D[4r + L/16][L%16].
+    __device__ __forceinline__ static int row_of(int t, int r)
+    {
+        return (threadIdx.x >> 6) / WN * WTM + 16 * t + 4 * r + ((threadIdx.x & 63) >> 4);
+    }
+    __device__ __forceinline__ static int col_of(int u)
+    {
+        return (threadIdx.x >> 6) % WN * WTN + 16 * u + (threadIdx.x & 15);
+    }
+
+    // Block (t, u) of C: C = alpha*v + beta*C (C read only when beta != 0)
+    __device__ __forceinline__ static void store_block(const KernelArgs &p, int bidx, int m0, int n0, int t,
+                                                       int u, const f64x4 &v)
+    {
+        const int col = n0 + col_of(u);
+        if (col >= p.N) return;
+        double *Cb = static_cast<double *>(p.C) + (int64_t)bidx * p.strideC + col;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = m0 + row_of(t, r);
+            if (row >= p.M) continue;
+            double *c = Cb + (int64_t)row * p.ldc;
+            double x = p.alpha_d * v[r];
+            if (p.beta_d != 0.0) x += p.beta_d * *c;
+            __builtin_nontemporal_store(x, c);
+        }
+    }
+
+    __device__ __forceinline__ static void epilogue(const KernelArgs &p, int bidx, int m0, int n0,
+                                                    const f64x4 (&acc)[TM][TN])
+    {
+#pragma unroll
+        for (int t = 0; t < TM; ++t)
+#pragma unroll
+            for (int u = 0; u < TN; ++u)
+                store_block(p, bidx, m0, n0, t, u, acc[t][u]);
+    }
+
+    // stream-K: this workgroup's partial tile, BM x BN doubles row-major, with
+    // agent-scope stores (visible to every XCD once acknowledged)
+    __device__ __forceinline__ static void store_partial(void *part, const f64x4 (&acc)[TM][TN])
+    {
+        uint64_t *P = static_cast<uint64_t *>(part);
+#pragma unroll
+        for (int t = 0; t < TM; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int u = 0; u < TN; ++u) {
+                    // the element as a scalar first: a bit cast applied to a vector
+                    // element read element 0 whatever the index
+                    const double d = acc[t][u][r];
+                    __hip_atomic_store(P + row_of(t, r) * BN + col_of(u), __builtin_bit_cast(uint64_t, d),
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+    }
+
+    // stream-K: the last contributor me of split tile (bidx, m0, n0), whose
+    // iterations start at a0 and belong to workgroups g0..g1, adds the terms
+    // in ascending K (g0 first, its own sums from registers in their place;
+    // the others' partial tiles with agent-scope loads) and writes C.  One
+    // 16x16 block at a time, so that only its four sums are live beside the
+    // accumulators.
+    __device__ __forceinline__ static void finish(const KernelArgs &p, int bidx, int m0, int n0, int64_t a0,
+                                                  int64_t g0, int64_t g1, int64_t me,
+                                                  const f64x4 (&acc)[TM][TN])
+    {
+        constexpr int TSZ = BM * BN;
+        const uint64_t *part = static_cast<const uint64_t *>(p.sk_part);
+        const int first_slot = p.sk_total * g0 / p.sk_grid == a0 ? 0 : 1;
+#pragma unroll
+        for (int t = 0; t < TM; ++t)
+#pragma unroll
+            for (int u = 0; u < TN; ++u) {
+                f64x4 sum;
+                for (int64_t g = g0; g <= g1; ++g) {
+                    f64x4 v = acc[t][u];
+                    if (g != me) {
+                        const uint64_t *pg = part + (g * 2 + (g == g0 ? first_slot : 0)) * TSZ + col_of(u);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            v[r] = __builtin_bit_cast(double, __hip_atomic_load(pg + row_of(t, r) * BN,
+                                                                                __ATOMIC_RELAXED,
+                                                                                __HIP_MEMORY_SCOPE_AGENT));
+                    }
+                    sum = g == g0 ? v : sum + v;
+                }
+                store_block(p, bidx, m0, n0, t, u, sum);
+            }
+    }
+};
+
+template <int BM, int BN, int BK, int WM, int WN, bool TA, bool TB, bool V2>
 __global__ void __launch_bounds__(WM * WN * 64)
 gemm_f64_kernel(KernelArgs p)
 {
-    static_assert(BK % 16 == 0, "K-slab");
-    constexpr int NT = WM * WN * 64;
-    constexpr int WTM = BM / WM, WTN = BN / WN, TM = WTM / 16, TN = WTN / 16;
-    static_assert(TM * 16 * WM == BM && TN * 16 * WN == BN, "tile");
-    constexpr int VEC = V2 ? 2 : 1;
-    using OpA = F64Operand<BM, BK, NT, TA, VEC>;    // A^T in memory: rows are k
-    using OpB = F64Operand<BN, BK, NT, !TB, VEC>;   // B in memory: rows are k
-    constexpr int A_ELEMS = BK * OpA::P, B_ELEMS = BK * OpB::P, STAGE = A_ELEMS + B_ELEMS;
-    __shared__ __attribute__((aligned(16))) double smem[2 * STAGE];
-
+    using F = F64Tile<BM, BN, BK, WM, WN, TA, TB, V2>;
+    __shared__ __attribute__((aligned(16))) double smem[F::SMEM];
     int bidx, tm, tn;
     map_tile(p, bidx, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave / WN, wn = wave % WN;
-    const int g = lane >> 4, li = lane & 15;
-
-    const double *Ap = static_cast<const double *>(p.A) + (int64_t)bidx * p.strideA +
-                       (TA ? (int64_t)m0 : (int64_t)m0 * p.lda);
-    const double *Bp = static_cast<const double *>(p.B) + (int64_t)bidx * p.strideB +
-                       (TB ? (int64_t)n0 * p.ldb : (int64_t)n0);
-    const int64_t a_kstep = TA ? (int64_t)BK * p.lda : (int64_t)BK;
-    const int64_t b_kstep = TB ? (int64_t)BK : (int64_t)BK * p.ldb;
-    const int mrem = p.M - m0, nrem = p.N - n0;
     const int K = bidx == p.tail_batch ? p.k_tail : p.K;  // split-K's last chunk may be shorter
-
-    f64x4 acc[TM][TN];
+    f64x4 acc[F::TM][F::TN];
 #pragma unroll
-    for (int t = 0; t < TM; ++t)
+    for (int t = 0; t < F::TM; ++t)
 #pragma unroll
-        for (int u = 0; u < TN; ++u)
+        for (int u = 0; u < F::TN; ++u)
             acc[t][u] = f64x4{0.0, 0.0, 0.0, 0.0};
+    F::run(p, smem, bidx, m0, n0, 0, K, acc);
+    F::epilogue(p, bidx, m0, n0, acc);
+}
 
-    OpA la;
-    OpB lb;
-    auto load_slab = [&](int kt) {
-        const int krem = K - kt * BK;
-        const double *a = Ap + (int64_t)kt * a_kstep;
-        const double *b = Bp + (int64_t)kt * b_kstep;
-        if constexpr (TA) la.load(a, p.lda, krem, mrem, tid);
-        else              la.load(a, p.lda, mrem, krem, tid);
-        if constexpr (TB) lb.load(b, p.ldb, nrem, krem, tid);
-        else              lb.load(b, p.ldb, krem, nrem, tid);
-    };
-    // MFMA steps of k = 4; in each 16-deep group h of the slab, lane group g
-    // takes k = 16h + 8(g&1) + 4(g>>1) + s at step s
-    const int g_row = 8 * (g & 1) + 4 * (g >> 1);
-    auto compute = [&](int stage) {
-        const double *sa = smem + stage * STAGE + wm * WTM + li;
-        const double *sb = smem + stage * STAGE + A_ELEMS + wn * WTN + li;
+// Stream-K for fp64: the partition, segments and completion of gemm_sk_kernel
+// (gemm_kernel.hpp), with double partial tiles.
+template <int BM, int BN, int BK, int WM, int WN, bool TA, bool TB, bool V2>
+__global__ void __launch_bounds__(WM * WN * 64)
+gemm_f64_sk_kernel(KernelArgs p)
+{
+    using F = F64Tile<BM, BN, BK, WM, WN, TA, TB, V2>;
+    __shared__ __attribute__((aligned(16))) double smem[F::SMEM];
+    __shared__ int last_arrival;
+    const int L = logical_wg();
+    const int iters = p.sk_iters;
+    const int64_t beg = p.sk_total * L / p.sk_grid, end = p.sk_total * (L + 1) / p.sk_grid;
+    for (int64_t it = beg; it < end;) {
+        const int tile = (int)(it / iters);
+        const int k0 = (int)(it - (int64_t)tile * iters);
+        const int k1 = end - it < iters - k0 ? k0 + (int)(end - it) : iters;
+        int bidx, tm, tn;
+        tile_coords(p, tile, bidx, tm, tn);
+        const int m0 = tm * BM, n0 = tn * BN;
+        const int64_t ko = (int64_t)k0 * p.sk_unit;  // first k of the segment
+        const int K = k1 == iters ? p.K - (int)ko : (k1 - k0) * p.sk_unit;
+        f64x4 acc[F::TM][F::TN];
 #pragma unroll
-        for (int hs = 0; hs < BK / 4; ++hs) {
-            const int kr = 16 * (hs >> 2) + g_row + (hs & 3);
-            double a[TM], b[TN];
+        for (int t = 0; t < F::TM; ++t)
 #pragma unroll
-            for (int t = 0; t < TM; ++t) a[t] = sa[kr * OpA::P + 16 * t];
-#pragma unroll
-            for (int u = 0; u < TN; ++u) b[u] = sb[kr * OpB::P + 16 * u];
-#pragma unroll
-            for (int t = 0; t < TM; ++t)
-#pragma unroll
-                for (int u = 0; u < TN; ++u)
-                    acc[t][u] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[t], b[u], acc[t][u], 0, 0, 0);
+            for (int u = 0; u < F::TN; ++u)
+                acc[t][u] = f64x4{0.0, 0.0, 0.0, 0.0};
+        F::run(p, smem, bidx, m0, n0, ko, K, acc);
+        if (k0 == 0 && k1 == iters) {
+            F::epilogue(p, bidx, m0, n0, acc);
+        } else {
+            const int64_t a0 = (int64_t)tile * iters;
+            int64_t g0, g1;
+            sk_owners(p, a0, g0, g1);
+            const bool last = sk_arrive(p, g0, g1, last_arrival, [&] {
+                F::store_partial(static_cast<double *>(p.sk_part) +
+                                     ((int64_t)L * 2 + (it == beg ? 0 : 1)) * (BM * BN), acc);
+            });
+            if (last) F::finish(p, bidx, m0, n0, a0, g0, g1, L, acc);
         }
-    };
-
-    // two LDS stages; the next slab is fetched to registers during the current one
-    const int nk = (K + BK - 1) / BK;
-    lds_poison<2 * STAGE * 8>(smem);
-    load_slab(0);
-    la.store(smem, tid);
-    lb.store(smem + A_ELEMS, tid);
-    __syncthreads();
-    for (int kt = 0; kt + 1 < nk; ++kt) {
-        load_slab(kt + 1);
-        // a wave multiplying outranks one at its stores and barrier (four
-        // waves share each SIMD): about 1% in a same-box A/B
-        __builtin_amdgcn_s_setprio(1);
-        compute(kt & 1);
-        __builtin_amdgcn_s_setprio(0);
-        double *st = smem + ((kt + 1) & 1) * STAGE;
-        la.store(st, tid);
-        lb.store(st + A_ELEMS, tid);
-        __syncthreads();
-        lds_poison<STAGE * 8>(smem + (kt & 1) * STAGE);  // read by every wave
+        it += k1 - k0;
+        __syncthreads();  // the next segment refills the LDS stages
     }
-    compute((nk - 1) & 1);
-
-    // epilogue: C = alpha*acc + beta*C (C read only when beta != 0)
-    double *Cb = static_cast<double *>(p.C) + (int64_t)bidx * p.strideC;
-    const bool use_beta = p.beta_d != 0.0;
-#pragma unroll
-    for (int t = 0; t < TM; ++t)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = m0 + wm * WTM + 16 * t + 4 * r + g;
-            if (row >= p.M) continue;
-            double *crow = Cb + (int64_t)row * p.ldc;
-#pragma unroll
-            for (int u = 0; u < TN; ++u) {
-                const int col = n0 + wn * WTN + 16 * u + li;
-                if (col >= p.N) continue;
-                double v = p.alpha_d * acc[t][u][r];
-                if (use_beta) v += p.beta_d * crow[col];
-                __builtin_nontemporal_store(v, crow + col);
-            }
-        }
 }
 
 }  // namespace mgemm

@@ -1565,6 +1565,50 @@ __device__ __forceinline__ uint32_t sk_get1(const uint32_t *at)
     return __hip_atomic_load(at, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Count-in of one contribution to a split tile whose contributors are the
+// stream-K workgroups g0..g1; true when this workgroup completes the tile.
+// Each contributor counts in once.  If all the others already have (the
+// counter reads g1 - g0), this one is the last: it skips its partial tile,
+// finishes from its registers and clears the counter for the next launch.
+// Otherwise `store` writes its partial tile with agent-scope stores, every
+// wave waits until they are acknowledged (then visible to every XCD), and
+// the workgroup counts in with a wrapping increment (limit g1 - g0): the one
+// that reads g1 - g0 is the last, and the same increment has reset the
+// counter.  `flag` is a workgroup-shared int.  Call from uniform control flow.
+template <typename Store>
+__device__ __forceinline__ bool sk_arrive(const KernelArgs &p, int64_t g0, int64_t g1, int &flag, Store &&store)
+{
+    unsigned *count = p.sk_count + g0;
+    const unsigned others = (unsigned)(g1 - g0);
+    if (threadIdx.x == 0)
+        flag = __hip_atomic_load(count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == others;
+    __syncthreads();
+    // one value for the whole workgroup (read back from LDS): a uniform branch
+    bool last = __builtin_amdgcn_readfirstlane(flag);
+    if (!last) {
+        store();
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (threadIdx.x == 0)
+            flag = __builtin_amdgcn_atomic_inc32(count, others, __ATOMIC_RELAXED, "agent") == others;
+        __syncthreads();
+        last = __builtin_amdgcn_readfirstlane(flag);
+    } else if (threadIdx.x == 0) {
+        __hip_atomic_store(count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return last;
+}
+
+// Stream-K partition: stream-K workgroup L takes (tile, iteration) pairs
+// [T*L/G, T*(L+1)/G) (T = sk_total, G = sk_grid); a split tile whose pairs
+// start at a0 belongs to workgroups g0 .. g1, the owners of its first and
+// last pairs (owner(x) = ((x+1)*G - 1) / T).
+__device__ __forceinline__ void sk_owners(const KernelArgs &p, int64_t a0, int64_t &g0, int64_t &g1)
+{
+    g0 = ((a0 + 1) * p.sk_grid - 1) / p.sk_total;
+    g1 = ((a0 + p.sk_iters) * p.sk_grid - 1) / p.sk_total;
+}
+
 // The last contributor's share of stream-K: split tile (bidx, m0, n0), whose
 // iterations start at a0 and belong to workgroups g0..g1, this one (me)
 // among them.  Its own sums are still in `acc`; the others' partial tiles
@@ -1690,36 +1734,14 @@ gemm_sk_kernel(KernelArgs p)
             }
         } else {
             const int64_t a0 = (int64_t)tile * iters;
-            const int64_t g0 = ((a0 + 1) * p.sk_grid - 1) / p.sk_total;
-            const int64_t g1 = ((a0 + iters) * p.sk_grid - 1) / p.sk_total;
-            unsigned *count = p.sk_count + g0;
-            const unsigned others = (unsigned)(g1 - g0);
-            // Each contributor counts in once.  If all the others have, this
-            // workgroup is the last: it finishes from its registers without
-            // writing its partial tile, and clears the counter for the next launch.
-            if (threadIdx.x == 0)
-                last_arrival = __hip_atomic_load(count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == others;
-            __syncthreads();
-            // one value for the whole workgroup (read back from LDS): a uniform branch
-            bool last = __builtin_amdgcn_readfirstlane(last_arrival);
-            if (!last) {
+            int64_t g0, g1;
+            sk_owners(p, a0, g0, g1);
+            const bool last = sk_arrive(p, g0, g1, last_arrival, [&] {
                 // the whole BM x BN tile, row-major, into partial slot (L, first or last)
                 void *slot = static_cast<PT *>(p.sk_part) + ((int64_t)L * 2 + (it == beg ? 0 : 1)) * (BM * BN);
                 if (dma) sk_store_partial<D::IL_A, D::IL_B, TM, TN, WTM, WTN, WN, BN>(slot, acc);
                 else     sk_store_partial<R::IL_A, R::IL_B, TM, TN, WTM, WTN, WN, BN>(slot, acc);
-                // The agent-scope stores have reached the point of coherence once
-                // they are acknowledged: every wave waits for its own before the
-                // barrier, so the workgroup counts in only after all of its partial
-                // sums are visible to every XCD.
-                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-                __syncthreads();
-                if (threadIdx.x == 0)
-                    last_arrival = __builtin_amdgcn_atomic_inc32(count, others, __ATOMIC_RELAXED, "agent") == others;
-                __syncthreads();
-                last = __builtin_amdgcn_readfirstlane(last_arrival);
-            } else if (threadIdx.x == 0) {
-                __hip_atomic_store(count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
+            });
             // (the range-checked epilogue for every finished tile: one more
             // instance of the unchecked one ran the 16-bit 4-byte-copy builds
             // out of scalar registers for their copies' buffer resources)

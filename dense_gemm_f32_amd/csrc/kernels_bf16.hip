@@ -30,22 +30,22 @@ const Variant *bf16_variants(int *count)
         // deeper ring hides the loads of a lone workgroup), two of 64 when a CU
         // holds several workgroups
         MGEMM_VARIANT(__bf16, 2, 128, 128, 64, 2, 4, true, "mgemm_bf16_128x128x64_w2x4", {2.35f, 0.00964f, 1.5f, 1.07f},
-                      MGEMM_SK(__bf16, 128, 128, 64, 2, 4, true, 1)),
+                      MGEMM_SK16(__bf16, 128, 128, 64, 2, 4, true, 1)),
         MGEMM_VARIANT_D(__bf16, 2, 128, 128, 64, 2, 4, true, 2, "mgemm_bf16_128x128x64_w2x4_d2", {2.46f, 0.00829f, 1.5f, 1.39f},
-                        MGEMM_SK(__bf16, 128, 128, 64, 2, 4, true, 2)),
+                        MGEMM_SK16(__bf16, 128, 128, 64, 2, 4, true, 2)),
         // rows 4-byte aligned (and K even): 4-byte copies into LDS, every tile
         MGEMM_VARIANT_D(__bf16, 2, 128, 128, 64, 2, 2, false, 4, "mgemm_bf16_128x128x64_w2x2_d4_u", {},
-                        MGEMM_SK(__bf16, 128, 128, 64, 2, 2, false, 4)),
+                        MGEMM_SK16(__bf16, 128, 128, 64, 2, 2, false, 4)),
         MGEMM_VARIANT(__bf16, 2, 128, 128, 64, 2, 2, false, "mgemm_bf16_128x128x64_w2x2_u", {},
-                      MGEMM_SK(__bf16, 128, 128, 64, 2, 2, false, 1)),
+                      MGEMM_SK16(__bf16, 128, 128, 64, 2, 2, false, 1)),
         MGEMM_VARIANT(__bf16, 2, 64, 64, 64, 2, 2, true, "mgemm_bf16_64x64x64_w2x2", {0.44f, 0.00391f, 1.1f, 1.73f},
-                      MGEMM_SK(__bf16, 64, 64, 64, 2, 2, true, 1)),
+                      MGEMM_SK16(__bf16, 64, 64, 64, 2, 2, true, 1)),
         MGEMM_VARIANT_D(__bf16, 2, 64, 64, 64, 2, 2, true, 2, "mgemm_bf16_64x64x64_w2x2_d2", {0.45f, 0.00335f, 1.1f, 2.32f},
-                        MGEMM_SK(__bf16, 64, 64, 64, 2, 2, true, 2)),
+                        MGEMM_SK16(__bf16, 64, 64, 64, 2, 2, true, 2)),
         MGEMM_VARIANT_D(__bf16, 2, 64, 64, 64, 2, 2, false, 4, "mgemm_bf16_64x64x64_w2x2_d4_u", {},
-                        MGEMM_SK(__bf16, 64, 64, 64, 2, 2, false, 4)),
+                        MGEMM_SK16(__bf16, 64, 64, 64, 2, 2, false, 4)),
         MGEMM_VARIANT(__bf16, 2, 64, 64, 64, 2, 2, false, "mgemm_bf16_64x64x64_w2x2_u", {},
-                      MGEMM_SK(__bf16, 64, 64, 64, 2, 2, false, 1)),
+                      MGEMM_SK16(__bf16, 64, 64, 64, 2, 2, false, 1)),
     };
     *count = sizeof(table) / sizeof(table[0]);
     return table;

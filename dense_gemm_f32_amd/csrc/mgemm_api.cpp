@@ -185,6 +185,7 @@ mgemm_status validate_and_plan(int dtype, int c_dtype, int transA, int transB, i
     // (and a build of this transpose and C type: the 64x64 int8 tiles take
     // A K-contiguous and B K-contiguous only)
     const bool wide_c = c_dtype == MGEMM_F32 || c_dtype == MGEMM_I32 || c_dtype == MGEMM_F64;
+    auto sk_launcher = [&](const Variant &v) { return (wide_c ? v.sk : v.sk16)[transA][transB]; };
     auto offsets_ok = [&](const Variant &v) {
         return (wide_c ? v.fn : v.fn16)[transA][transB] != nullptr &&
                (!dw_copies(v) || (a.fast_ok && dw_rows)) &&
@@ -198,7 +199,7 @@ mgemm_status validate_and_plan(int dtype, int c_dtype, int transA, int transB, i
     int pick = -1;
     if (forced >= 0) {
         const Variant *v = variant_by_id(forced);
-        if (v && (!v->vec || vec_ok) && offsets_ok(*v) && (!need_sk || v->sk[transA][transB]))
+        if (v && (!v->vec || vec_ok) && offsets_ok(*v) && (!need_sk || sk_launcher(*v)))
             pick = forced - t.first_id;
         // a forced variant the operands do not allow falls back to the automatic choice
     }
@@ -206,7 +207,7 @@ mgemm_status validate_and_plan(int dtype, int c_dtype, int transA, int transB, i
         return ((M + v.bm - 1) / v.bm) * ((N + v.bn - 1) / v.bn) * batch;
     };
     // need_sk: only builds with a stream-K launch for this transpose
-    auto has_sk = [&](const Variant &v) { return !need_sk || v.sk[transA][transB] != nullptr; };
+    auto has_sk = [&](const Variant &v) { return !need_sk || sk_launcher(v) != nullptr; };
     auto eligible = [&](const Variant &v) { return v.vec == vec_ok && offsets_ok(v) && has_sk(v); };
     if (pick < 0 && !need_sk && (dtype == MGEMM_F16 || dtype == MGEMM_BF16) && K <= 128) {
         // A shallow K (the whole product is a couple of slabs, e.g. attention
@@ -483,7 +484,9 @@ mgemm_status make_streamk_plan(int dtype, int c_dtype, int transA, int transB, i
 {
     sp->tiles = 0;
     sp->workspace_bytes = 0;
-    if (workgroups < 0 || dtype == MGEMM_F64 || c_dtype != partial_dtype(dtype)) return MGEMM_INVALID_ARG;
+    // C of the partial sums' type, or (16-bit inputs) of the inputs' own type
+    const bool c16 = (dtype == MGEMM_F16 || dtype == MGEMM_BF16) && c_dtype == dtype;
+    if (workgroups < 0 || (c_dtype != partial_dtype(dtype) && !c16)) return MGEMM_INVALID_ARG;
     mgemm_status st = validate_and_plan(dtype, c_dtype, transA, transB, M, N, K, alpha, A, lda, 0, B, ldb,
                                         0, beta, C, ldc, 0, 1, &sp->plan, -1, true);
     if (st != MGEMM_OK || sp->plan.kind != Plan::GEMM) return st;
@@ -527,7 +530,8 @@ mgemm_status run_streamk(int dtype, int c_dtype, int transA, int transB, int64_t
     }
     if (workspace == nullptr || !aligned(workspace, 16) || workspace_bytes < sp.workspace_bytes)
         return MGEMM_INVALID_ARG;
-    const LaunchFn fn = sp.plan.var->sk[transA][transB];
+    const bool wide_c = c_dtype == MGEMM_F32 || c_dtype == MGEMM_I32 || c_dtype == MGEMM_F64;
+    const LaunchFn fn = (wide_c ? sp.plan.var->sk : sp.plan.var->sk16)[transA][transB];
     if (fn == nullptr) return MGEMM_INVALID_ARG;
     err = fn(sp.plan.args, (unsigned)sp.plan.grid, stream);
     return err == hipSuccess ? MGEMM_OK : MGEMM_HIP_ERROR;
@@ -764,7 +768,8 @@ mgemm_status gemm_streamk(mgemm_dtype in_dtype, mgemm_dtype c_dtype, mgemm_op tr
                           void *C, int64_t ldc, int64_t workgroups, void *workspace,
                           int64_t workspace_bytes, hipStream_t stream)
 {
-    if ((double)(float)alpha != alpha || (double)(float)beta != beta) return MGEMM_INVALID_ARG;
+    if (in_dtype != MGEMM_F64 && ((double)(float)alpha != alpha || (double)(float)beta != beta))
+        return MGEMM_INVALID_ARG;
     return run_streamk(in_dtype, c_dtype, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
                        workgroups, workspace, workspace_bytes, stream);
 }

@@ -47,6 +47,7 @@ struct Variant {
     LaunchFn fn16[2][2];  // [transA][transB], C in the inputs' 16-bit type (16-bit tables only)
     Cost cost;            // zero: no estimate
     LaunchFn sk[2][2];    // stream-K launch of the same tile, fp32 C (int32 for int8); null: none
+    LaunchFn sk16[2][2];  // stream-K launch with C in the inputs' 16-bit type (16-bit tables only)
 };
 
 template <typename T, int BM, int BN, int BK, int WM, int WN, bool TA, bool TB, bool V, int D, typename CT>
@@ -85,6 +86,22 @@ hipError_t launch_gemm_f64(const KernelArgs &a, unsigned grid, hipStream_t s)
                            dim3(grid), dim3(WM * WN * 64), args, 0, s);
 }
 
+template <int BM, int BN, int BK, int WM, int WN, bool TA, bool TB, bool V>
+hipError_t launch_gemm_f64_sk(const KernelArgs &a, unsigned grid, hipStream_t s)
+{
+    KernelArgs copy = a;
+    void *args[] = {&copy};
+    return hipLaunchKernel(reinterpret_cast<const void *>(&gemm_f64_sk_kernel<BM, BN, BK, WM, WN, TA, TB, V>),
+                           dim3(grid), dim3(WM * WN * 64), args, 0, s);
+}
+
+// stream-K launchers of an fp64 build (the trailing argument after its Cost)
+#define MGEMM_SK_F64(BM, BN, BK, WM, WN, V)                                                  \
+    {{launch_gemm_f64_sk<BM, BN, BK, WM, WN, false, false, V>,                               \
+      launch_gemm_f64_sk<BM, BN, BK, WM, WN, false, true, V>},                               \
+     {launch_gemm_f64_sk<BM, BN, BK, WM, WN, true, false, V>,                                \
+      launch_gemm_f64_sk<BM, BN, BK, WM, WN, true, true, V>}}
+
 // fp64 inputs: double C
 #define MGEMM_VARIANT_F64(BM, BN, BK, WM, WN, V, NAME, ...)                                  \
     {5, BM, BN, BK, WM, WN, V, 1, NAME,                                                      \
@@ -102,12 +119,17 @@ hipError_t launch_gemm_f64(const KernelArgs &a, unsigned grid, hipStream_t s)
 
 // The trailing argument of each macro is the build's Cost, {t0, tk, reg, solo}
 // ({}: no estimate), optionally followed by its stream-K launchers
-// (MGEMM_SK or MGEMM_SK_I8; omitted: none).
-#define MGEMM_SK(T, BM, BN, BK, WM, WN, V, D)                                                \
-    {{launch_gemm_sk<T, BM, BN, BK, WM, WN, false, false, V, D, float>,                      \
-      launch_gemm_sk<T, BM, BN, BK, WM, WN, false, true, V, D, float>},                      \
-     {launch_gemm_sk<T, BM, BN, BK, WM, WN, true, false, V, D, float>,                       \
-      launch_gemm_sk<T, BM, BN, BK, WM, WN, true, true, V, D, float>}}
+// (MGEMM_SK, MGEMM_SK16 for both C types of 16-bit inputs, MGEMM_SK_I8 /
+// MGEMM_SK_I8_ALL, MGEMM_SK_F64; omitted: none).
+#define MGEMM_SK_C(T, BM, BN, BK, WM, WN, V, D, CT)                                          \
+    {{launch_gemm_sk<T, BM, BN, BK, WM, WN, false, false, V, D, CT>,                         \
+      launch_gemm_sk<T, BM, BN, BK, WM, WN, false, true, V, D, CT>},                         \
+     {launch_gemm_sk<T, BM, BN, BK, WM, WN, true, false, V, D, CT>,                          \
+      launch_gemm_sk<T, BM, BN, BK, WM, WN, true, true, V, D, CT>}}
+#define MGEMM_SK(T, BM, BN, BK, WM, WN, V, D) MGEMM_SK_C(T, BM, BN, BK, WM, WN, V, D, float)
+// 16-bit inputs: stream-K with fp32 C, then with C in the inputs' own type
+#define MGEMM_SK16(T, BM, BN, BK, WM, WN, V, D)                                              \
+    MGEMM_SK_C(T, BM, BN, BK, WM, WN, V, D, float), MGEMM_SK_C(T, BM, BN, BK, WM, WN, V, D, T)
 #define MGEMM_SK_I8(BM, BN, BK, WM, WN, V, D)                                                 \
     {{nullptr, launch_gemm_sk<int8_t, BM, BN, BK, WM, WN, false, true, V, D, int32_t>},       \
      {nullptr, nullptr}}

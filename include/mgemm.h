@@ -391,11 +391,14 @@ mgemm_status mgemm_splitk_plan(mgemm_dtype in_dtype, mgemm_op transA, mgemm_op t
  * (1000x1027x999 fp32: 272 tiles of 64x64); on grids that fill the device
  * the one-pass entry points are faster, and the automatic plan of
  * gemm_splitk does not choose it.
- *   in_dtype  MGEMM_F32, MGEMM_F16, MGEMM_BF16 (then c_dtype MGEMM_F32) or
- *          MGEMM_I8 (c_dtype MGEMM_I32); other pairs and MGEMM_F64 give
- *          MGEMM_INVALID_ARG.
- *   alpha, beta  double, exactly representable as float (int8: integral,
- *          as gemm_strided_batched_ex).
+ *   in_dtype  MGEMM_F32 (c_dtype MGEMM_F32), MGEMM_F16 or MGEMM_BF16
+ *          (c_dtype MGEMM_F32 or the inputs' own type: the partial sums stay
+ *          fp32 and C is rounded once), MGEMM_I8 (c_dtype MGEMM_I32) or
+ *          MGEMM_F64 (c_dtype MGEMM_F64, fp64 partial sums); other pairs
+ *          give MGEMM_INVALID_ARG.
+ *   alpha, beta  double; for every in_dtype but MGEMM_F64 exactly
+ *          representable as float (int8: integral, as
+ *          gemm_strided_batched_ex).
  *   workgroups  n > 0: n workgroups, capped at MGEMM_STREAMK_MAX_WORKGROUPS
  *          and at the number of (tile, iteration) pairs; 0: 512 (two per
  *          CU), capped likewise.
@@ -409,13 +412,13 @@ mgemm_status mgemm_splitk_plan(mgemm_dtype in_dtype, mgemm_op transA, mgemm_op t
  *          kernel ends, so a workspace is then reusable by calls of any
  *          size without clearing.  Non-zero counters give wrong C for split
  *          tiles (never a hang).  The rest holds two partial tiles per
- *          workgroup, fp32 (int32 for int8), overwritten.  Calls that share
+ *          workgroup, fp32 (int32 for int8, fp64 for fp64), overwritten.  Calls that share
  *          a workspace must be ordered on one stream.
  * A and B are read, C is read only when beta != 0; layouts, leading
  * dimensions and quick returns are those of gemm_strided_batched_ex with
- * batch 1.  Results differ from the one-pass kernels only by fp32 summation
- * order where a tile is split, and are identical for integer-valued inputs
- * whose sums are exact.
+ * batch 1.  Results differ from the one-pass kernels only by the summation
+ * order (fp32; fp64 for fp64) where a tile is split, and are identical for
+ * integer-valued inputs whose sums are exact.
  * Errors: as gemm_strided_batched_ex, plus MGEMM_INVALID_ARG for
  * workgroups < 0 or a missing, misaligned or short workspace; nothing is
  * launched then.

@@ -425,12 +425,15 @@ def test_streamk_rules_without_a_gpu():
     assert need == mg.STREAMK_COUNTER_BYTES + 32 * 2 * 64 * 64 * 4   # 1 tile x 32 iterations: 32 workgroups
     assert call(wbytes=need - 1) == 1
     assert call(alpha=1.0 + 2 ** -40) == 1                     # not a float
-    assert call(in_dt=1, c_dt=1) == 1                          # fp32 C only for 16-bit inputs
+    assert call(in_dt=1, c_dt=2) == 1                          # fp32 C or the inputs' own type
+    assert call(in_dt=0, c_dt=1) == 1                          # fp32 inputs: fp32 C only
     assert call(in_dt=3, c_dt=4, tB=1, alpha=1.5) == 1         # int8: integral alpha
-    assert call(in_dt=5, c_dt=5) == 1                          # no fp64 stream-K
+    assert call(in_dt=5, c_dt=0) == 1                          # fp64 inputs: double C only
+    assert call(in_dt=5, c_dt=5, ws=ALIGNED + 8) == 1          # fp64: the same workspace rules
     # nothing to do: OK without a workspace
-    for in_dt, c_dt, tB in ((0, 0, 0), (2, 0, 0), (3, 4, 1)):
+    for in_dt, c_dt, tB in ((0, 0, 0), (2, 0, 0), (2, 2, 0), (1, 1, 0), (3, 4, 1), (5, 5, 0)):
         assert call(in_dt, c_dt, M=0, ws=None, wbytes=0, tB=tB) == 0
+    assert call(5, 5, M=0, alpha=1.0 + 2 ** -40, ws=None, wbytes=0) == 0   # fp64 takes doubles
 
 
 def test_splitk_rules_without_a_gpu():
@@ -498,8 +501,13 @@ def test_streamk_plans():
     for M, K in ((0, 64), (64, 0)):
         z = mg.streamk_plan("f32", M, 64, K, lda=max(K, 1))
         assert z["workspace_bytes"] == 0 and z["variant"]["id"] == -1
-    with pytest.raises(mg.MgemmError):
-        mg.streamk_plan("f64", 100, 100, 100)
+    # fp64: 16-deep iterations and double partial tiles; 16-byte rows take the vector builds
+    f64 = mg.streamk_plan("f64", 1000, 1027, 999, lda=1000, ldb=1028)
+    assert f64["k_per_iteration"] == 16 and f64["iterations"] == 63
+    assert not f64["variant"]["name"].endswith("_u")
+    assert f64["workspace_bytes"] == (mg.STREAMK_COUNTER_BYTES +
+                                      512 * 2 * f64["variant"]["block_m"] * f64["variant"]["block_n"] * 8)
+    assert mg.streamk_plan("f64", 1000, 1027, 999, lda=999, ldb=1027)["variant"]["name"].endswith("_u")
     with pytest.raises(mg.MgemmError):
         mg.streamk_plan("f32", 100, 100, 100, -1)
     # int8 with an MN-contiguous operand: the 128x128 tiles (transposing LDS reads)

@@ -596,13 +596,16 @@ def test_splitk_auto_on_a_deep_k_shape():
     full_check(p, exact=True, what="256x256x8192 automatic split-K")
 
 
-@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "i8"])
-def test_streamk_exact(dtype):
+@pytest.mark.parametrize("dtype,c_dtype", [("f32", "f32"), ("f16", "f32"), ("bf16", "f32"), ("i8", "i32"),
+                                           ("f64", "f64"), ("f16", "f16"), ("bf16", "bf16")])
+def test_streamk_exact(dtype, c_dtype):
     # integer-valued inputs: bit-exact however the tiles are split between
     # workgroups; shapes with edge tiles and K tails, the 4-byte-copy builds
     # (odd leading dimensions), one workgroup, and one workgroup per
-    # (tile, iteration) pair
+    # (tile, iteration) pair.  A 16-bit C holds the exact sum rounded once
+    # (the data stay small enough for binary16's range).
     i8 = dtype == "i8"
+    lo, hi = (-128, 127) if i8 else (-4, 4) if c_dtype in ("f16", "bf16") else (-20, 20)
     trans = [(False, False), (False, True), (True, False), (True, True)]
     cases = [((1000, 1027, 999), 0), ((1000, 1027, 999), 37), ((150, 133, 700), 0),
              ((70, 300, 1111), 5), ((200, 190, 2050), 1), ((64, 64, 300), None)]
@@ -613,21 +616,80 @@ def test_streamk_exact(dtype):
                 wgs = plan["tiles"] * plan["iterations"]
             ab = (3.0, -2.0) if i8 else (1.5, 0.5)
             p = wl.Problem(dtype, M, N, K, transA=tA, transB=tB, alpha=ab[0], beta=ab[1], dist="int",
-                           int_lo=-128 if i8 else -20, int_hi=127 if i8 else 20, c_dist="int",
-                           c_dtype="i32" if i8 else "f32", seed=131 + n, streamk=wgs)
+                           int_lo=lo, int_hi=hi, c_dist="int", c_dtype=c_dtype, seed=131 + n,
+                           streamk=wgs)
             plan = mg.streamk_plan(dtype, M, N, K, wgs, transA=int(tA), transB=int(tB), lda=p.lda,
                                    ldb=p.ldb)
-            full_check(p, exact=True, what=f"stream-K {dtype} tA={int(tA)} tB={int(tB)} "
+            full_check(p, exact=True, what=f"stream-K {dtype}->{c_dtype} tA={int(tA)} tB={int(tB)} "
                        f"{plan['variant']['name']} x{plan['workgroups']} over {plan['tiles']} tiles "
                        f"of {plan['iterations']} iterations")
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_streamk_float_inputs_within_tolerance(dtype):
+SK_ES = {"f32": 4, "f16": 2, "bf16": 2, "i8": 1, "f64": 8}
+SK_GRANULE = {"f32": 32, "f16": 64, "bf16": 64, "i8": 128, "f64": 16}
+
+
+@pytest.mark.parametrize("dtype,c_dtype", [("f32", "f32"), ("f16", "f32"), ("f16", "f16"), ("bf16", "f32"),
+                                           ("bf16", "bf16"), ("i8", "i32"), ("f64", "f64")])
+def test_streamk_every_build_exact(dtype, c_dtype):
+    # each build's stream-K launch, forced, on every transpose it has: edge tiles, a last
+    # iteration shorter than the granule (a whole number of 16-byte chunks on the
+    # aligned builds, so that the DMA ring takes it), 37 workgroups over a few
+    # dozen (tile, iteration) pairs, so that most tiles are split
+    es, unit = SK_ES[dtype], SK_GRANULE[dtype]
+    code = {"f32": 0, "f16": 1, "bf16": 2, "i8": 3, "f64": 5}[dtype]
+    i8 = dtype == "i8"
+    seen = set()
+    try:
+        for v in mg.variants():
+            if v["dtype"] != code or v["pipe"] == 6:
+                continue
+            mg.force_variant(dtype, v["id"])
+            aligned = not v["name"].endswith("_u")
+            narrow_dw = v["pipe"] == 4 and es < 4
+            M, N = 2 * v["block_m"] + 17, 2 * v["block_n"] + 9
+            K = 4 * unit + (3 * 16 // es if aligned else 5 if not narrow_dw else 4 // es * 3)
+
+            def ld(cols):
+                if aligned:
+                    return -(-cols // (16 // es)) * (16 // es)
+                if narrow_dw:   # whole 4-byte pieces, not whole 16-byte chunks
+                    piece = 4 // es
+                    x = -(-cols // piece) * piece
+                    return x + piece if (x * es) % 16 == 0 else x
+                return cols + 1 if cols % 2 == 0 else cols
+
+            hits = 0
+            for n, (tA, tB) in enumerate(itertools.product((False, True), repeat=2)):
+                lda, ldb = ld(M if tA else K), ld(K if tB else N)
+                plan = mg.streamk_plan(dtype, M, N, K, 37, transA=int(tA), transB=int(tB), lda=lda, ldb=ldb)
+                if plan["variant"]["name"] != v["name"]:
+                    continue   # no stream-K launch of this build for this transpose
+                ab = (3.0, -2.0) if i8 else (1.5, 0.5)
+                lo, hi = (-128, 127) if i8 else (-4, 4)
+                p = wl.Problem(dtype, M, N, K, transA=tA, transB=tB, lda=lda, ldb=ldb, alpha=ab[0],
+                               beta=ab[1], dist="int", int_lo=lo, int_hi=hi, c_dist="int", c_dtype=c_dtype,
+                               seed=150 + n, streamk=37)
+                full_check(p, exact=True, what=f"stream-K forced {v['name']} ({c_dtype} C) tA={int(tA)} "
+                           f"tB={int(tB)} over {plan['tiles']} tiles of {plan['iterations']} iterations")
+                hits += 1
+            if hits:
+                seen.add(v["name"])
+    finally:
+        mg.force_variant(dtype, None)
+    log(f"  stream-K builds run: {sorted(seen)}")
+    # every 128x128 and 64x64 build of the 32-bit-accumulating types has a launch; fp64 all but 2x4 waves
+    want = {"f32": 6, "f16": 8, "bf16": 8, "i8": 8, "f64": 5}[dtype]
+    assert len(seen) == want, sorted(seen)
+
+
+@pytest.mark.parametrize("dtype,c_dtype", [("f32", "f32"), ("bf16", "f32"), ("bf16", "bf16"), ("f16", "f16"),
+                                           ("f64", "f64")])
+def test_streamk_float_inputs_within_tolerance(dtype, c_dtype):
     p = wl.Problem(dtype, 1000, 1027, 999, alpha=0.75, beta=-1.25,
-                   dist="normal" if dtype == "bf16" else "uniform", c_dist="uniform", seed=141,
-                   streamk=0)
-    full_check(p, what=f"stream-K {dtype} 1000x1027x999")
+                   dist="normal" if dtype in ("bf16", "f16") else "uniform", c_dist="uniform",
+                   c_dtype=c_dtype, seed=141, streamk=0)
+    full_check(p, what=f"stream-K {dtype}->{c_dtype} 1000x1027x999")
 
 
 def test_streamk_quick_returns_and_shared_workspace():

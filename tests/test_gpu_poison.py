@@ -16,7 +16,8 @@ covers every build of every type:
 - the SPREAD order of the 256x256 16-bit builds (MN-contiguous B, that is
   transB = N);
 - int8 (transposing 8-bit reads for MN-contiguous operands) and fp64;
-- split-K chunks and stream-K segments, whose rings restart per segment.
+- split-K chunks and stream-K segments, whose rings restart per segment
+  (fp32, bf16 with fp32 and bf16 C, int8 and fp64).
 """
 import itertools
 
@@ -67,12 +68,12 @@ def builds(dtype):
     return [v for v in mg.variants() if v["dtype"] == CODE[dtype] and v["pipe"] != 6]
 
 
-def int_problem(dtype, M, N, K, tA, tB, lda, ldb, seed):
+def int_problem(dtype, M, N, K, tA, tB, lda, ldb, seed, c_dtype="f32"):
     if dtype == "i8":
         return wl.Problem("i8", M, N, K, transA=tA, transB=tB, lda=lda, ldb=ldb, alpha=3.0, beta=-2.0,
                           dist="int", int_lo=-128, int_hi=127, c_dist="int", c_dtype="i32", seed=seed)
     return wl.Problem(dtype, M, N, K, transA=tA, transB=tB, lda=lda, ldb=ldb, alpha=1.0, beta=-1.0,
-                      dist="int", int_lo=-8, int_hi=8, c_dist="int", seed=seed)
+                      dist="int", int_lo=-8, int_hi=8, c_dist="int", c_dtype=c_dtype, seed=seed)
 
 
 def lds(dtype, cols, aligned, narrow_dw):
@@ -124,11 +125,13 @@ def test_every_build_under_lds_poison(dtype):
 
 
 # (K, lda, ldb) per type: fp32 with odd rows (the 4-byte-copy build), bf16 with
-# 16-byte rows (the DMA ring), int8 N x N with 16-byte rows
-STREAM_SHAPES = {"f32": (999, 999, 1027), "bf16": (1000, 1000, 1032), "i8": (1024, 1024, 1040)}
+# 16-byte rows (the DMA ring), int8 N x N with 16-byte rows, fp64 with 16-byte
+# rows and a K tail
+STREAM_SHAPES = {"f32": (999, 999, 1027), "bf16": (1000, 1000, 1032), "i8": (1024, 1024, 1040),
+                 "f64": (999, 1000, 1028)}
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16", "i8"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "i8", "f64"])
 def test_streamk_and_splitk_under_lds_poison(dtype):
     tB = False   # B MN-contiguous: int8 through its transposing reads
     K, lda, ldb = STREAM_SHAPES[dtype]
@@ -136,6 +139,10 @@ def test_streamk_and_splitk_under_lds_poison(dtype):
         p = int_problem(dtype, 1000, 1027, K, False, tB, lda, ldb, seed=260 + wgs)
         p.streamk = wgs
         exact(p, f"stream-K x{wgs or 512}")
+    if dtype == "bf16":   # C in the inputs' own type
+        p = int_problem(dtype, 1000, 1027, K, False, tB, lda, ldb, seed=265, c_dtype="bf16")
+        p.streamk = 0
+        exact(p, "stream-K, bf16 C")
     K3 = 3 * K
     p = int_problem(dtype, 300, 260, K3, False, tB, K3, K3 if tB else (260 if dtype != "bf16" else 264),
                     seed=270)
