@@ -800,12 +800,16 @@ struct RegPath {
 //   3  one stage of BK = BKR, for K <= BKR only (one slab, e.g. attention
 //      scores over a 64-wide head): half the LDS, so that two workgroups
 //      share a CU and one's C stores overlap the other's loads;
-//   4  4-byte copies, BK = BKR, NS = 2, for every tile of a problem whose
-//      rows are 4-byte aligned (and, for 8/16-bit elements, whose K is a
-//      multiple of the 4-byte piece): each lane copies one piece, and lanes
-//      whose piece lies past the matrix (row, column or k) are masked to
-//      zero by the buffer range check, so edges and leading dimensions that
-//      are no multiple of 16 bytes need no register path.
+//   4  for every tile of a problem whose rows are 4-byte aligned (and, for
+//      8/16-bit elements, whose K is a multiple of the 4-byte piece), BK =
+//      BKR, NS = 2.  Whole slabs with operand rows after them are copied 16
+//      bytes per lane at 4-byte aligned addresses (a multi-dword access
+//      needs only dword alignment; measured as fast as on 16-byte aligned
+//      rows).  The last slab of a tile takes 4-byte copies: each lane copies
+//      one piece, and lanes whose piece lies past the matrix (row, column or
+//      k) are masked to zero by the buffer range check, so edges, K tails and
+//      leading dimensions that are no multiple of 16 bytes need no register
+//      path.
 //
 // LDS layouts (bank-conflict free for every access of this path):
 //   KC  operand K-contiguous in memory: rows of BK elements (RB = 64 or 128
@@ -832,7 +836,7 @@ struct DmaPath {
     static constexpr bool F32 = (ES == 4);
     static constexpr int WTM = BM / WM, WTN = BN / WN;
     static constexpr int TM = WTM / 32, TN = WTN / 32;
-    static constexpr bool DW = PIPE == 4;  // 4-byte copies, every tile
+    static constexpr bool DW = PIPE == 4;  // every tile; 4-byte copies on the last slab
     static constexpr bool ONE = PIPE == 3;  // one stage, one slab (K <= BKR)
     static constexpr int BK = PIPE == 2 || DW || ONE ? BKR : BKR / 2;
     static constexpr int NS = PIPE == 1 ? 4 : ONE ? 1 : 2;
@@ -863,7 +867,15 @@ struct DmaPath {
     static constexpr int CPY = DW ? 256 : 1024;  // LDS bytes one copy instruction fills
     static_assert(A_BYTES % (CPY * NW) == 0 && B_BYTES % (CPY * NW) == 0, "DMA split");
     static constexpr int A_IPW = A_BYTES / CPY / NW, B_IPW = B_BYTES / CPY / NW;
-    static constexpr int LPS = A_IPW + B_IPW;  // DMA loads per slab per thread
+    // 4-byte-copy builds copy every slab but a tile's last with 16-byte
+    // copies (issue()); those counts per wave
+    static constexpr int A_IPW16 = A_BYTES / 1024 / NW, B_IPW16 = B_BYTES / 1024 / NW;
+    static_assert(!DW || (A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0), "16-byte DMA split");
+    // DMA loads per slab per thread, as the waits count them: the 16-byte
+    // count in the 4-byte-copy builds, whose only slab of 4-byte copies is
+    // the last (a wait that allows fewer loads in flight than there are
+    // waits longer, never too short)
+    static constexpr int LPS = DW ? A_IPW16 + B_IPW16 : A_IPW + B_IPW;
     static_assert((NS - 1) * LPS <= 63, "vmcnt range");
     static_assert(A_KC || A_ROWB >= 128, "MC rows of at least 128 bytes");
     static_assert(B_KC || B_ROWB >= 128, "MC rows of at least 128 bytes");
@@ -910,6 +922,8 @@ struct DmaPath {
     // chunk that straddles the m/n edge is read whole: it is 16-byte aligned
     // and holds a valid element, so it lies inside a mapped page, and its
     // values past the edge feed only rows or columns of C that are not stored.
+    // (The 4-byte-copy builds also use these copies on rows that are only
+    // 4-byte aligned, on whole slabs that end before row K-1; see issue().)
     // CHECK false (interior tiles with whole slabs): no masking, and the
     // offsets do not depend on the slab.
     template <bool KC, int IL, int ROWB, int IPW, bool CHECK>
@@ -1089,9 +1103,11 @@ struct DmaPath {
 
     // CHECK: mask copies against the matrix edges and K (edge tiles, a K
     // tail); without it the tile must be interior with whole slabs.
+    // k_more: the operands have rows past this K (a split-K chunk or
+    // stream-K segment that ends before the end of K)
     template <bool CHECK>
     __device__ __forceinline__ static void run(const KernelArgs &p, char *smem, int bidx, int m0, int n0,
-                                               f32x16 (&acc)[TM][TN])
+                                               f32x16 (&acc)[TM][TN], bool k_more = false)
     {
         const int tid = threadIdx.x;
         const int lane = tid & 63;
@@ -1118,6 +1134,9 @@ struct DmaPath {
 
         auto stage = [&](int s) { return smem + (s % NS) * STAGE; };
         const int mrem = p.M - m0, nrem = p.N - n0;
+        // 4-byte-copy builds: rows of at least 16 bytes take 16-byte copies
+        // on every slab but the last
+        const bool wide = DW && p.M * ES >= 16 && p.N * ES >= 16;
         // 16-byte copy q (of LPS: A's first, then B's) of slab s into stage
         // st, the same copies as issue(s) makes
         auto copy_of = [&](int s, char *st, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb, int q) {
@@ -1135,14 +1154,33 @@ struct DmaPath {
             const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bp + (int64_t)s * b_kstep);
             if constexpr (DW) {
                 const int krem = p.K - s * BK;
+                if (wide && (krem > BK || (krem == BK && k_more))) {
+                    // 16-byte copies of rows that may be only 4-byte aligned
+                    // (a multi-dword access needs dword alignment alone): the
+                    // slab is whole, so no KC chunk straddles the end of K,
+                    // and a row of the operand follows its last row, so an MC
+                    // chunk that straddles the m/n edge reads at most 16-ES
+                    // bytes past its row's last element, which lie in a later
+                    // row (wide: at least 16 bytes per row)
 #pragma unroll
-                for (int q = 0; q < A_IPW; ++q)
-                    dma_dw<A_KC, IL_A, A_ROWB, A_IPW>(ra, st, lda_b, w, lane, q, A_KC ? mrem : krem,
-                                                      A_KC ? krem : mrem);
+                    for (int q = 0; q < A_IPW16; ++q)
+                        dma_one<A_KC, IL_A, A_ROWB, A_IPW16, true>(ra, st, lda_b, w, lane, q, A_KC ? mrem : krem,
+                                                                   A_KC ? krem : mrem);
 #pragma unroll
-                for (int q = 0; q < B_IPW; ++q)
-                    dma_dw<B_KC, IL_B, B_ROWB, B_IPW>(rb, st + A_BYTES, ldb_b, w, lane, q,
-                                                      B_KC ? nrem : krem, B_KC ? krem : nrem);
+                    for (int q = 0; q < B_IPW16; ++q)
+                        dma_one<B_KC, IL_B, B_ROWB, B_IPW16, true>(rb, st + A_BYTES, ldb_b, w, lane, q,
+                                                                   B_KC ? nrem : krem, B_KC ? krem : nrem);
+                } else {
+                    // the last slab: 4-byte pieces, each checked against K and the edges
+#pragma unroll
+                    for (int q = 0; q < A_IPW; ++q)
+                        dma_dw<A_KC, IL_A, A_ROWB, A_IPW>(ra, st, lda_b, w, lane, q, A_KC ? mrem : krem,
+                                                          A_KC ? krem : mrem);
+#pragma unroll
+                    for (int q = 0; q < B_IPW; ++q)
+                        dma_dw<B_KC, IL_B, B_ROWB, B_IPW>(rb, st + A_BYTES, ldb_b, w, lane, q,
+                                                          B_KC ? nrem : krem, B_KC ? krem : nrem);
+                }
             } else {
                 // CHECK is fixed for the whole tile: a branch between checked
                 // and unchecked copies inside one loop cost the LDS address
@@ -1463,7 +1501,8 @@ gemm_kernel(KernelArgs p)
             if (full && pk.K == D::BK) D::template run<false>(pk, smem, bidx, m0, n0, acc);
             else                       D::template run<true>(pk, smem, bidx, m0, n0, acc);
         } else {
-            D::template run<true>(pk, smem, bidx, m0, n0, acc);
+            // a split-K chunk before the last has the next chunk's rows after it
+            D::template run<true>(pk, smem, bidx, m0, n0, acc, p.tail_batch >= 0 && bidx != p.tail_batch);
         }
         if (full)
             epilogue<false, D::IL_A, D::IL_B, TM, TN, WTM, WTN, WN, CT>(pk, bidx, m0, n0, acc);
@@ -1712,7 +1751,7 @@ gemm_sk_kernel(KernelArgs p)
         const bool full = m0 + BM <= p.M && n0 + BN <= p.N;
         bool dma = ALL_DMA;
         if constexpr (ALL_DMA) {
-            D::template run<true>(pk, smem, bidx, m0, n0, acc);
+            D::template run<true>(pk, smem, bidx, m0, n0, acc, k1 < iters);
         } else {
             if constexpr (VECOK) {
                 if (pk.fast_ok && pk.K % D::CH == 0) {

@@ -9,9 +9,14 @@ const Variant *f32_variants(int *count)
     // per unit of K, register-path factor, one-round factor); a build without
     // an estimate runs only when forced or when no estimated build fits.
     // Rounds: 256x256 0.234 us per K (0.91 of the matrix peak per CU),
-    // 128x128 0.0605 (0.88), 64x64 two-stage 0.0166 (0.80), the 4-byte-copy
-    // builds 0.0658 and 0.0185.  The 64x64 tiles lose per flop but win where
-    // the larger tiles leave a last round mostly empty (4608^3: 324 tiles of
+    // 128x128 0.0605 (0.88), 64x64 two-stage 0.0166 (0.80).  The 4-byte-copy
+    // builds copy all but a tile's last slab 16 bytes at a time: on the same
+    // box their rate per K matched their aligned siblings' within 2% (odd
+    // leading dimensions, 1024^2 to 6144^2, K 256 to 4096), with 0.7 (64x64)
+    // and 1.4 us (128x128) more per round; their estimates are the
+    // siblings' with that added (with 4-byte copies throughout they were
+    // 0.0658 and 0.0185).  The 64x64 tiles lose per flop but win where the
+    // larger tiles leave a last round mostly empty (4608^3: 324 tiles of
     // 256x256 are two rounds, 5184 of 64x64 twenty-one).  The 64x64 two-stage
     // build's register factor is its one-round figure (1000^3: 39 us against
     // 26 us for 1024^3 on the DMA path); over several rounds it measured 1.2
@@ -22,7 +27,7 @@ const Variant *f32_variants(int *count)
         MGEMM_VARIANT_F32(128, 128, 32, 2, 2, true, "mgemm_f32_128x128x32_w2x2", {6.6f, 0.0605f, 1.15f, 1.25f},
                           MGEMM_SK(float, 128, 128, 32, 2, 2, true, 1)),
         MGEMM_VARIANT_F32_D(128, 128, 32, 2, 2, false, 4, "mgemm_f32_128x128x32_w2x2_d4_u",
-                            {9.9f, 0.0658f, 1.0f, 1.25f}, MGEMM_SK(float, 128, 128, 32, 2, 2, false, 4)),
+                            {8.0f, 0.0606f, 1.0f, 1.2f}, MGEMM_SK(float, 128, 128, 32, 2, 2, false, 4)),
         MGEMM_VARIANT_F32(128, 128, 32, 2, 2, false, "mgemm_f32_128x128x32_w2x2_u", {},
                           MGEMM_SK(float, 128, 128, 32, 2, 2, false, 1)),
         // 64x64: two stages of 32 (one barrier per 16 MFMAs) measured 9-14%
@@ -34,7 +39,7 @@ const Variant *f32_variants(int *count)
         // 49.0 against 50.6 us, stream-K 36.4 against 37.8, split-K 44.2
         // against 39.9; not kept)
         MGEMM_VARIANT_F32_D(64, 64, 32, 2, 2, false, 4, "mgemm_f32_64x64x32_w2x2_d4_u",
-                            {2.9f, 0.0185f, 1.0f, 1.6f}, MGEMM_SK(float, 64, 64, 32, 2, 2, false, 4)),
+                            {2.8f, 0.0168f, 1.0f, 1.6f}, MGEMM_SK(float, 64, 64, 32, 2, 2, false, 4)),
         MGEMM_VARIANT_F32(64, 64, 32, 2, 2, false, "mgemm_f32_64x64x32_w2x2_u", {},
                           MGEMM_SK(float, 64, 64, 32, 2, 2, false, 1)),
         // small problems: 16x16 tiles, the waves of a workgroup sharing K

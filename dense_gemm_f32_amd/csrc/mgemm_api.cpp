@@ -366,16 +366,20 @@ struct SplitPlan {
 // stands in for C or the workspace when only the variant choice is wanted
 const void *const kAnyAligned = reinterpret_cast<const void *>((uintptr_t)256);
 
-// Small grids of builds without 16-byte loads: when the plain grid is at most
-// two rounds of 256 workgroups and its build copies 4 bytes per lane (or has
-// only the range-checked register path), about one workgroup per CU leaves
-// the load latency exposed.  Three chunks of all of C triple the
-// workgroups per CU.  Applied only where one tile's MFMA work is at least
-// 5 us at the matrix peak, so that the two extra launches stay small beside
-// it.  (Measured, plain -> 3 chunks: ragged 1000x1027x999 fp32 56 -> 46 us,
-// 1100^3 fp32 58 -> 42, the ragged shape in fp64 94 -> 66; the rule leaves
-// alone bf16 ragged (31 -> 34), aligned fp32 1024^3 (26 -> 28) and aligned
-// fp64 1024^3 (65 -> 70).)
+// Small grids of builds without 16-byte aligned rows: when the plain grid is
+// at most one and a half rounds of 256 workgroups (a second round at most
+// half full) and its build is one of the 4-byte-copy or range-checked
+// register builds, three chunks of all of C spread the last round's tiles
+// and put two or three workgroups on every CU to hide each other's loads.
+// Applied only where one tile's MFMA work is at least 5 us at the matrix
+// peak, so that the two extra launches stay small beside it.  Measured,
+// plain -> 3 chunks (fp32 with odd leading dimensions unless noted): 600^2 x
+// 999, 100 tiles, 32.0 -> 23.4 us; 1000x1024x999, 256 tiles, 31.3 -> 31.9;
+// 1000^2 x 2000, 256 tiles, 54.2 -> 48.1; ragged 1000x1027x999, 272 tiles,
+// 44.1 -> 37.4; 1100^3, 324 tiles, 47.4 -> 41.4; the ragged shape in fp64
+// 89.7 -> 65.6.  A second round more than half full loses: 1300^2 x 999, 441
+// tiles, 43.9 -> 54.3.  The rule leaves alone bf16 ragged (31 -> 34),
+// aligned fp32 1024^3 (26 -> 28) and aligned fp64 1024^3 (65 -> 70).
 int64_t small_grid_splits(int dtype, int transA, int transB, int64_t M, int64_t N, int64_t K,
                           const void *A, int64_t lda, const void *B, int64_t ldb)
 {
@@ -384,7 +388,7 @@ int64_t small_grid_splits(int dtype, int transA, int transB, int64_t M, int64_t 
                           0, 0.0, kAnyAligned, N, 0, 1, &full) != MGEMM_OK ||
         full.kind != Plan::GEMM)
         return 1;
-    if (full.grid > 512 || full.var->vec) return 1;
+    if (full.grid > 384 || full.var->vec) return 1;
     // matrix peak per CU, flop/s: fp32 157.3 T, fp64 78.6 T, 16-bit 2516.6 T, int8 5000 T over 256 CUs
     const double per_cu = dtype == MGEMM_F32 ? 157.3e12 / 256 : dtype == MGEMM_F64 ? 78.6e12 / 256
                         : dtype == MGEMM_I8 ? 5000e12 / 256 : 2516.6e12 / 256;
