@@ -847,9 +847,11 @@ struct DmaPath {
     static constexpr int G = F32 ? BK / 8 : BK * ES / 32;  // k-groups (32 bytes of k) per slab
     static constexpr bool A_KC = !TA, B_KC = TB;
     static constexpr bool A_TR = TA && !F32, B_TR = !TB && !F32;
-    // raised priority while multiplying (not with 4-byte copies, whose four
-    // times as many copy instructions lost 4% on the ragged fp32 shape)
-    static constexpr bool PRIO = !DW && (F32 || B_KC);
+    // raised priority while multiplying (with 4-byte copies on every slab
+    // the 4-byte-copy builds lost 4% to it on the ragged fp32 shape; with
+    // 16-byte copies on all but the last slab they gain 0-2%, same-box A/B
+    // over odd leading dimensions from 1000x1024x999 to 3000x3001x2999)
+    static constexpr bool PRIO = F32 || B_KC;
     // 256x256 16-bit tiles whose B is MN-contiguous (transposing fragment
     // reads): each group's fragment reads are issued at two per MFMA from
     // its start, and after the slab barrier the copies of the next slab
