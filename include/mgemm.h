@@ -52,7 +52,8 @@
  *   inside a kernel surface at the caller's next synchronisation.
  * Aliasing.  C must not overlap A or B.
  * Alignment.  Only element alignment is required; wider (16-byte) accesses
- *   are used when pointers, leading dimensions and strides allow them.
+ *   are used when pointers, leading dimensions and strides allow them
+ *   (rows aligned to 4 bytes are enough for all but a tile's last K-slab).
  */
 #ifndef MGEMM_H
 #define MGEMM_H
@@ -298,8 +299,10 @@ typedef struct {
     int lds_bytes;     /* LDS per workgroup */
     int pipe;          /* DMA-path schedule: 1 = four LDS stages of
                           block_k/2, 2 = two stages of block_k, 3 = one
-                          stage of block_k (K <= block_k only), 4 = 4-byte
-                          copies in two stages of block_k (every tile);
+                          stage of block_k (K <= block_k only), 4 = rows
+                          4-byte aligned, two stages of block_k, 16-byte
+                          copies but 4-byte ones on a tile's last slab
+                          (every tile);
                           6 = small-problem kernel: one 16x16 tile per
                           workgroup, its waves_n waves sharing K, operands
                           through registers, K <= block_k */
