@@ -721,6 +721,54 @@ def test_streamk_quick_returns_and_shared_workspace():
         assert left == 0, f"{left} counter bytes non-zero after stream-K {q.M}x{q.N}x{q.K}"
 
 
+ODD_ROW_BUILDS = {"f32": "mgemm_f32_%dx%dx32_w2x2_d4_u", "bf16": "mgemm_bf16_%dx%dx64_w2x2_d4_u",
+                  "f16": "mgemm_f16_%dx%dx64_w2x2_d4_u", "i8": "mgemm_i8_%dx%dx128_w2x2_d4_u"}
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16", "i8"])
+def test_odd_row_builds_copy_rules_exact(dtype):
+    # The builds for rows that are only 4-byte aligned copy 16 bytes per lane on
+    # every whole slab with operand rows after it and 4 bytes on a tile's last
+    # slab.  Cases: MN-contiguous operands whose edge chunks straddle the m/n
+    # edge; M or N too small for 16-byte rows (4-byte copies throughout); K a
+    # whole number of slabs (the last one whole but at the end of K); one slab
+    # plus one piece; strided batches with rows packed tight.  Integer data,
+    # compared exactly.
+    es = {"f32": 4, "bf16": 2, "f16": 2, "i8": 1}[dtype]
+    piece = 4 // es
+    i8 = dtype == "i8"
+    ids = {v["name"]: v["id"] for v in mg.variants()}
+    bk = {"f32": 32, "bf16": 64, "f16": 64, "i8": 128}[dtype]
+
+    def odd(cols):   # a whole number of 4-byte pieces, not of 16 bytes
+        x = -(-cols // piece) * piece
+        return x + piece if (x * es) % 16 == 0 else x
+
+    cases = [(133, 129, 3 * bk + piece, 1), (130, 70, 2 * bk, 1), (97, 3 if es == 4 else 6, 3 * bk, 1),
+             (3 if es == 4 else 6, 90, 2 * bk + piece, 1), (70, 75, bk + piece, 3), (200, 203, 5 * bk, 2)]
+    try:
+        for tile in (64, 128):
+            name = ODD_ROW_BUILDS[dtype] % (tile, tile)
+            mg.force_variant(dtype, ids[name])
+            for n, (M, N, K, batch) in enumerate(cases):
+                for tA, tB in itertools.product((False, True), repeat=2):
+                    if i8 and tile == 64 and (tA or not tB):
+                        continue   # the 64x64 int8 tiles take A and B K-contiguous only
+                    lda, ldb = odd(M if tA else K), odd(K if tB else N)
+                    a_rows, b_rows = (K if tA else M), (N if tB else K)
+                    p = wl.Problem(dtype, M, N, K, transA=tA, transB=tB, lda=lda, ldb=ldb, batch=batch,
+                                   strideA=a_rows * lda, strideB=b_rows * ldb,
+                                   alpha=3.0 if i8 else 1.5, beta=-2.0 if i8 else 0.5, dist="int",
+                                   int_lo=-128 if i8 else -8, int_hi=127 if i8 else 8, c_dist="int",
+                                   c_dtype="i32" if i8 else "f32", seed=170 + n)
+                    info, _ = mg.select(dtype, int(tA), int(tB), M, N, K, p.alpha, 16, lda, p.strideA, 16, ldb,
+                                        p.strideB, p.beta, 16, p.ldc, p.strideC, batch)
+                    assert info["name"] == name, (info["name"], name)
+                    full_check(p, exact=True, what=f"{name} tA={int(tA)} tB={int(tB)} {M}x{N}x{K} batch {batch}")
+    finally:
+        mg.force_variant(dtype, None)
+
+
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_one_stage_builds_shallow_k_exact(dtype):
     # the one-stage 256x256 builds (K of one slab at most): full and edge tiles, a K tail
