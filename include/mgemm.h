@@ -450,8 +450,8 @@ typedef struct {
 
 /* Fill *out with gemm_streamk's plan (A and B stand for the operand
  * addresses: their alignment matters, their contents do not).  Pure host;
- * MGEMM_INVALID_ARG for workgroups < 0, an in_dtype without stream-K, or
- * out == NULL. */
+ * MGEMM_INVALID_ARG for workgroups < 0, an unknown in_dtype, or out ==
+ * NULL. */
 mgemm_status mgemm_streamk_plan(mgemm_dtype in_dtype, mgemm_op transA, mgemm_op transB,
                                 int64_t M, int64_t N, int64_t K,
                                 const void *A, int64_t lda, const void *B, int64_t ldb,
