@@ -16,8 +16,8 @@ const Variant *bf16_variants(int *count)
     // the 256x256 tile), and without it the choice took them at 3000^3 and
     // 7000^3 where the large tile is faster.  K <= 128 (store-bound) takes the
     // 256x256 4x2-wave tile first.  Builds without an estimate run when
-    // forced, or by preference order when no estimated build fits (unaligned
-    // rows: 4-byte copies first).
+    // forced, or by preference order when no estimated build fits (rows not
+    // 4-byte aligned, or offsets past 32 bits: the register-path builds).
     static const Variant table[] = {
         MGEMM_VARIANT_D(__bf16, 2, 256, 256, 64, 2, 4, true, 2, "mgemm_bf16_256x256x64_w2x4_d2", {10.7f, 0.0219f, 1.6f, 1.0f}),
         MGEMM_VARIANT(__bf16, 2, 256, 256, 64, 2, 4, true, "mgemm_bf16_256x256x64_w2x4", {}),
@@ -29,20 +29,30 @@ const Variant *bf16_variants(int *count)
         // 128x128 with eight waves: four stages of 32 for one-round grids (the
         // deeper ring hides the loads of a lone workgroup), two of 64 when a CU
         // holds several workgroups
-        MGEMM_VARIANT(__bf16, 2, 128, 128, 64, 2, 4, true, "mgemm_bf16_128x128x64_w2x4", {2.35f, 0.00964f, 1.5f, 1.07f},
+        MGEMM_VARIANT(__bf16, 2, 128, 128, 64, 2, 4, true, "mgemm_bf16_128x128x64_w2x4", {2.35f, 0.00964f, 1.65f, 1.07f},
                       MGEMM_SK16(__bf16, 128, 128, 64, 2, 4, true, 1)),
-        MGEMM_VARIANT_D(__bf16, 2, 128, 128, 64, 2, 4, true, 2, "mgemm_bf16_128x128x64_w2x4_d2", {2.46f, 0.00829f, 1.5f, 1.39f},
+        MGEMM_VARIANT_D(__bf16, 2, 128, 128, 64, 2, 4, true, 2, "mgemm_bf16_128x128x64_w2x4_d2", {2.46f, 0.00829f, 1.65f, 1.39f},
                         MGEMM_SK16(__bf16, 128, 128, 64, 2, 4, true, 2)),
-        // rows 4-byte aligned (and K even): 4-byte copies into LDS, every tile
-        MGEMM_VARIANT_D(__bf16, 2, 128, 128, 64, 2, 2, false, 4, "mgemm_bf16_128x128x64_w2x2_d4_u", {},
+        // rows 4-byte aligned (and K even), every tile: 16-byte copies on all
+        // but a tile's last slab, which takes 4-byte copies.  Estimates: a fit
+        // on rows only 4-byte aligned (1.3 to 1.5 times the two-stage
+        // siblings' time per K on the same box, bf16 and f16 alike).  On
+        // 16-byte aligned rows with a K tail they beat the siblings' register
+        // path by 1.3 to 1.65x (bf16 2048^2 x 2046: 28.3 against 44.1 us;
+        // 3000^2 x 2998: 94.7 against 119.7; 4096^2 x 4094: 122.8 against
+        // 163.3), which is what the siblings' register factors (1.6, 1.65;
+        // 1.1 and 1.5 before) now say
+        MGEMM_VARIANT_D(__bf16, 2, 128, 128, 64, 2, 2, false, 4, "mgemm_bf16_128x128x64_w2x2_d4_u",
+                        {3.06f, 0.00845f, 1.0f, 1.55f},
                         MGEMM_SK16(__bf16, 128, 128, 64, 2, 2, false, 4)),
         MGEMM_VARIANT(__bf16, 2, 128, 128, 64, 2, 2, false, "mgemm_bf16_128x128x64_w2x2_u", {},
                       MGEMM_SK16(__bf16, 128, 128, 64, 2, 2, false, 1)),
-        MGEMM_VARIANT(__bf16, 2, 64, 64, 64, 2, 2, true, "mgemm_bf16_64x64x64_w2x2", {0.44f, 0.00391f, 1.1f, 1.73f},
+        MGEMM_VARIANT(__bf16, 2, 64, 64, 64, 2, 2, true, "mgemm_bf16_64x64x64_w2x2", {0.44f, 0.00391f, 1.6f, 1.73f},
                       MGEMM_SK16(__bf16, 64, 64, 64, 2, 2, true, 1)),
-        MGEMM_VARIANT_D(__bf16, 2, 64, 64, 64, 2, 2, true, 2, "mgemm_bf16_64x64x64_w2x2_d2", {0.45f, 0.00335f, 1.1f, 2.32f},
+        MGEMM_VARIANT_D(__bf16, 2, 64, 64, 64, 2, 2, true, 2, "mgemm_bf16_64x64x64_w2x2_d2", {0.45f, 0.00335f, 1.6f, 2.32f},
                         MGEMM_SK16(__bf16, 64, 64, 64, 2, 2, true, 2)),
-        MGEMM_VARIANT_D(__bf16, 2, 64, 64, 64, 2, 2, false, 4, "mgemm_bf16_64x64x64_w2x2_d4_u", {},
+        MGEMM_VARIANT_D(__bf16, 2, 64, 64, 64, 2, 2, false, 4, "mgemm_bf16_64x64x64_w2x2_d4_u",
+                        {0.90f, 0.00427f, 1.0f, 2.2f},
                         MGEMM_SK16(__bf16, 64, 64, 64, 2, 2, false, 4)),
         MGEMM_VARIANT(__bf16, 2, 64, 64, 64, 2, 2, false, "mgemm_bf16_64x64x64_w2x2_u", {},
                       MGEMM_SK16(__bf16, 64, 64, 64, 2, 2, false, 1)),

@@ -16,7 +16,8 @@ const Variant *i8_variants(int *count)
     // round), 64x64 0.0014 to 0.0020.  The register-path factor (16-byte
     // rows, K no multiple of 16) is a round estimate.  Builds without an
     // estimate run when forced, or by preference order when no estimated
-    // build fits (unaligned rows: 4-byte copies first).
+    // build fits (rows not 4-byte aligned, or offsets past 32 bits: the
+    // register-path builds).
     static const Variant table[] = {
         MGEMM_VARIANT_I8_ALL(256, 256, 128, 2, 4, true, 2, "mgemm_i8_256x256x128_w2x4_d2", {8.0f, 0.0121f, 1.5f, 1.15f}),
         MGEMM_VARIANT_I8_ALL(256, 256, 128, 2, 4, true, 1, "mgemm_i8_256x256x128_w2x4", {}),
@@ -26,8 +27,12 @@ const Variant *i8_variants(int *count)
                          MGEMM_SK_I8_ALL(128, 128, 128, 2, 4, true, 1)),
         MGEMM_VARIANT_I8_ALL(128, 128, 128, 2, 4, true, 2, "mgemm_i8_128x128x128_w2x4_d2", {3.59f, 0.00336f, 1.5f, 1.35f},
                          MGEMM_SK_I8_ALL(128, 128, 128, 2, 4, true, 2)),
-        // rows 4-byte aligned (and K a multiple of 4): 4-byte copies into LDS, every tile
-        MGEMM_VARIANT_I8_ALL(128, 128, 128, 2, 2, false, 4, "mgemm_i8_128x128x128_w2x2_d4_u", {},
+        // rows 4-byte aligned (and K a multiple of 4), every tile: 16-byte
+        // copies on all but a tile's last slab (4-byte copies).  Estimates from
+        // a same-box fit against the two-stage siblings, scaled by their
+        // table/fit ratios: 1.4 to 1.5 times their time per K
+        MGEMM_VARIANT_I8_ALL(128, 128, 128, 2, 2, false, 4, "mgemm_i8_128x128x128_w2x2_d4_u",
+                             {4.2f, 0.0046f, 1.0f, 1.35f},
                          MGEMM_SK_I8_ALL(128, 128, 128, 2, 2, false, 4)),
         MGEMM_VARIANT_I8_ALL(128, 128, 128, 2, 2, false, 1, "mgemm_i8_128x128x128_w2x2_u", {},
                          MGEMM_SK_I8_ALL(128, 128, 128, 2, 2, false, 1)),
@@ -35,7 +40,8 @@ const Variant *i8_variants(int *count)
                          MGEMM_SK_I8(64, 64, 128, 2, 2, true, 1)),
         MGEMM_VARIANT_I8(64, 64, 128, 2, 2, true, 2, "mgemm_i8_64x64x128_w2x2_d2", {0.82f, 0.00139f, 1.5f, 3.16f},
                          MGEMM_SK_I8(64, 64, 128, 2, 2, true, 2)),
-        MGEMM_VARIANT_I8(64, 64, 128, 2, 2, false, 4, "mgemm_i8_64x64x128_w2x2_d4_u", {},
+        MGEMM_VARIANT_I8(64, 64, 128, 2, 2, false, 4, "mgemm_i8_64x64x128_w2x2_d4_u",
+                         {0.84f, 0.00206f, 1.0f, 2.8f},
                          MGEMM_SK_I8(64, 64, 128, 2, 2, false, 4)),
         MGEMM_VARIANT_I8(64, 64, 128, 2, 2, false, 1, "mgemm_i8_64x64x128_w2x2_u", {},
                          MGEMM_SK_I8(64, 64, 128, 2, 2, false, 1)),

@@ -39,8 +39,9 @@ struct Variant {
     int wm, wn;           // wavefront grid
     bool vec;             // needs 16-byte aligned A/B rows (dwordx4 loads)
     int pipe;             // DMA-path schedule (1: 4 stages of bk/2, 2: 2 stages of bk,
-                          // 3: 1 stage of bk, K <= bk only, 4: 4-byte copies, 2 stages
-                          // of bk, every tile); 6: small-problem kernel (gemm_small.hpp,
+                          // 3: 1 stage of bk, K <= bk only, 4: rows 4-byte aligned, 2
+                          // stages of bk, 16-byte copies but 4-byte ones on a tile's last
+                          // slab, every tile); 6: small-problem kernel (gemm_small.hpp,
                           // registers only, K <= bk, wn waves sharing K)
     const char *name;
     LaunchFn fn[2][2];    // [transA][transB], fp32 C (int32 C for int8, double C for fp64 inputs)
