@@ -11,7 +11,8 @@
 // operand traffic per flop is small and a register-staged, double-buffered
 // tile keeps the matrix cores fed.  Every tile uses range-checked loads
 // (out-of-range elements read as zero), so edges and unaligned leading
-// dimensions need no second path.
+// dimensions need no second path.  The tile (F64Tile) serves the one-pass
+// kernel and the stream-K kernel, whose segments run it over a K range.
 //
 // LDS holds both operands k-major, [BK][P] doubles.  At MFMA step s of a
 // 16-deep group, lane (g = lane/16, i = lane%16) reads row
@@ -132,8 +133,8 @@ struct F64Tile {
     static constexpr int SMEM = 2 * STAGE;          // doubles of LDS
 
     // acc += op(A) x op(B) over K columns of A (rows of B) for the tile at
-    // (m0, n0) of batch entry bidx, starting `k_off` columns in; mrem, nrem:
-    // rows and columns of the tile inside C.
+    // (m0, n0) of batch entry bidx, starting `k_off` columns in (a stream-K
+    // segment); rows past M, columns past N and k past K read as zero.
     __device__ __forceinline__ static void run(const KernelArgs &p, double *smem, int bidx, int m0, int n0,
                                                int64_t k_off, int K, f64x4 (&acc)[TM][TN])
     {

@@ -804,12 +804,13 @@ struct RegPath {
 //      8/16-bit elements, whose K is a multiple of the 4-byte piece), BK =
 //      BKR, NS = 2.  Whole slabs with operand rows after them are copied 16
 //      bytes per lane at 4-byte aligned addresses (a multi-dword access
-//      needs only dword alignment; measured as fast as on 16-byte aligned
-//      rows).  The last slab of a tile takes 4-byte copies: each lane copies
-//      one piece, and lanes whose piece lies past the matrix (row, column or
-//      k) are masked to zero by the buffer range check, so edges, K tails and
-//      leading dimensions that are no multiple of 16 bytes need no register
-//      path.
+//      needs only dword alignment; fp32 measured as fast as on 16-byte
+//      aligned rows, 16-bit and int8 1.3 to 1.5 times slower per K, still
+//      well ahead of the register path).  The last slab of a tile takes
+//      4-byte copies: each lane copies one piece, and lanes whose piece lies
+//      past the matrix (row, column or k) are masked to zero by the buffer
+//      range check, so edges, K tails and leading dimensions that are no
+//      multiple of 16 bytes need no register path.
 //
 // LDS layouts (bank-conflict free for every access of this path):
 //   KC  operand K-contiguous in memory: rows of BK elements (RB = 64 or 128
