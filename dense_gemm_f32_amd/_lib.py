@@ -183,7 +183,8 @@ def _extent(rows, cols, ld, stride, batch):
 
 
 def _addr(x, need_elems: int, elem_size: int, what: str):
-    """Device address of x; for tensors also checks device and size."""
+    """(device address, CUDA device index or None) of x; for tensors also checks the
+    device, element size, layout and size."""
     if x is None:
         return None, None
     if isinstance(x, int):
@@ -199,16 +200,29 @@ def _addr(x, need_elems: int, elem_size: int, what: str):
         raise ValueError(f"{what} must be a contiguous buffer (express strides with ld/stride)")
     if x.numel() < need_elems:
         raise ValueError(f"{what}: buffer holds {x.numel()} elements, sizes need {need_elems}")
-    return x.data_ptr(), x.device
+    return x.data_ptr(), x.get_device()
+
+
+_current_raw_stream = None   # device index -> handle of torch's current stream there
 
 
 def _stream(stream, device):
+    """Launch stream handle: `stream` itself, else torch's current stream on `device` (a
+    CUDA device index), else None (the library's default, the null stream)."""
     if stream is not None:
         return int(stream)
     if device is None:
         return None
-    import torch
-    return torch.cuda.current_stream(device).cuda_stream
+    global _current_raw_stream
+    if _current_raw_stream is None:
+        import torch
+        # the raw handle without building a Stream object (about 0.06 against 1.9 us a
+        # call, which matters for launches of a few microseconds); the public call
+        # otherwise
+        raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        _current_raw_stream = raw if raw is not None else (
+            lambda index: torch.cuda.current_stream(index).cuda_stream)
+    return _current_raw_stream(device)
 
 
 def _workspace_on(nbytes, device, stream, launch, zero=False):
