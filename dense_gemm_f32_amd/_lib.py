@@ -187,6 +187,15 @@ def _addr(x, need_elems: int, elem_size: int, what: str):
     device, element size, layout and size."""
     if x is None:
         return None, None
+    if type(x) is int:
+        return x, None
+    # the common case in one expression; anything else takes the checks below,
+    # which name what is wrong
+    try:
+        if x.is_cuda and x.element_size() == elem_size and x.numel() >= need_elems and x.is_contiguous():
+            return x.data_ptr(), x.get_device()
+    except (AttributeError, TypeError):
+        pass
     if isinstance(x, int):
         return x, None
     import torch
